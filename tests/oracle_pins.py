@@ -1,0 +1,306 @@
+"""Pins for the CPU oracle: checks against values that do not come from the
+oracle itself.
+
+Each ``pin_*`` takes a loaded oracle build and raises AssertionError when it
+disagrees with:
+  - hand-derived worked examples (tests/golden/*.json, derivations inside);
+  - closed forms and invariants of absmax quantization (error at most half a
+    quantization step, the absmax element maps to +-127, signs kept);
+  - library routines the special cases reduce to (numpy int64 / float64
+    matmul, numpy's float16 conversion);
+  - metamorphic relations (power-of-two scaling, joint permutation of the
+    hidden dimension).
+
+Sources of the method: LLM.int8() abstract (taxoreview.com page, second
+paragraph) and "LLM.int8(): A Procedure for Int8 Matrix Multiplication in
+Transformer Language Models", section "The LLM.int8() Methodology".
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+# |x - q*s/127| <= s/254 * (1 + SLACK): the two fp32 roundings in
+# x * fp32(127/s) move the product by at most 127 * 2^-23 quantization steps,
+# i.e. 3.03e-5 of the half step; 2^-14 = 6.1e-5 leaves margin.
+SLACK = 2.0 ** -14
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _case(seed, T, K, N, n_dims=0, factor=15.0, x_dist="normal", w_sigma=0.05):
+    return synth.random_case(seed, T, K, N, n_dims=n_dims, factor=factor, x_dist=x_dist,
+                             w_sigma=w_sigma)
+
+
+# ------------------------------------------------------------------ fp16 codec
+
+def pin_f16_codec(orc):
+    """Decode every binary16 pattern and encode doubles, against numpy."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    fin = np.isfinite(ref)
+    got = np.array([orc.f16_decode(int(b)) for b in bits[fin][::7]])
+    assert np.array_equal(got, ref[fin][::7]), "fp16 decode"
+    for b in (0x7C00, 0xFC00):
+        assert np.isinf(orc.f16_decode(b))
+    rng = np.random.default_rng(7)
+    v = rng.standard_normal(3000) * 10.0 ** rng.integers(-9, 6, 3000)
+    # exact ties between neighbours, both parities, and the range edges
+    grid = np.arange(0, 64, dtype=np.float64)
+    ties = (1024 + grid + 0.5) * 2.0 ** -10 * 4            # halfway points in [4, 8)
+    sub_ties = (grid + 0.5) * 2.0 ** -24                   # halfway points among subnormals
+    edges = np.array([65504.0, 65519.99, 65520.0, 1e6, 2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26,
+                      2.0 ** -14 - 2.0 ** -25, 0.0, -0.0])
+    v = np.concatenate([v, ties, -ties, sub_ties, edges])
+    with np.errstate(over="ignore"):
+        ref = v.astype(np.float16).view(np.uint16)
+    got = np.array([orc.f16_encode(x) for x in v], dtype=np.uint16)
+    assert np.array_equal(got, ref), f"fp16 encode: {np.flatnonzero(got != ref)[:5]}"
+
+
+# -------------------------------------------------------- hand-worked examples
+
+def pin_hand_example(orc):
+    g = _load("hand_2x4x2.json")
+    X = np.array(g["X"], np.float16)
+    W = np.array(g["W"], np.float16)
+    Wq, sw = orc.quantize_weight(W)
+    assert np.array_equal(Wq, np.array(g["Wq_NK"], np.int8)), "hand Wq"
+    assert np.array_equal(sw, np.array(g["sw"], np.float32)), "hand sw"
+    r = orc.mixed_matmul(X, Wq, sw, W, g["tau"])
+    assert r["idx"].tolist() == g["idx"], "hand idx"
+    assert np.array_equal(r["sx"], np.array(g["sx"], np.float32)), "hand sx"
+    assert np.array_equal(r["xq"], np.array(g["Xq"], np.int8)), "hand Xq"
+    assert np.array_equal(r["acc"], np.array(g["acc"], np.int32)), "hand acc"
+    num = np.array([a / b + c for a, b, c in g["Y64_num"]]).reshape(2, 2)
+    assert np.allclose(r["Y64"], num, rtol=1e-14, atol=0), "hand Y64"
+    assert np.array_equal(r["Y"].astype(np.float64), np.array(g["Y"])), "hand Y"
+
+
+def pin_quant_ties(orc):
+    g = _load("quant_ties.json")
+    for c in g["cases"]:
+        row = np.array([c["row"]], np.float16)
+        flag = np.zeros(row.shape[1], np.uint8)
+        q, s = orc.quantize_rows(row, flag)
+        assert float(s[0]) == c["s"], f"scale {c['note']}"
+        assert q[0].tolist() == c["q"], f"row quant {c['note']}: {q[0].tolist()}"
+        # the same values as one weight column
+        wq, sw = orc.quantize_weight(row.T.copy())
+        assert float(sw[0]) == c["s"] and wq[0].tolist() == c["q"], f"weight {c['note']}"
+
+
+# --------------------------------------------------------------- outlier set
+
+def pin_detect(orc):
+    for seed, (T, K) in enumerate([(16, 64), (37, 80), (5, 304), (64, 128)]):
+        X, _ = _case(100 + seed, T, K, 8, n_dims=3, factor=9.0)
+        for tau in (6.0, 3.5, 1.0):
+            ref = np.any(np.abs(X.astype(np.float32)) >= np.float32(tau), axis=0)
+            assert np.array_equal(orc.detect(X, tau).astype(bool), ref), f"detect tau={tau}"
+        assert orc.detect(X, 0.0).all(), "tau = 0 flags every dimension"
+        assert not orc.detect(X, float("inf")).any(), "tau = inf flags none"
+    # exact tie at the threshold counts as crossing; the next fp16 below does not
+    X = np.zeros((3, 16), np.float16)
+    X[1, 5] = 6.0
+    X[2, 9] = -6.0
+    X[0, 11] = np.float16(6.0) - np.float16(2.0 ** -8)     # 5.99609375
+    f = orc.detect(X, 6.0)
+    assert f.tolist() == [1 if k in (5, 9) else 0 for k in range(16)], "tie handling"
+
+
+def pin_compact(orc):
+    rng = np.random.default_rng(3)
+    for K in (1, 16, 100, 1000):
+        for p in (0.0, 0.1, 0.5, 1.0):
+            flag = (rng.random(K) < p).astype(np.uint8)
+            assert np.array_equal(orc.compact(flag), np.flatnonzero(flag)), "compact"
+
+
+def pin_tiny_config(orc):
+    w = synth.WORKLOADS["tiny"]
+    X = synth.make_x(w)
+    flag = orc.detect(X, w.tau)
+    assert orc.compact(flag).tolist() == [3, 17], "tiny config outlier set"
+
+
+# ----------------------------------------------------- quantizer invariants
+
+def _check_absmax_rows(Xf, q, s, excluded):
+    """Invariants of symmetric absmax quantization of each row of Xf (float64)
+    over the columns not in `excluded` (bool per column)."""
+    keep = ~excluded
+    ref_s = np.abs(Xf[:, keep]).max(axis=1) if keep.any() else np.zeros(len(Xf))
+    assert np.array_equal(s.astype(np.float64), ref_s), "scale = absmax over kept columns"
+    assert np.all(q[:, excluded] == 0), "excluded columns are zero"
+    assert np.all(np.abs(q.astype(np.int32)) <= 127), "range [-127, 127]"
+    for t in range(len(Xf)):
+        if s[t] == 0:
+            assert not q[t].any(), "zero scale gives zero row"
+            continue
+        xk = Xf[t, keep]
+        qk = q[t, keep].astype(np.float64)
+        am = np.argmax(np.abs(xk))
+        assert qk[am] == np.sign(xk[am]) * 127, "absmax element maps to +-127"
+        assert np.all((np.sign(qk) == np.sign(xk)) | (qk == 0)), "sign kept or zero"
+        err = np.abs(xk - qk * float(s[t]) / 127.0)
+        assert np.all(err <= float(s[t]) / 254.0 * (1 + SLACK)), "error above half a step"
+        # values far from a rounding boundary quantize to the nearest integer
+        exact = xk * 127.0 / float(s[t])
+        safe = np.abs(exact - np.floor(exact) - 0.5) > 1e-3
+        assert np.array_equal(qk[safe], np.rint(exact[safe])), "nearest level"
+
+
+def pin_quant_invariants(orc):
+    for seed, (T, K, nd, dist) in enumerate([(16, 64, 2, "normal"), (33, 96, 5, "laplace"),
+                                             (7, 160, 0, "normal"), (20, 48, 48, "normal")]):
+        X, W = _case(200 + seed, T, K, 40, n_dims=nd, x_dist=dist)
+        X[3 % T] = 0                                    # an all-zero row
+        flag = orc.detect(X, 6.0)
+        q, s = orc.quantize_rows(X, flag)
+        _check_absmax_rows(X.astype(np.float64), q, s, flag.astype(bool))
+        Wq, sw = orc.quantize_weight(W)
+        assert Wq.shape == (W.shape[1], W.shape[0]), "Wq stored [N,K]"
+        _check_absmax_rows(W.T.astype(np.float64), Wq, sw, np.zeros(K, bool))
+    # grid values quantize exactly: x = j * s / 127 with s = 127 -> q = j
+    j = np.arange(-127, 128, dtype=np.float64)
+    row = np.array([j], np.float16)
+    q, s = orc.quantize_rows(row, np.zeros(row.shape[1], np.uint8))
+    assert np.array_equal(q[0].astype(np.float64), j) and s[0] == 127.0, "grid values"
+    # a row whose largest entry sits in an outlier column takes its scale
+    # from the remaining columns
+    X = np.array([[1.0, -3.0, 50.0, 2.0]], np.float16)
+    q, s = orc.quantize_rows(X, np.array([0, 0, 1, 0], np.uint8))
+    assert s[0] == 3.0 and q[0].tolist() == [42, -127, 0, 85], "outlier excluded from scale"
+
+
+# ------------------------------------------------------------- int8 matmul
+
+def pin_gemm(orc):
+    rng = np.random.default_rng(11)
+    for M, K, N in [(1, 1, 1), (3, 17, 5), (16, 64, 48), (9, 256, 33)]:
+        a = rng.integers(-127, 128, (M, K)).astype(np.int8)
+        b = rng.integers(-127, 128, (N, K)).astype(np.int8)
+        ref = a.astype(np.int64) @ b.astype(np.int64).T
+        assert np.array_equal(orc.int8_gemm(a, b).astype(np.int64), ref), "int8 gemm"
+    # the extreme sum 127*127*K fits int32 up to K = 133144 and not beyond
+    a = np.full((1, 133144), 127, np.int8)
+    assert int(orc.int8_gemm(a, a)[0, 0]) == 127 * 127 * 133144, "largest in-range sum"
+    a = np.full((1, 133145), 127, np.int8)
+    try:
+        orc.int8_gemm(a, a)
+    except OverflowError:
+        pass
+    else:
+        raise AssertionError("overflow past 133144 not reported")
+
+
+# --------------------------------------------------- the whole method's Y
+
+def pin_tau_inf(orc):
+    """No outliers: Y is the plain vector-wise int8 matmul, i.e. the product
+    of the dequantized operands (numpy float64 matmul)."""
+    for seed, (T, K, N) in enumerate([(16, 64, 48), (21, 96, 40)]):
+        X, W = _case(300 + seed, T, K, N, n_dims=2)
+        Wq, sw = orc.quantize_weight(W)
+        r = orc.mixed_matmul(X, Wq, sw, W, float("inf"))
+        assert r["o"] == 0
+        xd = r["xq"].astype(np.float64) * r["sx"].astype(np.float64)[:, None] / 127.0
+        wd = Wq.astype(np.float64) * sw.astype(np.float64)[:, None] / 127.0
+        ref = xd @ wd.T
+        assert np.allclose(r["Y64"], ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max()), "tau=inf"
+        assert np.array_equal(r["Y"], ref.astype(np.float16)), "tau=inf fp16"
+
+
+def pin_tau_zero(orc):
+    """Every dimension an outlier: Y is the 16-bit matmul (numpy float64,
+    then one rounding to fp16)."""
+    for seed, (T, K, N) in enumerate([(16, 64, 48), (5, 80, 24)]):
+        X, W = _case(400 + seed, T, K, N)
+        Wq, sw = orc.quantize_weight(W)
+        r = orc.mixed_matmul(X, Wq, sw, W, 0.0)
+        assert r["o"] == K and not r["xq"].any() and not r["sx"].any()
+        ref = X.astype(np.float64) @ W.astype(np.float64)
+        assert np.allclose(r["Y64"], ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max()), "tau=0"
+        assert np.array_equal(r["Y"], ref.astype(np.float16)), "tau=0 fp16"
+
+
+def pin_error_bound(orc):
+    """|Y64 - X W| <= sum over non-outlier k of |x| e_w + |w_hat| e_x, with
+    e = s/254 (1 + SLACK) the per-element quantization bound (x w - xh wh =
+    x (w - wh) + wh (x - xh)); outlier dimensions contribute no error."""
+    for seed, (T, K, N, nd) in enumerate([(16, 64, 48, 2), (24, 128, 56, 6), (8, 96, 32, 0)]):
+        X, W = _case(500 + seed, T, K, N, n_dims=nd)
+        Wq, sw = orc.quantize_weight(W)
+        r = orc.mixed_matmul(X, Wq, sw, W, 6.0)
+        Xf, Wf = X.astype(np.float64), W.astype(np.float64)
+        keep = ~r["flag"].astype(bool)
+        ex = r["sx"].astype(np.float64) / 254 * (1 + SLACK)
+        ew = sw.astype(np.float64) / 254 * (1 + SLACK)
+        wh = Wq.T.astype(np.float64) * sw.astype(np.float64)[None, :] / 127
+        bound = (np.abs(Xf[:, keep]).sum(1)[:, None] * ew[None, :]
+                 + ex[:, None] * np.abs(wh[keep]).sum(0)[None, :])
+        exact = Xf @ Wf
+        err = np.abs(r["Y64"] - exact)
+        assert np.all(err <= bound + 1e-12 * np.abs(Xf) @ np.abs(Wf)), "quantization error bound"
+        if nd:
+            assert r["o"] >= nd
+
+
+def pin_metamorphic_scale(orc):
+    """X * 2^e with tau * 2^e: same outliers, Xq and acc; s_x and Y scale by 2^e."""
+    X, W = _case(600, 12, 64, 24, n_dims=2)
+    Wq, sw = orc.quantize_weight(W)
+    base = orc.mixed_matmul(X, Wq, sw, W, 6.0)
+    for e in (-3, 2):
+        Xs = (X.astype(np.float64) * 2.0 ** e).astype(np.float16)
+        r = orc.mixed_matmul(Xs, Wq, sw, W, 6.0 * 2.0 ** e)
+        assert np.array_equal(r["idx"], base["idx"]) and np.array_equal(r["xq"], base["xq"])
+        assert np.array_equal(r["acc"], base["acc"])
+        assert np.array_equal(r["sx"], base["sx"] * np.float32(2.0 ** e))
+        assert np.allclose(r["Y64"], base["Y64"] * 2.0 ** e, rtol=1e-13, atol=0)
+
+
+def pin_permutation(orc):
+    """Permuting the hidden dimension of X's columns and W's rows together
+    permutes the outlier set and leaves s_x, s_w, acc and Y unchanged."""
+    X, W = _case(700, 10, 80, 16, n_dims=3)
+    Wq, sw = orc.quantize_weight(W)
+    base = orc.mixed_matmul(X, Wq, sw, W, 6.0)
+    perm = np.random.default_rng(5).permutation(80)
+    Xp, Wp = X[:, perm].copy(), W[perm].copy()
+    Wqp, swp = orc.quantize_weight(Wp)
+    assert np.array_equal(swp, sw) and np.array_equal(Wqp, Wq[:, perm])
+    r = orc.mixed_matmul(Xp, Wqp, swp, Wp, 6.0)
+    inv = np.argsort(perm)
+    assert sorted(perm[r["idx"]].tolist()) == base["idx"].tolist()
+    assert sorted(inv[base["idx"]].tolist()) == r["idx"].tolist()
+    assert np.array_equal(r["sx"], base["sx"]) and np.array_equal(r["acc"], base["acc"])
+    assert np.allclose(r["Y64"], base["Y64"], rtol=1e-12, atol=1e-12)
+
+
+def pin_row_sample(orc):
+    """Sampled rows reproduce the same rows of the full computation (the
+    outlier set is still taken over all rows)."""
+    X, W = _case(800, 30, 64, 20, n_dims=2)
+    Wq, sw = orc.quantize_weight(W)
+    full = orc.mixed_matmul(X, Wq, sw, W, 6.0)
+    rows = np.array([29, 0, 7, 7, 13])
+    r = orc.mixed_matmul(X, Wq, sw, W, 6.0, rows=rows)
+    assert np.array_equal(r["idx"], full["idx"])
+    for key in ("xq", "sx", "acc", "Y"):
+        assert np.array_equal(r[key], full[key][rows]), key
+
+
+ALL_PINS = [pin_f16_codec, pin_hand_example, pin_quant_ties, pin_detect, pin_compact,
+            pin_tiny_config, pin_quant_invariants, pin_gemm, pin_tau_inf, pin_tau_zero,
+            pin_error_bound, pin_metamorphic_scale, pin_permutation, pin_row_sample]

@@ -1,0 +1,50 @@
+"""Each plausible mistake planted in a copy of the oracle must be caught by
+at least one pin.  The mutants are compiled from edited copies of oracle.c
+into a temporary directory; the committed oracle is never touched.  CPU only."""
+import os
+
+import pytest
+
+import oracle
+from tests import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+# (name, text in oracle.c, replacement)
+MUTANTS = [
+    ("threshold_strict", "fabsf(oh_f32(X[t * K + k])) >= tau", "fabsf(oh_f32(X[t * K + k])) > tau"),
+    ("threshold_signed", "fabsf(oh_f32(X[t * K + k])) >= tau", "oh_f32(X[t * K + k]) >= tau"),
+    ("round_half_away", "float q = rintf(p);", "float q = roundf(p);"),
+    ("round_truncate", "float q = rintf(p);", "float q = truncf(p);"),
+    ("range_128", "float r = 127.0f / s;", "float r = 128.0f / s;"),
+    ("row_scale_includes_outliers", "if (flag[k]) continue;", ";"),
+    ("outlier_column_kept", "flag[k] ? 0 : quant_one", "0 ? 0 : quant_one"),
+    ("drop_16bit_part", "double y = y8 + y16;", "double y = y8;"),
+    ("dequant_wrong_constant", "/ 16129.0", "/ 16384.0"),
+    ("dequant_one_scale", "(double)c->sx[m] * (double)c->sw[n]", "(double)c->sx[m] * (double)c->sw[0]"),
+    ("int32_wraparound", "int64_t s = 0;\n            for (int64_t k = 0; k < c->K; ++k) s += (int64_t)a[k] * (int64_t)b[k];\n            if (s > INT32_MAX",
+     "int32_t s = 0;\n            for (int64_t k = 0; k < c->K; ++k) s += (int32_t)a[k] * (int32_t)b[k];\n            if (s > INT32_MAX"),
+    ("compact_reversed", "idx[o++] = (int32_t)k;", "idx[o++] = (int32_t)(K - 1 - k);"),
+    ("f16_ties_away", "(frac == 0.5 && fmod(fl, 2.0) != 0.0)", "(frac == 0.5)"),
+    ("weight_scale_first_rows", "for (int64_t k = 0; k < c->K; ++k) {\n            float a = fabsf(oh_f32(c->W[k * c->N + n]));",
+     "for (int64_t k = 0; k < c->K / 2; ++k) {\n            float a = fabsf(oh_f32(c->W[k * c->N + n]));"),
+    ("outlier_value_from_wrong_row", "oh_decode(c->X[t * c->K + k]) * oh_decode(c->W16[k * c->N + n])",
+     "oh_decode(c->X[k]) * oh_decode(c->W16[k * c->N + n])"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation site for {name} not found in oracle.c"
+    path = tmp_path / "oracle_mutant.c"
+    path.write_text(src.replace(old, new))
+    lib = oracle.build(str(path), str(tmp_path / f"liboracle_{name}.so"))
+    orc = oracle.Oracle(lib)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, OverflowError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, f"mutant {name} passed every pin"
