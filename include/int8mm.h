@@ -1,0 +1,142 @@
+/*
+ * int8mm.h - C ABI of the LLM.int8() mixed-precision matrix multiplication
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (LLM.int8() abstract, taxoreview.com page dblp:280/8696,
+ * second paragraph; restated in "LLM.int8(): A Procedure for Int8 Matrix
+ * Multiplication in Transformer Language Models", section "The LLM.int8()
+ * Methodology"):
+ *
+ *   Y = LLM.int8()(X, W, tau),  X fp16 [T,K], W fp16 [K,N], Y fp16 [T,N]
+ *
+ *   1. outlier feature dimensions: k is an outlier when |X[t,k]| >= tau for
+ *      some row t (the pages pick outliers by magnitude; ">=" and the
+ *      absolute threshold are this library's reading);
+ *   2. vector-wise quantization, one normalization constant per inner
+ *      product: s_x[t] = absmax of row t over non-outlier k, s_w[n] = absmax
+ *      of column n of W; q = clamp(rint(v * fp32(127/s)), -127, 127), round
+ *      half to even, s = 0 -> q = 0; outlier columns of Xq are 0;
+ *   3. int8 matmul with int32 accumulation, acc = Xq . Wq^T, dequantized by
+ *      the outer product of the scales: y8 = acc * s_x[t] * s_w[n] / 127^2;
+ *   4. the isolated outlier dimensions go through a 16-bit matmul,
+ *      y16 = sum over outlier k of X[t,k] * W[k,n] (fp16 operands, fp32
+ *      accumulation), and Y = fp16(y8 + y16), rounded once.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless noted.  All buffers are owned by
+ *     the caller; the library never allocates or frees memory on any call.
+ *   - Matrices are row-major and dense (leading dimension = row length).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *     enqueue work on it and return without synchronizing; results are valid
+ *     once the stream reaches that point.
+ *   - Arguments are validated on the host before anything is enqueued; on a
+ *     non-zero status nothing was enqueued, except INT8MM_E_HIP, which
+ *     reports a launch failure from the HIP runtime.
+ *   - Inputs must be finite; NaN/Inf inputs give unspecified results.
+ *   - Calls on different streams may run concurrently when they use
+ *     different workspaces and outputs.  The library holds no mutable global
+ *     state.
+ *   - Shape limits: T, K, N >= 1; K % 16 == 0; N % 8 == 0; K <= 133136 (the
+ *     largest multiple of 16 with 127*127*K < 2^31, so int32 accumulators
+ *     cannot overflow); T <= 2^24 - 1 and T*N <= 2^38 (launch-grid limits).
+ *     Every pointer must be 16-byte aligned.
+ */
+#ifndef INT8MM_H
+#define INT8MM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    INT8MM_OK = 0,
+    INT8MM_E_NULL = 1,        /* a required pointer is NULL */
+    INT8MM_E_SHAPE = 2,       /* T, K or N outside the limits above */
+    INT8MM_E_TAU = 3,         /* tau is NaN or negative */
+    INT8MM_E_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+    INT8MM_E_WORKSPACE = 5,   /* workspace smaller than the size query returns */
+    INT8MM_E_UNSUPPORTED = 6, /* a valid request this build does not implement */
+    INT8MM_E_HIP = 7          /* the HIP runtime reported a launch error */
+} int8mm_status;
+
+#define INT8MM_MAX_K 133136
+#define INT8MM_MAX_T 16777215
+#define INT8MM_MAX_TN 274877906944.0 /* 2^38 */
+
+/* Static, human-readable name of a status code (host only; never NULL). */
+const char* int8mm_status_string(int status);
+
+/* Bytes of device workspace that int8_mixed_matmul and its variants need
+ * for this shape (host only, enqueues nothing).  The size covers the
+ * worst case in which every hidden dimension is an outlier.
+ * bytes: host pointer, receives the size.  Errors: E_NULL, E_SHAPE. */
+int int8_mixed_matmul_workspace_size(int64_t T, int64_t K, int64_t N, size_t* bytes);
+
+/* Weight conversion to Int8 ("converted to Int8" at load time, LLM.int8()
+ * abstract): column-wise absmax quantization, one scale per output column
+ * n (one per inner product).
+ *   W16: fp16 [K,N] row-major (read only)
+ *   Wq:  int8 [N,K] row-major, i.e. stored transposed with K contiguous
+ *        (written; K*N bytes)
+ *   sw:  fp32 [N] column scales s_w[n] = max_k |W[k,n]| (written)
+ * Errors: E_NULL, E_SHAPE, E_ALIGN, E_HIP. */
+int int8_quantize_weight(const void* W16, int64_t K, int64_t N, int8_t* Wq, float* sw,
+                         void* stream);
+
+/* The whole LLM.int8() matmul (steps 1-4 above) on a converted weight.
+ *   X:   fp16 [T,K] activations (read only)
+ *   Wq, sw: from int8_quantize_weight (read only)
+ *   W16: fp16 [K,N], the 16-bit weight; only its outlier rows are read.
+ *        NULL is rejected with E_UNSUPPORTED (no dequantized-row fallback).
+ *   tau: outlier threshold, tau >= 0 (+inf: no outliers; 0: every
+ *        dimension is an outlier and Y is the fp16 matmul)
+ *   Y:   fp16 [T,N] (written)
+ *   workspace: device buffer of at least the size query's bytes; its
+ *        contents on entry are ignored and on return are unspecified.
+ * Errors: E_NULL, E_SHAPE, E_TAU, E_ALIGN, E_WORKSPACE, E_UNSUPPORTED, E_HIP. */
+int int8_mixed_matmul(const void* X, int64_t T, int64_t K, const int8_t* Wq, const float* sw,
+                      const void* W16, int64_t N, float tau, void* Y, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* int8_mixed_matmul that also writes its intermediates (for bit-exact
+ * checking).  Each output may be NULL to skip it:
+ *   count: int32 [1]   number of outlier dimensions o
+ *   idx:   int32 [K]   outlier dimensions, ascending, in idx[0..o)
+ *   xq:    int8  [T,K] quantized activations (outlier columns 0)
+ *   sx:    fp32  [T]   row scales
+ *   acc:   int32 [T,N] int8 matmul accumulators before dequantization
+ * It runs the same kernels as int8_mixed_matmul for T > 16 (for smaller T
+ * the plain call takes the single-kernel decode path instead).
+ * Errors: as int8_mixed_matmul. */
+int int8_mixed_matmul_debug(const void* X, int64_t T, int64_t K, const int8_t* Wq,
+                            const float* sw, const void* W16, int64_t N, float tau, void* Y,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            int32_t* count, int32_t* idx, int8_t* xq, float* sx, int32_t* acc);
+
+/* Steps 1-2 on the activation side only: finds the outlier dimensions,
+ * quantizes X row-wise and gathers the outlier columns of X, all into the
+ * workspace.  Lets several weights that share one X (e.g. the query, key
+ * and value projections) reuse one pass, and lets a profiler time the
+ * matmul by itself.  Arguments as int8_mixed_matmul; N is only used for
+ * the workspace size check.
+ * Errors: E_NULL, E_SHAPE, E_TAU, E_ALIGN, E_WORKSPACE, E_HIP. */
+int int8mm_quantize_activations(const void* X, int64_t T, int64_t K, int64_t N, float tau,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Steps 3-4 on a workspace filled by int8mm_quantize_activations with the
+ * same T and K (the workspace is read only here and may be reused for any
+ * number of weights).  X is read only through the gathered copy in the
+ * workspace.  Arguments as int8_mixed_matmul.
+ * Errors: E_NULL, E_SHAPE, E_ALIGN, E_WORKSPACE, E_UNSUPPORTED, E_HIP. */
+int int8mm_matmul_prepared(const void* workspace, size_t workspace_bytes, int64_t T, int64_t K,
+                           const int8_t* Wq, const float* sw, const void* W16, int64_t N,
+                           void* Y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INT8MM_H */

@@ -1,0 +1,195 @@
+"""LLM.int8() mixed-precision matmul for AMD MI355X (gfx950).
+
+Thin ctypes binding over ``libint8mm.so`` (C ABI in ``include/int8mm.h``).
+Every step of the computation runs in the library's HIP kernels; this module
+only checks tensor metadata, allocates outputs/workspace with torch and passes
+device pointers and the current HIP stream.  There is no CPU fallback: if the
+library is missing, importing the binding raises.
+
+The method (LLM.int8() abstract, taxoreview.com page dblp:280/8696, second
+paragraph; "LLM.int8(): A Procedure for Int8 Matrix Multiplication in
+Transformer Language Models", section "The LLM.int8() Methodology"):
+outlier hidden dimensions of X (|x| >= tau in some row) go through a 16-bit
+matmul, the rest through an Int8 matmul with one absmax scale per row of X
+and per column of W.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+# torch first: it carries the HIP runtime this process uses, and the library
+# must bind to that same runtime (same soname) rather than load a second one.
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libint8mm.so")
+
+OK, E_NULL, E_SHAPE, E_TAU, E_ALIGN, E_WORKSPACE, E_UNSUPPORTED, E_HIP = range(8)
+MAX_K = 133136
+
+EXPORTS = [
+    "int8mm_status_string",
+    "int8_mixed_matmul_workspace_size",
+    "int8_quantize_weight",
+    "int8_mixed_matmul",
+    "int8_mixed_matmul_debug",
+    "int8mm_quantize_activations",
+    "int8mm_matmul_prepared",
+]
+
+
+class Int8mmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run int8_mixed_precision_amd/build.py "
+                          "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, vp, f32, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
+    c_int = ctypes.c_int
+    lib.int8mm_status_string.argtypes = [c_int]
+    lib.int8mm_status_string.restype = ctypes.c_char_p
+    lib.int8_mixed_matmul_workspace_size.argtypes = [i64, i64, i64, ctypes.POINTER(sz)]
+    lib.int8_quantize_weight.argtypes = [vp, i64, i64, vp, vp, vp]
+    lib.int8_mixed_matmul.argtypes = [vp, i64, i64, vp, vp, vp, i64, f32, vp, vp, sz, vp]
+    lib.int8_mixed_matmul_debug.argtypes = [vp, i64, i64, vp, vp, vp, i64, f32, vp, vp, sz, vp,
+                                            vp, vp, vp, vp, vp]
+    lib.int8mm_quantize_activations.argtypes = [vp, i64, i64, i64, f32, vp, sz, vp]
+    lib.int8mm_matmul_prepared.argtypes = [vp, sz, i64, i64, vp, vp, vp, i64, vp, vp]
+    for name in EXPORTS[1:]:
+        getattr(lib, name).restype = c_int
+    return lib
+
+
+_lib = _load()
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (for tests that call the ABI directly)."""
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return _lib.int8mm_status_string(status).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != OK:
+        raise Int8mmError(status, where)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t: torch.Tensor, dtype, ndim: int, name: str) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
+    if t.dtype != dtype or t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ndim}-d {dtype} tensor, "
+                         f"got {t.dtype} {tuple(t.shape)}")
+
+
+def workspace_size(T: int, K: int, N: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(_lib.int8_mixed_matmul_workspace_size(T, K, N, ctypes.byref(out)),
+           "int8_mixed_matmul_workspace_size")
+    return out.value
+
+
+def new_workspace(T: int, K: int, N: int, device=None) -> torch.Tensor:
+    return torch.empty(workspace_size(T, K, N), dtype=torch.uint8, device=device or "cuda")
+
+
+def quantize_weight(W16: torch.Tensor, out: tuple | None = None):
+    """W16 fp16 [K,N] -> (Wq int8 [N,K], sw fp32 [N])."""
+    _need(W16, torch.float16, 2, "W16")
+    K, N = W16.shape
+    if out is None:
+        Wq = torch.empty((N, K), dtype=torch.int8, device=W16.device)
+        sw = torch.empty(N, dtype=torch.float32, device=W16.device)
+    else:
+        Wq, sw = out
+    _check(_lib.int8_quantize_weight(_ptr(W16), K, N, _ptr(Wq), _ptr(sw), _stream()),
+           "int8_quantize_weight")
+    return Wq, sw
+
+
+def _mm_args(X, Wq, sw, W16):
+    _need(X, torch.float16, 2, "X")
+    _need(Wq, torch.int8, 2, "Wq")
+    _need(sw, torch.float32, 1, "sw")
+    T, K = X.shape
+    N = Wq.shape[0]
+    if Wq.shape[1] != K or sw.shape[0] != N:
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, Wq {tuple(Wq.shape)}, "
+                         f"sw {tuple(sw.shape)}")
+    if W16 is not None:
+        _need(W16, torch.float16, 2, "W16")
+        if tuple(W16.shape) != (K, N):
+            raise ValueError(f"W16 must be [{K},{N}], got {tuple(W16.shape)}")
+    return T, K, N
+
+
+def mixed_matmul(X, Wq, sw, W16, tau: float, workspace=None, out=None) -> torch.Tensor:
+    """Y fp16 [T,N] = LLM.int8()(X, W, tau)."""
+    T, K, N = _mm_args(X, Wq, sw, W16)
+    if workspace is None:
+        workspace = new_workspace(T, K, N, X.device)
+    Y = out if out is not None else torch.empty((T, N), dtype=torch.float16, device=X.device)
+    _check(_lib.int8_mixed_matmul(_ptr(X), T, K, _ptr(Wq), _ptr(sw), _ptr(W16), N, float(tau),
+                                  _ptr(Y), _ptr(workspace), workspace.numel(), _stream()),
+           "int8_mixed_matmul")
+    return Y
+
+
+def mixed_matmul_debug(X, Wq, sw, W16, tau: float, workspace=None) -> dict:
+    """Y plus the intermediates count, idx, xq, sx and acc (see the header)."""
+    T, K, N = _mm_args(X, Wq, sw, W16)
+    dev = X.device
+    if workspace is None:
+        workspace = new_workspace(T, K, N, dev)
+    r = {"Y": torch.empty((T, N), dtype=torch.float16, device=dev),
+         "count": torch.zeros(4, dtype=torch.int32, device=dev),
+         "idx": torch.zeros(K, dtype=torch.int32, device=dev),
+         "xq": torch.empty((T, K), dtype=torch.int8, device=dev),
+         "sx": torch.empty(T, dtype=torch.float32, device=dev),
+         "acc": torch.empty((T, N), dtype=torch.int32, device=dev)}
+    _check(_lib.int8_mixed_matmul_debug(_ptr(X), T, K, _ptr(Wq), _ptr(sw), _ptr(W16), N,
+                                        float(tau), _ptr(r["Y"]), _ptr(workspace),
+                                        workspace.numel(), _stream(), _ptr(r["count"]),
+                                        _ptr(r["idx"]), _ptr(r["xq"]), _ptr(r["sx"]),
+                                        _ptr(r["acc"])),
+           "int8_mixed_matmul_debug")
+    return r
+
+
+def quantize_activations(X, N: int, tau: float, workspace) -> None:
+    """Activation-side steps into `workspace` (see int8mm_quantize_activations)."""
+    _need(X, torch.float16, 2, "X")
+    T, K = X.shape
+    _check(_lib.int8mm_quantize_activations(_ptr(X), T, K, N, float(tau), _ptr(workspace),
+                                            workspace.numel(), _stream()),
+           "int8mm_quantize_activations")
+
+
+def matmul_prepared(workspace, T: int, K: int, Wq, sw, W16, out=None) -> torch.Tensor:
+    """Matmul steps on a prepared workspace (see int8mm_matmul_prepared)."""
+    _need(Wq, torch.int8, 2, "Wq")
+    N = Wq.shape[0]
+    Y = out if out is not None else torch.empty((T, N), dtype=torch.float16, device=Wq.device)
+    _check(_lib.int8mm_matmul_prepared(_ptr(workspace), workspace.numel(), T, K, _ptr(Wq),
+                                       _ptr(sw), _ptr(W16), N, _ptr(Y), _stream()),
+           "int8mm_matmul_prepared")
+    return Y

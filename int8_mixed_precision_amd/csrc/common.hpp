@@ -1,0 +1,72 @@
+// Internal declarations shared by the HIP translation units of libint8mm.
+// Not part of the public ABI (that is include/int8mm.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace i8mm {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+// Device workspace of one activation pass.  All regions are 256-byte aligned.
+//   flags   u32 [kw]     bit k%32 of word k/32 set when dimension k is an outlier
+//   wprefix i32 [kw]     number of outlier dimensions before word w
+//   count   i32 [4]      count[0] = o, count[1] = o rounded up to 16
+//   idx     i32 [K]      outlier dimensions, ascending
+//   sx      f32 [T]      row scales
+//   xq      i8  [T,K]    quantized activations, outlier columns 0
+//   xo      f16 [T,opad] outlier columns of X, row stride count[1], zero padded
+struct Workspace {
+    uint32_t* flags;
+    int32_t* wprefix;
+    int32_t* count;
+    int32_t* idx;
+    float* sx;
+    int8_t* xq;
+    _Float16* xo;
+    size_t bytes;   // total bytes the layout needs
+};
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Layout of the workspace for (T, K) at `base` (base may be NULL to size it).
+Workspace carve_workspace(void* base, int64_t T, int64_t K);
+
+// ---- activation side (k_activation.hip)
+hipError_t launch_activation_pass(const _Float16* X, int64_t T, int64_t K, float tau,
+                                  const Workspace& ws, hipStream_t stream);
+
+// ---- weight side (k_weight.hip)
+hipError_t launch_quantize_weight(const _Float16* W, int64_t K, int64_t N, int8_t* Wq, float* sw,
+                                  hipStream_t stream);
+
+// ---- int8 GEMM + dequantization + 16-bit outlier GEMM (k_gemm.hip)
+struct GemmArgs {
+    const int8_t* xq;      // [T,K]
+    const float* sx;       // [T]
+    const int8_t* wq;      // [N,K]
+    const float* sw;       // [N]
+    const _Float16* xo;    // [T,opad]
+    const int32_t* idx;    // [K]
+    const int32_t* count;  // [2]
+    const _Float16* w16;   // [K,N]
+    _Float16* y;           // [T,N]
+    int32_t* acc_out;      // [T,N] or NULL
+    int64_t T, K, N;
+};
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
+
+// ---- debug copies (k_activation.hip)
+hipError_t launch_debug_copies(const Workspace& ws, int64_t T, int64_t K, int32_t* count,
+                               int32_t* idx, int8_t* xq, float* sx, hipStream_t stream);
+
+}  // namespace i8mm

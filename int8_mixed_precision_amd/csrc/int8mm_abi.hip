@@ -1,0 +1,152 @@
+// C ABI of libint8mm (declared in include/int8mm.h): host-side argument
+// validation, workspace layout and the launch sequence of each entry point.
+// No entry point allocates, frees or synchronizes.
+#include <math.h>
+
+#include "../../include/int8mm.h"
+#include "common.hpp"
+
+using namespace i8mm;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_shape(int64_t T, int64_t K, int64_t N) {
+    if (T < 1 || K < 1 || N < 1) return INT8MM_E_SHAPE;
+    if (K % 16 != 0 || N % 8 != 0 || K > INT8MM_MAX_K) return INT8MM_E_SHAPE;
+    // launch limits: one workgroup of 256 lanes per row in the quantize pass
+    // and per 128x128 output tile in the matmul keep every grid below 2^32
+    // work-items
+    if (T > INT8MM_MAX_T || (double)T * (double)N > INT8MM_MAX_TN) return INT8MM_E_SHAPE;
+    return INT8MM_OK;
+}
+
+int check_tau(float tau) {
+    if (isnan(tau) || tau < 0.0f) return INT8MM_E_TAU;
+    return INT8MM_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? INT8MM_OK : INT8MM_E_HIP; }
+
+// Validation shared by int8_mixed_matmul and its debug variant.
+int check_matmul(const void* X, int64_t T, int64_t K, const int8_t* Wq, const float* sw,
+                 const void* W16, int64_t N, float tau, void* Y, void* workspace,
+                 size_t workspace_bytes) {
+    if (!X || !Wq || !sw || !Y || !workspace) return INT8MM_E_NULL;
+    int st = check_shape(T, K, N);
+    if (st) return st;
+    st = check_tau(tau);
+    if (st) return st;
+    if (!aligned16(X) || !aligned16(Wq) || !aligned16(sw) || !aligned16(Y) ||
+        !aligned16(workspace) || (W16 && !aligned16(W16)))
+        return INT8MM_E_ALIGN;
+    if (workspace_bytes < carve_workspace(nullptr, T, K).bytes) return INT8MM_E_WORKSPACE;
+    if (!W16) return INT8MM_E_UNSUPPORTED;
+    return INT8MM_OK;
+}
+
+int run_matmul(const void* X, int64_t T, int64_t K, const int8_t* Wq, const float* sw,
+               const void* W16, int64_t N, float tau, void* Y, void* workspace,
+               hipStream_t stream, int32_t* acc_out) {
+    Workspace ws = carve_workspace(workspace, T, K);
+    hipError_t e = launch_activation_pass(static_cast<const _Float16*>(X), T, K, tau, ws, stream);
+    if (e != hipSuccess) return INT8MM_E_HIP;
+    GemmArgs g{ws.xq, ws.sx, Wq, sw, ws.xo, ws.idx, ws.count,
+               static_cast<const _Float16*>(W16), static_cast<_Float16*>(Y), acc_out, T, K, N};
+    return hip_status(launch_gemm(g, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* int8mm_status_string(int status) {
+    switch (status) {
+        case INT8MM_OK: return "ok";
+        case INT8MM_E_NULL: return "a required pointer is NULL";
+        case INT8MM_E_SHAPE: return "shape outside the supported limits";
+        case INT8MM_E_TAU: return "tau is NaN or negative";
+        case INT8MM_E_ALIGN: return "a pointer is not 16-byte aligned";
+        case INT8MM_E_WORKSPACE: return "workspace too small";
+        case INT8MM_E_UNSUPPORTED: return "unsupported request";
+        case INT8MM_E_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int int8_mixed_matmul_workspace_size(int64_t T, int64_t K, int64_t N, size_t* bytes) {
+    if (!bytes) return INT8MM_E_NULL;
+    int st = check_shape(T, K, N);
+    if (st) return st;
+    *bytes = carve_workspace(nullptr, T, K).bytes;
+    return INT8MM_OK;
+}
+
+int int8_quantize_weight(const void* W16, int64_t K, int64_t N, int8_t* Wq, float* sw,
+                         void* stream) {
+    if (!W16 || !Wq || !sw) return INT8MM_E_NULL;
+    int st = check_shape(1, K, N);
+    if (st) return st;
+    if (!aligned16(W16) || !aligned16(Wq) || !aligned16(sw)) return INT8MM_E_ALIGN;
+    return hip_status(launch_quantize_weight(static_cast<const _Float16*>(W16), K, N, Wq, sw,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int int8_mixed_matmul(const void* X, int64_t T, int64_t K, const int8_t* Wq, const float* sw,
+                      const void* W16, int64_t N, float tau, void* Y, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    int st = check_matmul(X, T, K, Wq, sw, W16, N, tau, Y, workspace, workspace_bytes);
+    if (st) return st;
+    return run_matmul(X, T, K, Wq, sw, W16, N, tau, Y, workspace,
+                      static_cast<hipStream_t>(stream), nullptr);
+}
+
+int int8_mixed_matmul_debug(const void* X, int64_t T, int64_t K, const int8_t* Wq,
+                            const float* sw, const void* W16, int64_t N, float tau, void* Y,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            int32_t* count, int32_t* idx, int8_t* xq, float* sx, int32_t* acc) {
+    int st = check_matmul(X, T, K, Wq, sw, W16, N, tau, Y, workspace, workspace_bytes);
+    if (st) return st;
+    if ((count && !aligned16(count)) || (idx && !aligned16(idx)) || (xq && !aligned16(xq)) ||
+        (sx && !aligned16(sx)) || (acc && !aligned16(acc)))
+        return INT8MM_E_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = run_matmul(X, T, K, Wq, sw, W16, N, tau, Y, workspace, s, acc);
+    if (st) return st;
+    Workspace ws = carve_workspace(workspace, T, K);
+    return hip_status(launch_debug_copies(ws, T, K, count, idx, xq, sx, s));
+}
+
+int int8mm_quantize_activations(const void* X, int64_t T, int64_t K, int64_t N, float tau,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    if (!X || !workspace) return INT8MM_E_NULL;
+    int st = check_shape(T, K, N);
+    if (st) return st;
+    st = check_tau(tau);
+    if (st) return st;
+    if (!aligned16(X) || !aligned16(workspace)) return INT8MM_E_ALIGN;
+    Workspace ws = carve_workspace(workspace, T, K);
+    if (workspace_bytes < ws.bytes) return INT8MM_E_WORKSPACE;
+    return hip_status(launch_activation_pass(static_cast<const _Float16*>(X), T, K, tau, ws,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int int8mm_matmul_prepared(const void* workspace, size_t workspace_bytes, int64_t T, int64_t K,
+                           const int8_t* Wq, const float* sw, const void* W16, int64_t N,
+                           void* Y, void* stream) {
+    if (!workspace || !Wq || !sw || !Y) return INT8MM_E_NULL;
+    int st = check_shape(T, K, N);
+    if (st) return st;
+    if (!aligned16(workspace) || !aligned16(Wq) || !aligned16(sw) || !aligned16(Y) ||
+        (W16 && !aligned16(W16)))
+        return INT8MM_E_ALIGN;
+    Workspace ws = carve_workspace(const_cast<void*>(workspace), T, K);
+    if (workspace_bytes < ws.bytes) return INT8MM_E_WORKSPACE;
+    if (!W16) return INT8MM_E_UNSUPPORTED;
+    GemmArgs g{ws.xq, ws.sx, Wq, sw, ws.xo, ws.idx, ws.count,
+               static_cast<const _Float16*>(W16), static_cast<_Float16*>(Y), nullptr, T, K, N};
+    return hip_status(launch_gemm(g, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

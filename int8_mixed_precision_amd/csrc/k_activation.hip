@@ -1,0 +1,259 @@
+// Activation side of LLM.int8(): outlier-dimension detection, isolation
+// (compaction of the outlier indices) and vector-wise (row-wise) int8
+// quantization of the remaining activations.
+//
+// Method: LLM.int8() abstract (taxoreview.com page dblp:280/8696, second
+// paragraph) - outlier feature dimensions are isolated and everything else is
+// quantized with one normalization constant per inner product, i.e. per row
+// of X; "LLM.int8(): A Procedure for Int8 Matrix Multiplication in
+// Transformer Language Models" (summarizepaper.com), bullet summary -
+// outliers are picked by magnitude.
+//
+// Readings of the pages: k is an outlier when |X[t,k]| >= tau in some row;
+// the row scale is the absmax over non-outlier columns;
+// q = clamp(rint(x * fp32(127 / s)), -127, 127) with an IEEE fp32 divide.
+//
+// All three kernels stream X with 16-byte loads (8 halves per lane) and are
+// bound by HBM bandwidth; the X re-read of the quantize pass is served from
+// cache for the row a workgroup is working on.
+#include "common.hpp"
+
+namespace i8mm {
+
+namespace {
+
+constexpr int kDetectThreads = 256;
+constexpr int kDetectCols = kDetectThreads * 8;   // columns per workgroup
+constexpr int kDetectRows = 16;                    // rows per workgroup
+constexpr int kCompactThreads = 1024;
+constexpr int kQuantThreads = 256;
+
+__device__ inline float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+
+// Zeroes the outlier bitmap and the count before a detection pass.
+__global__ void k_clear(uint32_t* __restrict__ flags, int64_t kw, int32_t* __restrict__ count) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < kw) flags[i] = 0u;
+    if (i < 4) count[i] = 0;
+}
+
+// flags[k/32] bit k%32 |= (|X[t,k]| >= tau) over the workgroup's rows.
+// Each lane owns 8 consecutive columns; 4 lanes form one 32-bit word, which
+// is merged with one atomicOr only when some bit is set.
+__global__ __launch_bounds__(kDetectThreads) void k_detect(const uint16_t* __restrict__ X,
+                                                           int64_t T, int64_t K, float tau,
+                                                           uint32_t* __restrict__ flags) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t c0 = ((int64_t)blockIdx.x * kDetectThreads + threadIdx.x) * 8;
+    uint32_t m = 0;
+    // grid-stride over chunks of kDetectRows rows (grid.y is capped at 65535)
+    for (int64_t r0 = (int64_t)blockIdx.y * kDetectRows; c0 < K && r0 < T;
+         r0 += (int64_t)gridDim.y * kDetectRows) {
+        const int64_t r1 = r0 + kDetectRows < T ? r0 + kDetectRows : T;
+        const uint16_t* p = X + r0 * K + c0;
+        int64_t r = r0;
+        for (; r + 4 <= r1; r += 4, p += 4 * K) {
+            uint4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const uint4*>(p + u * K);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float x = h2f((uint16_t)(w[e >> 1] >> ((e & 1) * 16)));
+                    m |= (__builtin_fabsf(x) >= tau ? 1u : 0u) << e;
+                }
+            }
+        }
+        for (; r < r1; ++r, p += K) {
+            uint4 v = *reinterpret_cast<const uint4*>(p);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float x = h2f((uint16_t)(w[e >> 1] >> ((e & 1) * 16)));
+                m |= (__builtin_fabsf(x) >= tau ? 1u : 0u) << e;
+            }
+        }
+    }
+    uint32_t word = m << ((lane & 3) * 8);
+    word |= __shfl_xor(word, 1);
+    word |= __shfl_xor(word, 2);
+    if ((lane & 3) == 0 && word != 0u && c0 < K) atomicOr(&flags[c0 >> 5], word);
+}
+
+// Isolation of the outlier dimensions: one workgroup turns the bitmap into
+// the ascending index list idx[0..o), per-word prefix counts and o.
+// Popcounts are scanned across the workgroup (wave prefix by shuffles, wave
+// totals through LDS).
+__global__ __launch_bounds__(kCompactThreads) void k_compact(const uint32_t* __restrict__ flags,
+                                                             int64_t kw,
+                                                             int32_t* __restrict__ wprefix,
+                                                             int32_t* __restrict__ idx,
+                                                             int32_t* __restrict__ count) {
+    __shared__ int wave_tot[kCompactThreads / kWave];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wv = tid / kWave;
+    const int64_t per = (kw + kCompactThreads - 1) / kCompactThreads;
+    const int64_t w0 = tid * per;
+    const int64_t w1 = w0 + per < kw ? w0 + per : kw;
+    int local = 0;
+    for (int64_t w = w0; w < w1; ++w) local += __builtin_popcount(flags[w]);
+    // inclusive scan inside the wave
+    int incl = local;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        int v = __shfl_up(incl, d);
+        if (lane >= d) incl += v;
+    }
+    if (lane == kWave - 1) wave_tot[wv] = incl;
+    __syncthreads();
+    int before = 0;
+    for (int i = 0; i < wv; ++i) before += wave_tot[i];
+    int run = before + incl - local;   // exclusive prefix of this thread
+    for (int64_t w = w0; w < w1; ++w) {
+        wprefix[w] = run;
+        uint32_t f = flags[w];
+        while (f) {
+            int b = __builtin_ctz(f);
+            idx[run++] = (int32_t)(w * 32 + b);
+            f &= f - 1u;
+        }
+    }
+    if (tid == kCompactThreads - 1) {
+        count[0] = run;
+        count[1] = (run + 15) & ~15;
+    }
+}
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, d));
+    return v;
+}
+
+__device__ inline int8_t quant(float x, float r) {
+    float q = __builtin_rintf(x * r);
+    q = __builtin_fminf(__builtin_fmaxf(q, -127.0f), 127.0f);
+    return (int8_t)(int)q;
+}
+
+// Row-wise quantization of one row t per workgroup, over the non-outlier
+// columns, plus the gather of the row's outlier values into xo.
+__global__ __launch_bounds__(kQuantThreads) void k_rowquant(
+    const uint16_t* __restrict__ X, int64_t K, const uint32_t* __restrict__ flags,
+    const int32_t* __restrict__ wprefix, const int32_t* __restrict__ count,
+    int8_t* __restrict__ xq, float* __restrict__ sx, _Float16* __restrict__ xo) {
+    __shared__ float red[kQuantThreads / kWave];
+    const int tid = threadIdx.x;
+    const int64_t t = blockIdx.x;
+    const uint16_t* row = X + t * K;
+    const int64_t nch = K / 8;
+    float mx = 0.0f;
+    for (int64_t c = tid; c < nch; c += kQuantThreads) {
+        uint4 v = *reinterpret_cast<const uint4*>(row + c * 8);
+        uint32_t fm = (flags[c >> 2] >> ((c & 3) * 8)) & 0xFFu;
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float a = __builtin_fabsf(h2f((uint16_t)(w[e >> 1] >> ((e & 1) * 16))));
+            mx = ((fm >> e) & 1u) ? mx : __builtin_fmaxf(mx, a);
+        }
+    }
+    mx = wave_max(mx);
+    if ((tid & (kWave - 1)) == 0) red[tid / kWave] = mx;
+    __syncthreads();
+    mx = red[0];
+#pragma unroll
+    for (int i = 1; i < kQuantThreads / kWave; ++i) mx = __builtin_fmaxf(mx, red[i]);
+    const float r = mx > 0.0f ? 127.0f / mx : 0.0f;
+    const int64_t opad = count[1];
+    const int64_t o = count[0];
+    _Float16* xo_row = xo + t * opad;
+    for (int64_t c = tid; c < nch; c += kQuantThreads) {
+        uint4 v = *reinterpret_cast<const uint4*>(row + c * 8);
+        const uint32_t word = flags[c >> 2];
+        uint32_t fm = (word >> ((c & 3) * 8)) & 0xFFu;
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            uint16_t hb = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
+            float x = h2f(hb);
+            uint32_t q = ((fm >> e) & 1u) ? 0u : (uint32_t)(uint8_t)quant(x, r);
+            packed[e >> 2] |= q << ((e & 3) * 8);
+        }
+        *reinterpret_cast<uint2*>(xq + t * K + c * 8) = make_uint2(packed[0], packed[1]);
+        if (fm) {
+            const int base_bit = (int)(c & 3) * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if ((fm >> e) & 1u) {
+                    int bit = base_bit + e;
+                    int pos = wprefix[c >> 2] + __builtin_popcount(word & ((1u << bit) - 1u));
+                    xo_row[pos] = __builtin_bit_cast(_Float16, (uint16_t)(w[e >> 1] >> ((e & 1) * 16)));
+                }
+            }
+        }
+    }
+    for (int64_t j = o + tid; j < opad; j += kQuantThreads) xo_row[j] = (_Float16)0.0f;
+    if (tid == 0) sx[t] = mx;
+}
+
+}  // namespace
+
+hipError_t launch_activation_pass(const _Float16* X, int64_t T, int64_t K, float tau,
+                                  const Workspace& ws, hipStream_t stream) {
+    const int64_t kw = ceil_div(K, 32);
+    const uint16_t* xb = reinterpret_cast<const uint16_t*>(X);
+    int clear_blocks = (int)ceil_div(kw > 4 ? kw : 4, 256);
+    hipLaunchKernelGGL(k_clear, dim3(clear_blocks), dim3(256), 0, stream, ws.flags, kw, ws.count);
+    const int64_t row_chunks = ceil_div(T, kDetectRows);
+    dim3 dgrid((unsigned)ceil_div(K, kDetectCols), (unsigned)(row_chunks < 65535 ? row_chunks : 65535));
+    hipLaunchKernelGGL(k_detect, dgrid, dim3(kDetectThreads), 0, stream, xb, T, K, tau, ws.flags);
+    hipLaunchKernelGGL(k_compact, dim3(1), dim3(kCompactThreads), 0, stream, ws.flags, kw,
+                       ws.wprefix, ws.idx, ws.count);
+    hipLaunchKernelGGL(k_rowquant, dim3((unsigned)T), dim3(kQuantThreads), 0, stream, xb, K,
+                       ws.flags, ws.wprefix, ws.count, ws.xq, ws.sx, ws.xo);
+    return hipGetLastError();
+}
+
+hipError_t launch_debug_copies(const Workspace& ws, int64_t T, int64_t K, int32_t* count,
+                               int32_t* idx, int8_t* xq, float* sx, hipStream_t stream) {
+    hipError_t e = hipSuccess;
+    if (count && e == hipSuccess)
+        e = hipMemcpyAsync(count, ws.count, sizeof(int32_t), hipMemcpyDeviceToDevice, stream);
+    if (idx && e == hipSuccess)
+        e = hipMemcpyAsync(idx, ws.idx, sizeof(int32_t) * (size_t)K, hipMemcpyDeviceToDevice,
+                           stream);
+    if (xq && e == hipSuccess)
+        e = hipMemcpyAsync(xq, ws.xq, (size_t)(T * K), hipMemcpyDeviceToDevice, stream);
+    if (sx && e == hipSuccess)
+        e = hipMemcpyAsync(sx, ws.sx, sizeof(float) * (size_t)T, hipMemcpyDeviceToDevice, stream);
+    return e;
+}
+
+Workspace carve_workspace(void* base, int64_t T, int64_t K) {
+    Workspace w{};
+    const int64_t kw = ceil_div(K, 32);
+    size_t off = 0;
+    char* b = static_cast<char*>(base);
+    auto take = [&](size_t n) {
+        char* p = b ? b + off : nullptr;
+        off += align256(n);
+        return p;
+    };
+    w.flags = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)kw));
+    w.wprefix = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)kw));
+    w.count = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * 4));
+    w.idx = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)K));
+    w.sx = reinterpret_cast<float*>(take(sizeof(float) * (size_t)T));
+    w.xq = reinterpret_cast<int8_t*>(take((size_t)T * (size_t)K));
+    // worst case: every dimension an outlier, o = K (K % 16 == 0, so opad <= K)
+    w.xo = reinterpret_cast<_Float16*>(take(sizeof(_Float16) * (size_t)T * (size_t)K));
+    w.bytes = off;
+    return w;
+}
+
+}  // namespace i8mm

@@ -1,0 +1,123 @@
+"""The C ABI on the CPU: the library loads, exports every function that
+include/int8mm.h declares, and validates arguments on the host before any
+HIP call (fake, never-dereferenced device addresses are enough for that)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "int8mm.h")
+
+
+@pytest.fixture(scope="module")
+def mm():
+    import int8_mixed_precision_amd as mm
+    return mm
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_lists_entry_points():
+    names = header_functions()
+    assert "int8_mixed_matmul" in names and "int8_quantize_weight" in names
+    assert len(names) == 7, names
+
+
+def test_exports_every_declared_symbol(mm):
+    lib = mm.lib()
+    for name in header_functions():
+        assert hasattr(lib, name), f"{name} not exported"
+    assert sorted(mm.EXPORTS) == header_functions()
+
+
+def test_status_strings(mm):
+    for s in range(8):
+        assert mm.status_string(s)
+    assert mm.status_string(99) == "unknown status"
+    assert mm.status_string(0) == "ok"
+
+
+def test_workspace_size(mm):
+    small = mm.workspace_size(16, 64, 48)
+    big = mm.workspace_size(2048, 12288, 49152)
+    # Xq (T*K bytes) plus the worst-case gathered outlier columns (2*T*K)
+    assert big >= 3 * 2048 * 12288 and big < 3 * 2048 * 12288 + (1 << 20)
+    assert 0 < small < big
+    assert mm.workspace_size(16, 64, 8) == small    # N does not change the size
+    with pytest.raises(mm.Int8mmError) as e:
+        mm.workspace_size(16, 60, 48)
+    assert e.value.status == mm.E_SHAPE
+
+
+FAKE = 1 << 40   # 16-byte aligned, never dereferenced by a validation failure
+
+
+def call_mm(lib, X=FAKE, T=16, K=64, Wq=FAKE, sw=FAKE, W16=FAKE, N=48, tau=6.0, Y=FAKE,
+            ws=FAKE, ws_bytes=1 << 30):
+    vp = ctypes.c_void_p
+    return lib.int8_mixed_matmul(vp(X) if X else None, T, K, vp(Wq) if Wq else None,
+                                 vp(sw) if sw else None, vp(W16) if W16 else None, N, tau,
+                                 vp(Y) if Y else None, vp(ws) if ws else None, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=0), 1), (dict(Wq=0), 1), (dict(sw=0), 1), (dict(Y=0), 1), (dict(ws=0), 1),
+    (dict(T=0), 2), (dict(K=0), 2), (dict(N=0), 2), (dict(T=-3), 2),
+    (dict(K=72), 2),                      # K % 16 != 0
+    (dict(N=44), 2),                      # N % 8 != 0
+    (dict(K=133136 + 16), 2),             # int32 accumulator bound
+    (dict(T=1 << 24), 2),                 # launch-grid bound
+    (dict(tau=float("nan")), 3), (dict(tau=-1.0), 3), (dict(tau=-1e-30), 3),
+    (dict(X=FAKE + 8), 4), (dict(Wq=FAKE + 1), 4), (dict(Y=FAKE + 2), 4), (dict(W16=FAKE + 4), 4),
+    (dict(ws_bytes=100), 5),
+    (dict(W16=0), 6),                     # memory-halved variant not built
+])
+def test_matmul_validation(mm, kw, status):
+    assert call_mm(mm.lib(), **kw) == status
+
+
+def test_largest_k_accepted_by_shape_check(mm):
+    assert mm.workspace_size(1, 133136, 8) > 0
+
+
+def test_tau_infinity_is_valid_input(mm):
+    # +inf passes validation: the failure reported here is the workspace size
+    assert call_mm(mm.lib(), tau=math.inf, ws_bytes=1) == mm.E_WORKSPACE
+    assert call_mm(mm.lib(), tau=0.0, ws_bytes=1) == mm.E_WORKSPACE
+
+
+def test_quantize_weight_validation(mm):
+    lib, vp = mm.lib(), ctypes.c_void_p
+    assert lib.int8_quantize_weight(None, 64, 48, vp(FAKE), vp(FAKE), None) == mm.E_NULL
+    assert lib.int8_quantize_weight(vp(FAKE), 60, 48, vp(FAKE), vp(FAKE), None) == mm.E_SHAPE
+    assert lib.int8_quantize_weight(vp(FAKE), 64, 47, vp(FAKE), vp(FAKE), None) == mm.E_SHAPE
+    assert lib.int8_quantize_weight(vp(FAKE), 64, 48, vp(FAKE + 3), vp(FAKE), None) == mm.E_ALIGN
+
+
+def test_staged_entry_points_validation(mm):
+    lib, vp = mm.lib(), ctypes.c_void_p
+    assert lib.int8mm_quantize_activations(None, 16, 64, 48, 6.0, vp(FAKE), 1 << 30, None) == 1
+    assert lib.int8mm_quantize_activations(vp(FAKE), 16, 64, 48, float("nan"), vp(FAKE),
+                                           1 << 30, None) == 3
+    assert lib.int8mm_quantize_activations(vp(FAKE), 16, 64, 48, 6.0, vp(FAKE), 10, None) == 5
+    assert lib.int8mm_matmul_prepared(vp(FAKE), 1 << 30, 16, 64, vp(FAKE), vp(FAKE), None, 48,
+                                      vp(FAKE), None) == mm.E_UNSUPPORTED
+    assert lib.int8mm_matmul_prepared(vp(FAKE), 10, 16, 64, vp(FAKE), vp(FAKE), vp(FAKE), 48,
+                                      vp(FAKE), None) == mm.E_WORKSPACE
+    assert lib.int8_mixed_matmul_debug(vp(FAKE), 16, 64, vp(FAKE), vp(FAKE), vp(FAKE), 48, 6.0,
+                                       vp(FAKE), vp(FAKE), 1 << 30, None, vp(FAKE + 4), None,
+                                       None, None, None) == mm.E_ALIGN
+
+
+def test_binding_rejects_cpu_tensors(mm):
+    import torch
+    X = torch.zeros(16, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        mm.quantize_weight(X)

@@ -1,0 +1,201 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bit-exact: the outlier count and index set, Xq, s_x, Wq, s_w and the int32
+accumulators.  fp16 output: max|dY| <= 1e-3 * max|Y_oracle| (the output
+tolerance of the method's statement; one fp16 ulp at the top binade is
+2^-10 < 1e-3 of max|Y|, so independent final roundings fit inside it).
+
+Small shapes are checked element by element everywhere; the full-size
+projection workloads are checked in full for every integer tensor the
+oracle can produce quickly (outlier set, Xq, s_x, Wq, s_w) and on sampled
+rows for acc and Y (the oracle's matmul is the slow part).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+Y_RTOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def mm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import int8_mixed_precision_amd as mm
+    return mm
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def gpu(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def check_y(y_gpu, y_ref, what):
+    yg = y_gpu.astype(np.float64)
+    yr = y_ref.astype(np.float64)
+    assert np.all(np.isfinite(yg)), f"{what}: non-finite output"
+    scale = np.abs(yr).max()
+    err = np.abs(yg - yr).max()
+    assert err <= Y_RTOL * scale, f"{what}: max|dY| = {err:.3e} > 1e-3 * {scale:.3e}"
+    return err / max(scale, 1e-30)
+
+
+def run_case(mm, name, X, W, tau, rows=None, plain_too=True):
+    T, K = X.shape
+    N = W.shape[1]
+    say(f"[case] {name}: T={T} K={K} N={N} tau={tau}")
+    Xd, Wd = gpu(X), gpu(W)
+    Wq, sw = mm.quantize_weight(Wd)
+    r = mm.mixed_matmul_debug(Xd, Wq, sw, Wd, tau)
+    Yp = mm.mixed_matmul(Xd, Wq, sw, Wd, tau) if plain_too else None
+    torch.cuda.synchronize()
+    say(f"[case] {name}: GPU done")
+
+    Wq_o, sw_o = oracle.quantize_weight(W)
+    assert np.array_equal(Wq.cpu().numpy(), Wq_o), f"{name}: Wq differs"
+    assert np.array_equal(sw.cpu().numpy(), sw_o), f"{name}: s_w differs"
+
+    flag = oracle.detect(X, tau)
+    idx_o = oracle.compact(flag)
+    o = int(r["count"][0].item())
+    assert o == len(idx_o), f"{name}: o = {o}, oracle {len(idx_o)}"
+    assert np.array_equal(r["idx"][:o].cpu().numpy(), idx_o), f"{name}: outlier set differs"
+    xq_o, sx_o = oracle.quantize_rows(X, flag)
+    assert np.array_equal(r["sx"].cpu().numpy(), sx_o), f"{name}: s_x differs"
+    assert np.array_equal(r["xq"].cpu().numpy(), xq_o), f"{name}: Xq differs"
+
+    sel = np.arange(T) if rows is None else np.asarray(rows)
+    ref = oracle.mixed_matmul(X, Wq_o, sw_o, W, tau, rows=None if rows is None else sel)
+    sel_t = torch.from_numpy(sel).cuda()
+    acc = r["acc"].index_select(0, sel_t).cpu().numpy()
+    assert np.array_equal(acc, ref["acc"]), f"{name}: acc differs in {np.sum(acc != ref['acc'])}"
+    Y = r["Y"].index_select(0, sel_t).cpu().numpy()
+    rel = check_y(Y, ref["Y"], name)
+    if Yp is not None:
+        Yp_s = Yp.index_select(0, sel_t).cpu().numpy()
+        if T > 16:
+            # same kernels as the debug entry point
+            assert np.array_equal(Yp_s.view(np.uint16), Y.view(np.uint16)), f"{name}: plain != debug"
+        else:
+            check_y(Yp_s, ref["Y"], name + " (plain)")
+    say(f"[case] {name}: ok, o={o}, rel err {rel:.2e}")
+    return r, ref
+
+
+def test_tiny_config(mm):
+    w = synth.WORKLOADS["tiny"]
+    X, W = synth.make_x(w), synth.make_w(w)
+    r, _ = run_case(mm, "tiny", X, W, w.tau)
+    assert r["idx"][:2].cpu().tolist() == [3, 17]
+
+
+@pytest.mark.parametrize("T,K,N,nd,dist", [
+    (1, 16, 8, 0, "normal"), (37, 80, 200, 2, "normal"), (129, 272, 136, 5, "laplace"),
+    (300, 1040, 520, 3, "normal"), (17, 4096, 264, 40, "normal"), (260, 528, 1032, 20, "laplace"),
+])
+def test_ragged_shapes(mm, T, K, N, nd, dist):
+    X, W = synth.random_case(10_000 + T + K + N, T, K, N, n_dims=nd, x_dist=dist)
+    run_case(mm, f"ragged {T}x{K}x{N}", X, W, 6.0)
+
+
+def test_tau_zero_every_dimension_outlier(mm):
+    X, W = synth.random_case(21, 70, 1024, 136)
+    r, ref = run_case(mm, "tau=0", X, W, 0.0)
+    assert int(r["count"][0]) == 1024 and not r["xq"].any()
+    # the result is the 16-bit matmul
+    y16 = (X.astype(np.float64) @ W.astype(np.float64)).astype(np.float16)
+    check_y(r["Y"].cpu().numpy(), y16, "tau=0 vs fp16 matmul")
+
+
+def test_tau_infinity_pure_int8(mm):
+    X, W = synth.random_case(22, 65, 320, 96, n_dims=4)
+    r, _ = run_case(mm, "tau=inf", X, W, float("inf"))
+    assert int(r["count"][0]) == 0
+
+
+def test_zero_rows_and_exact_tie(mm):
+    X, W = synth.random_case(23, 40, 128, 64)
+    X[5] = 0                      # zero row: s_x = 0, Xq row 0
+    X[7, :] = 0
+    X[7, 9] = 6.0                 # row whose only nonzero is an outlier at the tie
+    X[11, 33] = -6.0              # exact tie, negative
+    r, _ = run_case(mm, "zero rows + ties", X, W, 6.0)
+    idx = r["idx"][:int(r["count"][0])].cpu().tolist()
+    assert 9 in idx and 33 in idx
+    assert float(r["sx"][7]) == 0.0 and float(r["sx"][5]) == 0.0
+
+
+def test_largest_k(mm):
+    """K at the int32 bound with every quantized value at +-127: the largest
+    accumulator magnitude 127^2 * K must come out exactly."""
+    K = 133136
+    X = np.ones((3, K), np.float16)
+    X[1] = -1
+    W = np.full((K, 16), 0.125, np.float16)   # Y = +-K/8 stays finite in fp16
+    r, _ = run_case(mm, "largest K", X, W, 6.0)
+    acc = r["acc"].cpu().numpy()
+    assert acc[0, 0] == 127 * 127 * K and acc[1, 0] == -127 * 127 * K
+
+
+def test_staged_entry_points_match(mm):
+    X, W = synth.random_case(24, 96, 512, 264, n_dims=3)
+    W2 = synth.random_case(25, 1, 512, 136)[1]
+    say("[case] staged entry points")
+    Xd, Wd, W2d = gpu(X), gpu(W), gpu(W2)
+    Wq, sw = mm.quantize_weight(Wd)
+    Wq2, sw2 = mm.quantize_weight(W2d)
+    ws = mm.new_workspace(96, 512, 264)
+    mm.quantize_activations(Xd, 264, 6.0, ws)
+    Y1 = mm.matmul_prepared(ws, 96, 512, Wq, sw, Wd)
+    Y2 = mm.matmul_prepared(ws, 96, 512, Wq2, sw2, W2d)   # one pass of X, two weights
+    R1 = mm.mixed_matmul(Xd, Wq, sw, Wd, 6.0)
+    R2 = mm.mixed_matmul(Xd, Wq2, sw2, W2d, 6.0)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, R1) and torch.equal(Y2, R2)
+
+
+# ----------------------------------------------------------- full-size workloads
+
+def _sample_rows(T, rowsel, n=12, seed=0):
+    """Rows to check against the oracle: first, last, random, and rows that
+    carry planted outliers."""
+    rng = np.random.default_rng(seed)
+    rows = {0, T - 1, *rng.choice(T, n, replace=False).tolist()}
+    if rowsel is not None:
+        for j in range(min(3, len(rowsel))):
+            rows.add(int(np.flatnonzero(rowsel[j])[0]))
+    return sorted(rows)
+
+
+def test_decode_config(mm):
+    w = synth.WORKLOADS["dec"]
+    X, W = synth.make_x(w), synth.make_w(w)
+    r, _ = run_case(mm, "dec (full)", X, W, w.tau)
+    assert sorted(r["idx"][:int(r["count"][0])].cpu().tolist()) == sorted(synth.planted(w)[0].tolist())
+
+
+@pytest.mark.parametrize("name", ["up", "down"])
+def test_prefill_config(mm, name):
+    w = synth.WORKLOADS[name]
+    X, W = synth.make_x(w), synth.make_w(w)
+    dims, _, rowsel = synth.planted(w)
+    r, _ = run_case(mm, f"{name} (sampled rows)", X, W, w.tau,
+                    rows=_sample_rows(w.T, rowsel), plain_too=True)
+    idx = set(r["idx"][:int(r["count"][0])].cpu().tolist())
+    assert set(dims.tolist()) <= idx
+
+
+@pytest.mark.parametrize("name", ["sweep_qkv_256", "sweep_out_0"])
+def test_sweep_config(mm, name):
+    w = synth.WORKLOADS[name]
+    X, W = synth.make_x(w), synth.make_w(w)
+    r, _ = run_case(mm, f"{name} (sampled rows)", X, W, w.tau, rows=_sample_rows(w.T, None, n=8))
+    assert int(r["count"][0]) >= w.n_dims
