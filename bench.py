@@ -1,0 +1,295 @@
+"""Benchmark of the LLM.int8() mixed-precision matmul on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill|decode]
+                    [--no-cpu-baseline]
+
+A step is one full int8_mixed_matmul call (outlier detection, isolation,
+row-wise quantization, int8 MFMA matmul, dequantization and the 16-bit
+outlier matmul) on a weight converted to Int8 beforehand (the conversion runs
+once at load time and is timed separately).  Inputs are seeded synthetic
+tensors already resident in HBM.
+
+Headline (`value`): int8-mixed matmul TOPS = 2*T*K*N / t_step on the
+prefill 175B-class FFN up-projection, X fp16 [2048,12288] with 7 planted
+outlier dimensions, W fp16 [12288,49152], tau = 6.  Also reported: weight
+GB/s = (K*N + 4*N) / t_step on the decode FFN up-projection X [8,8192],
+W [8192,28672], with 8 rotating weight copies so that no call finds its
+weight in the 256 MB last-level cache.
+
+Per-kernel durations come from HIP events recorded on the stream the
+library launches on, inside the timed loop; the roofline objects divide
+the algorithmic work of one launch by that duration.  The CPU baseline is
+the test oracle (plain C, this machine's host cores) timed on a row sample of
+the prefill workload.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, published
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
+DECODE_ROTATE = 8
+CPU_THREADS = 16             # host-core share of one GPU on the box
+CPU_TARGET_S = 15.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--only", choices=["prefill", "decode"], default=None)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def src_digest(names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "int8_mixed_precision_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(profile_name: str, digest: str, launches_key: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the kernel source as it is now (else None)."""
+    path = os.path.join(ROOT, "profiles", profile_name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_src_sha") != digest:
+        return None
+    return d.get(launches_key)
+
+
+def timed_loop(torch, steps, warmup, body):
+    """Runs body(i, evs) warmup + steps times; returns the wall time of the
+    timed steps (synchronized on both sides) and the event lists."""
+    for i in range(warmup):
+        body(i, None)
+    torch.cuda.synchronize()
+    evs = []
+    t0 = time.perf_counter()
+    for i in range(steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        body(i, e)
+        evs.append(e)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, evs
+
+
+def bench_prefill(torch, mm, synth, steps, warmup):
+    w = synth.WORKLOADS["up"]
+    T, K, N = w.T, w.K, w.N
+    log(f"prefill: generating X [{T},{K}], W [{K},{N}]")
+    X = torch.from_numpy(synth.make_x(w, threads=CPU_THREADS)).cuda()
+    Wh = synth.make_w(w, threads=CPU_THREADS)
+    W16 = torch.from_numpy(Wh).cuda()
+    del Wh
+    Wq = torch.empty((N, K), dtype=torch.int8, device="cuda")
+    sw = torch.empty(N, dtype=torch.float32, device="cuda")
+    # weight conversion (once per weight), timed on its own
+    for _ in range(2):
+        mm.quantize_weight(W16, out=(Wq, sw))
+    torch.cuda.synchronize()
+    qa, qb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    qa.record()
+    for _ in range(5):
+        mm.quantize_weight(W16, out=(Wq, sw))
+    qb.record()
+    torch.cuda.synchronize()
+    q_ms = qa.elapsed_time(qb) / 5
+
+    ws = mm.new_workspace(T, K, N)
+    Y = torch.empty((T, N), dtype=torch.float16, device="cuda")
+
+    def step(i, e):
+        # int8_mixed_matmul == quantize_activations + matmul_prepared (same
+        # kernels, same stream); the split lets the events bracket the matmul
+        if e is not None:
+            e[0].record()
+        mm.quantize_activations(X, N, w.tau, ws)
+        if e is not None:
+            e[1].record()
+        mm.matmul_prepared(ws, T, K, Wq, sw, W16, out=Y)
+        if e is not None:
+            e[2].record()
+
+    log(f"prefill: {warmup} warmup + {steps} timed steps")
+    wall, evs = timed_loop(torch, steps, warmup, step)
+    act_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    gemm_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    # the outlier count of this X (one debug call, outside the timed loop)
+    dbg = mm.mixed_matmul_debug(X, Wq, sw, W16, w.tau)
+    o = int(dbg["count"][0])
+    del dbg
+    ops = 2.0 * T * K * N
+    ms_step = wall * 1e3 / steps
+    return {
+        "T": T, "K": K, "N": N, "tau": w.tau, "o": o, "ms_per_step": ms_step,
+        "tops": ops * steps / wall / 1e12,
+        "activation_ms": act_ms, "gemm_ms": gemm_ms,
+        "gemm_tops": ops / (gemm_ms * 1e-3) / 1e12,
+        "quantize_weight_ms": q_ms,
+        "quantize_weight_gbs": (2.0 * K * N + K * N + 4.0 * N) / (q_ms * 1e-3) / 1e9,
+    }
+
+
+def bench_decode(torch, mm, synth, steps, warmup):
+    w = synth.WORKLOADS["dec"]
+    T, K, N = w.T, w.K, w.N
+    log(f"decode: generating X [{T},{K}], W [{K},{N}], {DECODE_ROTATE} weight copies")
+    X = torch.from_numpy(synth.make_x(w, threads=CPU_THREADS)).cuda()
+    W16_0 = torch.from_numpy(synth.make_w(w, threads=CPU_THREADS)).cuda()
+    Wq0, sw0 = mm.quantize_weight(W16_0)
+    sets = [(Wq0, sw0, W16_0)]
+    for _ in range(DECODE_ROTATE - 1):
+        sets.append((Wq0.clone(), sw0.clone(), W16_0.clone()))
+    ws = mm.new_workspace(T, K, N)
+    Y = torch.empty((T, N), dtype=torch.float16, device="cuda")
+
+    def step(i, e):
+        Wq, sw, W16 = sets[i % DECODE_ROTATE]
+        if e is not None:
+            e[0].record()
+        mm.mixed_matmul(X, Wq, sw, W16, w.tau, workspace=ws, out=Y)
+        if e is not None:
+            e[1].record()
+            e[2].record()
+
+    log(f"decode: {warmup} warmup + {steps} timed steps")
+    wall, evs = timed_loop(torch, steps, warmup, step)
+    call_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    dbg = mm.mixed_matmul_debug(X, Wq0, sw0, W16_0, w.tau)
+    o = int(dbg["count"][0])
+    wbytes = K * N + 4.0 * N
+    alg_bytes = 2.0 * T * K + K * N + 4.0 * N + 2.0 * o * N + 2.0 * T * N
+    return {
+        "T": T, "K": K, "N": N, "tau": w.tau, "o": o, "ms_per_step": wall * 1e3 / steps,
+        "weight_gbs": wbytes * steps / wall / 1e9, "call_ms": call_ms,
+        "alg_bytes": alg_bytes, "alg_gbs": alg_bytes / (call_ms * 1e-3) / 1e9,
+    }
+
+
+def cpu_baseline(synth, T, K, N):
+    """The oracle, timed on the host cores, on a row sample of the prefill
+    workload (outlier detection over all rows, the rest on the sample)."""
+    import oracle
+    w = synth.WORKLOADS["up"]
+    X = synth.make_x(w, threads=CPU_THREADS)
+    W = synth.make_w(w, threads=CPU_THREADS)
+    Wq, sw = oracle.quantize_weight(W, threads=CPU_THREADS)
+    # size the sample from a 2-row probe so the timed run takes ~CPU_TARGET_S
+    t0 = time.perf_counter()
+    oracle.mixed_matmul(X, Wq, sw, W, w.tau, rows=np.arange(2), threads=CPU_THREADS)
+    probe = time.perf_counter() - t0
+    rows = int(max(CPU_THREADS, min(T, CPU_TARGET_S / max(probe / 2, 1e-6))))
+    rows -= rows % CPU_THREADS if rows > CPU_THREADS else 0
+    sample = np.linspace(0, T - 1, rows).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.mixed_matmul(X, Wq, sw, W, w.tau, rows=sample, threads=CPU_THREADS)
+    dt = time.perf_counter() - t0
+    return {
+        "value": 2.0 * rows * K * N / dt / 1e12, "unit": "TOPS", "cores": CPU_THREADS,
+        "kind": "oracle",
+        "sample": f"{rows} of {T} rows of the prefill up-projection (outlier detection over "
+                  f"all {T} rows), {dt:.1f} s; weight conversion untimed",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the multi-GPU sharding is a design note only)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import int8_mixed_precision_amd as mm
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    pre = dec = None
+    if args.only in (None, "prefill"):
+        pre = bench_prefill(torch, mm, synth, args.steps, args.warmup)
+        log(f"prefill: {pre['tops']:.1f} TOPS ({pre['ms_per_step']:.3f} ms/step), "
+            f"gemm {pre['gemm_ms']:.3f} ms, activation pass {pre['activation_ms']:.3f} ms")
+        torch.cuda.empty_cache()
+    if args.only in (None, "decode"):
+        dec = bench_decode(torch, mm, synth, args.steps, args.warmup)
+        log(f"decode: {dec['weight_gbs']:.1f} GB/s weight ({dec['call_ms'] * 1e3:.1f} us/call)")
+
+    gemm_digest = src_digest(["k_gemm.hip", "common.hpp"])
+    out = {
+        "metric": "int8-mixed matmul TOPS @ T=2048 K=12288 N=49152; weight GB/s @ T=8",
+        "higher_is_better": True, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "scaling": "weak", "vs_baseline": None, "dtype": "i8", "data": "synthetic",
+    }
+    if pre is not None:
+        ach = pre["gemm_tops"]
+        out.update({
+            "value": round(pre["tops"], 2), "unit": "TOPS",
+            "ms_per_step": round(pre["ms_per_step"], 4),
+            "config": {"workload": "prefill 175B-class FFN up-projection (LLM.int8() matmul, "
+                                   "W pre-converted to Int8)",
+                       "T": pre["T"], "K": pre["K"], "N": pre["N"], "tau": pre["tau"],
+                       "outlier_dims": pre["o"],
+                       "fraction_8bit": round((pre["K"] - pre["o"]) / pre["K"], 6)},
+            "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_INT8_TOPS,
+                         "unit": "TFLOP/s", "frac": round(ach / PEAK_INT8_TOPS, 4),
+                         "traffic": measured_traffic("gemm_i8_prefill_up_traffic.json",
+                                                     gemm_digest, "hbm_bytes_per_launch"),
+                         "kernel": "k_gemm_i8 (int8 MFMA + fused dequant/fp16 outlier epilogue)",
+                         "work": "2*T*K*N int8 ops per launch", "ms": round(pre["gemm_ms"], 4)},
+            "stages_ms": {"activation_pass": round(pre["activation_ms"], 4),
+                          "gemm": round(pre["gemm_ms"], 4)},
+            "quantize_weight": {"ms": round(pre["quantize_weight_ms"], 4),
+                                "GB/s": round(pre["quantize_weight_gbs"], 1),
+                                "bytes": "2KN read + KN + 4N written"},
+        })
+    if dec is not None:
+        d = {"metric": "weight GB/s @ T=8", "value": round(dec["weight_gbs"], 1), "unit": "GB/s",
+             "ms_per_step": round(dec["ms_per_step"], 5),
+             "config": {"workload": "decode FFN up-projection, W pre-converted to Int8, "
+                                    f"{DECODE_ROTATE} rotating weight copies",
+                        "T": dec["T"], "K": dec["K"], "N": dec["N"], "tau": dec["tau"],
+                        "outlier_dims": dec["o"]},
+             "roofline": {"bound": "hbm", "achieved": round(dec["alg_gbs"], 1),
+                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                          "frac": round(dec["alg_gbs"] / PEAK_HBM_GBS, 4),
+                          "traffic": None, "kernel": "whole int8_mixed_matmul call",
+                          "work": "2TK + KN + 4N + 2oN + 2TN bytes per call",
+                          "ms": round(dec["call_ms"], 5)}}
+        if pre is None:
+            out.update({"value": d["value"], "unit": "GB/s", "ms_per_step": d["ms_per_step"],
+                        "config": d["config"], "roofline": d["roofline"]})
+        else:
+            out["decode"] = d
+    if not args.no_cpu_baseline and pre is not None:
+        log("cpu baseline: oracle on a row sample")
+        out["cpu_baseline"] = cpu_baseline(synth, pre["T"], pre["K"], pre["N"])
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -49,6 +49,95 @@ __device__ inline int swz(int row, int c) {
     return c ^ ((row / RPW) & (CPR - 1));
 }
 
+// Epilogue shared by the matmul kernels, for one wave's TM x TN grid of
+// 32x32 accumulator tiles whose top-left output element is (mb, nb).
+// 32x32 accumulator layout: lane holds column (lane & 31) and, in register
+// r, row 8*(r/4) + 4*(lane/32) + (r%4) of the tile.
+template <int TM, int TN, bool WRITE_ACC>
+__device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a, int64_t mb,
+                                         int64_t nb, int lane) {
+    const int64_t T = a.T, N = a.N;
+    const int col_l = lane & 31;
+    const int row_l = (lane >> 5) * 4;
+    if (WRITE_ACC && a.acc_out) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int64_t n = nb + j * 32 + col_l;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t m = mb + i * 32 + (r >> 2) * 8 + row_l + (r & 3);
+                    if (m < T && n < N) a.acc_out[m * N + n] = acc[i][j][r];
+                }
+            }
+    }
+    // dequantization by the outer product of the scales (1/127^2 folded
+    // into the column scale)
+    float swn[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int64_t n = nb + j * 32 + col_l;
+        swn[j] = n < N ? a.sw[n] * (1.0f / 16129.0f) : 0.0f;
+    }
+    const int o = a.count[0];
+    const int opad = a.count[1];
+    // one 32-row strip of tiles at a time keeps the fp32 values of only TN
+    // tiles live next to the integer accumulators
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        v16f y[TN];
+        {
+            float sxm[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t m = mb + i * 32 + (r >> 2) * 8 + row_l + (r & 3);
+                sxm[r] = m < T ? a.sx[m] : 0.0f;
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) y[j][r] = (float)acc[i][j][r] * sxm[r] * swn[j];
+        }
+        // 16-bit matmul over the isolated outlier dimensions, 16 at a time,
+        // with the dequantized values as the fp32 C operand
+        for (int jc = 0; jc < opad; jc += 16) {
+            const int jl = jc + (lane >> 5) * 8;   // first of this lane's 8 outlier slots
+            const int64_t mrow = mb + i * 32 + (lane & 31);
+            const v8h xa = mrow < T ? *reinterpret_cast<const v8h*>(a.xo + mrow * opad + jl)
+                                    : v8h{0, 0, 0, 0, 0, 0, 0, 0};
+            int64_t rowoff[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) rowoff[e] = (jl + e < o) ? (int64_t)a.idx[jl + e] * N : -1;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int64_t n = nb + j * 32 + col_l;
+                v8h wb;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    wb[e] = (rowoff[e] >= 0 && n < N) ? a.w16[rowoff[e] + n] : (_Float16)0.0f;
+                y[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xa, wb, y[j], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int64_t n = nb + j * 32 + col_l;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t m = mb + i * 32 + (r >> 2) * 8 + row_l + (r & 3);
+                if (m < T && n < N) a.y[m * N + n] = (_Float16)y[j][r];
+            }
+        }
+    }
+}
+
+// XCD-aware renumbering: hardware deals workgroups round-robin over the 8
+// XCDs; give each XCD a contiguous range of logical tiles, M fastest, so the
+// M-tiles that share one weight panel run under the same L2.
+__device__ __forceinline__ int64_t xcd_tile(int64_t bid, int64_t nb) {
+    return (nb & 7) == 0 ? (bid & 7) * (nb >> 3) + (bid >> 3) : bid;
+}
+
 template <int BM, int BN, int BK, int WAVES_M, bool WRITE_ACC>
 __global__ __launch_bounds__(kThreads) void k_gemm_i8(GemmArgs a) {
     using C = Cfg<BM, BN, BK, WAVES_M>;
@@ -61,12 +150,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_i8(GemmArgs a) {
     const int64_t T = a.T, K = a.K, N = a.N;
     const int64_t MT = ceil_div(T, BM);
 
-    // XCD-aware renumbering: hardware deals workgroups round-robin over the
-    // 8 XCDs; give each XCD a contiguous range of logical tiles (M fastest),
-    // so the M-tiles that share one weight panel hit the same L2.
-    int64_t bid = blockIdx.x;
-    const int64_t nb = gridDim.x;
-    if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+    const int64_t bid = xcd_tile(blockIdx.x, gridDim.x);
     const int64_t m0 = (bid % MT) * BM;
     const int64_t n0 = (bid / MT) * BN;
 
@@ -146,85 +230,173 @@ __global__ __launch_bounds__(kThreads) void k_gemm_i8(GemmArgs a) {
         __syncthreads();
     }
 
-    // ---------------- epilogue
-    // 32x32 accumulator layout: lane holds column (lane & 31) and, in register
-    // r, row 8*(r/4) + 4*(lane/32) + (r%4) of the tile.
-    const int col_l = lane & 31;
-    const int row_l = (lane >> 5) * 4;
-    if (WRITE_ACC && a.acc_out) {
-#pragma unroll
-        for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-            for (int j = 0; j < C::TN; ++j) {
-                const int64_t n = n0 + wn0 + j * 32 + col_l;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int64_t m = m0 + wm0 + i * 32 + (r >> 2) * 8 + row_l + (r & 3);
-                    if (m < T && n < N) a.acc_out[m * N + n] = acc[i][j][r];
-                }
-            }
-    }
-    float swn[C::TN];
-#pragma unroll
-    for (int j = 0; j < C::TN; ++j) {
-        const int64_t n = n0 + wn0 + j * 32 + col_l;
-        swn[j] = n < N ? a.sw[n] * (1.0f / 16129.0f) : 0.0f;
-    }
-    v16f y[C::TM][C::TN];
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i) {
-        float sxm[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int64_t m = m0 + wm0 + i * 32 + (r >> 2) * 8 + row_l + (r & 3);
-            sxm[r] = m < T ? a.sx[m] : 0.0f;
-        }
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) y[i][j][r] = (float)acc[i][j][r] * sxm[r] * swn[j];
-    }
+    epilogue<C::TM, C::TN, WRITE_ACC>(acc, a, m0 + wm0, n0 + wn0, lane);
+}
 
-    // 16-bit matmul over the isolated outlier dimensions, 16 at a time.
-    const int o = a.count[0];
-    const int opad = a.count[1];
-    for (int jc = 0; jc < opad; jc += 16) {
-        const int jl = jc + (lane >> 5) * 8;   // first of this lane's 8 outlier slots
-        v8h xa[C::TM], wb[C::TN];
-#pragma unroll
-        for (int i = 0; i < C::TM; ++i) {
-            const int64_t m = m0 + wm0 + i * 32 + (lane & 31);
-            xa[i] = m < T ? *reinterpret_cast<const v8h*>(a.xo + m * opad + jl)
-                          : v8h{0, 0, 0, 0, 0, 0, 0, 0};
-        }
-        int64_t rowoff[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) rowoff[e] = (jl + e < o) ? (int64_t)a.idx[jl + e] * N : -1;
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j) {
-            const int64_t n = n0 + wn0 + j * 32 + col_l;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                wb[j][e] = (rowoff[e] >= 0 && n < N) ? a.w16[rowoff[e] + n] : (_Float16)0.0f;
-        }
-#pragma unroll
-        for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-            for (int j = 0; j < C::TN; ++j)
-                y[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xa[i], wb[j], y[i][j], 0, 0, 0);
-    }
+// 16-byte copy global -> LDS without VGPR staging (global_load_lds_dwordx4).
+// The wave's 64 lanes land contiguously at lds_dst + 16 * lane; lds_dst must
+// be wave-uniform.  Written as inline asm so that the compiler's wait-count
+// insertion, which cannot tell which LDS bytes such a copy writes, does not
+// add a full vmcnt(0) before every LDS read; the kernels below wait for the
+// copies themselves (s_waitcnt vmcnt + barrier) before reading the stage.
+// The instruction has no register result.  m0 carries the LDS address; no
+// other instruction in these kernels uses m0.
+__device__ __forceinline__ void copy_to_lds16(const void* gsrc, const void* lds_dst) {
+    const uint32_t la =
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)lds_dst;
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gsrc), "s"(la)
+                 : "memory");
+}
 
+// s_waitcnt immediate that waits until at most `n` vector-memory operations
+// are outstanding (expcnt and lgkmcnt left at their no-wait maxima).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0xF70; }
+// s_waitcnt immediate for lgkmcnt(0) only (vmcnt 63, expcnt 7 = no wait)
+constexpr int kLgkm0 = 0xC07F;
+
+// Large-tile kernel for prefill shapes: a 256x256 workgroup tile, each wave a
+// 128x128 grid of 4x4 MFMA tiles (256 int32 accumulators per lane), so every
+// 16-byte LDS fragment feeds four MFMAs.  Operands go from global memory
+// straight into LDS (global_load_lds_dwordx4: no VGPR staging, no LDS store
+// instructions) through a ring of STAGES buffers of 32 KB (BK = 64).  A wave
+// instruction fills 1 KB of LDS, lane l landing at byte 16*l, so the XOR
+// swizzle is applied by choosing which global chunk each lane fetches.
+//
+// Software pipeline per k-tile (two 32-deep sub-steps, fragments F0/F1):
+//   issue the global->LDS copy of tile kt+STAGES-1
+//   ds_read F1 (tile kt, second half)   interleaved with  16 MFMA on F0
+//   wait until tile kt+1 has landed, barrier
+//   ds_read F0 (tile kt+1, first half)  interleaved with  16 MFMA on F1
+// so LDS latency hides under MFMA work and there is one barrier per tile.
+// Requires K % 64 == 0; rows past T or N are clamped to the last valid row
+// (they only feed outputs that are never stored).
+template <int STAGES, bool WRITE_ACC>
+__global__ __launch_bounds__(kThreads) void k_gemm_i8_big(GemmArgs a) {
+    constexpr int BM = 256, BN = 256, BK = 64, TM = 4, TN = 4;
+    constexpr int STAGE_BYTES = (BM + BN) * BK;
+    constexpr int LOADS = (BM + BN) * BK / 16 / kThreads;   // 16-byte copies per lane per tile
+    __shared__ __attribute__((aligned(1024))) int8_t lds[STAGES * STAGE_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t T = a.T, K = a.K, N = a.N;
+    const int64_t MT = ceil_div(T, BM);
+    const int64_t bid = xcd_tile(blockIdx.x, gridDim.x);
+    const int64_t m0 = (bid % MT) * BM;
+    const int64_t n0 = (bid / MT) * BN;
+    const int wm0 = (wave & 1) * 128;
+    const int wn0 = (wave >> 1) * 128;
+
+    // copy assignment: wave w fills the 1 KB groups 4w..4w+3 of A and of B;
+    // in a group, lane l writes row 16g + l/4, physical chunk l%4.  Addresses
+    // are a per-workgroup scalar base plus a 32-bit lane offset (a 256-row
+    // panel spans at most 256 * 133136 bytes).
+    const int8_t* abase = a.xq + m0 * K;
+    const int8_t* bbase = a.wq + n0 * K;
+    uint32_t aoffg[4], boffg[4];
 #pragma unroll
-    for (int i = 0; i < C::TM; ++i)
+    for (int u = 0; u < 4; ++u) {
+        const int row = (wave * 4 + u) * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ ((row >> 1) & 3);
+        const int64_t ra = m0 + row < T ? row : T - 1 - m0;
+        const int64_t rb = n0 + row < N ? row : N - 1 - n0;
+        aoffg[u] = (uint32_t)(ra * K + c * 16);
+        boffg[u] = (uint32_t)(rb * K + c * 16);
+    }
+    auto issue = [&](int kt, int stage) {
+        int8_t* dst = lds + stage * STAGE_BYTES + wave * 4 * 1024;
+        const int8_t* ak = abase + (int64_t)kt * BK;
+        const int8_t* bk = bbase + (int64_t)kt * BK;
 #pragma unroll
-        for (int j = 0; j < C::TN; ++j) {
-            const int64_t n = n0 + wn0 + j * 32 + col_l;
+        for (int u = 0; u < 4; ++u) copy_to_lds16(ak + aoffg[u], dst + u * 1024);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t m = m0 + wm0 + i * 32 + (r >> 2) * 8 + row_l + (r & 3);
-                if (m < T && n < N) a.y[m * N + n] = (_Float16)y[i][j][r];
-            }
+        for (int u = 0; u < 4; ++u) copy_to_lds16(bk + boffg[u], dst + BM * BK + u * 1024);
+    };
+
+    v16i acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+
+    // fragment offsets inside a stage (identical for every stage)
+    int aoff[2][TM], boff[2][TN];
+#pragma unroll
+    for (int ss = 0; ss < 2; ++ss) {
+        const int c = ss * 2 + (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int row = wm0 + i * 32 + (lane & 31);
+            aoff[ss][i] = row * BK + ((c ^ ((row >> 1) & 3)) * 16);
         }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int row = wn0 + j * 32 + (lane & 31);
+            boff[ss][j] = BM * BK + row * BK + ((c ^ ((row >> 1) & 3)) * 16);
+        }
+    }
+    auto read_frags = [&](const int8_t* base, int ss, v4i (&af)[TM], v4i (&bf)[TN]) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const v4i*>(base + aoff[ss][i]);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bf[j] = *reinterpret_cast<const v4i*>(base + boff[ss][j]);
+    };
+    auto mfmas = [&](const v4i (&af)[TM], const v4i (&bf)[TN]) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+    };
+    // 8 fragment reads spread over 16 MFMAs
+    auto interleave = [&]() {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one DS read
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // two MFMA
+        }
+    };
+
+    // The ring always has STAGES-1 copies in flight: past the last tile the
+    // loop re-copies tile KT-1 into a buffer that is never read again, which
+    // keeps the body free of branches and the wait count constant.
+    const int KT = (int)(K / BK);
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st) issue(st < KT ? st : KT - 1, st);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS * (STAGES - 2)));
+    __syncthreads();
+    v4i af0[TM], bf0[TN], af1[TM], bf1[TN];
+    read_frags(lds, 0, af0, bf0);
+
+    int s_cur = 0, s_issue = STAGES - 1;
+    for (int kt = 0; kt < KT; ++kt) {
+        // F0 (read at the end of the previous iteration) is complete
+        __builtin_amdgcn_s_waitcnt(kLgkm0);
+        const int s_next = s_cur + 1 == STAGES ? 0 : s_cur + 1;
+        const int8_t* cur = lds + s_cur * STAGE_BYTES;
+        issue(kt + STAGES - 1 < KT ? kt + STAGES - 1 : KT - 1, s_issue);
+        read_frags(cur, 1, af1, bf1);
+        mfmas(af0, bf0);
+        interleave();
+        // tile kt+1 has landed (only the STAGES-2 newer copies may still
+        // fly) and this wave's F1 reads are done before the barrier, after
+        // which the stage may be overwritten
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS * (STAGES - 2)) & ~0xF00);
+        __syncthreads();
+        read_frags(lds + s_next * STAGE_BYTES, 0, af0, bf0);
+        mfmas(af1, bf1);
+        interleave();
+        s_cur = s_next;
+        s_issue = s_issue + 1 == STAGES ? 0 : s_issue + 1;
+    }
+    // no LDS copy may still be in flight when the workgroup retires
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    epilogue<TM, TN, WRITE_ACC>(acc, a, m0 + wm0, n0 + wn0, lane);
 }
 
 template <int BM, int BN, int BK, int WAVES_M>
@@ -241,7 +413,20 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+template <int STAGES>
+hipError_t launch_big(const GemmArgs& a, hipStream_t stream) {
+    const int64_t tiles = ceil_div(a.T, 256) * ceil_div(a.N, 256);
+    if (a.acc_out)
+        hipLaunchKernelGGL((k_gemm_i8_big<STAGES, true>), dim3((unsigned)tiles), dim3(kThreads), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((k_gemm_i8_big<STAGES, false>), dim3((unsigned)tiles), dim3(kThreads), 0,
+                           stream, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
+    if (a.T > 128 && a.K % 64 == 0) return launch_big<3>(a, stream);
     if (a.T <= 32) return launch_cfg<32, 256, 128, 1>(a, stream);
     return launch_cfg<128, 128, 64, 2>(a, stream);
 }

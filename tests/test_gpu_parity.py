@@ -100,6 +100,10 @@ def test_tiny_config(mm):
 @pytest.mark.parametrize("T,K,N,nd,dist", [
     (1, 16, 8, 0, "normal"), (37, 80, 200, 2, "normal"), (129, 272, 136, 5, "laplace"),
     (300, 1040, 520, 3, "normal"), (17, 4096, 264, 40, "normal"), (260, 528, 1032, 20, "laplace"),
+    # shapes on the large-tile kernel (T > 128, K % 64 == 0): one and two
+    # k-tiles, ragged T and N against the 256x256 tile, many outliers
+    (129, 64, 8, 1, "normal"), (513, 128, 264, 2, "normal"), (300, 1024, 520, 3, "laplace"),
+    (257, 2048, 1000, 70, "normal"),
 ])
 def test_ragged_shapes(mm, T, K, N, nd, dist):
     X, W = synth.random_case(10_000 + T + K + N, T, K, N, n_dims=nd, x_dist=dist)
