@@ -50,6 +50,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--only", choices=["prefill", "decode"], default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain 1 GiB device-to-device copy (a kernel of known "
+                        "traffic, for scaling the HBM byte counters)")
     return p.parse_args()
 
 
@@ -228,6 +231,16 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("copy calibration: 3 copies of 1 GiB")
 
     pre = dec = None
     if args.only in (None, "prefill"):

@@ -233,20 +233,20 @@ __global__ __launch_bounds__(kThreads) void k_gemm_i8(GemmArgs a) {
     epilogue<C::TM, C::TN, WRITE_ACC>(acc, a, m0 + wm0, n0 + wn0, lane);
 }
 
-// 16-byte copy global -> LDS without VGPR staging (global_load_lds_dwordx4).
-// The wave's 64 lanes land contiguously at lds_dst + 16 * lane; lds_dst must
-// be wave-uniform.  Written as inline asm so that the compiler's wait-count
+// 16-byte copy global -> LDS without VGPR staging (global_load_lds_dwordx4,
+// address = wave-uniform base + 32-bit lane offset).  The wave's 64 lanes
+// land contiguously at lds_dst + 16 * lane; lds_dst must be wave-uniform.  Written as inline asm so that the compiler's wait-count
 // insertion, which cannot tell which LDS bytes such a copy writes, does not
 // add a full vmcnt(0) before every LDS read; the kernels below wait for the
 // copies themselves (s_waitcnt vmcnt + barrier) before reading the stage.
 // The instruction has no register result.  m0 carries the LDS address; no
 // other instruction in these kernels uses m0.
-__device__ __forceinline__ void copy_to_lds16(const void* gsrc, const void* lds_dst) {
+__device__ __forceinline__ void copy_to_lds16(const void* gbase, uint32_t goff, const void* lds_dst) {
     const uint32_t la =
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)lds_dst;
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
-                 : "v"(gsrc), "s"(la)
+                 : "v"(goff), "s"(gbase), "s"(la)
                  : "memory");
 }
 
@@ -256,27 +256,47 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0xF70; }
 // s_waitcnt immediate for lgkmcnt(0) only (vmcnt 63, expcnt 7 = no wait)
 constexpr int kLgkm0 = 0xC07F;
 
-// Large-tile kernel for prefill shapes: a 256x256 workgroup tile, each wave a
-// 128x128 grid of 4x4 MFMA tiles (256 int32 accumulators per lane), so every
-// 16-byte LDS fragment feeds four MFMAs.  Operands go from global memory
-// straight into LDS (global_load_lds_dwordx4: no VGPR staging, no LDS store
-// instructions) through a ring of STAGES buffers of 32 KB (BK = 64).  A wave
-// instruction fills 1 KB of LDS, lane l landing at byte 16*l, so the XOR
-// swizzle is applied by choosing which global chunk each lane fetches.
+// XOR swizzle of the four 16-byte chunks of a 64-byte LDS row.  A fragment
+// read has lanes 0..31 on 32 consecutive rows at one logical chunk; with this
+// swizzle any 8 consecutive rows land on 8 distinct 16-byte slots of a
+// 128-byte window and any 16 consecutive rows on 16 distinct slots of a
+// 256-byte window, so the read is free of bank conflicts whether the LDS
+// serves 8 or 16 lanes of a ds_read_b128 per cycle.
+__device__ __forceinline__ int big_swz(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
+
+// Large-tile kernel for prefill shapes: a 256x256 workgroup tile split over
+// 2 x WN waves; each wave owns a 128 x (256/WN) grid of 32x32 MFMA tiles.
+// Operands go from global memory straight into LDS (global_load_lds_dwordx4:
+// no VGPR staging, no LDS store instructions) through a ring of 4 buffers of
+// 32 KB (BK = 64).  A wave instruction fills 1 KB of LDS, lane l landing at
+// byte 16*l, so the swizzle is applied by choosing which global chunk each
+// lane fetches.
 //
-// Software pipeline per k-tile (two 32-deep sub-steps, fragments F0/F1):
-//   issue the global->LDS copy of tile kt+STAGES-1
-//   ds_read F1 (tile kt, second half)   interleaved with  16 MFMA on F0
-//   wait until tile kt+1 has landed, barrier
-//   ds_read F0 (tile kt+1, first half)  interleaved with  16 MFMA on F1
-// so LDS latency hides under MFMA work and there is one barrier per tile.
-// Requires K % 64 == 0; rows past T or N are clamped to the last valid row
-// (they only feed outputs that are never stored).
-template <int STAGES, bool WRITE_ACC>
-__global__ __launch_bounds__(kThreads) void k_gemm_i8_big(GemmArgs a) {
-    constexpr int BM = 256, BN = 256, BK = 64, TM = 4, TN = 4;
+// With WN = 4 (8 waves, 128 int32 accumulators per lane) two waves share
+// each SIMD: while one waits to issue its copies the other keeps the MFMA
+// pipe busy.  WN = 2 (4 waves, 256 accumulators) maximizes fragment reuse
+// instead.
+//
+// Per k-tile kt (two 32-deep sub-steps with fragments F0/F1):
+//   first half:  ds_read F1 of tile kt          under the MFMAs on F0
+//   wait until tile kt+1 has landed, barrier    (tile kt is now fully read)
+//   second half: copy tile kt+4 into kt's buffer, ds_read F0 of tile kt+1,
+//                under the MFMAs on F1
+// Each half is hand-ordered so that reads come early and every MFMA is
+// preceded by at most one read and one copy.  Requires K % 64 == 0; rows past
+// T or N are clamped to the last valid row (they only feed outputs that are
+// never stored).
+template <int WN, bool WRITE_ACC>
+__global__ __launch_bounds__(128 * WN) void k_gemm_i8_big(GemmArgs a) {
+    constexpr int BM = 256, BN = 256, BK = 64, STAGES = 4;
+    constexpr int WAVES = 2 * WN, THREADS = 64 * WAVES;
+    constexpr int TM = 4, TN = BN / WN / 32;
+    constexpr int NF = TM + TN;                      // fragments per sub-step
+    constexpr int NM = TM * TN;                      // MFMAs per sub-step
     constexpr int STAGE_BYTES = (BM + BN) * BK;
-    constexpr int LOADS = (BM + BN) * BK / 16 / kThreads;   // 16-byte copies per lane per tile
+    constexpr int GPW = 16 / WAVES;                  // 1 KB groups of A (and of B) per wave
+    constexpr int LOADS = 2 * GPW;                   // copies per lane per tile
+    static_assert(NF <= NM && LOADS <= NM, "interleave needs one MFMA per read and copy");
     __shared__ __attribute__((aligned(1024))) int8_t lds[STAGES * STAGE_BYTES];
 
     const int tid = threadIdx.x;
@@ -288,32 +308,31 @@ __global__ __launch_bounds__(kThreads) void k_gemm_i8_big(GemmArgs a) {
     const int64_t m0 = (bid % MT) * BM;
     const int64_t n0 = (bid / MT) * BN;
     const int wm0 = (wave & 1) * 128;
-    const int wn0 = (wave >> 1) * 128;
+    const int wn0 = (wave >> 1) * (BN / WN);
 
-    // copy assignment: wave w fills the 1 KB groups 4w..4w+3 of A and of B;
-    // in a group, lane l writes row 16g + l/4, physical chunk l%4.  Addresses
-    // are a per-workgroup scalar base plus a 32-bit lane offset (a 256-row
-    // panel spans at most 256 * 133136 bytes).
+    // copy assignment: wave w fills the 1 KB groups GPW*w .. GPW*w+GPW-1 of A
+    // and of B; in a group, lane l writes row 16g + l/4, physical chunk l%4.
+    // Copy u < GPW is an A group, u >= GPW a B group.  Addresses are a
+    // per-workgroup scalar base plus a 32-bit lane offset (a 256-row panel
+    // spans at most 256 * 133136 bytes).
     const int8_t* abase = a.xq + m0 * K;
     const int8_t* bbase = a.wq + n0 * K;
-    uint32_t aoffg[4], boffg[4];
+    uint32_t goff[LOADS];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int row = (wave * 4 + u) * 16 + (lane >> 2);
-        const int c = (lane & 3) ^ ((row >> 1) & 3);
+    for (int u = 0; u < GPW; ++u) {
+        const int row = (wave * GPW + u) * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ big_swz(row);
         const int64_t ra = m0 + row < T ? row : T - 1 - m0;
         const int64_t rb = n0 + row < N ? row : N - 1 - n0;
-        aoffg[u] = (uint32_t)(ra * K + c * 16);
-        boffg[u] = (uint32_t)(rb * K + c * 16);
+        goff[u] = (uint32_t)(ra * K + c * 16);
+        goff[GPW + u] = (uint32_t)(rb * K + c * 16);
     }
-    auto issue = [&](int kt, int stage) {
-        int8_t* dst = lds + stage * STAGE_BYTES + wave * 4 * 1024;
-        const int8_t* ak = abase + (int64_t)kt * BK;
-        const int8_t* bk = bbase + (int64_t)kt * BK;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) copy_to_lds16(ak + aoffg[u], dst + u * 1024);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) copy_to_lds16(bk + boffg[u], dst + BM * BK + u * 1024);
+    auto copy = [&](int u, int kt, int stage) {
+        const bool isa = u < GPW;
+        const int8_t* base = (isa ? abase : bbase) + (int64_t)kt * BK;
+        const int8_t* dst = lds + stage * STAGE_BYTES + (isa ? 0 : BM * BK) +
+                            (wave * GPW + (isa ? u : u - GPW)) * 1024;
+        copy_to_lds16(base, goff[u], dst);
     };
 
     v16i acc[TM][TN];
@@ -324,75 +343,69 @@ __global__ __launch_bounds__(kThreads) void k_gemm_i8_big(GemmArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-    // fragment offsets inside a stage (identical for every stage)
-    int aoff[2][TM], boff[2][TN];
+    // fragment offsets inside a stage (identical for every stage): fragment
+    // q < TM is A tile q, q >= TM is B tile q-TM, for sub-step ss
+    int foff[2][NF];
 #pragma unroll
     for (int ss = 0; ss < 2; ++ss) {
         const int c = ss * 2 + (lane >> 5);
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int row = wm0 + i * 32 + (lane & 31);
-            aoff[ss][i] = row * BK + ((c ^ ((row >> 1) & 3)) * 16);
+            foff[ss][i] = row * BK + ((c ^ big_swz(row)) * 16);
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const int row = wn0 + j * 32 + (lane & 31);
-            boff[ss][j] = BM * BK + row * BK + ((c ^ ((row >> 1) & 3)) * 16);
+            const int col = wn0 + j * 32 + (lane & 31);
+            foff[ss][TM + j] = BM * BK + col * BK + ((c ^ big_swz(col)) * 16);
         }
     }
-    auto read_frags = [&](const int8_t* base, int ss, v4i (&af)[TM], v4i (&bf)[TN]) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const v4i*>(base + aoff[ss][i]);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) bf[j] = *reinterpret_cast<const v4i*>(base + boff[ss][j]);
-    };
-    auto mfmas = [&](const v4i (&af)[TM], const v4i (&bf)[TN]) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
-    };
-    // 8 fragment reads spread over 16 MFMAs
-    auto interleave = [&]() {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one DS read
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // two MFMA
-        }
+    v4i f0[NF], f1[NF];
+    auto mfma = [&](const v4i (&f)[NF], int m) {
+        const int i = m / TN, j = m % TN;
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f[i], f[TM + j], acc[i][j], 0, 0, 0);
     };
 
-    // The ring always has STAGES-1 copies in flight: past the last tile the
-    // loop re-copies tile KT-1 into a buffer that is never read again, which
-    // keeps the body free of branches and the wait count constant.
+    // Prologue: tiles 0..3 in flight, wait for tile 0, first F0.  Past the
+    // last tile, copies re-fetch tile KT-1 into a buffer that is never read
+    // again, which keeps the loop free of branches and the wait count fixed.
     const int KT = (int)(K / BK);
 #pragma unroll
-    for (int st = 0; st < STAGES - 1; ++st) issue(st < KT ? st : KT - 1, st);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS * (STAGES - 2)));
+    for (int st = 0; st < STAGES; ++st)
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) copy(u, st < KT ? st : KT - 1, st);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS * (STAGES - 1)));
     __syncthreads();
-    v4i af0[TM], bf0[TN], af1[TM], bf1[TN];
-    read_frags(lds, 0, af0, bf0);
+#pragma unroll
+    for (int q = 0; q < NF; ++q) f0[q] = *reinterpret_cast<const v4i*>(lds + foff[0][q]);
 
-    int s_cur = 0, s_issue = STAGES - 1;
+    int s_cur = 0;
     for (int kt = 0; kt < KT; ++kt) {
-        // F0 (read at the end of the previous iteration) is complete
-        __builtin_amdgcn_s_waitcnt(kLgkm0);
-        const int s_next = s_cur + 1 == STAGES ? 0 : s_cur + 1;
+        const int s_next = (s_cur + 1) & (STAGES - 1);
         const int8_t* cur = lds + s_cur * STAGE_BYTES;
-        issue(kt + STAGES - 1 < KT ? kt + STAGES - 1 : KT - 1, s_issue);
-        read_frags(cur, 1, af1, bf1);
-        mfmas(af0, bf0);
-        interleave();
-        // tile kt+1 has landed (only the STAGES-2 newer copies may still
-        // fly) and this wave's F1 reads are done before the barrier, after
-        // which the stage may be overwritten
+        const int8_t* nxt = lds + s_next * STAGE_BYTES;
+        const int kcopy = kt + STAGES < KT ? kt + STAGES : KT - 1;
+        __builtin_amdgcn_s_waitcnt(kLgkm0);   // F0 has arrived
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            if (m < NF) f1[m] = *reinterpret_cast<const v4i*>(cur + foff[1][m]);
+            mfma(f0, m);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // tile kt+1 has landed (tiles kt+2, kt+3 may still fly) and this
+        // wave's F1 reads are complete; after the barrier nobody reads tile kt
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS * (STAGES - 2)) & ~0xF00);
         __syncthreads();
-        read_frags(lds + s_next * STAGE_BYTES, 0, af0, bf0);
-        mfmas(af1, bf1);
-        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            if (m < NF) f0[m] = *reinterpret_cast<const v4i*>(nxt + foff[0][m]);
+            if (m < LOADS) copy(m, kcopy, s_cur);
+            mfma(f1, m);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         s_cur = s_next;
-        s_issue = s_issue + 1 == STAGES ? 0 : s_issue + 1;
     }
     // no LDS copy may still be in flight when the workgroup retires
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -413,20 +426,20 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-template <int STAGES>
+template <int WN>
 hipError_t launch_big(const GemmArgs& a, hipStream_t stream) {
     const int64_t tiles = ceil_div(a.T, 256) * ceil_div(a.N, 256);
     if (a.acc_out)
-        hipLaunchKernelGGL((k_gemm_i8_big<STAGES, true>), dim3((unsigned)tiles), dim3(kThreads), 0,
+        hipLaunchKernelGGL((k_gemm_i8_big<WN, true>), dim3((unsigned)tiles), dim3(128 * WN), 0,
                            stream, a);
     else
-        hipLaunchKernelGGL((k_gemm_i8_big<STAGES, false>), dim3((unsigned)tiles), dim3(kThreads), 0,
+        hipLaunchKernelGGL((k_gemm_i8_big<WN, false>), dim3((unsigned)tiles), dim3(128 * WN), 0,
                            stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
-    if (a.T > 128 && a.K % 64 == 0) return launch_big<3>(a, stream);
+    if (a.T > 128 && a.K % 64 == 0) return launch_big<4>(a, stream);
     if (a.T <= 32) return launch_cfg<32, 256, 128, 1>(a, stream);
     return launch_cfg<128, 128, 64, 2>(a, stream);
 }
