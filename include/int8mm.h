@@ -108,8 +108,9 @@ int int8_mixed_matmul(const void* X, int64_t T, int64_t K, const int8_t* Wq, con
  *   xq:    int8  [T,K] quantized activations (outlier columns 0)
  *   sx:    fp32  [T]   row scales
  *   acc:   int32 [T,N] int8 matmul accumulators before dequantization
- * It runs the same kernels as int8_mixed_matmul for T > 16 (for smaller T
- * the plain call takes the single-kernel decode path instead).
+ * It runs the same kernels as int8_mixed_matmul (the single-kernel decode
+ * path when the shape qualifies, the staged kernels otherwise) and adds
+ * only the stores of the intermediates.
  * Errors: as int8_mixed_matmul. */
 int int8_mixed_matmul_debug(const void* X, int64_t T, int64_t K, const int8_t* Wq,
                             const float* sw, const void* W16, int64_t N, float tau, void* Y,

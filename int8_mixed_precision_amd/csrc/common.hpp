@@ -65,6 +65,13 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 
+// ---- single-kernel decode path (k_decode.hip)
+bool decode_path_supported(int64_t T, int64_t K, int64_t N);
+hipError_t launch_decode(const _Float16* X, int64_t T, int64_t K, const int8_t* Wq,
+                         const float* sw, const _Float16* W16, int64_t N, float tau,
+                         _Float16* Y, int32_t* dbg_count, int32_t* dbg_idx, int8_t* dbg_xq,
+                         float* dbg_sx, int32_t* dbg_acc, hipStream_t stream);
+
 // ---- debug copies (k_activation.hip)
 hipError_t launch_debug_copies(const Workspace& ws, int64_t T, int64_t K, int32_t* count,
                                int32_t* idx, int8_t* xq, float* sx, hipStream_t stream);

@@ -48,13 +48,21 @@ int check_matmul(const void* X, int64_t T, int64_t K, const int8_t* Wq, const fl
 
 int run_matmul(const void* X, int64_t T, int64_t K, const int8_t* Wq, const float* sw,
                const void* W16, int64_t N, float tau, void* Y, void* workspace,
-               hipStream_t stream, int32_t* acc_out) {
+               hipStream_t stream, int32_t* count, int32_t* idx, int8_t* xq, float* sx,
+               int32_t* acc) {
+    if (decode_path_supported(T, K, N))
+        return hip_status(launch_decode(static_cast<const _Float16*>(X), T, K, Wq, sw,
+                                        static_cast<const _Float16*>(W16), N, tau,
+                                        static_cast<_Float16*>(Y), count, idx, xq, sx, acc,
+                                        stream));
     Workspace ws = carve_workspace(workspace, T, K);
     hipError_t e = launch_activation_pass(static_cast<const _Float16*>(X), T, K, tau, ws, stream);
     if (e != hipSuccess) return INT8MM_E_HIP;
     GemmArgs g{ws.xq, ws.sx, Wq, sw, ws.xo, ws.idx, ws.count,
-               static_cast<const _Float16*>(W16), static_cast<_Float16*>(Y), acc_out, T, K, N};
-    return hip_status(launch_gemm(g, stream));
+               static_cast<const _Float16*>(W16), static_cast<_Float16*>(Y), acc, T, K, N};
+    e = launch_gemm(g, stream);
+    if (e != hipSuccess) return INT8MM_E_HIP;
+    return hip_status(launch_debug_copies(ws, T, K, count, idx, xq, sx, stream));
 }
 
 }  // namespace
@@ -99,7 +107,8 @@ int int8_mixed_matmul(const void* X, int64_t T, int64_t K, const int8_t* Wq, con
     int st = check_matmul(X, T, K, Wq, sw, W16, N, tau, Y, workspace, workspace_bytes);
     if (st) return st;
     return run_matmul(X, T, K, Wq, sw, W16, N, tau, Y, workspace,
-                      static_cast<hipStream_t>(stream), nullptr);
+                      static_cast<hipStream_t>(stream), nullptr, nullptr, nullptr, nullptr,
+                      nullptr);
 }
 
 int int8_mixed_matmul_debug(const void* X, int64_t T, int64_t K, const int8_t* Wq,
@@ -111,11 +120,8 @@ int int8_mixed_matmul_debug(const void* X, int64_t T, int64_t K, const int8_t* W
     if ((count && !aligned16(count)) || (idx && !aligned16(idx)) || (xq && !aligned16(xq)) ||
         (sx && !aligned16(sx)) || (acc && !aligned16(acc)))
         return INT8MM_E_ALIGN;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    st = run_matmul(X, T, K, Wq, sw, W16, N, tau, Y, workspace, s, acc);
-    if (st) return st;
-    Workspace ws = carve_workspace(workspace, T, K);
-    return hip_status(launch_debug_copies(ws, T, K, count, idx, xq, sx, s));
+    return run_matmul(X, T, K, Wq, sw, W16, N, tau, Y, workspace,
+                      static_cast<hipStream_t>(stream), count, idx, xq, sx, acc);
 }
 
 int int8mm_quantize_activations(const void* X, int64_t T, int64_t K, int64_t N, float tau,

@@ -110,6 +110,17 @@ def test_ragged_shapes(mm, T, K, N, nd, dist):
     run_case(mm, f"ragged {T}x{K}x{N}", X, W, 6.0)
 
 
+@pytest.mark.parametrize("T,K,N,nd,tau", [
+    (1, 4096, 1000, 3, 6.0), (3, 4096, 8, 0, 6.0), (8, 8192, 2056, 6, 6.0),
+    (16, 4096, 520, 5, 6.0), (8, 8192, 264, 300, 6.0),   # o > 256: values read from X
+    (2, 4096, 136, 0, 0.0),                              # every dimension an outlier
+])
+def test_decode_path(mm, T, K, N, nd, tau):
+    """Shapes on the single-kernel decode path (T <= 16, K in {4096, 8192})."""
+    X, W = synth.random_case(30_000 + T + K + N + nd, T, K, N, n_dims=nd)
+    run_case(mm, f"decode path {T}x{K}x{N} tau={tau}", X, W, tau)
+
+
 def test_tau_zero_every_dimension_outlier(mm):
     X, W = synth.random_case(21, 70, 1024, 136)
     r, ref = run_case(mm, "tau=0", X, W, 0.0)
