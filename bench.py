@@ -68,17 +68,22 @@ def src_digest(names) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(profile_name: str, digest: str, launches_key: str):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
-    was taken on the kernel source as it is now (else None)."""
+def measured_traffic(profile_name: str, digest: str, key: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary
+    (profiles/*.md, 'key: value' lines), if it was taken on the kernel
+    source as it is now (else None)."""
     path = os.path.join(ROOT, "profiles", profile_name)
     if not os.path.exists(path):
         return None
+    vals = {}
     with open(path) as f:
-        d = json.load(f)
-    if d.get("kernel_src_sha") != digest:
+        for line in f:
+            if ":" in line and line.strip().startswith("- "):
+                k, v = line.strip()[2:].split(":", 1)
+                vals[k.strip().strip("`")] = v.strip().strip("`")
+    if vals.get("kernel_src_sha") != digest or key not in vals:
         return None
-    return d.get(launches_key)
+    return float(vals[key])
 
 
 def timed_loop(torch, steps, warmup, body):
@@ -167,25 +172,41 @@ def bench_decode(torch, mm, synth, steps, warmup):
     ws = mm.new_workspace(T, K, N)
     Y = torch.empty((T, N), dtype=torch.float16, device="cuda")
 
+    # A decode call is tens of microseconds of GPU work, less than the Python
+    # binding takes to issue it, so the steps are launched from a HIP graph
+    # (one replay = DECODE_ROTATE calls, one per weight copy), as a serving
+    # loop would.  The graph holds only the library's own kernel launches.
+    def one_round():
+        for Wq, sw, W16 in sets:
+            mm.mixed_matmul(X, Wq, sw, W16, w.tau, workspace=ws, out=Y)
+
+    one_round()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        one_round()
+    torch.cuda.synchronize()
+    rounds = max(1, (steps + DECODE_ROTATE - 1) // DECODE_ROTATE)
+    steps = rounds * DECODE_ROTATE
+
     def step(i, e):
-        Wq, sw, W16 = sets[i % DECODE_ROTATE]
         if e is not None:
             e[0].record()
-        mm.mixed_matmul(X, Wq, sw, W16, w.tau, workspace=ws, out=Y)
+        graph.replay()
         if e is not None:
             e[1].record()
             e[2].record()
 
-    log(f"decode: {warmup} warmup + {steps} timed steps")
-    wall, evs = timed_loop(torch, steps, warmup, step)
-    call_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    log(f"decode: {warmup} warmup + {rounds} timed graph replays of {DECODE_ROTATE} calls")
+    wall, evs = timed_loop(torch, rounds, max(1, warmup // DECODE_ROTATE + 1), step)
+    call_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) / DECODE_ROTATE
     dbg = mm.mixed_matmul_debug(X, Wq0, sw0, W16_0, w.tau)
     o = int(dbg["count"][0])
     wbytes = K * N + 4.0 * N
     alg_bytes = 2.0 * T * K + K * N + 4.0 * N + 2.0 * o * N + 2.0 * T * N
     return {
         "T": T, "K": K, "N": N, "tau": w.tau, "o": o, "ms_per_step": wall * 1e3 / steps,
-        "weight_gbs": wbytes * steps / wall / 1e9, "call_ms": call_ms,
+        "steps": steps, "weight_gbs": wbytes * steps / wall / 1e9, "call_ms": call_ms,
         "alg_bytes": alg_bytes, "alg_gbs": alg_bytes / (call_ms * 1e-3) / 1e9,
     }
 
@@ -198,12 +219,16 @@ def cpu_baseline(synth, T, K, N):
     X = synth.make_x(w, threads=CPU_THREADS)
     W = synth.make_w(w, threads=CPU_THREADS)
     Wq, sw = oracle.quantize_weight(W, threads=CPU_THREADS)
-    # size the sample from a 2-row probe so the timed run takes ~CPU_TARGET_S
-    t0 = time.perf_counter()
-    oracle.mixed_matmul(X, Wq, sw, W, w.tau, rows=np.arange(2), threads=CPU_THREADS)
-    probe = time.perf_counter() - t0
-    rows = int(max(CPU_THREADS, min(T, CPU_TARGET_S / max(probe / 2, 1e-6))))
-    rows -= rows % CPU_THREADS if rows > CPU_THREADS else 0
+    # size the sample so the timed run takes ~CPU_TARGET_S: a two-point fit
+    # separates the fixed cost (detection over all rows) from the cost per row
+    def run(nrows):
+        t0 = time.perf_counter()
+        oracle.mixed_matmul(X, Wq, sw, W, w.tau, rows=np.arange(nrows), threads=CPU_THREADS)
+        return time.perf_counter() - t0
+    t_a, t_b = run(CPU_THREADS), run(2 * CPU_THREADS)
+    per_row = max((t_b - t_a) / CPU_THREADS, 1e-6)
+    rows = int(min(T, max(CPU_THREADS, (CPU_TARGET_S - t_a + CPU_THREADS * per_row) / per_row)))
+    rows -= rows % CPU_THREADS
     sample = np.linspace(0, T - 1, rows).astype(np.int64)
     t0 = time.perf_counter()
     oracle.mixed_matmul(X, Wq, sw, W, w.tau, rows=sample, threads=CPU_THREADS)
@@ -253,6 +278,7 @@ def main():
         log(f"decode: {dec['weight_gbs']:.1f} GB/s weight ({dec['call_ms'] * 1e3:.1f} us/call)")
 
     gemm_digest = src_digest(["k_gemm.hip", "common.hpp"])
+    decode_digest = src_digest(["k_decode.hip", "common.hpp"])
     out = {
         "metric": "int8-mixed matmul TOPS @ T=2048 K=12288 N=49152; weight GB/s @ T=8",
         "higher_is_better": True, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -270,9 +296,9 @@ def main():
                        "fraction_8bit": round((pre["K"] - pre["o"]) / pre["K"], 6)},
             "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_INT8_TOPS,
                          "unit": "TFLOP/s", "frac": round(ach / PEAK_INT8_TOPS, 4),
-                         "traffic": measured_traffic("gemm_i8_prefill_up_traffic.json",
+                         "traffic": measured_traffic("gemm_i8_prefill_up_traffic.md",
                                                      gemm_digest, "hbm_bytes_per_launch"),
-                         "kernel": "k_gemm_i8 (int8 MFMA + fused dequant/fp16 outlier epilogue)",
+                         "kernel": "k_gemm_i8_big (int8 MFMA + fused dequant/fp16 outlier epilogue)",
                          "work": "2*T*K*N int8 ops per launch", "ms": round(pre["gemm_ms"], 4)},
             "stages_ms": {"activation_pass": round(pre["activation_ms"], 4),
                           "gemm": round(pre["gemm_ms"], 4)},
@@ -282,7 +308,8 @@ def main():
         })
     if dec is not None:
         d = {"metric": "weight GB/s @ T=8", "value": round(dec["weight_gbs"], 1), "unit": "GB/s",
-             "ms_per_step": round(dec["ms_per_step"], 5),
+             "ms_per_step": round(dec["ms_per_step"], 5), "steps": dec["steps"],
+             "launch": "HIP graph replay of 8 calls (one per rotating weight copy)",
              "config": {"workload": "decode FFN up-projection, W pre-converted to Int8, "
                                     f"{DECODE_ROTATE} rotating weight copies",
                         "T": dec["T"], "K": dec["K"], "N": dec["N"], "tau": dec["tau"],
@@ -290,7 +317,8 @@ def main():
              "roofline": {"bound": "hbm", "achieved": round(dec["alg_gbs"], 1),
                           "peak": PEAK_HBM_GBS, "unit": "GB/s",
                           "frac": round(dec["alg_gbs"] / PEAK_HBM_GBS, 4),
-                          "traffic": None, "kernel": "whole int8_mixed_matmul call",
+                          "traffic": measured_traffic("decode_dec_traffic.md", decode_digest, "hbm_bytes_per_launch"),
+                          "kernel": "k_decode (the whole int8_mixed_matmul call)",
                           "work": "2TK + KN + 4N + 2oN + 2TN bytes per call",
                           "ms": round(dec["call_ms"], 5)}}
         if pre is None:

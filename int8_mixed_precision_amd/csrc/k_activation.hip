@@ -18,6 +18,10 @@
 // cache for the row a workgroup is working on.
 #include "common.hpp"
 
+// Quantization must round x * r and any following add separately, exactly
+// like the definition; no multiply-add contraction in this file.
+#pragma clang fp contract(off)
+
 namespace i8mm {
 
 namespace {

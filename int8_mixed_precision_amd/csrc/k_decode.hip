@@ -29,6 +29,10 @@
 // T <= 16, K in {4096, 8192}, T*K <= 65536.
 #include "common.hpp"
 
+// Quantization must round x * r and any following add separately, exactly
+// like the definition; no multiply-add contraction in this file.
+#pragma clang fp contract(off)
+
 namespace i8mm {
 
 namespace {
@@ -42,12 +46,6 @@ constexpr int kMaxXK = 65536;          // T*K bytes of Xq kept in LDS
 constexpr int kMaxOutliersLds = 256;   // outlier values cached in LDS
 
 __device__ inline float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
-
-__device__ inline int8_t quant(float x, float r) {
-    float q = __builtin_rintf(x * r);
-    q = __builtin_fminf(__builtin_fmaxf(q, -127.0f), 127.0f);
-    return (int8_t)(int)q;
-}
 
 struct DecodeArgs {
     const uint16_t* x;      // [T,K] fp16 bits
@@ -74,6 +72,7 @@ struct Smem {
     float xo[kMaxT * kMaxOutliersLds];         // X values of the first outliers
     float wmax[kWaves][kMaxT];
     float sx[kMaxT];
+    float rx[kMaxT];                           // 127 / s_x (0 when s_x = 0)
     int32_t wtot[kWaves * 2];
 };
 
@@ -226,23 +225,42 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
         pc[j] += before;
     }
     __syncthreads();   // sx ready
-    // quantize the owned columns into LDS; gather the outliers
+    if (tid < T) {
+        const float sxt = sm.sx[tid];
+        sm.rx[tid] = sxt > 0.0f ? 127.0f / sxt : 0.0f;   // IEEE fp32 divide
+    }
+    __syncthreads();   // rx ready
+    // Quantize the owned columns into LDS and gather the outliers.
+    // q = rint(x * r) by the 1.5 * 2^23 addition: for |p| < 2^22, p + 1.5*2^23
+    // rounds p to the nearest integer (ties to even) and the low byte of the
+    // result's bit pattern is that integer as int8.  |x| <= s_x makes
+    // |p| <= 127 * (1 + 2^-23), so q is within [-127, 127] without a clamp.
+    // The multiply and the add stay separate roundings (no contraction).
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
         const int c = tid + kThreads * j;
+        // byte mask that zeroes the outlier columns of the chunk
+        uint32_t keep[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            keep[h] = 0u;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                keep[h] |= ((fm[j] >> (4 * h + e)) & 1u) ? 0u : (0xFFu << (8 * e));
+        }
 #pragma unroll
         for (int t = 0; t < TMAX; ++t) {
             {
-                const float sxt = t < T ? sm.sx[t] : 0.0f;
-                const float rr = sxt > 0.0f ? 127.0f / sxt : 0.0f;
+                const float rr = t < T ? sm.rx[t] : 0.0f;
                 uint32_t packed[2] = {0u, 0u};
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const uint32_t q = ((fm[j] >> e) & 1u)
-                                           ? 0u
-                                           : (uint32_t)(uint8_t)quant(chunk_val(xr[j][t], e), rr);
-                    packed[e >> 2] |= q << ((e & 3) * 8);
+                    const float p = __fmul_rn(chunk_val(xr[j][t], e), rr);
+                    const uint32_t bits = __builtin_bit_cast(uint32_t, __fadd_rn(p, 12582912.0f));
+                    packed[e >> 2] |= (bits & 0xFFu) << ((e & 3) * 8);
                 }
+                packed[0] &= keep[0];
+                packed[1] &= keep[1];
                 *reinterpret_cast<uint2*>(&sm.xq[t * ldx + c * 8]) = make_uint2(packed[0], packed[1]);
                 if (blockIdx.x == 0 && a.dbg_xq && t < T)
                     *reinterpret_cast<uint2*>(a.dbg_xq + (int64_t)t * K + c * 8) =

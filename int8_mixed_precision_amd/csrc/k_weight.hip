@@ -13,6 +13,10 @@
 // through LDS (coalesced fp16 reads along N, coalesced int8 writes along K).
 #include "common.hpp"
 
+// Quantization must round x * r and any following add separately, exactly
+// like the definition; no multiply-add contraction in this file.
+#pragma clang fp contract(off)
+
 namespace i8mm {
 
 namespace {

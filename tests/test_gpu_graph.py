@@ -1,0 +1,43 @@
+"""The plain entry point captured in a HIP graph (as the decode benchmark
+launches it): every replay, with eager work and synchronizations in
+between, must give exactly the eager result."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import int8_mixed_precision_amd as mm
+    return mm
+
+
+@pytest.mark.parametrize("T,K,N", [(8, 8192, 1040), (300, 1024, 520)])
+def test_graph_replays_match_eager(mm, T, K, N):
+    print(f"[case] graph replay {T}x{K}x{N}", flush=True)
+    X, W = synth.random_case(40_000 + T, T, K, N, n_dims=3)
+    Xd = torch.from_numpy(X).cuda()
+    Wd = torch.from_numpy(W).cuda()
+    Wq, sw = mm.quantize_weight(Wd)
+    ws = mm.new_workspace(T, K, N)
+    Y = torch.empty((T, N), dtype=torch.float16, device="cuda")
+    eager = mm.mixed_matmul(Xd, Wq, sw, Wd, 6.0).clone()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mm.mixed_matmul(Xd, Wq, sw, Wd, 6.0, workspace=ws, out=Y)
+    for rep in range(4):
+        Y.fill_(0)
+        # eager work between replays, on the same workspace-free path
+        other = mm.mixed_matmul(Xd, Wq, sw, Wd, 6.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Y, eager), f"replay {rep} differs"
+        assert torch.equal(other, eager)
