@@ -110,7 +110,7 @@ def bench_prefill(torch, mm, synth, steps, warmup):
     Wh = synth.make_w(w, threads=CPU_THREADS)
     W16 = torch.from_numpy(Wh).cuda()
     del Wh
-    Wq = torch.empty((N, K), dtype=torch.int8, device="cuda")
+    Wq = torch.empty(mm.weight_bytes(K, N), dtype=torch.int8, device="cuda")
     sw = torch.empty(N, dtype=torch.float32, device="cuda")
     # weight conversion (once per weight), timed on its own
     for _ in range(2):

@@ -75,12 +75,17 @@ const char* int8mm_status_string(int status);
  * bytes: host pointer, receives the size.  Errors: E_NULL, E_SHAPE. */
 int int8_mixed_matmul_workspace_size(int64_t T, int64_t K, int64_t N, size_t* bytes);
 
+/* Bytes of the converted weight Wq for a [K,N] weight (host only, enqueues
+ * nothing); currently K*N.  Callers size Wq with this query: the layout is
+ * the library's.  Errors: E_NULL, E_SHAPE. */
+int int8_quantize_weight_size(int64_t K, int64_t N, size_t* bytes);
+
 /* Weight conversion to Int8 ("converted to Int8" at load time, LLM.int8()
  * abstract): column-wise absmax quantization, one scale per output column
  * n (one per inner product).
  *   W16: fp16 [K,N] row-major (read only)
- *   Wq:  int8 [N,K] row-major, i.e. stored transposed with K contiguous
- *        (written; K*N bytes)
+ *   Wq:  int8, int8_quantize_weight_size() bytes: [N,K] row-major, i.e. the
+ *        transpose of W with K contiguous, Wq[n*K + k] (written)
  *   sw:  fp32 [N] column scales s_w[n] = max_k |W[k,n]| (written)
  * Errors: E_NULL, E_SHAPE, E_ALIGN, E_HIP. */
 int int8_quantize_weight(const void* W16, int64_t K, int64_t N, int8_t* Wq, float* sw,
@@ -88,7 +93,7 @@ int int8_quantize_weight(const void* W16, int64_t K, int64_t N, int8_t* Wq, floa
 
 /* The whole LLM.int8() matmul (steps 1-4 above) on a converted weight.
  *   X:   fp16 [T,K] activations (read only)
- *   Wq, sw: from int8_quantize_weight (read only)
+ *   Wq, sw: from int8_quantize_weight for the same K and N (read only)
  *   W16: fp16 [K,N], the 16-bit weight; only its outlier rows are read.
  *        NULL is rejected with E_UNSUPPORTED (no dequantized-row fallback).
  *   tau: outlier threshold, tau >= 0 (+inf: no outliers; 0: every

@@ -31,6 +31,7 @@ MAX_K = 133136
 EXPORTS = [
     "int8mm_status_string",
     "int8_mixed_matmul_workspace_size",
+    "int8_quantize_weight_size",
     "int8_quantize_weight",
     "int8_mixed_matmul",
     "int8_mixed_matmul_debug",
@@ -55,6 +56,7 @@ def _load() -> ctypes.CDLL:
     lib.int8mm_status_string.argtypes = [c_int]
     lib.int8mm_status_string.restype = ctypes.c_char_p
     lib.int8_mixed_matmul_workspace_size.argtypes = [i64, i64, i64, ctypes.POINTER(sz)]
+    lib.int8_quantize_weight_size.argtypes = [i64, i64, ctypes.POINTER(sz)]
     lib.int8_quantize_weight.argtypes = [vp, i64, i64, vp, vp, vp]
     lib.int8_mixed_matmul.argtypes = [vp, i64, i64, vp, vp, vp, i64, f32, vp, vp, sz, vp]
     lib.int8_mixed_matmul_debug.argtypes = [vp, i64, i64, vp, vp, vp, i64, f32, vp, vp, sz, vp,
@@ -112,15 +114,27 @@ def new_workspace(T: int, K: int, N: int, device=None) -> torch.Tensor:
     return torch.empty(workspace_size(T, K, N), dtype=torch.uint8, device=device or "cuda")
 
 
+def weight_bytes(K: int, N: int) -> int:
+    """Bytes of the converted weight (layout in include/int8mm.h)."""
+    out = ctypes.c_size_t(0)
+    _check(_lib.int8_quantize_weight_size(K, N, ctypes.byref(out)), "int8_quantize_weight_size")
+    return out.value
+
+
 def quantize_weight(W16: torch.Tensor, out: tuple | None = None):
-    """W16 fp16 [K,N] -> (Wq int8 [N,K], sw fp32 [N])."""
+    """W16 fp16 [K,N] -> (Wq int8 [weight_bytes(K,N)], the library's layout
+    (currently [N,K] row-major), sw fp32 [N])."""
     _need(W16, torch.float16, 2, "W16")
     K, N = W16.shape
     if out is None:
-        Wq = torch.empty((N, K), dtype=torch.int8, device=W16.device)
+        Wq = torch.empty(weight_bytes(K, N), dtype=torch.int8, device=W16.device)
         sw = torch.empty(N, dtype=torch.float32, device=W16.device)
     else:
         Wq, sw = out
+        _need(Wq, torch.int8, 1, "Wq")
+        _need(sw, torch.float32, 1, "sw")
+        if Wq.numel() != weight_bytes(K, N) or sw.numel() != N:
+            raise ValueError("output buffers have the wrong size")
     _check(_lib.int8_quantize_weight(_ptr(W16), K, N, _ptr(Wq), _ptr(sw), _stream()),
            "int8_quantize_weight")
     return Wq, sw
@@ -128,13 +142,13 @@ def quantize_weight(W16: torch.Tensor, out: tuple | None = None):
 
 def _mm_args(X, Wq, sw, W16):
     _need(X, torch.float16, 2, "X")
-    _need(Wq, torch.int8, 2, "Wq")
+    _need(Wq, torch.int8, 1, "Wq")
     _need(sw, torch.float32, 1, "sw")
     T, K = X.shape
-    N = Wq.shape[0]
-    if Wq.shape[1] != K or sw.shape[0] != N:
-        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, Wq {tuple(Wq.shape)}, "
-                         f"sw {tuple(sw.shape)}")
+    N = sw.shape[0]
+    if Wq.numel() != weight_bytes(K, N):
+        raise ValueError(f"Wq has {Wq.numel()} bytes, a [{K},{N}] weight needs "
+                         f"{weight_bytes(K, N)}")
     if W16 is not None:
         _need(W16, torch.float16, 2, "W16")
         if tuple(W16.shape) != (K, N):
@@ -186,8 +200,11 @@ def quantize_activations(X, N: int, tau: float, workspace) -> None:
 
 def matmul_prepared(workspace, T: int, K: int, Wq, sw, W16, out=None) -> torch.Tensor:
     """Matmul steps on a prepared workspace (see int8mm_matmul_prepared)."""
-    _need(Wq, torch.int8, 2, "Wq")
-    N = Wq.shape[0]
+    _need(Wq, torch.int8, 1, "Wq")
+    _need(sw, torch.float32, 1, "sw")
+    N = sw.shape[0]
+    if Wq.numel() != weight_bytes(K, N):
+        raise ValueError("Wq does not match K and N")
     Y = out if out is not None else torch.empty((T, N), dtype=torch.float16, device=Wq.device)
     _check(_lib.int8mm_matmul_prepared(_ptr(workspace), workspace.numel(), T, K, _ptr(Wq),
                                        _ptr(sw), _ptr(W16), N, _ptr(Y), _stream()),

@@ -38,6 +38,9 @@ struct Workspace {
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Bytes of the converted weight: int8 [N,K] row-major (K contiguous).
+inline int64_t wq_bytes(int64_t K, int64_t N) { return K * N; }
+
 // Layout of the workspace for (T, K) at `base` (base may be NULL to size it).
 Workspace carve_workspace(void* base, int64_t T, int64_t K);
 

@@ -91,6 +91,14 @@ int int8_mixed_matmul_workspace_size(int64_t T, int64_t K, int64_t N, size_t* by
     return INT8MM_OK;
 }
 
+int int8_quantize_weight_size(int64_t K, int64_t N, size_t* bytes) {
+    if (!bytes) return INT8MM_E_NULL;
+    int st = check_shape(1, K, N);
+    if (st) return st;
+    *bytes = (size_t)wq_bytes(K, N);
+    return INT8MM_OK;
+}
+
 int int8_quantize_weight(const void* W16, int64_t K, int64_t N, int8_t* Wq, float* sw,
                          void* stream) {
     if (!W16 || !Wq || !sw) return INT8MM_E_NULL;

@@ -27,7 +27,7 @@ def header_functions():
 def test_header_lists_entry_points():
     names = header_functions()
     assert "int8_mixed_matmul" in names and "int8_quantize_weight" in names
-    assert len(names) == 7, names
+    assert len(names) == 8, names
 
 
 def test_exports_every_declared_symbol(mm):
@@ -81,6 +81,14 @@ def call_mm(lib, X=FAKE, T=16, K=64, Wq=FAKE, sw=FAKE, W16=FAKE, N=48, tau=6.0, 
 ])
 def test_matmul_validation(mm, kw, status):
     assert call_mm(mm.lib(), **kw) == status
+
+
+def test_weight_bytes(mm):
+    assert mm.weight_bytes(64, 48) == 48 * 64
+    assert mm.weight_bytes(80, 200) == 200 * 80
+    assert mm.weight_bytes(12288, 49152) == 12288 * 49152
+    with pytest.raises(mm.Int8mmError):
+        mm.weight_bytes(60, 48)
 
 
 def test_largest_k_accepted_by_shape_check(mm):

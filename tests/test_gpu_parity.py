@@ -16,6 +16,7 @@ import torch
 
 import oracle
 import synth
+from tests.layout import padding_is_zero, unblock_weight
 
 pytestmark = pytest.mark.gpu
 
@@ -60,7 +61,9 @@ def run_case(mm, name, X, W, tau, rows=None, plain_too=True):
     say(f"[case] {name}: GPU done")
 
     Wq_o, sw_o = oracle.quantize_weight(W)
-    assert np.array_equal(Wq.cpu().numpy(), Wq_o), f"{name}: Wq differs"
+    wq_gpu = Wq.cpu().numpy()
+    assert np.array_equal(unblock_weight(wq_gpu, K, N), Wq_o), f"{name}: Wq differs"
+    assert padding_is_zero(wq_gpu, K, N), f"{name}: Wq padding not zero"
     assert np.array_equal(sw.cpu().numpy(), sw_o), f"{name}: s_w differs"
 
     flag = oracle.detect(X, tau)
