@@ -10,24 +10,32 @@
 // At decode sizes the work is a stream of the int8 weight (K*N bytes) past
 // a tiny activation, so the kernel is bound by HBM bandwidth; the design
 // keeps that stream going from the first instruction to the last:
-//   - each wave owns whole 16-row blocks of Wq over all of K (one block per
-//     wave at the projection sizes), so the streaming loop has no barrier
-//     and no cross-wave reduction; waves drift apart and overlap freely;
-//   - every wave first issues the loads of its first 16 KB weight chunk,
-//     then its workgroup recomputes the activation side from X
-//     (T*K fp16, cache resident): a thread owns whole 8-column chunks across
-//     all T rows, so the outlier flags of its columns need no exchange; row
-//     absmax by wave shuffles and LDS; ascending outlier indices by a
-//     popcount prefix scan; Xq to LDS;
+//   - one workgroup per compute unit owns bpw whole 16-row blocks of Wq
+//     (bpw = ceil(blocks / CUs), so the weight spreads evenly over the chip);
+//     the blocks are cut into 16 KB chunks (16 rows x 1024 k) that the eight
+//     waves take from an LDS counter as they go, so waves that the SIMD
+//     arbitration favours simply take more chunks and all of them finish
+//     together; each chunk's int32 partial sums are added into LDS (exact and
+//     order independent);
+//   - every wave first issues the loads of its first chunk, then the
+//     workgroup recomputes the activation side from X (T*K fp16, cache
+//     resident): a thread owns whole 8-column pieces across all T rows, so
+//     the outlier flags of its columns need no exchange; row absmax by a
+//     transposed butterfly and LDS; ascending outlier indices by a popcount
+//     prefix scan; Xq to LDS;
 //   - Wq goes from global memory straight into registers as the A operand of
 //     v_mfma_i32_16x16x64_i8 (16 weight rows x 64 k), through a ring of three
-//     chunks of 16 loads; the B operand (the T activation rows as columns,
-//     zero padded) is read from LDS per k-step;
-//   - at the end of a block the wave dequantizes its int32 sums, adds the
-//     fp16 outlier product in fp32 and rounds Y to fp16 once.
+//     chunks of 16 loads per wave; the B operand (the T activation rows as
+//     columns, zero padded) is read from LDS per k-step;
+//   - after the stream the workgroup dequantizes the int32 sums, adds the
+//     fp16 outlier product in fp32 (W16 values of the first outliers were
+//     fetched during the stream) and rounds Y to fp16 once.
 // Limits (host checks them; other shapes use the general kernels):
 // T <= 16, K in {4096, 8192}, T*K <= 65536.
 #include "common.hpp"
+
+#include <algorithm>
+#include <atomic>
 
 // Quantization must round x * r and any following add separately, exactly
 // like the definition; no multiply-add contraction in this file.
@@ -44,6 +52,8 @@ constexpr int kMaxT = 16;
 constexpr int kMaxK = 8192;
 constexpr int kMaxXK = 65536;          // T*K bytes of Xq kept in LDS
 constexpr int kMaxOutliersLds = 256;   // outlier values cached in LDS
+constexpr int kMaxBpw = 8;             // 16-row blocks per workgroup
+constexpr int kW16Cache = 16;          // outliers whose W16 values are staged in LDS
 
 __device__ inline float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
 
@@ -56,6 +66,7 @@ struct DecodeArgs {
     float tau;
     uint32_t tau16;         // bits of the smallest fp16 >= tau (0x7C00 if none finite)
     int T, K, N;
+    int bpw;                // 16-row blocks per workgroup (1..8)
     // optional debug outputs (NULL to skip); workgroup 0 writes all but acc
     int32_t* dbg_count;
     int32_t* dbg_idx;
@@ -70,11 +81,16 @@ struct Smem {
     int8_t xq[kMaxXK + kMaxT * 16];
     int32_t idx[kMaxK];                        // outlier dims, ascending
     float xo[kMaxT * kMaxOutliersLds];         // X values of the first outliers
+    int32_t acc[kMaxBpw][kRows][16];           // int32 sums [block][row][t]
+    uint32_t w16o[kW16Cache][kMaxBpw * kRows / 2];   // W16[idx_j, n] pairs of the rows
+    float sw[kMaxBpw * kRows];                 // s_w of the rows
     float wmax[kWaves][kMaxT];
     float sx[kMaxT];
     float rx[kMaxT];                           // 127 / s_x (0 when s_x = 0)
     int32_t wtot[kWaves * 2];
+    int32_t next;                              // next chunk to hand out
 };
+static_assert(sizeof(Smem::acc) == kThreads * 16, "one 16-byte clear per thread");
 
 // Packed unsigned max of two pairs of 16-bit lanes.
 __device__ inline uint32_t pk_max_u16(uint32_t a, uint32_t b) {
@@ -102,29 +118,62 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) Smem sm;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // wave-uniform (a scalar), so the chunk loop below is uniform control flow
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int T = a.T, K = a.K, N = a.N;
     const int ldx = K + 16;                    // LDS row stride of Xq
     const int nblocks = (N + kRows - 1) / kRows;
-    const int gwave = blockIdx.x * kWaves + wave;   // this wave's blocks: gwave, +nwaves, ...
-    const int nwaves = gridDim.x * kWaves;
+    // this workgroup's weight rows n0 .. n0 + rows - 1 (rows past N are read
+    // as row N-1 and never stored); chunk id -> block id / CPB, k-chunk id % CPB
+    const int b0 = blockIdx.x * a.bpw;
+    const int nbw = a.bpw < nblocks - b0 ? a.bpw : nblocks - b0;
+    const int rows = nbw * kRows;
+    const int n0 = b0 * kRows;
+    const int total = nbw * CPB;
 
-    // Load i of chunk c of block blk: lane l holds weight row blk*16 + l%16
-    // and bytes c*1024 + 64 i + 16*(l/16) .. +16.
+    // Load i of a chunk: lane l holds weight row n0 + 16 (id / CPB) + l % 16
+    // and bytes 1024 (id % CPB) + 64 i + 16 (l / 16) .. +16.  Ids past the end
+    // read the first kilobyte of Wq on every lane instead (one line per
+    // load, never used): loads stay unconditional, so the wait counts stay
+    // exact.
     const int kl = (lane >> 4) * 16;
-    // Rows past N re-read row N-1 (their outputs are never stored); loads
-    // are unconditional so the wait counts stay exact.
-    auto issue = [&](int blk, int c, v4i (&buf)[kLoads]) {
-        const int n = blk * kRows + (lane & 15);
-        const int8_t* p = a.wq + (int64_t)(n < N ? n : N - 1) * K + c * kChunkK + kl;
+    // loads lo .. hi-1 of chunk id into buf (lo and hi are constants)
+    auto issue_part = [&](int id, v4i (&buf)[kLoads], int lo, int hi) {
+        const int n = n0 + (id / CPB) * kRows + (lane & 15);
+        const int64_t off =
+            id < total ? (int64_t)(n < N ? n : N - 1) * K + (id % CPB) * kChunkK + kl : 0;
+        const int8_t* p = a.wq + off;
 #pragma unroll
-        for (int i = 0; i < kLoads; ++i) buf[i] = *reinterpret_cast<const v4i*>(p + i * 64);
+        for (int i = 0; i < kLoads; ++i)
+            if (i >= lo && i < hi) buf[i] = *reinterpret_cast<const v4i*>(p + i * 64);
     };
+    auto issue = [&](int id, v4i (&buf)[kLoads]) { issue_part(id, buf, 0, kLoads); };
 
-    // The prologue's X loads go out first and their first use (the column
-    // maxima) comes before any weight load is issued: vector-memory counters
-    // retire in order, so a later wait on X would also wait for weight data.
-    // Rows t >= T re-read row T-1: a repeated row changes neither the
+    // s_w of the rows, one float4 per thread (n0 and N are multiples of 8,
+    // so a group of 4 rows is all in range or read as the last 4)
+    float4 sw4;
+    {
+        const int n = tid * 4 < rows && n0 + tid * 4 < N ? n0 + tid * 4 : N - 4;
+        sw4 = *reinterpret_cast<const float4*>(a.sw + n);
+    }
+    reinterpret_cast<uint4*>(&sm.acc[0][0][0])[tid] = make_uint4(0u, 0u, 0u, 0u);
+    if (tid == 0) sm.next = 3 * kWaves;   // chunks 0 .. 23 go out statically
+
+    // wave w starts with chunks w, w + 8 and w + 16; later ones come from the
+    // LDS counter, so each wave's ids increase in the order it uses them.
+    // X is loaded before any weight: vector-memory counters retire in order,
+    // so a wait on X would also wait for weight loads issued before it.  The
+    // first chunk then goes out in four parts spread over the activation
+    // work: the memory pipe takes a CU's requests only as fast as it returns
+    // data, so a wave issuing all of it at once would stall there instead of
+    // computing (issuing more of the weight earlier, before X or from the
+    // second chunk, measured slower).  Scheduling barriers keep each part
+    // where it is.
+    constexpr int G1 = kLoads / 4, G2 = kLoads / 2, G3 = 3 * kLoads / 4;
+    v4i ring[3][kLoads];
+    int id0 = wave, id1 = wave + kWaves, id2 = wave + 2 * kWaves;
+
+    // X: rows t >= T re-read row T-1: a repeated row changes neither the
     // column maxima nor anything used later (rows >= T of Xq and xo are never
     // read), and unconditional loads keep the wait counts exact.
     uint4 xr[CPT][TMAX];
@@ -153,15 +202,13 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
         for (int e = 0; e < 8; ++e)
             fm[j] |= (((cm[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu) >= a.tau16 ? 1u : 0u) << e;
     }
-    // the flags must be final (so X has arrived) before the first weight
-    // load is issued: an empty asm that consumes them and orders memory
+    // the flags must be final (so X has arrived) before more weight loads
+    // are issued: an empty asm that consumes them and orders memory
 #pragma unroll
     for (int j = 0; j < CPT; ++j) asm volatile("" ::"v"(fm[j]) : "memory");
-    // Ring loads are unconditional (a wave without a block re-reads the
-    // clamped last row; nothing uses it) so the wait analysis sees one path.
-    v4i ring[3][kLoads];
-    int blk = gwave;
-    issue(blk, 0, ring[0]);
+    if (tid * 4 < rows) *reinterpret_cast<float4*>(&sm.sw[tid * 4]) = sw4;
+    issue_part(id0, ring[0], 0, G1);
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- activation side, recomputed per workgroup, from registers.
     // Row absmax over the non-outlier columns: mask the outlier halves, then
@@ -183,15 +230,34 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
         const uint32_t mh = (m & 0xFFFFu) > (m >> 16) ? (m & 0xFFFFu) : (m >> 16);
         rmax[t] = h2f((uint16_t)mh);
     }
+    // Row maxima over the wave by a transposed butterfly: each exchange at
+    // distance d = 32, 16, ... halves the rows a lane carries (it keeps the
+    // half picked by its lane bit d and sends the other half); plain
+    // exchanges then finish the one row left.  Lane l ends with the maximum
+    // of row l / (64 / TMAX): log2(64) + TMAX - 1 exchanges instead of
+    // log2(64) per row.
+    {
+        float v[TMAX];
 #pragma unroll
-    for (int t = 0; t < TMAX; ++t) {
-        if (t < T) {
-            float v = rmax[t];
+        for (int t = 0; t < TMAX; ++t) v[t] = rmax[t];
 #pragma unroll
-            for (int d = 32; d >= 1; d >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, d));
-            if (lane == 0) sm.wmax[wave][t] = v;
+        for (int cnt = TMAX, d = 32; cnt > 1; cnt >>= 1, d >>= 1) {
+            const bool up = (lane & d) != 0;
+#pragma unroll
+            for (int i = 0; i < cnt / 2; ++i) {
+                const float send = up ? v[i] : v[i + cnt / 2];
+                const float keep = up ? v[i + cnt / 2] : v[i];
+                v[i] = __builtin_fmaxf(keep, __shfl_xor(send, d));
+            }
         }
+#pragma unroll
+        for (int d = 32 / TMAX; d >= 1; d >>= 1) v[0] = __builtin_fmaxf(v[0], __shfl_xor(v[0], d));
+        const int r = lane / (64 / TMAX);
+        if (lane % (64 / TMAX) == 0 && r < T) sm.wmax[wave][r] = v[0];
     }
+    __builtin_amdgcn_sched_barrier(0);
+    issue_part(id0, ring[0], G1, G2);
+    __builtin_amdgcn_sched_barrier(0);
     // positions of the outliers: prefix count over the chunk order
     int pc[CPT];
 #pragma unroll
@@ -207,11 +273,15 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
         pc[j] = incl - cnt;
     }
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    issue_part(id0, ring[0], G2, G3);
+    __builtin_amdgcn_sched_barrier(0);
     if (tid < T) {
         float v = sm.wmax[0][tid];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w) v = __builtin_fmaxf(v, sm.wmax[w][tid]);
         sm.sx[tid] = v;
+        sm.rx[tid] = v > 0.0f ? 127.0f / v : 0.0f;   // IEEE fp32 divide
     }
     int o = 0;
 #pragma unroll
@@ -224,22 +294,22 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
         }
         pc[j] += before;
     }
-    __syncthreads();   // sx ready
-    if (tid < T) {
-        const float sxt = sm.sx[tid];
-        sm.rx[tid] = sxt > 0.0f ? 127.0f / sxt : 0.0f;   // IEEE fp32 divide
-    }
-    __syncthreads();   // rx ready
+    __syncthreads();   // sx, rx ready
+    __builtin_amdgcn_sched_barrier(0);
+    issue_part(id0, ring[0], G3, kLoads);
+    __builtin_amdgcn_sched_barrier(0);
     // Quantize the owned columns into LDS and gather the outliers.
     // q = rint(x * r) by the 1.5 * 2^23 addition: for |p| < 2^22, p + 1.5*2^23
     // rounds p to the nearest integer (ties to even) and the low byte of the
     // result's bit pattern is that integer as int8.  |x| <= s_x makes
     // |p| <= 127 * (1 + 2^-23), so q is within [-127, 127] without a clamp.
-    // The multiply and the add stay separate roundings (no contraction).
+    // The product and the add stay separate roundings: p = fma(x, r, +0) is
+    // the fp32 product x * r rounded once (one mixed fp16/fp32 instruction),
+    // then the add rounds again.  Bytes are packed with v_perm.
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
         const int c = tid + kThreads * j;
-        // byte mask that zeroes the outlier columns of the chunk
+        // byte mask that zeroes the outlier columns of the piece
         uint32_t keep[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -250,33 +320,21 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
         }
 #pragma unroll
         for (int t = 0; t < TMAX; ++t) {
-            {
-                const float rr = t < T ? sm.rx[t] : 0.0f;
-                uint32_t packed[2] = {0u, 0u};
+            const float rr = t < T ? sm.rx[t] : 0.0f;
+            uint32_t f[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float p = __fmul_rn(chunk_val(xr[j][t], e), rr);
-                    const uint32_t bits = __builtin_bit_cast(uint32_t, __fadd_rn(p, 12582912.0f));
-                    packed[e >> 2] |= (bits & 0xFFu) << ((e & 3) * 8);
-                }
-                packed[0] &= keep[0];
-                packed[1] &= keep[1];
-                *reinterpret_cast<uint2*>(&sm.xq[t * ldx + c * 8]) = make_uint2(packed[0], packed[1]);
-                if (blockIdx.x == 0 && a.dbg_xq && t < T)
-                    *reinterpret_cast<uint2*>(a.dbg_xq + (int64_t)t * K + c * 8) =
-                        make_uint2(packed[0], packed[1]);
-                if (fm[j]) {
-                    int pos = pc[j];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        if ((fm[j] >> e) & 1u) {
-                            if (pos < kMaxOutliersLds)
-                                sm.xo[t * kMaxOutliersLds + pos] = chunk_val(xr[j][t], e);
-                            ++pos;
-                        }
-                    }
-                }
+            for (int e = 0; e < 8; ++e) {
+                const float p = __builtin_fmaf(chunk_val(xr[j][t], e), rr, 0.0f);
+                f[e] = __builtin_bit_cast(uint32_t, __fadd_rn(p, 12582912.0f));
             }
+            uint32_t packed[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t lo = __builtin_amdgcn_perm(f[4 * h + 1], f[4 * h], 0x0c0c0400u);
+                const uint32_t hi = __builtin_amdgcn_perm(f[4 * h + 3], f[4 * h + 2], 0x0c0c0400u);
+                packed[h] = __builtin_amdgcn_perm(hi, lo, 0x05040100u) & keep[h];
+            }
+            *reinterpret_cast<uint2*>(&sm.xq[t * ldx + c * 8]) = make_uint2(packed[0], packed[1]);
         }
         if (fm[j]) {
             int pos = pc[j];
@@ -285,6 +343,11 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
                 if ((fm[j] >> e) & 1u) {
                     sm.idx[pos] = c * 8 + e;
                     if (blockIdx.x == 0 && a.dbg_idx) a.dbg_idx[pos] = c * 8 + e;
+                    if (pos < kMaxOutliersLds) {
+#pragma unroll
+                        for (int t = 0; t < TMAX; ++t)
+                            sm.xo[t * kMaxOutliersLds + pos] = chunk_val(xr[j][t], e);
+                    }
                     ++pos;
                 }
             }
@@ -292,57 +355,96 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
     }
     if (blockIdx.x == 0 && tid == 0 && a.dbg_count) a.dbg_count[0] = o;
     if (blockIdx.x == 0 && a.dbg_sx && tid < T) a.dbg_sx[tid] = sm.sx[tid];
-    issue(blk, 1, ring[1]);
-    issue(blk, 2, ring[2]);
     __syncthreads();   // Xq, idx, xo ready
+    if (blockIdx.x == 0 && a.dbg_xq) {
+        for (int i = tid; i < T * (K / 8); i += kThreads) {
+            const int t = i / (K / 8), c8 = (i % (K / 8)) * 8;
+            *reinterpret_cast<uint2*>(a.dbg_xq + (int64_t)t * K + c8) =
+                *reinterpret_cast<const uint2*>(&sm.xq[t * ldx + c8]);
+        }
+    }
+    // W16 values of the first outliers for the workgroup's rows, fetched now
+    // (idx is complete only after the barrier above) so that the end of the
+    // kernel does not wait on them: thread -> outlier slot tid / 64 + 8 h,
+    // row pair 2 (tid % 64); slots past o read the first dword of W16 (never
+    // used).
+    uint32_t w16v[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int j = (tid >> 6) + 8 * h;
+        const int r = 2 * (tid & 63);
+        const int n = r < rows && n0 + r < N ? n0 + r : 0;
+        const int64_t off = j < o ? (int64_t)sm.idx[j] * N + n : 0;
+        w16v[h] = *reinterpret_cast<const uint32_t*>(a.w16 + off);
+    }
+    issue(id1, ring[1]);
+    issue(id2, ring[2]);
 
-    // ---- stream this wave's blocks.  Per block the chunk loop is fully
-    // unrolled with a compile-time ring slot, so the wait before each chunk
-    // leaves the two younger chunks in flight; the next block's first chunks
-    // go out after the epilogue (at the projection sizes a wave has exactly
-    // one block).
+    // ---- stream the workgroup's chunks.  The loop body is unrolled over the
+    // three ring slots (compile-time register indices) and every slot is
+    // re-issued on every pass, with one exit test at the end: each path into
+    // a slot's use then has the two younger slots' loads behind it, so the
+    // wait before a chunk leaves them in flight.  A slot whose id is past the
+    // end skips its MFMAs (a uniform branch with no loads inside).  A chunk's
+    // next id is taken from the LDS counter before its MFMAs, used after them.
     const int tcol = lane & 15;                         // B column = activation row t
     const int8_t* xrow = &sm.xq[(tcol < T ? tcol : 0) * ldx + kl];
-    auto process_block = [&](int b) {
+    // 16x16 accumulator layout: lane holds column lane%16 (t) and, in
+    // register v, row 4*(lane/16) + v of the block
+    int32_t* accrow = &sm.acc[0][4 * (lane >> 4)][tcol];
+    auto consume = [&](int id, v4i (&buf)[kLoads]) -> int {
+        if (id >= total) return total;
+        int nid = 0;
+        if (lane == 0) nid = atomicAdd(&sm.next, 1);
+        const int8_t* xk = xrow + (id % CPB) * kChunkK;
         v4i acc = {0, 0, 0, 0};
 #pragma unroll
-        for (int c = 0; c < CPB; ++c) {
-            v4i(&buf)[kLoads] = ring[c % 3];
-#pragma unroll
-            for (int i = 0; i < kLoads; ++i) {
-                const v4i xb = tcol < T ? *reinterpret_cast<const v4i*>(xrow + c * kChunkK + i * 64)
-                                        : v4i{0, 0, 0, 0};
-                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(buf[i], xb, acc, 0, 0, 0);
-            }
-            if (c + 3 < CPB) issue(b, c + 3, buf);
+        for (int i = 0; i < kLoads; ++i) {
+            const v4i xb = tcol < T ? *reinterpret_cast<const v4i*>(xk + i * 64) : v4i{0, 0, 0, 0};
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(buf[i], xb, acc, 0, 0, 0);
         }
-        // 16x16 accumulator layout: lane holds column lane%16 (t) and, in
-        // register v, row 4*(lane/16) + v of the block
-        if (tcol < T) {
+        int32_t* d = accrow + (id / CPB) * (kRows * 16);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int n = b * kRows + 4 * (lane >> 4) + v;
-                if (n < N) {
-                    if (a.dbg_acc) a.dbg_acc[(int64_t)tcol * N + n] = acc[v];
-                    float y = (float)acc[v] * sm.sx[tcol] * (a.sw[n] * (1.0f / 16129.0f));
-                    for (int jj = 0; jj < o; ++jj) {
-                        const int k = sm.idx[jj];
-                        const float xv = jj < kMaxOutliersLds ? sm.xo[tcol * kMaxOutliersLds + jj]
-                                                              : h2f(a.x[(int64_t)tcol * K + k]);
-                        y += xv * (float)a.w16[(int64_t)k * N + n];
-                    }
-                    a.y[(int64_t)tcol * N + n] = (_Float16)y;
-                }
-            }
-        }
+        for (int v = 0; v < 4; ++v) atomicAdd(d + v * 16, acc[v]);
+        return __builtin_amdgcn_readfirstlane(nid);
     };
-    // first block in straight-line code (at the projection sizes the only one)
-    if (blk < nblocks) process_block(blk);
-    for (blk += nwaves; blk < nblocks; blk += nwaves) {
-        issue(blk, 0, ring[0]);
-        issue(blk, 1, ring[1]);
-        issue(blk, 2, ring[2]);
-        process_block(blk);
+    // ids increase in the order the slots are used (0, 1, 2, 0, ...), so once
+    // slot 0's next id is past the end every pending one is
+    if (id0 < total) {
+        do {
+            id0 = consume(id0, ring[0]);
+            issue(id0, ring[0]);
+            id1 = consume(id1, ring[1]);
+            issue(id1, ring[1]);
+            id2 = consume(id2, ring[2]);
+            issue(id2, ring[2]);
+        } while (id0 < total);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) sm.w16o[(tid >> 6) + 8 * h][tid & 63] = w16v[h];
+    __syncthreads();   // sums and W16 values complete
+
+    // ---- epilogue: y = acc * s_x * s_w / 127^2 + sum_j X[t, idx_j] W16[idx_j, n],
+    // one fp16 rounding; consecutive threads take consecutive rows n.
+    const int oc = o < kW16Cache ? o : kW16Cache;
+    for (int e = tid; e < rows * T; e += kThreads) {
+        const int r = e % rows, t = e / rows;
+        const int n = n0 + r;
+        if (n >= N) continue;
+        const int32_t acc = sm.acc[r >> 4][r & 15][t];
+        if (a.dbg_acc) a.dbg_acc[(int64_t)t * N + n] = acc;
+        float y = (float)acc * sm.sx[t] * (sm.sw[r] * (1.0f / 16129.0f));
+        for (int j = 0; j < oc; ++j) {
+            const uint32_t pr = sm.w16o[j][r >> 1];
+            y += sm.xo[t * kMaxOutliersLds + j] * h2f((uint16_t)((r & 1) ? pr >> 16 : pr & 0xFFFFu));
+        }
+        for (int j = oc; j < o; ++j) {
+            const int k = sm.idx[j];
+            const float xv = j < kMaxOutliersLds ? sm.xo[t * kMaxOutliersLds + j]
+                                                 : h2f(a.x[(int64_t)t * K + k]);
+            y += xv * (float)a.w16[(int64_t)k * N + n];
+        }
+        a.y[(int64_t)t * N + n] = (_Float16)y;
     }
 }
 
@@ -367,14 +469,37 @@ bool decode_path_supported(int64_t T, int64_t K, int64_t N) {
     return T >= 1 && T <= kMaxT && (K == 4096 || K == 8192) && T * K <= kMaxXK;
 }
 
+// Compute units of the current device, cached per device (an immutable
+// property; concurrent first calls store the same value).
+static int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        return 256;
+    if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
 hipError_t launch_decode(const _Float16* X, int64_t T, int64_t K, const int8_t* Wq,
                          const float* sw, const _Float16* W16, int64_t N, float tau,
                          _Float16* Y, int32_t* dbg_count, int32_t* dbg_idx, int8_t* dbg_xq,
                          float* dbg_sx, int32_t* dbg_acc, hipStream_t stream) {
-    DecodeArgs a{reinterpret_cast<const uint16_t*>(X), Wq, sw, W16, Y, tau, tau_to_f16_ceil(tau),
-                 (int)T, (int)K, (int)N, dbg_count, dbg_idx, dbg_xq, dbg_sx, dbg_acc};
+    // One workgroup per compute unit (the LDS footprint allows no more), each
+    // owning bpw whole 16-row blocks: bpw = ceil(blocks / CUs) spreads the
+    // weight evenly (N = 28672: 1792 blocks = 256 CUs x 7); past 8 blocks per
+    // CU the grid grows instead.
     const int64_t nblocks = ceil_div(N, kRows);
-    const unsigned grid = (unsigned)ceil_div(nblocks, kWaves);   // one 16-row block per wave
+    const int bpw = (int)std::min<int64_t>(kMaxBpw, std::max<int64_t>(1, ceil_div(nblocks, device_cus())));
+    DecodeArgs a{reinterpret_cast<const uint16_t*>(X), Wq, sw, W16, Y, tau, tau_to_f16_ceil(tau),
+                 (int)T, (int)K, (int)N, bpw, dbg_count, dbg_idx, dbg_xq, dbg_sx, dbg_acc};
+    const unsigned grid = (unsigned)ceil_div(nblocks, bpw);
     if (K == 4096)
         hipLaunchKernelGGL(k_decode<4>, dim3(grid), dim3(kThreads), 0, stream, a);
     else if (K == 8192)
