@@ -69,8 +69,10 @@ class Oracle:
         lib.oracle_quantize_rows.argtypes = [vp, i64, i64, vp, vp, i64, vp, vp]
         lib.oracle_int8_gemm.argtypes = [vp, i64, i64, vp, i64, vp, c_int]
         lib.oracle_int8_gemm.restype = i64
-        lib.oracle_output.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp, vp,
-                                      c_int]
+        lib.oracle_output.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp,
+                                      vp, c_int]
+        lib.oracle_dequant_weight.argtypes = [ctypes.c_int8, f32]
+        lib.oracle_dequant_weight.restype = ctypes.c_uint16
         lib.oracle_mixed_matmul.argtypes = [vp, i64, i64, vp, vp, vp, i64, f32, vp, i64,
                                             vp, vp, vp, vp, vp, vp, vp, c_int]
         lib.oracle_mixed_matmul.restype = i64
@@ -133,11 +135,22 @@ class Oracle:
             raise OverflowError(f"{bad} accumulators do not fit int32")
         return acc
 
-    def output(self, acc, sx, sw, X, W16, idx, rows=None, threads: int = 0):
-        """(Y fp16 [M,N], Y64 float64 [M,N] before the final rounding)."""
+    def dequant_weight(self, q: int, sw: float) -> int:
+        """fp16 bits of the weight value recovered from Int8 code q and
+        column scale sw (memory-halved variant)."""
+        return int(self.lib.oracle_dequant_weight(int(q), float(sw)))
+
+    def output(self, acc, sx, sw, X, W16, idx, rows=None, threads: int = 0, Wq=None):
+        """(Y fp16 [M,N], Y64 float64 [M,N] before the final rounding).
+        W16 None: memory-halved variant, outlier rows recovered from Wq."""
         X = _f16(X)
-        W16 = _f16(W16)
-        K, N = W16.shape
+        K = X.shape[1]
+        if W16 is not None:
+            W16 = _f16(W16)
+            N = W16.shape[1]
+        else:
+            Wq = np.ascontiguousarray(Wq, np.int8)
+            N = Wq.shape[0]
         acc = np.ascontiguousarray(acc, np.int32)
         M = acc.shape[0]
         idx = np.ascontiguousarray(idx, np.int32)
@@ -145,18 +158,21 @@ class Oracle:
         Y = np.empty((M, N), np.float16)
         Y64 = np.empty((M, N), np.float64)
         self.lib.oracle_output(_p(acc), _p(np.ascontiguousarray(sx, np.float32)),
-                               _p(np.ascontiguousarray(sw, np.float32)), _p(X), _p(W16), _p(r),
-                               M, K, N, _p(idx), len(idx), _p(Y), _p(Y64), threads)
+                               _p(np.ascontiguousarray(sw, np.float32)), _p(X), _p(W16),
+                               _p(Wq if W16 is None else None), _p(r), M, K, N, _p(idx), len(idx),
+                               _p(Y), _p(Y64), threads)
         return Y, Y64
 
     def mixed_matmul(self, X, Wq, sw, W16, tau: float, rows=None, threads: int = 0):
         """The whole method.  Returns a dict with flag, idx, o, xq, sx, acc,
-        Y, Y64 (xq/sx/acc/Y/Y64 for the sampled rows when `rows` is given)."""
+        Y, Y64 (xq/sx/acc/Y/Y64 for the sampled rows when `rows` is given).
+        W16 None: the memory-halved variant."""
         X = _f16(X)
-        W16 = _f16(W16)
         T, K = X.shape
-        N = W16.shape[1]
         Wq = np.ascontiguousarray(Wq, np.int8)
+        if W16 is not None:
+            W16 = _f16(W16)
+        N = Wq.shape[0]
         sw = np.ascontiguousarray(sw, np.float32)
         r = None if rows is None else np.ascontiguousarray(rows, np.int64)
         M = T if r is None else len(r)

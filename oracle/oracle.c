@@ -31,7 +31,12 @@
  *   - dequantization: y8 = acc * s_x[t] * s_w[n] / 127^2 (fp64 here);
  *   - the 16-bit part multiplies the fp16 values X[t,k] and W[k,n] of the
  *     outlier dimensions exactly (fp64 here);
- *   - Y = fp16(y8 + y16), rounded once, to nearest even.
+ *   - Y = fp16(y8 + y16), rounded once, to nearest even;
+ *   - memory-halved variant (no 16-bit weight kept, [A]: inference memory
+ *     "cut by half"): the outlier rows of W are recovered from the Int8
+ *     weight, W^[k,n] = fp16(fp32(q[n,k] * fp32(s_w[n] / 127))) (an IEEE fp32
+ *     divide, one fp32 multiply, one rounding to fp16, each to nearest even),
+ *     and the 16-bit part multiplies X[t,k] by W^[k,n] instead.
  *
  * Parity pins: every function below is checked in tests/ against values
  * that do not come from this file (hand-derived examples, closed forms,
@@ -288,11 +293,23 @@ int64_t oracle_int8_gemm(const int8_t* Xq, int64_t M, int64_t K, const int8_t* W
  *   y16 = sum_{j<o} X[t,idx_j] * W[idx_j,n]       (t = rows[m] or m)
  *   Y   = fp16(y8 + y16)
  * all in fp64 (fp16 x fp16 products are exact there).  Y64, when given,
- * receives y8 + y16 before the final rounding. */
+ * receives y8 + y16 before the final rounding.  Without W16 (NULL), the
+ * memory-halved variant: W[idx_j,n] is the fp16 value recovered from the
+ * Int8 weight, see oracle_dequant_weight. */
 typedef struct {
     const int32_t* acc; const float* sx; const float* sw; const uint16_t* X; const uint16_t* W16;
-    const int64_t* rows; int64_t M, K, N; const int32_t* idx; int64_t o; uint16_t* Y; double* Y64;
+    const int8_t* Wq; const int64_t* rows; int64_t M, K, N; const int32_t* idx; int64_t o;
+    uint16_t* Y; double* Y64;
 } out_ctx;
+
+/* The 16-bit value of weight element (k, n) recovered from its Int8 code
+ * q = Wq[n,k] and column scale s_w[n]: fp16(fp32(q * fp32(s_w / 127))),
+ * each step rounded to nearest even (the divide an IEEE fp32 divide). */
+uint16_t oracle_dequant_weight(int8_t q, float sw) {
+    const float d = sw / 127.0f;
+    const float v = (float)q * d;
+    return oh_encode((double)v);
+}
 
 static void out_span(void* p, int64_t lo, int64_t hi) {
     out_ctx* c = (out_ctx*)p;
@@ -303,7 +320,9 @@ static void out_span(void* p, int64_t lo, int64_t hi) {
             double y16 = 0.0;
             for (int64_t j = 0; j < c->o; ++j) {
                 int64_t k = c->idx[j];
-                y16 += oh_decode(c->X[t * c->K + k]) * oh_decode(c->W16[k * c->N + n]);
+                const uint16_t w = c->W16 ? c->W16[k * c->N + n]
+                                          : oracle_dequant_weight(c->Wq[n * c->K + k], c->sw[n]);
+                y16 += oh_decode(c->X[t * c->K + k]) * oh_decode(w);
             }
             double y = y8 + y16;
             if (c->Y64) c->Y64[m * c->N + n] = y;
@@ -313,17 +332,18 @@ static void out_span(void* p, int64_t lo, int64_t hi) {
 }
 
 void oracle_output(const int32_t* acc, const float* sx, const float* sw, const uint16_t* X,
-                   const uint16_t* W16, const int64_t* rows, int64_t M, int64_t K, int64_t N,
-                   const int32_t* idx, int64_t o, uint16_t* Y, double* Y64, int nthreads) {
-    out_ctx c = {acc, sx, sw, X, W16, rows, M, K, N, idx, o, Y, Y64};
+                   const uint16_t* W16, const int8_t* Wq, const int64_t* rows, int64_t M,
+                   int64_t K, int64_t N, const int32_t* idx, int64_t o, uint16_t* Y, double* Y64,
+                   int nthreads) {
+    out_ctx c = {acc, sx, sw, X, W16, Wq, rows, M, K, N, idx, o, Y, Y64};
     o_parallel(M, nthreads, out_span, &c);
 }
 
 /* ----------------------------------------------------- the whole method */
 
 /* All steps in the pages' order, on a quantized weight (Wq, s_w) and the
- * 16-bit weight W16: detect -> isolate -> quantize rows -> int8 matmul ->
- * dequantize + 16-bit outlier matmul.  Detection always looks at all T rows
+ * 16-bit weight W16 (NULL: the memory-halved variant): detect -> isolate ->
+ * quantize rows -> int8 matmul -> dequantize + 16-bit outlier matmul.  Detection always looks at all T rows
  * of X; the other steps run on the M rows listed in `rows` (all when NULL).
  * Outputs (any but Y may be NULL): flag[K], idx[K], Xq[M,K], sx[M],
  * acc[M,N], Y[M,N], Y64[M,N].  Returns o, or -1 on allocation failure,
@@ -345,7 +365,7 @@ int64_t oracle_mixed_matmul(const uint16_t* X, int64_t T, int64_t K, const int8_
         o = oracle_compact(flag, K, idx);
         oracle_quantize_rows(X, T, K, flag, rows, M, xq, sx);
         if (oracle_int8_gemm(xq, M, K, Wq, N, acc, nthreads) != 0) o = -2;
-        else oracle_output(acc, sx, sw, X, W16, rows, M, K, N, idx, o, Y, Y64, nthreads);
+        else oracle_output(acc, sx, sw, X, W16, Wq, rows, M, K, N, idx, o, Y, Y64, nthreads);
     }
     if (!flag_out) free(flag);
     if (!idx_out) free(idx);

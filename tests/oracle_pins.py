@@ -86,6 +86,82 @@ def pin_hand_example(orc):
     assert np.array_equal(r["Y"].astype(np.float64), np.array(g["Y"])), "hand Y"
 
 
+def pin_hand_memory_halved(orc):
+    """The hand example without the 16-bit weight (outlier row recovered
+    from the Int8 weight)."""
+    g = _load("hand_2x4x2.json")
+    h = g["memory_halved"]
+    X = np.array(g["X"], np.float16)
+    W = np.array(g["W"], np.float16)
+    Wq, sw = orc.quantize_weight(W)
+    for n in range(2):
+        bits = orc.dequant_weight(int(Wq[n, 3]), float(sw[n]))
+        assert orc.f16_decode(bits) == h["What_row3"][n], "hand recovered weight"
+    r = orc.mixed_matmul(X, Wq, sw, None, g["tau"])
+    assert np.array_equal(r["acc"], np.array(g["acc"], np.int32)), "hand acc (memory-halved)"
+    num = np.array([a / b + c for a, b, c in h["Y64_num"]]).reshape(2, 2)
+    assert np.allclose(r["Y64"], num, rtol=1e-14, atol=0), "hand Y64 (memory-halved)"
+    assert np.array_equal(r["Y"].astype(np.float64), np.array(h["Y"])), "hand Y (memory-halved)"
+
+
+def pin_dequant_weight(orc):
+    """Recovered weight values: within half an fp16 step (plus the two fp32
+    roundings) of q * s_w / 127, odd in q, monotone in q, exact for
+    s_w = 127 (the codes themselves), 0 for q = 0."""
+    rng = np.random.default_rng(7)
+    scales = [127.0, 2.0, 0.015, 3.0e-5, 0.4990234375, 1000.0] + list(rng.uniform(1e-3, 50, 6))
+    for s in scales:
+        s = float(np.float32(s))
+        vals = np.array([orc.f16_decode(orc.dequant_weight(q, s)) for q in range(-127, 128)])
+        exact = np.arange(-127, 128) * s / 127.0
+        # half an fp16 ulp of the value (2^-11 relative, 2^-25 absolute below
+        # the normal range) plus the fp32 divide and multiply (2^-23 each)
+        bound = np.abs(exact) * (2.0 ** -11 + 2.0 ** -22) + 2.0 ** -25
+        assert np.all(np.abs(vals - exact) <= bound), f"recovered weight error, s_w={s}"
+        assert vals[127] == 0.0, "q = 0"
+        assert np.array_equal(vals[::-1], -vals), "odd in q"
+        assert np.all(np.diff(vals) >= 0), "monotone in q"
+        if s == 127.0:
+            assert np.array_equal(vals, np.arange(-127, 128, dtype=np.float64)), "s_w = 127"
+
+
+def pin_memory_halved_tau_zero(orc):
+    """tau = 0, memory-halved: every dimension is an outlier and Xq is 0, so
+    Y is the fp16 matmul of X with the recovered weight, rounded once
+    (numpy float64 matmul; the recovered values come from
+    pin_dequant_weight's function)."""
+    for seed, (T, K, N) in enumerate([(5, 32, 16), (17, 48, 24)]):
+        X, W = _case(300 + seed, T, K, N, n_dims=2, factor=9.0)
+        Wq, sw = orc.quantize_weight(W)
+        What = np.empty((K, N), np.float64)
+        for n in range(N):
+            for k in range(K):
+                What[k, n] = orc.f16_decode(orc.dequant_weight(int(Wq[n, k]), float(sw[n])))
+        r = orc.mixed_matmul(X, Wq, sw, None, 0.0)
+        ref = X.astype(np.float64) @ What
+        assert r["o"] == K and not r["xq"].any(), "tau = 0 isolates everything"
+        assert np.allclose(r["Y64"], ref, rtol=1e-13, atol=1e-300), "memory-halved tau=0 Y64"
+        assert np.array_equal(r["Y"], ref.astype(np.float16)), "memory-halved tau=0 Y"
+
+
+def pin_memory_halved_exact_weight(orc):
+    """When every weight is its own Int8 code (integer values with a 127 in
+    each column, so s_w = 127 and W^ = W exactly), the memory-halved result
+    equals the result with the 16-bit weight, bit for bit."""
+    rng = np.random.default_rng(11)
+    for T, K, N in [(6, 32, 16), (9, 64, 8)]:
+        X, _ = _case(400 + K, T, K, N, n_dims=3, factor=9.0)
+        W = rng.integers(-127, 128, size=(K, N)).astype(np.float16)
+        W[rng.integers(0, K, size=N), np.arange(N)] = 127.0
+        Wq, sw = orc.quantize_weight(W)
+        assert np.all(sw == 127.0) and np.array_equal(Wq.T.astype(np.float16), W)
+        a = orc.mixed_matmul(X, Wq, sw, W, 6.0)
+        b = orc.mixed_matmul(X, Wq, sw, None, 6.0)
+        assert a["o"] > 0
+        assert np.array_equal(a["Y"], b["Y"]) and np.array_equal(a["Y64"], b["Y64"]), \
+            "memory-halved with exact weights"
+
+
 def pin_quant_ties(orc):
     g = _load("quant_ties.json")
     for c in g["cases"]:
@@ -303,4 +379,6 @@ def pin_row_sample(orc):
 
 ALL_PINS = [pin_f16_codec, pin_hand_example, pin_quant_ties, pin_detect, pin_compact,
             pin_tiny_config, pin_quant_invariants, pin_gemm, pin_tau_inf, pin_tau_zero,
-            pin_error_bound, pin_metamorphic_scale, pin_permutation, pin_row_sample]
+            pin_error_bound, pin_metamorphic_scale, pin_permutation, pin_row_sample,
+            pin_hand_memory_halved, pin_dequant_weight, pin_memory_halved_tau_zero,
+            pin_memory_halved_exact_weight]

@@ -28,8 +28,15 @@ MUTANTS = [
     ("f16_ties_away", "(frac == 0.5 && fmod(fl, 2.0) != 0.0)", "(frac == 0.5)"),
     ("weight_scale_first_rows", "for (int64_t k = 0; k < c->K; ++k) {\n            float a = fabsf(oh_f32(c->W[k * c->N + n]));",
      "for (int64_t k = 0; k < c->K / 2; ++k) {\n            float a = fabsf(oh_f32(c->W[k * c->N + n]));"),
-    ("outlier_value_from_wrong_row", "oh_decode(c->X[t * c->K + k]) * oh_decode(c->W16[k * c->N + n])",
-     "oh_decode(c->X[k]) * oh_decode(c->W16[k * c->N + n])"),
+    ("outlier_value_from_wrong_row", "oh_decode(c->X[t * c->K + k]) * oh_decode(w)",
+     "oh_decode(c->X[k]) * oh_decode(w)"),
+    ("recovered_weight_unrounded", "y16 += oh_decode(c->X[t * c->K + k]) * oh_decode(w);",
+     "y16 += oh_decode(c->X[t * c->K + k]) * (c->W16 ? oh_decode(w) : (double)((float)c->Wq[n * c->K + k] * (c->sw[n] / 127.0f)));"),
+    ("recovered_weight_128", "const float d = sw / 127.0f;", "const float d = sw / 128.0f;"),
+    ("recovered_weight_transposed", "oracle_dequant_weight(c->Wq[n * c->K + k], c->sw[n])",
+     "oracle_dequant_weight(c->Wq[(k * c->N + n) % (c->N * c->K)], c->sw[n])"),
+    ("recovered_weight_ignored", ": oracle_dequant_weight(c->Wq[n * c->K + k], c->sw[n]);",
+     ": (uint16_t)0;"),
 ]
 
 
