@@ -143,6 +143,21 @@ def bench_prefill(torch, mm, synth, steps, warmup):
     wall, evs = timed_loop(torch, steps, warmup, step)
     act_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     gemm_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    # the memory-halved variant (no 16-bit weight: outlier rows recovered
+    # from the Int8 weight), same steps
+    def step_halved(i, e):
+        if e is not None:
+            e[0].record()
+        mm.quantize_activations(X, N, w.tau, ws)
+        if e is not None:
+            e[1].record()
+        mm.matmul_prepared(ws, T, K, Wq, sw, None, out=Y)
+        if e is not None:
+            e[2].record()
+
+    log(f"prefill, memory-halved: {warmup} warmup + {steps} timed steps")
+    wall_h, evs_h = timed_loop(torch, steps, warmup, step_halved)
+    gemm_h_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs_h]))
     # the outlier count of this X (one debug call, outside the timed loop)
     dbg = mm.mixed_matmul_debug(X, Wq, sw, W16, w.tau)
     o = int(dbg["count"][0])
@@ -154,6 +169,8 @@ def bench_prefill(torch, mm, synth, steps, warmup):
         "tops": ops * steps / wall / 1e12,
         "activation_ms": act_ms, "gemm_ms": gemm_ms,
         "gemm_tops": ops / (gemm_ms * 1e-3) / 1e12,
+        "halved_tops": ops * steps / wall_h / 1e12, "halved_ms_per_step": wall_h * 1e3 / steps,
+        "halved_gemm_ms": gemm_h_ms,
         "quantize_weight_ms": q_ms,
         "quantize_weight_gbs": (2.0 * K * N + K * N + 4.0 * N) / (q_ms * 1e-3) / 1e9,
     }
@@ -200,6 +217,30 @@ def bench_decode(torch, mm, synth, steps, warmup):
     log(f"decode: {warmup} warmup + {rounds} timed graph replays of {DECODE_ROTATE} calls")
     wall, evs = timed_loop(torch, rounds, max(1, warmup // DECODE_ROTATE + 1), step)
     call_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) / DECODE_ROTATE
+
+    # the memory-halved variant: no 16-bit weight passed at all
+    def one_round_halved():
+        for Wq, sw, _ in sets:
+            mm.mixed_matmul(X, Wq, sw, None, w.tau, workspace=ws, out=Y)
+
+    one_round_halved()
+    torch.cuda.synchronize()
+    graph_h = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph_h):
+        one_round_halved()
+    torch.cuda.synchronize()
+
+    def step_halved(i, e):
+        if e is not None:
+            e[0].record()
+        graph_h.replay()
+        if e is not None:
+            e[1].record()
+            e[2].record()
+
+    log(f"decode, memory-halved: {rounds} timed graph replays")
+    wall_h, evs_h = timed_loop(torch, rounds, max(1, warmup // DECODE_ROTATE + 1), step_halved)
+    call_h_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs_h])) / DECODE_ROTATE
     dbg = mm.mixed_matmul_debug(X, Wq0, sw0, W16_0, w.tau)
     o = int(dbg["count"][0])
     wbytes = K * N + 4.0 * N
@@ -208,6 +249,7 @@ def bench_decode(torch, mm, synth, steps, warmup):
         "T": T, "K": K, "N": N, "tau": w.tau, "o": o, "ms_per_step": wall * 1e3 / steps,
         "steps": steps, "weight_gbs": wbytes * steps / wall / 1e9, "call_ms": call_ms,
         "alg_bytes": alg_bytes, "alg_gbs": alg_bytes / (call_ms * 1e-3) / 1e9,
+        "halved_weight_gbs": wbytes * steps / wall_h / 1e9, "halved_call_ms": call_h_ms,
     }
 
 
@@ -271,11 +313,13 @@ def main():
     if args.only in (None, "prefill"):
         pre = bench_prefill(torch, mm, synth, args.steps, args.warmup)
         log(f"prefill: {pre['tops']:.1f} TOPS ({pre['ms_per_step']:.3f} ms/step), "
-            f"gemm {pre['gemm_ms']:.3f} ms, activation pass {pre['activation_ms']:.3f} ms")
+            f"gemm {pre['gemm_ms']:.3f} ms, activation pass {pre['activation_ms']:.3f} ms; "
+            f"memory-halved {pre['halved_tops']:.1f} TOPS")
         torch.cuda.empty_cache()
     if args.only in (None, "decode"):
         dec = bench_decode(torch, mm, synth, args.steps, args.warmup)
-        log(f"decode: {dec['weight_gbs']:.1f} GB/s weight ({dec['call_ms'] * 1e3:.1f} us/call)")
+        log(f"decode: {dec['weight_gbs']:.1f} GB/s weight ({dec['call_ms'] * 1e3:.1f} us/call); "
+            f"memory-halved {dec['halved_weight_gbs']:.1f} GB/s ({dec['halved_call_ms'] * 1e3:.1f} us/call)")
 
     gemm_digest = src_digest(["k_gemm.hip", "common.hpp"])
     decode_digest = src_digest(["k_decode.hip", "common.hpp"])
@@ -302,6 +346,11 @@ def main():
                          "work": "2*T*K*N int8 ops per launch", "ms": round(pre["gemm_ms"], 4)},
             "stages_ms": {"activation_pass": round(pre["activation_ms"], 4),
                           "gemm": round(pre["gemm_ms"], 4)},
+            "memory_halved": {"note": "W16 not passed: outlier rows recovered from the Int8 "
+                                      "weight (same X, W, tau)",
+                              "TOPS": round(pre["halved_tops"], 2),
+                              "ms_per_step": round(pre["halved_ms_per_step"], 4),
+                              "gemm_ms": round(pre["halved_gemm_ms"], 4)},
             "quantize_weight": {"ms": round(pre["quantize_weight_ms"], 4),
                                 "GB/s": round(pre["quantize_weight_gbs"], 1),
                                 "bytes": "2KN read + KN + 4N written"},
@@ -320,7 +369,11 @@ def main():
                           "traffic": measured_traffic("decode_dec_traffic.md", decode_digest, "hbm_bytes_per_launch"),
                           "kernel": "k_decode (the whole int8_mixed_matmul call)",
                           "work": "2TK + KN + 4N + 2oN + 2TN bytes per call",
-                          "ms": round(dec["call_ms"], 5)}}
+                          "ms": round(dec["call_ms"], 5)},
+             "memory_halved": {"note": "W16 not passed: outlier rows recovered from the Int8 "
+                                       "weight",
+                               "weight GB/s": round(dec["halved_weight_gbs"], 1),
+                               "call_ms": round(dec["halved_call_ms"], 5)}}
         if pre is None:
             out.update({"value": d["value"], "unit": "GB/s", "ms_per_step": d["ms_per_step"],
                         "config": d["config"], "roofline": d["roofline"]})

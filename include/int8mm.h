@@ -58,7 +58,8 @@ typedef enum {
     INT8MM_E_TAU = 3,         /* tau is NaN or negative */
     INT8MM_E_ALIGN = 4,       /* a pointer is not 16-byte aligned */
     INT8MM_E_WORKSPACE = 5,   /* workspace smaller than the size query returns */
-    INT8MM_E_UNSUPPORTED = 6, /* a valid request this build does not implement */
+    INT8MM_E_UNSUPPORTED = 6, /* a valid request this build does not implement (no entry
+                                 point returns it today; kept so codes stay stable) */
     INT8MM_E_HIP = 7          /* the HIP runtime reported a launch error */
 } int8mm_status;
 
@@ -95,13 +96,16 @@ int int8_quantize_weight(const void* W16, int64_t K, int64_t N, int8_t* Wq, floa
  *   X:   fp16 [T,K] activations (read only)
  *   Wq, sw: from int8_quantize_weight for the same K and N (read only)
  *   W16: fp16 [K,N], the 16-bit weight; only its outlier rows are read.
- *        NULL is rejected with E_UNSUPPORTED (no dequantized-row fallback).
+ *        NULL selects the memory-halved variant (only the Int8 weight is
+ *        kept, LLM.int8() abstract: inference memory cut by half): the
+ *        outlier rows are recovered from Wq as
+ *        W^[k,n] = fp16(fp32(Wq[n,k] * fp32(sw[n] / 127))).
  *   tau: outlier threshold, tau >= 0 (+inf: no outliers; 0: every
  *        dimension is an outlier and Y is the fp16 matmul)
  *   Y:   fp16 [T,N] (written)
  *   workspace: device buffer of at least the size query's bytes; its
  *        contents on entry are ignored and on return are unspecified.
- * Errors: E_NULL, E_SHAPE, E_TAU, E_ALIGN, E_WORKSPACE, E_UNSUPPORTED, E_HIP. */
+ * Errors: E_NULL, E_SHAPE, E_TAU, E_ALIGN, E_WORKSPACE, E_HIP. */
 int int8_mixed_matmul(const void* X, int64_t T, int64_t K, const int8_t* Wq, const float* sw,
                       const void* W16, int64_t N, float tau, void* Y, void* workspace,
                       size_t workspace_bytes, void* stream);
@@ -136,7 +140,7 @@ int int8mm_quantize_activations(const void* X, int64_t T, int64_t K, int64_t N, 
  * same T and K (the workspace is read only here and may be reused for any
  * number of weights).  X is read only through the gathered copy in the
  * workspace.  Arguments as int8_mixed_matmul.
- * Errors: E_NULL, E_SHAPE, E_ALIGN, E_WORKSPACE, E_UNSUPPORTED, E_HIP. */
+ * Errors: E_NULL, E_SHAPE, E_ALIGN, E_WORKSPACE, E_HIP. */
 int int8mm_matmul_prepared(const void* workspace, size_t workspace_bytes, int64_t T, int64_t K,
                            const int8_t* Wq, const float* sw, const void* W16, int64_t N,
                            void* Y, void* stream);

@@ -38,6 +38,17 @@ struct Workspace {
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// A weight value recovered from its Int8 code q and column scale s_w
+// (memory-halved variant): fp16(fp32(q * fp32(s_w / 127))).  The product is
+// rounded to fp32 first: the empty asm keeps the compiler from fusing the
+// multiply and the conversion into one v_fma_mixlo_f16 (a single rounding
+// of the exact product straight to fp16).
+__device__ __forceinline__ _Float16 recover_weight(int8_t q, float d) {
+    float v = (float)q * d;
+    asm volatile("" : "+v"(v));
+    return (_Float16)v;
+}
+
 // Bytes of the converted weight: int8 [N,K] row-major (K contiguous).
 inline int64_t wq_bytes(int64_t K, int64_t N) { return K * N; }
 
@@ -61,7 +72,7 @@ struct GemmArgs {
     const _Float16* xo;    // [T,opad]
     const int32_t* idx;    // [K]
     const int32_t* count;  // [2]
-    const _Float16* w16;   // [K,N]
+    const _Float16* w16;   // [K,N], or NULL: outlier rows recovered from wq
     _Float16* y;           // [T,N]
     int32_t* acc_out;      // [T,N] or NULL
     int64_t T, K, N;

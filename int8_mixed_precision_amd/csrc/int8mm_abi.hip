@@ -42,7 +42,6 @@ int check_matmul(const void* X, int64_t T, int64_t K, const int8_t* Wq, const fl
         !aligned16(workspace) || (W16 && !aligned16(W16)))
         return INT8MM_E_ALIGN;
     if (workspace_bytes < carve_workspace(nullptr, T, K).bytes) return INT8MM_E_WORKSPACE;
-    if (!W16) return INT8MM_E_UNSUPPORTED;
     return INT8MM_OK;
 }
 
@@ -157,7 +156,6 @@ int int8mm_matmul_prepared(const void* workspace, size_t workspace_bytes, int64_
         return INT8MM_E_ALIGN;
     Workspace ws = carve_workspace(const_cast<void*>(workspace), T, K);
     if (workspace_bytes < ws.bytes) return INT8MM_E_WORKSPACE;
-    if (!W16) return INT8MM_E_UNSUPPORTED;
     GemmArgs g{ws.xq, ws.sx, Wq, sw, ws.xo, ws.idx, ws.count,
                static_cast<const _Float16*>(W16), static_cast<_Float16*>(Y), nullptr, T, K, N};
     return hip_status(launch_gemm(g, static_cast<hipStream_t>(stream)));

@@ -61,7 +61,7 @@ struct DecodeArgs {
     const uint16_t* x;      // [T,K] fp16 bits
     const int8_t* wq;       // [N,K]
     const float* sw;        // [N]
-    const _Float16* w16;    // [K,N]
+    const _Float16* w16;    // [K,N], or NULL: outlier rows recovered from wq
     _Float16* y;            // [T,N]
     float tau;
     uint32_t tau16;         // bits of the smallest fp16 >= tau (0x7C00 if none finite)
@@ -368,14 +368,26 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
     // kernel does not wait on them: thread -> outlier slot tid / 64 + 8 h,
     // row pair 2 (tid % 64); slots past o read the first dword of W16 (never
     // used).
+    // Without W16 (memory-halved variant) the two values are recovered from
+    // the Int8 weight instead: fp16(q[n,k] * fp32(s_w[n] / 127)).
     uint32_t w16v[2];
+    const bool recover = a.w16 == nullptr;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int j = (tid >> 6) + 8 * h;
         const int r = 2 * (tid & 63);
         const int n = r < rows && n0 + r < N ? n0 + r : 0;
-        const int64_t off = j < o ? (int64_t)sm.idx[j] * N + n : 0;
-        w16v[h] = *reinterpret_cast<const uint32_t*>(a.w16 + off);
+        if (!recover) {
+            const int64_t off = j < o ? (int64_t)sm.idx[j] * N + n : 0;
+            w16v[h] = *reinterpret_cast<const uint32_t*>(a.w16 + off);
+        } else {
+            const int k = j < o ? sm.idx[j] : 0;
+            const int8_t q0 = a.wq[(int64_t)n * K + k], q1 = a.wq[(int64_t)(n + 1) * K + k];
+            // s_w of the pair from LDS (the pair past the rows is never used)
+            const float d0 = sm.sw[r & 127] / 127.0f, d1 = sm.sw[(r + 1) & 127] / 127.0f;
+            w16v[h] = (uint32_t)__builtin_bit_cast(uint16_t, recover_weight(q0, d0)) |
+                      ((uint32_t)__builtin_bit_cast(uint16_t, recover_weight(q1, d1)) << 16);
+        }
     }
     issue(id1, ring[1]);
     issue(id2, ring[2]);
@@ -442,7 +454,9 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
             const int k = sm.idx[j];
             const float xv = j < kMaxOutliersLds ? sm.xo[t * kMaxOutliersLds + j]
                                                  : h2f(a.x[(int64_t)t * K + k]);
-            y += xv * (float)a.w16[(int64_t)k * N + n];
+            const _Float16 w = recover ? recover_weight(a.wq[(int64_t)n * K + k], sm.sw[r] / 127.0f)
+                                       : a.w16[(int64_t)k * N + n];
+            y += xv * (float)w;
         }
         a.y[(int64_t)t * N + n] = (_Float16)y;
     }

@@ -80,6 +80,15 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a,
         const int64_t n = nb + j * 32 + col_l;
         swn[j] = n < N ? a.sw[n] * (1.0f / 16129.0f) : 0.0f;
     }
+    // memory-halved variant (no W16): the outlier rows are recovered from the
+    // Int8 weight, W^[k,n] = fp16(q[n,k] * fp32(s_w[n] / 127))
+    const bool recover = a.w16 == nullptr;
+    float dn[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int64_t n = nb + j * 32 + col_l;
+        dn[j] = recover && n < N ? a.sw[n] / 127.0f : 0.0f;
+    }
     const int o = a.count[0];
     const int opad = a.count[1];
     // one 32-row strip of tiles at a time keeps the fp32 values of only TN
@@ -106,16 +115,24 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a,
             const int64_t mrow = mb + i * 32 + (lane & 31);
             const v8h xa = mrow < T ? *reinterpret_cast<const v8h*>(a.xo + mrow * opad + jl)
                                     : v8h{0, 0, 0, 0, 0, 0, 0, 0};
-            int64_t rowoff[8];
+            int64_t kk[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) rowoff[e] = (jl + e < o) ? (int64_t)a.idx[jl + e] * N : -1;
+            for (int e = 0; e < 8; ++e) kk[e] = (jl + e < o) ? (int64_t)a.idx[jl + e] : -1;
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const int64_t n = nb + j * 32 + col_l;
                 v8h wb;
+                if (!recover) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    wb[e] = (rowoff[e] >= 0 && n < N) ? a.w16[rowoff[e] + n] : (_Float16)0.0f;
+                    for (int e = 0; e < 8; ++e)
+                        wb[e] = (kk[e] >= 0 && n < N) ? a.w16[kk[e] * N + n] : (_Float16)0.0f;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        wb[e] = (kk[e] >= 0 && n < N)
+                                    ? recover_weight(a.wq[n * a.K + kk[e]], dn[j])
+                                    : (_Float16)0.0f;
+                }
                 y[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xa, wb, y[j], 0, 0, 0);
             }
         }

@@ -77,7 +77,6 @@ def call_mm(lib, X=FAKE, T=16, K=64, Wq=FAKE, sw=FAKE, W16=FAKE, N=48, tau=6.0, 
     (dict(tau=float("nan")), 3), (dict(tau=-1.0), 3), (dict(tau=-1e-30), 3),
     (dict(X=FAKE + 8), 4), (dict(Wq=FAKE + 1), 4), (dict(Y=FAKE + 2), 4), (dict(W16=FAKE + 4), 4),
     (dict(ws_bytes=100), 5),
-    (dict(W16=0), 6),                     # memory-halved variant not built
 ])
 def test_matmul_validation(mm, kw, status):
     assert call_mm(mm.lib(), **kw) == status
@@ -115,8 +114,10 @@ def test_staged_entry_points_validation(mm):
     assert lib.int8mm_quantize_activations(vp(FAKE), 16, 64, 48, float("nan"), vp(FAKE),
                                            1 << 30, None) == 3
     assert lib.int8mm_quantize_activations(vp(FAKE), 16, 64, 48, 6.0, vp(FAKE), 10, None) == 5
-    assert lib.int8mm_matmul_prepared(vp(FAKE), 1 << 30, 16, 64, vp(FAKE), vp(FAKE), None, 48,
-                                      vp(FAKE), None) == mm.E_UNSUPPORTED
+    assert lib.int8mm_matmul_prepared(vp(FAKE), 1 << 30, 16, 64, vp(FAKE), vp(FAKE),
+                                      vp(FAKE + 2), 48, vp(FAKE), None) == mm.E_ALIGN
+    assert lib.int8mm_matmul_prepared(None, 1 << 30, 16, 64, vp(FAKE), vp(FAKE), None, 48,
+                                      vp(FAKE), None) == mm.E_NULL
     assert lib.int8mm_matmul_prepared(vp(FAKE), 10, 16, 64, vp(FAKE), vp(FAKE), vp(FAKE), 48,
                                       vp(FAKE), None) == mm.E_WORKSPACE
     assert lib.int8_mixed_matmul_debug(vp(FAKE), 16, 64, vp(FAKE), vp(FAKE), vp(FAKE), 48, 6.0,

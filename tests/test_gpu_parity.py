@@ -49,14 +49,17 @@ def check_y(y_gpu, y_ref, what):
     return err / max(scale, 1e-30)
 
 
-def run_case(mm, name, X, W, tau, rows=None, plain_too=True):
+def run_case(mm, name, X, W, tau, rows=None, plain_too=True, halved=False):
+    """halved: the memory-halved variant (no 16-bit weight passed; outlier
+    rows recovered from the Int8 weight on both sides)."""
     T, K = X.shape
     N = W.shape[1]
-    say(f"[case] {name}: T={T} K={K} N={N} tau={tau}")
+    say(f"[case] {name}: T={T} K={K} N={N} tau={tau}{' (memory-halved)' if halved else ''}")
     Xd, Wd = gpu(X), gpu(W)
     Wq, sw = mm.quantize_weight(Wd)
-    r = mm.mixed_matmul_debug(Xd, Wq, sw, Wd, tau)
-    Yp = mm.mixed_matmul(Xd, Wq, sw, Wd, tau) if plain_too else None
+    W16 = None if halved else Wd
+    r = mm.mixed_matmul_debug(Xd, Wq, sw, W16, tau)
+    Yp = mm.mixed_matmul(Xd, Wq, sw, W16, tau) if plain_too else None
     torch.cuda.synchronize()
     say(f"[case] {name}: GPU done")
 
@@ -76,7 +79,8 @@ def run_case(mm, name, X, W, tau, rows=None, plain_too=True):
     assert np.array_equal(r["xq"].cpu().numpy(), xq_o), f"{name}: Xq differs"
 
     sel = np.arange(T) if rows is None else np.asarray(rows)
-    ref = oracle.mixed_matmul(X, Wq_o, sw_o, W, tau, rows=None if rows is None else sel)
+    ref = oracle.mixed_matmul(X, Wq_o, sw_o, None if halved else W, tau,
+                              rows=None if rows is None else sel)
     sel_t = torch.from_numpy(sel).cuda()
     acc = r["acc"].index_select(0, sel_t).cpu().numpy()
     assert np.array_equal(acc, ref["acc"]), f"{name}: acc differs in {np.sum(acc != ref['acc'])}"
@@ -122,6 +126,21 @@ def test_decode_path(mm, T, K, N, nd, tau):
     """Shapes on the single-kernel decode path (T <= 16, K in {4096, 8192})."""
     X, W = synth.random_case(30_000 + T + K + N + nd, T, K, N, n_dims=nd)
     run_case(mm, f"decode path {T}x{K}x{N} tau={tau}", X, W, tau)
+
+
+@pytest.mark.parametrize("T,K,N,nd,tau", [
+    (37, 80, 200, 2, 6.0), (300, 1040, 520, 3, 6.0),          # staged kernels
+    (257, 2048, 1000, 70, 6.0), (129, 64, 8, 1, 6.0),          # large-tile kernel
+    (1, 4096, 1000, 3, 6.0), (8, 8192, 264, 300, 6.0),         # decode kernel, o > 16
+    (16, 4096, 520, 20, 6.0),
+    (70, 1024, 136, 0, 0.0), (2, 4096, 136, 0, 0.0),           # every dimension an outlier
+])
+def test_memory_halved(mm, T, K, N, nd, tau):
+    """W16 = NULL: outlier rows recovered from the Int8 weight."""
+    X, W = synth.random_case(50_000 + T + K + N + nd, T, K, N, n_dims=nd)
+    r, ref = run_case(mm, f"memory-halved {T}x{K}x{N} tau={tau}", X, W, tau, halved=True)
+    if tau == 0.0:
+        assert int(r["count"][0]) == K
 
 
 def test_tau_zero_every_dimension_outlier(mm):
