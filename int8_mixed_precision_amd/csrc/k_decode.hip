@@ -54,6 +54,7 @@ constexpr int kMaxXK = 65536;          // T*K bytes of Xq kept in LDS
 constexpr int kMaxOutliersLds = 256;   // outlier values cached in LDS
 constexpr int kMaxBpw = 8;             // 16-row blocks per workgroup
 constexpr int kW16Cache = 16;          // outliers whose W16 values are staged in LDS
+constexpr int kChunkKConst = 1024;     // k covered by one weight chunk
 
 __device__ inline float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
 
@@ -83,6 +84,8 @@ struct Smem {
     float xo[kMaxT * kMaxOutliersLds];         // X values of the first outliers
     int32_t acc[kMaxBpw][kRows][16];           // int32 sums [block][row][t]
     uint32_t w16o[kW16Cache][kMaxBpw * kRows / 2];   // W16[idx_j, n] pairs of the rows
+    int8_t wqo[kW16Cache][kMaxBpw * kRows];    // Wq[n, idx_j] (memory-halved variant)
+    int32_t cfirst[kMaxK / kChunkKConst + 1];   // first outlier at or past k = 1024 c
     float sw[kMaxBpw * kRows];                 // s_w of the rows
     float wmax[kWaves][kMaxT];
     float sx[kMaxT];
@@ -106,6 +109,7 @@ __device__ inline float chunk_val(const uint4& v, int e) {
 
 constexpr int kLoads = 16;                    // 16-byte loads per lane per chunk (16 KB/wave)
 constexpr int kChunkK = kLoads * 64;          // k covered by one chunk
+static_assert(kChunkK == kChunkKConst, "chunk size");
 
 
 // CPB = K / 1024 chunks per 16-row block; a thread owns CPT = K / 4096
@@ -353,6 +357,14 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
             }
         }
     }
+    // number of outliers before each 1024-column chunk: the thread owning the
+    // first 8-column piece of chunk cc knows it (its prefix count)
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        const int c8 = tid + kThreads * j;
+        if ((c8 & (kChunkK / 8 - 1)) == 0) sm.cfirst[c8 / (kChunkK / 8)] = pc[j];
+    }
+    if (tid == 0) sm.cfirst[K / kChunkK] = o;
     if (blockIdx.x == 0 && tid == 0 && a.dbg_count) a.dbg_count[0] = o;
     if (blockIdx.x == 0 && a.dbg_sx && tid < T) a.dbg_sx[tid] = sm.sx[tid];
     __syncthreads();   // Xq, idx, xo ready
@@ -368,25 +380,18 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
     // kernel does not wait on them: thread -> outlier slot tid / 64 + 8 h,
     // row pair 2 (tid % 64); slots past o read the first dword of W16 (never
     // used).
-    // Without W16 (memory-halved variant) the two values are recovered from
-    // the Int8 weight instead: fp16(q[n,k] * fp32(s_w[n] / 127)).
-    uint32_t w16v[2];
+    // Without W16 (memory-halved variant) nothing is fetched: the Int8 codes
+    // of the outlier columns are picked out of the weight stream itself.
+    uint32_t w16v[2] = {0u, 0u};
     const bool recover = a.w16 == nullptr;
+    if (!recover) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int j = (tid >> 6) + 8 * h;
-        const int r = 2 * (tid & 63);
-        const int n = r < rows && n0 + r < N ? n0 + r : 0;
-        if (!recover) {
+        for (int h = 0; h < 2; ++h) {
+            const int j = (tid >> 6) + 8 * h;
+            const int r = 2 * (tid & 63);
+            const int n = r < rows && n0 + r < N ? n0 + r : 0;
             const int64_t off = j < o ? (int64_t)sm.idx[j] * N + n : 0;
             w16v[h] = *reinterpret_cast<const uint32_t*>(a.w16 + off);
-        } else {
-            const int k = j < o ? sm.idx[j] : 0;
-            const int8_t q0 = a.wq[(int64_t)n * K + k], q1 = a.wq[(int64_t)(n + 1) * K + k];
-            // s_w of the pair from LDS (the pair past the rows is never used)
-            const float d0 = sm.sw[r & 127] / 127.0f, d1 = sm.sw[(r + 1) & 127] / 127.0f;
-            w16v[h] = (uint32_t)__builtin_bit_cast(uint16_t, recover_weight(q0, d0)) |
-                      ((uint32_t)__builtin_bit_cast(uint16_t, recover_weight(q1, d1)) << 16);
         }
     }
     issue(id1, ring[1]);
@@ -418,6 +423,25 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
         int32_t* d = accrow + (id / CPB) * (kRows * 16);
 #pragma unroll
         for (int v = 0; v < 4; ++v) atomicAdd(d + v * 16, acc[v]);
+        if (recover) {
+            // memory-halved variant: the chunk holds Wq[n, k] for its 16 rows
+            // and 1024 columns; copy the codes of the outlier columns in it
+            // (the first kW16Cache outliers) to LDS.  Column k sits in load
+            // (k / 64) % 16, on lanes 16 ((k / 16) % 4) + row, byte k % 16.
+            const int c = id % CPB;
+            const int jhi = sm.cfirst[c + 1] < kW16Cache ? sm.cfirst[c + 1] : kW16Cache;
+            for (int j = sm.cfirst[c]; j < jhi; ++j) {
+                const int k = sm.idx[j] - c * kChunkK;
+                const int ii = k >> 6;
+                v4i v = buf[0];
+#pragma unroll
+                for (int m = 1; m < kLoads; ++m) v = ii == m ? buf[m] : v;
+                const int b = k & 15;
+                const int dw = (b >> 2) == 0 ? v[0] : (b >> 2) == 1 ? v[1] : (b >> 2) == 2 ? v[2] : v[3];
+                if ((lane >> 4) == ((k >> 4) & 3))
+                    sm.wqo[j][(id / CPB) * kRows + (lane & 15)] = (int8_t)(dw >> (8 * (b & 3)));
+            }
+        }
         return __builtin_amdgcn_readfirstlane(nid);
     };
     // ids increase in the order the slots are used (0, 1, 2, 0, ...), so once
@@ -432,9 +456,11 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
             issue(id2, ring[2]);
         } while (id0 < total);
     }
+    if (!recover) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) sm.w16o[(tid >> 6) + 8 * h][tid & 63] = w16v[h];
-    __syncthreads();   // sums and W16 values complete
+        for (int h = 0; h < 2; ++h) sm.w16o[(tid >> 6) + 8 * h][tid & 63] = w16v[h];
+    }
+    __syncthreads();   // sums and W16 values (or codes) complete
 
     // ---- epilogue: y = acc * s_x * s_w / 127^2 + sum_j X[t, idx_j] W16[idx_j, n],
     // one fp16 rounding; consecutive threads take consecutive rows n.
@@ -446,9 +472,16 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
         const int32_t acc = sm.acc[r >> 4][r & 15][t];
         if (a.dbg_acc) a.dbg_acc[(int64_t)t * N + n] = acc;
         float y = (float)acc * sm.sx[t] * (sm.sw[r] * (1.0f / 16129.0f));
-        for (int j = 0; j < oc; ++j) {
-            const uint32_t pr = sm.w16o[j][r >> 1];
-            y += sm.xo[t * kMaxOutliersLds + j] * h2f((uint16_t)((r & 1) ? pr >> 16 : pr & 0xFFFFu));
+        if (!recover) {
+            for (int j = 0; j < oc; ++j) {
+                const uint32_t pr = sm.w16o[j][r >> 1];
+                y += sm.xo[t * kMaxOutliersLds + j] *
+                     h2f((uint16_t)((r & 1) ? pr >> 16 : pr & 0xFFFFu));
+            }
+        } else {
+            const float dr = sm.sw[r] / 127.0f;
+            for (int j = 0; j < oc; ++j)
+                y += sm.xo[t * kMaxOutliersLds + j] * (float)recover_weight(sm.wqo[j][r], dr);
         }
         for (int j = oc; j < o; ++j) {
             const int k = sm.idx[j];
