@@ -1,7 +1,7 @@
 """Benchmark of the LLM.int8() mixed-precision matmul on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill|decode]
-                    [--no-cpu-baseline]
+                    [--no-cpu-baseline] [--sweep]
 
 A step is one full int8_mixed_matmul call (outlier detection, isolation,
 row-wise quantization, int8 MFMA matmul, dequantization and the 16-bit
@@ -50,6 +50,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--only", choices=["prefill", "decode"], default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--sweep", action="store_true",
+                   help="instead of the headline run: the four projections of a 175B-class "
+                        "block at T=4096 with 0, 8, 64 and 256 planted outlier dimensions "
+                        "(time against the outlier count); prints one JSON line")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device-to-device copy (a kernel of known "
                         "traffic, for scaling the HBM byte counters)")
@@ -253,6 +257,49 @@ def bench_decode(torch, mm, synth, steps, warmup):
     }
 
 
+def bench_sweep(torch, mm, synth, steps, warmup):
+    """Every sweep workload: the full call (activation pass + matmul, both
+    timed by events on the library's stream), with and without the 16-bit
+    weight.  Inputs are generated per workload and freed after it."""
+    rows = []
+    for name, w in synth.WORKLOADS.items():
+        if not name.startswith("sweep_"):
+            continue
+        T, K, N = w.T, w.K, w.N
+        log(f"sweep {name}: T={T} K={K} N={N}, {w.n_dims} planted dims")
+        X = torch.from_numpy(synth.make_x(w, threads=CPU_THREADS)).cuda()
+        W16 = torch.from_numpy(synth.make_w(w, threads=CPU_THREADS)).cuda()
+        Wq, sw = mm.quantize_weight(W16)
+        ws = mm.new_workspace(T, K, N)
+        Y = torch.empty((T, N), dtype=torch.float16, device="cuda")
+        res = {"workload": name, "T": T, "K": K, "N": N, "planted": w.n_dims}
+        for tag, w16 in (("", W16), ("halved_", None)):
+            def step(i, e, w16=w16):
+                if e is not None:
+                    e[0].record()
+                mm.quantize_activations(X, N, w.tau, ws)
+                if e is not None:
+                    e[1].record()
+                mm.matmul_prepared(ws, T, K, Wq, sw, w16, out=Y)
+                if e is not None:
+                    e[2].record()
+            wall, evs = timed_loop(torch, steps, warmup, step)
+            act = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+            gemm = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+            res[tag + "ms"] = round(wall * 1e3 / steps, 4)
+            res[tag + "TOPS"] = round(2.0 * T * K * N * steps / wall / 1e12, 1)
+            res[tag + "activation_ms"] = round(act, 4)
+            res[tag + "gemm_ms"] = round(gemm, 4)
+        dbg = mm.mixed_matmul_debug(X, Wq, sw, W16, w.tau)
+        res["o"] = int(dbg["count"][0])
+        rows.append(res)
+        log(f"sweep {name}: o={res['o']}, {res['ms']:.3f} ms ({res['TOPS']} TOPS), "
+            f"memory-halved {res['halved_ms']:.3f} ms")
+        del X, W16, Wq, sw, ws, Y, dbg
+        torch.cuda.empty_cache()
+    return rows
+
+
 def cpu_baseline(synth, T, K, N):
     """The oracle, timed on the host cores, on a row sample of the prefill
     workload (outlier detection over all rows, the rest on the sample)."""
@@ -308,6 +355,14 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         log("copy calibration: 3 copies of 1 GiB")
+
+    if args.sweep:
+        rows = bench_sweep(torch, mm, synth, args.steps, args.warmup)
+        print(json.dumps({"metric": "int8-mixed matmul time vs outlier count, 175B-class "
+                                    "block projections at T=4096", "unit": "ms",
+                          "steps": args.steps, "warmup": args.warmup, "data": "synthetic",
+                          "results": rows}), flush=True)
+        return
 
     pre = dec = None
     if args.only in (None, "prefill"):
