@@ -63,6 +63,9 @@ class Oracle:
         lib.oracle_f16_encode.restype = ctypes.c_uint16
         lib.oracle_max_threads.restype = c_int
         lib.oracle_quantize_weight.argtypes = [vp, i64, i64, vp, vp, c_int]
+        lib.oracle_quantize_weight_typed.argtypes = [vp, c_int, i64, i64, vp, vp, c_int]
+        lib.oracle_bf16_decode.argtypes = [ctypes.c_uint16]
+        lib.oracle_bf16_decode.restype = ctypes.c_float
         lib.oracle_detect.argtypes = [vp, i64, i64, f32, vp]
         lib.oracle_compact.argtypes = [vp, i64, vp]
         lib.oracle_compact.restype = i64
@@ -96,6 +99,26 @@ class Oracle:
         sw = np.empty(N, np.float32)
         self.lib.oracle_quantize_weight(_p(W), K, N, _p(Wq), _p(sw), threads)
         return Wq, sw
+
+    WEIGHT_TYPES = {"f16": 0, "bf16": 1, "f32": 2}
+
+    def quantize_weight_typed(self, W: np.ndarray, wtype: str, threads: int = 0):
+        """A 16- or 32-bit checkpoint weight [K,N] -> (Wq int8 [N,K], s_w [N]).
+        wtype "f16" (float16 array), "bf16" (uint16 array of bfloat16 bits)
+        or "f32" (float32 array)."""
+        dt = {"f16": np.float16, "bf16": np.uint16, "f32": np.float32}[wtype]
+        W = np.ascontiguousarray(W)
+        if W.dtype != dt:
+            raise TypeError(f"{wtype} weight must be {np.dtype(dt)}, got {W.dtype}")
+        K, N = W.shape
+        Wq = np.empty((N, K), np.int8)
+        sw = np.empty(N, np.float32)
+        self.lib.oracle_quantize_weight_typed(_p(W), self.WEIGHT_TYPES[wtype], K, N, _p(Wq),
+                                              _p(sw), threads)
+        return Wq, sw
+
+    def bf16_decode(self, bits: int) -> float:
+        return float(self.lib.oracle_bf16_decode(bits))
 
     def detect(self, X: np.ndarray, tau: float) -> np.ndarray:
         """Outlier flags uint8 [K]."""

@@ -151,30 +151,52 @@ int oracle_max_threads(void) { return o_threads(0); }
 
 /* --------------------------------------------- step: weight quantization */
 
+/* bfloat16: the upper 16 bits of an IEEE binary32 (exact widening). */
+float oracle_bf16_decode(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
 /* Column-wise ("vector-wise", one constant per inner product) absmax int8
- * conversion of a 16-bit weight [A]: for every output column n,
- *   s_w[n] = max_k |W[k,n]|,  Wq[n,k] = quant(W[k,n], s_w[n]).
- * W is fp16 [K,N] row-major; Wq is stored [N,K] (K contiguous). */
-typedef struct { const uint16_t* W; int64_t K, N; int8_t* Wq; float* sw; } qw_ctx;
+ * conversion of a 16- or 32-bit checkpoint weight [A]: for every output
+ * column n,
+ *   s_w[n] = max_k |W[k,n]|,  Wq[n,k] = quant(W[k,n], s_w[n]),
+ * on the checkpoint's own values (fp16 and bf16 widen to fp32 exactly).
+ * W is [K,N] row-major of type 0 = fp16, 1 = bf16, 2 = fp32; Wq is stored
+ * [N,K] (K contiguous). */
+typedef struct { const void* W; int type; int64_t K, N; int8_t* Wq; float* sw; } qw_ctx;
+
+static float w_value(const qw_ctx* c, int64_t i) {
+    if (c->type == 1) return oracle_bf16_decode(((const uint16_t*)c->W)[i]);
+    if (c->type == 2) return ((const float*)c->W)[i];
+    return oh_f32(((const uint16_t*)c->W)[i]);
+}
 
 static void qw_span(void* p, int64_t lo, int64_t hi) {
     qw_ctx* c = (qw_ctx*)p;
     for (int64_t n = lo; n < hi; ++n) {
         float s = 0.0f;
         for (int64_t k = 0; k < c->K; ++k) {
-            float a = fabsf(oh_f32(c->W[k * c->N + n]));
+            float a = fabsf(w_value(c, k * c->N + n));
             if (a > s) s = a;
         }
         c->sw[n] = s;
         for (int64_t k = 0; k < c->K; ++k)
-            c->Wq[n * c->K + k] = quant_one(oh_f32(c->W[k * c->N + n]), s);
+            c->Wq[n * c->K + k] = quant_one(w_value(c, k * c->N + n), s);
     }
+}
+
+void oracle_quantize_weight_typed(const void* W, int type, int64_t K, int64_t N, int8_t* Wq,
+                                  float* sw, int nthreads) {
+    qw_ctx c = {W, type, K, N, Wq, sw};
+    o_parallel(N, nthreads, qw_span, &c);
 }
 
 void oracle_quantize_weight(const uint16_t* W, int64_t K, int64_t N, int8_t* Wq, float* sw,
                             int nthreads) {
-    qw_ctx c = {W, K, N, Wq, sw};
-    o_parallel(N, nthreads, qw_span, &c);
+    oracle_quantize_weight_typed(W, 0, K, N, Wq, sw, nthreads);
 }
 
 /* ---------------------------------------------- step: outlier detection */

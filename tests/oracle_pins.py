@@ -162,6 +162,60 @@ def pin_memory_halved_exact_weight(orc):
             "memory-halved with exact weights"
 
 
+def pin_bf16_decode(orc):
+    """Every bfloat16 bit pattern widens exactly as torch converts it."""
+    import torch
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).float().numpy()
+    mine = np.array([orc.bf16_decode(int(b)) for b in bits], np.float32)
+    same = (mine == ref) | (np.isnan(mine) & np.isnan(ref))
+    assert same.all(), "bf16 decode"
+
+
+def pin_typed_weight_hand(orc):
+    """Hand-derived conversions of an fp32 and a bf16 checkpoint column."""
+    g = _load("typed_weight.json")
+    f = g["f32"]
+    col = np.array(f["column"], np.float32)
+    assert col[0] == np.float32(1.0 - 2.0 ** -20)
+    Wq, sw = orc.quantize_weight_typed(col.reshape(-1, 1), "f32")
+    assert float(sw[0]) == f["sw"] and Wq[0].tolist() == f["q"], f"fp32 column: {Wq[0].tolist()}"
+    Wq16, _ = orc.quantize_weight(col.astype(np.float16).reshape(-1, 1))
+    assert Wq16[0].tolist() == f["q_if_fp16"], "the same column in fp16"
+    b = g["bf16"]
+    bits = np.array(b["column_bits"], np.uint16)
+    assert [orc.bf16_decode(int(x)) for x in bits] == b["column"]
+    Wq, sw = orc.quantize_weight_typed(bits.reshape(-1, 1), "bf16")
+    assert float(sw[0]) == b["sw"] and Wq[0].tolist() == b["q"], f"bf16 column: {Wq[0].tolist()}"
+
+
+def pin_typed_weight_containers(orc):
+    """The conversion depends on the values, not on the container: fp16
+    weights stored as fp32 (always exact) and as bf16 (when exact there)
+    give the fp16 result; fp32 weights satisfy the quantizer invariants."""
+    rng = np.random.default_rng(5)
+    for K, N in [(64, 48), (128, 24)]:
+        W = (rng.standard_normal((K, N)) * 0.02).astype(np.float16)
+        ref = orc.quantize_weight(W)
+        got = orc.quantize_weight_typed(W.astype(np.float32), "f32")
+        assert np.array_equal(ref[0], got[0]) and np.array_equal(ref[1], got[1]), "fp32 container"
+        # values with at most 8 significant bits are exact in bf16 and fp16
+        Wb = (np.round(rng.standard_normal((K, N)) * 64) / 256).astype(np.float16)
+        bits = (Wb.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        assert np.array_equal(bits.astype(np.uint32) << 16, Wb.astype(np.float32).view(np.uint32))
+        ref = orc.quantize_weight(Wb)
+        got = orc.quantize_weight_typed(bits, "bf16")
+        assert np.array_equal(ref[0], got[0]) and np.array_equal(ref[1], got[1]), "bf16 container"
+        # fp32 values: absmax element -> +-127, |x - q s/127| <= s/254 (1 + 2^-14)
+        W32 = (rng.standard_normal((K, N)) * 0.02).astype(np.float32)
+        Wq, sw = orc.quantize_weight_typed(W32, "f32")
+        assert np.array_equal(sw, np.abs(W32).max(axis=0)), "fp32 scale"
+        amax = np.abs(W32).argmax(axis=0)
+        assert np.array_equal(np.abs(Wq[np.arange(N), amax]), np.full(N, 127)), "absmax -> 127"
+        err = np.abs(W32.T.astype(np.float64) - Wq * (sw.astype(np.float64)[:, None] / 127.0))
+        assert np.all(err <= sw[:, None] / 254.0 * (1 + 2.0 ** -14)), "fp32 quantization error"
+
+
 def pin_quant_ties(orc):
     g = _load("quant_ties.json")
     for c in g["cases"]:
@@ -381,4 +435,5 @@ ALL_PINS = [pin_f16_codec, pin_hand_example, pin_quant_ties, pin_detect, pin_com
             pin_tiny_config, pin_quant_invariants, pin_gemm, pin_tau_inf, pin_tau_zero,
             pin_error_bound, pin_metamorphic_scale, pin_permutation, pin_row_sample,
             pin_hand_memory_halved, pin_dequant_weight, pin_memory_halved_tau_zero,
-            pin_memory_halved_exact_weight]
+            pin_memory_halved_exact_weight, pin_bf16_decode, pin_typed_weight_hand,
+            pin_typed_weight_containers]

@@ -26,13 +26,18 @@ MUTANTS = [
      "int32_t s = 0;\n            for (int64_t k = 0; k < c->K; ++k) s += (int32_t)a[k] * (int32_t)b[k];\n            if (s > INT32_MAX"),
     ("compact_reversed", "idx[o++] = (int32_t)k;", "idx[o++] = (int32_t)(K - 1 - k);"),
     ("f16_ties_away", "(frac == 0.5 && fmod(fl, 2.0) != 0.0)", "(frac == 0.5)"),
-    ("weight_scale_first_rows", "for (int64_t k = 0; k < c->K; ++k) {\n            float a = fabsf(oh_f32(c->W[k * c->N + n]));",
-     "for (int64_t k = 0; k < c->K / 2; ++k) {\n            float a = fabsf(oh_f32(c->W[k * c->N + n]));"),
+    ("weight_scale_first_rows", "for (int64_t k = 0; k < c->K; ++k) {\n            float a = fabsf(w_value(c, k * c->N + n));",
+     "for (int64_t k = 0; k < c->K / 2; ++k) {\n            float a = fabsf(w_value(c, k * c->N + n));"),
     ("outlier_value_from_wrong_row", "oh_decode(c->X[t * c->K + k]) * oh_decode(w)",
      "oh_decode(c->X[k]) * oh_decode(w)"),
     ("recovered_weight_unrounded", "y16 += oh_decode(c->X[t * c->K + k]) * oh_decode(w);",
      "y16 += oh_decode(c->X[t * c->K + k]) * (c->W16 ? oh_decode(w) : (double)((float)c->Wq[n * c->K + k] * (c->sw[n] / 127.0f)));"),
     ("recovered_weight_128", "const float d = sw / 127.0f;", "const float d = sw / 128.0f;"),
+    ("bf16_decode_shift", "uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;"),
+    ("f32_weight_read_as_f16", "if (c->type == 2) return ((const float*)c->W)[i];",
+     "if (c->type == 3) return ((const float*)c->W)[i];"),
+    ("f32_weight_rounded_to_f16", "if (c->type == 2) return ((const float*)c->W)[i];",
+     "if (c->type == 2) return oh_f32(oh_encode((double)((const float*)c->W)[i]));"),
     ("recovered_weight_transposed", "oracle_dequant_weight(c->Wq[n * c->K + k], c->sw[n])",
      "oracle_dequant_weight(c->Wq[(k * c->N + n) % (c->N * c->K)], c->sw[n])"),
     ("recovered_weight_ignored", ": oracle_dequant_weight(c->Wq[n * c->K + k], c->sw[n]);",
