@@ -92,6 +92,27 @@ int int8_quantize_weight_size(int64_t K, int64_t N, size_t* bytes);
 int int8_quantize_weight(const void* W16, int64_t K, int64_t N, int8_t* Wq, float* sw,
                          void* stream);
 
+/* Checkpoint types accepted by int8_quantize_weight_typed. */
+enum {
+    INT8MM_WEIGHT_F16 = 0,   /* IEEE binary16 */
+    INT8MM_WEIGHT_BF16 = 1,  /* bfloat16 (upper half of binary32) */
+    INT8MM_WEIGHT_F32 = 2    /* IEEE binary32 */
+};
+
+/* Weight conversion from a 16- or 32-bit checkpoint (LLM.int8() abstract: a
+ * 16/32-bit checkpoint is loaded, converted to Int8 and used immediately).
+ * The column scale and the codes are taken on the checkpoint's own values:
+ * s_w[n] = max_k |W[k,n]|, Wq[n,k] = clamp(rint(W[k,n] * fp32(127/s_w[n]))).
+ *   W:     [K,N] row-major of type wtype (read only)
+ *   Wq, sw: as int8_quantize_weight (written)
+ *   W16_out: NULL, or fp16 [K,N] (written): W rounded to fp16 (nearest
+ *          even), the 16-bit weight of the outlier path for checkpoints that
+ *          are not fp16.  With the memory-halved variant (W16 = NULL in the
+ *          matmul) no 16-bit copy is needed.
+ * Errors: E_NULL, E_SHAPE, E_ALIGN, E_UNSUPPORTED (unknown wtype), E_HIP. */
+int int8_quantize_weight_typed(const void* W, int wtype, int64_t K, int64_t N, int8_t* Wq,
+                               float* sw, void* W16_out, void* stream);
+
 /* The whole LLM.int8() matmul (steps 1-4 above) on a converted weight.
  *   X:   fp16 [T,K] activations (read only)
  *   Wq, sw: from int8_quantize_weight for the same K and N (read only)

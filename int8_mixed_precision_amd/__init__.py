@@ -26,6 +26,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libint8mm.so")
 
 OK, E_NULL, E_SHAPE, E_TAU, E_ALIGN, E_WORKSPACE, E_UNSUPPORTED, E_HIP = range(8)
+WEIGHT_F16, WEIGHT_BF16, WEIGHT_F32 = range(3)
 MAX_K = 133136
 
 EXPORTS = [
@@ -33,6 +34,7 @@ EXPORTS = [
     "int8_mixed_matmul_workspace_size",
     "int8_quantize_weight_size",
     "int8_quantize_weight",
+    "int8_quantize_weight_typed",
     "int8_mixed_matmul",
     "int8_mixed_matmul_debug",
     "int8mm_quantize_activations",
@@ -58,6 +60,7 @@ def _load() -> ctypes.CDLL:
     lib.int8_mixed_matmul_workspace_size.argtypes = [i64, i64, i64, ctypes.POINTER(sz)]
     lib.int8_quantize_weight_size.argtypes = [i64, i64, ctypes.POINTER(sz)]
     lib.int8_quantize_weight.argtypes = [vp, i64, i64, vp, vp, vp]
+    lib.int8_quantize_weight_typed.argtypes = [vp, c_int, i64, i64, vp, vp, vp, vp]
     lib.int8_mixed_matmul.argtypes = [vp, i64, i64, vp, vp, vp, i64, f32, vp, vp, sz, vp]
     lib.int8_mixed_matmul_debug.argtypes = [vp, i64, i64, vp, vp, vp, i64, f32, vp, vp, sz, vp,
                                             vp, vp, vp, vp, vp]
@@ -138,6 +141,27 @@ def quantize_weight(W16: torch.Tensor, out: tuple | None = None):
     _check(_lib.int8_quantize_weight(_ptr(W16), K, N, _ptr(Wq), _ptr(sw), _stream()),
            "int8_quantize_weight")
     return Wq, sw
+
+
+_WEIGHT_TYPES = {torch.float16: WEIGHT_F16, torch.bfloat16: WEIGHT_BF16,
+                 torch.float32: WEIGHT_F32}
+
+
+def quantize_checkpoint(W: torch.Tensor, fp16_copy: bool = False):
+    """A 16- or 32-bit checkpoint weight [K,N] (fp16, bf16 or fp32) ->
+    (Wq, sw, W16) with W16 the fp16 copy for the outlier path when
+    fp16_copy, else None (for the memory-halved variant)."""
+    if not isinstance(W, torch.Tensor) or W.dtype not in _WEIGHT_TYPES:
+        raise ValueError("W must be a float16, bfloat16 or float32 tensor")
+    _need(W, W.dtype, 2, "W")
+    K, N = W.shape
+    Wq = torch.empty(weight_bytes(K, N), dtype=torch.int8, device=W.device)
+    sw = torch.empty(N, dtype=torch.float32, device=W.device)
+    W16 = torch.empty((K, N), dtype=torch.float16, device=W.device) if fp16_copy else None
+    _check(_lib.int8_quantize_weight_typed(_ptr(W), _WEIGHT_TYPES[W.dtype], K, N, _ptr(Wq),
+                                           _ptr(sw), _ptr(W16), _stream()),
+           "int8_quantize_weight_typed")
+    return Wq, sw, W16
 
 
 def _mm_args(X, Wq, sw, W16):

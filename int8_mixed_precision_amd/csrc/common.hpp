@@ -60,8 +60,10 @@ hipError_t launch_activation_pass(const _Float16* X, int64_t T, int64_t K, float
                                   const Workspace& ws, hipStream_t stream);
 
 // ---- weight side (k_weight.hip)
-hipError_t launch_quantize_weight(const _Float16* W, int64_t K, int64_t N, int8_t* Wq, float* sw,
-                                  hipStream_t stream);
+// weight checkpoint types (the values of INT8MM_WEIGHT_* in include/int8mm.h)
+constexpr int kWeightF16 = 0, kWeightBF16 = 1, kWeightF32 = 2;
+hipError_t launch_quantize_weight(const void* W, int wtype, int64_t K, int64_t N, int8_t* Wq,
+                                  float* sw, _Float16* w16, hipStream_t stream);
 
 // ---- int8 GEMM + dequantization + 16-bit outlier GEMM (k_gemm.hip)
 struct GemmArgs {

@@ -98,14 +98,26 @@ int int8_quantize_weight_size(int64_t K, int64_t N, size_t* bytes) {
     return INT8MM_OK;
 }
 
-int int8_quantize_weight(const void* W16, int64_t K, int64_t N, int8_t* Wq, float* sw,
-                         void* stream) {
-    if (!W16 || !Wq || !sw) return INT8MM_E_NULL;
+int int8_quantize_weight_typed(const void* W, int wtype, int64_t K, int64_t N, int8_t* Wq,
+                               float* sw, void* W16_out, void* stream) {
+    static_assert(INT8MM_WEIGHT_F16 == kWeightF16 && INT8MM_WEIGHT_BF16 == kWeightBF16 &&
+                      INT8MM_WEIGHT_F32 == kWeightF32,
+                  "weight type codes");
+    if (!W || !Wq || !sw) return INT8MM_E_NULL;
     int st = check_shape(1, K, N);
     if (st) return st;
-    if (!aligned16(W16) || !aligned16(Wq) || !aligned16(sw)) return INT8MM_E_ALIGN;
-    return hip_status(launch_quantize_weight(static_cast<const _Float16*>(W16), K, N, Wq, sw,
+    if (wtype != INT8MM_WEIGHT_F16 && wtype != INT8MM_WEIGHT_BF16 && wtype != INT8MM_WEIGHT_F32)
+        return INT8MM_E_UNSUPPORTED;
+    if (!aligned16(W) || !aligned16(Wq) || !aligned16(sw) || (W16_out && !aligned16(W16_out)))
+        return INT8MM_E_ALIGN;
+    return hip_status(launch_quantize_weight(W, wtype, K, N, Wq, sw,
+                                             static_cast<_Float16*>(W16_out),
                                              static_cast<hipStream_t>(stream)));
+}
+
+int int8_quantize_weight(const void* W16, int64_t K, int64_t N, int8_t* Wq, float* sw,
+                         void* stream) {
+    return int8_quantize_weight_typed(W16, INT8MM_WEIGHT_F16, K, N, Wq, sw, nullptr, stream);
 }
 
 int int8_mixed_matmul(const void* X, int64_t T, int64_t K, const int8_t* Wq, const float* sw,

@@ -1,7 +1,9 @@
-// Weight side of LLM.int8(): a 16-bit weight is converted to Int8 once, at
-// load time (LLM.int8() abstract, taxoreview.com page dblp:280/8696, second
-// paragraph), with one absmax scale per output column n - the column is one
-// operand of the inner products that produce column n of Y.
+// Weight side of LLM.int8(): a 16- or 32-bit checkpoint weight (fp16, bf16
+// or fp32) is converted to Int8 once, at load time (LLM.int8() abstract,
+// taxoreview.com page dblp:280/8696, second paragraph), with one absmax
+// scale per output column n - the column is one operand of the inner
+// products that produce column n of Y.  The scale and the codes are taken
+// on the checkpoint's own values.
 //
 //   s_w[n] = max_k |W[k,n]|,  Wq[n,k] = clamp(rint(W[k,n] * fp32(127/s_w[n])), -127, 127)
 //
@@ -10,7 +12,7 @@
 //
 // Two HBM-bound passes: a column-absmax reduction (16-byte loads along rows,
 // one atomicMax per column per workgroup) and a tiled quantize + transpose
-// through LDS (coalesced fp16 reads along N, coalesced int8 writes along K).
+// through LDS (coalesced reads along N, coalesced int8 writes along K).
 #include "common.hpp"
 
 // Quantization must round x * r and any following add separately, exactly
@@ -30,6 +32,28 @@ constexpr int kTrK = 128;                   // k extent of a tile
 constexpr int kTrN = 64;                    // n extent of a tile
 
 __device__ inline float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+__device__ inline float bf2f(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
+
+// Eight consecutive weight values starting at element `off` (a multiple of
+// 8) of a [K,N] checkpoint of type WT, widened to fp32 (exact for fp16 and
+// bf16): one 16-byte load for the 16-bit types, two for fp32.
+template <int WT>
+__device__ inline void load8(const void* W, int64_t off, float (&v)[8]) {
+    if (WT == kWeightF32) {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(W) + off);
+        const float4 a = p[0], b = p[1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W) + off);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint16_t b = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
+            v[e] = WT == kWeightBF16 ? bf2f(b) : h2f(b);
+        }
+    }
+}
 
 __global__ void k_zero_f32(float* __restrict__ p, int64_t n) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -38,33 +62,29 @@ __global__ void k_zero_f32(float* __restrict__ p, int64_t n) {
 
 // Column absmax over the workgroup's rows; merged into sw with an unsigned
 // atomicMax on the float bits (valid because every value is >= +0).
-__global__ __launch_bounds__(kColThreads) void k_colmax(const uint16_t* __restrict__ W, int64_t K,
+template <int WT>
+__global__ __launch_bounds__(kColThreads) void k_colmax(const void* __restrict__ W, int64_t K,
                                                         int64_t N, float* __restrict__ sw) {
     const int64_t c0 = ((int64_t)blockIdx.x * kColThreads + threadIdx.x) * 8;
     if (c0 >= N) return;
     const int64_t k0 = (int64_t)blockIdx.y * kColRows;
     const int64_t k1 = k0 + kColRows < K ? k0 + kColRows : K;
     float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    const uint16_t* p = W + k0 * N + c0;
     int64_t k = k0;
-    for (; k + 4 <= k1; k += 4, p += 4 * N) {
-        uint4 v[4];
+    for (; k + 4 <= k1; k += 4) {
+        float v[4][8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const uint4*>(p + u * N);
+        for (int u = 0; u < 4; ++u) load8<WT>(W, (k + u) * N + c0, v[u]);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                m[e] = __builtin_fmaxf(m[e], __builtin_fabsf(h2f((uint16_t)(w[e >> 1] >> ((e & 1) * 16)))));
-        }
+            for (int e = 0; e < 8; ++e) m[e] = __builtin_fmaxf(m[e], __builtin_fabsf(v[u][e]));
     }
-    for (; k < k1; ++k, p += N) {
-        uint4 v = *reinterpret_cast<const uint4*>(p);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    for (; k < k1; ++k) {
+        float v[8];
+        load8<WT>(W, k * N + c0, v);
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            m[e] = __builtin_fmaxf(m[e], __builtin_fabsf(h2f((uint16_t)(w[e >> 1] >> ((e & 1) * 16)))));
+        for (int e = 0; e < 8; ++e) m[e] = __builtin_fmaxf(m[e], __builtin_fabsf(v[e]));
     }
     unsigned int* swu = reinterpret_cast<unsigned int*>(sw);
 #pragma unroll
@@ -80,17 +100,21 @@ __device__ inline int8_t quant(float x, float r) {
 
 // One tile of kTrK rows (k) by kTrN columns (n): read W[k0.., n0..] along n,
 // quantize with the column's scale, transpose through LDS, write Wq[n0.., k0..]
-// along k.
-__global__ __launch_bounds__(kTrThreads) void k_quant_transpose(const uint16_t* __restrict__ W,
+// along k.  With w16 given, the fp16 copy of the values (round to nearest
+// even) is written to w16[k, n] on the way (the 16-bit weight of the outlier
+// path, for checkpoints that are not fp16).
+template <int WT>
+__global__ __launch_bounds__(kTrThreads) void k_quant_transpose(const void* __restrict__ W,
                                                                 int64_t K, int64_t N,
                                                                 const float* __restrict__ sw,
-                                                                int8_t* __restrict__ Wq) {
+                                                                int8_t* __restrict__ Wq,
+                                                                _Float16* __restrict__ w16) {
     // +16 bytes per row spreads the transposed byte stores over banks
     __shared__ __attribute__((aligned(16))) int8_t tile[kTrN][kTrK + 16];
     const int tid = threadIdx.x;
     const int64_t n0 = (int64_t)blockIdx.x * kTrN;
     const int64_t k0 = (int64_t)blockIdx.y * kTrK;
-    // read phase: 8 lanes cover one 64-column row segment (8 halves each)
+    // read phase: 8 lanes cover one 64-column row segment (8 values each)
     const int cn = (tid & 7) * 8;           // column inside the tile
     const int64_t n = n0 + cn;
     float r[8];
@@ -101,14 +125,20 @@ __global__ __launch_bounds__(kTrThreads) void k_quant_transpose(const uint16_t* 
     }
     for (int kr = tid >> 3; kr < kTrK; kr += kTrThreads / 8) {
         const int64_t k = k0 + kr;
-        uint32_t w[4] = {0u, 0u, 0u, 0u};
+        float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         if (k < K && n < N) {
-            uint4 v = *reinterpret_cast<const uint4*>(W + k * N + n);
-            w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+            load8<WT>(W, k * N + n, v);
+            if (w16) {
+                uint32_t h[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    h[e] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[2 * e]) |
+                           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[2 * e + 1]) << 16);
+                *reinterpret_cast<uint4*>(w16 + k * N + n) = make_uint4(h[0], h[1], h[2], h[3]);
+            }
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            tile[cn + e][kr] = quant(h2f((uint16_t)(w[e >> 1] >> ((e & 1) * 16))), r[e]);
+        for (int e = 0; e < 8; ++e) tile[cn + e][kr] = quant(v[e], r[e]);
     }
     __syncthreads();
     // write phase: 8 lanes cover one 128-byte row of Wq
@@ -121,17 +151,27 @@ __global__ __launch_bounds__(kTrThreads) void k_quant_transpose(const uint16_t* 
     }
 }
 
+template <int WT>
+hipError_t launch_typed(const void* W, int64_t K, int64_t N, int8_t* Wq, float* sw,
+                        _Float16* w16, hipStream_t stream) {
+    hipLaunchKernelGGL(k_zero_f32, dim3((unsigned)ceil_div(N, 256)), dim3(256), 0, stream, sw, N);
+    hipLaunchKernelGGL(k_colmax<WT>, dim3((unsigned)ceil_div(N, kColCols), (unsigned)ceil_div(K, kColRows)),
+                       dim3(kColThreads), 0, stream, W, K, N, sw);
+    hipLaunchKernelGGL(k_quant_transpose<WT>, dim3((unsigned)ceil_div(N, kTrN), (unsigned)ceil_div(K, kTrK)),
+                       dim3(kTrThreads), 0, stream, W, K, N, sw, Wq, w16);
+    return hipGetLastError();
+}
+
 }  // namespace
 
-hipError_t launch_quantize_weight(const _Float16* W, int64_t K, int64_t N, int8_t* Wq, float* sw,
-                                  hipStream_t stream) {
-    const uint16_t* wb = reinterpret_cast<const uint16_t*>(W);
-    hipLaunchKernelGGL(k_zero_f32, dim3((unsigned)ceil_div(N, 256)), dim3(256), 0, stream, sw, N);
-    hipLaunchKernelGGL(k_colmax, dim3((unsigned)ceil_div(N, kColCols), (unsigned)ceil_div(K, kColRows)),
-                       dim3(kColThreads), 0, stream, wb, K, N, sw);
-    hipLaunchKernelGGL(k_quant_transpose, dim3((unsigned)ceil_div(N, kTrN), (unsigned)ceil_div(K, kTrK)),
-                       dim3(kTrThreads), 0, stream, wb, K, N, sw, Wq);
-    return hipGetLastError();
+hipError_t launch_quantize_weight(const void* W, int wtype, int64_t K, int64_t N, int8_t* Wq,
+                                  float* sw, _Float16* w16, hipStream_t stream) {
+    switch (wtype) {
+        case kWeightF16: return launch_typed<kWeightF16>(W, K, N, Wq, sw, w16, stream);
+        case kWeightBF16: return launch_typed<kWeightBF16>(W, K, N, Wq, sw, w16, stream);
+        case kWeightF32: return launch_typed<kWeightF32>(W, K, N, Wq, sw, w16, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace i8mm

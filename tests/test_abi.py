@@ -27,7 +27,7 @@ def header_functions():
 def test_header_lists_entry_points():
     names = header_functions()
     assert "int8_mixed_matmul" in names and "int8_quantize_weight" in names
-    assert len(names) == 8, names
+    assert len(names) == 9, names
 
 
 def test_exports_every_declared_symbol(mm):
@@ -106,6 +106,16 @@ def test_quantize_weight_validation(mm):
     assert lib.int8_quantize_weight(vp(FAKE), 60, 48, vp(FAKE), vp(FAKE), None) == mm.E_SHAPE
     assert lib.int8_quantize_weight(vp(FAKE), 64, 47, vp(FAKE), vp(FAKE), None) == mm.E_SHAPE
     assert lib.int8_quantize_weight(vp(FAKE), 64, 48, vp(FAKE + 3), vp(FAKE), None) == mm.E_ALIGN
+
+
+def test_quantize_weight_typed_validation(mm):
+    lib, vp = mm.lib(), ctypes.c_void_p
+    q = lib.int8_quantize_weight_typed
+    assert q(None, mm.WEIGHT_F32, 64, 48, vp(FAKE), vp(FAKE), None, None) == mm.E_NULL
+    assert q(vp(FAKE), mm.WEIGHT_BF16, 60, 48, vp(FAKE), vp(FAKE), None, None) == mm.E_SHAPE
+    assert q(vp(FAKE), 3, 64, 48, vp(FAKE), vp(FAKE), None, None) == mm.E_UNSUPPORTED
+    assert q(vp(FAKE), -1, 64, 48, vp(FAKE), vp(FAKE), None, None) == mm.E_UNSUPPORTED
+    assert q(vp(FAKE), mm.WEIGHT_F32, 64, 48, vp(FAKE), vp(FAKE), vp(FAKE + 2), None) == mm.E_ALIGN
 
 
 def test_staged_entry_points_validation(mm):
