@@ -48,6 +48,20 @@ def _f16(a) -> np.ndarray:
     return a
 
 
+HTYPES = {"f16": 0, "bf16": 1}
+
+
+def _h16(a, htype: str) -> np.ndarray:
+    """A 16-bit array of the given type: float16 for "f16", uint16 bit
+    patterns for "bf16" (numpy has no bfloat16)."""
+    if htype == "f16":
+        return _f16(a)
+    a = np.ascontiguousarray(a)
+    if htype != "bf16" or a.dtype != np.uint16:
+        raise TypeError(f"expected {htype} data (uint16 bits for bf16), got {a.dtype}")
+    return a
+
+
 class Oracle:
     """One loaded build of ``oracle.c`` (the default one, or a variant a test
     compiled from an edited copy)."""
@@ -66,18 +80,22 @@ class Oracle:
         lib.oracle_quantize_weight_typed.argtypes = [vp, c_int, i64, i64, vp, vp, c_int]
         lib.oracle_bf16_decode.argtypes = [ctypes.c_uint16]
         lib.oracle_bf16_decode.restype = ctypes.c_float
-        lib.oracle_detect.argtypes = [vp, i64, i64, f32, vp]
+        lib.oracle_detect.argtypes = [vp, i64, i64, f32, vp, c_int]
         lib.oracle_compact.argtypes = [vp, i64, vp]
         lib.oracle_compact.restype = i64
-        lib.oracle_quantize_rows.argtypes = [vp, i64, i64, vp, vp, i64, vp, vp]
+        lib.oracle_quantize_rows.argtypes = [vp, i64, i64, vp, vp, i64, vp, vp, c_int]
         lib.oracle_int8_gemm.argtypes = [vp, i64, i64, vp, i64, vp, c_int]
         lib.oracle_int8_gemm.restype = i64
         lib.oracle_output.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp,
-                                      vp, c_int]
+                                      vp, c_int, c_int]
+        lib.oracle_dequant_weight_h.argtypes = [ctypes.c_int8, f32, c_int]
+        lib.oracle_dequant_weight_h.restype = ctypes.c_uint16
+        lib.oracle_bf16_encode.argtypes = [ctypes.c_double]
+        lib.oracle_bf16_encode.restype = ctypes.c_uint16
         lib.oracle_dequant_weight.argtypes = [ctypes.c_int8, f32]
         lib.oracle_dequant_weight.restype = ctypes.c_uint16
         lib.oracle_mixed_matmul.argtypes = [vp, i64, i64, vp, vp, vp, i64, f32, vp, i64,
-                                            vp, vp, vp, vp, vp, vp, vp, c_int]
+                                            vp, vp, vp, vp, vp, vp, vp, c_int, c_int]
         lib.oracle_mixed_matmul.restype = i64
         self.lib = lib
         self.path = path
@@ -120,12 +138,15 @@ class Oracle:
     def bf16_decode(self, bits: int) -> float:
         return float(self.lib.oracle_bf16_decode(bits))
 
-    def detect(self, X: np.ndarray, tau: float) -> np.ndarray:
+    def bf16_encode(self, x: float) -> int:
+        return int(self.lib.oracle_bf16_encode(float(x)))
+
+    def detect(self, X: np.ndarray, tau: float, htype: str = "f16") -> np.ndarray:
         """Outlier flags uint8 [K]."""
-        X = _f16(X)
+        X = _h16(X, htype)
         T, K = X.shape
         flag = np.empty(K, np.uint8)
-        self.lib.oracle_detect(_p(X), T, K, tau, _p(flag))
+        self.lib.oracle_detect(_p(X), T, K, tau, _p(flag), HTYPES[htype])
         return flag
 
     def compact(self, flag: np.ndarray) -> np.ndarray:
@@ -134,16 +155,17 @@ class Oracle:
         o = self.lib.oracle_compact(_p(flag), len(flag), _p(idx))
         return idx[:o].copy()
 
-    def quantize_rows(self, X: np.ndarray, flag: np.ndarray, rows=None):
+    def quantize_rows(self, X: np.ndarray, flag: np.ndarray, rows=None, htype: str = "f16"):
         """(Xq int8 [M,K], s_x float32 [M]) for the listed rows (all when None)."""
-        X = _f16(X)
+        X = _h16(X, htype)
         T, K = X.shape
         flag = np.ascontiguousarray(flag, np.uint8)
         r = None if rows is None else np.ascontiguousarray(rows, np.int64)
         M = T if r is None else len(r)
         Xq = np.empty((M, K), np.int8)
         sx = np.empty(M, np.float32)
-        self.lib.oracle_quantize_rows(_p(X), T, K, _p(flag), _p(r), M, _p(Xq), _p(sx))
+        self.lib.oracle_quantize_rows(_p(X), T, K, _p(flag), _p(r), M, _p(Xq), _p(sx),
+                                      HTYPES[htype])
         return Xq, sx
 
     def int8_gemm(self, Xq: np.ndarray, Wq: np.ndarray, threads: int = 0):
@@ -158,18 +180,20 @@ class Oracle:
             raise OverflowError(f"{bad} accumulators do not fit int32")
         return acc
 
-    def dequant_weight(self, q: int, sw: float) -> int:
-        """fp16 bits of the weight value recovered from Int8 code q and
+    def dequant_weight(self, q: int, sw: float, htype: str = "f16") -> int:
+        """16-bit bits of the weight value recovered from Int8 code q and
         column scale sw (memory-halved variant)."""
-        return int(self.lib.oracle_dequant_weight(int(q), float(sw)))
+        return int(self.lib.oracle_dequant_weight_h(int(q), float(sw), HTYPES[htype]))
 
-    def output(self, acc, sx, sw, X, W16, idx, rows=None, threads: int = 0, Wq=None):
-        """(Y fp16 [M,N], Y64 float64 [M,N] before the final rounding).
-        W16 None: memory-halved variant, outlier rows recovered from Wq."""
-        X = _f16(X)
+    def output(self, acc, sx, sw, X, W16, idx, rows=None, threads: int = 0, Wq=None,
+               htype: str = "f16"):
+        """(Y [M,N] (float16, or uint16 bf16 bits), Y64 float64 [M,N] before
+        the final rounding).  W16 None: memory-halved variant, outlier rows
+        recovered from Wq."""
+        X = _h16(X, htype)
         K = X.shape[1]
         if W16 is not None:
-            W16 = _f16(W16)
+            W16 = _h16(W16, htype)
             N = W16.shape[1]
         else:
             Wq = np.ascontiguousarray(Wq, np.int8)
@@ -178,23 +202,25 @@ class Oracle:
         M = acc.shape[0]
         idx = np.ascontiguousarray(idx, np.int32)
         r = None if rows is None else np.ascontiguousarray(rows, np.int64)
-        Y = np.empty((M, N), np.float16)
+        Y = np.empty((M, N), np.float16 if htype == "f16" else np.uint16)
         Y64 = np.empty((M, N), np.float64)
         self.lib.oracle_output(_p(acc), _p(np.ascontiguousarray(sx, np.float32)),
                                _p(np.ascontiguousarray(sw, np.float32)), _p(X), _p(W16),
                                _p(Wq if W16 is None else None), _p(r), M, K, N, _p(idx), len(idx),
-                               _p(Y), _p(Y64), threads)
+                               _p(Y), _p(Y64), threads, HTYPES[htype])
         return Y, Y64
 
-    def mixed_matmul(self, X, Wq, sw, W16, tau: float, rows=None, threads: int = 0):
+    def mixed_matmul(self, X, Wq, sw, W16, tau: float, rows=None, threads: int = 0,
+                     htype: str = "f16"):
         """The whole method.  Returns a dict with flag, idx, o, xq, sx, acc,
         Y, Y64 (xq/sx/acc/Y/Y64 for the sampled rows when `rows` is given).
-        W16 None: the memory-halved variant."""
-        X = _f16(X)
+        W16 None: the memory-halved variant.  htype "bf16": X, W16 and Y are
+        bfloat16 (uint16 bit arrays)."""
+        X = _h16(X, htype)
         T, K = X.shape
         Wq = np.ascontiguousarray(Wq, np.int8)
         if W16 is not None:
-            W16 = _f16(W16)
+            W16 = _h16(W16, htype)
         N = Wq.shape[0]
         sw = np.ascontiguousarray(sw, np.float32)
         r = None if rows is None else np.ascontiguousarray(rows, np.int64)
@@ -204,11 +230,11 @@ class Oracle:
         xq = np.empty((M, K), np.int8)
         sx = np.empty(M, np.float32)
         acc = np.empty((M, N), np.int32)
-        Y = np.empty((M, N), np.float16)
+        Y = np.empty((M, N), np.float16 if htype == "f16" else np.uint16)
         Y64 = np.empty((M, N), np.float64)
         o = self.lib.oracle_mixed_matmul(_p(X), T, K, _p(Wq), _p(sw), _p(W16), N, tau, _p(r), M,
                                          _p(flag), _p(idx), _p(xq), _p(sx), _p(acc), _p(Y),
-                                         _p(Y64), threads)
+                                         _p(Y64), threads, HTYPES[htype])
         if o == -2:
             raise OverflowError("int32 accumulator overflow")
         if o < 0:

@@ -36,7 +36,11 @@
  *     "cut by half"): the outlier rows of W are recovered from the Int8
  *     weight, W^[k,n] = fp16(fp32(q[n,k] * fp32(s_w[n] / 127))) (an IEEE fp32
  *     divide, one fp32 multiply, one rounding to fp16, each to nearest even),
- *     and the 16-bit part multiplies X[t,k] by W^[k,n] instead.
+ *     and the 16-bit part multiplies X[t,k] by W^[k,n] instead;
+ *   - bf16 variant ("16-bit" is not specified on the pages): X, W16 and Y
+ *     are bfloat16 instead of fp16; every step is the same, values widen to
+ *     fp32 exactly, Y is rounded once to the nearest bf16 (ties to even) and
+ *     a recovered weight value is rounded to bf16.
  *
  * Parity pins: every function below is checked in tests/ against values
  * that do not come from this file (hand-derived examples, closed forms,
@@ -97,6 +101,44 @@ uint16_t oracle_f16_encode(double x) { return oh_encode(x); }
 /* fp32 value of an fp16 element (exact: binary16 is a subset of binary32). */
 static float oh_f32(uint16_t h) { return (float)oh_decode(h); }
 
+/* ------------------------------------------------------------ bf16 codec */
+
+/* bfloat16: the upper 16 bits of an IEEE binary32 (exact widening). */
+float oracle_bf16_decode(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Nearest bfloat16 to a double, ties to even (one rounding): 8 significant
+ * bits, the binary32 exponent range, subnormal step 2^-133. */
+uint16_t oracle_bf16_encode(double x) {
+    if (isnan(x)) return 0x7FC0;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    /* Largest finite is (2 - 2^-7) * 2^127; halfway to 2^128 is
+       (2 - 2^-8) * 2^127, and that tie goes to the even neighbour 2^128. */
+    if (a >= ldexp(2.0 - ldexp(1.0, -8), 127)) return sign | 0x7F80;
+    int e = -126;                                   /* subnormals share 2^-133 */
+    if (a >= ldexp(1.0, -126)) e = ilogb(a);        /* 2^e <= a < 2^(e+1) */
+    double step = ldexp(1.0, e - 7);
+    double q = a / step;                            /* exact: power-of-two divide */
+    double fl = floor(q);
+    double frac = q - fl;
+    double n = fl;
+    if (frac > 0.5 || (frac == 0.5 && fmod(fl, 2.0) != 0.0)) n = fl + 1.0;
+    float r = (float)(n * step);                    /* exact: a bfloat16 value */
+    uint32_t u;
+    memcpy(&u, &r, sizeof u);
+    return sign | (uint16_t)(u >> 16);
+}
+
+/* The 16-bit element types of X, W16 and Y: 0 = fp16, 1 = bf16. */
+static double h_decode(int ht, uint16_t b) { return ht ? (double)oracle_bf16_decode(b) : oh_decode(b); }
+static float h_f32(int ht, uint16_t b) { return (float)h_decode(ht, b); }
+static uint16_t h_encode(int ht, double x) { return ht ? oracle_bf16_encode(x) : oh_encode(x); }
+
 /* ---------------------------------------------------- the quantizer itself */
 
 /* Symmetric absmax quantization of one value with scale s (see header). */
@@ -151,14 +193,6 @@ int oracle_max_threads(void) { return o_threads(0); }
 
 /* --------------------------------------------- step: weight quantization */
 
-/* bfloat16: the upper 16 bits of an IEEE binary32 (exact widening). */
-float oracle_bf16_decode(uint16_t b) {
-    uint32_t u = (uint32_t)b << 16;
-    float f;
-    memcpy(&f, &u, sizeof f);
-    return f;
-}
-
 /* Column-wise ("vector-wise", one constant per inner product) absmax int8
  * conversion of a 16- or 32-bit checkpoint weight [A]: for every output
  * column n,
@@ -203,12 +237,12 @@ void oracle_quantize_weight(const uint16_t* W, int64_t K, int64_t N, int8_t* Wq,
 
 /* Outlier feature dimensions [A], found by magnitude [S]:
  *   flag[k] = 1 iff |X[t,k]| >= tau for some row t.
- * The fp16 value is compared exactly (in fp32). */
-void oracle_detect(const uint16_t* X, int64_t T, int64_t K, float tau, uint8_t* flag) {
+ * The 16-bit value (fp16 or bf16, type ht) is compared exactly (in fp32). */
+void oracle_detect(const uint16_t* X, int64_t T, int64_t K, float tau, uint8_t* flag, int ht) {
     for (int64_t k = 0; k < K; ++k) {
         flag[k] = 0;
         for (int64_t t = 0; t < T; ++t) {
-            if (fabsf(oh_f32(X[t * K + k])) >= tau) { flag[k] = 1; break; }
+            if (fabsf(h_f32(ht, X[t * K + k])) >= tau) { flag[k] = 1; break; }
         }
     }
 }
@@ -231,7 +265,7 @@ int64_t oracle_compact(const uint8_t* flag, int64_t K, int32_t* idx) {
  * rows == NULL quantizes every row; otherwise row m of the output is row
  * rows[m] of X (a sample). */
 void oracle_quantize_rows(const uint16_t* X, int64_t T, int64_t K, const uint8_t* flag,
-                          const int64_t* rows, int64_t M, int8_t* Xq, float* sx) {
+                          const int64_t* rows, int64_t M, int8_t* Xq, float* sx, int ht) {
     (void)T;
     for (int64_t m = 0; m < M; ++m) {
         int64_t t = rows ? rows[m] : m;
@@ -239,12 +273,12 @@ void oracle_quantize_rows(const uint16_t* X, int64_t T, int64_t K, const uint8_t
         float s = 0.0f;
         for (int64_t k = 0; k < K; ++k) {
             if (flag[k]) continue;
-            float a = fabsf(oh_f32(xr[k]));
+            float a = fabsf(h_f32(ht, xr[k]));
             if (a > s) s = a;
         }
         sx[m] = s;
         for (int64_t k = 0; k < K; ++k)
-            Xq[m * K + k] = flag[k] ? 0 : quant_one(oh_f32(xr[k]), s);
+            Xq[m * K + k] = flag[k] ? 0 : quant_one(h_f32(ht, xr[k]), s);
     }
 }
 
@@ -313,25 +347,28 @@ int64_t oracle_int8_gemm(const int8_t* Xq, int64_t M, int64_t K, const int8_t* W
  * 16-bit matrix multiplication over the isolated outlier dimensions [A]:
  *   y8  = acc[m,n] * s_x[m] * s_w[n] / 127^2
  *   y16 = sum_{j<o} X[t,idx_j] * W[idx_j,n]       (t = rows[m] or m)
- *   Y   = fp16(y8 + y16)
- * all in fp64 (fp16 x fp16 products are exact there).  Y64, when given,
+ *   Y   = fp16(y8 + y16)   (bf16 when ht = 1: the bf16 variant of the path)
+ * all in fp64 (fp16 x fp16 and bf16 x bf16 products are exact there).  Y64, when given,
  * receives y8 + y16 before the final rounding.  Without W16 (NULL), the
  * memory-halved variant: W[idx_j,n] is the fp16 value recovered from the
  * Int8 weight, see oracle_dequant_weight. */
 typedef struct {
     const int32_t* acc; const float* sx; const float* sw; const uint16_t* X; const uint16_t* W16;
     const int8_t* Wq; const int64_t* rows; int64_t M, K, N; const int32_t* idx; int64_t o;
-    uint16_t* Y; double* Y64;
+    uint16_t* Y; double* Y64; int ht;
 } out_ctx;
 
-/* The 16-bit value of weight element (k, n) recovered from its Int8 code
- * q = Wq[n,k] and column scale s_w[n]: fp16(fp32(q * fp32(s_w / 127))),
- * each step rounded to nearest even (the divide an IEEE fp32 divide). */
-uint16_t oracle_dequant_weight(int8_t q, float sw) {
+/* The 16-bit value (type ht) of weight element (k, n) recovered from its
+ * Int8 code q = Wq[n,k] and column scale s_w[n]: fp16(fp32(q * fp32(s_w/127)))
+ * (bf16 for ht = 1), each step rounded to nearest even (the divide an IEEE
+ * fp32 divide). */
+uint16_t oracle_dequant_weight_h(int8_t q, float sw, int ht) {
     const float d = sw / 127.0f;
     const float v = (float)q * d;
-    return oh_encode((double)v);
+    return h_encode(ht, (double)v);
 }
+
+uint16_t oracle_dequant_weight(int8_t q, float sw) { return oracle_dequant_weight_h(q, sw, 0); }
 
 static void out_span(void* p, int64_t lo, int64_t hi) {
     out_ctx* c = (out_ctx*)p;
@@ -343,12 +380,12 @@ static void out_span(void* p, int64_t lo, int64_t hi) {
             for (int64_t j = 0; j < c->o; ++j) {
                 int64_t k = c->idx[j];
                 const uint16_t w = c->W16 ? c->W16[k * c->N + n]
-                                          : oracle_dequant_weight(c->Wq[n * c->K + k], c->sw[n]);
-                y16 += oh_decode(c->X[t * c->K + k]) * oh_decode(w);
+                                          : oracle_dequant_weight_h(c->Wq[n * c->K + k], c->sw[n], c->ht);
+                y16 += h_decode(c->ht, c->X[t * c->K + k]) * h_decode(c->ht, w);
             }
             double y = y8 + y16;
             if (c->Y64) c->Y64[m * c->N + n] = y;
-            c->Y[m * c->N + n] = oh_encode(y);
+            c->Y[m * c->N + n] = h_encode(c->ht, y);
         }
     }
 }
@@ -356,15 +393,16 @@ static void out_span(void* p, int64_t lo, int64_t hi) {
 void oracle_output(const int32_t* acc, const float* sx, const float* sw, const uint16_t* X,
                    const uint16_t* W16, const int8_t* Wq, const int64_t* rows, int64_t M,
                    int64_t K, int64_t N, const int32_t* idx, int64_t o, uint16_t* Y, double* Y64,
-                   int nthreads) {
-    out_ctx c = {acc, sx, sw, X, W16, Wq, rows, M, K, N, idx, o, Y, Y64};
+                   int nthreads, int ht) {
+    out_ctx c = {acc, sx, sw, X, W16, Wq, rows, M, K, N, idx, o, Y, Y64, ht};
     o_parallel(M, nthreads, out_span, &c);
 }
 
 /* ----------------------------------------------------- the whole method */
 
 /* All steps in the pages' order, on a quantized weight (Wq, s_w) and the
- * 16-bit weight W16 (NULL: the memory-halved variant): detect -> isolate ->
+ * 16-bit weight W16 (NULL: the memory-halved variant), with X, W16 and Y of
+ * 16-bit type ht (0 fp16, 1 bf16): detect -> isolate ->
  * quantize rows -> int8 matmul -> dequantize + 16-bit outlier matmul.  Detection always looks at all T rows
  * of X; the other steps run on the M rows listed in `rows` (all when NULL).
  * Outputs (any but Y may be NULL): flag[K], idx[K], Xq[M,K], sx[M],
@@ -374,7 +412,7 @@ int64_t oracle_mixed_matmul(const uint16_t* X, int64_t T, int64_t K, const int8_
                             const float* sw, const uint16_t* W16, int64_t N, float tau,
                             const int64_t* rows, int64_t M,
                             uint8_t* flag_out, int32_t* idx_out, int8_t* xq_out, float* sx_out,
-                            int32_t* acc_out, uint16_t* Y, double* Y64, int nthreads) {
+                            int32_t* acc_out, uint16_t* Y, double* Y64, int nthreads, int ht) {
     if (!rows) M = T;
     uint8_t* flag = flag_out ? flag_out : (uint8_t*)malloc((size_t)K);
     int32_t* idx = idx_out ? idx_out : (int32_t*)malloc(sizeof(int32_t) * (size_t)K);
@@ -383,11 +421,11 @@ int64_t oracle_mixed_matmul(const uint16_t* X, int64_t T, int64_t K, const int8_
     int32_t* acc = acc_out ? acc_out : (int32_t*)malloc(sizeof(int32_t) * (size_t)(M * N));
     int64_t o = -1;
     if (flag && idx && xq && sx && acc) {
-        oracle_detect(X, T, K, tau, flag);
+        oracle_detect(X, T, K, tau, flag, ht);
         o = oracle_compact(flag, K, idx);
-        oracle_quantize_rows(X, T, K, flag, rows, M, xq, sx);
+        oracle_quantize_rows(X, T, K, flag, rows, M, xq, sx, ht);
         if (oracle_int8_gemm(xq, M, K, Wq, N, acc, nthreads) != 0) o = -2;
-        else oracle_output(acc, sx, sw, X, W16, Wq, rows, M, K, N, idx, o, Y, Y64, nthreads);
+        else oracle_output(acc, sx, sw, X, W16, Wq, rows, M, K, N, idx, o, Y, Y64, nthreads, ht);
     }
     if (!flag_out) free(flag);
     if (!idx_out) free(idx);

@@ -216,6 +216,81 @@ def pin_typed_weight_containers(orc):
         assert np.all(err <= sw[:, None] / 254.0 * (1 + 2.0 ** -14)), "fp32 quantization error"
 
 
+def _bf16_bits(a):
+    """float32 values that are exact in bf16 -> their bf16 bit patterns."""
+    u = np.ascontiguousarray(a, np.float32).view(np.uint32)
+    assert not np.any(u & 0xFFFF), "value not exact in bf16"
+    return (u >> 16).astype(np.uint16)
+
+
+def pin_bf16_encode(orc):
+    """Rounding to bfloat16: every finite pattern round-trips; exact
+    midpoints go to the even neighbour and anything off the midpoint to
+    the nearer one; the overflow and underflow edges; and on fp32 inputs
+    the integer round-half-even of the bit pattern."""
+    pos = np.arange(0, 0x7F80, dtype=np.uint32)              # +0 .. max finite
+    vals = np.array([orc.bf16_decode(int(b)) for b in pos], np.float64)
+    for b, v in zip(pos[::97], vals[::97]):
+        assert orc.bf16_encode(v) == b and orc.bf16_encode(-v) == (b | 0x8000), f"round trip {b:#x}"
+    for i in range(0, len(pos) - 1, 89):
+        lo, hi = vals[i], vals[i + 1]
+        mid = (lo + hi) / 2                                   # exact in double
+        even = int(pos[i]) if pos[i] % 2 == 0 else int(pos[i + 1])
+        assert orc.bf16_encode(mid) == even, f"midpoint above {pos[i]:#x}"
+        d = (hi - lo) / 1024
+        assert orc.bf16_encode(mid - d) == pos[i] and orc.bf16_encode(mid + d) == pos[i + 1]
+    top = (2 - 2.0 ** -8) * 2.0 ** 127
+    assert orc.bf16_encode(top) == 0x7F80 and orc.bf16_encode(np.nextafter(top, 0)) == 0x7F7F
+    assert orc.bf16_encode(2.0 ** -134) == 0 and orc.bf16_encode(1.5 * 2.0 ** -134) == 1
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal(4000) * np.exp2(rng.integers(-130, 120, 4000))).astype(np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    ref = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)   # integer RNE
+    mine = np.array([orc.bf16_encode(float(v)) for v in x], np.uint16)
+    assert np.array_equal(mine, ref), "rounding of fp32 values"
+
+
+def pin_hand_bf16(orc):
+    """The hand example in the bf16 variant."""
+    g = _load("hand_2x4x2.json")
+    X = _bf16_bits(np.array(g["X"], np.float32))
+    W = np.array(g["W"], np.float32)
+    Wq, sw = orc.quantize_weight_typed(_bf16_bits(W), "bf16")
+    assert np.array_equal(Wq, np.array(g["Wq_NK"], np.int8)) and sw.tolist() == g["sw"]
+    r = orc.mixed_matmul(X, Wq, sw, _bf16_bits(W), g["tau"], htype="bf16")
+    assert r["idx"].tolist() == g["idx"] and np.array_equal(r["xq"], np.array(g["Xq"], np.int8))
+    assert np.array_equal(r["acc"], np.array(g["acc"], np.int32)), "hand acc (bf16)"
+    num = np.array([a / b + c for a, b, c in g["Y64_num"]]).reshape(2, 2)
+    assert np.allclose(r["Y64"], num, rtol=1e-14, atol=0), "hand Y64 (bf16)"
+    Y = np.array([[orc.bf16_decode(int(b)) for b in row] for row in r["Y"]])
+    assert np.array_equal(Y, np.array(g["bf16"]["Y"])), f"hand Y (bf16): {Y.tolist()}"
+
+
+def pin_bf16_same_values(orc):
+    """Inputs exact in both fp16 and bf16: the bf16 variant gives the same
+    outlier set, Xq, s_x, acc and Y64 as the fp16 path, and Y is the bf16
+    rounding of Y64; tau = 0 gives the float64 matmul of the inputs."""
+    rng = np.random.default_rng(9)
+    for T, K, N in [(6, 48, 16), (13, 64, 24)]:
+        # at most 8 significant bits and small exponents: exact in both types
+        X = (np.round(rng.standard_normal((T, K)) * 32) / 32).astype(np.float32)
+        X[:, 5] *= 8
+        W = (np.round(rng.standard_normal((K, N)) * 64) / 2048).astype(np.float32)
+        Xh, Wh = X.astype(np.float16), W.astype(np.float16)
+        Xb, Wb = _bf16_bits(X), _bf16_bits(W)
+        Wq, sw = orc.quantize_weight(Wh)
+        for tau in (6.0, 0.0, float("inf")):
+            a = orc.mixed_matmul(Xh, Wq, sw, Wh, tau)
+            b = orc.mixed_matmul(Xb, Wq, sw, Wb, tau, htype="bf16")
+            for key in ("idx", "xq", "sx", "acc", "Y64"):
+                assert np.array_equal(a[key], b[key]), f"bf16 variant {key}, tau={tau}"
+            enc = np.array([[orc.bf16_encode(v) for v in row] for row in b["Y64"]], np.uint16)
+            assert np.array_equal(b["Y"], enc), "bf16 rounding of Y64"
+            if tau == 0.0:
+                assert np.allclose(b["Y64"], X.astype(np.float64) @ W.astype(np.float64),
+                                   rtol=1e-13, atol=1e-300), "tau = 0 (bf16)"
+
+
 def pin_quant_ties(orc):
     g = _load("quant_ties.json")
     for c in g["cases"]:
@@ -436,4 +511,4 @@ ALL_PINS = [pin_f16_codec, pin_hand_example, pin_quant_ties, pin_detect, pin_com
             pin_error_bound, pin_metamorphic_scale, pin_permutation, pin_row_sample,
             pin_hand_memory_halved, pin_dequant_weight, pin_memory_halved_tau_zero,
             pin_memory_halved_exact_weight, pin_bf16_decode, pin_typed_weight_hand,
-            pin_typed_weight_containers]
+            pin_typed_weight_containers, pin_bf16_encode, pin_hand_bf16, pin_bf16_same_values]

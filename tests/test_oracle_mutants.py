@@ -12,8 +12,8 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
 # (name, text in oracle.c, replacement)
 MUTANTS = [
-    ("threshold_strict", "fabsf(oh_f32(X[t * K + k])) >= tau", "fabsf(oh_f32(X[t * K + k])) > tau"),
-    ("threshold_signed", "fabsf(oh_f32(X[t * K + k])) >= tau", "oh_f32(X[t * K + k]) >= tau"),
+    ("threshold_strict", "fabsf(h_f32(ht, X[t * K + k])) >= tau", "fabsf(h_f32(ht, X[t * K + k])) > tau"),
+    ("threshold_signed", "fabsf(h_f32(ht, X[t * K + k])) >= tau", "h_f32(ht, X[t * K + k]) >= tau"),
     ("round_half_away", "float q = rintf(p);", "float q = roundf(p);"),
     ("round_truncate", "float q = rintf(p);", "float q = truncf(p);"),
     ("range_128", "float r = 127.0f / s;", "float r = 128.0f / s;"),
@@ -28,20 +28,26 @@ MUTANTS = [
     ("f16_ties_away", "(frac == 0.5 && fmod(fl, 2.0) != 0.0)", "(frac == 0.5)"),
     ("weight_scale_first_rows", "for (int64_t k = 0; k < c->K; ++k) {\n            float a = fabsf(w_value(c, k * c->N + n));",
      "for (int64_t k = 0; k < c->K / 2; ++k) {\n            float a = fabsf(w_value(c, k * c->N + n));"),
-    ("outlier_value_from_wrong_row", "oh_decode(c->X[t * c->K + k]) * oh_decode(w)",
-     "oh_decode(c->X[k]) * oh_decode(w)"),
-    ("recovered_weight_unrounded", "y16 += oh_decode(c->X[t * c->K + k]) * oh_decode(w);",
-     "y16 += oh_decode(c->X[t * c->K + k]) * (c->W16 ? oh_decode(w) : (double)((float)c->Wq[n * c->K + k] * (c->sw[n] / 127.0f)));"),
+    ("outlier_value_from_wrong_row", "h_decode(c->ht, c->X[t * c->K + k]) * h_decode(c->ht, w)",
+     "h_decode(c->ht, c->X[k]) * h_decode(c->ht, w)"),
+    ("recovered_weight_unrounded", "y16 += h_decode(c->ht, c->X[t * c->K + k]) * h_decode(c->ht, w);",
+     "y16 += h_decode(c->ht, c->X[t * c->K + k]) * (c->W16 ? h_decode(c->ht, w) : (double)((float)c->Wq[n * c->K + k] * (c->sw[n] / 127.0f)));"),
     ("recovered_weight_128", "const float d = sw / 127.0f;", "const float d = sw / 128.0f;"),
     ("bf16_decode_shift", "uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;"),
     ("f32_weight_read_as_f16", "if (c->type == 2) return ((const float*)c->W)[i];",
      "if (c->type == 3) return ((const float*)c->W)[i];"),
     ("f32_weight_rounded_to_f16", "if (c->type == 2) return ((const float*)c->W)[i];",
      "if (c->type == 2) return oh_f32(oh_encode((double)((const float*)c->W)[i]));"),
-    ("recovered_weight_transposed", "oracle_dequant_weight(c->Wq[n * c->K + k], c->sw[n])",
-     "oracle_dequant_weight(c->Wq[(k * c->N + n) % (c->N * c->K)], c->sw[n])"),
-    ("recovered_weight_ignored", ": oracle_dequant_weight(c->Wq[n * c->K + k], c->sw[n]);",
+    ("recovered_weight_transposed", "oracle_dequant_weight_h(c->Wq[n * c->K + k], c->sw[n], c->ht)",
+     "oracle_dequant_weight_h(c->Wq[(k * c->N + n) % (c->N * c->K)], c->sw[n], c->ht)"),
+    ("recovered_weight_ignored", ": oracle_dequant_weight_h(c->Wq[n * c->K + k], c->sw[n], c->ht);",
      ": (uint16_t)0;"),
+    ("bf16_output_rounded_as_fp16", "c->Y[m * c->N + n] = h_encode(c->ht, y);",
+     "c->Y[m * c->N + n] = h_encode(0, y);"),
+    ("bf16_encode_ties_away", "double n = fl;\n    if (frac > 0.5 || (frac == 0.5 && fmod(fl, 2.0) != 0.0)) n = fl + 1.0;\n    float r",
+     "double n = fl;\n    if (frac >= 0.5) n = fl + 1.0;\n    float r"),
+    ("bf16_input_read_as_fp16", "static float h_f32(int ht, uint16_t b) { return (float)h_decode(ht, b); }",
+     "static float h_f32(int ht, uint16_t b) { (void)ht; return (float)oh_decode(b); }"),
 ]
 
 
