@@ -147,6 +147,24 @@ int int8_mixed_matmul_debug(const void* X, int64_t T, int64_t K, const int8_t* W
                             void* workspace, size_t workspace_bytes, void* stream,
                             int32_t* count, int32_t* idx, int8_t* xq, float* sx, int32_t* acc);
 
+/* The bf16 variant of the whole path ("16-bit" is not fixed by the pages):
+ * X, W16 and Y are bfloat16 instead of fp16; every step is the same (values
+ * widen to fp32 exactly, the 16-bit matmul multiplies bf16 values with fp32
+ * accumulation, Y is rounded once to the nearest bf16, ties to even; a
+ * recovered weight value (W16 = NULL) is rounded to bf16).  Wq and sw come
+ * from int8_quantize_weight_typed on the bf16 (or any) checkpoint.
+ * Arguments, workspace and errors as int8_mixed_matmul. */
+int int8_mixed_matmul_bf16(const void* X, int64_t T, int64_t K, const int8_t* Wq,
+                           const float* sw, const void* W16, int64_t N, float tau, void* Y,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* int8_mixed_matmul_debug for the bf16 variant. */
+int int8_mixed_matmul_bf16_debug(const void* X, int64_t T, int64_t K, const int8_t* Wq,
+                                 const float* sw, const void* W16, int64_t N, float tau, void* Y,
+                                 void* workspace, size_t workspace_bytes, void* stream,
+                                 int32_t* count, int32_t* idx, int8_t* xq, float* sx,
+                                 int32_t* acc);
+
 /* Steps 1-2 on the activation side only: finds the outlier dimensions,
  * quantizes X row-wise and gathers the outlier columns of X, all into the
  * workspace.  Lets several weights that share one X (e.g. the query, key

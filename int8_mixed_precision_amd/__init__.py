@@ -37,6 +37,8 @@ EXPORTS = [
     "int8_quantize_weight_typed",
     "int8_mixed_matmul",
     "int8_mixed_matmul_debug",
+    "int8_mixed_matmul_bf16",
+    "int8_mixed_matmul_bf16_debug",
     "int8mm_quantize_activations",
     "int8mm_matmul_prepared",
 ]
@@ -64,6 +66,8 @@ def _load() -> ctypes.CDLL:
     lib.int8_mixed_matmul.argtypes = [vp, i64, i64, vp, vp, vp, i64, f32, vp, vp, sz, vp]
     lib.int8_mixed_matmul_debug.argtypes = [vp, i64, i64, vp, vp, vp, i64, f32, vp, vp, sz, vp,
                                             vp, vp, vp, vp, vp]
+    lib.int8_mixed_matmul_bf16.argtypes = lib.int8_mixed_matmul.argtypes
+    lib.int8_mixed_matmul_bf16_debug.argtypes = lib.int8_mixed_matmul_debug.argtypes
     lib.int8mm_quantize_activations.argtypes = [vp, i64, i64, i64, f32, vp, sz, vp]
     lib.int8mm_matmul_prepared.argtypes = [vp, sz, i64, i64, vp, vp, vp, i64, vp, vp]
     for name in EXPORTS[1:]:
@@ -165,7 +169,11 @@ def quantize_checkpoint(W: torch.Tensor, fp16_copy: bool = False):
 
 
 def _mm_args(X, Wq, sw, W16):
-    _need(X, torch.float16, 2, "X")
+    """Checks the operands; X, W16 and Y share one 16-bit type: float16, or
+    bfloat16 for the bf16 variant."""
+    if not isinstance(X, torch.Tensor) or X.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("X must be a float16 or bfloat16 tensor")
+    _need(X, X.dtype, 2, "X")
     _need(Wq, torch.int8, 1, "Wq")
     _need(sw, torch.float32, 1, "sw")
     T, K = X.shape
@@ -174,21 +182,25 @@ def _mm_args(X, Wq, sw, W16):
         raise ValueError(f"Wq has {Wq.numel()} bytes, a [{K},{N}] weight needs "
                          f"{weight_bytes(K, N)}")
     if W16 is not None:
-        _need(W16, torch.float16, 2, "W16")
+        _need(W16, X.dtype, 2, "W16")
         if tuple(W16.shape) != (K, N):
             raise ValueError(f"W16 must be [{K},{N}], got {tuple(W16.shape)}")
     return T, K, N
 
 
 def mixed_matmul(X, Wq, sw, W16, tau: float, workspace=None, out=None) -> torch.Tensor:
-    """Y fp16 [T,N] = LLM.int8()(X, W, tau)."""
+    """Y [T,N] = LLM.int8()(X, W, tau), in X's 16-bit type (float16, or
+    bfloat16 for the bf16 variant).  W16 None: memory-halved variant."""
     T, K, N = _mm_args(X, Wq, sw, W16)
     if workspace is None:
         workspace = new_workspace(T, K, N, X.device)
-    Y = out if out is not None else torch.empty((T, N), dtype=torch.float16, device=X.device)
-    _check(_lib.int8_mixed_matmul(_ptr(X), T, K, _ptr(Wq), _ptr(sw), _ptr(W16), N, float(tau),
-                                  _ptr(Y), _ptr(workspace), workspace.numel(), _stream()),
-           "int8_mixed_matmul")
+    Y = out if out is not None else torch.empty((T, N), dtype=X.dtype, device=X.device)
+    if Y.dtype != X.dtype or tuple(Y.shape) != (T, N) or not Y.is_contiguous():
+        raise ValueError("out must be a contiguous [T,N] tensor of X's dtype")
+    fn, name = ((_lib.int8_mixed_matmul_bf16, "int8_mixed_matmul_bf16")
+                if X.dtype == torch.bfloat16 else (_lib.int8_mixed_matmul, "int8_mixed_matmul"))
+    _check(fn(_ptr(X), T, K, _ptr(Wq), _ptr(sw), _ptr(W16), N, float(tau), _ptr(Y),
+              _ptr(workspace), workspace.numel(), _stream()), name)
     return Y
 
 
@@ -198,18 +210,18 @@ def mixed_matmul_debug(X, Wq, sw, W16, tau: float, workspace=None) -> dict:
     dev = X.device
     if workspace is None:
         workspace = new_workspace(T, K, N, dev)
-    r = {"Y": torch.empty((T, N), dtype=torch.float16, device=dev),
+    r = {"Y": torch.empty((T, N), dtype=X.dtype, device=dev),
          "count": torch.zeros(4, dtype=torch.int32, device=dev),
          "idx": torch.zeros(K, dtype=torch.int32, device=dev),
          "xq": torch.empty((T, K), dtype=torch.int8, device=dev),
          "sx": torch.empty(T, dtype=torch.float32, device=dev),
          "acc": torch.empty((T, N), dtype=torch.int32, device=dev)}
-    _check(_lib.int8_mixed_matmul_debug(_ptr(X), T, K, _ptr(Wq), _ptr(sw), _ptr(W16), N,
-                                        float(tau), _ptr(r["Y"]), _ptr(workspace),
-                                        workspace.numel(), _stream(), _ptr(r["count"]),
-                                        _ptr(r["idx"]), _ptr(r["xq"]), _ptr(r["sx"]),
-                                        _ptr(r["acc"])),
-           "int8_mixed_matmul_debug")
+    fn, name = ((_lib.int8_mixed_matmul_bf16_debug, "int8_mixed_matmul_bf16_debug")
+                if X.dtype == torch.bfloat16
+                else (_lib.int8_mixed_matmul_debug, "int8_mixed_matmul_debug"))
+    _check(fn(_ptr(X), T, K, _ptr(Wq), _ptr(sw), _ptr(W16), N, float(tau), _ptr(r["Y"]),
+              _ptr(workspace), workspace.numel(), _stream(), _ptr(r["count"]), _ptr(r["idx"]),
+              _ptr(r["xq"]), _ptr(r["sx"]), _ptr(r["acc"])), name)
     return r
 
 

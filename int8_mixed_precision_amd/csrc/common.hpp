@@ -13,8 +13,28 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef uint16_t v8u16 __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
+
+// 16-bit element type of X, W16 and Y (and of the gathered outlier columns):
+// fp16, or bf16 for the bf16 variant.  Kernels store them as raw 16-bit
+// patterns and convert with these helpers.
+constexpr int kHalfF16 = 0, kHalfBF16 = 1;
+
+template <int HT>
+__device__ __forceinline__ float h16_to_f32(uint16_t b) {
+    if constexpr (HT == kHalfBF16) return __builtin_bit_cast(float, (uint32_t)b << 16);
+    else return (float)__builtin_bit_cast(_Float16, b);
+}
+
+// fp32 -> 16-bit, round to nearest even
+template <int HT>
+__device__ __forceinline__ uint16_t f32_to_h16(float f) {
+    if constexpr (HT == kHalfBF16) return __builtin_bit_cast(uint16_t, (__bf16)f);
+    else return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
 
 // Device workspace of one activation pass.  All regions are 256-byte aligned.
 //   flags   u32 [kw]     bit k%32 of word k/32 set when dimension k is an outlier
@@ -23,7 +43,7 @@ constexpr int kWave = 64;
 //   idx     i32 [K]      outlier dimensions, ascending
 //   sx      f32 [T]      row scales
 //   xq      i8  [T,K]    quantized activations, outlier columns 0
-//   xo      f16 [T,opad] outlier columns of X, row stride count[1], zero padded
+//   xo      16-bit [T,opad] outlier columns of X, row stride count[1], zero padded
 struct Workspace {
     uint32_t* flags;
     int32_t* wprefix;
@@ -31,7 +51,7 @@ struct Workspace {
     int32_t* idx;
     float* sx;
     int8_t* xq;
-    _Float16* xo;
+    uint16_t* xo;
     size_t bytes;   // total bytes the layout needs
 };
 
@@ -39,14 +59,15 @@ __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // A weight value recovered from its Int8 code q and column scale s_w
-// (memory-halved variant): fp16(fp32(q * fp32(s_w / 127))).  The product is
-// rounded to fp32 first: the empty asm keeps the compiler from fusing the
-// multiply and the conversion into one v_fma_mixlo_f16 (a single rounding
-// of the exact product straight to fp16).
-__device__ __forceinline__ _Float16 recover_weight(int8_t q, float d) {
+// (memory-halved variant): fp16(fp32(q * fp32(s_w / 127))) (bf16 for the bf16
+// variant).  The product is rounded to fp32 first: the empty asm keeps the
+// compiler from fusing the multiply and the conversion into one
+// v_fma_mixlo_f16 (a single rounding of the exact product straight to fp16).
+template <int HT>
+__device__ __forceinline__ uint16_t recover_weight(int8_t q, float d) {
     float v = (float)q * d;
     asm volatile("" : "+v"(v));
-    return (_Float16)v;
+    return f32_to_h16<HT>(v);
 }
 
 // Bytes of the converted weight: int8 [N,K] row-major (K contiguous).
@@ -56,7 +77,7 @@ inline int64_t wq_bytes(int64_t K, int64_t N) { return K * N; }
 Workspace carve_workspace(void* base, int64_t T, int64_t K);
 
 // ---- activation side (k_activation.hip)
-hipError_t launch_activation_pass(const _Float16* X, int64_t T, int64_t K, float tau,
+hipError_t launch_activation_pass(const uint16_t* X, int ht, int64_t T, int64_t K, float tau,
                                   const Workspace& ws, hipStream_t stream);
 
 // ---- weight side (k_weight.hip)
@@ -71,21 +92,21 @@ struct GemmArgs {
     const float* sx;       // [T]
     const int8_t* wq;      // [N,K]
     const float* sw;       // [N]
-    const _Float16* xo;    // [T,opad]
+    const uint16_t* xo;    // [T,opad] 16-bit
     const int32_t* idx;    // [K]
     const int32_t* count;  // [2]
-    const _Float16* w16;   // [K,N], or NULL: outlier rows recovered from wq
-    _Float16* y;           // [T,N]
+    const uint16_t* w16;   // [K,N] 16-bit, or NULL: outlier rows recovered from wq
+    uint16_t* y;           // [T,N] 16-bit
     int32_t* acc_out;      // [T,N] or NULL
     int64_t T, K, N;
 };
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_gemm(const GemmArgs& a, int ht, hipStream_t stream);
 
 // ---- single-kernel decode path (k_decode.hip)
 bool decode_path_supported(int64_t T, int64_t K, int64_t N);
-hipError_t launch_decode(const _Float16* X, int64_t T, int64_t K, const int8_t* Wq,
-                         const float* sw, const _Float16* W16, int64_t N, float tau,
-                         _Float16* Y, int32_t* dbg_count, int32_t* dbg_idx, int8_t* dbg_xq,
+hipError_t launch_decode(const uint16_t* X, int ht, int64_t T, int64_t K, const int8_t* Wq,
+                         const float* sw, const uint16_t* W16, int64_t N, float tau,
+                         uint16_t* Y, int32_t* dbg_count, int32_t* dbg_idx, int8_t* dbg_xq,
                          float* dbg_sx, int32_t* dbg_acc, hipStream_t stream);
 
 // ---- debug copies (k_activation.hip)

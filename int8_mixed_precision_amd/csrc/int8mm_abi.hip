@@ -45,21 +45,22 @@ int check_matmul(const void* X, int64_t T, int64_t K, const int8_t* Wq, const fl
     return INT8MM_OK;
 }
 
-int run_matmul(const void* X, int64_t T, int64_t K, const int8_t* Wq, const float* sw,
+// ht: 16-bit type of X, W16 and Y (kHalfF16, or kHalfBF16 for the bf16 variant)
+int run_matmul(const void* X, int ht, int64_t T, int64_t K, const int8_t* Wq, const float* sw,
                const void* W16, int64_t N, float tau, void* Y, void* workspace,
                hipStream_t stream, int32_t* count, int32_t* idx, int8_t* xq, float* sx,
                int32_t* acc) {
+    const uint16_t* x16 = static_cast<const uint16_t*>(X);
+    const uint16_t* w16 = static_cast<const uint16_t*>(W16);
+    uint16_t* y16 = static_cast<uint16_t*>(Y);
     if (decode_path_supported(T, K, N))
-        return hip_status(launch_decode(static_cast<const _Float16*>(X), T, K, Wq, sw,
-                                        static_cast<const _Float16*>(W16), N, tau,
-                                        static_cast<_Float16*>(Y), count, idx, xq, sx, acc,
-                                        stream));
+        return hip_status(launch_decode(x16, ht, T, K, Wq, sw, w16, N, tau, y16, count, idx, xq,
+                                        sx, acc, stream));
     Workspace ws = carve_workspace(workspace, T, K);
-    hipError_t e = launch_activation_pass(static_cast<const _Float16*>(X), T, K, tau, ws, stream);
+    hipError_t e = launch_activation_pass(x16, ht, T, K, tau, ws, stream);
     if (e != hipSuccess) return INT8MM_E_HIP;
-    GemmArgs g{ws.xq, ws.sx, Wq, sw, ws.xo, ws.idx, ws.count,
-               static_cast<const _Float16*>(W16), static_cast<_Float16*>(Y), acc, T, K, N};
-    e = launch_gemm(g, stream);
+    GemmArgs g{ws.xq, ws.sx, Wq, sw, ws.xo, ws.idx, ws.count, w16, y16, acc, T, K, N};
+    e = launch_gemm(g, ht, stream);
     if (e != hipSuccess) return INT8MM_E_HIP;
     return hip_status(launch_debug_copies(ws, T, K, count, idx, xq, sx, stream));
 }
@@ -125,22 +126,49 @@ int int8_mixed_matmul(const void* X, int64_t T, int64_t K, const int8_t* Wq, con
                       size_t workspace_bytes, void* stream) {
     int st = check_matmul(X, T, K, Wq, sw, W16, N, tau, Y, workspace, workspace_bytes);
     if (st) return st;
-    return run_matmul(X, T, K, Wq, sw, W16, N, tau, Y, workspace,
+    return run_matmul(X, kHalfF16, T, K, Wq, sw, W16, N, tau, Y, workspace,
                       static_cast<hipStream_t>(stream), nullptr, nullptr, nullptr, nullptr,
                       nullptr);
+}
+
+int int8_mixed_matmul_bf16(const void* X, int64_t T, int64_t K, const int8_t* Wq,
+                           const float* sw, const void* W16, int64_t N, float tau, void* Y,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_matmul(X, T, K, Wq, sw, W16, N, tau, Y, workspace, workspace_bytes);
+    if (st) return st;
+    return run_matmul(X, kHalfBF16, T, K, Wq, sw, W16, N, tau, Y, workspace,
+                      static_cast<hipStream_t>(stream), nullptr, nullptr, nullptr, nullptr,
+                      nullptr);
+}
+
+static int matmul_debug(int ht, const void* X, int64_t T, int64_t K, const int8_t* Wq,
+                        const float* sw, const void* W16, int64_t N, float tau, void* Y,
+                        void* workspace, size_t workspace_bytes, void* stream, int32_t* count,
+                        int32_t* idx, int8_t* xq, float* sx, int32_t* acc) {
+    int st = check_matmul(X, T, K, Wq, sw, W16, N, tau, Y, workspace, workspace_bytes);
+    if (st) return st;
+    if ((count && !aligned16(count)) || (idx && !aligned16(idx)) || (xq && !aligned16(xq)) ||
+        (sx && !aligned16(sx)) || (acc && !aligned16(acc)))
+        return INT8MM_E_ALIGN;
+    return run_matmul(X, ht, T, K, Wq, sw, W16, N, tau, Y, workspace,
+                      static_cast<hipStream_t>(stream), count, idx, xq, sx, acc);
 }
 
 int int8_mixed_matmul_debug(const void* X, int64_t T, int64_t K, const int8_t* Wq,
                             const float* sw, const void* W16, int64_t N, float tau, void* Y,
                             void* workspace, size_t workspace_bytes, void* stream,
                             int32_t* count, int32_t* idx, int8_t* xq, float* sx, int32_t* acc) {
-    int st = check_matmul(X, T, K, Wq, sw, W16, N, tau, Y, workspace, workspace_bytes);
-    if (st) return st;
-    if ((count && !aligned16(count)) || (idx && !aligned16(idx)) || (xq && !aligned16(xq)) ||
-        (sx && !aligned16(sx)) || (acc && !aligned16(acc)))
-        return INT8MM_E_ALIGN;
-    return run_matmul(X, T, K, Wq, sw, W16, N, tau, Y, workspace,
-                      static_cast<hipStream_t>(stream), count, idx, xq, sx, acc);
+    return matmul_debug(kHalfF16, X, T, K, Wq, sw, W16, N, tau, Y, workspace, workspace_bytes,
+                        stream, count, idx, xq, sx, acc);
+}
+
+int int8_mixed_matmul_bf16_debug(const void* X, int64_t T, int64_t K, const int8_t* Wq,
+                                 const float* sw, const void* W16, int64_t N, float tau, void* Y,
+                                 void* workspace, size_t workspace_bytes, void* stream,
+                                 int32_t* count, int32_t* idx, int8_t* xq, float* sx,
+                                 int32_t* acc) {
+    return matmul_debug(kHalfBF16, X, T, K, Wq, sw, W16, N, tau, Y, workspace, workspace_bytes,
+                        stream, count, idx, xq, sx, acc);
 }
 
 int int8mm_quantize_activations(const void* X, int64_t T, int64_t K, int64_t N, float tau,
@@ -153,7 +181,7 @@ int int8mm_quantize_activations(const void* X, int64_t T, int64_t K, int64_t N, 
     if (!aligned16(X) || !aligned16(workspace)) return INT8MM_E_ALIGN;
     Workspace ws = carve_workspace(workspace, T, K);
     if (workspace_bytes < ws.bytes) return INT8MM_E_WORKSPACE;
-    return hip_status(launch_activation_pass(static_cast<const _Float16*>(X), T, K, tau, ws,
+    return hip_status(launch_activation_pass(static_cast<const uint16_t*>(X), kHalfF16, T, K, tau, ws,
                                              static_cast<hipStream_t>(stream)));
 }
 
@@ -169,8 +197,8 @@ int int8mm_matmul_prepared(const void* workspace, size_t workspace_bytes, int64_
     Workspace ws = carve_workspace(const_cast<void*>(workspace), T, K);
     if (workspace_bytes < ws.bytes) return INT8MM_E_WORKSPACE;
     GemmArgs g{ws.xq, ws.sx, Wq, sw, ws.xo, ws.idx, ws.count,
-               static_cast<const _Float16*>(W16), static_cast<_Float16*>(Y), nullptr, T, K, N};
-    return hip_status(launch_gemm(g, static_cast<hipStream_t>(stream)));
+               static_cast<const uint16_t*>(W16), static_cast<uint16_t*>(Y), nullptr, T, K, N};
+    return hip_status(launch_gemm(g, kHalfF16, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -32,8 +32,6 @@ constexpr int kDetectRows = 16;                    // rows per workgroup
 constexpr int kCompactThreads = 1024;
 constexpr int kQuantThreads = 256;
 
-__device__ inline float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
-
 // Zeroes the outlier bitmap and the count before a detection pass.
 __global__ void k_clear(uint32_t* __restrict__ flags, int64_t kw, int32_t* __restrict__ count) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -44,6 +42,7 @@ __global__ void k_clear(uint32_t* __restrict__ flags, int64_t kw, int32_t* __res
 // flags[k/32] bit k%32 |= (|X[t,k]| >= tau) over the workgroup's rows.
 // Each lane owns 8 consecutive columns; 4 lanes form one 32-bit word, which
 // is merged with one atomicOr only when some bit is set.
+template <int HT>
 __global__ __launch_bounds__(kDetectThreads) void k_detect(const uint16_t* __restrict__ X,
                                                            int64_t T, int64_t K, float tau,
                                                            uint32_t* __restrict__ flags) {
@@ -65,7 +64,7 @@ __global__ __launch_bounds__(kDetectThreads) void k_detect(const uint16_t* __res
                 const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    float x = h2f((uint16_t)(w[e >> 1] >> ((e & 1) * 16)));
+                    float x = h16_to_f32<HT>((uint16_t)(w[e >> 1] >> ((e & 1) * 16)));
                     m |= (__builtin_fabsf(x) >= tau ? 1u : 0u) << e;
                 }
             }
@@ -75,7 +74,7 @@ __global__ __launch_bounds__(kDetectThreads) void k_detect(const uint16_t* __res
             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                float x = h2f((uint16_t)(w[e >> 1] >> ((e & 1) * 16)));
+                float x = h16_to_f32<HT>((uint16_t)(w[e >> 1] >> ((e & 1) * 16)));
                 m |= (__builtin_fabsf(x) >= tau ? 1u : 0u) << e;
             }
         }
@@ -144,11 +143,13 @@ __device__ inline int8_t quant(float x, float r) {
 }
 
 // Row-wise quantization of one row t per workgroup, over the non-outlier
-// columns, plus the gather of the row's outlier values into xo.
+// columns, plus the gather of the row's outlier values (16-bit patterns,
+// unchanged) into xo.
+template <int HT>
 __global__ __launch_bounds__(kQuantThreads) void k_rowquant(
     const uint16_t* __restrict__ X, int64_t K, const uint32_t* __restrict__ flags,
     const int32_t* __restrict__ wprefix, const int32_t* __restrict__ count,
-    int8_t* __restrict__ xq, float* __restrict__ sx, _Float16* __restrict__ xo) {
+    int8_t* __restrict__ xq, float* __restrict__ sx, uint16_t* __restrict__ xo) {
     __shared__ float red[kQuantThreads / kWave];
     const int tid = threadIdx.x;
     const int64_t t = blockIdx.x;
@@ -161,7 +162,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_rowquant(
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            float a = __builtin_fabsf(h2f((uint16_t)(w[e >> 1] >> ((e & 1) * 16))));
+            float a = __builtin_fabsf(h16_to_f32<HT>((uint16_t)(w[e >> 1] >> ((e & 1) * 16))));
             mx = ((fm >> e) & 1u) ? mx : __builtin_fmaxf(mx, a);
         }
     }
@@ -174,7 +175,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_rowquant(
     const float r = mx > 0.0f ? 127.0f / mx : 0.0f;
     const int64_t opad = count[1];
     const int64_t o = count[0];
-    _Float16* xo_row = xo + t * opad;
+    uint16_t* xo_row = xo + t * opad;
     for (int64_t c = tid; c < nch; c += kQuantThreads) {
         uint4 v = *reinterpret_cast<const uint4*>(row + c * 8);
         const uint32_t word = flags[c >> 2];
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_rowquant(
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             uint16_t hb = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
-            float x = h2f(hb);
+            float x = h16_to_f32<HT>(hb);
             uint32_t q = ((fm >> e) & 1u) ? 0u : (uint32_t)(uint8_t)quant(x, r);
             packed[e >> 2] |= q << ((e & 3) * 8);
         }
@@ -196,30 +197,36 @@ __global__ __launch_bounds__(kQuantThreads) void k_rowquant(
                 if ((fm >> e) & 1u) {
                     int bit = base_bit + e;
                     int pos = wprefix[c >> 2] + __builtin_popcount(word & ((1u << bit) - 1u));
-                    xo_row[pos] = __builtin_bit_cast(_Float16, (uint16_t)(w[e >> 1] >> ((e & 1) * 16)));
+                    xo_row[pos] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
                 }
             }
         }
     }
-    for (int64_t j = o + tid; j < opad; j += kQuantThreads) xo_row[j] = (_Float16)0.0f;
+    for (int64_t j = o + tid; j < opad; j += kQuantThreads) xo_row[j] = 0;   // +0 in both types
     if (tid == 0) sx[t] = mx;
 }
 
 }  // namespace
 
-hipError_t launch_activation_pass(const _Float16* X, int64_t T, int64_t K, float tau,
-                                  const Workspace& ws, hipStream_t stream) {
+template <int HT>
+static void launch_activation_typed(const uint16_t* xb, int64_t T, int64_t K, float tau,
+                             const Workspace& ws, hipStream_t stream) {
     const int64_t kw = ceil_div(K, 32);
-    const uint16_t* xb = reinterpret_cast<const uint16_t*>(X);
     int clear_blocks = (int)ceil_div(kw > 4 ? kw : 4, 256);
     hipLaunchKernelGGL(k_clear, dim3(clear_blocks), dim3(256), 0, stream, ws.flags, kw, ws.count);
     const int64_t row_chunks = ceil_div(T, kDetectRows);
     dim3 dgrid((unsigned)ceil_div(K, kDetectCols), (unsigned)(row_chunks < 65535 ? row_chunks : 65535));
-    hipLaunchKernelGGL(k_detect, dgrid, dim3(kDetectThreads), 0, stream, xb, T, K, tau, ws.flags);
+    hipLaunchKernelGGL(k_detect<HT>, dgrid, dim3(kDetectThreads), 0, stream, xb, T, K, tau, ws.flags);
     hipLaunchKernelGGL(k_compact, dim3(1), dim3(kCompactThreads), 0, stream, ws.flags, kw,
                        ws.wprefix, ws.idx, ws.count);
-    hipLaunchKernelGGL(k_rowquant, dim3((unsigned)T), dim3(kQuantThreads), 0, stream, xb, K,
+    hipLaunchKernelGGL(k_rowquant<HT>, dim3((unsigned)T), dim3(kQuantThreads), 0, stream, xb, K,
                        ws.flags, ws.wprefix, ws.count, ws.xq, ws.sx, ws.xo);
+}
+
+hipError_t launch_activation_pass(const uint16_t* X, int ht, int64_t T, int64_t K, float tau,
+                                  const Workspace& ws, hipStream_t stream) {
+    if (ht == kHalfBF16) launch_activation_typed<kHalfBF16>(X, T, K, tau, ws, stream);
+    else launch_activation_typed<kHalfF16>(X, T, K, tau, ws, stream);
     return hipGetLastError();
 }
 
@@ -255,7 +262,7 @@ Workspace carve_workspace(void* base, int64_t T, int64_t K) {
     w.sx = reinterpret_cast<float*>(take(sizeof(float) * (size_t)T));
     w.xq = reinterpret_cast<int8_t*>(take((size_t)T * (size_t)K));
     // worst case: every dimension an outlier, o = K (K % 16 == 0, so opad <= K)
-    w.xo = reinterpret_cast<_Float16*>(take(sizeof(_Float16) * (size_t)T * (size_t)K));
+    w.xo = reinterpret_cast<uint16_t*>(take(sizeof(uint16_t) * (size_t)T * (size_t)K));
     w.bytes = off;
     return w;
 }

@@ -56,16 +56,15 @@ constexpr int kMaxBpw = 8;             // 16-row blocks per workgroup
 constexpr int kW16Cache = 16;          // outliers whose W16 values are staged in LDS
 constexpr int kChunkKConst = 1024;     // k covered by one weight chunk
 
-__device__ inline float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
 
 struct DecodeArgs {
-    const uint16_t* x;      // [T,K] fp16 bits
+    const uint16_t* x;      // [T,K] 16-bit (fp16, or bf16 for the bf16 variant)
     const int8_t* wq;       // [N,K]
     const float* sw;        // [N]
-    const _Float16* w16;    // [K,N], or NULL: outlier rows recovered from wq
-    _Float16* y;            // [T,N]
+    const uint16_t* w16;    // [K,N] 16-bit, or NULL: outlier rows recovered from wq
+    uint16_t* y;            // [T,N] 16-bit
     float tau;
-    uint32_t tau16;         // bits of the smallest fp16 >= tau (0x7C00 if none finite)
+    uint32_t tau16;         // bits of the smallest 16-bit value >= tau (+inf if none finite)
     int T, K, N;
     int bpw;                // 16-row blocks per workgroup (1..8)
     // optional debug outputs (NULL to skip); workgroup 0 writes all but acc
@@ -102,9 +101,10 @@ __device__ inline uint32_t pk_max_u16(uint32_t a, uint32_t b) {
     return lo | (hi << 16);
 }
 
+template <int HT>
 __device__ inline float chunk_val(const uint4& v, int e) {
     const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
-    return h2f((uint16_t)(w >> ((e & 1) * 16)));
+    return h16_to_f32<HT>((uint16_t)(w >> ((e & 1) * 16)));
 }
 
 constexpr int kLoads = 16;                    // 16-byte loads per lane per chunk (16 KB/wave)
@@ -115,7 +115,7 @@ static_assert(kChunkK == kChunkKConst, "chunk size");
 // CPB = K / 1024 chunks per 16-row block; a thread owns CPT = K / 4096
 // chunks of 8 columns (c = tid + 512 j) in the activation prologue, for all
 // T <= TMAX = 64 / CPB rows (so T * CPT <= 16 chunks of X per thread).
-template <int CPB>
+template <int CPB, int HT>
 __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
     constexpr int CPT = CPB / 4;
     constexpr int TMAX = 64 / CPB;
@@ -188,8 +188,9 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
             xr[j][t] = *reinterpret_cast<const uint4*>(a.x + (int64_t)(t < T ? t : T - 1) * K +
                                                        (tid + kThreads * j) * 8);
     // Magnitudes as fp16 bit patterns: for non-negative halves the unsigned
-    // order is the numeric order, so |x| >= tau <=> bits(|x|) >= tau16, with
-    // tau16 the bits of the smallest fp16 >= tau (0x7C00 when none is finite).
+    // order is the numeric order (fp16 and bf16 alike), so |x| >= tau <=>
+    // bits(|x|) >= tau16, with tau16 the bits of the smallest 16-bit value
+    // >= tau (+inf when none is finite).
     // Column maxima over the T rows by packed unsigned 16-bit max.
     uint32_t fm[CPT];
 #pragma unroll
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
             }
         }
         const uint32_t mh = (m & 0xFFFFu) > (m >> 16) ? (m & 0xFFFFu) : (m >> 16);
-        rmax[t] = h2f((uint16_t)mh);
+        rmax[t] = h16_to_f32<HT>((uint16_t)mh);
     }
     // Row maxima over the wave by a transposed butterfly: each exchange at
     // distance d = 32, 16, ... halves the rows a lane carries (it keeps the
@@ -328,7 +329,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
             uint32_t f[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float p = __builtin_fmaf(chunk_val(xr[j][t], e), rr, 0.0f);
+                const float p = __builtin_fmaf(chunk_val<HT>(xr[j][t], e), rr, 0.0f);
                 f[e] = __builtin_bit_cast(uint32_t, __fadd_rn(p, 12582912.0f));
             }
             uint32_t packed[2];
@@ -350,7 +351,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
                     if (pos < kMaxOutliersLds) {
 #pragma unroll
                         for (int t = 0; t < TMAX; ++t)
-                            sm.xo[t * kMaxOutliersLds + pos] = chunk_val(xr[j][t], e);
+                            sm.xo[t * kMaxOutliersLds + pos] = chunk_val<HT>(xr[j][t], e);
                     }
                     ++pos;
                 }
@@ -476,36 +477,41 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
             for (int j = 0; j < oc; ++j) {
                 const uint32_t pr = sm.w16o[j][r >> 1];
                 y += sm.xo[t * kMaxOutliersLds + j] *
-                     h2f((uint16_t)((r & 1) ? pr >> 16 : pr & 0xFFFFu));
+                     h16_to_f32<HT>((uint16_t)((r & 1) ? pr >> 16 : pr & 0xFFFFu));
             }
         } else {
             const float dr = sm.sw[r] / 127.0f;
             for (int j = 0; j < oc; ++j)
-                y += sm.xo[t * kMaxOutliersLds + j] * (float)recover_weight(sm.wqo[j][r], dr);
+                y += sm.xo[t * kMaxOutliersLds + j] *
+                     h16_to_f32<HT>(recover_weight<HT>(sm.wqo[j][r], dr));
         }
         for (int j = oc; j < o; ++j) {
             const int k = sm.idx[j];
             const float xv = j < kMaxOutliersLds ? sm.xo[t * kMaxOutliersLds + j]
-                                                 : h2f(a.x[(int64_t)t * K + k]);
-            const _Float16 w = recover ? recover_weight(a.wq[(int64_t)n * K + k], sm.sw[r] / 127.0f)
+                                                 : h16_to_f32<HT>(a.x[(int64_t)t * K + k]);
+            const uint16_t w = recover ? recover_weight<HT>(a.wq[(int64_t)n * K + k], sm.sw[r] / 127.0f)
                                        : a.w16[(int64_t)k * N + n];
-            y += xv * (float)w;
+            y += xv * h16_to_f32<HT>(w);
         }
-        a.y[(int64_t)t * N + n] = (_Float16)y;
+        a.y[(int64_t)t * N + n] = f32_to_h16<HT>(y);
     }
 }
 
 }  // namespace
 
-// Bits of the smallest binary16 value >= tau (tau >= 0 and not NaN), or
-// 0x7C00 (+inf) when no finite binary16 value reaches tau.  Found by a binary
-// search over the non-negative bit patterns, whose unsigned order is the
-// numeric order; the fp16 -> fp32 conversion is exact.
-static uint32_t tau_to_f16_ceil(float tau) {
-    uint32_t lo = 0, hi = 0x7C00;   // answer in [lo, hi]
+// Bits of the smallest 16-bit value (binary16, or bfloat16 for ht = bf16)
+// >= tau (tau >= 0 and not NaN), or the +inf pattern when no finite value
+// reaches tau.  Found by a binary search over the non-negative bit patterns,
+// whose unsigned order is the numeric order; both widenings to fp32 are
+// exact.
+static uint32_t tau_to_h16_ceil(float tau, int ht) {
+    const uint32_t inf = ht == kHalfBF16 ? 0x7F80u : 0x7C00u;
+    uint32_t lo = 0, hi = inf;   // answer in [lo, hi]
     while (lo < hi) {
         const uint32_t mid = (lo + hi) / 2;
-        if ((float)__builtin_bit_cast(_Float16, (uint16_t)mid) >= tau) hi = mid;
+        const float v = ht == kHalfBF16 ? __builtin_bit_cast(float, mid << 16)
+                                        : (float)__builtin_bit_cast(_Float16, (uint16_t)mid);
+        if (v >= tau) hi = mid;
         else lo = mid + 1;
     }
     return lo;
@@ -534,9 +540,9 @@ static int device_cus() {
     return cus;
 }
 
-hipError_t launch_decode(const _Float16* X, int64_t T, int64_t K, const int8_t* Wq,
-                         const float* sw, const _Float16* W16, int64_t N, float tau,
-                         _Float16* Y, int32_t* dbg_count, int32_t* dbg_idx, int8_t* dbg_xq,
+hipError_t launch_decode(const uint16_t* X, int ht, int64_t T, int64_t K, const int8_t* Wq,
+                         const float* sw, const uint16_t* W16, int64_t N, float tau,
+                         uint16_t* Y, int32_t* dbg_count, int32_t* dbg_idx, int8_t* dbg_xq,
                          float* dbg_sx, int32_t* dbg_acc, hipStream_t stream) {
     // One workgroup per compute unit (the LDS footprint allows no more), each
     // owning bpw whole 16-row blocks: bpw = ceil(blocks / CUs) spreads the
@@ -544,15 +550,17 @@ hipError_t launch_decode(const _Float16* X, int64_t T, int64_t K, const int8_t* 
     // CU the grid grows instead.
     const int64_t nblocks = ceil_div(N, kRows);
     const int bpw = (int)std::min<int64_t>(kMaxBpw, std::max<int64_t>(1, ceil_div(nblocks, device_cus())));
-    DecodeArgs a{reinterpret_cast<const uint16_t*>(X), Wq, sw, W16, Y, tau, tau_to_f16_ceil(tau),
+    DecodeArgs a{X, Wq, sw, W16, Y, tau, tau_to_h16_ceil(tau, ht),
                  (int)T, (int)K, (int)N, bpw, dbg_count, dbg_idx, dbg_xq, dbg_sx, dbg_acc};
     const unsigned grid = (unsigned)ceil_div(nblocks, bpw);
-    if (K == 4096)
-        hipLaunchKernelGGL(k_decode<4>, dim3(grid), dim3(kThreads), 0, stream, a);
-    else if (K == 8192)
-        hipLaunchKernelGGL(k_decode<8>, dim3(grid), dim3(kThreads), 0, stream, a);
-    else
-        return hipErrorInvalidValue;
+    if (K != 4096 && K != 8192) return hipErrorInvalidValue;
+    if (ht == kHalfBF16) {
+        if (K == 4096) hipLaunchKernelGGL((k_decode<4, kHalfBF16>), dim3(grid), dim3(kThreads), 0, stream, a);
+        else hipLaunchKernelGGL((k_decode<8, kHalfBF16>), dim3(grid), dim3(kThreads), 0, stream, a);
+    } else {
+        if (K == 4096) hipLaunchKernelGGL((k_decode<4, kHalfF16>), dim3(grid), dim3(kThreads), 0, stream, a);
+        else hipLaunchKernelGGL((k_decode<8, kHalfF16>), dim3(grid), dim3(kThreads), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

@@ -53,7 +53,7 @@ __device__ inline int swz(int row, int c) {
 // 32x32 accumulator tiles whose top-left output element is (mb, nb).
 // 32x32 accumulator layout: lane holds column (lane & 31) and, in register
 // r, row 8*(r/4) + 4*(lane/32) + (r%4) of the tile.
-template <int TM, int TN, bool WRITE_ACC>
+template <int TM, int TN, bool WRITE_ACC, int HT>
 __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a, int64_t mb,
                                          int64_t nb, int lane) {
     const int64_t T = a.T, N = a.N;
@@ -113,27 +113,34 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a,
         for (int jc = 0; jc < opad; jc += 16) {
             const int jl = jc + (lane >> 5) * 8;   // first of this lane's 8 outlier slots
             const int64_t mrow = mb + i * 32 + (lane & 31);
-            const v8h xa = mrow < T ? *reinterpret_cast<const v8h*>(a.xo + mrow * opad + jl)
-                                    : v8h{0, 0, 0, 0, 0, 0, 0, 0};
+            const v8u16 xa = mrow < T ? *reinterpret_cast<const v8u16*>(a.xo + mrow * opad + jl)
+                                      : v8u16{0, 0, 0, 0, 0, 0, 0, 0};
             int64_t kk[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) kk[e] = (jl + e < o) ? (int64_t)a.idx[jl + e] : -1;
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const int64_t n = nb + j * 32 + col_l;
-                v8h wb;
+                v8u16 wb;
                 if (!recover) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
-                        wb[e] = (kk[e] >= 0 && n < N) ? a.w16[kk[e] * N + n] : (_Float16)0.0f;
+                        wb[e] = (kk[e] >= 0 && n < N) ? a.w16[kk[e] * N + n] : (uint16_t)0;
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
                         wb[e] = (kk[e] >= 0 && n < N)
-                                    ? recover_weight(a.wq[n * a.K + kk[e]], dn[j])
-                                    : (_Float16)0.0f;
+                                    ? recover_weight<HT>(a.wq[n * a.K + kk[e]], dn[j])
+                                    : (uint16_t)0;
                 }
-                y[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xa, wb, y[j], 0, 0, 0);
+                if constexpr (HT == kHalfBF16)
+                    y[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, xa),
+                                                                   __builtin_bit_cast(v8bf, wb),
+                                                                   y[j], 0, 0, 0);
+                else
+                    y[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, xa),
+                                                                  __builtin_bit_cast(v8h, wb),
+                                                                  y[j], 0, 0, 0);
             }
         }
 #pragma unroll
@@ -142,7 +149,7 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a,
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t m = mb + i * 32 + (r >> 2) * 8 + row_l + (r & 3);
-                if (m < T && n < N) a.y[m * N + n] = (_Float16)y[j][r];
+                if (m < T && n < N) a.y[m * N + n] = f32_to_h16<HT>(y[j][r]);
             }
         }
     }
@@ -155,7 +162,7 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t bid, int64_t nb) {
     return (nb & 7) == 0 ? (bid & 7) * (nb >> 3) + (bid >> 3) : bid;
 }
 
-template <int BM, int BN, int BK, int WAVES_M, bool WRITE_ACC>
+template <int BM, int BN, int BK, int WAVES_M, bool WRITE_ACC, int HT>
 __global__ __launch_bounds__(kThreads) void k_gemm_i8(GemmArgs a) {
     using C = Cfg<BM, BN, BK, WAVES_M>;
     __shared__ __attribute__((aligned(16))) int8_t As[2][BM * BK];
@@ -247,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_i8(GemmArgs a) {
         __syncthreads();
     }
 
-    epilogue<C::TM, C::TN, WRITE_ACC>(acc, a, m0 + wm0, n0 + wn0, lane);
+    epilogue<C::TM, C::TN, WRITE_ACC, HT>(acc, a, m0 + wm0, n0 + wn0, lane);
 }
 
 // 16-byte copy global -> LDS without VGPR staging (global_load_lds_dwordx4,
@@ -303,7 +310,7 @@ __device__ __forceinline__ int big_swz(int row) { return ((row >> 1) & 3) ^ ((ro
 // preceded by at most one read and one copy.  Requires K % 64 == 0; rows past
 // T or N are clamped to the last valid row (they only feed outputs that are
 // never stored).
-template <int WN, bool WRITE_ACC>
+template <int WN, bool WRITE_ACC, int HT>
 __global__ __launch_bounds__(128 * WN) void k_gemm_i8_big(GemmArgs a) {
     constexpr int BM = 256, BN = 256, BK = 64, STAGES = 4;
     constexpr int WAVES = 2 * WN, THREADS = 64 * WAVES;
@@ -426,39 +433,45 @@ __global__ __launch_bounds__(128 * WN) void k_gemm_i8_big(GemmArgs a) {
     }
     // no LDS copy may still be in flight when the workgroup retires
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    epilogue<TM, TN, WRITE_ACC>(acc, a, m0 + wm0, n0 + wn0, lane);
+    epilogue<TM, TN, WRITE_ACC, HT>(acc, a, m0 + wm0, n0 + wn0, lane);
 }
 
-template <int BM, int BN, int BK, int WAVES_M>
+template <int BM, int BN, int BK, int WAVES_M, int HT>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
     const int64_t tiles = ceil_div(a.T, BM) * ceil_div(a.N, BN);
     if (a.acc_out)
-        hipLaunchKernelGGL((k_gemm_i8<BM, BN, BK, WAVES_M, true>), dim3((unsigned)tiles), dim3(kThreads),
-                           0, stream, a);
+        hipLaunchKernelGGL((k_gemm_i8<BM, BN, BK, WAVES_M, true, HT>), dim3((unsigned)tiles),
+                           dim3(kThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL((k_gemm_i8<BM, BN, BK, WAVES_M, false>), dim3((unsigned)tiles), dim3(kThreads),
-                           0, stream, a);
+        hipLaunchKernelGGL((k_gemm_i8<BM, BN, BK, WAVES_M, false, HT>), dim3((unsigned)tiles),
+                           dim3(kThreads), 0, stream, a);
     return hipGetLastError();
+}
+
+template <int WN, int HT>
+hipError_t launch_big(const GemmArgs& a, hipStream_t stream) {
+    const int64_t tiles = ceil_div(a.T, 256) * ceil_div(a.N, 256);
+    if (a.acc_out)
+        hipLaunchKernelGGL((k_gemm_i8_big<WN, true, HT>), dim3((unsigned)tiles), dim3(128 * WN), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((k_gemm_i8_big<WN, false, HT>), dim3((unsigned)tiles), dim3(128 * WN), 0,
+                           stream, a);
+    return hipGetLastError();
+}
+
+template <int HT>
+hipError_t launch_gemm_typed(const GemmArgs& a, hipStream_t stream) {
+    if (a.T > 128 && a.K % 64 == 0) return launch_big<4, HT>(a, stream);
+    if (a.T <= 32) return launch_cfg<32, 256, 128, 1, HT>(a, stream);
+    return launch_cfg<128, 128, 64, 2, HT>(a, stream);
 }
 
 }  // namespace
 
-template <int WN>
-hipError_t launch_big(const GemmArgs& a, hipStream_t stream) {
-    const int64_t tiles = ceil_div(a.T, 256) * ceil_div(a.N, 256);
-    if (a.acc_out)
-        hipLaunchKernelGGL((k_gemm_i8_big<WN, true>), dim3((unsigned)tiles), dim3(128 * WN), 0,
-                           stream, a);
-    else
-        hipLaunchKernelGGL((k_gemm_i8_big<WN, false>), dim3((unsigned)tiles), dim3(128 * WN), 0,
-                           stream, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
-    if (a.T > 128 && a.K % 64 == 0) return launch_big<4>(a, stream);
-    if (a.T <= 32) return launch_cfg<32, 256, 128, 1>(a, stream);
-    return launch_cfg<128, 128, 64, 2>(a, stream);
+hipError_t launch_gemm(const GemmArgs& a, int ht, hipStream_t stream) {
+    return ht == kHalfBF16 ? launch_gemm_typed<kHalfBF16>(a, stream)
+                           : launch_gemm_typed<kHalfF16>(a, stream);
 }
 
 }  // namespace i8mm

@@ -27,7 +27,7 @@ def header_functions():
 def test_header_lists_entry_points():
     names = header_functions()
     assert "int8_mixed_matmul" in names and "int8_quantize_weight" in names
-    assert len(names) == 9, names
+    assert len(names) == 11, names
 
 
 def test_exports_every_declared_symbol(mm):
