@@ -162,6 +162,38 @@ def bench_prefill(torch, mm, synth, steps, warmup):
     log(f"prefill, memory-halved: {warmup} warmup + {steps} timed steps")
     wall_h, evs_h = timed_loop(torch, steps, warmup, step_halved)
     gemm_h_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs_h]))
+    # the bf16 variant on the same values rounded to bf16 (whole calls)
+    Xb, Wb = X.to(torch.bfloat16), W16.to(torch.bfloat16)
+    Wqb, swb, _ = mm.quantize_checkpoint(Wb)
+    Yb = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+
+    def step_bf16(i, e):
+        if e is not None:
+            e[0].record()
+        mm.mixed_matmul(Xb, Wqb, swb, Wb, w.tau, workspace=ws, out=Yb)
+        if e is not None:
+            e[1].record()
+            e[2].record()
+
+    log(f"prefill, bf16 variant: {warmup} warmup + {steps} timed steps")
+    wall_b, _ = timed_loop(torch, steps, warmup, step_bf16)
+    # weight conversion from fp32 and bf16 checkpoints
+    conv = {}
+    W32 = W16.float()
+    for tag, Wc in (("bf16", Wb), ("f32", W32)):
+        mm.quantize_checkpoint(Wc)
+        torch.cuda.synchronize()
+        ca, cb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ca.record()
+        for _ in range(3):
+            mm.quantize_checkpoint(Wc)
+        cb.record()
+        torch.cuda.synchronize()
+        ms = ca.elapsed_time(cb) / 3
+        conv[tag] = {"ms": round(ms, 4),
+                     "GB/s": round((Wc.element_size() * K * N + K * N + 4.0 * N) /
+                                   (ms * 1e-3) / 1e9, 1)}
+    del W32, Xb, Wb, Wqb, swb, Yb
     # the outlier count of this X (one debug call, outside the timed loop)
     dbg = mm.mixed_matmul_debug(X, Wq, sw, W16, w.tau)
     o = int(dbg["count"][0])
@@ -175,6 +207,8 @@ def bench_prefill(torch, mm, synth, steps, warmup):
         "gemm_tops": ops / (gemm_ms * 1e-3) / 1e12,
         "halved_tops": ops * steps / wall_h / 1e12, "halved_ms_per_step": wall_h * 1e3 / steps,
         "halved_gemm_ms": gemm_h_ms,
+        "bf16_tops": ops * steps / wall_b / 1e12, "bf16_ms_per_step": wall_b * 1e3 / steps,
+        "convert": conv,
         "quantize_weight_ms": q_ms,
         "quantize_weight_gbs": (2.0 * K * N + K * N + 4.0 * N) / (q_ms * 1e-3) / 1e9,
     }
@@ -245,6 +279,40 @@ def bench_decode(torch, mm, synth, steps, warmup):
     log(f"decode, memory-halved: {rounds} timed graph replays")
     wall_h, evs_h = timed_loop(torch, rounds, max(1, warmup // DECODE_ROTATE + 1), step_halved)
     call_h_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs_h])) / DECODE_ROTATE
+
+    # the bf16 variant: bf16 X and W16 (the same values rounded), weight
+    # copies converted from the bf16 checkpoint
+    Xb = X.to(torch.bfloat16)
+    sets_b = []
+    for _, _, W16 in sets:
+        Wb = W16.to(torch.bfloat16)
+        Wqb, swb, _ = mm.quantize_checkpoint(Wb)
+        sets_b.append((Wqb, swb, Wb))
+    Yb = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+
+    def one_round_bf16():
+        for Wq, sw, Wb in sets_b:
+            mm.mixed_matmul(Xb, Wq, sw, Wb, w.tau, workspace=ws, out=Yb)
+
+    one_round_bf16()
+    torch.cuda.synchronize()
+    graph_b = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph_b):
+        one_round_bf16()
+    torch.cuda.synchronize()
+
+    def step_bf16(i, e):
+        if e is not None:
+            e[0].record()
+        graph_b.replay()
+        if e is not None:
+            e[1].record()
+            e[2].record()
+
+    log(f"decode, bf16 variant: {rounds} timed graph replays")
+    wall_b, evs_b = timed_loop(torch, rounds, max(1, warmup // DECODE_ROTATE + 1), step_bf16)
+    call_b_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs_b])) / DECODE_ROTATE
+    del sets_b, graph_b
     dbg = mm.mixed_matmul_debug(X, Wq0, sw0, W16_0, w.tau)
     o = int(dbg["count"][0])
     wbytes = K * N + 4.0 * N
@@ -254,6 +322,7 @@ def bench_decode(torch, mm, synth, steps, warmup):
         "steps": steps, "weight_gbs": wbytes * steps / wall / 1e9, "call_ms": call_ms,
         "alg_bytes": alg_bytes, "alg_gbs": alg_bytes / (call_ms * 1e-3) / 1e9,
         "halved_weight_gbs": wbytes * steps / wall_h / 1e9, "halved_call_ms": call_h_ms,
+        "bf16_weight_gbs": wbytes * steps / wall_b / 1e9, "bf16_call_ms": call_b_ms,
     }
 
 
@@ -369,12 +438,13 @@ def main():
         pre = bench_prefill(torch, mm, synth, args.steps, args.warmup)
         log(f"prefill: {pre['tops']:.1f} TOPS ({pre['ms_per_step']:.3f} ms/step), "
             f"gemm {pre['gemm_ms']:.3f} ms, activation pass {pre['activation_ms']:.3f} ms; "
-            f"memory-halved {pre['halved_tops']:.1f} TOPS")
+            f"memory-halved {pre['halved_tops']:.1f} TOPS, bf16 {pre['bf16_tops']:.1f} TOPS")
         torch.cuda.empty_cache()
     if args.only in (None, "decode"):
         dec = bench_decode(torch, mm, synth, args.steps, args.warmup)
         log(f"decode: {dec['weight_gbs']:.1f} GB/s weight ({dec['call_ms'] * 1e3:.1f} us/call); "
-            f"memory-halved {dec['halved_weight_gbs']:.1f} GB/s ({dec['halved_call_ms'] * 1e3:.1f} us/call)")
+            f"memory-halved {dec['halved_weight_gbs']:.1f} GB/s ({dec['halved_call_ms'] * 1e3:.1f} us/call), "
+            f"bf16 {dec['bf16_weight_gbs']:.1f} GB/s ({dec['bf16_call_ms'] * 1e3:.1f} us/call)")
 
     gemm_digest = src_digest(["k_gemm.hip", "common.hpp"])
     decode_digest = src_digest(["k_decode.hip", "common.hpp"])
@@ -406,9 +476,16 @@ def main():
                               "TOPS": round(pre["halved_tops"], 2),
                               "ms_per_step": round(pre["halved_ms_per_step"], 4),
                               "gemm_ms": round(pre["halved_gemm_ms"], 4)},
+            "bf16_variant": {"note": "X, W16, Y bfloat16 (the same values rounded to bf16); "
+                                     "whole int8_mixed_matmul_bf16 calls",
+                             "TOPS": round(pre["bf16_tops"], 2),
+                             "ms_per_step": round(pre["bf16_ms_per_step"], 4)},
             "quantize_weight": {"ms": round(pre["quantize_weight_ms"], 4),
                                 "GB/s": round(pre["quantize_weight_gbs"], 1),
-                                "bytes": "2KN read + KN + 4N written"},
+                                "bytes": "one read of W (2KN, or 4KN for fp32) + KN + 4N "
+                                         "written",
+                                "from_bf16": pre["convert"]["bf16"],
+                                "from_f32": pre["convert"]["f32"]},
         })
     if dec is not None:
         d = {"metric": "weight GB/s @ T=8", "value": round(dec["weight_gbs"], 1), "unit": "GB/s",
@@ -428,7 +505,10 @@ def main():
              "memory_halved": {"note": "W16 not passed: outlier rows recovered from the Int8 "
                                        "weight",
                                "weight GB/s": round(dec["halved_weight_gbs"], 1),
-                               "call_ms": round(dec["halved_call_ms"], 5)}}
+                               "call_ms": round(dec["halved_call_ms"], 5)},
+             "bf16_variant": {"note": "X, W16, Y bfloat16",
+                              "weight GB/s": round(dec["bf16_weight_gbs"], 1),
+                              "call_ms": round(dec["bf16_call_ms"], 5)}}
         if pre is None:
             out.update({"value": d["value"], "unit": "GB/s", "ms_per_step": d["ms_per_step"],
                         "config": d["config"], "roofline": d["roofline"]})
