@@ -90,6 +90,22 @@ def measured_traffic(profile_name: str, digest: str, key: str):
     return float(vals[key])
 
 
+PREWARM_S = 0.3
+
+
+def prewarm(torch, body, seconds=PREWARM_S):
+    """Untimed calls for `seconds` of wall time before the warmup steps: the
+    GPU's clocks ramp up over tens of milliseconds after idle time (host-side
+    input generation), and a few warmup steps alone leave the first timed
+    loop of a run measurably slower than later ones."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for i in range(4):
+            body(i, None)
+        torch.cuda.synchronize()
+
+
 def timed_loop(torch, steps, warmup, body):
     """Runs body(i, evs) warmup + steps times; returns the wall time of the
     timed steps (synchronized on both sides) and the event lists."""
@@ -143,7 +159,8 @@ def bench_prefill(torch, mm, synth, steps, warmup):
         if e is not None:
             e[2].record()
 
-    log(f"prefill: {warmup} warmup + {steps} timed steps")
+    log(f"prefill: {PREWARM_S} s prewarm, {warmup} warmup + {steps} timed steps")
+    prewarm(torch, step)
     wall, evs = timed_loop(torch, steps, warmup, step)
     act_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     gemm_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
@@ -252,7 +269,9 @@ def bench_decode(torch, mm, synth, steps, warmup):
             e[1].record()
             e[2].record()
 
-    log(f"decode: {warmup} warmup + {rounds} timed graph replays of {DECODE_ROTATE} calls")
+    log(f"decode: {PREWARM_S} s prewarm, {warmup} warmup + {rounds} timed graph replays of "
+        f"{DECODE_ROTATE} calls")
+    prewarm(torch, step)
     wall, evs = timed_loop(torch, rounds, max(1, warmup // DECODE_ROTATE + 1), step)
     call_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) / DECODE_ROTATE
 
@@ -352,6 +371,7 @@ def bench_sweep(torch, mm, synth, steps, warmup):
                 mm.matmul_prepared(ws, T, K, Wq, sw, w16, out=Y)
                 if e is not None:
                     e[2].record()
+            prewarm(torch, step, 0.15)
             wall, evs = timed_loop(torch, steps, warmup, step)
             act = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
             gemm = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))

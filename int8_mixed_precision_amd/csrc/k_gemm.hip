@@ -91,68 +91,86 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a,
     }
     const int o = a.count[0];
     const int opad = a.count[1];
-    // one 32-row strip of tiles at a time keeps the fp32 values of only TN
-    // tiles live next to the integer accumulators
+    // dequantize every tile (the integer accumulators die here, so the fp32
+    // values take their registers; keeping the fp32 values in the integer
+    // array through bit casts instead was compiled wrongly - the four rows of
+    // a lane's row group were stored from one register)
+    v16f y[TM][TN];
+    // rows as 32-bit values (T < 2^24); rows past T read the last row's
+    // scale (those outputs are never stored), so the loads are unconditional
+    const int Ti = (int)T;
+    int mrow0 = (int)mb + row_l;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-        v16f y[TN];
-        {
-            float sxm[16];
+        float sxm[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t m = mb + i * 32 + (r >> 2) * 8 + row_l + (r & 3);
-                sxm[r] = m < T ? a.sx[m] : 0.0f;
-            }
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) y[j][r] = (float)acc[i][j][r] * sxm[r] * swn[j];
+        for (int r = 0; r < 16; ++r) {
+            const int m = mrow0 + i * 32 + (r >> 2) * 8 + (r & 3);
+            sxm[r] = a.sx[m < Ti ? m : Ti - 1];
         }
-        // 16-bit matmul over the isolated outlier dimensions, 16 at a time,
-        // with the dequantized values as the fp32 C operand
-        for (int jc = 0; jc < opad; jc += 16) {
-            const int jl = jc + (lane >> 5) * 8;   // first of this lane's 8 outlier slots
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) y[i][j][r] = (float)acc[i][j][r] * sxm[r] * swn[j];
+    }
+    // 16-bit matmul over the isolated outlier dimensions, 16 at a time, with
+    // the dequantized values as the fp32 C operand.  A group's weight
+    // fragments (8 gathered values of one column per lane) are loaded once
+    // and serve all TM row strips.
+    for (int jc = 0; jc < opad; jc += 16) {
+        const int jl = jc + (lane >> 5) * 8;   // first of this lane's 8 outlier slots
+        int kk[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kk[e] = (jl + e < o) ? a.idx[jl + e] : -1;
+        v8u16 wb[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int64_t n = nb + j * 32 + col_l;
+            if (!recover) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    wb[j][e] = (kk[e] >= 0 && n < N) ? a.w16[(int64_t)kk[e] * N + n] : (uint16_t)0;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    wb[j][e] = (kk[e] >= 0 && n < N)
+                                   ? recover_weight<HT>(a.wq[n * a.K + kk[e]], dn[j])
+                                   : (uint16_t)0;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
             const int64_t mrow = mb + i * 32 + (lane & 31);
             const v8u16 xa = mrow < T ? *reinterpret_cast<const v8u16*>(a.xo + mrow * opad + jl)
                                       : v8u16{0, 0, 0, 0, 0, 0, 0, 0};
-            int64_t kk[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) kk[e] = (jl + e < o) ? (int64_t)a.idx[jl + e] : -1;
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
-                const int64_t n = nb + j * 32 + col_l;
-                v8u16 wb;
-                if (!recover) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        wb[e] = (kk[e] >= 0 && n < N) ? a.w16[kk[e] * N + n] : (uint16_t)0;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        wb[e] = (kk[e] >= 0 && n < N)
-                                    ? recover_weight<HT>(a.wq[n * a.K + kk[e]], dn[j])
-                                    : (uint16_t)0;
-                }
                 if constexpr (HT == kHalfBF16)
-                    y[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, xa),
-                                                                   __builtin_bit_cast(v8bf, wb),
-                                                                   y[j], 0, 0, 0);
+                    y[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(v8bf, xa), __builtin_bit_cast(v8bf, wb[j]), y[i][j],
+                        0, 0, 0);
                 else
-                    y[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, xa),
-                                                                  __builtin_bit_cast(v8h, wb),
-                                                                  y[j], 0, 0, 0);
+                    y[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                        __builtin_bit_cast(v8h, xa), __builtin_bit_cast(v8h, wb[j]), y[i][j],
+                        0, 0, 0);
             }
         }
+    }
+    // the row indices are recomputed here rather than kept live through the
+    // outlier loop (an empty asm hides the earlier values from the compiler)
+    asm volatile("" : "+v"(mrow0));
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int64_t n = nb + j * 32 + col_l;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int64_t m = mb + i * 32 + (r >> 2) * 8 + row_l + (r & 3);
-                if (m < T && n < N) a.y[m * N + n] = f32_to_h16<HT>(y[j][r]);
+                const int m = mrow0 + i * 32 + (r >> 2) * 8 + (r & 3);
+                if (m < Ti && n < N)
+                    a.y[(int64_t)m * N + n] = f32_to_h16<HT>(y[i][j][r]);
             }
         }
-    }
 }
 
 // XCD-aware renumbering: hardware deals workgroups round-robin over the 8
