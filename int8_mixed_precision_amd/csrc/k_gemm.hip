@@ -53,9 +53,21 @@ __device__ inline int swz(int row, int c) {
 // 32x32 accumulator tiles whose top-left output element is (mb, nb).
 // 32x32 accumulator layout: lane holds column (lane & 31) and, in register
 // r, row 8*(r/4) + 4*(lane/32) + (r%4) of the tile.
-template <int TM, int TN, bool WRITE_ACC, int HT>
+// What the large-tile kernel hands its epilogue for staging the outlier
+// operands through LDS (the other kernels pass an empty one).
+struct StageCtx {
+    int8_t* lds;      // at least kStageBytes, free once the main loop is done
+    int tid;          // 0 .. 511
+    int64_t m0, n0;   // the workgroup's 256 x 256 output tile
+};
+constexpr int kOC = 32;                       // outliers per staged chunk
+constexpr int kOS = kOC * 2 + 16;             // bytes per staged row / column (padded)
+constexpr int kStageHalf = 256 * kOS;         // X part (rows) or W part (columns)
+constexpr int kStageBytes = 4 * kStageHalf;   // two buffers of X and W
+
+template <int TM, int TN, bool WRITE_ACC, int HT, bool STAGED = false>
 __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a, int64_t mb,
-                                         int64_t nb, int lane) {
+                                         int64_t nb, int lane, const StageCtx& sc = StageCtx{}) {
     const int64_t T = a.T, N = a.N;
     const int col_l = lane & 31;
     const int row_l = (lane >> 5) * 4;
@@ -113,46 +125,151 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a,
 #pragma unroll
             for (int r = 0; r < 16; ++r) y[i][j][r] = (float)acc[i][j][r] * sxm[r] * swn[j];
     }
-    // 16-bit matmul over the isolated outlier dimensions, 16 at a time, with
-    // the dequantized values as the fp32 C operand.  A group's weight
-    // fragments (8 gathered values of one column per lane) are loaded once
-    // and serve all TM row strips.
-    for (int jc = 0; jc < opad; jc += 16) {
-        const int jl = jc + (lane >> 5) * 8;   // first of this lane's 8 outlier slots
-        int kk[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) kk[e] = (jl + e < o) ? a.idx[jl + e] : -1;
-        v8u16 wb[TN];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int64_t n = nb + j * 32 + col_l;
-            if (!recover) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    wb[j][e] = (kk[e] >= 0 && n < N) ? a.w16[(int64_t)kk[e] * N + n] : (uint16_t)0;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    wb[j][e] = (kk[e] >= 0 && n < N)
-                                   ? recover_weight<HT>(a.wq[n * a.K + kk[e]], dn[j])
-                                   : (uint16_t)0;
+    if constexpr (!STAGED) {
+        // 16-bit matmul over the isolated outlier dimensions, 16 at a time, with
+        // the dequantized values as the fp32 C operand.  A group's weight
+        // fragments (8 gathered values of one column per lane) are loaded once
+        // and serve all TM row strips.
+        for (int jc = 0; jc < opad; jc += 16) {
+            const int jl = jc + (lane >> 5) * 8;   // first of this lane's 8 outlier slots
+            int kk[8];
+    #pragma unroll
+            for (int e = 0; e < 8; ++e) kk[e] = (jl + e < o) ? a.idx[jl + e] : -1;
+            v8u16 wb[TN];
+    #pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int64_t n = nb + j * 32 + col_l;
+                if (!recover) {
+    #pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        wb[j][e] = (kk[e] >= 0 && n < N) ? a.w16[(int64_t)kk[e] * N + n] : (uint16_t)0;
+                } else {
+    #pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        wb[j][e] = (kk[e] >= 0 && n < N)
+                                       ? recover_weight<HT>(a.wq[n * a.K + kk[e]], dn[j])
+                                       : (uint16_t)0;
+                }
+            }
+    #pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int64_t mrow = mb + i * 32 + (lane & 31);
+                const v8u16 xa = mrow < T ? *reinterpret_cast<const v8u16*>(a.xo + mrow * opad + jl)
+                                          : v8u16{0, 0, 0, 0, 0, 0, 0, 0};
+    #pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    if constexpr (HT == kHalfBF16)
+                        y[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(v8bf, xa), __builtin_bit_cast(v8bf, wb[j]), y[i][j],
+                            0, 0, 0);
+                    else
+                        y[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                            __builtin_bit_cast(v8h, xa), __builtin_bit_cast(v8h, wb[j]), y[i][j],
+                            0, 0, 0);
+                }
             }
         }
+    } else if (opad > 0) {
+        // Staged through LDS, kOC outliers per chunk, double buffered: the
+        // 512 threads load the chunk's X columns (256 rows x kOC, coalesced
+        // along the compacted outliers) and W rows (kOC x 256 columns,
+        // transposed on the way into LDS so that a lane's 8 outliers of one
+        // column are contiguous), then every wave reads its MFMA fragments
+        // from LDS.  The next chunk's loads fly during this chunk's MFMAs;
+        // the outlier indices are fetched one chunk ahead of their use.
+        __syncthreads();   // the main loop's LDS reads are complete
+        const int t = sc.tid;
+        const int e = t & 31, cb = t >> 5;        // W: outlier slot, 16-column block
+        const int xr = t >> 1, xh = t & 1;        // X: tile row, 16-outlier half
+        const int64_t xrow = sc.m0 + xr;
+        float dcol[16];
+        if (recover) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int64_t mrow = mb + i * 32 + (lane & 31);
-            const v8u16 xa = mrow < T ? *reinterpret_cast<const v8u16*>(a.xo + mrow * opad + jl)
-                                      : v8u16{0, 0, 0, 0, 0, 0, 0, 0};
+            for (int c = 0; c < 16; ++c) {
+                const int64_t n = sc.n0 + cb * 16 + c;
+                dcol[c] = n < N ? a.sw[n] / 127.0f : 0.0f;
+            }
+        }
+        int k_next = e < o ? a.idx[e] : -1;
+        uint4 wv[2], xv[2];
+        auto load_chunk = [&](int jc) {
+            const int k = k_next;
+            k_next = jc + kOC + e < o ? a.idx[jc + kOC + e] : -1;
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                if constexpr (HT == kHalfBF16)
-                    y[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(v8bf, xa), __builtin_bit_cast(v8bf, wb[j]), y[i][j],
-                        0, 0, 0);
-                else
-                    y[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                        __builtin_bit_cast(v8h, xa), __builtin_bit_cast(v8h, wb[j]), y[i][j],
-                        0, 0, 0);
+            for (int h = 0; h < 2; ++h) {
+                const int64_t n = sc.n0 + cb * 16 + h * 8;
+                if (!recover) {
+                    wv[h] = (k >= 0 && n < N)
+                                ? *reinterpret_cast<const uint4*>(a.w16 + (int64_t)k * N + n)
+                                : make_uint4(0u, 0u, 0u, 0u);
+                } else {
+                    uint32_t p[4];
+#pragma unroll
+                    for (int c = 0; c < 8; c += 2) {
+                        const int64_t n0c = n + c;
+                        const uint16_t lo = (k >= 0 && n0c < N)
+                                                ? recover_weight<HT>(a.wq[n0c * a.K + k], dcol[h * 8 + c])
+                                                : (uint16_t)0;
+                        const uint16_t hi = (k >= 0 && n0c + 1 < N)
+                                                ? recover_weight<HT>(a.wq[(n0c + 1) * a.K + k],
+                                                                     dcol[h * 8 + c + 1])
+                                                : (uint16_t)0;
+                        p[c >> 1] = (uint32_t)lo | ((uint32_t)hi << 16);
+                    }
+                    wv[h] = make_uint4(p[0], p[1], p[2], p[3]);
+                }
+                const int jx = jc + xh * 16 + h * 8;
+                xv[h] = (xrow < T && jx < opad)
+                            ? *reinterpret_cast<const uint4*>(a.xo + xrow * opad + jx)
+                            : make_uint4(0u, 0u, 0u, 0u);
+            }
+        };
+        auto store_chunk = [&](int buf) {
+            int8_t* xs = sc.lds + buf * 2 * kStageHalf;
+            int8_t* ws = xs + kStageHalf;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                *reinterpret_cast<uint4*>(xs + xr * kOS + xh * 32 + h * 16) = xv[h];
+                const uint32_t w4[4] = {wv[h].x, wv[h].y, wv[h].z, wv[h].w};
+#pragma unroll
+                for (int c = 0; c < 8; ++c)
+                    *reinterpret_cast<uint16_t*>(ws + (cb * 16 + h * 8 + c) * kOS + e * 2) =
+                        (uint16_t)(w4[c >> 1] >> ((c & 1) * 16));
+            }
+        };
+        load_chunk(0);
+        for (int jc = 0; jc < opad; jc += kOC) {
+            const int buf = (jc / kOC) & 1;
+            store_chunk(buf);
+            __syncthreads();
+            if (jc + kOC < opad) load_chunk(jc + kOC);
+            const int8_t* xs = sc.lds + buf * 2 * kStageHalf;
+            const int8_t* ws = xs + kStageHalf;
+            const int wm0 = (int)(mb - sc.m0), wn0 = (int)(nb - sc.n0);
+#pragma unroll
+            for (int ks = 0; ks < kOC / 16; ++ks) {
+                if (jc + ks * 16 >= opad) break;
+                const int ko = ks * 32 + (lane >> 5) * 16;
+                v8u16 wb[TN];
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    wb[j] = *reinterpret_cast<const v8u16*>(ws + (wn0 + j * 32 + col_l) * kOS + ko);
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
+                    const v8u16 xa =
+                        *reinterpret_cast<const v8u16*>(xs + (wm0 + i * 32 + col_l) * kOS + ko);
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) {
+                        if constexpr (HT == kHalfBF16)
+                            y[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                __builtin_bit_cast(v8bf, xa), __builtin_bit_cast(v8bf, wb[j]),
+                                y[i][j], 0, 0, 0);
+                        else
+                            y[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                                __builtin_bit_cast(v8h, xa), __builtin_bit_cast(v8h, wb[j]),
+                                y[i][j], 0, 0, 0);
+                    }
+                }
             }
         }
     }
@@ -449,9 +566,12 @@ __global__ __launch_bounds__(128 * WN) void k_gemm_i8_big(GemmArgs a) {
         }
         s_cur = s_next;
     }
-    // no LDS copy may still be in flight when the workgroup retires
+    // no LDS copy may still be in flight when the LDS is reused or the
+    // workgroup retires
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    epilogue<TM, TN, WRITE_ACC, HT>(acc, a, m0 + wm0, n0 + wn0, lane);
+    static_assert(THREADS == 512 && STAGES * STAGE_BYTES >= kStageBytes, "staged epilogue");
+    epilogue<TM, TN, WRITE_ACC, HT, true>(acc, a, m0 + wm0, n0 + wn0, lane,
+                                          StageCtx{lds, tid, m0, n0});
 }
 
 template <int BM, int BN, int BK, int WAVES_M, int HT>
