@@ -50,6 +50,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--only", choices=["prefill", "decode"], default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-variants", action="store_true",
+                   help="skip the memory-halved and bf16 variants (profiling runs that should "
+                        "see only the headline kernels)")
     p.add_argument("--sweep", action="store_true",
                    help="instead of the headline run: the four projections of a 175B-class "
                         "block at T=4096 with 0, 8, 64 and 256 planted outlier dimensions "
@@ -122,48 +125,11 @@ def timed_loop(torch, steps, warmup, body):
     return time.perf_counter() - t0, evs
 
 
-def bench_prefill(torch, mm, synth, steps, warmup):
-    w = synth.WORKLOADS["up"]
+def prefill_variants(torch, mm, w, X, W16, Wq, sw, ws, Y, steps, warmup):
+    """The memory-halved and bf16 variants of the prefill step and the
+    fp32/bf16 checkpoint conversion, on the same inputs."""
     T, K, N = w.T, w.K, w.N
-    log(f"prefill: generating X [{T},{K}], W [{K},{N}]")
-    X = torch.from_numpy(synth.make_x(w, threads=CPU_THREADS)).cuda()
-    Wh = synth.make_w(w, threads=CPU_THREADS)
-    W16 = torch.from_numpy(Wh).cuda()
-    del Wh
-    Wq = torch.empty(mm.weight_bytes(K, N), dtype=torch.int8, device="cuda")
-    sw = torch.empty(N, dtype=torch.float32, device="cuda")
-    # weight conversion (once per weight), timed on its own
-    for _ in range(2):
-        mm.quantize_weight(W16, out=(Wq, sw))
-    torch.cuda.synchronize()
-    qa, qb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    qa.record()
-    for _ in range(5):
-        mm.quantize_weight(W16, out=(Wq, sw))
-    qb.record()
-    torch.cuda.synchronize()
-    q_ms = qa.elapsed_time(qb) / 5
-
-    ws = mm.new_workspace(T, K, N)
-    Y = torch.empty((T, N), dtype=torch.float16, device="cuda")
-
-    def step(i, e):
-        # int8_mixed_matmul == quantize_activations + matmul_prepared (same
-        # kernels, same stream); the split lets the events bracket the matmul
-        if e is not None:
-            e[0].record()
-        mm.quantize_activations(X, N, w.tau, ws)
-        if e is not None:
-            e[1].record()
-        mm.matmul_prepared(ws, T, K, Wq, sw, W16, out=Y)
-        if e is not None:
-            e[2].record()
-
-    log(f"prefill: {PREWARM_S} s prewarm, {warmup} warmup + {steps} timed steps")
-    prewarm(torch, step)
-    wall, evs = timed_loop(torch, steps, warmup, step)
-    act_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    gemm_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ops = 2.0 * T * K * N
     # the memory-halved variant (no 16-bit weight: outlier rows recovered
     # from the Int8 weight), same steps
     def step_halved(i, e):
@@ -211,6 +177,55 @@ def bench_prefill(torch, mm, synth, steps, warmup):
                      "GB/s": round((Wc.element_size() * K * N + K * N + 4.0 * N) /
                                    (ms * 1e-3) / 1e9, 1)}
     del W32, Xb, Wb, Wqb, swb, Yb
+    return {"halved_tops": ops * steps / wall_h / 1e12, "halved_ms_per_step": wall_h * 1e3 / steps,
+            "halved_gemm_ms": gemm_h_ms,
+            "bf16_tops": ops * steps / wall_b / 1e12, "bf16_ms_per_step": wall_b * 1e3 / steps,
+            "convert": conv}
+
+
+def bench_prefill(torch, mm, synth, steps, warmup, variants=True):
+    w = synth.WORKLOADS["up"]
+    T, K, N = w.T, w.K, w.N
+    log(f"prefill: generating X [{T},{K}], W [{K},{N}]")
+    X = torch.from_numpy(synth.make_x(w, threads=CPU_THREADS)).cuda()
+    Wh = synth.make_w(w, threads=CPU_THREADS)
+    W16 = torch.from_numpy(Wh).cuda()
+    del Wh
+    Wq = torch.empty(mm.weight_bytes(K, N), dtype=torch.int8, device="cuda")
+    sw = torch.empty(N, dtype=torch.float32, device="cuda")
+    # weight conversion (once per weight), timed on its own
+    for _ in range(2):
+        mm.quantize_weight(W16, out=(Wq, sw))
+    torch.cuda.synchronize()
+    qa, qb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    qa.record()
+    for _ in range(5):
+        mm.quantize_weight(W16, out=(Wq, sw))
+    qb.record()
+    torch.cuda.synchronize()
+    q_ms = qa.elapsed_time(qb) / 5
+
+    ws = mm.new_workspace(T, K, N)
+    Y = torch.empty((T, N), dtype=torch.float16, device="cuda")
+
+    def step(i, e):
+        # int8_mixed_matmul == quantize_activations + matmul_prepared (same
+        # kernels, same stream); the split lets the events bracket the matmul
+        if e is not None:
+            e[0].record()
+        mm.quantize_activations(X, N, w.tau, ws)
+        if e is not None:
+            e[1].record()
+        mm.matmul_prepared(ws, T, K, Wq, sw, W16, out=Y)
+        if e is not None:
+            e[2].record()
+
+    log(f"prefill: {PREWARM_S} s prewarm, {warmup} warmup + {steps} timed steps")
+    prewarm(torch, step)
+    wall, evs = timed_loop(torch, steps, warmup, step)
+    act_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    gemm_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    extra = prefill_variants(torch, mm, w, X, W16, Wq, sw, ws, Y, steps, warmup) if variants else {}
     # the outlier count of this X (one debug call, outside the timed loop)
     dbg = mm.mixed_matmul_debug(X, Wq, sw, W16, w.tau)
     o = int(dbg["count"][0])
@@ -222,59 +237,18 @@ def bench_prefill(torch, mm, synth, steps, warmup):
         "tops": ops * steps / wall / 1e12,
         "activation_ms": act_ms, "gemm_ms": gemm_ms,
         "gemm_tops": ops / (gemm_ms * 1e-3) / 1e12,
-        "halved_tops": ops * steps / wall_h / 1e12, "halved_ms_per_step": wall_h * 1e3 / steps,
-        "halved_gemm_ms": gemm_h_ms,
-        "bf16_tops": ops * steps / wall_b / 1e12, "bf16_ms_per_step": wall_b * 1e3 / steps,
-        "convert": conv,
         "quantize_weight_ms": q_ms,
         "quantize_weight_gbs": (2.0 * K * N + K * N + 4.0 * N) / (q_ms * 1e-3) / 1e9,
+        **extra,
     }
 
 
-def bench_decode(torch, mm, synth, steps, warmup):
-    w = synth.WORKLOADS["dec"]
+def decode_variants(torch, mm, w, X, sets, ws, Y, rounds, warmup):
+    """The memory-halved and bf16 variants of the decode call (graph replays
+    over the same rotating weight copies)."""
     T, K, N = w.T, w.K, w.N
-    log(f"decode: generating X [{T},{K}], W [{K},{N}], {DECODE_ROTATE} weight copies")
-    X = torch.from_numpy(synth.make_x(w, threads=CPU_THREADS)).cuda()
-    W16_0 = torch.from_numpy(synth.make_w(w, threads=CPU_THREADS)).cuda()
-    Wq0, sw0 = mm.quantize_weight(W16_0)
-    sets = [(Wq0, sw0, W16_0)]
-    for _ in range(DECODE_ROTATE - 1):
-        sets.append((Wq0.clone(), sw0.clone(), W16_0.clone()))
-    ws = mm.new_workspace(T, K, N)
-    Y = torch.empty((T, N), dtype=torch.float16, device="cuda")
-
-    # A decode call is tens of microseconds of GPU work, less than the Python
-    # binding takes to issue it, so the steps are launched from a HIP graph
-    # (one replay = DECODE_ROTATE calls, one per weight copy), as a serving
-    # loop would.  The graph holds only the library's own kernel launches.
-    def one_round():
-        for Wq, sw, W16 in sets:
-            mm.mixed_matmul(X, Wq, sw, W16, w.tau, workspace=ws, out=Y)
-
-    one_round()
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        one_round()
-    torch.cuda.synchronize()
-    rounds = max(1, (steps + DECODE_ROTATE - 1) // DECODE_ROTATE)
     steps = rounds * DECODE_ROTATE
-
-    def step(i, e):
-        if e is not None:
-            e[0].record()
-        graph.replay()
-        if e is not None:
-            e[1].record()
-            e[2].record()
-
-    log(f"decode: {PREWARM_S} s prewarm, {warmup} warmup + {rounds} timed graph replays of "
-        f"{DECODE_ROTATE} calls")
-    prewarm(torch, step)
-    wall, evs = timed_loop(torch, rounds, max(1, warmup // DECODE_ROTATE + 1), step)
-    call_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) / DECODE_ROTATE
-
+    wbytes = K * N + 4.0 * N
     # the memory-halved variant: no 16-bit weight passed at all
     def one_round_halved():
         for Wq, sw, _ in sets:
@@ -332,6 +306,55 @@ def bench_decode(torch, mm, synth, steps, warmup):
     wall_b, evs_b = timed_loop(torch, rounds, max(1, warmup // DECODE_ROTATE + 1), step_bf16)
     call_b_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs_b])) / DECODE_ROTATE
     del sets_b, graph_b
+    return {"halved_weight_gbs": wbytes * steps / wall_h / 1e9, "halved_call_ms": call_h_ms,
+            "bf16_weight_gbs": wbytes * steps / wall_b / 1e9, "bf16_call_ms": call_b_ms}
+
+
+def bench_decode(torch, mm, synth, steps, warmup, variants=True):
+    w = synth.WORKLOADS["dec"]
+    T, K, N = w.T, w.K, w.N
+    log(f"decode: generating X [{T},{K}], W [{K},{N}], {DECODE_ROTATE} weight copies")
+    X = torch.from_numpy(synth.make_x(w, threads=CPU_THREADS)).cuda()
+    W16_0 = torch.from_numpy(synth.make_w(w, threads=CPU_THREADS)).cuda()
+    Wq0, sw0 = mm.quantize_weight(W16_0)
+    sets = [(Wq0, sw0, W16_0)]
+    for _ in range(DECODE_ROTATE - 1):
+        sets.append((Wq0.clone(), sw0.clone(), W16_0.clone()))
+    ws = mm.new_workspace(T, K, N)
+    Y = torch.empty((T, N), dtype=torch.float16, device="cuda")
+
+    # A decode call is tens of microseconds of GPU work, less than the Python
+    # binding takes to issue it, so the steps are launched from a HIP graph
+    # (one replay = DECODE_ROTATE calls, one per weight copy), as a serving
+    # loop would.  The graph holds only the library's own kernel launches.
+    def one_round():
+        for Wq, sw, W16 in sets:
+            mm.mixed_matmul(X, Wq, sw, W16, w.tau, workspace=ws, out=Y)
+
+    one_round()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        one_round()
+    torch.cuda.synchronize()
+    rounds = max(1, (steps + DECODE_ROTATE - 1) // DECODE_ROTATE)
+    steps = rounds * DECODE_ROTATE
+
+    def step(i, e):
+        if e is not None:
+            e[0].record()
+        graph.replay()
+        if e is not None:
+            e[1].record()
+            e[2].record()
+
+    log(f"decode: {PREWARM_S} s prewarm, {warmup} warmup + {rounds} timed graph replays of "
+        f"{DECODE_ROTATE} calls")
+    prewarm(torch, step)
+    wall, evs = timed_loop(torch, rounds, max(1, warmup // DECODE_ROTATE + 1), step)
+    call_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) / DECODE_ROTATE
+
+    extra = decode_variants(torch, mm, w, X, sets, ws, Y, rounds, warmup) if variants else {}
     dbg = mm.mixed_matmul_debug(X, Wq0, sw0, W16_0, w.tau)
     o = int(dbg["count"][0])
     wbytes = K * N + 4.0 * N
@@ -340,8 +363,7 @@ def bench_decode(torch, mm, synth, steps, warmup):
         "T": T, "K": K, "N": N, "tau": w.tau, "o": o, "ms_per_step": wall * 1e3 / steps,
         "steps": steps, "weight_gbs": wbytes * steps / wall / 1e9, "call_ms": call_ms,
         "alg_bytes": alg_bytes, "alg_gbs": alg_bytes / (call_ms * 1e-3) / 1e9,
-        "halved_weight_gbs": wbytes * steps / wall_h / 1e9, "halved_call_ms": call_h_ms,
-        "bf16_weight_gbs": wbytes * steps / wall_b / 1e9, "bf16_call_ms": call_b_ms,
+        **extra,
     }
 
 
@@ -455,16 +477,18 @@ def main():
 
     pre = dec = None
     if args.only in (None, "prefill"):
-        pre = bench_prefill(torch, mm, synth, args.steps, args.warmup)
+        pre = bench_prefill(torch, mm, synth, args.steps, args.warmup, not args.no_variants)
         log(f"prefill: {pre['tops']:.1f} TOPS ({pre['ms_per_step']:.3f} ms/step), "
-            f"gemm {pre['gemm_ms']:.3f} ms, activation pass {pre['activation_ms']:.3f} ms; "
-            f"memory-halved {pre['halved_tops']:.1f} TOPS, bf16 {pre['bf16_tops']:.1f} TOPS")
+            f"gemm {pre['gemm_ms']:.3f} ms, activation pass {pre['activation_ms']:.3f} ms"
+            + (f"; memory-halved {pre['halved_tops']:.1f} TOPS, bf16 {pre['bf16_tops']:.1f} TOPS"
+               if "halved_tops" in pre else ""))
         torch.cuda.empty_cache()
     if args.only in (None, "decode"):
-        dec = bench_decode(torch, mm, synth, args.steps, args.warmup)
-        log(f"decode: {dec['weight_gbs']:.1f} GB/s weight ({dec['call_ms'] * 1e3:.1f} us/call); "
-            f"memory-halved {dec['halved_weight_gbs']:.1f} GB/s ({dec['halved_call_ms'] * 1e3:.1f} us/call), "
-            f"bf16 {dec['bf16_weight_gbs']:.1f} GB/s ({dec['bf16_call_ms'] * 1e3:.1f} us/call)")
+        dec = bench_decode(torch, mm, synth, args.steps, args.warmup, not args.no_variants)
+        log(f"decode: {dec['weight_gbs']:.1f} GB/s weight ({dec['call_ms'] * 1e3:.1f} us/call)"
+            + (f"; memory-halved {dec['halved_weight_gbs']:.1f} GB/s "
+               f"({dec['halved_call_ms'] * 1e3:.1f} us/call), bf16 {dec['bf16_weight_gbs']:.1f} GB/s "
+               f"({dec['bf16_call_ms'] * 1e3:.1f} us/call)" if "halved_weight_gbs" in dec else ""))
 
     gemm_digest = src_digest(["k_gemm.hip", "common.hpp"])
     decode_digest = src_digest(["k_decode.hip", "common.hpp"])
@@ -491,22 +515,23 @@ def main():
                          "work": "2*T*K*N int8 ops per launch", "ms": round(pre["gemm_ms"], 4)},
             "stages_ms": {"activation_pass": round(pre["activation_ms"], 4),
                           "gemm": round(pre["gemm_ms"], 4)},
-            "memory_halved": {"note": "W16 not passed: outlier rows recovered from the Int8 "
-                                      "weight (same X, W, tau)",
-                              "TOPS": round(pre["halved_tops"], 2),
-                              "ms_per_step": round(pre["halved_ms_per_step"], 4),
-                              "gemm_ms": round(pre["halved_gemm_ms"], 4)},
-            "bf16_variant": {"note": "X, W16, Y bfloat16 (the same values rounded to bf16); "
-                                     "whole int8_mixed_matmul_bf16 calls",
-                             "TOPS": round(pre["bf16_tops"], 2),
-                             "ms_per_step": round(pre["bf16_ms_per_step"], 4)},
             "quantize_weight": {"ms": round(pre["quantize_weight_ms"], 4),
                                 "GB/s": round(pre["quantize_weight_gbs"], 1),
                                 "bytes": "one read of W (2KN, or 4KN for fp32) + KN + 4N "
-                                         "written",
-                                "from_bf16": pre["convert"]["bf16"],
-                                "from_f32": pre["convert"]["f32"]},
+                                         "written"},
         })
+        if "halved_tops" in pre:
+            out["memory_halved"] = {"note": "W16 not passed: outlier rows recovered from the "
+                                            "Int8 weight (same X, W, tau)",
+                                    "TOPS": round(pre["halved_tops"], 2),
+                                    "ms_per_step": round(pre["halved_ms_per_step"], 4),
+                                    "gemm_ms": round(pre["halved_gemm_ms"], 4)}
+            out["bf16_variant"] = {"note": "X, W16, Y bfloat16 (the same values rounded to "
+                                           "bf16); whole int8_mixed_matmul_bf16 calls",
+                                   "TOPS": round(pre["bf16_tops"], 2),
+                                   "ms_per_step": round(pre["bf16_ms_per_step"], 4)}
+            out["quantize_weight"]["from_bf16"] = pre["convert"]["bf16"]
+            out["quantize_weight"]["from_f32"] = pre["convert"]["f32"]
     if dec is not None:
         d = {"metric": "weight GB/s @ T=8", "value": round(dec["weight_gbs"], 1), "unit": "GB/s",
              "ms_per_step": round(dec["ms_per_step"], 5), "steps": dec["steps"],
@@ -521,14 +546,15 @@ def main():
                           "traffic": measured_traffic("decode_dec_traffic.md", decode_digest, "hbm_bytes_per_launch"),
                           "kernel": "k_decode (the whole int8_mixed_matmul call)",
                           "work": "2TK + KN + 4N + 2oN + 2TN bytes per call",
-                          "ms": round(dec["call_ms"], 5)},
-             "memory_halved": {"note": "W16 not passed: outlier rows recovered from the Int8 "
-                                       "weight",
-                               "weight GB/s": round(dec["halved_weight_gbs"], 1),
-                               "call_ms": round(dec["halved_call_ms"], 5)},
-             "bf16_variant": {"note": "X, W16, Y bfloat16",
-                              "weight GB/s": round(dec["bf16_weight_gbs"], 1),
-                              "call_ms": round(dec["bf16_call_ms"], 5)}}
+                          "ms": round(dec["call_ms"], 5)}}
+        if "halved_weight_gbs" in dec:
+            d["memory_halved"] = {"note": "W16 not passed: outlier rows recovered from the "
+                                          "Int8 weight",
+                                  "weight GB/s": round(dec["halved_weight_gbs"], 1),
+                                  "call_ms": round(dec["halved_call_ms"], 5)}
+            d["bf16_variant"] = {"note": "X, W16, Y bfloat16",
+                                 "weight GB/s": round(dec["bf16_weight_gbs"], 1),
+                                 "call_ms": round(dec["bf16_call_ms"], 5)}
         if pre is None:
             out.update({"value": d["value"], "unit": "GB/s", "ms_per_step": d["ms_per_step"],
                         "config": d["config"], "roofline": d["roofline"]})
