@@ -206,6 +206,86 @@ __global__ __launch_bounds__(kQuantThreads) void k_rowquant(
     if (tid == 0) sx[t] = mx;
 }
 
+// k_rowquant for rows of at most kQuantThreads * kRowCache * 8 values: the
+// row is read from HBM once into registers (one pass instead of two), the
+// outlier bitmap once into LDS, and every load is issued before the first
+// use (chunks past the row re-read chunk 0; nothing uses them).
+// CACHE = 16-byte chunks per thread: K <= 16384 (8) or K <= 49152 (24).
+template <int HT, int kRowCache>
+__global__ __launch_bounds__(kQuantThreads) void k_rowquant_cached(
+    const uint16_t* __restrict__ X, int64_t K, const uint32_t* __restrict__ flags,
+    const int32_t* __restrict__ wprefix, const int32_t* __restrict__ count,
+    int8_t* __restrict__ xq, float* __restrict__ sx, uint16_t* __restrict__ xo) {
+    __shared__ float red[kQuantThreads / kWave];
+    __shared__ uint32_t fl[kQuantThreads * kRowCache / 4];
+    const int tid = threadIdx.x;
+    const int64_t t = blockIdx.x;
+    const uint16_t* row = X + t * K;
+    const int nch = (int)(K / 8);
+    uint4 v[kRowCache];
+#pragma unroll
+    for (int i = 0; i < kRowCache; ++i) {
+        const int c = tid + kQuantThreads * i;
+        v[i] = *reinterpret_cast<const uint4*>(row + (c < nch ? c : 0) * 8);
+    }
+    const int kw = (nch + 3) / 4;
+    for (int w = tid; w < kw; w += kQuantThreads) fl[w] = flags[w];
+    __syncthreads();
+    float mx = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kRowCache; ++i) {
+        const int c = tid + kQuantThreads * i;
+        if (c < nch) {
+            const uint32_t fm = (fl[c >> 2] >> ((c & 3) * 8)) & 0xFFu;
+            const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float a = __builtin_fabsf(h16_to_f32<HT>((uint16_t)(w[e >> 1] >> ((e & 1) * 16))));
+                mx = ((fm >> e) & 1u) ? mx : __builtin_fmaxf(mx, a);
+            }
+        }
+    }
+    mx = wave_max(mx);
+    if ((tid & (kWave - 1)) == 0) red[tid / kWave] = mx;
+    __syncthreads();
+    mx = red[0];
+#pragma unroll
+    for (int i = 1; i < kQuantThreads / kWave; ++i) mx = __builtin_fmaxf(mx, red[i]);
+    const float r = mx > 0.0f ? 127.0f / mx : 0.0f;
+    const int64_t opad = count[1];
+    const int64_t o = count[0];
+    uint16_t* xo_row = xo + t * opad;
+#pragma unroll
+    for (int i = 0; i < kRowCache; ++i) {
+        const int c = tid + kQuantThreads * i;
+        if (c >= nch) continue;
+        const uint32_t word = fl[c >> 2];
+        const uint32_t fm = (word >> ((c & 3) * 8)) & 0xFFu;
+        const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+        uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float x = h16_to_f32<HT>((uint16_t)(w[e >> 1] >> ((e & 1) * 16)));
+            const uint32_t q = ((fm >> e) & 1u) ? 0u : (uint32_t)(uint8_t)quant(x, r);
+            packed[e >> 2] |= q << ((e & 3) * 8);
+        }
+        *reinterpret_cast<uint2*>(xq + t * K + (int64_t)c * 8) = make_uint2(packed[0], packed[1]);
+        if (fm) {
+            const int base_bit = (c & 3) * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if ((fm >> e) & 1u) {
+                    const int bit = base_bit + e;
+                    const int pos = wprefix[c >> 2] + __builtin_popcount(word & ((1u << bit) - 1u));
+                    xo_row[pos] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
+                }
+            }
+        }
+    }
+    for (int64_t j = o + tid; j < opad; j += kQuantThreads) xo_row[j] = 0;   // +0 in both types
+    if (tid == 0) sx[t] = mx;
+}
+
 }  // namespace
 
 template <int HT>
@@ -219,8 +299,15 @@ static void launch_activation_typed(const uint16_t* xb, int64_t T, int64_t K, fl
     hipLaunchKernelGGL(k_detect<HT>, dgrid, dim3(kDetectThreads), 0, stream, xb, T, K, tau, ws.flags);
     hipLaunchKernelGGL(k_compact, dim3(1), dim3(kCompactThreads), 0, stream, ws.flags, kw,
                        ws.wprefix, ws.idx, ws.count);
-    hipLaunchKernelGGL(k_rowquant<HT>, dim3((unsigned)T), dim3(kQuantThreads), 0, stream, xb, K,
-                       ws.flags, ws.wprefix, ws.count, ws.xq, ws.sx, ws.xo);
+    if (K <= (int64_t)kQuantThreads * 8 * 8)
+        hipLaunchKernelGGL((k_rowquant_cached<HT, 8>), dim3((unsigned)T), dim3(kQuantThreads), 0,
+                           stream, xb, K, ws.flags, ws.wprefix, ws.count, ws.xq, ws.sx, ws.xo);
+    else if (K <= (int64_t)kQuantThreads * 24 * 8)
+        hipLaunchKernelGGL((k_rowquant_cached<HT, 24>), dim3((unsigned)T), dim3(kQuantThreads), 0,
+                           stream, xb, K, ws.flags, ws.wprefix, ws.count, ws.xq, ws.sx, ws.xo);
+    else
+        hipLaunchKernelGGL(k_rowquant<HT>, dim3((unsigned)T), dim3(kQuantThreads), 0, stream, xb,
+                           K, ws.flags, ws.wprefix, ws.count, ws.xq, ws.sx, ws.xo);
 }
 
 hipError_t launch_activation_pass(const uint16_t* X, int ht, int64_t T, int64_t K, float tau,
