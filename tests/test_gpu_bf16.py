@@ -56,9 +56,10 @@ def check_y_bf16(y_bits, ref_bits, what):
     return err / max(scale, 1e-30), same
 
 
-def run_bf16(mm, name, X16, W16, tau, halved=False, big=None):
+def run_bf16(mm, name, X16, W16, tau, halved=False, big=None, rows=None):
     """X16, W16: seeded fp16 data, rounded to bf16 here; `big` plants one
-    activation value beyond the fp16 range (bf16 has fp32's exponent)."""
+    activation value beyond the fp16 range (bf16 has fp32's exponent);
+    `rows`: check acc and Y on these rows only (full-size workloads)."""
     Xb, Wb = to_bf16_bits(X16), to_bf16_bits(W16)
     if big is not None:
         Xb[big] = 0x47C3   # 99840.0, beyond fp16's 65504
@@ -73,16 +74,20 @@ def run_bf16(mm, name, X16, W16, tau, halved=False, big=None):
     Wq_o, sw_o = oracle.quantize_weight_typed(Wb, "bf16")
     assert np.array_equal(unblock_weight(Wq.cpu().numpy(), K, N), Wq_o), f"{name}: Wq"
     assert np.array_equal(sw.cpu().numpy(), sw_o), f"{name}: s_w"
-    ref = oracle.mixed_matmul(Xb, Wq_o, sw_o, None if halved else Wb, tau, htype="bf16")
+    sel = np.arange(T) if rows is None else np.asarray(rows)
+    ref = oracle.mixed_matmul(Xb, Wq_o, sw_o, None if halved else Wb, tau, htype="bf16",
+                              rows=None if rows is None else sel)
     o = int(r["count"][0])
     assert o == ref["o"] and np.array_equal(r["idx"][:o].cpu().numpy(), ref["idx"]), \
         f"{name}: outlier set"
-    assert np.array_equal(r["xq"].cpu().numpy(), ref["xq"]), f"{name}: Xq"
-    assert np.array_equal(r["sx"].cpu().numpy(), ref["sx"]), f"{name}: s_x"
-    assert np.array_equal(r["acc"].cpu().numpy(), ref["acc"]), f"{name}: acc"
-    ybits = r["Y"].view(torch.int16).cpu().numpy().view(np.uint16)
+    sel_t = torch.from_numpy(sel).cuda()
+    pick = lambda t: t.index_select(0, sel_t).cpu()
+    assert np.array_equal(pick(r["xq"]).numpy(), ref["xq"]), f"{name}: Xq"
+    assert np.array_equal(pick(r["sx"]).numpy(), ref["sx"]), f"{name}: s_x"
+    assert np.array_equal(pick(r["acc"]).numpy(), ref["acc"]), f"{name}: acc"
+    ybits = pick(r["Y"]).view(torch.int16).numpy().view(np.uint16)
     rel, same = check_y_bf16(ybits, ref["Y"], name)
-    check_y_bf16(Yp.view(torch.int16).cpu().numpy().view(np.uint16), ref["Y"], name + " (plain)")
+    check_y_bf16(pick(Yp).view(torch.int16).numpy().view(np.uint16), ref["Y"], name + " (plain)")
     say(f"[case] bf16 {name}: ok, o={o}, rel {rel:.2e}, identical {same:.4f}")
     return r, ref
 
@@ -107,3 +112,15 @@ def test_bf16_beyond_fp16_range(mm, T, K, N):
     X, W = synth.random_case(61_000 + T + K, T, K, N, n_dims=2)
     r, ref = run_bf16(mm, f"beyond fp16 {T}x{K}x{N}", X, W, 6.0, big=(T // 2, 33))
     assert 33 in ref["idx"].tolist()
+
+
+@pytest.mark.parametrize("name,halved", [("dec", False), ("dec", True), ("up", False)])
+def test_bf16_config(mm, name, halved):
+    """The decode and prefill up-projection workloads at full size in bf16
+    (acc and Y on sampled rows for the prefill one)."""
+    from tests.test_gpu_parity import _sample_rows
+    w = synth.WORKLOADS[name]
+    X, W = synth.make_x(w), synth.make_w(w)
+    rows = None if w.T <= 16 else _sample_rows(w.T, synth.planted(w)[2], n=6)
+    r, ref = run_bf16(mm, f"{name} (full size)", X, W, w.tau, halved=halved, rows=rows)
+    assert set(synth.planted(w)[0].tolist()) <= set(ref["idx"].tolist())

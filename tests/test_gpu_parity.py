@@ -236,3 +236,25 @@ def test_sweep_config(mm, name):
     X, W = synth.make_x(w), synth.make_w(w)
     r, _ = run_case(mm, f"{name} (sampled rows)", X, W, w.tau, rows=_sample_rows(w.T, None, n=8))
     assert int(r["count"][0]) >= w.n_dims
+
+
+@pytest.mark.parametrize("name", ["dec", "up"])
+def test_memory_halved_config(mm, name):
+    """The memory-halved variant (no 16-bit weight) on the decode and prefill
+    up-projection workloads at full size (acc and Y on sampled rows for the
+    prefill one)."""
+    w = synth.WORKLOADS[name]
+    X, W = synth.make_x(w), synth.make_w(w)
+    dims, _, rowsel = synth.planted(w)
+    rows = None if w.T <= 16 else _sample_rows(w.T, rowsel, n=6)
+    r, _ = run_case(mm, f"{name} memory-halved", X, W, w.tau, rows=rows, halved=True)
+    assert set(dims.tolist()) <= set(r["idx"][:int(r["count"][0])].cpu().tolist())
+
+
+@pytest.mark.parametrize("name", ["sweep_up_64", "sweep_down_8"])
+def test_sweep_config_more(mm, name):
+    """Two more projections of the 175B-class block sweep (T = 4096)."""
+    w = synth.WORKLOADS[name]
+    X, W = synth.make_x(w), synth.make_w(w)
+    r, _ = run_case(mm, f"{name} (sampled rows)", X, W, w.tau, rows=_sample_rows(w.T, None, n=6))
+    assert int(r["count"][0]) >= w.n_dims
