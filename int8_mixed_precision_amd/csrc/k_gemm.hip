@@ -56,7 +56,7 @@ __device__ inline int swz(int row, int c) {
 // What the large-tile kernel hands its epilogue for staging the outlier
 // operands through LDS (the other kernels pass an empty one).
 struct StageCtx {
-    int8_t* lds;      // at least kStageBytes, free once the main loop is done
+    int8_t* lds;      // at least kStageBytes and kYBytes, free once the main loop is done
     int tid;          // 0 .. 511
     int64_t m0, n0;   // the workgroup's 256 x 256 output tile
 };
@@ -64,6 +64,8 @@ constexpr int kOC = 32;                       // outliers per staged chunk
 constexpr int kOS = kOC * 2 + 16;             // bytes per staged row / column (padded)
 constexpr int kStageHalf = 256 * kOS;         // X part (rows) or W part (columns)
 constexpr int kStageBytes = 4 * kStageHalf;   // two buffers of X and W
+constexpr int kYS = 256 * 2 + 16;             // bytes per row of the staged Y tile (padded)
+constexpr int kYBytes = 256 * kYS;            // the 256 x 256 tile of 16-bit Y values
 
 template <int TM, int TN, bool WRITE_ACC, int HT, bool STAGED = false>
 __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a, int64_t mb,
@@ -114,11 +116,20 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a,
     int mrow0 = (int)mb + row_l;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
+        // registers r = 4g .. 4g+3 hold four consecutive rows starting at a
+        // multiple of 4 (sx is 256-byte aligned): one 16-byte load when all
+        // four are below T
         float sxm[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int m = mrow0 + i * 32 + (r >> 2) * 8 + (r & 3);
-            sxm[r] = a.sx[m < Ti ? m : Ti - 1];
+        for (int g = 0; g < 4; ++g) {
+            const int m = mrow0 + i * 32 + g * 8;
+            if (m + 3 < Ti) {
+                const float4 v = *reinterpret_cast<const float4*>(a.sx + m);
+                sxm[4 * g] = v.x; sxm[4 * g + 1] = v.y; sxm[4 * g + 2] = v.z; sxm[4 * g + 3] = v.w;
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) sxm[4 * g + q] = a.sx[m + q < Ti ? m + q : Ti - 1];
+            }
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j)
@@ -272,6 +283,37 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a,
                 }
             }
         }
+    }
+    if constexpr (STAGED) {
+        // Y through LDS: every wave writes its 16-bit values into a row-major
+        // 256 x 256 tile, then the workgroup stores whole 16-byte pieces of
+        // rows (1 KB per wave instruction) instead of 2-byte scattered
+        // stores.  Rows are padded by 16 bytes, so the two row groups of a
+        // lane write (rows 4 apart) fall on different banks.
+        __syncthreads();   // every LDS read of the main loop and the outlier stage is done
+        const int wm0 = (int)(mb - sc.m0), wn0 = (int)(nb - sc.n0);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int ml = wm0 + i * 32 + (r >> 2) * 8 + row_l + (r & 3);
+                    const int nl = wn0 + j * 32 + col_l;
+                    *reinterpret_cast<uint16_t*>(sc.lds + ml * kYS + nl * 2) =
+                        f32_to_h16<HT>(y[i][j][r]);
+                }
+        __syncthreads();
+        const int c = sc.tid & 31;
+        const int64_t n = sc.n0 + c * 8;   // N % 8 == 0: a piece is all in or all out
+#pragma unroll
+        for (int p = 0; p < 16; ++p) {
+            const int row = (sc.tid >> 5) + 16 * p;
+            const int64_t m = sc.m0 + row;
+            const uint4 v = *reinterpret_cast<const uint4*>(sc.lds + row * kYS + c * 16);
+            if (m < T && n < N) *reinterpret_cast<uint4*>(a.y + m * N + n) = v;
+        }
+        return;
     }
     // the row indices are recomputed here rather than kept live through the
     // outlier loop (an empty asm hides the earlier values from the compiler)
@@ -456,7 +498,10 @@ __global__ __launch_bounds__(128 * WN) void k_gemm_i8_big(GemmArgs a) {
     constexpr int GPW = 16 / WAVES;                  // 1 KB groups of A (and of B) per wave
     constexpr int LOADS = 2 * GPW;                   // copies per lane per tile
     static_assert(NF <= NM && LOADS <= NM, "interleave needs one MFMA per read and copy");
-    __shared__ __attribute__((aligned(1024))) int8_t lds[STAGES * STAGE_BYTES];
+    // the operand ring, reused after the main loop by the epilogue (outlier
+    // stage, then the Y tile)
+    constexpr int LDS_BYTES = STAGES * STAGE_BYTES > kYBytes ? STAGES * STAGE_BYTES : kYBytes;
+    __shared__ __attribute__((aligned(1024))) int8_t lds[LDS_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -569,7 +614,8 @@ __global__ __launch_bounds__(128 * WN) void k_gemm_i8_big(GemmArgs a) {
     // no LDS copy may still be in flight when the LDS is reused or the
     // workgroup retires
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    static_assert(THREADS == 512 && STAGES * STAGE_BYTES >= kStageBytes, "staged epilogue");
+    static_assert(THREADS == 512 && BM == 256 && BN == 256 && LDS_BYTES >= kStageBytes,
+                  "staged epilogue: 512 threads, 256 x 256 tile");
     epilogue<TM, TN, WRITE_ACC, HT, true>(acc, a, m0 + wm0, n0 + wn0, lane,
                                           StageCtx{lds, tid, m0, n0});
 }
