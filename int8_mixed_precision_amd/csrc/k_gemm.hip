@@ -56,9 +56,13 @@ __device__ inline int swz(int row, int c) {
 // What the large-tile kernel hands its epilogue for staging the outlier
 // operands through LDS (the other kernels pass an empty one).
 struct StageCtx {
-    int8_t* lds;      // at least kStageBytes and kYBytes, free once the main loop is done
-    int tid;          // 0 .. 511
-    int64_t m0, n0;   // the workgroup's 256 x 256 output tile
+    int8_t* lds;         // at least kStageBytes and kYBytes, free once the main loop is done
+    int tid;             // 0 .. 511
+    int64_t m0, n0;      // the workgroup's 256 x 256 output tile
+    float* sxs;          // 256 floats of LDS outside the above for the tile's row scales
+    float sx_pre;        // s_x of tile row tid (tid < 256; the last row past T)
+    const float* sw_pre; // s_w of the lane's TN columns (0 past N)
+    int o, opad;         // outlier count and its padded value
 };
 constexpr int kOC = 32;                       // outliers per staged chunk
 constexpr int kOS = kOC * 2 + 16;             // bytes per staged row / column (padded)
@@ -88,11 +92,14 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a,
     }
     // dequantization by the outer product of the scales (1/127^2 folded
     // into the column scale)
+    // (the large-tile kernel read s_w, s_x and the counts before its main
+    // loop, so their latency is hidden; s_x reaches every lane through LDS)
     float swn[TN];
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
         const int64_t n = nb + j * 32 + col_l;
-        swn[j] = n < N ? a.sw[n] * (1.0f / 16129.0f) : 0.0f;
+        if constexpr (STAGED) swn[j] = sc.sw_pre[j] * (1.0f / 16129.0f);
+        else swn[j] = n < N ? a.sw[n] * (1.0f / 16129.0f) : 0.0f;
     }
     // memory-halved variant (no W16): the outlier rows are recovered from the
     // Int8 weight, W^[k,n] = fp16(q[n,k] * fp32(s_w[n] / 127))
@@ -101,10 +108,15 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a,
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
         const int64_t n = nb + j * 32 + col_l;
-        dn[j] = recover && n < N ? a.sw[n] / 127.0f : 0.0f;
+        if constexpr (STAGED) dn[j] = recover ? sc.sw_pre[j] / 127.0f : 0.0f;
+        else dn[j] = recover && n < N ? a.sw[n] / 127.0f : 0.0f;
     }
-    const int o = a.count[0];
-    const int opad = a.count[1];
+    const int o = STAGED ? sc.o : a.count[0];
+    const int opad = STAGED ? sc.opad : a.count[1];
+    if constexpr (STAGED) {
+        if (sc.tid < 256) sc.sxs[sc.tid] = sc.sx_pre;
+        __syncthreads();
+    }
     // dequantize every tile (the integer accumulators die here, so the fp32
     // values take their registers; keeping the fp32 values in the integer
     // array through bit casts instead was compiled wrongly - the four rows of
@@ -123,7 +135,10 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a,
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int m = mrow0 + i * 32 + g * 8;
-            if (m + 3 < Ti) {
+            if (STAGED) {
+                const float4 v = *reinterpret_cast<const float4*>(sc.sxs + (m - (int)sc.m0));
+                sxm[4 * g] = v.x; sxm[4 * g + 1] = v.y; sxm[4 * g + 2] = v.z; sxm[4 * g + 3] = v.w;
+            } else if (m + 3 < Ti) {
                 const float4 v = *reinterpret_cast<const float4*>(a.sx + m);
                 sxm[4 * g] = v.x; sxm[4 * g + 1] = v.y; sxm[4 * g + 2] = v.z; sxm[4 * g + 3] = v.w;
             } else {
@@ -502,6 +517,7 @@ __global__ __launch_bounds__(128 * WN) void k_gemm_i8_big(GemmArgs a) {
     // stage, then the Y tile)
     constexpr int LDS_BYTES = STAGES * STAGE_BYTES > kYBytes ? STAGES * STAGE_BYTES : kYBytes;
     __shared__ __attribute__((aligned(1024))) int8_t lds[LDS_BYTES];
+    __shared__ __attribute__((aligned(16))) float sxs[BM];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -513,6 +529,15 @@ __global__ __launch_bounds__(128 * WN) void k_gemm_i8_big(GemmArgs a) {
     const int64_t n0 = (bid / MT) * BN;
     const int wm0 = (wave & 1) * 128;
     const int wn0 = (wave >> 1) * (BN / WN);
+    // what the epilogue needs, read now (the main loop hides the latency)
+    const float sx_pre = a.sx[m0 + (tid & (BM - 1)) < T ? m0 + (tid & (BM - 1)) : T - 1];
+    float sw_pre[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int64_t n = n0 + wn0 + j * 32 + (lane & 31);
+        sw_pre[j] = n < N ? a.sw[n] : 0.0f;
+    }
+    const int o_pre = a.count[0], opad_pre = a.count[1];
 
     // copy assignment: wave w fills the 1 KB groups GPW*w .. GPW*w+GPW-1 of A
     // and of B; in a group, lane l writes row 16g + l/4, physical chunk l%4.
@@ -616,8 +641,9 @@ __global__ __launch_bounds__(128 * WN) void k_gemm_i8_big(GemmArgs a) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     static_assert(THREADS == 512 && BM == 256 && BN == 256 && LDS_BYTES >= kStageBytes,
                   "staged epilogue: 512 threads, 256 x 256 tile");
-    epilogue<TM, TN, WRITE_ACC, HT, true>(acc, a, m0 + wm0, n0 + wn0, lane,
-                                          StageCtx{lds, tid, m0, n0});
+    epilogue<TM, TN, WRITE_ACC, HT, true>(
+        acc, a, m0 + wm0, n0 + wn0, lane,
+        StageCtx{lds, tid, m0, n0, sxs, sx_pre, sw_pre, o_pre, opad_pre});
 }
 
 template <int BM, int BN, int BK, int WAVES_M, int HT>
