@@ -135,15 +135,17 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a,
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int m = mrow0 + i * 32 + g * 8;
-            if (STAGED) {
+            if constexpr (STAGED) {
                 const float4 v = *reinterpret_cast<const float4*>(sc.sxs + (m - (int)sc.m0));
                 sxm[4 * g] = v.x; sxm[4 * g + 1] = v.y; sxm[4 * g + 2] = v.z; sxm[4 * g + 3] = v.w;
-            } else if (m + 3 < Ti) {
-                const float4 v = *reinterpret_cast<const float4*>(a.sx + m);
-                sxm[4 * g] = v.x; sxm[4 * g + 1] = v.y; sxm[4 * g + 2] = v.z; sxm[4 * g + 3] = v.w;
             } else {
+                if (m + 3 < Ti) {
+                    const float4 v = *reinterpret_cast<const float4*>(a.sx + m);
+                    sxm[4 * g] = v.x; sxm[4 * g + 1] = v.y; sxm[4 * g + 2] = v.z; sxm[4 * g + 3] = v.w;
+                } else {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) sxm[4 * g + q] = a.sx[m + q < Ti ? m + q : Ti - 1];
+                    for (int q = 0; q < 4; ++q) sxm[4 * g + q] = a.sx[m + q < Ti ? m + q : Ti - 1];
+                }
             }
         }
 #pragma unroll
