@@ -44,6 +44,10 @@ __device__ __forceinline__ uint16_t f32_to_h16(float f) {
 //   sx      f32 [T]      row scales
 //   xq      i8  [T,K]    quantized activations, outlier columns 0
 //   xo      16-bit [T,opad] outlier columns of X, row stride count[1], zero padded
+// and, only when the matmul splits K in two (gemm_ksplit), after all of the above:
+//   ks_count i32 [tiles]            per output tile, halves finished (zeroed by the
+//                                   matmul's launch)
+//   ks_part  i32 [tiles][2][65536]  each half's int32 sums of its 256 x 256 tile
 struct Workspace {
     uint32_t* flags;
     int32_t* wprefix;
@@ -52,7 +56,9 @@ struct Workspace {
     float* sx;
     int8_t* xq;
     uint16_t* xo;
-    size_t bytes;   // total bytes the layout needs
+    int32_t* ks_count;   // NULL without the K split
+    int32_t* ks_part;
+    size_t bytes;        // total bytes the layout needs
 };
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -73,8 +79,16 @@ __device__ __forceinline__ uint16_t recover_weight(int8_t q, float d) {
 // Bytes of the converted weight: int8 [N,K] row-major (K contiguous).
 inline int64_t wq_bytes(int64_t K, int64_t N) { return K * N; }
 
-// Layout of the workspace for (T, K) at `base` (base may be NULL to size it).
-Workspace carve_workspace(void* base, int64_t T, int64_t K);
+// Compute units of the current device (256 if it cannot be queried).
+int device_cus();
+
+// 2 when the large-tile matmul of (T, K, N) runs each 256 x 256 output tile
+// as two halves of K on the current device, else 1.
+int gemm_ksplit(int64_t T, int64_t K, int64_t N);
+
+// Layout of the workspace for (T, K, N) at `base` (base may be NULL to size
+// it); ksplit = 2 adds the regions of the K split.
+Workspace carve_workspace(void* base, int64_t T, int64_t K, int64_t N, int ksplit);
 
 // ---- activation side (k_activation.hip)
 hipError_t launch_activation_pass(const uint16_t* X, int ht, int64_t T, int64_t K, float tau,
@@ -99,6 +113,9 @@ struct GemmArgs {
     uint16_t* y;           // [T,N] 16-bit
     int32_t* acc_out;      // [T,N] or NULL
     int64_t T, K, N;
+    int ksplit;            // 1, or 2: K split in two halves (large-tile kernel only)
+    int32_t* ks_count;     // [tiles] (ksplit = 2; zeroed by launch_gemm)
+    int32_t* ks_part;      // [tiles][2][65536] (ksplit = 2)
 };
 hipError_t launch_gemm(const GemmArgs& a, int ht, hipStream_t stream);
 

@@ -29,6 +29,16 @@ int check_tau(float tau) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? INT8MM_OK : INT8MM_E_HIP; }
 
+// The K split of the matmul (gemm_ksplit) when the workspace is large enough
+// for its regions, else none.  The size query reserves them whenever the
+// split applies, and every entry point decides the same way from the same
+// (T, K, N, workspace_bytes), so the activation pass and the matmul of one
+// workspace always agree on its layout.
+int ksplit_for(int64_t T, int64_t K, int64_t N, size_t workspace_bytes) {
+    if (gemm_ksplit(T, K, N) != 2) return 1;
+    return workspace_bytes >= carve_workspace(nullptr, T, K, N, 2).bytes ? 2 : 1;
+}
+
 // Validation shared by int8_mixed_matmul and its debug variant.
 int check_matmul(const void* X, int64_t T, int64_t K, const int8_t* Wq, const float* sw,
                  const void* W16, int64_t N, float tau, void* Y, void* workspace,
@@ -41,25 +51,27 @@ int check_matmul(const void* X, int64_t T, int64_t K, const int8_t* Wq, const fl
     if (!aligned16(X) || !aligned16(Wq) || !aligned16(sw) || !aligned16(Y) ||
         !aligned16(workspace) || (W16 && !aligned16(W16)))
         return INT8MM_E_ALIGN;
-    if (workspace_bytes < carve_workspace(nullptr, T, K).bytes) return INT8MM_E_WORKSPACE;
+    if (workspace_bytes < carve_workspace(nullptr, T, K, N, 1).bytes) return INT8MM_E_WORKSPACE;
     return INT8MM_OK;
 }
 
 // ht: 16-bit type of X, W16 and Y (kHalfF16, or kHalfBF16 for the bf16 variant)
 int run_matmul(const void* X, int ht, int64_t T, int64_t K, const int8_t* Wq, const float* sw,
                const void* W16, int64_t N, float tau, void* Y, void* workspace,
-               hipStream_t stream, int32_t* count, int32_t* idx, int8_t* xq, float* sx,
-               int32_t* acc) {
+               size_t workspace_bytes, hipStream_t stream, int32_t* count, int32_t* idx,
+               int8_t* xq, float* sx, int32_t* acc) {
     const uint16_t* x16 = static_cast<const uint16_t*>(X);
     const uint16_t* w16 = static_cast<const uint16_t*>(W16);
     uint16_t* y16 = static_cast<uint16_t*>(Y);
     if (decode_path_supported(T, K, N))
         return hip_status(launch_decode(x16, ht, T, K, Wq, sw, w16, N, tau, y16, count, idx, xq,
                                         sx, acc, stream));
-    Workspace ws = carve_workspace(workspace, T, K);
+    const int ks = ksplit_for(T, K, N, workspace_bytes);
+    Workspace ws = carve_workspace(workspace, T, K, N, ks);
     hipError_t e = launch_activation_pass(x16, ht, T, K, tau, ws, stream);
     if (e != hipSuccess) return INT8MM_E_HIP;
-    GemmArgs g{ws.xq, ws.sx, Wq, sw, ws.xo, ws.idx, ws.count, w16, y16, acc, T, K, N};
+    GemmArgs g{ws.xq, ws.sx, Wq, sw, ws.xo, ws.idx, ws.count, w16, y16, acc, T, K, N,
+               ks, ws.ks_count, ws.ks_part};
     e = launch_gemm(g, ht, stream);
     if (e != hipSuccess) return INT8MM_E_HIP;
     return hip_status(launch_debug_copies(ws, T, K, count, idx, xq, sx, stream));
@@ -87,7 +99,7 @@ int int8_mixed_matmul_workspace_size(int64_t T, int64_t K, int64_t N, size_t* by
     if (!bytes) return INT8MM_E_NULL;
     int st = check_shape(T, K, N);
     if (st) return st;
-    *bytes = carve_workspace(nullptr, T, K).bytes;
+    *bytes = carve_workspace(nullptr, T, K, N, gemm_ksplit(T, K, N)).bytes;
     return INT8MM_OK;
 }
 
@@ -126,7 +138,7 @@ int int8_mixed_matmul(const void* X, int64_t T, int64_t K, const int8_t* Wq, con
                       size_t workspace_bytes, void* stream) {
     int st = check_matmul(X, T, K, Wq, sw, W16, N, tau, Y, workspace, workspace_bytes);
     if (st) return st;
-    return run_matmul(X, kHalfF16, T, K, Wq, sw, W16, N, tau, Y, workspace,
+    return run_matmul(X, kHalfF16, T, K, Wq, sw, W16, N, tau, Y, workspace, workspace_bytes,
                       static_cast<hipStream_t>(stream), nullptr, nullptr, nullptr, nullptr,
                       nullptr);
 }
@@ -136,7 +148,7 @@ int int8_mixed_matmul_bf16(const void* X, int64_t T, int64_t K, const int8_t* Wq
                            void* workspace, size_t workspace_bytes, void* stream) {
     int st = check_matmul(X, T, K, Wq, sw, W16, N, tau, Y, workspace, workspace_bytes);
     if (st) return st;
-    return run_matmul(X, kHalfBF16, T, K, Wq, sw, W16, N, tau, Y, workspace,
+    return run_matmul(X, kHalfBF16, T, K, Wq, sw, W16, N, tau, Y, workspace, workspace_bytes,
                       static_cast<hipStream_t>(stream), nullptr, nullptr, nullptr, nullptr,
                       nullptr);
 }
@@ -150,7 +162,7 @@ static int matmul_debug(int ht, const void* X, int64_t T, int64_t K, const int8_
     if ((count && !aligned16(count)) || (idx && !aligned16(idx)) || (xq && !aligned16(xq)) ||
         (sx && !aligned16(sx)) || (acc && !aligned16(acc)))
         return INT8MM_E_ALIGN;
-    return run_matmul(X, ht, T, K, Wq, sw, W16, N, tau, Y, workspace,
+    return run_matmul(X, ht, T, K, Wq, sw, W16, N, tau, Y, workspace, workspace_bytes,
                       static_cast<hipStream_t>(stream), count, idx, xq, sx, acc);
 }
 
@@ -179,8 +191,8 @@ int int8mm_quantize_activations(const void* X, int64_t T, int64_t K, int64_t N, 
     st = check_tau(tau);
     if (st) return st;
     if (!aligned16(X) || !aligned16(workspace)) return INT8MM_E_ALIGN;
-    Workspace ws = carve_workspace(workspace, T, K);
-    if (workspace_bytes < ws.bytes) return INT8MM_E_WORKSPACE;
+    if (workspace_bytes < carve_workspace(nullptr, T, K, N, 1).bytes) return INT8MM_E_WORKSPACE;
+    Workspace ws = carve_workspace(workspace, T, K, N, ksplit_for(T, K, N, workspace_bytes));
     return hip_status(launch_activation_pass(static_cast<const uint16_t*>(X), kHalfF16, T, K, tau, ws,
                                              static_cast<hipStream_t>(stream)));
 }
@@ -194,10 +206,12 @@ int int8mm_matmul_prepared(const void* workspace, size_t workspace_bytes, int64_
     if (!aligned16(workspace) || !aligned16(Wq) || !aligned16(sw) || !aligned16(Y) ||
         (W16 && !aligned16(W16)))
         return INT8MM_E_ALIGN;
-    Workspace ws = carve_workspace(const_cast<void*>(workspace), T, K);
-    if (workspace_bytes < ws.bytes) return INT8MM_E_WORKSPACE;
+    if (workspace_bytes < carve_workspace(nullptr, T, K, N, 1).bytes) return INT8MM_E_WORKSPACE;
+    const int ks = ksplit_for(T, K, N, workspace_bytes);
+    Workspace ws = carve_workspace(const_cast<void*>(workspace), T, K, N, ks);
     GemmArgs g{ws.xq, ws.sx, Wq, sw, ws.xo, ws.idx, ws.count,
-               static_cast<const uint16_t*>(W16), static_cast<uint16_t*>(Y), nullptr, T, K, N};
+               static_cast<const uint16_t*>(W16), static_cast<uint16_t*>(Y), nullptr, T, K, N,
+               ks, ws.ks_count, ws.ks_part};
     return hip_status(launch_gemm(g, kHalfF16, static_cast<hipStream_t>(stream)));
 }
 

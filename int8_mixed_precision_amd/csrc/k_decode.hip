@@ -524,7 +524,7 @@ bool decode_path_supported(int64_t T, int64_t K, int64_t N) {
 
 // Compute units of the current device, cached per device (an immutable
 // property; concurrent first calls store the same value).
-static int device_cus() {
+int device_cus() {
     static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;

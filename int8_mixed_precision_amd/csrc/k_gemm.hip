@@ -520,13 +520,20 @@ __global__ __launch_bounds__(128 * WN) void k_gemm_i8_big(GemmArgs a) {
     constexpr int LDS_BYTES = STAGES * STAGE_BYTES > kYBytes ? STAGES * STAGE_BYTES : kYBytes;
     __shared__ __attribute__((aligned(1024))) int8_t lds[LDS_BYTES];
     __shared__ __attribute__((aligned(16))) float sxs[BM];
+    __shared__ int ks_first;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t T = a.T, K = a.K, N = a.N;
     const int64_t MT = ceil_div(T, BM);
-    const int64_t bid = xcd_tile(blockIdx.x, gridDim.x);
+    // With the K split (S = 2) the grid holds every tile's first half, then
+    // every tile's second half: a unit never waits for another.
+    const int S = a.ksplit;
+    const int64_t tiles = (int64_t)gridDim.x / S;
+    const int half = (int)(blockIdx.x / tiles);
+    const int64_t tix = (int64_t)blockIdx.x - half * tiles;
+    const int64_t bid = xcd_tile(tix, tiles);
     const int64_t m0 = (bid % MT) * BM;
     const int64_t n0 = (bid / MT) * BN;
     const int wm0 = (wave & 1) * 128;
@@ -600,18 +607,20 @@ __global__ __launch_bounds__(128 * WN) void k_gemm_i8_big(GemmArgs a) {
     // Prologue: tiles 0..3 in flight, wait for tile 0, first F0.  Past the
     // last tile, copies re-fetch tile KT-1 into a buffer that is never read
     // again, which keeps the loop free of branches and the wait count fixed.
-    const int KT = (int)(K / BK);
+    // this unit's k-tiles KT0 .. KT-1 (K / BK is even when S = 2)
+    const int KT0 = half * (int)(K / BK / S);
+    const int KT = KT0 + (int)(K / BK / S);
 #pragma unroll
     for (int st = 0; st < STAGES; ++st)
 #pragma unroll
-        for (int u = 0; u < LOADS; ++u) copy(u, st < KT ? st : KT - 1, st);
+        for (int u = 0; u < LOADS; ++u) copy(u, KT0 + st < KT ? KT0 + st : KT - 1, st);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS * (STAGES - 1)));
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < NF; ++q) f0[q] = *reinterpret_cast<const v4i*>(lds + foff[0][q]);
 
     int s_cur = 0;
-    for (int kt = 0; kt < KT; ++kt) {
+    for (int kt = KT0; kt < KT; ++kt) {
         const int s_next = (s_cur + 1) & (STAGES - 1);
         const int8_t* cur = lds + s_cur * STAGE_BYTES;
         const int8_t* nxt = lds + s_next * STAGE_BYTES;
@@ -641,6 +650,57 @@ __global__ __launch_bounds__(128 * WN) void k_gemm_i8_big(GemmArgs a) {
     // no LDS copy may still be in flight when the LDS is reused or the
     // workgroup retires
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    if (S > 1) {
+        // K split: each half publishes its int32 sums, and the half that
+        // finishes second adds the other's (exact, order independent) and
+        // runs the epilogue.  The tile counters were zeroed at launch.
+        // The sums travel through device-coherent accesses (agent-scope
+        // atomic loads and stores: the other half may run on another XCD,
+        // whose L2 is not this one's), so no cache flush or invalidate is
+        // needed: a half's stores are complete (vmcnt 0) before its counter
+        // increment, and the second half reads only after its increment has
+        // returned the first's.  A half that finds the other one already
+        // done skips publishing its own sums.
+        uint64_t* mine = reinterpret_cast<uint64_t*>(a.ks_part) +
+                         ((tix * 2 + half) * WAVES + wave) * (TM * TN * 8 * 64);
+        const uint64_t* other = reinterpret_cast<const uint64_t*>(a.ks_part) +
+                                ((tix * 2 + (1 - half)) * WAVES + wave) * (TM * TN * 8 * 64);
+        if (tid == 0)
+            ks_first = __hip_atomic_load(&a.ks_count[tix], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const bool other_done = ks_first != 0;
+        if (!other_done) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const uint64_t v = (uint64_t)(uint32_t)acc[i][j][2 * q] |
+                                           ((uint64_t)(uint32_t)acc[i][j][2 * q + 1] << 32);
+                        __hip_atomic_store(mine + ((i * TN + j) * 8 + q) * 64 + lane, v,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        }
+        __syncthreads();   // every wave's sums are out (and ks_first is read)
+        if (tid == 0)
+            ks_first = __hip_atomic_fetch_add(&a.ks_count[tix], 1, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT) == 0;
+        __syncthreads();
+        if (ks_first) return;   // the other half finishes the tile
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const uint64_t v = __hip_atomic_load(other + ((i * TN + j) * 8 + q) * 64 + lane,
+                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    acc[i][j][2 * q] += (int32_t)(uint32_t)v;
+                    acc[i][j][2 * q + 1] += (int32_t)(uint32_t)(v >> 32);
+                }
+    }
     static_assert(THREADS == 512 && BM == 256 && BN == 256 && LDS_BYTES >= kStageBytes,
                   "staged epilogue: 512 threads, 256 x 256 tile");
     epilogue<TM, TN, WRITE_ACC, HT, true>(
@@ -660,9 +720,22 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+__global__ void k_zero_i32(int32_t* __restrict__ p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
+
 template <int WN, int HT>
 hipError_t launch_big(const GemmArgs& a, hipStream_t stream) {
-    const int64_t tiles = ceil_div(a.T, 256) * ceil_div(a.N, 256);
+    if (a.ksplit == 2) {
+        // the tile counters start at zero (a kernel rather than a memset, so
+        // the call can be captured in a graph); a split matmul is long enough
+        // that one more launch does not show
+        const int64_t n = ceil_div(a.T, 256) * ceil_div(a.N, 256);
+        hipLaunchKernelGGL(k_zero_i32, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, stream,
+                           a.ks_count, n);
+    }
+    const int64_t tiles = ceil_div(a.T, 256) * ceil_div(a.N, 256) * a.ksplit;
     if (a.acc_out)
         hipLaunchKernelGGL((k_gemm_i8_big<WN, true, HT>), dim3((unsigned)tiles), dim3(128 * WN), 0,
                            stream, a);
@@ -681,7 +754,25 @@ hipError_t launch_gemm_typed(const GemmArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+// The large-tile kernel runs one workgroup per CU at a time, so a grid of
+// `tiles` takes ceil(tiles / CUs) rounds.  Splitting K in two doubles the
+// units and halves their length; it pays where that removes at least a
+// quarter of the rounds (e.g. 384 tiles on 256 CUs: 2 rounds -> 1.5) and K
+// is long enough that publishing and adding the 256 KB of partial sums per
+// tile is small against the half tile (measured: down projection T=2048,
+// K=49152, N=12288 13% faster; at K=12288 the split was slower).
+int gemm_ksplit(int64_t T, int64_t K, int64_t N) {
+    if (!(T > 128 && K % 128 == 0 && K >= 24576)) return 1;
+    const int64_t tiles = ceil_div(T, 256) * ceil_div(N, 256);
+    const int64_t cus = device_cus();
+    const int64_t r1 = ceil_div(tiles, cus);          // rounds of whole tiles
+    const int64_t r2 = ceil_div(2 * tiles, cus);      // rounds of half tiles
+    return 2 * r2 <= 3 * r1 ? 2 : 1;                  // half-rounds r2/2 <= 3/4 of r1
+}
+
 hipError_t launch_gemm(const GemmArgs& a, int ht, hipStream_t stream) {
+    if (a.ksplit != 1 && !(a.ksplit == 2 && a.ks_count && a.ks_part && a.T > 128 && a.K % 128 == 0))
+        return hipErrorInvalidValue;
     return ht == kHalfBF16 ? launch_gemm_typed<kHalfBF16>(a, stream)
                            : launch_gemm_typed<kHalfF16>(a, stream);
 }

@@ -99,6 +99,7 @@ def run_bf16(mm, name, X16, W16, tau, halved=False, big=None, rows=None):
     (16, 4096, 520, 5, 6.0, True), (8, 8192, 2056, 6, 6.0, True),
     (70, 1024, 136, 0, 0.0, False), (2, 4096, 136, 0, 0.0, False),       # tau = 0
     (65, 320, 96, 4, float("inf"), False),                               # tau = inf
+    (300, 24576, 520, 3, 6.0, True),                                     # K split in two
 ])
 def test_bf16_path(mm, T, K, N, nd, tau, halved):
     X, W = synth.random_case(60_000 + T + K + N + nd, T, K, N, n_dims=nd)

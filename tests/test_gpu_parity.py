@@ -111,6 +111,9 @@ def test_tiny_config(mm):
     # k-tiles, ragged T and N against the 256x256 tile, many outliers
     (129, 64, 8, 1, "normal"), (513, 128, 264, 2, "normal"), (300, 1024, 520, 3, "laplace"),
     (257, 2048, 1000, 70, "normal"),
+    # K split in two halves (K >= 24576 and few tiles): ragged T and N, and
+    # 200 outliers through the second half's epilogue
+    (300, 24576, 520, 3, "normal"), (129, 24576, 264, 200, "laplace"),
 ])
 def test_ragged_shapes(mm, T, K, N, nd, dist):
     X, W = synth.random_case(10_000 + T + K + N, T, K, N, n_dims=nd, x_dist=dist)
@@ -132,7 +135,7 @@ def test_decode_path(mm, T, K, N, nd, tau):
     (37, 80, 200, 2, 6.0), (300, 1040, 520, 3, 6.0),          # staged kernels
     (257, 2048, 1000, 70, 6.0), (129, 64, 8, 1, 6.0),          # large-tile kernel
     (1, 4096, 1000, 3, 6.0), (8, 8192, 264, 300, 6.0),         # decode kernel, o > 16
-    (16, 4096, 520, 20, 6.0),
+    (16, 4096, 520, 20, 6.0), (300, 24576, 520, 3, 6.0),      # K split in two
     (70, 1024, 136, 0, 0.0), (2, 4096, 136, 0, 0.0),           # every dimension an outlier
 ])
 def test_memory_halved(mm, T, K, N, nd, tau):
@@ -182,21 +185,24 @@ def test_largest_k(mm):
     assert acc[0, 0] == 127 * 127 * K and acc[1, 0] == -127 * 127 * K
 
 
-def test_staged_entry_points_match(mm):
-    X, W = synth.random_case(24, 96, 512, 264, n_dims=3)
-    W2 = synth.random_case(25, 1, 512, 136)[1]
-    say("[case] staged entry points")
+@pytest.mark.parametrize("T,K,N1,N2", [(96, 512, 264, 136), (300, 24576, 520, 264)])
+def test_staged_entry_points_match(mm, T, K, N1, N2):
+    # the second shape runs the matmul with K split in two halves
+    X, W = synth.random_case(24, T, K, N1, n_dims=3)
+    W2 = synth.random_case(25, 1, K, N2)[1]
+    say(f"[case] staged entry points T={T} K={K} N={N1},{N2}")
     Xd, Wd, W2d = gpu(X), gpu(W), gpu(W2)
     Wq, sw = mm.quantize_weight(Wd)
     Wq2, sw2 = mm.quantize_weight(W2d)
-    ws = mm.new_workspace(96, 512, 264)
-    mm.quantize_activations(Xd, 264, 6.0, ws)
-    Y1 = mm.matmul_prepared(ws, 96, 512, Wq, sw, Wd)
-    Y2 = mm.matmul_prepared(ws, 96, 512, Wq2, sw2, W2d)   # one pass of X, two weights
+    ws = mm.new_workspace(T, K, N1)
+    mm.quantize_activations(Xd, N1, 6.0, ws)
+    Y1 = mm.matmul_prepared(ws, T, K, Wq, sw, Wd)
+    Y2 = mm.matmul_prepared(ws, T, K, Wq2, sw2, W2d)   # one pass of X, two weights
+    Y1b = mm.matmul_prepared(ws, T, K, Wq, sw, Wd)     # and the first again
     R1 = mm.mixed_matmul(Xd, Wq, sw, Wd, 6.0)
     R2 = mm.mixed_matmul(Xd, Wq2, sw2, W2d, 6.0)
     torch.cuda.synchronize()
-    assert torch.equal(Y1, R1) and torch.equal(Y2, R2)
+    assert torch.equal(Y1, R1) and torch.equal(Y2, R2) and torch.equal(Y1b, R1)
 
 
 # ----------------------------------------------------------- full-size workloads
