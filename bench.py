@@ -51,8 +51,9 @@ def parse():
     p.add_argument("--only", choices=["prefill", "decode"], default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-variants", action="store_true",
-                   help="skip the memory-halved and bf16 variants (profiling runs that should "
-                        "see only the headline kernels)")
+                   help="skip the memory-halved and bf16 variants and the down-projection "
+                        "context timing (profiling runs that should see only the headline "
+                        "kernels)")
     p.add_argument("--sweep", action="store_true",
                    help="instead of the headline run: the four projections of a 175B-class "
                         "block at T=4096 with 0, 8, 64 and 256 planted outlier dimensions "
@@ -241,6 +242,40 @@ def bench_prefill(torch, mm, synth, steps, warmup, variants=True):
         "quantize_weight_gbs": (2.0 * K * N + K * N + 4.0 * N) / (q_ms * 1e-3) / 1e9,
         **extra,
     }
+
+
+def bench_down(torch, mm, synth, steps, warmup):
+    """The prefill FFN down-projection workload (T=2048, K=49152, N=12288,
+    Laplace activations with planted and natural outliers): whole
+    int8_mixed_matmul calls on a pre-converted weight.  Context next to the
+    headline; 384 output tiles make 1.5 rounds on 256 CUs, which the matmul
+    runs as 768 half-K units."""
+    w = synth.WORKLOADS["down"]
+    T, K, N = w.T, w.K, w.N
+    log(f"down: generating X [{T},{K}], W [{K},{N}]")
+    X = torch.from_numpy(synth.make_x(w, threads=CPU_THREADS)).cuda()
+    W16 = torch.from_numpy(synth.make_w(w, threads=CPU_THREADS)).cuda()
+    Wq, sw = mm.quantize_weight(W16)
+    ws = mm.new_workspace(T, K, N)
+    Y = torch.empty((T, N), dtype=torch.float16, device="cuda")
+
+    def step(i, e):
+        if e is not None:
+            e[0].record()
+        mm.mixed_matmul(X, Wq, sw, W16, w.tau, workspace=ws, out=Y)
+        if e is not None:
+            e[1].record()
+
+    log(f"down: {PREWARM_S} s prewarm, {warmup} warmup + {steps} timed steps")
+    prewarm(torch, step)
+    wall, _ = timed_loop(torch, steps, warmup, step)
+    dbg = mm.mixed_matmul_debug(X, Wq, sw, W16, w.tau)
+    o = int(dbg["count"][0])
+    del dbg, X, W16, Wq, sw, ws, Y
+    torch.cuda.empty_cache()
+    return {"T": T, "K": K, "N": N, "tau": w.tau, "outlier_dims": o,
+            "ms_per_call": round(wall * 1e3 / steps, 4),
+            "TOPS": round(2.0 * T * K * N * steps / wall / 1e12, 2)}
 
 
 def decode_variants(torch, mm, w, X, sets, ws, Y, rounds, warmup):
@@ -483,6 +518,10 @@ def main():
             + (f"; memory-halved {pre['halved_tops']:.1f} TOPS, bf16 {pre['bf16_tops']:.1f} TOPS"
                if "halved_tops" in pre else ""))
         torch.cuda.empty_cache()
+    down = None
+    if args.only is None and not args.no_variants:
+        down = bench_down(torch, mm, synth, args.steps, args.warmup)
+        log(f"down: {down['TOPS']:.1f} TOPS ({down['ms_per_call']:.3f} ms/call, o = {down['outlier_dims']})")
     if args.only in (None, "decode"):
         dec = bench_decode(torch, mm, synth, args.steps, args.warmup, not args.no_variants)
         log(f"decode: {dec['weight_gbs']:.1f} GB/s weight ({dec['call_ms'] * 1e3:.1f} us/call)"
@@ -560,6 +599,10 @@ def main():
                         "config": d["config"], "roofline": d["roofline"]})
         else:
             out["decode"] = d
+    if down is not None:
+        out["other_configs"] = {"down": {
+            "workload": "prefill FFN down-projection (whole int8_mixed_matmul calls, W "
+                        "pre-converted to Int8)", **down}}
     if not args.no_cpu_baseline and pre is not None:
         log("cpu baseline: oracle on a row sample")
         out["cpu_baseline"] = cpu_baseline(synth, pre["T"], pre["K"], pre["N"])
