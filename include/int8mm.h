@@ -72,7 +72,11 @@ const char* int8mm_status_string(int status);
 
 /* Bytes of device workspace that int8_mixed_matmul and its variants need
  * for this shape (host only, enqueues nothing).  The size covers the
- * worst case in which every hidden dimension is an outlier.  For long K
+ * worst case in which every hidden dimension is an outlier, and room for
+ * min(K, 512) outlier rows of N 16-bit values into which the memory-halved
+ * variant (W16 = NULL) recovers the outlier rows of W once per call (with
+ * more outliers, or without that room, the matmul recovers them itself,
+ * more slowly).  For long K
  * (>= 24576) with a partial last round of 256 x 256 output tiles on the
  * current device, the matmul splits K in two and the size also covers, per
  * output tile, two 256 KB blocks of int32 partial sums and a counter; this
@@ -184,12 +188,12 @@ int int8mm_quantize_activations(const void* X, int64_t T, int64_t K, int64_t N, 
 /* Steps 3-4 on a workspace filled by int8mm_quantize_activations with the
  * same T and K.  The activation part of the workspace is only read here and
  * may be reused for any number of weights (any N the workspace size
- * covers); the K-split part (see the size query) is scratch of this call,
- * so matmuls on one workspace run one after another (one stream).  X is
- * read only through the gathered copy in the workspace.  Arguments as
- * int8_mixed_matmul.
+ * covers); the recovered-rows and K-split parts (see the size query) are
+ * scratch of this call, so matmuls on one workspace run one after another
+ * (one stream).  X is read only through the gathered copy in the
+ * workspace.  Arguments as int8_mixed_matmul.
  * Errors: E_NULL, E_SHAPE, E_ALIGN, E_WORKSPACE, E_HIP. */
-int int8mm_matmul_prepared(const void* workspace, size_t workspace_bytes, int64_t T, int64_t K,
+int int8mm_matmul_prepared(void* workspace, size_t workspace_bytes, int64_t T, int64_t K,
                            const int8_t* Wq, const float* sw, const void* W16, int64_t N,
                            void* Y, void* stream);
 

@@ -44,6 +44,9 @@ __device__ __forceinline__ uint16_t f32_to_h16(float f) {
 //   sx      f32 [T]      row scales
 //   xq      i8  [T,K]    quantized activations, outlier columns 0
 //   xo      16-bit [T,opad] outlier columns of X, row stride count[1], zero padded
+//   wrec    16-bit [min(K, kRecoverRows), N]  the outlier rows of W recovered from
+//           Wq for the memory-halved variant, row j = outlier j (present when the
+//           workspace is large enough for it)
 // and, only when the matmul splits K in two (gemm_ksplit), after all of the above:
 //   ks_count i32 [tiles]            per output tile, halves finished (zeroed by the
 //                                   matmul's launch)
@@ -56,6 +59,8 @@ struct Workspace {
     float* sx;
     int8_t* xq;
     uint16_t* xo;
+    uint16_t* wrec;      // NULL when the workspace has no room for it
+    int64_t wrec_rows;
     int32_t* ks_count;   // NULL without the K split
     int32_t* ks_part;
     size_t bytes;        // total bytes the layout needs
@@ -86,9 +91,20 @@ int device_cus();
 // as two halves of K on the current device, else 1.
 int gemm_ksplit(int64_t T, int64_t K, int64_t N);
 
+// Outlier rows the memory-halved variant recovers into the workspace before
+// the matmul (more outliers than this: the matmul recovers them itself).
+constexpr int64_t kRecoverRows = 512;
+
 // Layout of the workspace for (T, K, N) at `base` (base may be NULL to size
-// it); ksplit = 2 adds the regions of the K split.
-Workspace carve_workspace(void* base, int64_t T, int64_t K, int64_t N, int ksplit);
+// it); wrec adds the recovered-rows region, ksplit = 2 the K-split regions
+// (which need wrec).
+Workspace carve_workspace(void* base, int64_t T, int64_t K, int64_t N, bool wrec, int ksplit);
+
+// Recovers W^[j, n] = 16-bit(fp32(Wq[n, idx_j] * fp32(s_w[n] / 127))) for the
+// outliers j < o <= rows into out [rows, N] (nothing when o > rows).
+hipError_t launch_recover_rows(const int8_t* Wq, const float* sw, const int32_t* idx,
+                               const int32_t* count, int64_t K, int64_t N, int ht,
+                               uint16_t* out, int64_t rows, hipStream_t stream);
 
 // ---- activation side (k_activation.hip)
 hipError_t launch_activation_pass(const uint16_t* X, int ht, int64_t T, int64_t K, float tau,
@@ -109,7 +125,9 @@ struct GemmArgs {
     const uint16_t* xo;    // [T,opad] 16-bit
     const int32_t* idx;    // [K]
     const int32_t* count;  // [2]
-    const uint16_t* w16;   // [K,N] 16-bit, or NULL: outlier rows recovered from wq
+    const uint16_t* w16;   // [K,N] 16-bit (row idx_j), or NULL: outlier rows recovered from wq
+    int64_t w16_rows;      // > 0: w16 is [w16_rows, N] with row j = outlier j, valid when
+                           // o <= w16_rows (else the rows are recovered from wq)
     uint16_t* y;           // [T,N] 16-bit
     int32_t* acc_out;      // [T,N] or NULL
     int64_t T, K, N;

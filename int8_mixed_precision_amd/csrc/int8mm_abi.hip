@@ -29,14 +29,38 @@ int check_tau(float tau) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? INT8MM_OK : INT8MM_E_HIP; }
 
-// The K split of the matmul (gemm_ksplit) when the workspace is large enough
-// for its regions, else none.  The size query reserves them whenever the
-// split applies, and every entry point decides the same way from the same
-// (T, K, N, workspace_bytes), so the activation pass and the matmul of one
-// workspace always agree on its layout.
-int ksplit_for(int64_t T, int64_t K, int64_t N, size_t workspace_bytes) {
-    if (gemm_ksplit(T, K, N) != 2) return 1;
-    return workspace_bytes >= carve_workspace(nullptr, T, K, N, 2).bytes ? 2 : 1;
+// Optional workspace regions in use: the recovered outlier rows of the
+// memory-halved variant, then the matmul's K split (gemm_ksplit), each only
+// when the workspace is large enough for it.  The size query reserves both
+// (the split only where it applies), and every entry point decides the same
+// way from the same (T, K, N, workspace_bytes), so calls on one workspace
+// always agree on its layout.
+Workspace layout_for(void* base, int64_t T, int64_t K, int64_t N, size_t workspace_bytes) {
+    const bool wrec = workspace_bytes >= carve_workspace(nullptr, T, K, N, true, 1).bytes;
+    const int ks = wrec && gemm_ksplit(T, K, N) == 2 &&
+                           workspace_bytes >= carve_workspace(nullptr, T, K, N, true, 2).bytes
+                       ? 2
+                       : 1;
+    return carve_workspace(base, T, K, N, wrec, ks);
+}
+
+// Steps 3-4 on a prepared workspace: without W16 (memory-halved variant) the
+// outlier rows are first recovered into the workspace when it has room.
+int run_gemm(const Workspace& ws, int ht, int64_t T, int64_t K, const int8_t* Wq,
+             const float* sw, const uint16_t* w16, int64_t N, uint16_t* y16, int32_t* acc,
+             hipStream_t stream) {
+    const uint16_t* rows = w16;
+    int64_t nrows = 0;
+    if (!w16 && ws.wrec) {
+        hipError_t e = launch_recover_rows(Wq, sw, ws.idx, ws.count, K, N, ht, ws.wrec,
+                                           ws.wrec_rows, stream);
+        if (e != hipSuccess) return INT8MM_E_HIP;
+        rows = ws.wrec;
+        nrows = ws.wrec_rows;
+    }
+    GemmArgs g{ws.xq, ws.sx, Wq, sw, ws.xo, ws.idx, ws.count, rows, nrows, y16, acc, T, K, N,
+               ws.ks_count ? 2 : 1, ws.ks_count, ws.ks_part};
+    return hip_status(launch_gemm(g, ht, stream));
 }
 
 // Validation shared by int8_mixed_matmul and its debug variant.
@@ -51,7 +75,8 @@ int check_matmul(const void* X, int64_t T, int64_t K, const int8_t* Wq, const fl
     if (!aligned16(X) || !aligned16(Wq) || !aligned16(sw) || !aligned16(Y) ||
         !aligned16(workspace) || (W16 && !aligned16(W16)))
         return INT8MM_E_ALIGN;
-    if (workspace_bytes < carve_workspace(nullptr, T, K, N, 1).bytes) return INT8MM_E_WORKSPACE;
+    if (workspace_bytes < carve_workspace(nullptr, T, K, N, false, 1).bytes)
+        return INT8MM_E_WORKSPACE;
     return INT8MM_OK;
 }
 
@@ -66,14 +91,11 @@ int run_matmul(const void* X, int ht, int64_t T, int64_t K, const int8_t* Wq, co
     if (decode_path_supported(T, K, N))
         return hip_status(launch_decode(x16, ht, T, K, Wq, sw, w16, N, tau, y16, count, idx, xq,
                                         sx, acc, stream));
-    const int ks = ksplit_for(T, K, N, workspace_bytes);
-    Workspace ws = carve_workspace(workspace, T, K, N, ks);
+    Workspace ws = layout_for(workspace, T, K, N, workspace_bytes);
     hipError_t e = launch_activation_pass(x16, ht, T, K, tau, ws, stream);
     if (e != hipSuccess) return INT8MM_E_HIP;
-    GemmArgs g{ws.xq, ws.sx, Wq, sw, ws.xo, ws.idx, ws.count, w16, y16, acc, T, K, N,
-               ks, ws.ks_count, ws.ks_part};
-    e = launch_gemm(g, ht, stream);
-    if (e != hipSuccess) return INT8MM_E_HIP;
+    const int st = run_gemm(ws, ht, T, K, Wq, sw, w16, N, y16, acc, stream);
+    if (st) return st;
     return hip_status(launch_debug_copies(ws, T, K, count, idx, xq, sx, stream));
 }
 
@@ -99,7 +121,7 @@ int int8_mixed_matmul_workspace_size(int64_t T, int64_t K, int64_t N, size_t* by
     if (!bytes) return INT8MM_E_NULL;
     int st = check_shape(T, K, N);
     if (st) return st;
-    *bytes = carve_workspace(nullptr, T, K, N, gemm_ksplit(T, K, N)).bytes;
+    *bytes = carve_workspace(nullptr, T, K, N, true, gemm_ksplit(T, K, N)).bytes;
     return INT8MM_OK;
 }
 
@@ -191,13 +213,14 @@ int int8mm_quantize_activations(const void* X, int64_t T, int64_t K, int64_t N, 
     st = check_tau(tau);
     if (st) return st;
     if (!aligned16(X) || !aligned16(workspace)) return INT8MM_E_ALIGN;
-    if (workspace_bytes < carve_workspace(nullptr, T, K, N, 1).bytes) return INT8MM_E_WORKSPACE;
-    Workspace ws = carve_workspace(workspace, T, K, N, ksplit_for(T, K, N, workspace_bytes));
+    if (workspace_bytes < carve_workspace(nullptr, T, K, N, false, 1).bytes)
+        return INT8MM_E_WORKSPACE;
+    Workspace ws = layout_for(workspace, T, K, N, workspace_bytes);
     return hip_status(launch_activation_pass(static_cast<const uint16_t*>(X), kHalfF16, T, K, tau, ws,
                                              static_cast<hipStream_t>(stream)));
 }
 
-int int8mm_matmul_prepared(const void* workspace, size_t workspace_bytes, int64_t T, int64_t K,
+int int8mm_matmul_prepared(void* workspace, size_t workspace_bytes, int64_t T, int64_t K,
                            const int8_t* Wq, const float* sw, const void* W16, int64_t N,
                            void* Y, void* stream) {
     if (!workspace || !Wq || !sw || !Y) return INT8MM_E_NULL;
@@ -206,13 +229,11 @@ int int8mm_matmul_prepared(const void* workspace, size_t workspace_bytes, int64_
     if (!aligned16(workspace) || !aligned16(Wq) || !aligned16(sw) || !aligned16(Y) ||
         (W16 && !aligned16(W16)))
         return INT8MM_E_ALIGN;
-    if (workspace_bytes < carve_workspace(nullptr, T, K, N, 1).bytes) return INT8MM_E_WORKSPACE;
-    const int ks = ksplit_for(T, K, N, workspace_bytes);
-    Workspace ws = carve_workspace(const_cast<void*>(workspace), T, K, N, ks);
-    GemmArgs g{ws.xq, ws.sx, Wq, sw, ws.xo, ws.idx, ws.count,
-               static_cast<const uint16_t*>(W16), static_cast<uint16_t*>(Y), nullptr, T, K, N,
-               ks, ws.ks_count, ws.ks_part};
-    return hip_status(launch_gemm(g, kHalfF16, static_cast<hipStream_t>(stream)));
+    if (workspace_bytes < carve_workspace(nullptr, T, K, N, false, 1).bytes)
+        return INT8MM_E_WORKSPACE;
+    Workspace ws = layout_for(workspace, T, K, N, workspace_bytes);
+    return run_gemm(ws, kHalfF16, T, K, Wq, sw, static_cast<const uint16_t*>(W16), N,
+                    static_cast<uint16_t*>(Y), nullptr, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

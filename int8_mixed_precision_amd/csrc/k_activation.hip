@@ -332,7 +332,7 @@ hipError_t launch_debug_copies(const Workspace& ws, int64_t T, int64_t K, int32_
     return e;
 }
 
-Workspace carve_workspace(void* base, int64_t T, int64_t K, int64_t N, int ksplit) {
+Workspace carve_workspace(void* base, int64_t T, int64_t K, int64_t N, bool wrec, int ksplit) {
     Workspace w{};
     const int64_t kw = ceil_div(K, 32);
     size_t off = 0;
@@ -350,7 +350,14 @@ Workspace carve_workspace(void* base, int64_t T, int64_t K, int64_t N, int kspli
     w.xq = reinterpret_cast<int8_t*>(take((size_t)T * (size_t)K));
     // worst case: every dimension an outlier, o = K (K % 16 == 0, so opad <= K)
     w.xo = reinterpret_cast<uint16_t*>(take(sizeof(uint16_t) * (size_t)T * (size_t)K));
-    if (ksplit == 2) {
+    // optional regions after the fixed ones, so that a smaller workspace is a
+    // valid prefix: the recovered outlier rows, then the K split (which
+    // needs them)
+    if (wrec) {
+        w.wrec_rows = K < kRecoverRows ? K : kRecoverRows;
+        w.wrec = reinterpret_cast<uint16_t*>(take(sizeof(uint16_t) * (size_t)w.wrec_rows * (size_t)N));
+    }
+    if (wrec && ksplit == 2) {
         // after everything else, so the layout without the split is a prefix
         const int64_t tiles = ceil_div(T, 256) * ceil_div(N, 256);
         w.ks_count = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)tiles));

@@ -101,9 +101,14 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a,
         if constexpr (STAGED) swn[j] = sc.sw_pre[j] * (1.0f / 16129.0f);
         else swn[j] = n < N ? a.sw[n] * (1.0f / 16129.0f) : 0.0f;
     }
-    // memory-halved variant (no W16): the outlier rows are recovered from the
-    // Int8 weight, W^[k,n] = fp16(q[n,k] * fp32(s_w[n] / 127))
-    const bool recover = a.w16 == nullptr;
+    const int o = STAGED ? sc.o : a.count[0];
+    const int opad = STAGED ? sc.opad : a.count[1];
+    // 16-bit outlier rows: the caller's W16 (row idx_j), the rows recovered
+    // before the matmul (row j, when o fits), or - memory-halved variant
+    // without room for those - recovered here from the Int8 weight,
+    // W^[k,n] = fp16(q[n,k] * fp32(s_w[n] / 127))
+    const bool recover = a.w16 == nullptr || (a.w16_rows > 0 && o > a.w16_rows);
+    const bool by_pos = !recover && a.w16_rows > 0;   // W16 row = outlier position
     float dn[TN];
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
@@ -111,8 +116,6 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a,
         if constexpr (STAGED) dn[j] = recover ? sc.sw_pre[j] / 127.0f : 0.0f;
         else dn[j] = recover && n < N ? a.sw[n] / 127.0f : 0.0f;
     }
-    const int o = STAGED ? sc.o : a.count[0];
-    const int opad = STAGED ? sc.opad : a.count[1];
     if constexpr (STAGED) {
         if (sc.tid < 256) sc.sxs[sc.tid] = sc.sx_pre;
         __syncthreads();
@@ -162,7 +165,7 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a,
             const int jl = jc + (lane >> 5) * 8;   // first of this lane's 8 outlier slots
             int kk[8];
     #pragma unroll
-            for (int e = 0; e < 8; ++e) kk[e] = (jl + e < o) ? a.idx[jl + e] : -1;
+            for (int e = 0; e < 8; ++e) kk[e] = (jl + e < o) ? (by_pos ? jl + e : a.idx[jl + e]) : -1;
             v8u16 wb[TN];
     #pragma unroll
             for (int j = 0; j < TN; ++j) {
@@ -218,11 +221,13 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a,
                 dcol[c] = n < N ? a.sw[n] / 127.0f : 0.0f;
             }
         }
-        int k_next = e < o ? a.idx[e] : -1;
+        // k: the W16 row of slot e (the outlier's dimension, or its position
+        // for recovered rows), or the dimension whose Wq bytes are recovered
+        int k_next = e < o ? (by_pos ? e : a.idx[e]) : -1;
         uint4 wv[2], xv[2];
         auto load_chunk = [&](int jc) {
             const int k = k_next;
-            k_next = jc + kOC + e < o ? a.idx[jc + kOC + e] : -1;
+            k_next = jc + kOC + e < o ? (by_pos ? jc + kOC + e : a.idx[jc + kOC + e]) : -1;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int64_t n = sc.n0 + cb * 16 + h * 8;

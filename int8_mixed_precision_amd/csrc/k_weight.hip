@@ -164,7 +164,44 @@ hipError_t launch_typed(const void* W, int64_t K, int64_t N, int8_t* Wq, float* 
     return hipGetLastError();
 }
 
+// Memory-halved variant: the outlier rows of W recovered from the Int8
+// weight once per call, out[j, n] = 16-bit(fp32(Wq[n, idx_j] * fp32(s_w[n] /
+// 127))) (HT: fp16 or bf16), so that the matmul reads them as contiguous rows
+// like a caller's W16.  Thread -> column n (stores coalesced along n); the
+// y dimension of the grid strides over the outliers.  Each thread reads one
+// byte per outlier from its Wq row.  Nothing is written when o > rows: the
+// matmul then recovers the values itself.
+template <int HT>
+__global__ __launch_bounds__(256) void k_recover_rows(const int8_t* __restrict__ Wq,
+                                                      const float* __restrict__ sw,
+                                                      const int32_t* __restrict__ idx,
+                                                      const int32_t* __restrict__ count,
+                                                      int64_t K, int64_t N,
+                                                      uint16_t* __restrict__ out, int64_t rows) {
+    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t o = count[0];
+    if (n >= N || o > rows) return;
+    const float d = sw[n] / 127.0f;
+    const int8_t* wrow = Wq + n * K;
+    for (int64_t j = blockIdx.y; j < o; j += gridDim.y)
+        out[j * N + n] = recover_weight<HT>(wrow[idx[j]], d);
+}
+
 }  // namespace
+
+hipError_t launch_recover_rows(const int8_t* Wq, const float* sw, const int32_t* idx,
+                               const int32_t* count, int64_t K, int64_t N, int ht,
+                               uint16_t* out, int64_t rows, hipStream_t stream) {
+    // enough workgroups to fill the chip for any N; each strides over o
+    const dim3 grid((unsigned)ceil_div(N, 256), 16);
+    if (ht == kHalfBF16)
+        hipLaunchKernelGGL(k_recover_rows<kHalfBF16>, grid, dim3(256), 0, stream, Wq, sw, idx,
+                           count, K, N, out, rows);
+    else
+        hipLaunchKernelGGL(k_recover_rows<kHalfF16>, grid, dim3(256), 0, stream, Wq, sw, idx,
+                           count, K, N, out, rows);
+    return hipGetLastError();
+}
 
 hipError_t launch_quantize_weight(const void* W, int wtype, int64_t K, int64_t N, int8_t* Wq,
                                   float* sw, _Float16* w16, hipStream_t stream) {

@@ -47,16 +47,20 @@ def test_status_strings(mm):
 def test_workspace_size(mm):
     small = mm.workspace_size(16, 64, 48)
     big = mm.workspace_size(2048, 12288, 49152)
-    # Xq (T*K bytes) plus the worst-case gathered outlier columns (2*T*K)
-    assert big >= 3 * 2048 * 12288 and big < 3 * 2048 * 12288 + (1 << 20)
+    # Xq (T*K bytes), the worst-case gathered outlier columns (2*T*K) and
+    # min(K, 512) recovered 16-bit outlier rows of N values (memory-halved
+    # variant), plus alignment padding
+    rec = 2 * 512 * 49152
+    assert 3 * 2048 * 12288 + rec <= big < 3 * 2048 * 12288 + rec + (1 << 20)
     assert 0 < small < big
-    assert mm.workspace_size(16, 64, 8) == small    # N does not change the size
-    # ... unless the matmul splits K in two: then 2 x 256 KB of partial sums and
-    # a counter per 256 x 256 tile follow (384 tiles: 2 rounds on 256 CUs
-    # become 1.5; without a device the size query assumes 256 CUs)
+    assert mm.workspace_size(16, 64, 8) < small    # fewer recovered-row columns
+    # the matmul's K split adds 2 x 256 KB of partial sums and a counter per
+    # 256 x 256 tile (384 tiles: 2 rounds on 256 CUs become 1.5; without a
+    # device the size query assumes 256 CUs)
     down = mm.workspace_size(2048, 49152, 12288)
-    assert down >= 3 * 2048 * 49152 + 384 * (2 * 65536 * 4 + 4)
-    assert mm.workspace_size(4096, 49152, 12288) < 3 * 4096 * 49152 + (1 << 20)   # 3 full rounds
+    assert down >= 3 * 2048 * 49152 + 2 * 512 * 12288 + 384 * (2 * 65536 * 4 + 4)
+    t4096 = mm.workspace_size(4096, 49152, 12288)                         # 3 full rounds
+    assert t4096 < 3 * 4096 * 49152 + 2 * 512 * 12288 + (1 << 20)
     with pytest.raises(mm.Int8mmError) as e:
         mm.workspace_size(16, 60, 48)
     assert e.value.status == mm.E_SHAPE

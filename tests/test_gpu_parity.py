@@ -137,6 +137,8 @@ def test_decode_path(mm, T, K, N, nd, tau):
     (1, 4096, 1000, 3, 6.0), (8, 8192, 264, 300, 6.0),         # decode kernel, o > 16
     (16, 4096, 520, 20, 6.0), (300, 24576, 520, 3, 6.0),      # K split in two
     (70, 1024, 136, 0, 0.0), (2, 4096, 136, 0, 0.0),           # every dimension an outlier
+    (257, 1024, 264, 0, 0.0),       # o = 1024 > 512: rows recovered inside the matmul
+    (300, 2048, 520, 600, 6.0),     # about 600 outliers, the same
 ])
 def test_memory_halved(mm, T, K, N, nd, tau):
     """W16 = NULL: outlier rows recovered from the Int8 weight."""
@@ -199,10 +201,13 @@ def test_staged_entry_points_match(mm, T, K, N1, N2):
     Y1 = mm.matmul_prepared(ws, T, K, Wq, sw, Wd)
     Y2 = mm.matmul_prepared(ws, T, K, Wq2, sw2, W2d)   # one pass of X, two weights
     Y1b = mm.matmul_prepared(ws, T, K, Wq, sw, Wd)     # and the first again
+    H2 = mm.matmul_prepared(ws, T, K, Wq2, sw2, None)  # memory-halved
     R1 = mm.mixed_matmul(Xd, Wq, sw, Wd, 6.0)
     R2 = mm.mixed_matmul(Xd, Wq2, sw2, W2d, 6.0)
+    RH2 = mm.mixed_matmul(Xd, Wq2, sw2, None, 6.0)
     torch.cuda.synchronize()
     assert torch.equal(Y1, R1) and torch.equal(Y2, R2) and torch.equal(Y1b, R1)
+    assert torch.equal(H2, RH2)
 
 
 # ----------------------------------------------------------- full-size workloads
