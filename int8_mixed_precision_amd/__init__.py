@@ -110,6 +110,18 @@ def _need(t: torch.Tensor, dtype, ndim: int, name: str) -> None:
                          f"got {t.dtype} {tuple(t.shape)}")
 
 
+def _need_ws(ws) -> None:
+    """A workspace is a contiguous 1-d uint8 GPU tensor (its size is checked
+    by the library against the size query)."""
+    _need(ws, torch.uint8, 1, "workspace")
+
+
+def _need_out(Y, dtype, T: int, N: int) -> None:
+    _need(Y, dtype, 2, "out")
+    if tuple(Y.shape) != (T, N):
+        raise ValueError(f"out must be [{T},{N}], got {tuple(Y.shape)}")
+
+
 def workspace_size(T: int, K: int, N: int) -> int:
     out = ctypes.c_size_t(0)
     _check(_lib.int8_mixed_matmul_workspace_size(T, K, N, ctypes.byref(out)),
@@ -194,9 +206,9 @@ def mixed_matmul(X, Wq, sw, W16, tau: float, workspace=None, out=None) -> torch.
     T, K, N = _mm_args(X, Wq, sw, W16)
     if workspace is None:
         workspace = new_workspace(T, K, N, X.device)
+    _need_ws(workspace)
     Y = out if out is not None else torch.empty((T, N), dtype=X.dtype, device=X.device)
-    if Y.dtype != X.dtype or tuple(Y.shape) != (T, N) or not Y.is_contiguous():
-        raise ValueError("out must be a contiguous [T,N] tensor of X's dtype")
+    _need_out(Y, X.dtype, T, N)
     fn, name = ((_lib.int8_mixed_matmul_bf16, "int8_mixed_matmul_bf16")
                 if X.dtype == torch.bfloat16 else (_lib.int8_mixed_matmul, "int8_mixed_matmul"))
     _check(fn(_ptr(X), T, K, _ptr(Wq), _ptr(sw), _ptr(W16), N, float(tau), _ptr(Y),
@@ -210,6 +222,7 @@ def mixed_matmul_debug(X, Wq, sw, W16, tau: float, workspace=None) -> dict:
     dev = X.device
     if workspace is None:
         workspace = new_workspace(T, K, N, dev)
+    _need_ws(workspace)
     r = {"Y": torch.empty((T, N), dtype=X.dtype, device=dev),
          "count": torch.zeros(4, dtype=torch.int32, device=dev),
          "idx": torch.zeros(K, dtype=torch.int32, device=dev),
@@ -228,6 +241,7 @@ def mixed_matmul_debug(X, Wq, sw, W16, tau: float, workspace=None) -> dict:
 def quantize_activations(X, N: int, tau: float, workspace) -> None:
     """Activation-side steps into `workspace` (see int8mm_quantize_activations)."""
     _need(X, torch.float16, 2, "X")
+    _need_ws(workspace)
     T, K = X.shape
     _check(_lib.int8mm_quantize_activations(_ptr(X), T, K, N, float(tau), _ptr(workspace),
                                             workspace.numel(), _stream()),
@@ -235,13 +249,20 @@ def quantize_activations(X, N: int, tau: float, workspace) -> None:
 
 
 def matmul_prepared(workspace, T: int, K: int, Wq, sw, W16, out=None) -> torch.Tensor:
-    """Matmul steps on a prepared workspace (see int8mm_matmul_prepared)."""
+    """Matmul steps on a prepared workspace (see int8mm_matmul_prepared);
+    W16 None: memory-halved variant."""
+    _need_ws(workspace)
     _need(Wq, torch.int8, 1, "Wq")
     _need(sw, torch.float32, 1, "sw")
     N = sw.shape[0]
     if Wq.numel() != weight_bytes(K, N):
         raise ValueError("Wq does not match K and N")
+    if W16 is not None:
+        _need(W16, torch.float16, 2, "W16")
+        if tuple(W16.shape) != (K, N):
+            raise ValueError(f"W16 must be [{K},{N}], got {tuple(W16.shape)}")
     Y = out if out is not None else torch.empty((T, N), dtype=torch.float16, device=Wq.device)
+    _need_out(Y, torch.float16, T, N)
     _check(_lib.int8mm_matmul_prepared(_ptr(workspace), workspace.numel(), T, K, _ptr(Wq),
                                        _ptr(sw), _ptr(W16), N, _ptr(Y), _stream()),
            "int8mm_matmul_prepared")

@@ -150,3 +150,14 @@ def test_binding_rejects_cpu_tensors(mm):
     X = torch.zeros(16, 64, dtype=torch.float16)
     with pytest.raises(ValueError):
         mm.quantize_weight(X)
+    Wq = torch.zeros(64 * 48, dtype=torch.int8)
+    sw = torch.ones(48, dtype=torch.float32)
+    ws = torch.zeros(1 << 16, dtype=torch.uint8)
+    for call in (lambda: mm.mixed_matmul(X, Wq, sw, None, 6.0),
+                 lambda: mm.quantize_activations(X, 48, 6.0, ws),
+                 lambda: mm.matmul_prepared(ws, 16, 64, Wq, sw, None),
+                 lambda: mm.quantize_checkpoint(torch.zeros(64, 48))):
+        with pytest.raises(ValueError):
+            call()
+    with pytest.raises(TypeError):
+        mm.matmul_prepared(None, 16, 64, Wq, sw, None)
