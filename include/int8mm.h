@@ -72,11 +72,12 @@ const char* int8mm_status_string(int status);
 
 /* Bytes of device workspace that int8_mixed_matmul and its variants need
  * for this shape (host only, enqueues nothing).  The size covers the
- * worst case in which every hidden dimension is an outlier, and room for
- * min(K, 512) outlier rows of N 16-bit values into which the memory-halved
- * variant (W16 = NULL) recovers the outlier rows of W once per call (with
- * more outliers, or without that room, the matmul recovers them itself,
- * more slowly).  For long K
+ * worst case in which every hidden dimension is an outlier, and (except
+ * for the decode shapes that run as a single kernel: T <= 16, K 4096 or
+ * 8192, T*K <= 65536) room for min(K, 512) outlier rows of N 16-bit values
+ * into which the memory-halved variant (W16 = NULL) recovers the outlier
+ * rows of W once per call (with more outliers, or without that room, the
+ * matmul recovers them itself, more slowly).  For long K
  * (>= 24576) with a partial last round of 256 x 256 output tiles on the
  * current device, the matmul splits K in two and the size also covers, per
  * output tile, two 256 KB blocks of int32 partial sums and a counter; this

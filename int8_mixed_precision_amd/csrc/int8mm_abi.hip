@@ -121,7 +121,10 @@ int int8_mixed_matmul_workspace_size(int64_t T, int64_t K, int64_t N, size_t* by
     if (!bytes) return INT8MM_E_NULL;
     int st = check_shape(T, K, N);
     if (st) return st;
-    *bytes = carve_workspace(nullptr, T, K, N, true, gemm_ksplit(T, K, N)).bytes;
+    // the single-kernel decode path uses no workspace regions beyond the
+    // fixed ones (which int8mm_quantize_activations still needs)
+    const bool gemm = !decode_path_supported(T, K, N);
+    *bytes = carve_workspace(nullptr, T, K, N, gemm, gemm ? gemm_ksplit(T, K, N) : 1).bytes;
     return INT8MM_OK;
 }
 

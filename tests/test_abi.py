@@ -61,6 +61,8 @@ def test_workspace_size(mm):
     assert down >= 3 * 2048 * 49152 + 2 * 512 * 12288 + 384 * (2 * 65536 * 4 + 4)
     t4096 = mm.workspace_size(4096, 49152, 12288)                         # 3 full rounds
     assert t4096 < 3 * 4096 * 49152 + 2 * 512 * 12288 + (1 << 20)
+    # decode shapes run as one kernel and need only the fixed regions
+    assert mm.workspace_size(8, 8192, 28672) < 3 * 8 * 8192 + (1 << 16)
     with pytest.raises(mm.Int8mmError) as e:
         mm.workspace_size(16, 60, 48)
     assert e.value.status == mm.E_SHAPE
