@@ -144,6 +144,14 @@ hipError_t launch_decode(const uint16_t* X, int ht, int64_t T, int64_t K, const 
                          uint16_t* Y, int32_t* dbg_count, int32_t* dbg_idx, int8_t* dbg_xq,
                          float* dbg_sx, int32_t* dbg_acc, hipStream_t stream);
 
+// Decode shapes the single-kernel path does not take (T <= 16, K % 1024 == 0,
+// T*K <= 128 KB): the same weight stream with the activation side read from
+// a workspace the activation pass has filled (k_decode.hip).
+bool decode_pre_supported(int64_t T, int64_t K, int64_t N);
+hipError_t launch_decode_pre(int ht, int64_t T, int64_t K, const int8_t* Wq, const float* sw,
+                             const uint16_t* W16, int64_t N, uint16_t* Y, const Workspace& ws,
+                             int32_t* dbg_acc, hipStream_t stream);
+
 // ---- debug copies (k_activation.hip)
 hipError_t launch_debug_copies(const Workspace& ws, int64_t T, int64_t K, int32_t* count,
                                int32_t* idx, int8_t* xq, float* sx, hipStream_t stream);

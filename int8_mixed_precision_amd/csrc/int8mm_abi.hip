@@ -44,11 +44,15 @@ Workspace layout_for(void* base, int64_t T, int64_t K, int64_t N, size_t workspa
     return carve_workspace(base, T, K, N, wrec, ks);
 }
 
-// Steps 3-4 on a prepared workspace: without W16 (memory-halved variant) the
-// outlier rows are first recovered into the workspace when it has room.
-int run_gemm(const Workspace& ws, int ht, int64_t T, int64_t K, const int8_t* Wq,
-             const float* sw, const uint16_t* w16, int64_t N, uint16_t* y16, int32_t* acc,
-             hipStream_t stream) {
+// Steps 3-4 on a prepared workspace.  Few rows (T <= 16) stream the weight
+// through the decode kernel's precomputed mode; otherwise the GEMM runs, and
+// without W16 (memory-halved variant) the outlier rows are first recovered
+// into the workspace when it has room.
+int run_prepared(const Workspace& ws, int ht, int64_t T, int64_t K, const int8_t* Wq,
+                 const float* sw, const uint16_t* w16, int64_t N, uint16_t* y16, int32_t* acc,
+                 hipStream_t stream) {
+    if (decode_pre_supported(T, K, N))
+        return hip_status(launch_decode_pre(ht, T, K, Wq, sw, w16, N, y16, ws, acc, stream));
     const uint16_t* rows = w16;
     int64_t nrows = 0;
     if (!w16 && ws.wrec) {
@@ -94,7 +98,7 @@ int run_matmul(const void* X, int ht, int64_t T, int64_t K, const int8_t* Wq, co
     Workspace ws = layout_for(workspace, T, K, N, workspace_bytes);
     hipError_t e = launch_activation_pass(x16, ht, T, K, tau, ws, stream);
     if (e != hipSuccess) return INT8MM_E_HIP;
-    const int st = run_gemm(ws, ht, T, K, Wq, sw, w16, N, y16, acc, stream);
+    const int st = run_prepared(ws, ht, T, K, Wq, sw, w16, N, y16, acc, stream);
     if (st) return st;
     return hip_status(launch_debug_copies(ws, T, K, count, idx, xq, sx, stream));
 }
@@ -235,7 +239,7 @@ int int8mm_matmul_prepared(void* workspace, size_t workspace_bytes, int64_t T, i
     if (workspace_bytes < carve_workspace(nullptr, T, K, N, false, 1).bytes)
         return INT8MM_E_WORKSPACE;
     Workspace ws = layout_for(workspace, T, K, N, workspace_bytes);
-    return run_gemm(ws, kHalfF16, T, K, Wq, sw, static_cast<const uint16_t*>(W16), N,
+    return run_prepared(ws, kHalfF16, T, K, Wq, sw, static_cast<const uint16_t*>(W16), N,
                     static_cast<uint16_t*>(Y), nullptr, static_cast<hipStream_t>(stream));
 }
 

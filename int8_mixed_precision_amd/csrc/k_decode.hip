@@ -36,6 +36,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 // Quantization must round x * r and any following add separately, exactly
 // like the definition; no multiply-add contraction in this file.
@@ -67,6 +68,15 @@ struct DecodeArgs {
     uint32_t tau16;         // bits of the smallest 16-bit value >= tau (+inf if none finite)
     int T, K, N;
     int bpw;                // 16-row blocks per workgroup (1..8)
+    int cpb;                // K / 1024 (used when the chunk count is not a template constant)
+    // activation side computed beforehand by the activation-pass kernels
+    // (precomputed mode only): Xq [T,K], s_x [T], count {o, opad}, idx [o],
+    // the outlier columns of X [T,opad] 16-bit
+    const int8_t* xq_pre;
+    const float* sx_pre;
+    const int32_t* count_pre;
+    const int32_t* idx_pre;
+    const uint16_t* xo_pre;
     // optional debug outputs (NULL to skip); workgroup 0 writes all but acc
     int32_t* dbg_count;
     int32_t* dbg_idx;
@@ -77,14 +87,17 @@ struct DecodeArgs {
 
 // Xq rows carry a 16-byte pad: the B-operand read has 16 lanes on 16
 // different rows, which then fall on distinct banks.
-struct Smem {
-    int8_t xq[kMaxXK + kMaxT * 16];
-    int32_t idx[kMaxK];                        // outlier dims, ascending
-    float xo[kMaxT * kMaxOutliersLds];         // X values of the first outliers
+// XK: bytes of Xq; IDXN: outlier dimensions kept; OXL: outliers whose X
+// values are kept; NCF: entries of cfirst.
+template <int XK, int IDXN, int OXL, int NCF>
+struct SmemT {
+    int8_t xq[XK + kMaxT * 16];
+    int32_t idx[IDXN];                         // outlier dims, ascending
+    float xo[kMaxT * OXL];                     // X values of the first outliers
     int32_t acc[kMaxBpw][kRows][16];           // int32 sums [block][row][t]
     uint32_t w16o[kW16Cache][kMaxBpw * kRows / 2];   // W16[idx_j, n] pairs of the rows
     int8_t wqo[kW16Cache][kMaxBpw * kRows];    // Wq[n, idx_j] (memory-halved variant)
-    int32_t cfirst[kMaxK / kChunkKConst + 1];   // first outlier at or past k = 1024 c
+    int32_t cfirst[NCF];                       // first outlier at or past k = 1024 c
     float sw[kMaxBpw * kRows];                 // s_w of the rows
     float wmax[kWaves][kMaxT];
     float sx[kMaxT];
@@ -92,7 +105,15 @@ struct Smem {
     int32_t wtot[kWaves * 2];
     int32_t next;                              // next chunk to hand out
 };
+// activation side computed in the kernel: every outlier dimension in LDS
+using Smem = SmemT<kMaxXK, kMaxK, kMaxOutliersLds, kMaxK / kChunkKConst + 1>;
 static_assert(sizeof(Smem::acc) == kThreads * 16, "one 16-byte clear per thread");
+// activation side precomputed: twice the Xq room, only the first outliers
+constexpr int kMaxXKPre = 131072;              // T*K bytes of Xq kept in LDS
+constexpr int kOutliersLdsPre = 64;
+constexpr int kMaxCpbPre = kMaxXKPre / kChunkKConst;
+using SmemPre = SmemT<kMaxXKPre, kW16Cache, kOutliersLdsPre, kMaxCpbPre + 1>;
+static_assert(sizeof(SmemPre) <= 160 * 1024, "LDS of one workgroup");
 
 // Packed unsigned max of two pairs of 16-bit lanes.
 __device__ inline uint32_t pk_max_u16(uint32_t a, uint32_t b) {
@@ -115,11 +136,18 @@ static_assert(kChunkK == kChunkKConst, "chunk size");
 // CPB = K / 1024 chunks per 16-row block; a thread owns CPT = K / 4096
 // chunks of 8 columns (c = tid + 512 j) in the activation prologue, for all
 // T <= TMAX = 64 / CPB rows (so T * CPT <= 16 chunks of X per thread).
-template <int CPB, int HT>
+// PRE: the activation side was computed by the activation-pass kernels and
+// is read from their workspace (CPB = 0: the chunk count is a.cpb); this
+// serves T <= 16 for any K that is a multiple of 1024 with T*K <= 128 KB.
+template <int CPB, int HT, bool PRE = false>
 __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
-    constexpr int CPT = CPB / 4;
-    constexpr int TMAX = 64 / CPB;
-    __shared__ __attribute__((aligned(16))) Smem sm;
+    static_assert(PRE == (CPB == 0), "the precomputed mode takes its chunk count at run time");
+    constexpr int CPT = PRE ? 1 : CPB / 4;
+    constexpr int TMAX = PRE ? 1 : 64 / CPB;
+    constexpr int OXL = PRE ? kOutliersLdsPre : kMaxOutliersLds;
+    using SM = typename std::conditional<PRE, SmemPre, Smem>::type;
+    __shared__ __attribute__((aligned(16))) SM sm;
+    const int cpb = PRE ? a.cpb : CPB;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     // wave-uniform (a scalar), so the chunk loop below is uniform control flow
@@ -128,24 +156,24 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
     const int ldx = K + 16;                    // LDS row stride of Xq
     const int nblocks = (N + kRows - 1) / kRows;
     // this workgroup's weight rows n0 .. n0 + rows - 1 (rows past N are read
-    // as row N-1 and never stored); chunk id -> block id / CPB, k-chunk id % CPB
+    // as row N-1 and never stored); chunk id -> block id / cpb, k-chunk id % cpb
     const int b0 = blockIdx.x * a.bpw;
     const int nbw = a.bpw < nblocks - b0 ? a.bpw : nblocks - b0;
     const int rows = nbw * kRows;
     const int n0 = b0 * kRows;
-    const int total = nbw * CPB;
+    const int total = nbw * cpb;
 
-    // Load i of a chunk: lane l holds weight row n0 + 16 (id / CPB) + l % 16
-    // and bytes 1024 (id % CPB) + 64 i + 16 (l / 16) .. +16.  Ids past the end
+    // Load i of a chunk: lane l holds weight row n0 + 16 (id / cpb) + l % 16
+    // and bytes 1024 (id % cpb) + 64 i + 16 (l / 16) .. +16.  Ids past the end
     // read the first kilobyte of Wq on every lane instead (one line per
     // load, never used): loads stay unconditional, so the wait counts stay
     // exact.
     const int kl = (lane >> 4) * 16;
     // loads lo .. hi-1 of chunk id into buf (lo and hi are constants)
     auto issue_part = [&](int id, v4i (&buf)[kLoads], int lo, int hi) {
-        const int n = n0 + (id / CPB) * kRows + (lane & 15);
+        const int n = n0 + (id / cpb) * kRows + (lane & 15);
         const int64_t off =
-            id < total ? (int64_t)(n < N ? n : N - 1) * K + (id % CPB) * kChunkK + kl : 0;
+            id < total ? (int64_t)(n < N ? n : N - 1) * K + (id % cpb) * kChunkK + kl : 0;
         const int8_t* p = a.wq + off;
 #pragma unroll
         for (int i = 0; i < kLoads; ++i)
@@ -177,204 +205,250 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
     v4i ring[3][kLoads];
     int id0 = wave, id1 = wave + kWaves, id2 = wave + 2 * kWaves;
 
-    // X: rows t >= T re-read row T-1: a repeated row changes neither the
-    // column maxima nor anything used later (rows >= T of Xq and xo are never
-    // read), and unconditional loads keep the wait counts exact.
-    uint4 xr[CPT][TMAX];
-#pragma unroll
-    for (int j = 0; j < CPT; ++j)
-#pragma unroll
-        for (int t = 0; t < TMAX; ++t)
-            xr[j][t] = *reinterpret_cast<const uint4*>(a.x + (int64_t)(t < T ? t : T - 1) * K +
-                                                       (tid + kThreads * j) * 8);
-    // Magnitudes as fp16 bit patterns: for non-negative halves the unsigned
-    // order is the numeric order (fp16 and bf16 alike), so |x| >= tau <=>
-    // bits(|x|) >= tau16, with tau16 the bits of the smallest 16-bit value
-    // >= tau (+inf when none is finite).
-    // Column maxima over the T rows by packed unsigned 16-bit max.
-    uint32_t fm[CPT];
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-        uint32_t cm[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int t = 0; t < TMAX; ++t) {
-            const uint32_t w[4] = {xr[j][t].x, xr[j][t].y, xr[j][t].z, xr[j][t].w};
-#pragma unroll
-            for (int d = 0; d < 4; ++d) cm[d] = pk_max_u16(cm[d], w[d] & 0x7FFF7FFFu);
-        }
-        fm[j] = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            fm[j] |= (((cm[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu) >= a.tau16 ? 1u : 0u) << e;
-    }
-    // the flags must be final (so X has arrived) before more weight loads
-    // are issued: an empty asm that consumes them and orders memory
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) asm volatile("" ::"v"(fm[j]) : "memory");
-    if (tid * 4 < rows) *reinterpret_cast<float4*>(&sm.sw[tid * 4]) = sw4;
-    issue_part(id0, ring[0], 0, G1);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // ---- activation side, recomputed per workgroup, from registers.
-    // Row absmax over the non-outlier columns: mask the outlier halves, then
-    // a packed max tree, one conversion to float per row.
-    float rmax[TMAX];
-#pragma unroll
-    for (int t = 0; t < TMAX; ++t) {
-        uint32_t m = 0u;
-#pragma unroll
+    int o = 0, opad = 0;   // outlier count (and, precomputed mode, its padded value)
+    if constexpr (!PRE) {
+        // X: rows t >= T re-read row T-1: a repeated row changes neither the
+        // column maxima nor anything used later (rows >= T of Xq and xo are never
+        // read), and unconditional loads keep the wait counts exact.
+        uint4 xr[CPT][TMAX];
+    #pragma unroll
+        for (int j = 0; j < CPT; ++j)
+    #pragma unroll
+            for (int t = 0; t < TMAX; ++t)
+                xr[j][t] = *reinterpret_cast<const uint4*>(a.x + (int64_t)(t < T ? t : T - 1) * K +
+                                                           (tid + kThreads * j) * 8);
+        // Magnitudes as fp16 bit patterns: for non-negative halves the unsigned
+        // order is the numeric order (fp16 and bf16 alike), so |x| >= tau <=>
+        // bits(|x|) >= tau16, with tau16 the bits of the smallest 16-bit value
+        // >= tau (+inf when none is finite).
+        // Column maxima over the T rows by packed unsigned 16-bit max.
+        uint32_t fm[CPT];
+    #pragma unroll
         for (int j = 0; j < CPT; ++j) {
-            const uint32_t w[4] = {xr[j][t].x, xr[j][t].y, xr[j][t].z, xr[j][t].w};
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const uint32_t keep = (((fm[j] >> (2 * d)) & 1u) ? 0u : 0x0000FFFFu) |
-                                      (((fm[j] >> (2 * d + 1)) & 1u) ? 0u : 0xFFFF0000u);
-                m = pk_max_u16(m, w[d] & 0x7FFF7FFFu & keep);
+            uint32_t cm[4] = {0u, 0u, 0u, 0u};
+    #pragma unroll
+            for (int t = 0; t < TMAX; ++t) {
+                const uint32_t w[4] = {xr[j][t].x, xr[j][t].y, xr[j][t].z, xr[j][t].w};
+    #pragma unroll
+                for (int d = 0; d < 4; ++d) cm[d] = pk_max_u16(cm[d], w[d] & 0x7FFF7FFFu);
             }
+            fm[j] = 0;
+    #pragma unroll
+            for (int e = 0; e < 8; ++e)
+                fm[j] |= (((cm[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu) >= a.tau16 ? 1u : 0u) << e;
         }
-        const uint32_t mh = (m & 0xFFFFu) > (m >> 16) ? (m & 0xFFFFu) : (m >> 16);
-        rmax[t] = h16_to_f32<HT>((uint16_t)mh);
-    }
-    // Row maxima over the wave by a transposed butterfly: each exchange at
-    // distance d = 32, 16, ... halves the rows a lane carries (it keeps the
-    // half picked by its lane bit d and sends the other half); plain
-    // exchanges then finish the one row left.  Lane l ends with the maximum
-    // of row l / (64 / TMAX): log2(64) + TMAX - 1 exchanges instead of
-    // log2(64) per row.
-    {
-        float v[TMAX];
-#pragma unroll
-        for (int t = 0; t < TMAX; ++t) v[t] = rmax[t];
-#pragma unroll
-        for (int cnt = TMAX, d = 32; cnt > 1; cnt >>= 1, d >>= 1) {
-            const bool up = (lane & d) != 0;
-#pragma unroll
-            for (int i = 0; i < cnt / 2; ++i) {
-                const float send = up ? v[i] : v[i + cnt / 2];
-                const float keep = up ? v[i + cnt / 2] : v[i];
-                v[i] = __builtin_fmaxf(keep, __shfl_xor(send, d));
-            }
-        }
-#pragma unroll
-        for (int d = 32 / TMAX; d >= 1; d >>= 1) v[0] = __builtin_fmaxf(v[0], __shfl_xor(v[0], d));
-        const int r = lane / (64 / TMAX);
-        if (lane % (64 / TMAX) == 0 && r < T) sm.wmax[wave][r] = v[0];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    issue_part(id0, ring[0], G1, G2);
-    __builtin_amdgcn_sched_barrier(0);
-    // positions of the outliers: prefix count over the chunk order
-    int pc[CPT];
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-        const int cnt = __builtin_popcount(fm[j]);
-        int incl = cnt;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const int v = __shfl_up(incl, d);
-            if (lane >= d) incl += v;
-        }
-        if (lane == 63) sm.wtot[j * kWaves + wave] = incl;
-        pc[j] = incl - cnt;
-    }
-    __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
-    issue_part(id0, ring[0], G2, G3);
-    __builtin_amdgcn_sched_barrier(0);
-    if (tid < T) {
-        float v = sm.wmax[0][tid];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) v = __builtin_fmaxf(v, sm.wmax[w][tid]);
-        sm.sx[tid] = v;
-        sm.rx[tid] = v > 0.0f ? 127.0f / v : 0.0f;   // IEEE fp32 divide
-    }
-    int o = 0;
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-        int before = o;
-        for (int w = 0; w < kWaves; ++w) {
-            const int tot = sm.wtot[j * kWaves + w];
-            if (w < wave) before += tot;
-            o += tot;
-        }
-        pc[j] += before;
-    }
-    __syncthreads();   // sx, rx ready
-    __builtin_amdgcn_sched_barrier(0);
-    issue_part(id0, ring[0], G3, kLoads);
-    __builtin_amdgcn_sched_barrier(0);
-    // Quantize the owned columns into LDS and gather the outliers.
-    // q = rint(x * r) by the 1.5 * 2^23 addition: for |p| < 2^22, p + 1.5*2^23
-    // rounds p to the nearest integer (ties to even) and the low byte of the
-    // result's bit pattern is that integer as int8.  |x| <= s_x makes
-    // |p| <= 127 * (1 + 2^-23), so q is within [-127, 127] without a clamp.
-    // The product and the add stay separate roundings: p = fma(x, r, +0) is
-    // the fp32 product x * r rounded once (one mixed fp16/fp32 instruction),
-    // then the add rounds again.  Bytes are packed with v_perm.
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-        const int c = tid + kThreads * j;
-        // byte mask that zeroes the outlier columns of the piece
-        uint32_t keep[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            keep[h] = 0u;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                keep[h] |= ((fm[j] >> (4 * h + e)) & 1u) ? 0u : (0xFFu << (8 * e));
-        }
-#pragma unroll
+        // the flags must be final (so X has arrived) before more weight loads
+        // are issued: an empty asm that consumes them and orders memory
+    #pragma unroll
+        for (int j = 0; j < CPT; ++j) asm volatile("" ::"v"(fm[j]) : "memory");
+        if (tid * 4 < rows) *reinterpret_cast<float4*>(&sm.sw[tid * 4]) = sw4;
+        issue_part(id0, ring[0], 0, G1);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- activation side, recomputed per workgroup, from registers.
+        // Row absmax over the non-outlier columns: mask the outlier halves, then
+        // a packed max tree, one conversion to float per row.
+        float rmax[TMAX];
+    #pragma unroll
         for (int t = 0; t < TMAX; ++t) {
-            const float rr = t < T ? sm.rx[t] : 0.0f;
-            uint32_t f[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float p = __builtin_fmaf(chunk_val<HT>(xr[j][t], e), rr, 0.0f);
-                f[e] = __builtin_bit_cast(uint32_t, __fadd_rn(p, 12582912.0f));
+            uint32_t m = 0u;
+    #pragma unroll
+            for (int j = 0; j < CPT; ++j) {
+                const uint32_t w[4] = {xr[j][t].x, xr[j][t].y, xr[j][t].z, xr[j][t].w};
+    #pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const uint32_t keep = (((fm[j] >> (2 * d)) & 1u) ? 0u : 0x0000FFFFu) |
+                                          (((fm[j] >> (2 * d + 1)) & 1u) ? 0u : 0xFFFF0000u);
+                    m = pk_max_u16(m, w[d] & 0x7FFF7FFFu & keep);
+                }
             }
-            uint32_t packed[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const uint32_t lo = __builtin_amdgcn_perm(f[4 * h + 1], f[4 * h], 0x0c0c0400u);
-                const uint32_t hi = __builtin_amdgcn_perm(f[4 * h + 3], f[4 * h + 2], 0x0c0c0400u);
-                packed[h] = __builtin_amdgcn_perm(hi, lo, 0x05040100u) & keep[h];
-            }
-            *reinterpret_cast<uint2*>(&sm.xq[t * ldx + c * 8]) = make_uint2(packed[0], packed[1]);
+            const uint32_t mh = (m & 0xFFFFu) > (m >> 16) ? (m & 0xFFFFu) : (m >> 16);
+            rmax[t] = h16_to_f32<HT>((uint16_t)mh);
         }
-        if (fm[j]) {
-            int pos = pc[j];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                if ((fm[j] >> e) & 1u) {
-                    sm.idx[pos] = c * 8 + e;
-                    if (blockIdx.x == 0 && a.dbg_idx) a.dbg_idx[pos] = c * 8 + e;
-                    if (pos < kMaxOutliersLds) {
-#pragma unroll
-                        for (int t = 0; t < TMAX; ++t)
-                            sm.xo[t * kMaxOutliersLds + pos] = chunk_val<HT>(xr[j][t], e);
+        // Row maxima over the wave by a transposed butterfly: each exchange at
+        // distance d = 32, 16, ... halves the rows a lane carries (it keeps the
+        // half picked by its lane bit d and sends the other half); plain
+        // exchanges then finish the one row left.  Lane l ends with the maximum
+        // of row l / (64 / TMAX): log2(64) + TMAX - 1 exchanges instead of
+        // log2(64) per row.
+        {
+            float v[TMAX];
+    #pragma unroll
+            for (int t = 0; t < TMAX; ++t) v[t] = rmax[t];
+    #pragma unroll
+            for (int cnt = TMAX, d = 32; cnt > 1; cnt >>= 1, d >>= 1) {
+                const bool up = (lane & d) != 0;
+    #pragma unroll
+                for (int i = 0; i < cnt / 2; ++i) {
+                    const float send = up ? v[i] : v[i + cnt / 2];
+                    const float keep = up ? v[i + cnt / 2] : v[i];
+                    v[i] = __builtin_fmaxf(keep, __shfl_xor(send, d));
+                }
+            }
+    #pragma unroll
+            for (int d = 32 / TMAX; d >= 1; d >>= 1) v[0] = __builtin_fmaxf(v[0], __shfl_xor(v[0], d));
+            const int r = lane / (64 / TMAX);
+            if (lane % (64 / TMAX) == 0 && r < T) sm.wmax[wave][r] = v[0];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        issue_part(id0, ring[0], G1, G2);
+        __builtin_amdgcn_sched_barrier(0);
+        // positions of the outliers: prefix count over the chunk order
+        int pc[CPT];
+    #pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            const int cnt = __builtin_popcount(fm[j]);
+            int incl = cnt;
+    #pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int v = __shfl_up(incl, d);
+                if (lane >= d) incl += v;
+            }
+            if (lane == 63) sm.wtot[j * kWaves + wave] = incl;
+            pc[j] = incl - cnt;
+        }
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        issue_part(id0, ring[0], G2, G3);
+        __builtin_amdgcn_sched_barrier(0);
+        if (tid < T) {
+            float v = sm.wmax[0][tid];
+    #pragma unroll
+            for (int w = 1; w < kWaves; ++w) v = __builtin_fmaxf(v, sm.wmax[w][tid]);
+            sm.sx[tid] = v;
+            sm.rx[tid] = v > 0.0f ? 127.0f / v : 0.0f;   // IEEE fp32 divide
+        }
+    #pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            int before = o;
+            for (int w = 0; w < kWaves; ++w) {
+                const int tot = sm.wtot[j * kWaves + w];
+                if (w < wave) before += tot;
+                o += tot;
+            }
+            pc[j] += before;
+        }
+        __syncthreads();   // sx, rx ready
+        __builtin_amdgcn_sched_barrier(0);
+        issue_part(id0, ring[0], G3, kLoads);
+        __builtin_amdgcn_sched_barrier(0);
+        // Quantize the owned columns into LDS and gather the outliers.
+        // q = rint(x * r) by the 1.5 * 2^23 addition: for |p| < 2^22, p + 1.5*2^23
+        // rounds p to the nearest integer (ties to even) and the low byte of the
+        // result's bit pattern is that integer as int8.  |x| <= s_x makes
+        // |p| <= 127 * (1 + 2^-23), so q is within [-127, 127] without a clamp.
+        // The product and the add stay separate roundings: p = fma(x, r, +0) is
+        // the fp32 product x * r rounded once (one mixed fp16/fp32 instruction),
+        // then the add rounds again.  Bytes are packed with v_perm.
+    #pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            const int c = tid + kThreads * j;
+            // byte mask that zeroes the outlier columns of the piece
+            uint32_t keep[2];
+    #pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                keep[h] = 0u;
+    #pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    keep[h] |= ((fm[j] >> (4 * h + e)) & 1u) ? 0u : (0xFFu << (8 * e));
+            }
+    #pragma unroll
+            for (int t = 0; t < TMAX; ++t) {
+                const float rr = t < T ? sm.rx[t] : 0.0f;
+                uint32_t f[8];
+    #pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float p = __builtin_fmaf(chunk_val<HT>(xr[j][t], e), rr, 0.0f);
+                    f[e] = __builtin_bit_cast(uint32_t, __fadd_rn(p, 12582912.0f));
+                }
+                uint32_t packed[2];
+    #pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t lo = __builtin_amdgcn_perm(f[4 * h + 1], f[4 * h], 0x0c0c0400u);
+                    const uint32_t hi = __builtin_amdgcn_perm(f[4 * h + 3], f[4 * h + 2], 0x0c0c0400u);
+                    packed[h] = __builtin_amdgcn_perm(hi, lo, 0x05040100u) & keep[h];
+                }
+                *reinterpret_cast<uint2*>(&sm.xq[t * ldx + c * 8]) = make_uint2(packed[0], packed[1]);
+            }
+            if (fm[j]) {
+                int pos = pc[j];
+    #pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    if ((fm[j] >> e) & 1u) {
+                        sm.idx[pos] = c * 8 + e;
+                        if (blockIdx.x == 0 && a.dbg_idx) a.dbg_idx[pos] = c * 8 + e;
+                        if (pos < OXL) {
+    #pragma unroll
+                            for (int t = 0; t < TMAX; ++t)
+                                sm.xo[t * OXL + pos] = chunk_val<HT>(xr[j][t], e);
+                        }
+                        ++pos;
                     }
-                    ++pos;
                 }
             }
         }
-    }
-    // number of outliers before each 1024-column chunk: the thread owning the
-    // first 8-column piece of chunk cc knows it (its prefix count)
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-        const int c8 = tid + kThreads * j;
-        if ((c8 & (kChunkK / 8 - 1)) == 0) sm.cfirst[c8 / (kChunkK / 8)] = pc[j];
-    }
-    if (tid == 0) sm.cfirst[K / kChunkK] = o;
-    if (blockIdx.x == 0 && tid == 0 && a.dbg_count) a.dbg_count[0] = o;
-    if (blockIdx.x == 0 && a.dbg_sx && tid < T) a.dbg_sx[tid] = sm.sx[tid];
-    __syncthreads();   // Xq, idx, xo ready
-    if (blockIdx.x == 0 && a.dbg_xq) {
-        for (int i = tid; i < T * (K / 8); i += kThreads) {
-            const int t = i / (K / 8), c8 = (i % (K / 8)) * 8;
-            *reinterpret_cast<uint2*>(a.dbg_xq + (int64_t)t * K + c8) =
-                *reinterpret_cast<const uint2*>(&sm.xq[t * ldx + c8]);
+        // number of outliers before each 1024-column chunk: the thread owning the
+        // first 8-column piece of chunk cc knows it (its prefix count)
+    #pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            const int c8 = tid + kThreads * j;
+            if ((c8 & (kChunkK / 8 - 1)) == 0) sm.cfirst[c8 / (kChunkK / 8)] = pc[j];
         }
+        if (tid == 0) sm.cfirst[K / kChunkK] = o;
+        if (blockIdx.x == 0 && tid == 0 && a.dbg_count) a.dbg_count[0] = o;
+        if (blockIdx.x == 0 && a.dbg_sx && tid < T) a.dbg_sx[tid] = sm.sx[tid];
+        __syncthreads();   // Xq, idx, xo ready
+        if (blockIdx.x == 0 && a.dbg_xq) {
+            for (int i = tid; i < T * (K / 8); i += kThreads) {
+                const int t = i / (K / 8), c8 = (i % (K / 8)) * 8;
+                *reinterpret_cast<uint2*>(a.dbg_xq + (int64_t)t * K + c8) =
+                    *reinterpret_cast<const uint2*>(&sm.xq[t * ldx + c8]);
+            }
+        }
+    } else {
+        // Activation side from the workspace of the activation-pass kernels:
+        // Xq rows into LDS, the row scales, the first outliers' dimensions
+        // and X values, and per 1024-column chunk how many of those first
+        // outliers precede it.  Xq (L2-resident) goes out first, all of it at
+        // once, then the first weight chunk, so that waiting for Xq leaves
+        // the weight loads in flight.
+        o = a.count_pre[0];
+        opad = a.count_pre[1];
+        constexpr int XV = kMaxXKPre / 16 / kThreads;   // 16-byte pieces per thread
+        const int nx = T * (K / 16);
+        uint4 xv[XV];
+#pragma unroll
+        for (int u = 0; u < XV; ++u) {
+            const int i = tid + kThreads * u;
+            xv[u] = i < nx ? *reinterpret_cast<const uint4*>(a.xq_pre + (int64_t)i * 16)
+                           : make_uint4(0u, 0u, 0u, 0u);
+        }
+        issue(id0, ring[0]);
+        if (tid * 4 < rows) *reinterpret_cast<float4*>(&sm.sw[tid * 4]) = sw4;
+        if (tid < T) sm.sx[tid] = a.sx_pre[tid];
+        if (tid < kW16Cache) sm.idx[tid] = tid < o ? a.idx_pre[tid] : 0;
+        for (int e = tid; e < T * OXL; e += kThreads) {
+            const int t = e / OXL, j = e - t * OXL;
+            sm.xo[t * OXL + j] = j < o ? h16_to_f32<HT>(a.xo_pre[(int64_t)t * opad + j]) : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < XV; ++u) {
+            const int i = tid + kThreads * u;
+            if (i < nx) {
+                const int t = i / (K / 16), c = i - t * (K / 16);
+                *reinterpret_cast<uint4*>(&sm.xq[t * ldx + c * 16]) = xv[u];
+            }
+        }
+        __syncthreads();   // the first outliers' dimensions are in LDS
+        // cfirst[c] counts only the first kW16Cache outliers, the only ones
+        // whose Int8 codes are picked out of the weight stream
+        const int lim = o < kW16Cache ? o : kW16Cache;
+        for (int c = tid; c <= cpb; c += kThreads) {
+            int before = 0;
+            for (int j = 0; j < lim; ++j) before += sm.idx[j] < c * kChunkK ? 1 : 0;
+            sm.cfirst[c] = before;
+        }
+        __syncthreads();   // Xq, idx, xo, cfirst ready
     }
     // W16 values of the first outliers for the workgroup's rows, fetched now
     // (idx is complete only after the barrier above) so that the end of the
@@ -414,14 +488,14 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
         if (id >= total) return total;
         int nid = 0;
         if (lane == 0) nid = atomicAdd(&sm.next, 1);
-        const int8_t* xk = xrow + (id % CPB) * kChunkK;
+        const int8_t* xk = xrow + (id % cpb) * kChunkK;
         v4i acc = {0, 0, 0, 0};
 #pragma unroll
         for (int i = 0; i < kLoads; ++i) {
             const v4i xb = tcol < T ? *reinterpret_cast<const v4i*>(xk + i * 64) : v4i{0, 0, 0, 0};
             acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(buf[i], xb, acc, 0, 0, 0);
         }
-        int32_t* d = accrow + (id / CPB) * (kRows * 16);
+        int32_t* d = accrow + (id / cpb) * (kRows * 16);
 #pragma unroll
         for (int v = 0; v < 4; ++v) atomicAdd(d + v * 16, acc[v]);
         if (recover) {
@@ -429,7 +503,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
             // and 1024 columns; copy the codes of the outlier columns in it
             // (the first kW16Cache outliers) to LDS.  Column k sits in load
             // (k / 64) % 16, on lanes 16 ((k / 16) % 4) + row, byte k % 16.
-            const int c = id % CPB;
+            const int c = id % cpb;
             const int jhi = sm.cfirst[c + 1] < kW16Cache ? sm.cfirst[c + 1] : kW16Cache;
             for (int j = sm.cfirst[c]; j < jhi; ++j) {
                 const int k = sm.idx[j] - c * kChunkK;
@@ -440,7 +514,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
                 const int b = k & 15;
                 const int dw = (b >> 2) == 0 ? v[0] : (b >> 2) == 1 ? v[1] : (b >> 2) == 2 ? v[2] : v[3];
                 if ((lane >> 4) == ((k >> 4) & 3))
-                    sm.wqo[j][(id / CPB) * kRows + (lane & 15)] = (int8_t)(dw >> (8 * (b & 3)));
+                    sm.wqo[j][(id / cpb) * kRows + (lane & 15)] = (int8_t)(dw >> (8 * (b & 3)));
             }
         }
         return __builtin_amdgcn_readfirstlane(nid);
@@ -476,19 +550,20 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
         if (!recover) {
             for (int j = 0; j < oc; ++j) {
                 const uint32_t pr = sm.w16o[j][r >> 1];
-                y += sm.xo[t * kMaxOutliersLds + j] *
+                y += sm.xo[t * OXL + j] *
                      h16_to_f32<HT>((uint16_t)((r & 1) ? pr >> 16 : pr & 0xFFFFu));
             }
         } else {
             const float dr = sm.sw[r] / 127.0f;
             for (int j = 0; j < oc; ++j)
-                y += sm.xo[t * kMaxOutliersLds + j] *
+                y += sm.xo[t * OXL + j] *
                      h16_to_f32<HT>(recover_weight<HT>(sm.wqo[j][r], dr));
         }
         for (int j = oc; j < o; ++j) {
-            const int k = sm.idx[j];
-            const float xv = j < kMaxOutliersLds ? sm.xo[t * kMaxOutliersLds + j]
-                                                 : h16_to_f32<HT>(a.x[(int64_t)t * K + k]);
+            const int k = PRE ? a.idx_pre[j] : sm.idx[j];
+            const float xv = j < OXL ? sm.xo[t * OXL + j]
+                             : PRE ? h16_to_f32<HT>(a.xo_pre[(int64_t)t * opad + j])
+                                   : h16_to_f32<HT>(a.x[(int64_t)t * K + k]);
             const uint16_t w = recover ? recover_weight<HT>(a.wq[(int64_t)n * K + k], sm.sw[r] / 127.0f)
                                        : a.w16[(int64_t)k * N + n];
             y += xv * h16_to_f32<HT>(w);
@@ -550,8 +625,9 @@ hipError_t launch_decode(const uint16_t* X, int ht, int64_t T, int64_t K, const 
     // CU the grid grows instead.
     const int64_t nblocks = ceil_div(N, kRows);
     const int bpw = (int)std::min<int64_t>(kMaxBpw, std::max<int64_t>(1, ceil_div(nblocks, device_cus())));
-    DecodeArgs a{X, Wq, sw, W16, Y, tau, tau_to_h16_ceil(tau, ht),
-                 (int)T, (int)K, (int)N, bpw, dbg_count, dbg_idx, dbg_xq, dbg_sx, dbg_acc};
+    DecodeArgs a{X, Wq, sw, W16, Y, tau, tau_to_h16_ceil(tau, ht), (int)T, (int)K, (int)N, bpw,
+                 (int)(K / kChunkK), nullptr, nullptr, nullptr, nullptr, nullptr,
+                 dbg_count, dbg_idx, dbg_xq, dbg_sx, dbg_acc};
     const unsigned grid = (unsigned)ceil_div(nblocks, bpw);
     if (K != 4096 && K != 8192) return hipErrorInvalidValue;
     if (ht == kHalfBF16) {
@@ -561,6 +637,28 @@ hipError_t launch_decode(const uint16_t* X, int ht, int64_t T, int64_t K, const 
         if (K == 4096) hipLaunchKernelGGL((k_decode<4, kHalfF16>), dim3(grid), dim3(kThreads), 0, stream, a);
         else hipLaunchKernelGGL((k_decode<8, kHalfF16>), dim3(grid), dim3(kThreads), 0, stream, a);
     }
+    return hipGetLastError();
+}
+
+bool decode_pre_supported(int64_t T, int64_t K, int64_t N) {
+    (void)N;
+    return T >= 1 && T <= kMaxT && K % kChunkK == 0 && T * K <= kMaxXKPre;
+}
+
+hipError_t launch_decode_pre(int ht, int64_t T, int64_t K, const int8_t* Wq, const float* sw,
+                             const uint16_t* W16, int64_t N, uint16_t* Y, const Workspace& ws,
+                             int32_t* dbg_acc, hipStream_t stream) {
+    if (!decode_pre_supported(T, K, N)) return hipErrorInvalidValue;
+    const int64_t nblocks = ceil_div(N, kRows);
+    const int bpw = (int)std::min<int64_t>(kMaxBpw, std::max<int64_t>(1, ceil_div(nblocks, device_cus())));
+    DecodeArgs a{nullptr, Wq, sw, W16, Y, 0.0f, 0u, (int)T, (int)K, (int)N, bpw,
+                 (int)(K / kChunkK), ws.xq, ws.sx, ws.count, ws.idx, ws.xo,
+                 nullptr, nullptr, nullptr, nullptr, dbg_acc};
+    const unsigned grid = (unsigned)ceil_div(nblocks, bpw);
+    if (ht == kHalfBF16)
+        hipLaunchKernelGGL((k_decode<0, kHalfBF16, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((k_decode<0, kHalfF16, true>), dim3(grid), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -100,6 +100,7 @@ def run_bf16(mm, name, X16, W16, tau, halved=False, big=None, rows=None):
     (70, 1024, 136, 0, 0.0, False), (2, 4096, 136, 0, 0.0, False),       # tau = 0
     (65, 320, 96, 4, float("inf"), False),                               # tau = inf
     (300, 24576, 520, 3, 6.0, True),                                     # K split in two
+    (16, 8192, 520, 5, 6.0, False), (8, 12288, 264, 30, 6.0, True),      # decode, precomputed
 ])
 def test_bf16_path(mm, T, K, N, nd, tau, halved):
     X, W = synth.random_case(60_000 + T + K + N + nd, T, K, N, n_dims=nd)

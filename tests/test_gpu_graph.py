@@ -18,7 +18,8 @@ def mm():
     return mm
 
 
-@pytest.mark.parametrize("T,K,N", [(8, 8192, 1040), (300, 1024, 520), (300, 24576, 520)])
+@pytest.mark.parametrize("T,K,N", [(8, 8192, 1040), (300, 1024, 520), (300, 24576, 520),
+                                   (16, 8192, 1040)])
 def test_graph_replays_match_eager(mm, T, K, N):
     print(f"[case] graph replay {T}x{K}x{N}", flush=True)
     X, W = synth.random_case(40_000 + T, T, K, N, n_dims=3)

@@ -131,6 +131,21 @@ def test_decode_path(mm, T, K, N, nd, tau):
     run_case(mm, f"decode path {T}x{K}x{N} tau={tau}", X, W, tau)
 
 
+@pytest.mark.parametrize("T,K,N,nd,tau,halved", [
+    (16, 8192, 1000, 6, 6.0, False), (16, 8192, 1000, 6, 6.0, True),   # T*K = 128 KB
+    (12, 5120, 520, 3, 6.0, False),                                    # K = 5 x 1024
+    (8, 12288, 1000, 40, 6.0, False), (8, 12288, 264, 40, 6.0, True),  # o > 16
+    (4, 16384, 264, 100, 6.0, False),                                  # o > 64: X from the workspace
+    (1, 1024, 8, 0, 0.0, False), (1, 1024, 8, 0, 0.0, True),           # every dimension an outlier
+])
+def test_decode_precomputed(mm, T, K, N, nd, tau, halved):
+    """Few rows off the single-kernel path: the activation-pass kernels, then
+    the decode kernel's weight stream with the activation side read from the
+    workspace."""
+    X, W = synth.random_case(32_000 + T + K + N + nd, T, K, N, n_dims=nd)
+    run_case(mm, f"decode (precomputed) {T}x{K}x{N} tau={tau}", X, W, tau, halved=halved)
+
+
 @pytest.mark.parametrize("T,K,N,nd,tau", [
     (37, 80, 200, 2, 6.0), (300, 1040, 520, 3, 6.0),          # staged kernels
     (257, 2048, 1000, 70, 6.0), (129, 64, 8, 1, 6.0),          # large-tile kernel
@@ -187,7 +202,8 @@ def test_largest_k(mm):
     assert acc[0, 0] == 127 * 127 * K and acc[1, 0] == -127 * 127 * K
 
 
-@pytest.mark.parametrize("T,K,N1,N2", [(96, 512, 264, 136), (300, 24576, 520, 264)])
+@pytest.mark.parametrize("T,K,N1,N2", [(96, 512, 264, 136), (300, 24576, 520, 264),
+                                       (16, 8192, 1000, 264)])
 def test_staged_entry_points_match(mm, T, K, N1, N2):
     # the second shape runs the matmul with K split in two halves
     X, W = synth.random_case(24, T, K, N1, n_dims=3)
