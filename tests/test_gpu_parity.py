@@ -114,6 +114,10 @@ def test_tiny_config(mm):
     # K split in two halves (K >= 24576 and few tiles): ragged T and N, and
     # 200 outliers through the second half's epilogue
     (300, 24576, 520, 3, "normal"), (129, 24576, 264, 200, "laplace"),
+    # the mid-size-T tiles (32x128x256, 64x128x256, 64x128x128) with K not a
+    # multiple of their k-tile, and T = 130 (K % 64 != 0) on 128x128x64
+    (32, 1040, 264, 4, "normal"), (50, 1296, 520, 3, "laplace"), (100, 1104, 392, 5, "normal"),
+    (128, 2064, 136, 2, "normal"), (130, 1040, 264, 3, "laplace"),
 ])
 def test_ragged_shapes(mm, T, K, N, nd, dist):
     X, W = synth.random_case(10_000 + T + K + N, T, K, N, n_dims=nd, x_dist=dist)
