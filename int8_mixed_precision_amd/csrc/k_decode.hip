@@ -53,7 +53,8 @@ constexpr int kMaxT = 16;
 constexpr int kMaxK = 8192;
 constexpr int kMaxXK = 65536;          // T*K bytes of Xq kept in LDS
 constexpr int kMaxOutliersLds = 256;   // outlier values cached in LDS
-constexpr int kMaxBpw = 8;             // 16-row blocks per workgroup
+constexpr int kMaxBpw = 12;            // 16-row blocks per workgroup (N <= 49152 in one round)
+constexpr int kSmallBpw = 8;           // LDS sized for at most this many in the common case
 constexpr int kW16Cache = 16;          // outliers whose W16 values are staged in LDS
 constexpr int kChunkKConst = 1024;     // k covered by one weight chunk
 
@@ -67,7 +68,7 @@ struct DecodeArgs {
     float tau;
     uint32_t tau16;         // bits of the smallest 16-bit value >= tau (+inf if none finite)
     int T, K, N;
-    int bpw;                // 16-row blocks per workgroup (1..8)
+    int bpw;                // 16-row blocks per workgroup (1..kMaxBpw)
     int cpb;                // K / 1024 (used when the chunk count is not a template constant)
     // activation side computed beforehand by the activation-pass kernels
     // (precomputed mode only): Xq [T,K], s_x [T], count {o, opad}, idx [o],
@@ -88,17 +89,17 @@ struct DecodeArgs {
 // Xq rows carry a 16-byte pad: the B-operand read has 16 lanes on 16
 // different rows, which then fall on distinct banks.
 // XK: bytes of Xq; IDXN: outlier dimensions kept; OXL: outliers whose X
-// values are kept; NCF: entries of cfirst.
-template <int XK, int IDXN, int OXL, int NCF>
+// values are kept; NCF: entries of cfirst; MAXB: 16-row blocks per workgroup.
+template <int XK, int IDXN, int OXL, int NCF, int MAXB>
 struct SmemT {
     int8_t xq[XK + kMaxT * 16];
     int32_t idx[IDXN];                         // outlier dims, ascending
     float xo[kMaxT * OXL];                     // X values of the first outliers
-    int32_t acc[kMaxBpw][kRows][16];           // int32 sums [block][row][t]
-    uint32_t w16o[kW16Cache][kMaxBpw * kRows / 2];   // W16[idx_j, n] pairs of the rows
-    int8_t wqo[kW16Cache][kMaxBpw * kRows];    // Wq[n, idx_j] (memory-halved variant)
+    int32_t acc[MAXB][kRows][16];              // int32 sums [block][row][t]
+    uint32_t w16o[kW16Cache][MAXB * kRows / 2];   // W16[idx_j, n] pairs of the rows
+    int8_t wqo[kW16Cache][MAXB * kRows];       // Wq[n, idx_j] (memory-halved variant)
     int32_t cfirst[NCF];                       // first outlier at or past k = 1024 c
-    float sw[kMaxBpw * kRows];                 // s_w of the rows
+    float sw[MAXB * kRows];                    // s_w of the rows
     float wmax[kWaves][kMaxT];
     float sx[kMaxT];
     float rx[kMaxT];                           // 127 / s_x (0 when s_x = 0)
@@ -106,14 +107,15 @@ struct SmemT {
     int32_t next;                              // next chunk to hand out
 };
 // activation side computed in the kernel: every outlier dimension in LDS
-using Smem = SmemT<kMaxXK, kMaxK, kMaxOutliersLds, kMaxK / kChunkKConst + 1>;
-static_assert(sizeof(Smem::acc) == kThreads * 16, "one 16-byte clear per thread");
+template <int MAXB>
+using Smem = SmemT<kMaxXK, kMaxK, kMaxOutliersLds, kMaxK / kChunkKConst + 1, MAXB>;
 // activation side precomputed: twice the Xq room, only the first outliers
 constexpr int kMaxXKPre = 131072;              // T*K bytes of Xq kept in LDS
 constexpr int kOutliersLdsPre = 64;
 constexpr int kMaxCpbPre = kMaxXKPre / kChunkKConst;
-using SmemPre = SmemT<kMaxXKPre, kW16Cache, kOutliersLdsPre, kMaxCpbPre + 1>;
-static_assert(sizeof(SmemPre) <= 160 * 1024, "LDS of one workgroup");
+template <int MAXB>
+using SmemPre = SmemT<kMaxXKPre, kW16Cache, kOutliersLdsPre, kMaxCpbPre + 1, MAXB>;
+static_assert(sizeof(SmemPre<kMaxBpw>) <= 160 * 1024, "LDS of one workgroup");
 
 // Packed unsigned max of two pairs of 16-bit lanes.
 __device__ inline uint32_t pk_max_u16(uint32_t a, uint32_t b) {
@@ -139,13 +141,21 @@ static_assert(kChunkK == kChunkKConst, "chunk size");
 // PRE: the activation side was computed by the activation-pass kernels and
 // is read from their workspace (CPB = 0: the chunk count is a.cpb); this
 // serves T <= 16 for any K that is a multiple of 1024 with T*K <= 128 KB.
-template <int CPB, int HT, bool PRE = false>
+// MAXB: the most 16-row blocks a workgroup owns (a.bpw <= MAXB); the LDS
+// arrays per row are sized for it (kSmallBpw keeps the common case's
+// footprint and code as small as they were).
+template <int CPB, int HT, bool PRE, int MAXB>
 __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
     static_assert(PRE == (CPB == 0), "the precomputed mode takes its chunk count at run time");
+    // W16 values of the first outliers fetched per thread during the stream
+    constexpr int kW16Pairs = MAXB * kRows / 2;
+    constexpr int kW16PerThread = kW16Cache * kW16Pairs / kThreads;
+    static_assert(kW16Cache * kW16Pairs == kW16PerThread * kThreads, "whole loads per thread");
     constexpr int CPT = PRE ? 1 : CPB / 4;
     constexpr int TMAX = PRE ? 1 : 64 / CPB;
     constexpr int OXL = PRE ? kOutliersLdsPre : kMaxOutliersLds;
-    using SM = typename std::conditional<PRE, SmemPre, Smem>::type;
+    using SM = typename std::conditional<PRE, SmemPre<MAXB>, Smem<MAXB>>::type;
+    static_assert(sizeof(SM::acc) % 16 == 0, "cleared in 16-byte pieces");
     __shared__ __attribute__((aligned(16))) SM sm;
     const int cpb = PRE ? a.cpb : CPB;
     const int tid = threadIdx.x;
@@ -188,7 +198,15 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
         const int n = tid * 4 < rows && n0 + tid * 4 < N ? n0 + tid * 4 : N - 4;
         sw4 = *reinterpret_cast<const float4*>(a.sw + n);
     }
-    reinterpret_cast<uint4*>(&sm.acc[0][0][0])[tid] = make_uint4(0u, 0u, 0u, 0u);
+    {
+        constexpr int kClr = (int)(sizeof(sm.acc) / 16);   // 16-byte pieces
+#pragma unroll
+        for (int i = 0; i < (kClr + kThreads - 1) / kThreads; ++i) {
+            const int q = tid + kThreads * i;
+            if (kClr % kThreads == 0 || q < kClr)
+                reinterpret_cast<uint4*>(&sm.acc[0][0][0])[q] = make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
     if (tid == 0) sm.next = 3 * kWaves;   // chunks 0 .. 23 go out statically
 
     // wave w starts with chunks w, w + 8 and w + 16; later ones come from the
@@ -452,18 +470,19 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
     }
     // W16 values of the first outliers for the workgroup's rows, fetched now
     // (idx is complete only after the barrier above) so that the end of the
-    // kernel does not wait on them: thread -> outlier slot tid / 64 + 8 h,
-    // row pair 2 (tid % 64); slots past o read the first dword of W16 (never
-    // used).
+    // kernel does not wait on them: value q = tid + 512 h is outlier slot
+    // q / kW16Pairs, row pair q % kW16Pairs; slots past o and rows past the
+    // workgroup's read the first dword of W16 (never used).
     // Without W16 (memory-halved variant) nothing is fetched: the Int8 codes
     // of the outlier columns are picked out of the weight stream itself.
-    uint32_t w16v[2] = {0u, 0u};
+    uint32_t w16v[kW16PerThread] = {};
     const bool recover = a.w16 == nullptr;
     if (!recover) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int j = (tid >> 6) + 8 * h;
-            const int r = 2 * (tid & 63);
+        for (int h = 0; h < kW16PerThread; ++h) {
+            const int q = tid + kThreads * h;
+            const int j = q / kW16Pairs;
+            const int r = 2 * (q % kW16Pairs);
             const int n = r < rows && n0 + r < N ? n0 + r : 0;
             const int64_t off = j < o ? (int64_t)sm.idx[j] * N + n : 0;
             w16v[h] = *reinterpret_cast<const uint32_t*>(a.w16 + off);
@@ -533,7 +552,10 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
     }
     if (!recover) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) sm.w16o[(tid >> 6) + 8 * h][tid & 63] = w16v[h];
+        for (int h = 0; h < kW16PerThread; ++h) {
+            const int q = tid + kThreads * h;
+            sm.w16o[q / kW16Pairs][q % kW16Pairs] = w16v[h];
+        }
     }
     __syncthreads();   // sums and W16 values (or codes) complete
 
@@ -615,14 +637,32 @@ int device_cus() {
     return cus;
 }
 
+// One instantiation per 16-bit type and LDS size (the smaller one whenever
+// the workgroup owns at most kSmallBpw blocks).
+template <int CPB, bool PRE>
+static void launch_k(int ht, const DecodeArgs& a, unsigned grid, hipStream_t stream) {
+    const bool small = a.bpw <= kSmallBpw;
+    if (ht == kHalfBF16) {
+        if (small)
+            hipLaunchKernelGGL((k_decode<CPB, kHalfBF16, PRE, kSmallBpw>), dim3(grid), dim3(kThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL((k_decode<CPB, kHalfBF16, PRE, kMaxBpw>), dim3(grid), dim3(kThreads), 0, stream, a);
+    } else {
+        if (small)
+            hipLaunchKernelGGL((k_decode<CPB, kHalfF16, PRE, kSmallBpw>), dim3(grid), dim3(kThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL((k_decode<CPB, kHalfF16, PRE, kMaxBpw>), dim3(grid), dim3(kThreads), 0, stream, a);
+    }
+}
+
 hipError_t launch_decode(const uint16_t* X, int ht, int64_t T, int64_t K, const int8_t* Wq,
                          const float* sw, const uint16_t* W16, int64_t N, float tau,
                          uint16_t* Y, int32_t* dbg_count, int32_t* dbg_idx, int8_t* dbg_xq,
                          float* dbg_sx, int32_t* dbg_acc, hipStream_t stream) {
     // One workgroup per compute unit (the LDS footprint allows no more), each
     // owning bpw whole 16-row blocks: bpw = ceil(blocks / CUs) spreads the
-    // weight evenly (N = 28672: 1792 blocks = 256 CUs x 7); past 8 blocks per
-    // CU the grid grows instead.
+    // weight evenly (N = 28672: 1792 blocks = 256 CUs x 7; N = 49152: x 12);
+    // past kMaxBpw blocks per CU the grid grows instead.
     const int64_t nblocks = ceil_div(N, kRows);
     const int bpw = (int)std::min<int64_t>(kMaxBpw, std::max<int64_t>(1, ceil_div(nblocks, device_cus())));
     DecodeArgs a{X, Wq, sw, W16, Y, tau, tau_to_h16_ceil(tau, ht), (int)T, (int)K, (int)N, bpw,
@@ -630,13 +670,8 @@ hipError_t launch_decode(const uint16_t* X, int ht, int64_t T, int64_t K, const 
                  dbg_count, dbg_idx, dbg_xq, dbg_sx, dbg_acc};
     const unsigned grid = (unsigned)ceil_div(nblocks, bpw);
     if (K != 4096 && K != 8192) return hipErrorInvalidValue;
-    if (ht == kHalfBF16) {
-        if (K == 4096) hipLaunchKernelGGL((k_decode<4, kHalfBF16>), dim3(grid), dim3(kThreads), 0, stream, a);
-        else hipLaunchKernelGGL((k_decode<8, kHalfBF16>), dim3(grid), dim3(kThreads), 0, stream, a);
-    } else {
-        if (K == 4096) hipLaunchKernelGGL((k_decode<4, kHalfF16>), dim3(grid), dim3(kThreads), 0, stream, a);
-        else hipLaunchKernelGGL((k_decode<8, kHalfF16>), dim3(grid), dim3(kThreads), 0, stream, a);
-    }
+    if (K == 4096) launch_k<4, false>(ht, a, grid, stream);
+    else launch_k<8, false>(ht, a, grid, stream);
     return hipGetLastError();
 }
 
@@ -655,10 +690,7 @@ hipError_t launch_decode_pre(int ht, int64_t T, int64_t K, const int8_t* Wq, con
                  (int)(K / kChunkK), ws.xq, ws.sx, ws.count, ws.idx, ws.xo,
                  nullptr, nullptr, nullptr, nullptr, dbg_acc};
     const unsigned grid = (unsigned)ceil_div(nblocks, bpw);
-    if (ht == kHalfBF16)
-        hipLaunchKernelGGL((k_decode<0, kHalfBF16, true>), dim3(grid), dim3(kThreads), 0, stream, a);
-    else
-        hipLaunchKernelGGL((k_decode<0, kHalfF16, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+    launch_k<0, true>(ht, a, grid, stream);
     return hipGetLastError();
 }
 

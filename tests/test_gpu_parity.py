@@ -128,6 +128,9 @@ def test_ragged_shapes(mm, T, K, N, nd, dist):
     (1, 4096, 1000, 3, 6.0), (3, 4096, 8, 0, 6.0), (8, 8192, 2056, 6, 6.0),
     (16, 4096, 520, 5, 6.0), (8, 8192, 264, 300, 6.0),   # o > 256: values read from X
     (2, 4096, 136, 0, 0.0),                              # every dimension an outlier
+    # 9 and 12 (the most) 16-row blocks per workgroup; 49160 columns: 3073
+    # blocks, one more workgroup holding a half block
+    (2, 4096, 36864, 3, 6.0), (1, 4096, 49160, 2, 6.0),
 ])
 def test_decode_path(mm, T, K, N, nd, tau):
     """Shapes on the single-kernel decode path (T <= 16, K in {4096, 8192})."""
@@ -141,6 +144,9 @@ def test_decode_path(mm, T, K, N, nd, tau):
     (8, 12288, 1000, 40, 6.0, False), (8, 12288, 264, 40, 6.0, True),  # o > 16
     (4, 16384, 264, 100, 6.0, False),                                  # o > 64: X from the workspace
     (1, 1024, 8, 0, 0.0, False), (1, 1024, 8, 0, 0.0, True),           # every dimension an outlier
+    # 12 and 10 blocks per workgroup (W16 values and codes of 192 rows)
+    (4, 1024, 49152, 5, 6.0, False), (4, 1024, 49152, 5, 6.0, True),
+    (3, 2048, 36872, 20, 6.0, False), (3, 2048, 36872, 20, 6.0, True),
 ])
 def test_decode_precomputed(mm, T, K, N, nd, tau, halved):
     """Few rows off the single-kernel path: the activation-pass kernels, then
