@@ -84,6 +84,11 @@ const char* int8mm_status_string(int status);
  * part depends on N and on the device's compute-unit count (256 when no
  * device can be queried).  A workspace at least as large as the size
  * without that part is accepted and runs the matmul without the split.
+ * For few rows with a long K (T <= 16, K a multiple of 1024, T*K > 131072)
+ * the size covers, instead of the recovered rows and the split, S slabs of
+ * int32 partial sums [S][T][N] (S = ceil(K / (1024 * floor(128 / T))) + 3,
+ * at most K / 1024): the decode kernel then streams K in slabs; without that
+ * room these shapes run through the matmul kernels.
  * bytes: host pointer, receives the size.  Errors: E_NULL, E_SHAPE. */
 int int8_mixed_matmul_workspace_size(int64_t T, int64_t K, int64_t N, size_t* bytes);
 
@@ -189,8 +194,8 @@ int int8mm_quantize_activations(const void* X, int64_t T, int64_t K, int64_t N, 
 /* Steps 3-4 on a workspace filled by int8mm_quantize_activations with the
  * same T and K.  The activation part of the workspace is only read here and
  * may be reused for any number of weights (any N the workspace size
- * covers); the recovered-rows and K-split parts (see the size query) are
- * scratch of this call, so matmuls on one workspace run one after another
+ * covers); the recovered-rows, K-split and K-slab parts (see the size
+ * query) are scratch of this call, so matmuls on one workspace run one after another
  * (one stream).  X is read only through the gathered copy in the
  * workspace.  Arguments as int8_mixed_matmul.
  * Errors: E_NULL, E_SHAPE, E_ALIGN, E_WORKSPACE, E_HIP. */

@@ -40,6 +40,9 @@ __device__ __forceinline__ uint16_t f32_to_h16(float f) {
 //   flags   u32 [kw]     bit k%32 of word k/32 set when dimension k is an outlier
 //   wprefix i32 [kw]     number of outlier dimensions before word w
 //   count   i32 [4]      count[0] = o, count[1] = o rounded up to 16
+//   segmax  f32 [nseg][16], segcnt i32 [nseg]   per 2048-column segment, the
+//           row maxima over its non-outlier columns and its outlier count
+//           (activation pass for T <= 16 only; nseg = ceil(K / 2048))
 //   idx     i32 [K]      outlier dimensions, ascending
 //   sx      f32 [T]      row scales
 //   xq      i8  [T,K]    quantized activations, outlier columns 0
@@ -51,10 +54,15 @@ __device__ __forceinline__ uint16_t f32_to_h16(float f) {
 //   ks_count i32 [tiles]            per output tile, halves finished (zeroed by the
 //                                   matmul's launch)
 //   ks_part  i32 [tiles][2][65536]  each half's int32 sums of its 256 x 256 tile
+// or, for T <= 16 with a long K (decode_split_reserve), instead of wrec and
+// the split:
+//   dpart    i32 [dslabs][T][N]     each K slab's int32 sums
 struct Workspace {
     uint32_t* flags;
     int32_t* wprefix;
     int32_t* count;
+    float* segmax;
+    int32_t* segcnt;
     int32_t* idx;
     float* sx;
     int8_t* xq;
@@ -63,6 +71,8 @@ struct Workspace {
     int64_t wrec_rows;
     int32_t* ks_count;   // NULL without the K split
     int32_t* ks_part;
+    int32_t* dpart;      // decode K slabs: int32 partial sums [dslabs][T][N], or NULL
+    int dslabs;          // slabs the dpart region holds (0 without it)
     size_t bytes;        // total bytes the layout needs
 };
 
@@ -95,10 +105,17 @@ int gemm_ksplit(int64_t T, int64_t K, int64_t N);
 // the matmul (more outliers than this: the matmul recovers them itself).
 constexpr int64_t kRecoverRows = 512;
 
+// Activation pass for few rows (T <= kSmallT): one workgroup per segment of
+// kSegCols columns holds every row of them, so it knows its outlier columns
+// without waiting for the rest of X.
+constexpr int kSmallT = 16;
+constexpr int kSegCols = 2048;
+
 // Layout of the workspace for (T, K, N) at `base` (base may be NULL to size
 // it); wrec adds the recovered-rows region, ksplit = 2 the K-split regions
-// (which need wrec).
-Workspace carve_workspace(void* base, int64_t T, int64_t K, int64_t N, bool wrec, int ksplit);
+// (which need wrec), dslabs > 0 the decode kernel's K-slab partial sums.
+Workspace carve_workspace(void* base, int64_t T, int64_t K, int64_t N, bool wrec, int ksplit,
+                          int dslabs = 0);
 
 // Recovers W^[j, n] = 16-bit(fp32(Wq[n, idx_j] * fp32(s_w[n] / 127))) for the
 // outliers j < o <= rows into out [rows, N] (nothing when o > rows).
@@ -151,6 +168,16 @@ bool decode_pre_supported(int64_t T, int64_t K, int64_t N);
 hipError_t launch_decode_pre(int ht, int64_t T, int64_t K, const int8_t* Wq, const float* sw,
                              const uint16_t* W16, int64_t N, uint16_t* Y, const Workspace& ws,
                              int32_t* dbg_acc, hipStream_t stream);
+
+// Few rows whose Xq is longer than the decode kernel keeps in LDS (T <= 16,
+// K % 1024 == 0, T*K > 128 KB): K is cut into slabs, each workgroup streams
+// one slab of its rows and writes int32 partial sums to ws.dpart, and a
+// second kernel adds them and finishes Y.  decode_split_reserve is the
+// number of slabs the workspace must hold (0: not such a shape).
+int decode_split_reserve(int64_t T, int64_t K, int64_t N);
+hipError_t launch_decode_split(int ht, int64_t T, int64_t K, const int8_t* Wq, const float* sw,
+                               const uint16_t* W16, int64_t N, uint16_t* Y, const Workspace& ws,
+                               int32_t* dbg_acc, hipStream_t stream);
 
 // ---- debug copies (k_activation.hip)
 hipError_t launch_debug_copies(const Workspace& ws, int64_t T, int64_t K, int32_t* count,

@@ -29,13 +29,17 @@ int check_tau(float tau) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? INT8MM_OK : INT8MM_E_HIP; }
 
-// Optional workspace regions in use: the recovered outlier rows of the
-// memory-halved variant, then the matmul's K split (gemm_ksplit), each only
-// when the workspace is large enough for it.  The size query reserves both
-// (the split only where it applies), and every entry point decides the same
-// way from the same (T, K, N, workspace_bytes), so calls on one workspace
-// always agree on its layout.
+// Optional workspace regions in use: for few rows with a long K (decode
+// shapes whose Xq exceeds the decode kernel's LDS) the K-slab partial sums;
+// otherwise the recovered outlier rows of the memory-halved variant, then
+// the matmul's K split (gemm_ksplit); each only when the workspace is large
+// enough for it.  The size query reserves what applies, and every entry
+// point decides the same way from the same (T, K, N, workspace_bytes), so
+// calls on one workspace always agree on its layout.
 Workspace layout_for(void* base, int64_t T, int64_t K, int64_t N, size_t workspace_bytes) {
+    const int ds = decode_split_reserve(T, K, N);
+    if (ds > 0 && workspace_bytes >= carve_workspace(nullptr, T, K, N, false, 1, ds).bytes)
+        return carve_workspace(base, T, K, N, false, 1, ds);
     const bool wrec = workspace_bytes >= carve_workspace(nullptr, T, K, N, true, 1).bytes;
     const int ks = wrec && gemm_ksplit(T, K, N) == 2 &&
                            workspace_bytes >= carve_workspace(nullptr, T, K, N, true, 2).bytes
@@ -45,14 +49,17 @@ Workspace layout_for(void* base, int64_t T, int64_t K, int64_t N, size_t workspa
 }
 
 // Steps 3-4 on a prepared workspace.  Few rows (T <= 16) stream the weight
-// through the decode kernel's precomputed mode; otherwise the GEMM runs, and
-// without W16 (memory-halved variant) the outlier rows are first recovered
-// into the workspace when it has room.
+// through the decode kernel's precomputed mode (with K slabs when Xq is long
+// and the workspace has their region); otherwise the GEMM runs, and without
+// W16 (memory-halved variant) the outlier rows are first recovered into the
+// workspace when it has room.
 int run_prepared(const Workspace& ws, int ht, int64_t T, int64_t K, const int8_t* Wq,
                  const float* sw, const uint16_t* w16, int64_t N, uint16_t* y16, int32_t* acc,
                  hipStream_t stream) {
     if (decode_pre_supported(T, K, N))
         return hip_status(launch_decode_pre(ht, T, K, Wq, sw, w16, N, y16, ws, acc, stream));
+    if (ws.dpart)
+        return hip_status(launch_decode_split(ht, T, K, Wq, sw, w16, N, y16, ws, acc, stream));
     const uint16_t* rows = w16;
     int64_t nrows = 0;
     if (!w16 && ws.wrec) {
@@ -126,9 +133,12 @@ int int8_mixed_matmul_workspace_size(int64_t T, int64_t K, int64_t N, size_t* by
     int st = check_shape(T, K, N);
     if (st) return st;
     // the single-kernel decode path uses no workspace regions beyond the
-    // fixed ones (which int8mm_quantize_activations still needs)
-    const bool gemm = !decode_path_supported(T, K, N);
-    *bytes = carve_workspace(nullptr, T, K, N, gemm, gemm ? gemm_ksplit(T, K, N) : 1).bytes;
+    // fixed ones (which int8mm_quantize_activations still needs); decode
+    // shapes with a long K take the K-slab partial sums instead of the
+    // matmul's regions
+    const int ds = decode_split_reserve(T, K, N);
+    const bool gemm = !decode_path_supported(T, K, N) && ds == 0;
+    *bytes = carve_workspace(nullptr, T, K, N, gemm, gemm ? gemm_ksplit(T, K, N) : 1, ds).bytes;
     return INT8MM_OK;
 }
 

@@ -286,11 +286,205 @@ __global__ __launch_bounds__(kQuantThreads) void k_rowquant_cached(
     if (tid == 0) sx[t] = mx;
 }
 
+// ---- activation pass for T <= kSmallT rows, two kernels over column
+// segments.  A workgroup of 256 lanes owns kSegCols = 2048 columns, a lane 8
+// of them in every row, so a column's outlier flag is the OR over the lane's
+// own rows and needs no exchange.
+
+constexpr int kSegThreads = kSegCols / 8;
+
+// Exclusive prefix sum over the workgroup (wave scan by shuffles, wave
+// totals through LDS); total receives the workgroup's sum.
+__device__ inline int block_excl_scan(int v, int* wtot, int& total) {
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+    int incl = v;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int u = __shfl_up(incl, d);
+        if (lane >= d) incl += u;
+    }
+    if (lane == kWave - 1) wtot[wv] = incl;
+    __syncthreads();
+    int before = 0;
+    total = 0;
+#pragma unroll
+    for (int w = 0; w < kSegThreads / kWave; ++w) {
+        before += w < wv ? wtot[w] : 0;
+        total += wtot[w];
+    }
+    return before + incl - v;
+}
+
+// Pass 1: the segment's outlier flags (whole bitmap words, written without
+// atomics), per row the maximum |x| over its non-outlier columns, and its
+// outlier count.
+template <int HT>
+__global__ __launch_bounds__(kSegThreads) void k_seg_scan(const uint16_t* __restrict__ X,
+                                                          int64_t T, int64_t K, float tau,
+                                                          uint32_t* __restrict__ flags,
+                                                          float* __restrict__ segmax,
+                                                          int32_t* __restrict__ segcnt) {
+    __shared__ float red[kSegThreads / kWave][kSmallT];
+    __shared__ int wtot[kSegThreads / kWave];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+    const int64_t c0 = (int64_t)blockIdx.x * kSegCols + tid * 8;
+    const bool in = c0 < K;
+    uint4 v[kSmallT];
+#pragma unroll
+    for (int t = 0; t < kSmallT; ++t)
+        if (t < T) v[t] = in ? *reinterpret_cast<const uint4*>(X + t * K + c0) : make_uint4(0u, 0u, 0u, 0u);
+    // lanes past K flag nothing (their zeros would pass |x| >= tau for tau = 0)
+    uint32_t fm = 0;
+#pragma unroll
+    for (int t = 0; t < kSmallT; ++t) {
+        if (t < T && in) {
+            const uint32_t w[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = h16_to_f32<HT>((uint16_t)(w[e >> 1] >> ((e & 1) * 16)));
+                fm |= (__builtin_fabsf(x) >= tau ? 1u : 0u) << e;
+            }
+        }
+    }
+    uint32_t word = fm << ((lane & 3) * 8);
+    word |= __shfl_xor(word, 1);
+    word |= __shfl_xor(word, 2);
+    if ((lane & 3) == 0 && in) flags[c0 >> 5] = word;
+#pragma unroll
+    for (int t = 0; t < kSmallT; ++t) {
+        if (t < T) {
+            const uint32_t w[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
+            float mx = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float a = __builtin_fabsf(h16_to_f32<HT>((uint16_t)(w[e >> 1] >> ((e & 1) * 16))));
+                mx = ((fm >> e) & 1u) ? mx : __builtin_fmaxf(mx, a);
+            }
+            mx = wave_max(mx);
+            if (lane == 0) red[wv][t] = mx;
+        }
+    }
+    int total = 0;
+    block_excl_scan(__builtin_popcount(fm), wtot, total);   // (its barrier also covers red)
+    if (tid < T) {
+        float mx = red[0][tid];
+#pragma unroll
+        for (int w = 1; w < kSegThreads / kWave; ++w) mx = __builtin_fmaxf(mx, red[w][tid]);
+        segmax[blockIdx.x * kSmallT + tid] = mx;
+    }
+    if (tid == 0) segcnt[blockIdx.x] = total;
+}
+
+// Pass 2: row scales s_x = max over the segments' maxima, outlier positions
+// = outliers of earlier segments + prefix inside this one; writes idx, the
+// quantized rows, the gathered outlier values (and, last segment, their zero
+// padding) and, from segment 0, s_x and the count.
+template <int HT>
+__global__ __launch_bounds__(kSegThreads) void k_seg_quant(
+    const uint16_t* __restrict__ X, int64_t T, int64_t K, const uint32_t* __restrict__ flags,
+    const float* __restrict__ segmax, const int32_t* __restrict__ segcnt, int32_t* __restrict__ idx,
+    int32_t* __restrict__ count, int8_t* __restrict__ xq, float* __restrict__ sx,
+    uint16_t* __restrict__ xo) {
+    __shared__ float red[kSegThreads / kSmallT][kSmallT];
+    __shared__ int cnt[2][kSegThreads / kSmallT];
+    __shared__ float sxs[kSmallT];
+    __shared__ int wtot[kSegThreads / kWave];
+    const int tid = threadIdx.x;
+    const int seg = blockIdx.x, nseg = gridDim.x;
+    const int64_t c0 = (int64_t)seg * kSegCols + tid * 8;
+    const bool in = c0 < K;
+    uint4 v[kSmallT];
+#pragma unroll
+    for (int t = 0; t < kSmallT; ++t)
+        if (t < T) v[t] = in ? *reinterpret_cast<const uint4*>(X + t * K + c0) : make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t fm = in ? (flags[c0 >> 5] >> ((c0 >> 3) & 3) * 8) & 0xFFu : 0u;
+    // the segments' maxima and counts, 16 partial reductions per row
+    {
+        const int t = tid % kSmallT, part = tid / kSmallT;
+        float mx = 0.0f;
+        int before = 0, all = 0;
+        for (int s = part; s < nseg; s += kSegThreads / kSmallT) {
+            if (t < T) mx = __builtin_fmaxf(mx, segmax[s * kSmallT + t]);
+            const int c = segcnt[s];
+            before += s < seg ? c : 0;
+            all += c;
+        }
+        red[part][t] = mx;
+        if (t == 0) {
+            cnt[0][part] = before;
+            cnt[1][part] = all;
+        }
+    }
+    __syncthreads();
+    if (tid < kSmallT) {
+        float mx = red[0][tid];
+#pragma unroll
+        for (int p = 1; p < kSegThreads / kSmallT; ++p) mx = __builtin_fmaxf(mx, red[p][tid]);
+        sxs[tid] = mx;
+    }
+    int before = 0, o = 0;
+#pragma unroll
+    for (int p = 0; p < kSegThreads / kSmallT; ++p) {
+        before += cnt[0][p];
+        o += cnt[1][p];
+    }
+    const int opad = (o + 15) & ~15;
+    int seg_total = 0;
+    const int pos0 = before + block_excl_scan(__builtin_popcount(fm), wtot, seg_total);   // barrier: sxs ready
+    if (seg == 0 && tid == 0) {
+        count[0] = o;
+        count[1] = opad;
+    }
+    if (seg == 0 && tid < T) sx[tid] = sxs[tid];
+    if (seg == nseg - 1)
+        for (int64_t e = tid; e < T * (opad - o); e += kSegThreads) {
+            const int64_t t = e / (opad - o), j = o + e % (opad - o);
+            xo[t * opad + j] = 0;   // +0 in both types
+        }
+    if (!in) return;
+    if (fm) {
+        int pos = pos0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if ((fm >> e) & 1u) idx[pos++] = (int32_t)(c0 + e);
+    }
+#pragma unroll
+    for (int t = 0; t < kSmallT; ++t) {
+        if (t < T) {
+            const float mx = sxs[t];
+            const float r = mx > 0.0f ? 127.0f / mx : 0.0f;
+            const uint32_t w[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
+            uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = h16_to_f32<HT>((uint16_t)(w[e >> 1] >> ((e & 1) * 16)));
+                const uint32_t q = ((fm >> e) & 1u) ? 0u : (uint32_t)(uint8_t)quant(x, r);
+                packed[e >> 2] |= q << ((e & 3) * 8);
+            }
+            *reinterpret_cast<uint2*>(xq + t * K + c0) = make_uint2(packed[0], packed[1]);
+            if (fm) {
+                int pos = pos0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if ((fm >> e) & 1u) xo[t * opad + pos++] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
+            }
+        }
+    }
+}
+
 }  // namespace
 
 template <int HT>
 static void launch_activation_typed(const uint16_t* xb, int64_t T, int64_t K, float tau,
                              const Workspace& ws, hipStream_t stream) {
+    if (T <= kSmallT) {
+        const dim3 grid((unsigned)ceil_div(K, kSegCols));
+        hipLaunchKernelGGL(k_seg_scan<HT>, grid, dim3(kSegThreads), 0, stream, xb, T, K, tau,
+                           ws.flags, ws.segmax, ws.segcnt);
+        hipLaunchKernelGGL(k_seg_quant<HT>, grid, dim3(kSegThreads), 0, stream, xb, T, K, ws.flags,
+                           ws.segmax, ws.segcnt, ws.idx, ws.count, ws.xq, ws.sx, ws.xo);
+        return;
+    }
     const int64_t kw = ceil_div(K, 32);
     int clear_blocks = (int)ceil_div(kw > 4 ? kw : 4, 256);
     hipLaunchKernelGGL(k_clear, dim3(clear_blocks), dim3(256), 0, stream, ws.flags, kw, ws.count);
@@ -332,7 +526,8 @@ hipError_t launch_debug_copies(const Workspace& ws, int64_t T, int64_t K, int32_
     return e;
 }
 
-Workspace carve_workspace(void* base, int64_t T, int64_t K, int64_t N, bool wrec, int ksplit) {
+Workspace carve_workspace(void* base, int64_t T, int64_t K, int64_t N, bool wrec, int ksplit,
+                          int dslabs) {
     Workspace w{};
     const int64_t kw = ceil_div(K, 32);
     size_t off = 0;
@@ -345,6 +540,9 @@ Workspace carve_workspace(void* base, int64_t T, int64_t K, int64_t N, bool wrec
     w.flags = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)kw));
     w.wprefix = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)kw));
     w.count = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * 4));
+    const int64_t nseg = ceil_div(K, kSegCols);
+    w.segmax = reinterpret_cast<float*>(take(sizeof(float) * (size_t)(nseg * kSmallT)));
+    w.segcnt = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)nseg));
     w.idx = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)K));
     w.sx = reinterpret_cast<float*>(take(sizeof(float) * (size_t)T));
     w.xq = reinterpret_cast<int8_t*>(take((size_t)T * (size_t)K));
@@ -362,6 +560,10 @@ Workspace carve_workspace(void* base, int64_t T, int64_t K, int64_t N, bool wrec
         const int64_t tiles = ceil_div(T, 256) * ceil_div(N, 256);
         w.ks_count = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)tiles));
         w.ks_part = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)tiles * 2 * 65536));
+    }
+    if (dslabs > 0) {
+        w.dslabs = dslabs;
+        w.dpart = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)dslabs * (size_t)T * (size_t)N));
     }
     w.bytes = off;
     return w;

@@ -78,6 +78,13 @@ struct DecodeArgs {
     const int32_t* count_pre;
     const int32_t* idx_pre;
     const uint16_t* xo_pre;
+    // K slabs (precomputed mode): the grid is slabs x groups of bpw blocks,
+    // slab s covers k-chunks s*cps .. (at most cps of them, cpb in all); with
+    // slabs > 1 each workgroup writes its int32 sums to part [slabs][T][N]
+    // and k_decode_finish completes Y
+    int slabs;
+    int cps;
+    int32_t* part;
     // optional debug outputs (NULL to skip); workgroup 0 writes all but acc
     int32_t* dbg_count;
     int32_t* dbg_idx;
@@ -157,17 +164,24 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
     using SM = typename std::conditional<PRE, SmemPre<MAXB>, Smem<MAXB>>::type;
     static_assert(sizeof(SM::acc) % 16 == 0, "cleared in 16-byte pieces");
     __shared__ __attribute__((aligned(16))) SM sm;
-    const int cpb = PRE ? a.cpb : CPB;
+    // slab and block group of this workgroup (slab-major grid)
+    const int groups = PRE ? (int)gridDim.x / a.slabs : (int)gridDim.x;
+    const int slab = PRE ? (int)blockIdx.x / groups : 0;
+    const int grp = (int)blockIdx.x - slab * groups;
+    // k-chunks of this workgroup's slab (all of K without slabs) and the
+    // slab's first k
+    const int cpb = PRE ? (a.cpb - slab * a.cps < a.cps ? a.cpb - slab * a.cps : a.cps) : CPB;
+    const int kbase = PRE ? slab * a.cps * kChunkK : 0;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     // wave-uniform (a scalar), so the chunk loop below is uniform control flow
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int T = a.T, K = a.K, N = a.N;
-    const int ldx = K + 16;                    // LDS row stride of Xq
+    const int ldx = cpb * kChunkK + 16;        // LDS row stride of Xq (the slab's k)
     const int nblocks = (N + kRows - 1) / kRows;
     // this workgroup's weight rows n0 .. n0 + rows - 1 (rows past N are read
     // as row N-1 and never stored); chunk id -> block id / cpb, k-chunk id % cpb
-    const int b0 = blockIdx.x * a.bpw;
+    const int b0 = grp * a.bpw;
     const int nbw = a.bpw < nblocks - b0 ? a.bpw : nblocks - b0;
     const int rows = nbw * kRows;
     const int n0 = b0 * kRows;
@@ -183,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
     auto issue_part = [&](int id, v4i (&buf)[kLoads], int lo, int hi) {
         const int n = n0 + (id / cpb) * kRows + (lane & 15);
         const int64_t off =
-            id < total ? (int64_t)(n < N ? n : N - 1) * K + (id % cpb) * kChunkK + kl : 0;
+            id < total ? (int64_t)(n < N ? n : N - 1) * K + kbase + (id % cpb) * kChunkK + kl : 0;
         const int8_t* p = a.wq + off;
 #pragma unroll
         for (int i = 0; i < kLoads; ++i)
@@ -433,12 +447,14 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
         o = a.count_pre[0];
         opad = a.count_pre[1];
         constexpr int XV = kMaxXKPre / 16 / kThreads;   // 16-byte pieces per thread
-        const int nx = T * (K / 16);
+        const int pr = cpb * (kChunkK / 16);            // pieces per row of the slab
+        const int nx = T * pr;
         uint4 xv[XV];
 #pragma unroll
         for (int u = 0; u < XV; ++u) {
             const int i = tid + kThreads * u;
-            xv[u] = i < nx ? *reinterpret_cast<const uint4*>(a.xq_pre + (int64_t)i * 16)
+            const int t = i / pr, c = i - t * pr;
+            xv[u] = i < nx ? *reinterpret_cast<const uint4*>(a.xq_pre + (int64_t)t * K + kbase + c * 16)
                            : make_uint4(0u, 0u, 0u, 0u);
         }
         issue(id0, ring[0]);
@@ -453,7 +469,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
         for (int u = 0; u < XV; ++u) {
             const int i = tid + kThreads * u;
             if (i < nx) {
-                const int t = i / (K / 16), c = i - t * (K / 16);
+                const int t = i / pr, c = i - t * pr;
                 *reinterpret_cast<uint4*>(&sm.xq[t * ldx + c * 16]) = xv[u];
             }
         }
@@ -463,7 +479,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
         const int lim = o < kW16Cache ? o : kW16Cache;
         for (int c = tid; c <= cpb; c += kThreads) {
             int before = 0;
-            for (int j = 0; j < lim; ++j) before += sm.idx[j] < c * kChunkK ? 1 : 0;
+            for (int j = 0; j < lim; ++j) before += sm.idx[j] < kbase + c * kChunkK ? 1 : 0;
             sm.cfirst[c] = before;
         }
         __syncthreads();   // Xq, idx, xo, cfirst ready
@@ -477,7 +493,9 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
     // of the outlier columns are picked out of the weight stream itself.
     uint32_t w16v[kW16PerThread] = {};
     const bool recover = a.w16 == nullptr;
-    if (!recover) {
+    // with K slabs the outlier terms are added by k_decode_finish
+    const bool split = PRE && a.slabs > 1;
+    if (!recover && !split) {
 #pragma unroll
         for (int h = 0; h < kW16PerThread; ++h) {
             const int q = tid + kThreads * h;
@@ -517,7 +535,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
         int32_t* d = accrow + (id / cpb) * (kRows * 16);
 #pragma unroll
         for (int v = 0; v < 4; ++v) atomicAdd(d + v * 16, acc[v]);
-        if (recover) {
+        if (recover && !split) {
             // memory-halved variant: the chunk holds Wq[n, k] for its 16 rows
             // and 1024 columns; copy the codes of the outlier columns in it
             // (the first kW16Cache outliers) to LDS.  Column k sits in load
@@ -525,7 +543,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
             const int c = id % cpb;
             const int jhi = sm.cfirst[c + 1] < kW16Cache ? sm.cfirst[c + 1] : kW16Cache;
             for (int j = sm.cfirst[c]; j < jhi; ++j) {
-                const int k = sm.idx[j] - c * kChunkK;
+                const int k = sm.idx[j] - kbase - c * kChunkK;
                 const int ii = k >> 6;
                 v4i v = buf[0];
 #pragma unroll
@@ -550,7 +568,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
             issue(id2, ring[2]);
         } while (id0 < total);
     }
-    if (!recover) {
+    if (!recover && !split) {
 #pragma unroll
         for (int h = 0; h < kW16PerThread; ++h) {
             const int q = tid + kThreads * h;
@@ -558,6 +576,17 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
         }
     }
     __syncthreads();   // sums and W16 values (or codes) complete
+    if constexpr (PRE) {
+        if (split) {
+            // this slab's int32 sums of the workgroup's rows
+            for (int e = tid; e < rows * T; e += kThreads) {
+                const int r = e % rows, t = e / rows;
+                const int n = n0 + r;
+                if (n < N) a.part[((int64_t)slab * T + t) * N + n] = sm.acc[r >> 4][r & 15][t];
+            }
+            return;
+        }
+    }
 
     // ---- epilogue: y = acc * s_x * s_w / 127^2 + sum_j X[t, idx_j] W16[idx_j, n],
     // one fp16 rounding; consecutive threads take consecutive rows n.
@@ -592,6 +621,41 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
         }
         a.y[(int64_t)t * N + n] = f32_to_h16<HT>(y);
     }
+}
+
+// Completes a call whose K was cut into slabs: acc = the sum of the slabs'
+// int32 partial sums (exact, in any order), then the decode kernel's
+// epilogue, y = acc * s_x * s_w / 127^2 + sum_j X[t, idx_j] W16[idx_j, n]
+// rounded once.  One thread per output (t, n): grid (N / 256, T), so the
+// partial sums are read coalesced along n and enough workgroups are in
+// flight to hide their latency; the W16 rows (or, memory-halved variant,
+// the Int8 codes the weight is recovered from) are read once per t, from
+// L2 after the first.
+template <int HT>
+__global__ __launch_bounds__(256) void k_decode_finish(DecodeArgs a) {
+    const int n = blockIdx.x * 256 + threadIdx.x;
+    const int t = blockIdx.y;
+    const int T = a.T, K = a.K, N = a.N;
+    if (n >= N) return;
+    const int o = a.count_pre[0], opad = a.count_pre[1];
+    const float swn = a.sw[n];
+    const bool recover = a.w16 == nullptr;
+    const float dr = swn / 127.0f;
+    const int32_t* p = a.part + (int64_t)t * N + n;
+    const int64_t sstride = (int64_t)T * N;
+    int32_t acc = 0;
+#pragma unroll 4
+    for (int sl = 0; sl < a.slabs; ++sl) acc += p[sl * sstride];
+    if (a.dbg_acc) a.dbg_acc[(int64_t)t * N + n] = acc;
+    float y = (float)acc * a.sx_pre[t] * (swn * (1.0f / 16129.0f));
+    const uint16_t* xo = a.xo_pre + (int64_t)t * opad;
+    for (int j = 0; j < o; ++j) {
+        const int k = a.idx_pre[j];
+        const uint16_t w = recover ? recover_weight<HT>(a.wq[(int64_t)n * K + k], dr)
+                                   : a.w16[(int64_t)k * N + n];
+        y += h16_to_f32<HT>(xo[j]) * h16_to_f32<HT>(w);
+    }
+    a.y[(int64_t)t * N + n] = f32_to_h16<HT>(y);
 }
 
 }  // namespace
@@ -667,6 +731,7 @@ hipError_t launch_decode(const uint16_t* X, int ht, int64_t T, int64_t K, const 
     const int bpw = (int)std::min<int64_t>(kMaxBpw, std::max<int64_t>(1, ceil_div(nblocks, device_cus())));
     DecodeArgs a{X, Wq, sw, W16, Y, tau, tau_to_h16_ceil(tau, ht), (int)T, (int)K, (int)N, bpw,
                  (int)(K / kChunkK), nullptr, nullptr, nullptr, nullptr, nullptr,
+                 1, (int)(K / kChunkK), nullptr,
                  dbg_count, dbg_idx, dbg_xq, dbg_sx, dbg_acc};
     const unsigned grid = (unsigned)ceil_div(nblocks, bpw);
     if (K != 4096 && K != 8192) return hipErrorInvalidValue;
@@ -688,9 +753,72 @@ hipError_t launch_decode_pre(int ht, int64_t T, int64_t K, const int8_t* Wq, con
     const int bpw = (int)std::min<int64_t>(kMaxBpw, std::max<int64_t>(1, ceil_div(nblocks, device_cus())));
     DecodeArgs a{nullptr, Wq, sw, W16, Y, 0.0f, 0u, (int)T, (int)K, (int)N, bpw,
                  (int)(K / kChunkK), ws.xq, ws.sx, ws.count, ws.idx, ws.xo,
+                 1, (int)(K / kChunkK), nullptr,
                  nullptr, nullptr, nullptr, nullptr, dbg_acc};
     const unsigned grid = (unsigned)ceil_div(nblocks, bpw);
     launch_k<0, true>(ht, a, grid, stream);
+    return hipGetLastError();
+}
+
+// K slabs for T <= 16 rows whose Xq exceeds the LDS room: at least
+// smin = ceil(chunks / most chunks per slab) slabs; up to three more are
+// tried, each with bpw = the blocks per workgroup that fill the chip once,
+// and the one with the least weight per compute unit (rounds of the grid x
+// the rows and k of one workgroup) wins.  The workspace holds smin + 3.
+namespace {
+struct SlabPlan {
+    int slabs, cps, bpw;
+};
+int split_smin(int64_t T, int64_t K) {
+    const int64_t chunks = K / kChunkK;
+    const int64_t per = kMaxXKPre / (T * kChunkK);   // >= 8 for T <= 16
+    return (int)ceil_div(chunks, per);
+}
+SlabPlan plan_slabs(int64_t T, int64_t K, int64_t N, int reserve) {
+    const int64_t chunks = K / kChunkK;
+    const int64_t nblocks = ceil_div(N, kRows);
+    const int64_t cus = device_cus();
+    SlabPlan best{0, 0, 0};
+    int64_t best_cost = 0;
+    for (int s = split_smin(T, K); s <= reserve; ++s) {
+        const int64_t cps = ceil_div(chunks, s);
+        const int64_t se = ceil_div(chunks, cps);   // slabs actually used
+        const int64_t bpw = std::min<int64_t>(kMaxBpw, std::max<int64_t>(1, ceil_div(nblocks * se, cus)));
+        const int64_t grid = ceil_div(nblocks, bpw) * se;
+        const int64_t cost = ceil_div(grid, cus) * bpw * cps;
+        if (best.slabs == 0 || cost < best_cost) {
+            best = SlabPlan{(int)se, (int)cps, (int)bpw};
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+}  // namespace
+
+int decode_split_reserve(int64_t T, int64_t K, int64_t N) {
+    (void)N;
+    if (!(T >= 1 && T <= kMaxT && K % kChunkK == 0 && T * K > kMaxXKPre)) return 0;
+    return (int)std::min<int64_t>(split_smin(T, K) + 3, K / kChunkK);
+}
+
+hipError_t launch_decode_split(int ht, int64_t T, int64_t K, const int8_t* Wq, const float* sw,
+                               const uint16_t* W16, int64_t N, uint16_t* Y, const Workspace& ws,
+                               int32_t* dbg_acc, hipStream_t stream) {
+    const int reserve = decode_split_reserve(T, K, N);
+    if (reserve == 0 || !ws.dpart || ws.dslabs < reserve) return hipErrorInvalidValue;
+    const SlabPlan p = plan_slabs(T, K, N, reserve);
+    const int64_t nblocks = ceil_div(N, kRows);
+    DecodeArgs a{nullptr, Wq, sw, W16, Y, 0.0f, 0u, (int)T, (int)K, (int)N, p.bpw,
+                 (int)(K / kChunkK), ws.xq, ws.sx, ws.count, ws.idx, ws.xo,
+                 p.slabs, p.cps, ws.dpart,
+                 nullptr, nullptr, nullptr, nullptr, dbg_acc};
+    const unsigned grid = (unsigned)(ceil_div(nblocks, p.bpw) * p.slabs);
+    launch_k<0, true>(ht, a, grid, stream);
+    const dim3 fgrid((unsigned)ceil_div(N, 256), (unsigned)T);
+    if (ht == kHalfBF16)
+        hipLaunchKernelGGL(k_decode_finish<kHalfBF16>, fgrid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(k_decode_finish<kHalfF16>, fgrid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

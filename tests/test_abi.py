@@ -63,6 +63,19 @@ def test_workspace_size(mm):
     assert t4096 < 3 * 4096 * 49152 + 2 * 512 * 12288 + (1 << 20)
     # decode shapes run as one kernel and need only the fixed regions
     assert mm.workspace_size(8, 8192, 28672) < 3 * 8 * 8192 + (1 << 16)
+    # few rows with a long K: S = ceil(48 / 16) + 3 = 6 slabs of int32
+    # partial sums [S][T][N] in place of the recovered rows
+    fixed = 3 * 8 * 49152 + 4 * 49152 + 49152 // 4    # + idx, flags and prefixes
+    dec_down = mm.workspace_size(8, 49152, 12288)
+    assert fixed + 6 * 8 * 12288 * 4 <= dec_down < fixed + 6 * 8 * 12288 * 4 + (1 << 16)
+    # T = 16: 8 chunks per slab, K = 12288 and 9216: S = 2 + 3
+    assert mm.workspace_size(16, 12288, 1000) >= 3 * 16 * 12288 + 5 * 16 * 1000 * 4
+    ws9 = mm.workspace_size(16, 9216, 264)
+    assert 3 * 16 * 9216 + 5 * 16 * 264 * 4 <= ws9 < 3 * 16 * 9216 + 5 * 16 * 264 * 4 + (1 << 16)
+    # T * K <= 128 KB (precomputed mode without slabs) and K not a multiple of
+    # 1024 keep the matmul's regions
+    assert mm.workspace_size(16, 8192, 1000) >= 3 * 16 * 8192 + 2 * 512 * 1000
+    assert mm.workspace_size(8, 49168, 1000) >= 3 * 8 * 49168 + 2 * 512 * 1000
     with pytest.raises(mm.Int8mmError) as e:
         mm.workspace_size(16, 60, 48)
     assert e.value.status == mm.E_SHAPE

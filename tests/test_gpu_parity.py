@@ -212,8 +212,35 @@ def test_largest_k(mm):
     assert acc[0, 0] == 127 * 127 * K and acc[1, 0] == -127 * 127 * K
 
 
+def test_largest_accumulator_in_slabs(mm):
+    """The same extreme accumulators with K = 130 x 1024 on the decode
+    kernel's K slabs: every slab's partial sum and their total exact."""
+    K = 133120
+    X = np.ones((3, K), np.float16)
+    X[1] = -1
+    W = np.full((K, 16), 0.125, np.float16)
+    r, _ = run_case(mm, "largest K in slabs", X, W, 6.0)
+    acc = r["acc"].cpu().numpy()
+    assert acc[0, 0] == 127 * 127 * K and acc[1, 0] == -127 * 127 * K
+
+
+@pytest.mark.parametrize("T,K,N,nd,tau,halved", [
+    (8, 49152, 1000, 10, 6.0, False), (8, 49152, 264, 10, 6.0, True),   # 48 chunks, >= 3 slabs
+    (16, 12288, 1000, 20, 6.0, False),                                  # 12 chunks, >= 2 slabs
+    (16, 9216, 520, 3, 6.0, True),                                      # slabs of unequal length
+    (12, 12288, 1032, 5, 6.0, False),                                   # half a block at the end
+    (1, 133120, 8, 2, 6.0, False),                                      # the longest K in slabs
+    (9, 16384, 136, 0, 0.0, False),                                     # every dimension an outlier
+])
+def test_decode_slabs(mm, T, K, N, nd, tau, halved):
+    """Few rows whose Xq exceeds the decode kernel's LDS: K streamed in slabs
+    by separate workgroups, partial sums added by a second kernel."""
+    X, W = synth.random_case(34_000 + T + K + N + nd, T, K, N, n_dims=nd)
+    run_case(mm, f"decode (K slabs) {T}x{K}x{N} tau={tau}", X, W, tau, halved=halved)
+
+
 @pytest.mark.parametrize("T,K,N1,N2", [(96, 512, 264, 136), (300, 24576, 520, 264),
-                                       (16, 8192, 1000, 264)])
+                                       (16, 8192, 1000, 264), (8, 49152, 1000, 264)])
 def test_staged_entry_points_match(mm, T, K, N1, N2):
     # the second shape runs the matmul with K split in two halves
     X, W = synth.random_case(24, T, K, N1, n_dims=3)
