@@ -292,6 +292,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_rowquant_cached(
 // own rows and needs no exchange.
 
 constexpr int kSegThreads = kSegCols / 8;
+static_assert(kSegThreads == 256 && kSmallT == 16, "row reductions: 16 rows x 16 lanes x 16 entries");
 
 // Exclusive prefix sum over the workgroup (wave scan by shuffles, wave
 // totals through LDS); total receives the workgroup's sum.
@@ -324,9 +325,9 @@ __global__ __launch_bounds__(kSegThreads) void k_seg_scan(const uint16_t* __rest
                                                           uint32_t* __restrict__ flags,
                                                           float* __restrict__ segmax,
                                                           int32_t* __restrict__ segcnt) {
-    __shared__ float red[kSegThreads / kWave][kSmallT];
+    __shared__ __attribute__((aligned(16))) float red[kSmallT][kSegThreads];
     __shared__ int wtot[kSegThreads / kWave];
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int64_t c0 = (int64_t)blockIdx.x * kSegCols + tid * 8;
     const bool in = c0 < K;
     uint4 v[kSmallT];
@@ -360,17 +361,28 @@ __global__ __launch_bounds__(kSegThreads) void k_seg_scan(const uint16_t* __rest
                 const float a = __builtin_fabsf(h16_to_f32<HT>((uint16_t)(w[e >> 1] >> ((e & 1) * 16))));
                 mx = ((fm >> e) & 1u) ? mx : __builtin_fmaxf(mx, a);
             }
-            mx = wave_max(mx);
-            if (lane == 0) red[wv][t] = mx;
+            red[t][tid] = mx;
         }
     }
     int total = 0;
     block_excl_scan(__builtin_popcount(fm), wtot, total);   // (its barrier also covers red)
-    if (tid < T) {
-        float mx = red[0][tid];
+    // row t = tid / 16: each of 16 lanes takes the maximum of 16 entries,
+    // then 4 exchanges inside the group of 16 lanes (instead of a 6-step
+    // wave reduction per row)
+    {
+        const int t = tid >> 4, part = tid & 15;
+        float mx = 0.0f;
+        if (t < T) {
+            const float4* q = reinterpret_cast<const float4*>(&red[t][part * 16]);
 #pragma unroll
-        for (int w = 1; w < kSegThreads / kWave; ++w) mx = __builtin_fmaxf(mx, red[w][tid]);
-        segmax[blockIdx.x * kSmallT + tid] = mx;
+            for (int i = 0; i < 4; ++i) {
+                const float4 f = q[i];
+                mx = __builtin_fmaxf(mx, __builtin_fmaxf(__builtin_fmaxf(f.x, f.y), __builtin_fmaxf(f.z, f.w)));
+            }
+        }
+#pragma unroll
+        for (int d = 8; d >= 1; d >>= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, d));
+        if (part == 0 && t < T) segmax[blockIdx.x * kSmallT + t] = mx;
     }
     if (tid == 0) segcnt[blockIdx.x] = total;
 }
