@@ -713,6 +713,133 @@ __global__ __launch_bounds__(128 * WN) void k_gemm_i8_big(GemmArgs a) {
         StageCtx{lds, tid, m0, n0, sxs, sx_pre, sw_pre, o_pre, opad_pre});
 }
 
+// XOR swizzle of the eight 16-byte chunks of a 128-byte LDS row (streaming
+// kernel): 8 consecutive rows land on 8 distinct chunks, and rows r and r+8
+// on different chunks too, so a fragment read (lanes on consecutive rows at
+// one logical chunk) is free of bank conflicts for 8- and 16-lane service.
+__device__ __forceinline__ int stream_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+// Streaming kernel for few rows (T <= 128, K % 128 == 0): the matmul is bound
+// by the weight stream, so both operands go from global memory straight into
+// LDS (global_load_lds_dwordx4, no VGPR staging) through a ring of STAGES
+// k-tiles of 128, STAGES - 1 of them in flight.  One barrier per k-tile: after it every wave's copies of
+// tile kt have landed and tile kt-1 is no longer read, so its buffer takes
+// tile kt+STAGES-1.  BM x BN tile, 4 waves of (BM/WAVES_M) x (BN/WAVES_N);
+// rows past T or N are clamped to the last row (never stored).
+template <int BM, int BN, int WAVES_M, int STAGES, bool WRITE_ACC, int HT>
+__global__ __launch_bounds__(256) void k_gemm_i8_stream(GemmArgs a) {
+    constexpr int BK = 128;
+    constexpr int WAVES_N = 4 / WAVES_M;
+    constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+    constexpr int TM = WM / 32, TN = WN / 32;
+    constexpr int STAGE_BYTES = (BM + BN) * BK;
+    constexpr int GA = BM * BK / 1024, GB = BN * BK / 1024;   // 1 KB groups of A and B
+    constexpr int LOADS = (GA + GB) / 4;                      // copies per lane per tile
+    static_assert(TM >= 1 && TN >= 1 && (GA + GB) % 4 == 0, "tile shape");
+    static_assert((STAGES - 2) * LOADS <= 63 && STAGES >= 3, "wait count range");
+    __shared__ __attribute__((aligned(1024))) int8_t lds[STAGES * STAGE_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t T = a.T, K = a.K, N = a.N;
+    const int64_t MT = ceil_div(T, BM);
+    const int64_t bid = xcd_tile(blockIdx.x, gridDim.x);
+    const int64_t m0 = (bid % MT) * BM;
+    const int64_t n0 = (bid / MT) * BN;
+    const int wm0 = (wave % WAVES_M) * WM;
+    const int wn0 = (wave / WAVES_M) * WN;
+
+    // copy u of this wave fills 1 KB group g = LOADS * wave + u of the tile
+    // (g < GA: rows 8g .. 8g+7 of A, else rows 8(g - GA) .. of B); lane l
+    // writes row 8g + l/8 at physical chunk l%8, so it fetches the logical
+    // chunk (l%8) ^ stream_swz(row).  32-bit lane offsets (a 128-row panel
+    // spans at most 128 * 133144 bytes).
+    const int8_t* abase = a.xq + m0 * K;
+    const int8_t* bbase = a.wq + n0 * K;
+    uint32_t goff[LOADS];
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+        const int g = LOADS * wave + u;
+        const bool isa = g < GA;
+        const int row = (isa ? g : g - GA) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ stream_swz(row);
+        const int64_t r = isa ? (m0 + row < T ? row : T - 1 - m0) : (n0 + row < N ? row : N - 1 - n0);
+        goff[u] = (uint32_t)(r * K + c * 16);
+    }
+    auto copy = [&](int u, int kt, int stage) {
+        const int g = LOADS * wave + u;
+        const bool isa = g < GA;
+        const int8_t* base = (isa ? abase : bbase) + (int64_t)kt * BK;
+        const int8_t* dst = lds + stage * STAGE_BYTES + (isa ? g * 1024 : BM * BK + (g - GA) * 1024);
+        copy_to_lds16(base, goff[u], dst);
+    };
+
+    v16i acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+
+    // fragment offsets inside a tile for k-step 0; k-step s adds 32 s bytes
+    // of logical k, i.e. logical chunk 2 s + lane / 32
+    const int KT = (int)(K / BK);
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st)
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) copy(u, st < KT ? st : KT - 1, st);
+
+    int s_cur = 0;
+    for (int kt = 0; kt < KT; ++kt) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((STAGES - 2) * LOADS));   // this wave's part of tile kt
+        __syncthreads();                                                 // everyone's part; tile kt-1 read
+        const int s_fill = s_cur == 0 ? STAGES - 1 : s_cur - 1;
+        const int kf = kt + STAGES - 1 < KT ? kt + STAGES - 1 : KT - 1;
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) copy(u, kf, s_fill);
+        const int8_t* cur = lds + s_cur * STAGE_BYTES;
+#pragma unroll
+        for (int s = 0; s < BK / 32; ++s) {
+            const int c = s * 2 + (lane >> 5);
+            v4i af[TM], bf[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int row = wm0 + i * 32 + (lane & 31);
+                af[i] = *reinterpret_cast<const v4i*>(cur + row * BK + ((c ^ stream_swz(row)) * 16));
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int row = wn0 + j * 32 + (lane & 31);
+                bf[j] = *reinterpret_cast<const v4i*>(cur + BM * BK + row * BK + ((c ^ stream_swz(row)) * 16));
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+        }
+        s_cur = s_cur == STAGES - 1 ? 0 : s_cur + 1;
+    }
+    // the copies past the last tile went to buffers no one reads; let them
+    // land before the workgroup ends
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    epilogue<TM, TN, WRITE_ACC, HT>(acc, a, m0 + wm0, n0 + wn0, lane);
+}
+
+template <int BM, int BN, int WAVES_M, int STAGES, int HT>
+hipError_t launch_stream(const GemmArgs& a, hipStream_t stream) {
+    const int64_t tiles = ceil_div(a.T, BM) * ceil_div(a.N, BN);
+    if (a.acc_out)
+        hipLaunchKernelGGL((k_gemm_i8_stream<BM, BN, WAVES_M, STAGES, true, HT>), dim3((unsigned)tiles),
+                           dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((k_gemm_i8_stream<BM, BN, WAVES_M, STAGES, false, HT>), dim3((unsigned)tiles),
+                           dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
 template <int BM, int BN, int BK, int WAVES_M, int HT>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
     const int64_t tiles = ceil_div(a.T, BM) * ceil_div(a.N, BN);
@@ -751,13 +878,21 @@ hipError_t launch_big(const GemmArgs& a, hipStream_t stream) {
 }
 
 // Below the large-tile kernel's range the matmul streams the weight past
-// few rows of X; deeper k-tiles and narrower n-tiles keep more of that stream
-// in flight.  Measured at K=8192, N=28672 with the weight not cache resident:
-// T=32 32x128x256 54.6 us (32x256x128: 88.3), T=64 64x128x256 59.7 us
-// (128x128x64: 97.9), T=128 64x128x128 80.7 us (128x128x64: 98.3).
+// few rows of X, and the time goes to keeping enough of that stream in
+// flight.  Measured at K=8192, N=28672 with the weight not cache resident
+// (GEMM kernel alone): T=32 streaming 64x64 (4 stages: 64 KB of LDS, two
+// workgroups per CU, 448 tiles all resident at once) 48-51 us, register-
+// staged 32x128x256 55 us, 32x256x128 88 us; T=64 streaming 64x64 54 us,
+// register-staged 64x128x256 60 us, 128x128x64 98 us; T=128 streaming
+// 128x128 (3 stages) 61 us, register-staged 64x128x128 81-87 us, 128x128x64
+// 98 us.  The register-staged kernels keep the shapes with K % 128 != 0.
 template <int HT>
 hipError_t launch_gemm_typed(const GemmArgs& a, hipStream_t stream) {
     if (a.T > 128 && a.K % 64 == 0) return launch_big<4, HT>(a, stream);
+    if (a.K % 128 == 0) {
+        if (a.T <= 64) return launch_stream<64, 64, 2, 4, HT>(a, stream);
+        return launch_stream<128, 128, 2, 3, HT>(a, stream);
+    }
     if (a.T <= 32) return launch_cfg<32, 128, 256, 1, HT>(a, stream);
     if (a.T <= 64) return launch_cfg<64, 128, 256, 2, HT>(a, stream);
     if (a.T <= 128) return launch_cfg<64, 128, 128, 2, HT>(a, stream);

@@ -118,6 +118,11 @@ def test_tiny_config(mm):
     # multiple of their k-tile, and T = 130 (K % 64 != 0) on 128x128x64
     (32, 1040, 264, 4, "normal"), (50, 1296, 520, 3, "laplace"), (100, 1104, 392, 5, "normal"),
     (128, 2064, 136, 2, "normal"), (130, 1040, 264, 3, "laplace"),
+    # the streaming kernels (K % 128 == 0): 64x64 tiles up to T = 64, 128x128
+    # up to 128; one k-tile, fewer k-tiles than ring stages, ragged T and N
+    (37, 256, 200, 2, "normal"), (50, 1152, 520, 3, "laplace"), (64, 2048, 136, 1, "normal"),
+    (17, 128, 72, 1, "normal"), (100, 1280, 392, 4, "normal"), (128, 4096, 1000, 6, "laplace"),
+    (65, 384, 8, 2, "normal"),
 ])
 def test_ragged_shapes(mm, T, K, N, nd, dist):
     X, W = synth.random_case(10_000 + T + K + N, T, K, N, n_dims=nd, x_dist=dist)
