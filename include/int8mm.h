@@ -84,7 +84,8 @@ const char* int8mm_status_string(int status);
  * part depends on N and on the device's compute-unit count (256 when no
  * device can be queried).  A workspace at least as large as the size
  * without that part is accepted and runs the matmul without the split.
- * For few rows with a long K (T <= 16, K a multiple of 1024, T*K > 131072)
+ * For few rows with a long K (K a multiple of 1024, T*K > 131072, and T <= 8,
+ * or T <= 16 with K >= 32768)
  * the size covers, instead of the recovered rows and the split, S slabs of
  * int32 partial sums [S][T][N] (S = ceil(K / (1024 * floor(128 / T))) + 3,
  * at most K / 1024): the decode kernel then streams K in slabs; without that

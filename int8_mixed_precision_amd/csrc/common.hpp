@@ -54,7 +54,7 @@ __device__ __forceinline__ uint16_t f32_to_h16(float f) {
 //   ks_count i32 [tiles]            per output tile, halves finished (zeroed by the
 //                                   matmul's launch)
 //   ks_part  i32 [tiles][2][65536]  each half's int32 sums of its 256 x 256 tile
-// or, for T <= 16 with a long K (decode_split_reserve), instead of wrec and
+// or, for few rows with a long K (decode_split_reserve), instead of wrec and
 // the split:
 //   dpart    i32 [dslabs][T][N]     each K slab's int32 sums
 struct Workspace {
@@ -161,7 +161,7 @@ hipError_t launch_decode(const uint16_t* X, int ht, int64_t T, int64_t K, const 
                          uint16_t* Y, int32_t* dbg_count, int32_t* dbg_idx, int8_t* dbg_xq,
                          float* dbg_sx, int32_t* dbg_acc, hipStream_t stream);
 
-// Decode shapes the single-kernel path does not take (T <= 16, K % 1024 == 0,
+// Decode shapes the single-kernel path does not take (T <= 8, K % 1024 == 0,
 // T*K <= 128 KB): the same weight stream with the activation side read from
 // a workspace the activation pass has filled (k_decode.hip).
 bool decode_pre_supported(int64_t T, int64_t K, int64_t N);
@@ -169,8 +169,9 @@ hipError_t launch_decode_pre(int ht, int64_t T, int64_t K, const int8_t* Wq, con
                              const uint16_t* W16, int64_t N, uint16_t* Y, const Workspace& ws,
                              int32_t* dbg_acc, hipStream_t stream);
 
-// Few rows whose Xq is longer than the decode kernel keeps in LDS (T <= 16,
-// K % 1024 == 0, T*K > 128 KB): K is cut into slabs, each workgroup streams
+// Few rows whose Xq is longer than the decode kernel keeps in LDS (T <= 8,
+// or T <= 16 with K >= 32768; K % 1024 == 0, T*K > 128 KB): K is cut into
+// slabs, each workgroup streams
 // one slab of its rows and writes int32 partial sums to ws.dpart, and a
 // second kernel adds them and finishes Y.  decode_split_reserve is the
 // number of slabs the workspace must hold (0: not such a shape).

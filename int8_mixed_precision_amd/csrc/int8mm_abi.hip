@@ -48,7 +48,8 @@ Workspace layout_for(void* base, int64_t T, int64_t K, int64_t N, size_t workspa
     return carve_workspace(base, T, K, N, wrec, ks);
 }
 
-// Steps 3-4 on a prepared workspace.  Few rows (T <= 16) stream the weight
+// Steps 3-4 on a prepared workspace.  Few rows (T <= 8, or T <= 16 with a
+// long K) stream the weight
 // through the decode kernel's precomputed mode (with K slabs when Xq is long
 // and the workspace has their region); otherwise the GEMM runs, and without
 // W16 (memory-halved variant) the outlier rows are first recovered into the

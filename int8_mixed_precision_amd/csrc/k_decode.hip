@@ -147,7 +147,8 @@ static_assert(kChunkK == kChunkKConst, "chunk size");
 // T <= TMAX = 64 / CPB rows (so T * CPT <= 16 chunks of X per thread).
 // PRE: the activation side was computed by the activation-pass kernels and
 // is read from their workspace (CPB = 0: the chunk count is a.cpb); this
-// serves T <= 16 for any K that is a multiple of 1024 with T*K <= 128 KB.
+// serves T <= 16 for any K that is a multiple of 1024 with T*K <= 128 KB
+// (the host sends it T <= 8 only, and longer K in slabs).
 // MAXB: the most 16-row blocks a workgroup owns (a.bpw <= MAXB); the LDS
 // arrays per row are sized for it (kSmallBpw keeps the common case's
 // footprint and code as small as they were).
@@ -740,9 +741,18 @@ hipError_t launch_decode(const uint16_t* X, int ht, int64_t T, int64_t K, const 
     return hipGetLastError();
 }
 
+// Which few-row shapes the decode kernel's precomputed mode takes.  Past 8
+// rows the streaming matmul kernel is faster unless K is long (measured,
+// whole calls: T=9..16 with K=8192, N=28672 2.5-4 us faster on the matmul;
+// T=12 and 16 with K=12288 and 16384 2-15 us faster; T=8..16 with K=49152,
+// N=12288 the K slabs 8-17 us faster; T=1..8 with K=12288 the precomputed
+// mode 1-5 us faster).
+constexpr int kMaxTPre = 8;                 // rows of the precomputed mode without slabs
+constexpr int64_t kSlabLongK = 32768;       // K from which 9..16 rows take the slabs
+
 bool decode_pre_supported(int64_t T, int64_t K, int64_t N) {
     (void)N;
-    return T >= 1 && T <= kMaxT && K % kChunkK == 0 && T * K <= kMaxXKPre;
+    return T >= 1 && T <= kMaxTPre && K % kChunkK == 0 && T * K <= kMaxXKPre;
 }
 
 hipError_t launch_decode_pre(int ht, int64_t T, int64_t K, const int8_t* Wq, const float* sw,
@@ -798,6 +808,7 @@ SlabPlan plan_slabs(int64_t T, int64_t K, int64_t N, int reserve) {
 int decode_split_reserve(int64_t T, int64_t K, int64_t N) {
     (void)N;
     if (!(T >= 1 && T <= kMaxT && K % kChunkK == 0 && T * K > kMaxXKPre)) return 0;
+    if (T > kMaxTPre && K < kSlabLongK) return 0;
     return (int)std::min<int64_t>(split_smin(T, K) + 3, K / kChunkK);
 }
 

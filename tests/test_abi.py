@@ -68,10 +68,14 @@ def test_workspace_size(mm):
     fixed = 3 * 8 * 49152 + 4 * 49152 + 49152 // 4    # + idx, flags and prefixes
     dec_down = mm.workspace_size(8, 49152, 12288)
     assert fixed + 6 * 8 * 12288 * 4 <= dec_down < fixed + 6 * 8 * 12288 * 4 + (1 << 16)
-    # T = 16: 8 chunks per slab, K = 12288 and 9216: S = 2 + 3
-    assert mm.workspace_size(16, 12288, 1000) >= 3 * 16 * 12288 + 5 * 16 * 1000 * 4
-    ws9 = mm.workspace_size(16, 9216, 264)
-    assert 3 * 16 * 9216 + 5 * 16 * 264 * 4 <= ws9 < 3 * 16 * 9216 + 5 * 16 * 264 * 4 + (1 << 16)
+    # T = 16 (8 chunks per slab) takes the slabs from K = 32768 on: S = 4 + 3;
+    # below that the matmul kernels run and the recovered rows are reserved
+    fixed16 = 3 * 16 * 32768 + 4 * 32768 + 32768 // 4
+    ws16 = mm.workspace_size(16, 32768, 264)
+    assert fixed16 + 7 * 16 * 264 * 4 <= ws16 < fixed16 + 7 * 16 * 264 * 4 + (1 << 16)
+    assert mm.workspace_size(16, 12288, 1000) >= 3 * 16 * 12288 + 2 * 512 * 1000
+    # T = 8, K = 24576: 16 chunks per slab, S = 2 + 3
+    assert mm.workspace_size(8, 24576, 264) >= 3 * 8 * 24576 + 5 * 8 * 264 * 4
     # T * K <= 128 KB (precomputed mode without slabs) and K not a multiple of
     # 1024 keep the matmul's regions
     assert mm.workspace_size(16, 8192, 1000) >= 3 * 16 * 8192 + 2 * 512 * 1000

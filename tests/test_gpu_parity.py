@@ -123,6 +123,8 @@ def test_tiny_config(mm):
     (37, 256, 200, 2, "normal"), (50, 1152, 520, 3, "laplace"), (64, 2048, 136, 1, "normal"),
     (17, 128, 72, 1, "normal"), (100, 1280, 392, 4, "normal"), (128, 4096, 1000, 6, "laplace"),
     (65, 384, 8, 2, "normal"),
+    # 9..16 rows go to the matmul kernels unless K is long
+    (16, 8192, 1000, 6, "normal"), (12, 5120, 520, 3, "laplace"), (16, 12288, 264, 20, "normal"),
 ])
 def test_ragged_shapes(mm, T, K, N, nd, dist):
     X, W = synth.random_case(10_000 + T + K + N, T, K, N, n_dims=nd, x_dist=dist)
@@ -144,8 +146,8 @@ def test_decode_path(mm, T, K, N, nd, tau):
 
 
 @pytest.mark.parametrize("T,K,N,nd,tau,halved", [
-    (16, 8192, 1000, 6, 6.0, False), (16, 8192, 1000, 6, 6.0, True),   # T*K = 128 KB
-    (12, 5120, 520, 3, 6.0, False),                                    # K = 5 x 1024
+    (8, 16384, 1000, 6, 6.0, False), (8, 16384, 1000, 6, 6.0, True),   # T*K = 128 KB
+    (6, 5120, 520, 3, 6.0, False),                                     # K = 5 x 1024
     (8, 12288, 1000, 40, 6.0, False), (8, 12288, 264, 40, 6.0, True),  # o > 16
     (4, 16384, 264, 100, 6.0, False),                                  # o > 64: X from the workspace
     (1, 1024, 8, 0, 0.0, False), (1, 1024, 8, 0, 0.0, True),           # every dimension an outlier
@@ -154,9 +156,9 @@ def test_decode_path(mm, T, K, N, nd, tau):
     (3, 2048, 36872, 20, 6.0, False), (3, 2048, 36872, 20, 6.0, True),
 ])
 def test_decode_precomputed(mm, T, K, N, nd, tau, halved):
-    """Few rows off the single-kernel path: the activation-pass kernels, then
-    the decode kernel's weight stream with the activation side read from the
-    workspace."""
+    """Few rows (T <= 8) off the single-kernel path: the activation-pass
+    kernels, then the decode kernel's weight stream with the activation side
+    read from the workspace."""
     X, W = synth.random_case(32_000 + T + K + N + nd, T, K, N, n_dims=nd)
     run_case(mm, f"decode (precomputed) {T}x{K}x{N} tau={tau}", X, W, tau, halved=halved)
 
@@ -231,11 +233,12 @@ def test_largest_accumulator_in_slabs(mm):
 
 @pytest.mark.parametrize("T,K,N,nd,tau,halved", [
     (8, 49152, 1000, 10, 6.0, False), (8, 49152, 264, 10, 6.0, True),   # 48 chunks, >= 3 slabs
-    (16, 12288, 1000, 20, 6.0, False),                                  # 12 chunks, >= 2 slabs
-    (16, 9216, 520, 3, 6.0, True),                                      # slabs of unequal length
-    (12, 12288, 1032, 5, 6.0, False),                                   # half a block at the end
+    (16, 32768, 1000, 20, 6.0, False),                                  # 32 chunks, >= 4 slabs
+    (12, 33792, 520, 3, 6.0, True),                                     # slabs of unequal length
+    (12, 32768, 1032, 5, 6.0, False),                                   # half a block at the end
+    (8, 24576, 264, 4, 6.0, True),                                      # 8 rows: from 16 KB of Xq on
     (1, 133120, 8, 2, 6.0, False),                                      # the longest K in slabs
-    (9, 16384, 136, 0, 0.0, False),                                     # every dimension an outlier
+    (9, 32768, 136, 0, 0.0, False),                                     # every dimension an outlier
 ])
 def test_decode_slabs(mm, T, K, N, nd, tau, halved):
     """Few rows whose Xq exceeds the decode kernel's LDS: K streamed in slabs
