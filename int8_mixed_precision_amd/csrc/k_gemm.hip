@@ -71,7 +71,10 @@ constexpr int kStageBytes = 4 * kStageHalf;   // two buffers of X and W
 constexpr int kYS = 256 * 2 + 16;             // bytes per row of the staged Y tile (padded)
 constexpr int kYBytes = 256 * kYS;            // the 256 x 256 tile of 16-bit Y values
 
-template <int TM, int TN, bool WRITE_ACC, int HT, bool STAGED = false>
+// SBN > 0 (streaming kernel, 256 threads, n-tile of SBN columns): with more
+// than 16 outliers the outlier W rows go through LDS like the large-tile
+// kernel's (sc.lds, sc.tid and sc.n0 used).
+template <int TM, int TN, bool WRITE_ACC, int HT, bool STAGED = false, int SBN = 0>
 __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a, int64_t mb,
                                          int64_t nb, int lane, const StageCtx& sc = StageCtx{}) {
     const int64_t T = a.T, N = a.N;
@@ -157,11 +160,115 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a,
             for (int r = 0; r < 16; ++r) y[i][j][r] = (float)acc[i][j][r] * sxm[r] * swn[j];
     }
     if constexpr (!STAGED) {
+        int jstart = 0;   // outliers done through LDS
+        if constexpr (SBN > 0) {
+            if (opad > 16) {
+                // the W rows of 32 outliers at a time: thread (slot e, column
+                // block cb) loads its outlier's row segment (16-byte loads
+                // along n) and writes it transposed into LDS, so that a lane's
+                // 8 outliers of one column are one 16-byte read; double
+                // buffered, the next chunk's loads in flight during this
+                // chunk's MFMAs.  X values come straight from the gathered
+                // columns (16 contiguous bytes per lane).
+                constexpr int CPB = SBN / 8;              // columns per block (8 blocks)
+                constexpr int NV = CPB / 8;               // 16-byte loads per thread
+                constexpr int kWS = SBN * kOS;            // bytes of one buffer
+                static_assert(NV >= 1 && NV * 64 == SBN, "n-tile of 64 or 128 columns");
+                __syncthreads();   // the main loop's LDS reads are complete
+                const int e = sc.tid & 31, cb = sc.tid >> 5;
+                float dcol[CPB];
+                if (recover) {
+#pragma unroll
+                    for (int c = 0; c < CPB; ++c) {
+                        const int64_t n = sc.n0 + cb * CPB + c;
+                        dcol[c] = n < N ? a.sw[n] / 127.0f : 0.0f;
+                    }
+                }
+                int k_next = e < o ? (by_pos ? e : a.idx[e]) : -1;
+                uint4 wv[NV];
+                auto load_chunk = [&](int jc) {
+                    const int k = k_next;
+                    k_next = jc + kOC + e < o ? (by_pos ? jc + kOC + e : a.idx[jc + kOC + e]) : -1;
+#pragma unroll
+                    for (int h = 0; h < NV; ++h) {
+                        const int64_t n = sc.n0 + cb * CPB + h * 8;
+                        if (!recover) {
+                            wv[h] = (k >= 0 && n < N)
+                                        ? *reinterpret_cast<const uint4*>(a.w16 + (int64_t)k * N + n)
+                                        : make_uint4(0u, 0u, 0u, 0u);
+                        } else {
+                            uint32_t p[4];
+#pragma unroll
+                            for (int c = 0; c < 8; c += 2) {
+                                const int64_t nc = n + c;
+                                const uint16_t lo = (k >= 0 && nc < N)
+                                                        ? recover_weight<HT>(a.wq[nc * a.K + k], dcol[h * 8 + c])
+                                                        : (uint16_t)0;
+                                const uint16_t hi = (k >= 0 && nc + 1 < N)
+                                                        ? recover_weight<HT>(a.wq[(nc + 1) * a.K + k],
+                                                                             dcol[h * 8 + c + 1])
+                                                        : (uint16_t)0;
+                                p[c >> 1] = (uint32_t)lo | ((uint32_t)hi << 16);
+                            }
+                            wv[h] = make_uint4(p[0], p[1], p[2], p[3]);
+                        }
+                    }
+                };
+                auto store_chunk = [&](int buf) {
+                    int8_t* ws = sc.lds + buf * kWS;
+#pragma unroll
+                    for (int h = 0; h < NV; ++h) {
+                        const uint32_t w4[4] = {wv[h].x, wv[h].y, wv[h].z, wv[h].w};
+#pragma unroll
+                        for (int c = 0; c < 8; ++c)
+                            *reinterpret_cast<uint16_t*>(ws + (cb * CPB + h * 8 + c) * kOS + e * 2) =
+                                (uint16_t)(w4[c >> 1] >> ((c & 1) * 16));
+                    }
+                };
+                load_chunk(0);
+                for (int jc = 0; jc < opad; jc += kOC) {
+                    const int buf = (jc / kOC) & 1;
+                    store_chunk(buf);
+                    __syncthreads();
+                    if (jc + kOC < opad) load_chunk(jc + kOC);
+                    const int8_t* ws = sc.lds + buf * kWS;
+                    const int wn0 = (int)(nb - sc.n0);
+#pragma unroll
+                    for (int ks = 0; ks < kOC / 16; ++ks) {
+                        if (jc + ks * 16 >= opad) break;
+                        const int ko = ks * 32 + (lane >> 5) * 16;
+                        const int jl = jc + ks * 16 + (lane >> 5) * 8;
+                        v8u16 wb[TN];
+#pragma unroll
+                        for (int j = 0; j < TN; ++j)
+                            wb[j] = *reinterpret_cast<const v8u16*>(ws + (wn0 + j * 32 + col_l) * kOS + ko);
+#pragma unroll
+                        for (int i = 0; i < TM; ++i) {
+                            const int64_t mrow = mb + i * 32 + (lane & 31);
+                            const v8u16 xa = mrow < T ? *reinterpret_cast<const v8u16*>(a.xo + mrow * opad + jl)
+                                                      : v8u16{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+                            for (int j = 0; j < TN; ++j) {
+                                if constexpr (HT == kHalfBF16)
+                                    y[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                        __builtin_bit_cast(v8bf, xa), __builtin_bit_cast(v8bf, wb[j]),
+                                        y[i][j], 0, 0, 0);
+                                else
+                                    y[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                                        __builtin_bit_cast(v8h, xa), __builtin_bit_cast(v8h, wb[j]),
+                                        y[i][j], 0, 0, 0);
+                            }
+                        }
+                    }
+                }
+                jstart = opad;
+            }
+        }
         // 16-bit matmul over the isolated outlier dimensions, 16 at a time, with
         // the dequantized values as the fp32 C operand.  A group's weight
         // fragments (8 gathered values of one column per lane) are loaded once
         // and serve all TM row strips.
-        for (int jc = 0; jc < opad; jc += 16) {
+        for (int jc = jstart; jc < opad; jc += 16) {
             const int jl = jc + (lane >> 5) * 8;   // first of this lane's 8 outlier slots
             int kk[8];
     #pragma unroll
@@ -825,7 +932,8 @@ __global__ __launch_bounds__(256) void k_gemm_i8_stream(GemmArgs a) {
     // the copies past the last tile went to buffers no one reads; let them
     // land before the workgroup ends
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    epilogue<TM, TN, WRITE_ACC, HT>(acc, a, m0 + wm0, n0 + wn0, lane);
+    epilogue<TM, TN, WRITE_ACC, HT, false, BN>(acc, a, m0 + wm0, n0 + wn0, lane,
+                                               StageCtx{lds, tid, m0, n0, nullptr, 0.0f, nullptr, 0, 0});
 }
 
 template <int BM, int BN, int WAVES_M, int STAGES, int HT>
@@ -884,14 +992,16 @@ hipError_t launch_big(const GemmArgs& a, hipStream_t stream) {
 // workgroups per CU, 448 tiles all resident at once) 48-51 us, register-
 // staged 32x128x256 55 us, 32x256x128 88 us; T=64 streaming 64x64 54 us,
 // register-staged 64x128x256 60 us, 128x128x64 98 us; T=128 streaming
-// 128x128 (3 stages) 61 us, register-staged 64x128x128 81-87 us, 128x128x64
-// 98 us.  The register-staged kernels keep the shapes with K % 128 != 0.
+// 128x128 (4 stages) 61-63 us, register-staged 64x128x128 81-87 us,
+// 128x128x64 98 us; with 256 outliers (their W rows staged through LDS)
+// T=64 62.5 us and T=128 71 us against 114 and 128 us.  The register-staged
+// kernels keep the shapes with K % 128 != 0.
 template <int HT>
 hipError_t launch_gemm_typed(const GemmArgs& a, hipStream_t stream) {
     if (a.T > 128 && a.K % 64 == 0) return launch_big<4, HT>(a, stream);
     if (a.K % 128 == 0) {
         if (a.T <= 64) return launch_stream<64, 64, 2, 4, HT>(a, stream);
-        return launch_stream<128, 128, 2, 3, HT>(a, stream);
+        return launch_stream<128, 128, 2, 4, HT>(a, stream);
     }
     if (a.T <= 32) return launch_cfg<32, 128, 256, 1, HT>(a, stream);
     if (a.T <= 64) return launch_cfg<64, 128, 256, 2, HT>(a, stream);

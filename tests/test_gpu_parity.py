@@ -122,7 +122,7 @@ def test_tiny_config(mm):
     # up to 128; one k-tile, fewer k-tiles than ring stages, ragged T and N
     (37, 256, 200, 2, "normal"), (50, 1152, 520, 3, "laplace"), (64, 2048, 136, 1, "normal"),
     (17, 128, 72, 1, "normal"), (100, 1280, 392, 4, "normal"), (128, 4096, 1000, 6, "laplace"),
-    (65, 384, 8, 2, "normal"),
+    (65, 384, 8, 2, "normal"), (100, 2048, 264, 70, "laplace"), (64, 1024, 200, 40, "normal"),
     # 9..16 rows go to the matmul kernels unless K is long
     (16, 8192, 1000, 6, "normal"), (12, 5120, 520, 3, "laplace"), (16, 12288, 264, 20, "normal"),
 ])
@@ -171,6 +171,7 @@ def test_decode_precomputed(mm, T, K, N, nd, tau, halved):
     (70, 1024, 136, 0, 0.0), (2, 4096, 136, 0, 0.0),           # every dimension an outlier
     (257, 1024, 264, 0, 0.0),       # o = 1024 > 512: rows recovered inside the matmul
     (300, 2048, 520, 600, 6.0),     # about 600 outliers, the same
+    (64, 2048, 264, 600, 6.0), (100, 2048, 520, 40, 6.0),   # streaming kernel, W rows through LDS
 ])
 def test_memory_halved(mm, T, K, N, nd, tau):
     """W16 = NULL: outlier rows recovered from the Int8 weight."""
