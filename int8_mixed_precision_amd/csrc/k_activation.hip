@@ -318,8 +318,10 @@ __device__ inline int block_excl_scan(int v, int* wtot, int& total) {
 
 // Pass 1: the segment's outlier flags (whole bitmap words, written without
 // atomics), per row the maximum |x| over its non-outlier columns, and its
-// outlier count.
-template <int HT>
+// outlier count.  TB: T rounded up to a power of two; rows T .. TB-1 re-read
+// row T-1 (a repeated row changes no flag and no maximum), so the loads are
+// unconditional and all in flight together.
+template <int HT, int TB>
 __global__ __launch_bounds__(kSegThreads) void k_seg_scan(const uint16_t* __restrict__ X,
                                                           int64_t T, int64_t K, float tau,
                                                           uint32_t* __restrict__ flags,
@@ -330,30 +332,29 @@ __global__ __launch_bounds__(kSegThreads) void k_seg_scan(const uint16_t* __rest
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int64_t c0 = (int64_t)blockIdx.x * kSegCols + tid * 8;
     const bool in = c0 < K;
-    uint4 v[kSmallT];
+    uint4 v[TB];
+    const uint16_t* xc = X + (in ? c0 : 0);
 #pragma unroll
-    for (int t = 0; t < kSmallT; ++t)
-        if (t < T) v[t] = in ? *reinterpret_cast<const uint4*>(X + t * K + c0) : make_uint4(0u, 0u, 0u, 0u);
-    // lanes past K flag nothing (their zeros would pass |x| >= tau for tau = 0)
+    for (int t = 0; t < TB; ++t) v[t] = *reinterpret_cast<const uint4*>(xc + (t < T ? t : T - 1) * K);
     uint32_t fm = 0;
 #pragma unroll
-    for (int t = 0; t < kSmallT; ++t) {
-        if (t < T && in) {
-            const uint32_t w[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
+    for (int t = 0; t < TB; ++t) {
+        const uint32_t w[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float x = h16_to_f32<HT>((uint16_t)(w[e >> 1] >> ((e & 1) * 16)));
-                fm |= (__builtin_fabsf(x) >= tau ? 1u : 0u) << e;
-            }
+        for (int e = 0; e < 8; ++e) {
+            const float x = h16_to_f32<HT>((uint16_t)(w[e >> 1] >> ((e & 1) * 16)));
+            fm |= (__builtin_fabsf(x) >= tau ? 1u : 0u) << e;
         }
     }
+    // lanes past K (which read column 0) flag nothing
+    if (!in) fm = 0;
     uint32_t word = fm << ((lane & 3) * 8);
     word |= __shfl_xor(word, 1);
     word |= __shfl_xor(word, 2);
     if ((lane & 3) == 0 && in) flags[c0 >> 5] = word;
 #pragma unroll
-    for (int t = 0; t < kSmallT; ++t) {
-        if (t < T) {
+    for (int t = 0; t < TB; ++t) {
+        {
             const uint32_t w[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
             float mx = 0.0f;
 #pragma unroll
@@ -361,7 +362,7 @@ __global__ __launch_bounds__(kSegThreads) void k_seg_scan(const uint16_t* __rest
                 const float a = __builtin_fabsf(h16_to_f32<HT>((uint16_t)(w[e >> 1] >> ((e & 1) * 16))));
                 mx = ((fm >> e) & 1u) ? mx : __builtin_fmaxf(mx, a);
             }
-            red[t][tid] = mx;
+            red[t][tid] = in ? mx : 0.0f;
         }
     }
     int total = 0;
@@ -390,87 +391,110 @@ __global__ __launch_bounds__(kSegThreads) void k_seg_scan(const uint16_t* __rest
 // Pass 2: row scales s_x = max over the segments' maxima, outlier positions
 // = outliers of earlier segments + prefix inside this one; writes idx, the
 // quantized rows, the gathered outlier values (and, last segment, their zero
-// padding) and, from segment 0, s_x and the count.
+// padding) and, from segment 0, s_x and the count.  Grid: segments x groups
+// of kQuantRows rows (rows past T re-read row T-1 and store nothing), so the
+// quantization is spread over T / kQuantRows times more workgroups; every
+// row group recomputes the segment's prefix from the bitmap.
+constexpr int kQuantRows = 2;
 template <int HT>
 __global__ __launch_bounds__(kSegThreads) void k_seg_quant(
     const uint16_t* __restrict__ X, int64_t T, int64_t K, const uint32_t* __restrict__ flags,
     const float* __restrict__ segmax, const int32_t* __restrict__ segcnt, int32_t* __restrict__ idx,
     int32_t* __restrict__ count, int8_t* __restrict__ xq, float* __restrict__ sx,
     uint16_t* __restrict__ xo) {
-    __shared__ float red[kSegThreads / kSmallT][kSmallT];
-    __shared__ int cnt[2][kSegThreads / kSmallT];
-    __shared__ float sxs[kSmallT];
+    constexpr int RB = kQuantRows, PARTS = kSegThreads / RB;
+    __shared__ float red[PARTS][RB];
+    __shared__ int cnt[2][PARTS];
+    __shared__ float sxs[RB], rxs[RB];
     __shared__ int wtot[kSegThreads / kWave];
     const int tid = threadIdx.x;
     const int seg = blockIdx.x, nseg = gridDim.x;
+    const int t0 = blockIdx.y * RB;                // this workgroup's rows t0 .. t0+RB-1
     const int64_t c0 = (int64_t)seg * kSegCols + tid * 8;
     const bool in = c0 < K;
-    uint4 v[kSmallT];
+    uint4 v[RB];
+    const uint16_t* xc = X + (in ? c0 : 0);
 #pragma unroll
-    for (int t = 0; t < kSmallT; ++t)
-        if (t < T) v[t] = in ? *reinterpret_cast<const uint4*>(X + t * K + c0) : make_uint4(0u, 0u, 0u, 0u);
+    for (int r = 0; r < RB; ++r) v[r] = *reinterpret_cast<const uint4*>(xc + (t0 + r < T ? t0 + r : T - 1) * K);
     const uint32_t fm = in ? (flags[c0 >> 5] >> ((c0 >> 3) & 3) * 8) & 0xFFu : 0u;
-    // the segments' maxima and counts, 16 partial reductions per row
+    // the segments' maxima of the RB rows and the outlier counts: thread
+    // (row r = tid % RB, part = tid / RB) takes segments part, part + PARTS, ...
     {
-        const int t = tid % kSmallT, part = tid / kSmallT;
+        const int r = tid % RB, part = tid / RB;
+        const int t = t0 + r < T ? t0 + r : T - 1;
         float mx = 0.0f;
         int before = 0, all = 0;
-        for (int s = part; s < nseg; s += kSegThreads / kSmallT) {
-            if (t < T) mx = __builtin_fmaxf(mx, segmax[s * kSmallT + t]);
+        for (int s = part; s < nseg; s += PARTS) {
+            mx = __builtin_fmaxf(mx, segmax[s * kSmallT + t]);
             const int c = segcnt[s];
             before += s < seg ? c : 0;
             all += c;
         }
-        red[part][t] = mx;
-        if (t == 0) {
+        red[part][r] = mx;
+        if (r == 0) {
             cnt[0][part] = before;
             cnt[1][part] = all;
         }
     }
     __syncthreads();
-    if (tid < kSmallT) {
-        float mx = red[0][tid];
-#pragma unroll
-        for (int p = 1; p < kSegThreads / kSmallT; ++p) mx = __builtin_fmaxf(mx, red[p][tid]);
-        sxs[tid] = mx;
+    // row scales: RB groups of 64 lanes reduce the parts (wave-wide maximum)
+    {
+        const int r = tid / kWave, l = tid & (kWave - 1);
+        if (r < RB) {
+            float mx = 0.0f;
+            for (int p = l; p < PARTS; p += kWave) mx = __builtin_fmaxf(mx, red[p][r]);
+            mx = wave_max(mx);
+            if (l == 0) {
+                sxs[r] = mx;
+                rxs[r] = mx > 0.0f ? 127.0f / mx : 0.0f;   // IEEE fp32 divide
+            }
+        }
     }
+    // outliers before this segment, and in all: each wave sums the parts
     int before = 0, o = 0;
+    {
+        const int l = tid & (kWave - 1);
+        for (int p = l; p < PARTS; p += kWave) {
+            before += cnt[0][p];
+            o += cnt[1][p];
+        }
 #pragma unroll
-    for (int p = 0; p < kSegThreads / kSmallT; ++p) {
-        before += cnt[0][p];
-        o += cnt[1][p];
+        for (int d = 32; d >= 1; d >>= 1) {
+            before += __shfl_xor(before, d);
+            o += __shfl_xor(o, d);
+        }
     }
     const int opad = (o + 15) & ~15;
     int seg_total = 0;
-    const int pos0 = before + block_excl_scan(__builtin_popcount(fm), wtot, seg_total);   // barrier: sxs ready
-    if (seg == 0 && tid == 0) {
+    const int pos0 = before + block_excl_scan(__builtin_popcount(fm), wtot, seg_total);   // barrier: sxs, rxs ready
+    if (seg == 0 && blockIdx.y == 0 && tid == 0) {
         count[0] = o;
         count[1] = opad;
     }
-    if (seg == 0 && tid < T) sx[tid] = sxs[tid];
+    if (seg == 0 && tid < RB && t0 + tid < T) sx[t0 + tid] = sxs[tid];
     if (seg == nseg - 1)
-        for (int64_t e = tid; e < T * (opad - o); e += kSegThreads) {
-            const int64_t t = e / (opad - o), j = o + e % (opad - o);
-            xo[t * opad + j] = 0;   // +0 in both types
+        for (int e = tid; e < RB * (opad - o); e += kSegThreads) {
+            const int r = e / (opad - o), j = o + e % (opad - o);
+            if (t0 + r < T) xo[(int64_t)(t0 + r) * opad + j] = 0;   // +0 in both types
         }
     if (!in) return;
-    if (fm) {
+    if (fm && blockIdx.y == 0) {
         int pos = pos0;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             if ((fm >> e) & 1u) idx[pos++] = (int32_t)(c0 + e);
     }
 #pragma unroll
-    for (int t = 0; t < kSmallT; ++t) {
+    for (int r = 0; r < RB; ++r) {
+        const int64_t t = t0 + r;
         if (t < T) {
-            const float mx = sxs[t];
-            const float r = mx > 0.0f ? 127.0f / mx : 0.0f;
-            const uint32_t w[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
+            const float rr = rxs[r];
+            const uint32_t w[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
             uint32_t packed[2] = {0u, 0u};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float x = h16_to_f32<HT>((uint16_t)(w[e >> 1] >> ((e & 1) * 16)));
-                const uint32_t q = ((fm >> e) & 1u) ? 0u : (uint32_t)(uint8_t)quant(x, r);
+                const uint32_t q = ((fm >> e) & 1u) ? 0u : (uint32_t)(uint8_t)quant(x, rr);
                 packed[e >> 2] |= q << ((e & 3) * 8);
             }
             *reinterpret_cast<uint2*>(xq + t * K + c0) = make_uint2(packed[0], packed[1]);
@@ -484,6 +508,17 @@ __global__ __launch_bounds__(kSegThreads) void k_seg_quant(
     }
 }
 
+template <int HT, int TB>
+void launch_seg(const uint16_t* xb, int64_t T, int64_t K, float tau, const Workspace& ws,
+                hipStream_t stream) {
+    const dim3 grid((unsigned)ceil_div(K, kSegCols));
+    hipLaunchKernelGGL((k_seg_scan<HT, TB>), grid, dim3(kSegThreads), 0, stream, xb, T, K, tau,
+                       ws.flags, ws.segmax, ws.segcnt);
+    const dim3 qgrid(grid.x, (unsigned)ceil_div(T, kQuantRows));
+    hipLaunchKernelGGL((k_seg_quant<HT>), qgrid, dim3(kSegThreads), 0, stream, xb, T, K,
+                       ws.flags, ws.segmax, ws.segcnt, ws.idx, ws.count, ws.xq, ws.sx, ws.xo);
+}
+
 }  // namespace
 
 template <int HT>
@@ -491,10 +526,11 @@ static void launch_activation_typed(const uint16_t* xb, int64_t T, int64_t K, fl
                              const Workspace& ws, hipStream_t stream) {
     if (T <= kSmallT) {
         const dim3 grid((unsigned)ceil_div(K, kSegCols));
-        hipLaunchKernelGGL(k_seg_scan<HT>, grid, dim3(kSegThreads), 0, stream, xb, T, K, tau,
-                           ws.flags, ws.segmax, ws.segcnt);
-        hipLaunchKernelGGL(k_seg_quant<HT>, grid, dim3(kSegThreads), 0, stream, xb, T, K, ws.flags,
-                           ws.segmax, ws.segcnt, ws.idx, ws.count, ws.xq, ws.sx, ws.xo);
+        if (T <= 1) launch_seg<HT, 1>(xb, T, K, tau, ws, stream);
+        else if (T <= 2) launch_seg<HT, 2>(xb, T, K, tau, ws, stream);
+        else if (T <= 4) launch_seg<HT, 4>(xb, T, K, tau, ws, stream);
+        else if (T <= 8) launch_seg<HT, 8>(xb, T, K, tau, ws, stream);
+        else launch_seg<HT, 16>(xb, T, K, tau, ws, stream);
         return;
     }
     const int64_t kw = ceil_div(K, 32);
