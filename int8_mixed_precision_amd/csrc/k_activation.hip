@@ -292,7 +292,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_rowquant_cached(
 // own rows and needs no exchange.
 
 constexpr int kSegThreads = kSegCols / 8;
-static_assert(kSegThreads == 256 && kSmallT == 16, "row reductions: 16 rows x 16 lanes x 16 entries");
+static_assert(kSegThreads == 256 && kSmallT % 16 == 0, "row reductions: 16 rows x 16 lanes x 16 entries");
 
 // Exclusive prefix sum over the workgroup (wave scan by shuffles, wave
 // totals through LDS); total receives the workgroup's sum.
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(kSegThreads) void k_seg_scan(const uint16_t* __rest
                                                           uint32_t* __restrict__ flags,
                                                           float* __restrict__ segmax,
                                                           int32_t* __restrict__ segcnt) {
-    __shared__ __attribute__((aligned(16))) float red[kSmallT][kSegThreads];
+    __shared__ __attribute__((aligned(16))) float red[TB][kSegThreads];
     __shared__ int wtot[kSegThreads / kWave];
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int64_t c0 = (int64_t)blockIdx.x * kSegCols + tid * 8;
@@ -367,11 +367,12 @@ __global__ __launch_bounds__(kSegThreads) void k_seg_scan(const uint16_t* __rest
     }
     int total = 0;
     block_excl_scan(__builtin_popcount(fm), wtot, total);   // (its barrier also covers red)
-    // row t = tid / 16: each of 16 lanes takes the maximum of 16 entries,
-    // then 4 exchanges inside the group of 16 lanes (instead of a 6-step
-    // wave reduction per row)
-    {
-        const int t = tid >> 4, part = tid & 15;
+    // row t = 16 g + tid / 16: each of 16 lanes takes the maximum of 16
+    // entries, then 4 exchanges inside the group of 16 lanes (instead of a
+    // 6-step wave reduction per row)
+#pragma unroll
+    for (int g = 0; g < (TB + 15) / 16; ++g) {
+        const int t = g * 16 + (tid >> 4), part = tid & 15;
         float mx = 0.0f;
         if (t < T) {
             const float4* q = reinterpret_cast<const float4*>(&red[t][part * 16]);
@@ -530,7 +531,8 @@ static void launch_activation_typed(const uint16_t* xb, int64_t T, int64_t K, fl
         else if (T <= 2) launch_seg<HT, 2>(xb, T, K, tau, ws, stream);
         else if (T <= 4) launch_seg<HT, 4>(xb, T, K, tau, ws, stream);
         else if (T <= 8) launch_seg<HT, 8>(xb, T, K, tau, ws, stream);
-        else launch_seg<HT, 16>(xb, T, K, tau, ws, stream);
+        else if (T <= 16) launch_seg<HT, 16>(xb, T, K, tau, ws, stream);
+        else launch_seg<HT, 32>(xb, T, K, tau, ws, stream);
         return;
     }
     const int64_t kw = ceil_div(K, 32);

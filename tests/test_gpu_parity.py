@@ -125,6 +125,9 @@ def test_tiny_config(mm):
     (65, 384, 8, 2, "normal"), (100, 2048, 264, 70, "laplace"), (64, 1024, 200, 40, "normal"),
     # 9..16 rows go to the matmul kernels unless K is long
     (16, 8192, 1000, 6, "normal"), (12, 5120, 520, 3, "laplace"), (16, 12288, 264, 20, "normal"),
+    # the two-kernel activation pass up to 32 rows: 17..32 rows, K past a
+    # whole 2048-column segment
+    (24, 2064, 136, 3, "normal"), (32, 6144, 264, 9, "laplace"), (19, 4112, 72, 2, "normal"),
 ])
 def test_ragged_shapes(mm, T, K, N, nd, dist):
     X, W = synth.random_case(10_000 + T + K + N, T, K, N, n_dims=nd, x_dist=dist)
@@ -172,6 +175,7 @@ def test_decode_precomputed(mm, T, K, N, nd, tau, halved):
     (257, 1024, 264, 0, 0.0),       # o = 1024 > 512: rows recovered inside the matmul
     (300, 2048, 520, 600, 6.0),     # about 600 outliers, the same
     (64, 2048, 264, 600, 6.0), (100, 2048, 520, 40, 6.0),   # streaming kernel, W rows through LDS
+    (30, 2048, 136, 0, 0.0),        # 30 rows, every dimension an outlier
 ])
 def test_memory_halved(mm, T, K, N, nd, tau):
     """W16 = NULL: outlier rows recovered from the Int8 weight."""
