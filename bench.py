@@ -278,6 +278,46 @@ def bench_down(torch, mm, synth, steps, warmup):
             "TOPS": round(2.0 * T * K * N * steps / wall / 1e12, 2)}
 
 
+def decode_batched(torch, mm, synth, w, sets, rounds, warmup, rows=(32, 128)):
+    """Batched decode on the decode workload's weights: T = 32 and 128 rows of
+    activations with the same recipe, whole calls from a HIP graph over the
+    rotating weight copies (the streaming matmul kernels).  Context only."""
+    out = []
+    K, N = w.K, w.N
+    for T in rows:
+        X = torch.from_numpy(synth.make_x(w, T=T, threads=CPU_THREADS)).cuda()
+        ws = mm.new_workspace(T, K, N)
+        Y = torch.empty((T, N), dtype=torch.float16, device="cuda")
+
+        def one_round():
+            for Wq, sw, W16 in sets:
+                mm.mixed_matmul(X, Wq, sw, W16, w.tau, workspace=ws, out=Y)
+
+        one_round()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            one_round()
+        torch.cuda.synchronize()
+
+        def step(i, e):
+            if e is not None:
+                e[0].record()
+            graph.replay()
+            if e is not None:
+                e[1].record()
+
+        prewarm(torch, step)
+        wall, _ = timed_loop(torch, rounds, max(1, warmup // DECODE_ROTATE + 1), step)
+        calls = rounds * DECODE_ROTATE
+        out.append({"T": T, "us_per_call": round(wall * 1e6 / calls, 2),
+                    "weight_GB/s": round(K * N * calls / wall / 1e9, 1),
+                    "TOPS": round(2.0 * T * K * N * calls / wall / 1e12, 1)})
+        del graph, X, ws, Y
+        torch.cuda.empty_cache()
+    return out
+
+
 def decode_variants(torch, mm, w, X, sets, ws, Y, rounds, warmup):
     """The memory-halved and bf16 variants of the decode call (graph replays
     over the same rotating weight copies)."""
@@ -390,6 +430,9 @@ def bench_decode(torch, mm, synth, steps, warmup, variants=True):
     call_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) / DECODE_ROTATE
 
     extra = decode_variants(torch, mm, w, X, sets, ws, Y, rounds, warmup) if variants else {}
+    if variants:
+        log("decode: batched rows (32, 128)")
+        extra["batched"] = decode_batched(torch, mm, synth, w, sets, rounds, warmup)
     dbg = mm.mixed_matmul_debug(X, Wq0, sw0, W16_0, w.tau)
     o = int(dbg["count"][0])
     wbytes = K * N + 4.0 * N
@@ -603,6 +646,11 @@ def main():
         out["other_configs"] = {"down": {
             "workload": "prefill FFN down-projection (whole int8_mixed_matmul calls, W "
                         "pre-converted to Int8)", **down}}
+    if dec is not None and "batched" in dec:
+        out.setdefault("other_configs", {})["batched_decode"] = {
+            "workload": "decode FFN up-projection weights (K=8192, N=28672, 8 rotating copies) "
+                        "with 32 and 128 activation rows, whole calls from a HIP graph",
+            "results": dec["batched"]}
     if not args.no_cpu_baseline and pre is not None:
         log("cpu baseline: oracle on a row sample")
         out["cpu_baseline"] = cpu_baseline(synth, pre["T"], pre["K"], pre["N"])
