@@ -71,10 +71,10 @@ constexpr int kStageBytes = 4 * kStageHalf;   // two buffers of X and W
 constexpr int kYS = 256 * 2 + 16;             // bytes per row of the staged Y tile (padded)
 constexpr int kYBytes = 256 * kYS;            // the 256 x 256 tile of 16-bit Y values
 
-// SBN > 0 (streaming kernel, 256 threads, n-tile of SBN columns): with more
+// SBN > 0 (streaming kernel, STH threads, n-tile of SBN columns): with more
 // than 16 outliers the outlier W rows go through LDS like the large-tile
 // kernel's (sc.lds, sc.tid and sc.n0 used).
-template <int TM, int TN, bool WRITE_ACC, int HT, bool STAGED = false, int SBN = 0>
+template <int TM, int TN, bool WRITE_ACC, int HT, bool STAGED = false, int SBN = 0, int STH = 256>
 __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a, int64_t mb,
                                          int64_t nb, int lane, const StageCtx& sc = StageCtx{}) {
     const int64_t T = a.T, N = a.N;
@@ -170,10 +170,10 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a,
                 // buffered, the next chunk's loads in flight during this
                 // chunk's MFMAs.  X values come straight from the gathered
                 // columns (16 contiguous bytes per lane).
-                constexpr int CPB = SBN / 8;              // columns per block (8 blocks)
+                constexpr int CPB = SBN / (STH / 32);     // columns per block (STH / 32 blocks)
                 constexpr int NV = CPB / 8;               // 16-byte loads per thread
                 constexpr int kWS = SBN * kOS;            // bytes of one buffer
-                static_assert(NV >= 1 && NV * 64 == SBN, "n-tile of 64 or 128 columns");
+                static_assert(NV >= 1 && NV * 8 * (STH / 32) == SBN, "whole 8-column pieces per thread");
                 __syncthreads();   // the main loop's LDS reads are complete
                 const int e = sc.tid & 31, cb = sc.tid >> 5;
                 float dcol[CPB];
@@ -833,16 +833,16 @@ __device__ __forceinline__ int stream_swz(int row) { return (row & 7) ^ ((row >>
 // tile kt have landed and tile kt-1 is no longer read, so its buffer takes
 // tile kt+STAGES-1.  BM x BN tile, 4 waves of (BM/WAVES_M) x (BN/WAVES_N);
 // rows past T or N are clamped to the last row (never stored).
-template <int BM, int BN, int WAVES_M, int STAGES, bool WRITE_ACC, int HT>
-__global__ __launch_bounds__(256) void k_gemm_i8_stream(GemmArgs a) {
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool WRITE_ACC, int HT>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_i8_stream(GemmArgs a) {
     constexpr int BK = 128;
-    constexpr int WAVES_N = 4 / WAVES_M;
+    constexpr int NW = WAVES_M * WAVES_N;
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     constexpr int TM = WM / 32, TN = WN / 32;
     constexpr int STAGE_BYTES = (BM + BN) * BK;
     constexpr int GA = BM * BK / 1024, GB = BN * BK / 1024;   // 1 KB groups of A and B
-    constexpr int LOADS = (GA + GB) / 4;                      // copies per lane per tile
-    static_assert(TM >= 1 && TN >= 1 && (GA + GB) % 4 == 0, "tile shape");
+    constexpr int LOADS = (GA + GB) / NW;                     // copies per lane per tile
+    static_assert(TM >= 1 && TN >= 1 && (GA + GB) % NW == 0, "tile shape");
     static_assert((STAGES - 2) * LOADS <= 63 && STAGES >= 3, "wait count range");
     __shared__ __attribute__((aligned(1024))) int8_t lds[STAGES * STAGE_BYTES];
 
@@ -932,19 +932,20 @@ __global__ __launch_bounds__(256) void k_gemm_i8_stream(GemmArgs a) {
     // the copies past the last tile went to buffers no one reads; let them
     // land before the workgroup ends
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    epilogue<TM, TN, WRITE_ACC, HT, false, BN>(acc, a, m0 + wm0, n0 + wn0, lane,
-                                               StageCtx{lds, tid, m0, n0, nullptr, 0.0f, nullptr, 0, 0});
+    epilogue<TM, TN, WRITE_ACC, HT, false, BN, 64 * NW>(acc, a, m0 + wm0, n0 + wn0, lane,
+                                                        StageCtx{lds, tid, m0, n0, nullptr, 0.0f, nullptr, 0, 0});
 }
 
-template <int BM, int BN, int WAVES_M, int STAGES, int HT>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int HT>
 hipError_t launch_stream(const GemmArgs& a, hipStream_t stream) {
     const int64_t tiles = ceil_div(a.T, BM) * ceil_div(a.N, BN);
+    constexpr int threads = 64 * WAVES_M * WAVES_N;
     if (a.acc_out)
-        hipLaunchKernelGGL((k_gemm_i8_stream<BM, BN, WAVES_M, STAGES, true, HT>), dim3((unsigned)tiles),
-                           dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((k_gemm_i8_stream<BM, BN, WAVES_M, WAVES_N, STAGES, true, HT>),
+                           dim3((unsigned)tiles), dim3(threads), 0, stream, a);
     else
-        hipLaunchKernelGGL((k_gemm_i8_stream<BM, BN, WAVES_M, STAGES, false, HT>), dim3((unsigned)tiles),
-                           dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((k_gemm_i8_stream<BM, BN, WAVES_M, WAVES_N, STAGES, false, HT>),
+                           dim3((unsigned)tiles), dim3(threads), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -996,12 +997,20 @@ hipError_t launch_big(const GemmArgs& a, hipStream_t stream) {
 // 128x128x64 98 us; with 256 outliers (their W rows staged through LDS)
 // T=64 62.5 us and T=128 71 us against 114 and 128 us.  The register-staged
 // kernels keep the shapes with K % 128 != 0.
+// 129..256 rows: a 256x128 streaming tile (4 waves of 64x128) while its
+// tiles fit the chip in one round and the large-tile kernel would not split
+// K - whole calls, T=160/256: K=8192 N=28672 109 -> 94 / 120 -> 101 us,
+// K=12288 N=12288 166 -> 130 us, K=4096 N=14336 66 -> 55 us; with 288 or
+// more tiles (N >= 36864) or a split K the large-tile kernel stays ahead.
 template <int HT>
 hipError_t launch_gemm_typed(const GemmArgs& a, hipStream_t stream) {
+    if (a.T > 128 && a.T <= 256 && a.K % 128 == 0 && ceil_div(a.N, 128) <= device_cus() &&
+        gemm_ksplit(a.T, a.K, a.N) == 1)
+        return launch_stream<256, 128, 4, 1, 3, HT>(a, stream);
     if (a.T > 128 && a.K % 64 == 0) return launch_big<4, HT>(a, stream);
     if (a.K % 128 == 0) {
-        if (a.T <= 64) return launch_stream<64, 64, 2, 4, HT>(a, stream);
-        return launch_stream<128, 128, 2, 4, HT>(a, stream);
+        if (a.T <= 64) return launch_stream<64, 64, 2, 2, 4, HT>(a, stream);
+        return launch_stream<128, 128, 2, 2, 4, HT>(a, stream);
     }
     if (a.T <= 32) return launch_cfg<32, 128, 256, 1, HT>(a, stream);
     if (a.T <= 64) return launch_cfg<64, 128, 256, 2, HT>(a, stream);

@@ -128,6 +128,9 @@ def test_tiny_config(mm):
     # the two-kernel activation pass up to 32 rows: 17..32 rows, K past a
     # whole 2048-column segment
     (24, 2064, 136, 3, "normal"), (32, 6144, 264, 9, "laplace"), (19, 4112, 72, 2, "normal"),
+    # 129..256 rows on the 256x128 streaming tile (one k-tile; ragged T and
+    # N; many outliers through the LDS stage)
+    (129, 128, 72, 1, "normal"), (200, 1152, 392, 5, "laplace"), (256, 2048, 264, 80, "normal"),
 ])
 def test_ragged_shapes(mm, T, K, N, nd, dist):
     X, W = synth.random_case(10_000 + T + K + N, T, K, N, n_dims=nd, x_dist=dist)
@@ -176,6 +179,7 @@ def test_decode_precomputed(mm, T, K, N, nd, tau, halved):
     (300, 2048, 520, 600, 6.0),     # about 600 outliers, the same
     (64, 2048, 264, 600, 6.0), (100, 2048, 520, 40, 6.0),   # streaming kernel, W rows through LDS
     (30, 2048, 136, 0, 0.0),        # 30 rows, every dimension an outlier
+    (160, 2048, 264, 300, 6.0),     # 256x128 streaming tile, recovered rows
 ])
 def test_memory_halved(mm, T, K, N, nd, tau):
     """W16 = NULL: outlier rows recovered from the Int8 weight."""
