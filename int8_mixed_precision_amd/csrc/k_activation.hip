@@ -206,18 +206,48 @@ __global__ __launch_bounds__(kQuantThreads) void k_rowquant(
     if (tid == 0) sx[t] = mx;
 }
 
+// Exclusive prefix sum over the workgroup (wave scan by shuffles, wave
+// totals through LDS); total receives the workgroup's sum.
+__device__ inline int block_excl_scan(int v, int* wtot, int& total) {
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+    int incl = v;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int u = __shfl_up(incl, d);
+        if (lane >= d) incl += u;
+    }
+    if (lane == kWave - 1) wtot[wv] = incl;
+    __syncthreads();
+    int before = 0;
+    total = 0;
+#pragma unroll
+    for (int w = 0; w < kQuantThreads / kWave; ++w) {
+        before += w < wv ? wtot[w] : 0;
+        total += wtot[w];
+    }
+    return before + incl - v;
+}
+
 // k_rowquant for rows of at most kQuantThreads * kRowCache * 8 values: the
 // row is read from HBM once into registers (one pass instead of two), the
 // outlier bitmap once into LDS, and every load is issued before the first
-// use (chunks past the row re-read chunk 0; nothing uses them).
+// use (chunks past the row re-read chunk 0; nothing uses them).  It also
+// isolates the outlier dimensions itself: every workgroup scans the bitmap
+// words it holds in LDS for their prefix counts (a few words per lane), and
+// workgroup 0 writes the ascending index list and the count, so no separate
+// compaction kernel runs.
 // CACHE = 16-byte chunks per thread: K <= 16384 (8) or K <= 49152 (24).
 template <int HT, int kRowCache>
 __global__ __launch_bounds__(kQuantThreads) void k_rowquant_cached(
     const uint16_t* __restrict__ X, int64_t K, const uint32_t* __restrict__ flags,
-    const int32_t* __restrict__ wprefix, const int32_t* __restrict__ count,
+    int32_t* __restrict__ idx, int32_t* __restrict__ count,
     int8_t* __restrict__ xq, float* __restrict__ sx, uint16_t* __restrict__ xo) {
+    constexpr int KW = kQuantThreads * kRowCache / 4;                  // bitmap words held
+    constexpr int WPT = (KW + kQuantThreads - 1) / kQuantThreads;      // words per lane
     __shared__ float red[kQuantThreads / kWave];
-    __shared__ uint32_t fl[kQuantThreads * kRowCache / 4];
+    __shared__ uint32_t fl[KW];
+    __shared__ int pf[KW];
+    __shared__ int wtot[kQuantThreads / kWave];
     const int tid = threadIdx.x;
     const int64_t t = blockIdx.x;
     const uint16_t* row = X + t * K;
@@ -231,6 +261,38 @@ __global__ __launch_bounds__(kQuantThreads) void k_rowquant_cached(
     const int kw = (nch + 3) / 4;
     for (int w = tid; w < kw; w += kQuantThreads) fl[w] = flags[w];
     __syncthreads();
+    // outliers before each word: lane l takes words WPT l .. WPT l + WPT - 1
+    int o = 0;
+    {
+        int cnt = 0;
+#pragma unroll
+        for (int i = 0; i < WPT; ++i) {
+            const int w = WPT * tid + i;
+            if (w < kw) cnt += __builtin_popcount(fl[w]);
+        }
+        int run = block_excl_scan(cnt, wtot, o);
+#pragma unroll
+        for (int i = 0; i < WPT; ++i) {
+            const int w = WPT * tid + i;
+            if (w < kw) {
+                pf[w] = run;
+                uint32_t f = fl[w];
+                if (blockIdx.x == 0) {
+                    int p = run;
+                    while (f) {
+                        idx[p++] = w * 32 + __builtin_ctz(f);
+                        f &= f - 1u;
+                    }
+                }
+                run += __builtin_popcount(fl[w]);
+            }
+        }
+    }
+    const int opad = (o + 15) & ~15;
+    if (blockIdx.x == 0 && tid == 0) {
+        count[0] = o;
+        count[1] = opad;
+    }
     float mx = 0.0f;
 #pragma unroll
     for (int i = 0; i < kRowCache; ++i) {
@@ -247,13 +309,11 @@ __global__ __launch_bounds__(kQuantThreads) void k_rowquant_cached(
     }
     mx = wave_max(mx);
     if ((tid & (kWave - 1)) == 0) red[tid / kWave] = mx;
-    __syncthreads();
+    __syncthreads();   // red, and the word prefixes pf
     mx = red[0];
 #pragma unroll
     for (int i = 1; i < kQuantThreads / kWave; ++i) mx = __builtin_fmaxf(mx, red[i]);
     const float r = mx > 0.0f ? 127.0f / mx : 0.0f;
-    const int64_t opad = count[1];
-    const int64_t o = count[0];
     uint16_t* xo_row = xo + t * opad;
 #pragma unroll
     for (int i = 0; i < kRowCache; ++i) {
@@ -276,13 +336,13 @@ __global__ __launch_bounds__(kQuantThreads) void k_rowquant_cached(
             for (int e = 0; e < 8; ++e) {
                 if ((fm >> e) & 1u) {
                     const int bit = base_bit + e;
-                    const int pos = wprefix[c >> 2] + __builtin_popcount(word & ((1u << bit) - 1u));
+                    const int pos = pf[c >> 2] + __builtin_popcount(word & ((1u << bit) - 1u));
                     xo_row[pos] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
                 }
             }
         }
     }
-    for (int64_t j = o + tid; j < opad; j += kQuantThreads) xo_row[j] = 0;   // +0 in both types
+    for (int j = o + tid; j < opad; j += kQuantThreads) xo_row[j] = 0;   // +0 in both types
     if (tid == 0) sx[t] = mx;
 }
 
@@ -293,28 +353,6 @@ __global__ __launch_bounds__(kQuantThreads) void k_rowquant_cached(
 
 constexpr int kSegThreads = kSegCols / 8;
 static_assert(kSegThreads == 256 && kSmallT % 16 == 0, "row reductions: 16 rows x 16 lanes x 16 entries");
-
-// Exclusive prefix sum over the workgroup (wave scan by shuffles, wave
-// totals through LDS); total receives the workgroup's sum.
-__device__ inline int block_excl_scan(int v, int* wtot, int& total) {
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
-    int incl = v;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int u = __shfl_up(incl, d);
-        if (lane >= d) incl += u;
-    }
-    if (lane == kWave - 1) wtot[wv] = incl;
-    __syncthreads();
-    int before = 0;
-    total = 0;
-#pragma unroll
-    for (int w = 0; w < kSegThreads / kWave; ++w) {
-        before += w < wv ? wtot[w] : 0;
-        total += wtot[w];
-    }
-    return before + incl - v;
-}
 
 // Pass 1: the segment's outlier flags (whole bitmap words, written without
 // atomics), per row the maximum |x| over its non-outlier columns, and its
@@ -541,17 +579,19 @@ static void launch_activation_typed(const uint16_t* xb, int64_t T, int64_t K, fl
     const int64_t row_chunks = ceil_div(T, kDetectRows);
     dim3 dgrid((unsigned)ceil_div(K, kDetectCols), (unsigned)(row_chunks < 65535 ? row_chunks : 65535));
     hipLaunchKernelGGL(k_detect<HT>, dgrid, dim3(kDetectThreads), 0, stream, xb, T, K, tau, ws.flags);
-    hipLaunchKernelGGL(k_compact, dim3(1), dim3(kCompactThreads), 0, stream, ws.flags, kw,
-                       ws.wprefix, ws.idx, ws.count);
-    if (K <= (int64_t)kQuantThreads * 8 * 8)
+    // rows held in registers: the quantize kernel isolates the outliers too
+    if (K <= (int64_t)kQuantThreads * 8 * 8) {
         hipLaunchKernelGGL((k_rowquant_cached<HT, 8>), dim3((unsigned)T), dim3(kQuantThreads), 0,
-                           stream, xb, K, ws.flags, ws.wprefix, ws.count, ws.xq, ws.sx, ws.xo);
-    else if (K <= (int64_t)kQuantThreads * 24 * 8)
+                           stream, xb, K, ws.flags, ws.idx, ws.count, ws.xq, ws.sx, ws.xo);
+    } else if (K <= (int64_t)kQuantThreads * 24 * 8) {
         hipLaunchKernelGGL((k_rowquant_cached<HT, 24>), dim3((unsigned)T), dim3(kQuantThreads), 0,
-                           stream, xb, K, ws.flags, ws.wprefix, ws.count, ws.xq, ws.sx, ws.xo);
-    else
+                           stream, xb, K, ws.flags, ws.idx, ws.count, ws.xq, ws.sx, ws.xo);
+    } else {
+        hipLaunchKernelGGL(k_compact, dim3(1), dim3(kCompactThreads), 0, stream, ws.flags, kw,
+                           ws.wprefix, ws.idx, ws.count);
         hipLaunchKernelGGL(k_rowquant<HT>, dim3((unsigned)T), dim3(kQuantThreads), 0, stream, xb,
                            K, ws.flags, ws.wprefix, ws.count, ws.xq, ws.sx, ws.xo);
+    }
 }
 
 hipError_t launch_activation_pass(const uint16_t* X, int ht, int64_t T, int64_t K, float tau,
