@@ -103,6 +103,7 @@ def run_bf16(mm, name, X16, W16, tau, halved=False, big=None, rows=None):
     (6, 16384, 520, 5, 6.0, False), (8, 12288, 264, 30, 6.0, True),      # decode, precomputed
     (8, 49152, 264, 4, 6.0, True), (16, 32768, 136, 3, 6.0, False),      # decode, K slabs
     (16, 8192, 520, 5, 6.0, False), (50, 1152, 520, 3, 6.0, True),       # streaming matmul
+    (100, 2048, 264, 70, 6.0, False), (200, 2048, 264, 40, 6.0, True),   # outlier W rows through LDS
 ])
 def test_bf16_path(mm, T, K, N, nd, tau, halved):
     X, W = synth.random_case(60_000 + T + K + N + nd, T, K, N, n_dims=nd)

@@ -19,7 +19,8 @@ def mm():
 
 
 @pytest.mark.parametrize("T,K,N", [(8, 8192, 1040), (300, 1024, 520), (300, 24576, 520),
-                                   (16, 8192, 1040), (8, 49152, 264), (4, 12288, 520)])
+                                   (16, 8192, 1040), (8, 49152, 264), (4, 12288, 520),
+                                   (200, 1024, 520), (64, 2048, 264)])
 def test_graph_replays_match_eager(mm, T, K, N):
     print(f"[case] graph replay {T}x{K}x{N}", flush=True)
     X, W = synth.random_case(40_000 + T, T, K, N, n_dims=3)
