@@ -230,6 +230,8 @@ def bench_prefill(torch, mm, synth, steps, warmup, variants=True):
     # the outlier count of this X (one debug call, outside the timed loop)
     dbg = mm.mixed_matmul_debug(X, Wq, sw, W16, w.tau)
     o = int(dbg["count"][0])
+    if variants:
+        extra["vendor_int8_gemm"] = vendor_int8_gemm(torch, dbg["xq"], Wq.view(N, K), steps, warmup)
     del dbg
     ops = 2.0 * T * K * N
     ms_step = wall * 1e3 / steps
@@ -242,6 +244,31 @@ def bench_prefill(torch, mm, synth, steps, warmup, variants=True):
         "quantize_weight_gbs": (2.0 * K * N + K * N + 4.0 * N) / (q_ms * 1e-3) / 1e9,
         **extra,
     }
+
+
+def vendor_int8_gemm(torch, xq, wq, steps, warmup):
+    """Context for the roofline: the vendor library's int8 GEMM (hipBLASLt
+    through torch._int_mm) on the same Xq [T,K] and Wq [N,K], int32 out - the
+    int8 product alone, without dequantization, outlier product or fp16 Y."""
+    T, K = xq.shape
+    N = wq.shape[0]
+    b = wq.t()
+
+    def step(i, e):
+        if e is not None:
+            e[0].record()
+        torch._int_mm(xq, b)
+        if e is not None:
+            e[1].record()
+
+    try:
+        prewarm(torch, step)
+        _, evs = timed_loop(torch, steps, warmup, step)
+    except RuntimeError as err:   # no int8 GEMM in this torch build
+        return {"note": f"unavailable: {str(err)[:80]}"}
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    return {"note": "torch._int_mm (hipBLASLt) on the same int8 operands, int32 out",
+            "ms": round(ms, 4), "TOPS": round(2.0 * T * K * N / (ms * 1e-3) / 1e12, 1)}
 
 
 def bench_down(torch, mm, synth, steps, warmup):
@@ -381,8 +408,35 @@ def decode_variants(torch, mm, w, X, sets, ws, Y, rounds, warmup):
     wall_b, evs_b = timed_loop(torch, rounds, max(1, warmup // DECODE_ROTATE + 1), step_bf16)
     call_b_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs_b])) / DECODE_ROTATE
     del sets_b, graph_b
+    # warm: the same weight copy in every call (235 MB, which the 256 MB
+    # last-level cache can hold) - context next to the cold metric
+    Wq0, sw0, W160 = sets[0]
+
+    def one_round_warm():
+        for _ in range(DECODE_ROTATE):
+            mm.mixed_matmul(X, Wq0, sw0, W160, w.tau, workspace=ws, out=Y)
+
+    one_round_warm()
+    torch.cuda.synchronize()
+    graph_w = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph_w):
+        one_round_warm()
+    torch.cuda.synchronize()
+
+    def step_warm(i, e):
+        if e is not None:
+            e[0].record()
+        graph_w.replay()
+        if e is not None:
+            e[1].record()
+
+    log(f"decode, warm weight: {rounds} timed graph replays")
+    prewarm(torch, step_warm)
+    wall_w, _ = timed_loop(torch, rounds, max(1, warmup // DECODE_ROTATE + 1), step_warm)
+    del graph_w
     return {"halved_weight_gbs": wbytes * steps / wall_h / 1e9, "halved_call_ms": call_h_ms,
-            "bf16_weight_gbs": wbytes * steps / wall_b / 1e9, "bf16_call_ms": call_b_ms}
+            "bf16_weight_gbs": wbytes * steps / wall_b / 1e9, "bf16_call_ms": call_b_ms,
+            "warm_weight_gbs": wbytes * steps / wall_w / 1e9, "warm_call_ms": wall_w * 1e3 / steps}
 
 
 def bench_decode(torch, mm, synth, steps, warmup, variants=True):
@@ -614,6 +668,12 @@ def main():
                                    "ms_per_step": round(pre["bf16_ms_per_step"], 4)}
             out["quantize_weight"]["from_bf16"] = pre["convert"]["bf16"]
             out["quantize_weight"]["from_f32"] = pre["convert"]["f32"]
+            # weight bytes the matmul needs: Int8 + scales against the 16-bit
+            # weight (memory-halved variant), or plus the 16-bit copy
+            K, N = pre["K"], pre["N"]
+            out["memory_halved"]["weight_memory_ratio"] = round((K * N + 4.0 * N) / (2.0 * K * N), 4)
+        if "vendor_int8_gemm" in pre:
+            out["roofline"]["vendor_int8_gemm"] = pre["vendor_int8_gemm"]
     if dec is not None:
         d = {"metric": "weight GB/s @ T=8", "value": round(dec["weight_gbs"], 1), "unit": "GB/s",
              "ms_per_step": round(dec["ms_per_step"], 5), "steps": dec["steps"],
@@ -637,6 +697,10 @@ def main():
             d["bf16_variant"] = {"note": "X, W16, Y bfloat16",
                                  "weight GB/s": round(dec["bf16_weight_gbs"], 1),
                                  "call_ms": round(dec["bf16_call_ms"], 5)}
+            d["warm"] = {"note": "one weight copy in every call (cache resident); the metric "
+                                 "rotates 8 copies",
+                         "weight GB/s": round(dec["warm_weight_gbs"], 1),
+                         "call_ms": round(dec["warm_call_ms"], 5)}
         if pre is None:
             out.update({"value": d["value"], "unit": "GB/s", "ms_per_step": d["ms_per_step"],
                         "config": d["config"], "roofline": d["roofline"]})
