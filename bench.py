@@ -19,7 +19,7 @@ weight in the 256 MB last-level cache.
 Per-kernel durations come from HIP events recorded on the stream the
 library launches on, inside the timed loop; the roofline objects divide
 the algorithmic work of one launch by that duration.  The CPU baseline is
-the test oracle (plain C, this machine's host cores) timed on a row sample of
+the test oracle (plain C, on the host's cores) timed on a row sample of
 the prefill workload.  Prints one JSON line.
 """
 from __future__ import annotations
@@ -39,7 +39,7 @@ sys.path.insert(0, ROOT)
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, published
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
 DECODE_ROTATE = 8
-CPU_THREADS = 16             # host-core share of one GPU on the box
+CPU_THREADS = 16             # host-core share of one GPU on an 8-GPU host
 CPU_TARGET_S = 15.0
 
 
