@@ -137,6 +137,31 @@ def test_ragged_shapes(mm, T, K, N, nd, dist):
     run_case(mm, f"ragged {T}x{K}x{N}", X, W, 6.0)
 
 
+def _random_shapes(n=24, seed=2024, max_macs=6e8):
+    """Seeded shapes spread over every route of the library: row counts of
+    the decode kernel, the streaming tiles and the large-tile kernel, K with
+    and without a multiple of 1024 / 128 / 64, ragged N; each with a few
+    planted outlier dimensions, every other one the memory-halved variant."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        T = int(rng.choice([rng.integers(1, 9), rng.integers(9, 33), rng.integers(33, 129),
+                            rng.integers(129, 400)]))
+        K = int(rng.choice([1024 * rng.integers(1, 17), 128 * rng.integers(1, 80),
+                            16 * rng.integers(1, 600)]))
+        N = int(8 * rng.integers(1, 160))
+        if T * K * N > max_macs:
+            continue
+        out.append((T, K, N, int(rng.integers(0, 9)), len(out) % 2 == 1))
+    return out
+
+
+@pytest.mark.parametrize("T,K,N,nd,halved", _random_shapes())
+def test_random_shapes(mm, T, K, N, nd, halved):
+    X, W = synth.random_case(50_000 + T + K + N + nd, T, K, N, n_dims=nd)
+    run_case(mm, f"random {T}x{K}x{N}{' halved' if halved else ''}", X, W, 6.0, halved=halved)
+
+
 @pytest.mark.parametrize("T,K,N,nd,tau", [
     (1, 4096, 1000, 3, 6.0), (3, 4096, 8, 0, 6.0), (8, 8192, 2056, 6, 6.0),
     (16, 4096, 520, 5, 6.0), (8, 8192, 264, 300, 6.0),   # o > 256: values read from X
