@@ -40,9 +40,9 @@ __device__ __forceinline__ uint16_t f32_to_h16(float f) {
 //   flags   u32 [kw]     bit k%32 of word k/32 set when dimension k is an outlier
 //   wprefix i32 [kw]     number of outlier dimensions before word w
 //   count   i32 [4]      count[0] = o, count[1] = o rounded up to 16
-//   segmax  f32 [nseg][32], segcnt i32 [nseg]   per 2048-column segment, the
+//   segmax  f32 [nseg][16], segcnt i32 [nseg]   per 2048-column segment, the
 //           row maxima over its non-outlier columns and its outlier count
-//           (activation pass for T <= 32 only; nseg = ceil(K / 2048))
+//           (activation pass for T <= 16 only; nseg = ceil(K / 2048))
 //   idx     i32 [K]      outlier dimensions, ascending
 //   sx      f32 [T]      row scales
 //   xq      i8  [T,K]    quantized activations, outlier columns 0
@@ -108,7 +108,7 @@ constexpr int64_t kRecoverRows = 512;
 // Activation pass for few rows (T <= kSmallT): one workgroup per segment of
 // kSegCols columns holds every row of them, so it knows its outlier columns
 // without waiting for the rest of X.
-constexpr int kSmallT = 32;
+constexpr int kSmallT = 16;
 constexpr int kSegCols = 2048;
 
 // Layout of the workspace for (T, K, N) at `base` (base may be NULL to size

@@ -618,8 +618,7 @@ static void launch_activation_typed(const uint16_t* xb, int64_t T, int64_t K, fl
         else if (T <= 2) launch_seg<HT, 2>(xb, T, K, tau, ws, stream);
         else if (T <= 4) launch_seg<HT, 4>(xb, T, K, tau, ws, stream);
         else if (T <= 8) launch_seg<HT, 8>(xb, T, K, tau, ws, stream);
-        else if (T <= 16) launch_seg<HT, 16>(xb, T, K, tau, ws, stream);
-        else launch_seg<HT, 32>(xb, T, K, tau, ws, stream);
+        else launch_seg<HT, 16>(xb, T, K, tau, ws, stream);
         return;
     }
     const int64_t kw = ceil_div(K, 32);

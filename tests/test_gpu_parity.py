@@ -125,8 +125,8 @@ def test_tiny_config(mm):
     (65, 384, 8, 2, "normal"), (100, 2048, 264, 70, "laplace"), (64, 1024, 200, 40, "normal"),
     # 9..16 rows go to the matmul kernels unless K is long
     (16, 8192, 1000, 6, "normal"), (12, 5120, 520, 3, "laplace"), (16, 12288, 264, 20, "normal"),
-    # the two-kernel activation pass up to 32 rows: 17..32 rows, K past a
-    # whole 2048-column segment
+    # 17..32 rows (detection without the clearing kernel), K past a whole
+    # 2048-column segment
     (24, 2064, 136, 3, "normal"), (32, 6144, 264, 9, "laplace"), (19, 4112, 72, 2, "normal"),
     # 129..256 rows on the 256x128 streaming tile (one k-tile; ragged T and
     # N; many outliers through the LDS stage)
