@@ -87,26 +87,27 @@ __global__ __launch_bounds__(kDetectThreads) void k_detect(const uint16_t* __res
 
 // Outlier flags for up to kOwnedMaxT rows without atomics: a workgroup owns
 // kOwnedCols columns (8 per lane, whole 32-bit words per 4 lanes) and reads
-// every row of them, its 4 waves taking rows 16 at a time (rows past T
-// re-read row T-1, so all 16 loads of a batch are in flight together); the
-// waves' flags are merged through LDS and every word of the bitmap is
-// stored, so no clearing kernel has to run first.  Whole calls, against the
-// clearing kernel + atomic detection: T=40 and 64 on K=8192, N=28672 2 us
-// faster, T=128 0.8 us; at T=200 and 256 3 us slower (too many rows per
-// workgroup), hence the limit.
+// every row of them, its kOwnedWaves waves taking rows 16 at a time (rows
+// past T re-read row T-1, so all 16 loads of a batch are in flight
+// together); the waves' flags are merged through LDS and every word of the
+// bitmap is stored, so no clearing kernel has to run first.
+// Whole calls against the clearing kernel + atomic detection: T=17-64 on
+// K=8192, N=28672 up to 2.9 us faster, T=128 0.9 us; 129-256 rows within
+// +-1 us either way, so they keep the other path.
 constexpr int kOwnedCols = 512;
+constexpr int kOwnedWaves = 16;
 constexpr int kOwnedMaxT = 128;
 template <int HT>
-__global__ __launch_bounds__(256) void k_detect_owned(const uint16_t* __restrict__ X, int64_t T,
-                                                       int64_t K, float tau,
-                                                       uint32_t* __restrict__ flags) {
-    __shared__ uint32_t wfm[4][kWave];
+__global__ __launch_bounds__(kOwnedWaves * kWave) void k_detect_owned(const uint16_t* __restrict__ X,
+                                                                      int64_t T, int64_t K, float tau,
+                                                                      uint32_t* __restrict__ flags) {
+    __shared__ uint32_t wfm[kOwnedWaves][kWave];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid >> 6;
     const int64_t c0 = (int64_t)blockIdx.x * kOwnedCols + lane * 8;
     const bool in = c0 < K;
     const uint16_t* xc = X + (in ? c0 : 0);
     uint32_t m = 0;
-    for (int64_t t0 = wv * 16; t0 < T; t0 += 64) {
+    for (int64_t t0 = wv * 16; t0 < T; t0 += 16 * kOwnedWaves) {
         uint4 v[16];
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
@@ -126,7 +127,9 @@ __global__ __launch_bounds__(256) void k_detect_owned(const uint16_t* __restrict
     wfm[wv][lane] = in ? m : 0u;   // lanes past K (which read column 0) flag nothing
     __syncthreads();
     if (wv == 0) {
-        const uint32_t f = wfm[0][lane] | wfm[1][lane] | wfm[2][lane] | wfm[3][lane];
+        uint32_t f = 0;
+#pragma unroll
+        for (int w = 0; w < kOwnedWaves; ++w) f |= wfm[w][lane];
         uint32_t word = f << ((lane & 3) * 8);
         word |= __shfl_xor(word, 1);
         word |= __shfl_xor(word, 2);
@@ -625,8 +628,8 @@ static void launch_activation_typed(const uint16_t* xb, int64_t T, int64_t K, fl
     if (T <= kOwnedMaxT) {
         // few enough rows for one workgroup per column block: flags stored
         // whole, no clearing kernel
-        hipLaunchKernelGGL(k_detect_owned<HT>, dim3((unsigned)ceil_div(K, kOwnedCols)), dim3(256), 0,
-                           stream, xb, T, K, tau, ws.flags);
+        hipLaunchKernelGGL(k_detect_owned<HT>, dim3((unsigned)ceil_div(K, kOwnedCols)),
+                           dim3(kOwnedWaves * kWave), 0, stream, xb, T, K, tau, ws.flags);
     } else {
         int clear_blocks = (int)ceil_div(kw > 4 ? kw : 4, 256);
         hipLaunchKernelGGL(k_clear, dim3(clear_blocks), dim3(256), 0, stream, ws.flags, kw, ws.count);
