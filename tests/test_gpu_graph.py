@@ -43,3 +43,34 @@ def test_graph_replays_match_eager(mm, T, K, N):
         torch.cuda.synchronize()
         assert torch.equal(Y, eager), f"replay {rep} differs"
         assert torch.equal(other, eager)
+
+
+def test_concurrent_streams_match_eager(mm):
+    """Calls on two streams at once, each with its own workspace and output
+    (different shapes and routes: the single decode kernel, the K-slab
+    decode, the streaming tile, the large-tile kernel with K split): the
+    library keeps no state between calls, so every result must equal the
+    eager single-stream one."""
+    print("[case] concurrent streams", flush=True)
+    cases = []
+    for i, (T, K, N) in enumerate([(8, 8192, 1040), (8, 49152, 264), (64, 2048, 264),
+                                   (300, 24576, 520)]):
+        X, W = synth.random_case(41_000 + i, T, K, N, n_dims=3)
+        Xd, Wd = torch.from_numpy(X).cuda(), torch.from_numpy(W).cuda()
+        Wq, sw = mm.quantize_weight(Wd)
+        eager = mm.mixed_matmul(Xd, Wq, sw, Wd, 6.0).clone()
+        cases.append((Xd, Wq, sw, Wd, eager, mm.new_workspace(T, K, N),
+                      torch.empty((T, N), dtype=torch.float16, device="cuda")))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rep in range(3):
+        for c in cases:
+            c[6].fill_(0)
+        torch.cuda.synchronize()
+        for i, (Xd, Wq, sw, Wd, eager, ws, Y) in enumerate(cases):
+            with torch.cuda.stream(streams[i % 2]):
+                for _ in range(3):
+                    mm.mixed_matmul(Xd, Wq, sw, Wd, 6.0, workspace=ws, out=Y)
+        torch.cuda.synchronize()
+        for i, c in enumerate(cases):
+            assert torch.equal(c[6], c[4]), f"case {i} differs on pass {rep}"
