@@ -826,13 +826,14 @@ __global__ __launch_bounds__(128 * WN) void k_gemm_i8_big(GemmArgs a) {
 // one logical chunk) is free of bank conflicts for 8- and 16-lane service.
 __device__ __forceinline__ int stream_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-// Streaming kernel for few rows (T <= 128, K % 128 == 0): the matmul is bound
-// by the weight stream, so both operands go from global memory straight into
+// Streaming kernel for 9..256 rows with K % 128 == 0: the matmul is bound by
+// the weight stream, so both operands go from global memory straight into
 // LDS (global_load_lds_dwordx4, no VGPR staging) through a ring of STAGES
-// k-tiles of 128, STAGES - 1 of them in flight.  One barrier per k-tile: after it every wave's copies of
-// tile kt have landed and tile kt-1 is no longer read, so its buffer takes
-// tile kt+STAGES-1.  BM x BN tile, 4 waves of (BM/WAVES_M) x (BN/WAVES_N);
-// rows past T or N are clamped to the last row (never stored).
+// k-tiles of 128, STAGES - 1 of them in flight.  One barrier per k-tile:
+// after it every wave's copies of tile kt have landed and tile kt-1 is no
+// longer read, so its buffer takes tile kt+STAGES-1.  BM x BN tile over
+// WAVES_M x WAVES_N waves of (BM/WAVES_M) x (BN/WAVES_N); rows past T or N
+// are clamped to the last row (never stored).
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool WRITE_ACC, int HT>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_i8_stream(GemmArgs a) {
     constexpr int BK = 128;
