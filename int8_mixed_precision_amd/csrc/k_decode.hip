@@ -24,7 +24,7 @@
 //     transposed butterfly and LDS; ascending outlier indices by a popcount
 //     prefix scan; Xq to LDS;
 //   - Wq goes from global memory straight into registers as the A operand of
-//     v_mfma_i32_16x16x64_i8 (16 weight rows x 64 k), through a ring of three
+//     v_mfma_i32_16x16x64_i8 (16 weight rows x 64 k), through a ring of two
 //     chunks of 16 loads per wave; the B operand (the T activation rows as
 //     columns, zero padded) is read from LDS per k-step;
 //   - after the stream the workgroup dequantizes the int32 sums, adds the
@@ -222,10 +222,10 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
                 reinterpret_cast<uint4*>(&sm.acc[0][0][0])[q] = make_uint4(0u, 0u, 0u, 0u);
         }
     }
-    if (tid == 0) sm.next = 3 * kWaves;   // chunks 0 .. 23 go out statically
+    if (tid == 0) sm.next = 2 * kWaves;   // chunks 0 .. 15 go out statically
 
-    // wave w starts with chunks w, w + 8 and w + 16; later ones come from the
-    // LDS counter, so each wave's ids increase in the order it uses them.
+    // wave w starts with chunks w and w + 8; later ones come from the LDS
+    // counter, so each wave's ids increase in the order it uses them.
     // X is loaded before any weight: vector-memory counters retire in order,
     // so a wait on X would also wait for weight loads issued before it.  The
     // first chunk then goes out in four parts spread over the activation
@@ -235,8 +235,10 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
     // second chunk, measured slower).  Scheduling barriers keep each part
     // where it is.
     constexpr int G1 = kLoads / 4, G2 = kLoads / 2, G3 = 3 * kLoads / 4;
-    v4i ring[3][kLoads];
-    int id0 = wave, id1 = wave + kWaves, id2 = wave + 2 * kWaves;
+    // two slots: whole calls measured equal or faster than with three (T=4,
+    // K=4096, N=14336 19.1 -> 17.5 us; T=8, K=12288, N=36864 94.7 -> 93.0 us)
+    v4i ring[2][kLoads];
+    int id0 = wave, id1 = wave + kWaves;
 
     int o = 0, opad = 0;   // outlier count (and, precomputed mode, its padded value)
     if constexpr (!PRE) {
@@ -508,13 +510,12 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
         }
     }
     issue(id1, ring[1]);
-    issue(id2, ring[2]);
 
     // ---- stream the workgroup's chunks.  The loop body is unrolled over the
-    // three ring slots (compile-time register indices) and every slot is
+    // two ring slots (compile-time register indices) and every slot is
     // re-issued on every pass, with one exit test at the end: each path into
-    // a slot's use then has the two younger slots' loads behind it, so the
-    // wait before a chunk leaves them in flight.  A slot whose id is past the
+    // a slot's use then has the other slot's loads behind it, so the wait
+    // before a chunk leaves them in flight.  A slot whose id is past the
     // end skips its MFMAs (a uniform branch with no loads inside).  A chunk's
     // next id is taken from the LDS counter before its MFMAs, used after them.
     const int tcol = lane & 15;                         // B column = activation row t
@@ -557,7 +558,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
         }
         return __builtin_amdgcn_readfirstlane(nid);
     };
-    // ids increase in the order the slots are used (0, 1, 2, 0, ...), so once
+    // ids increase in the order the slots are used (0, 1, 0, ...), so once
     // slot 0's next id is past the end every pending one is
     if (id0 < total) {
         do {
@@ -565,8 +566,6 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
             issue(id0, ring[0]);
             id1 = consume(id1, ring[1]);
             issue(id1, ring[1]);
-            id2 = consume(id2, ring[2]);
-            issue(id2, ring[2]);
         } while (id0 < total);
     }
     if (!recover && !split) {
