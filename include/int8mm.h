@@ -77,9 +77,10 @@ const char* int8mm_status_string(int status);
  * 8192, T*K <= 65536) room for min(K, 512) outlier rows of N 16-bit values
  * into which the memory-halved variant (W16 = NULL) recovers the outlier
  * rows of W once per call (with more outliers, or without that room, the
- * matmul recovers them itself, more slowly).  For long K
- * (>= 24576) with a partial last round of 256 x 256 output tiles on the
- * current device, the matmul splits K in two and the size also covers, per
+ * matmul recovers them itself, more slowly).  For long K (>= 24576, or
+ * >= 8192 past 256 rows) with a partial last round of 256 x 256 output
+ * tiles on the current device, the matmul splits K in two and the size
+ * also covers, per
  * output tile, two 256 KB blocks of int32 partial sums and a counter; this
  * part depends on N and on the device's compute-unit count (256 when no
  * device can be queried).  A workspace at least as large as the size

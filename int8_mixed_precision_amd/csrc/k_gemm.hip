@@ -1026,10 +1026,13 @@ hipError_t launch_gemm_typed(const GemmArgs& a, hipStream_t stream) {
 // units and halves their length; it pays where that removes at least a
 // quarter of the rounds (e.g. 384 tiles on 256 CUs: 2 rounds -> 1.5) and K
 // is long enough that publishing and adding the 256 KB of partial sums per
-// tile is small against the half tile (measured: down projection T=2048,
-// K=49152, N=12288 13% faster; at K=12288 the split was slower).
+// tile is small against the half tile.  Measured, whole calls: down
+// projection T=2048, K=49152, N=12288 13% faster; T=512, K=12288: N=36864
+// 344 -> 304 us, N=49152 347 -> 342 us (T=384, N=49152 1% slower).  Up to
+// 256 rows the 256x128 streaming tile takes the shapes with K below 24576.
 int gemm_ksplit(int64_t T, int64_t K, int64_t N) {
-    if (!(T > 128 && K % 128 == 0 && K >= 24576)) return 1;
+    const int64_t kmin = T > 256 ? 8192 : 24576;
+    if (!(T > 128 && K % 128 == 0 && K >= kmin)) return 1;
     const int64_t tiles = ceil_div(T, 256) * ceil_div(N, 256);
     const int64_t cus = device_cus();
     const int64_t r1 = ceil_div(tiles, cus);          // rounds of whole tiles

@@ -59,6 +59,10 @@ def test_workspace_size(mm):
     # device the size query assumes 256 CUs)
     down = mm.workspace_size(2048, 49152, 12288)
     assert down >= 3 * 2048 * 49152 + 2 * 512 * 12288 + 384 * (2 * 65536 * 4 + 4)
+    # past 256 rows from K = 8192: T=512, N=36864 gives 288 tiles (2 rounds -> 1.5)
+    t512 = mm.workspace_size(512, 12288, 36864)
+    assert t512 >= 3 * 512 * 12288 + 2 * 512 * 36864 + 288 * (2 * 65536 * 4 + 4)
+    assert mm.workspace_size(256, 12288, 36864) < 3 * 256 * 12288 + 2 * 512 * 36864 + (1 << 20)
     t4096 = mm.workspace_size(4096, 49152, 12288)                         # 3 full rounds
     assert t4096 < 3 * 4096 * 49152 + 2 * 512 * 12288 + (1 << 20)
     # decode shapes run as one kernel and need only the fixed regions

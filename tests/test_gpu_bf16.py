@@ -99,7 +99,7 @@ def run_bf16(mm, name, X16, W16, tau, halved=False, big=None, rows=None):
     (16, 4096, 520, 5, 6.0, True), (8, 8192, 2056, 6, 6.0, True),
     (70, 1024, 136, 0, 0.0, False), (2, 4096, 136, 0, 0.0, False),       # tau = 0
     (65, 320, 96, 4, float("inf"), False),                               # tau = inf
-    (300, 24576, 520, 3, 6.0, True),                                     # K split in two
+    (300, 24576, 520, 3, 6.0, True), (300, 8192, 264, 5, 6.0, False),   # K split in two
     (6, 16384, 520, 5, 6.0, False), (8, 12288, 264, 30, 6.0, True),      # decode, precomputed
     (8, 49152, 264, 4, 6.0, True), (16, 32768, 136, 3, 6.0, False),      # decode, K slabs
     (16, 8192, 520, 5, 6.0, False), (50, 1152, 520, 3, 6.0, True),       # streaming matmul

@@ -114,6 +114,8 @@ def test_tiny_config(mm):
     # K split in two halves (K >= 24576 and few tiles): ragged T and N, and
     # 200 outliers through the second half's epilogue
     (300, 24576, 520, 3, "normal"), (129, 24576, 264, 200, "laplace"),
+    # past 256 rows the split starts at K = 8192
+    (300, 8192, 520, 3, "normal"), (513, 12288, 264, 70, "laplace"),
     # the mid-size-T tiles (32x128x256, 64x128x256, 64x128x128) with K not a
     # multiple of their k-tile, and T = 130 (K % 64 != 0) on 128x128x64
     (32, 1040, 264, 4, "normal"), (50, 1296, 520, 3, "laplace"), (100, 1104, 392, 5, "normal"),
@@ -205,6 +207,7 @@ def test_decode_precomputed(mm, T, K, N, nd, tau, halved):
     (64, 2048, 264, 600, 6.0), (100, 2048, 520, 40, 6.0),   # streaming kernel, W rows through LDS
     (30, 2048, 136, 0, 0.0),        # 30 rows, every dimension an outlier
     (160, 2048, 264, 300, 6.0),     # 256x128 streaming tile, recovered rows
+    (300, 8192, 264, 40, 6.0),      # K split in two past 256 rows
 ])
 def test_memory_halved(mm, T, K, N, nd, tau):
     """W16 = NULL: outlier rows recovered from the Int8 weight."""
