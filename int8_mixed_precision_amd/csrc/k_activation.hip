@@ -31,6 +31,7 @@ constexpr int kDetectCols = kDetectThreads * 8;   // columns per workgroup
 constexpr int kDetectRows = 16;                    // rows per workgroup
 constexpr int kCompactThreads = 1024;
 constexpr int kQuantThreads = 256;
+constexpr int kRowThreads = 512;            // k_rowquant_cached
 
 // Zeroes the outlier bitmap and the count before a detection pass.
 __global__ void k_clear(uint32_t* __restrict__ flags, int64_t kw, int32_t* __restrict__ count) {
@@ -260,6 +261,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_rowquant(
 
 // Exclusive prefix sum over the workgroup (wave scan by shuffles, wave
 // totals through LDS); total receives the workgroup's sum.
+template <int NT = kQuantThreads>
 __device__ inline int block_excl_scan(int v, int* wtot, int& total) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
     int incl = v;
@@ -273,7 +275,7 @@ __device__ inline int block_excl_scan(int v, int* wtot, int& total) {
     int before = 0;
     total = 0;
 #pragma unroll
-    for (int w = 0; w < kQuantThreads / kWave; ++w) {
+    for (int w = 0; w < NT / kWave; ++w) {
         before += w < wv ? wtot[w] : 0;
         total += wtot[w];
     }
@@ -288,18 +290,23 @@ __device__ inline int block_excl_scan(int v, int* wtot, int& total) {
 // words it holds in LDS for their prefix counts (a few words per lane), and
 // workgroup 0 writes the ascending index list and the count, so no separate
 // compaction kernel runs.
-// CACHE = 16-byte chunks per thread: K <= 16384 (8) or K <= 49152 (24).
-template <int HT, int kRowCache>
-__global__ __launch_bounds__(kQuantThreads) void k_rowquant_cached(
+// kRowCache = 16-byte chunks per thread, NT threads: K <= 16384 (4 x 512)
+// or K <= 49152 (12 x 512).  Fewer chunks per thread and more threads per
+// row than 8 x 256 and 24 x 256 raised the occupancy: K = 49152, T = 2048
+// activation pass 124 -> 103 us; T = 4096 264 -> 222 us; K = 8192, T = 256
+// 11.1 -> 10.1 us; K = 12288 within 2% either way (6 x 1024 and 8 x 768
+// were no faster than 24 x 256).
+template <int HT, int kRowCache, int NT>
+__global__ __launch_bounds__(NT) void k_rowquant_cached(
     const uint16_t* __restrict__ X, int64_t K, const uint32_t* __restrict__ flags,
     int32_t* __restrict__ idx, int32_t* __restrict__ count,
     int8_t* __restrict__ xq, float* __restrict__ sx, uint16_t* __restrict__ xo) {
-    constexpr int KW = kQuantThreads * kRowCache / 4;                  // bitmap words held
-    constexpr int WPT = (KW + kQuantThreads - 1) / kQuantThreads;      // words per lane
-    __shared__ float red[kQuantThreads / kWave];
+    constexpr int KW = NT * kRowCache / 4;                  // bitmap words held
+    constexpr int WPT = (KW + NT - 1) / NT;      // words per lane
+    __shared__ float red[NT / kWave];
     __shared__ uint32_t fl[KW];
     __shared__ int pf[KW];
-    __shared__ int wtot[kQuantThreads / kWave];
+    __shared__ int wtot[NT / kWave];
     const int tid = threadIdx.x;
     const int64_t t = blockIdx.x;
     const uint16_t* row = X + t * K;
@@ -307,11 +314,11 @@ __global__ __launch_bounds__(kQuantThreads) void k_rowquant_cached(
     uint4 v[kRowCache];
 #pragma unroll
     for (int i = 0; i < kRowCache; ++i) {
-        const int c = tid + kQuantThreads * i;
+        const int c = tid + NT * i;
         v[i] = *reinterpret_cast<const uint4*>(row + (c < nch ? c : 0) * 8);
     }
     const int kw = (nch + 3) / 4;
-    for (int w = tid; w < kw; w += kQuantThreads) fl[w] = flags[w];
+    for (int w = tid; w < kw; w += NT) fl[w] = flags[w];
     __syncthreads();
     // outliers before each word: lane l takes words WPT l .. WPT l + WPT - 1
     int o = 0;
@@ -322,7 +329,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_rowquant_cached(
             const int w = WPT * tid + i;
             if (w < kw) cnt += __builtin_popcount(fl[w]);
         }
-        int run = block_excl_scan(cnt, wtot, o);
+        int run = block_excl_scan<NT>(cnt, wtot, o);
 #pragma unroll
         for (int i = 0; i < WPT; ++i) {
             const int w = WPT * tid + i;
@@ -348,7 +355,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_rowquant_cached(
     float mx = 0.0f;
 #pragma unroll
     for (int i = 0; i < kRowCache; ++i) {
-        const int c = tid + kQuantThreads * i;
+        const int c = tid + NT * i;
         if (c < nch) {
             const uint32_t fm = (fl[c >> 2] >> ((c & 3) * 8)) & 0xFFu;
             const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
@@ -364,12 +371,12 @@ __global__ __launch_bounds__(kQuantThreads) void k_rowquant_cached(
     __syncthreads();   // red, and the word prefixes pf
     mx = red[0];
 #pragma unroll
-    for (int i = 1; i < kQuantThreads / kWave; ++i) mx = __builtin_fmaxf(mx, red[i]);
+    for (int i = 1; i < NT / kWave; ++i) mx = __builtin_fmaxf(mx, red[i]);
     const float r = mx > 0.0f ? 127.0f / mx : 0.0f;
     uint16_t* xo_row = xo + t * opad;
 #pragma unroll
     for (int i = 0; i < kRowCache; ++i) {
-        const int c = tid + kQuantThreads * i;
+        const int c = tid + NT * i;
         if (c >= nch) continue;
         const uint32_t word = fl[c >> 2];
         const uint32_t fm = (word >> ((c & 3) * 8)) & 0xFFu;
@@ -394,7 +401,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_rowquant_cached(
             }
         }
     }
-    for (int j = o + tid; j < opad; j += kQuantThreads) xo_row[j] = 0;   // +0 in both types
+    for (int j = o + tid; j < opad; j += NT) xo_row[j] = 0;   // +0 in both types
     if (tid == 0) sx[t] = mx;
 }
 
@@ -638,11 +645,11 @@ static void launch_activation_typed(const uint16_t* xb, int64_t T, int64_t K, fl
         hipLaunchKernelGGL(k_detect<HT>, dgrid, dim3(kDetectThreads), 0, stream, xb, T, K, tau, ws.flags);
     }
     // rows held in registers: the quantize kernel isolates the outliers too
-    if (K <= (int64_t)kQuantThreads * 8 * 8) {
-        hipLaunchKernelGGL((k_rowquant_cached<HT, 8>), dim3((unsigned)T), dim3(kQuantThreads), 0,
+    if (K <= (int64_t)kRowThreads * 4 * 8) {
+        hipLaunchKernelGGL((k_rowquant_cached<HT, 4, kRowThreads>), dim3((unsigned)T), dim3(kRowThreads), 0,
                            stream, xb, K, ws.flags, ws.idx, ws.count, ws.xq, ws.sx, ws.xo);
-    } else if (K <= (int64_t)kQuantThreads * 24 * 8) {
-        hipLaunchKernelGGL((k_rowquant_cached<HT, 24>), dim3((unsigned)T), dim3(kQuantThreads), 0,
+    } else if (K <= (int64_t)kRowThreads * 12 * 8) {
+        hipLaunchKernelGGL((k_rowquant_cached<HT, 12, kRowThreads>), dim3((unsigned)T), dim3(kRowThreads), 0,
                            stream, xb, K, ws.flags, ws.idx, ws.count, ws.xq, ws.sx, ws.xo);
     } else {
         hipLaunchKernelGGL(k_compact, dim3(1), dim3(kCompactThreads), 0, stream, ws.flags, kw,
