@@ -139,6 +139,19 @@ def test_ragged_shapes(mm, T, K, N, nd, dist):
     run_case(mm, f"ragged {T}x{K}x{N}", X, W, 6.0)
 
 
+@pytest.mark.parametrize("T,K,nd,dist", [
+    (130, 16384, 5, "normal"),    # register-cached row quantizer, 4 chunks per lane: every word held
+    (130, 16400, 5, "normal"),    # 12 chunks per lane, most of them past the row
+    (129, 49152, 40, "laplace"),  # 12 chunks per lane, every word held, many outliers
+    (129, 49168, 7, "normal"),    # past the register cache: separate compaction, two-pass rows
+])
+def test_row_quantizer_limits(mm, T, K, nd, dist):
+    """The activation pass for more than 128 rows at the row lengths where
+    the row quantizer changes form."""
+    X, W = synth.random_case(60_000 + K, T, K, 136, n_dims=nd, x_dist=dist)
+    run_case(mm, f"row quantizer {T}x{K}x136", X, W, 6.0)
+
+
 def _random_shapes(n=24, seed=2024, max_macs=6e8):
     """Seeded shapes spread over every route of the library: row counts of
     the decode kernel, the streaming tiles and the large-tile kernel, K with
