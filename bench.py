@@ -586,8 +586,8 @@ def cpu_baseline(synth, T, K, N):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the multi-GPU sharding is a design note only)", file=sys.stderr)
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
+              "(sharding over several GPUs is described, not implemented)", file=sys.stderr)
         sys.exit(2)
     import torch
 

@@ -58,8 +58,8 @@ typedef enum {
     INT8MM_E_TAU = 3,         /* tau is NaN or negative */
     INT8MM_E_ALIGN = 4,       /* a pointer is not 16-byte aligned */
     INT8MM_E_WORKSPACE = 5,   /* workspace smaller than the size query returns */
-    INT8MM_E_UNSUPPORTED = 6, /* a valid request this build does not implement (no entry
-                                 point returns it today; kept so codes stay stable) */
+    INT8MM_E_UNSUPPORTED = 6, /* a request the library does not implement: a checkpoint
+                                 type code other than the INT8MM_WEIGHT_* values */
     INT8MM_E_HIP = 7          /* the HIP runtime reported a launch error */
 } int8mm_status;
 
