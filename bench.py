@@ -232,8 +232,12 @@ def bench_prefill(torch, mm, synth, steps, warmup, variants=True):
     o = int(dbg["count"][0])
     if variants:
         ours = lambda: mm.matmul_prepared(ws, T, K, Wq, sw, W16, out=Y)
-        extra["vendor_int8_gemm"] = vendor_int8_gemm(torch, dbg["xq"], Wq.view(N, K), steps, warmup,
+        # the converted weight as a plain [N,K] matrix (panels of 256 rows,
+        # k-tiles of 64 columns; both divide this workload's N and K)
+        wq_rows = Wq.view(N // 256, K // 64, 256, 64).permute(0, 2, 1, 3).reshape(N, K)
+        extra["vendor_int8_gemm"] = vendor_int8_gemm(torch, dbg["xq"], wq_rows, steps, warmup,
                                                      ours)
+        del wq_rows
     del dbg
     ops = 2.0 * T * K * N
     ms_step = wall * 1e3 / steps

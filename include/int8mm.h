@@ -25,7 +25,8 @@
  * Conventions for every entry point:
  *   - Pointers are DEVICE pointers unless noted.  All buffers are owned by
  *     the caller; the library never allocates or frees memory on any call.
- *   - Matrices are row-major and dense (leading dimension = row length).
+ *   - Matrices are row-major and dense (leading dimension = row length),
+ *     except the converted weight, whose layout int8_quantize_weight gives.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *     enqueue work on it and return without synchronizing; results are valid
  *     once the stream reaches that point.
@@ -96,15 +97,25 @@ int int8_mixed_matmul_workspace_size(int64_t T, int64_t K, int64_t N, size_t* by
 
 /* Bytes of the converted weight Wq for a [K,N] weight (host only, enqueues
  * nothing); currently K*N.  Callers size Wq with this query: the layout is
- * the library's.  Errors: E_NULL, E_SHAPE. */
+ * the library's (see int8_quantize_weight).  Errors: E_NULL, E_SHAPE. */
 int int8_quantize_weight_size(int64_t K, int64_t N, size_t* bytes);
 
 /* Weight conversion to Int8 ("converted to Int8" at load time, LLM.int8()
  * abstract): column-wise absmax quantization, one scale per output column
  * n (one per inner product).
  *   W16: fp16 [K,N] row-major (read only)
- *   Wq:  int8, int8_quantize_weight_size() bytes: [N,K] row-major, i.e. the
- *        transpose of W with K contiguous, Wq[n*K + k] (written)
+ *   Wq:  int8, int8_quantize_weight_size() bytes (written): the transpose of
+ *        W, [N,K], in a panel-blocked layout.  Rows n are grouped in panels
+ *        of 256 (the last panel has N % 256 rows when that is not 0); a
+ *        panel's K range is cut into k-tiles of 64 columns (the last one is
+ *        K % 64 wide when that is not 0); each (panel, k-tile) block is
+ *        stored row-major, blocks follow each other in k order inside a
+ *        panel and panels in row order, with no padding.  Element (n, k),
+ *        with p0 = n - n % 256, rows = min(256, N - p0), k0 = k - k % 64 and
+ *        w = min(64, K - k0), is at byte
+ *            p0*K + k0*rows + (n - p0)*w + (k - k0).
+ *        (16 consecutive rows of one k-tile are one contiguous kilobyte,
+ *        which is how the matmul kernels copy them.)
  *   sw:  fp32 [N] column scales s_w[n] = max_k |W[k,n]| (written)
  * Errors: E_NULL, E_SHAPE, E_ALIGN, E_HIP. */
 int int8_quantize_weight(const void* W16, int64_t K, int64_t N, int8_t* Wq, float* sw,

@@ -142,7 +142,8 @@ def weight_bytes(K: int, N: int) -> int:
 
 def quantize_weight(W16: torch.Tensor, out: tuple | None = None):
     """W16 fp16 [K,N] -> (Wq int8 [weight_bytes(K,N)], the library's layout
-    (currently [N,K] row-major), sw fp32 [N])."""
+    (the transpose [N,K], panel-blocked as include/int8mm.h describes),
+    sw fp32 [N])."""
     _need(W16, torch.float16, 2, "W16")
     K, N = W16.shape
     if out is None:

@@ -91,7 +91,36 @@ __device__ __forceinline__ uint16_t recover_weight(int8_t q, float d) {
     return f32_to_h16<HT>(v);
 }
 
-// Bytes of the converted weight: int8 [N,K] row-major (K contiguous).
+// Panel-blocked int8 layout of an [R,K] operand of the int8 matmul (the
+// converted weight, R = N, and the quantized activations in the workspace,
+// R = T): rows are grouped in panels of kPanel rows (the last panel may be
+// shorter), a panel's K range is cut into k-tiles of kKTile columns (the
+// last may be narrower, always a multiple of 16), and each (panel, k-tile)
+// block is stored row-major.  So the kKTile bytes of 16 consecutive rows of
+// one k-tile are one contiguous kilobyte: a wave's 16-byte-per-lane copy of
+// a tile slice touches 8 whole 128-byte lines instead of halves of 16 (the
+// CU's L2 -> LDS copy rate with 64-byte row pieces is about two thirds of
+// the rate with whole lines).  The blocks of a panel follow each other in k
+// order, the panels in row order; nothing is padded (R*K bytes in all).
+constexpr int64_t kPanel = 256;
+constexpr int64_t kKTile = 64;
+
+// Rows of the panel that holds row r.
+__host__ __device__ inline int64_t blk_rows(int64_t r, int64_t R) {
+    const int64_t p0 = r - r % kPanel;
+    return R - p0 < kPanel ? R - p0 : kPanel;
+}
+
+// Byte offset of element (r, k) of an [R,K] operand in the panel-blocked layout.
+__host__ __device__ inline int64_t blk_offset(int64_t r, int64_t k, int64_t R, int64_t K) {
+    const int64_t p0 = r - r % kPanel;          // first row of the panel
+    const int64_t rows = R - p0 < kPanel ? R - p0 : kPanel;
+    const int64_t k0 = k - k % kKTile;          // first column of the k-tile
+    const int64_t w = K - k0 < kKTile ? K - k0 : kKTile;
+    return p0 * K + k0 * rows + (r - p0) * w + (k - k0);
+}
+
+// Bytes of the converted weight: int8 [N,K] in the panel-blocked layout.
 inline int64_t wq_bytes(int64_t K, int64_t N) { return K * N; }
 
 // Compute units of the current device (256 if it cannot be queried).

@@ -200,7 +200,7 @@ __device__ inline int8_t quant(float x, float r) {
 // unchanged) into xo.
 template <int HT>
 __global__ __launch_bounds__(kQuantThreads) void k_rowquant(
-    const uint16_t* __restrict__ X, int64_t K, const uint32_t* __restrict__ flags,
+    const uint16_t* __restrict__ X, int64_t T, int64_t K, const uint32_t* __restrict__ flags,
     const int32_t* __restrict__ wprefix, const int32_t* __restrict__ count,
     int8_t* __restrict__ xq, float* __restrict__ sx, uint16_t* __restrict__ xo) {
     __shared__ float red[kQuantThreads / kWave];
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_rowquant(
             uint32_t q = ((fm >> e) & 1u) ? 0u : (uint32_t)(uint8_t)quant(x, r);
             packed[e >> 2] |= q << ((e & 3) * 8);
         }
-        *reinterpret_cast<uint2*>(xq + t * K + c * 8) = make_uint2(packed[0], packed[1]);
+        *reinterpret_cast<uint2*>(xq + blk_offset(t, c * 8, T, K)) = make_uint2(packed[0], packed[1]);
         if (fm) {
             const int base_bit = (int)(c & 3) * 8;
 #pragma unroll
@@ -298,7 +298,7 @@ __device__ inline int block_excl_scan(int v, int* wtot, int& total) {
 // were no faster than 24 x 256).
 template <int HT, int kRowCache, int NT>
 __global__ __launch_bounds__(NT) void k_rowquant_cached(
-    const uint16_t* __restrict__ X, int64_t K, const uint32_t* __restrict__ flags,
+    const uint16_t* __restrict__ X, int64_t T, int64_t K, const uint32_t* __restrict__ flags,
     int32_t* __restrict__ idx, int32_t* __restrict__ count,
     int8_t* __restrict__ xq, float* __restrict__ sx, uint16_t* __restrict__ xo) {
     constexpr int KW = NT * kRowCache / 4;                  // bitmap words held
@@ -388,7 +388,7 @@ __global__ __launch_bounds__(NT) void k_rowquant_cached(
             const uint32_t q = ((fm >> e) & 1u) ? 0u : (uint32_t)(uint8_t)quant(x, r);
             packed[e >> 2] |= q << ((e & 3) * 8);
         }
-        *reinterpret_cast<uint2*>(xq + t * K + (int64_t)c * 8) = make_uint2(packed[0], packed[1]);
+        *reinterpret_cast<uint2*>(xq + blk_offset(t, (int64_t)c * 8, T, K)) = make_uint2(packed[0], packed[1]);
         if (fm) {
             const int base_bit = (c & 3) * 8;
 #pragma unroll
@@ -595,7 +595,7 @@ __global__ __launch_bounds__(kSegThreads) void k_seg_quant(
                 const uint32_t q = ((fm >> e) & 1u) ? 0u : (uint32_t)(uint8_t)quant(x, rr);
                 packed[e >> 2] |= q << ((e & 3) * 8);
             }
-            *reinterpret_cast<uint2*>(xq + t * K + c0) = make_uint2(packed[0], packed[1]);
+            *reinterpret_cast<uint2*>(xq + blk_offset(t, c0, T, K)) = make_uint2(packed[0], packed[1]);
             if (fm) {
                 int pos = pos0;
 #pragma unroll
@@ -647,15 +647,15 @@ static void launch_activation_typed(const uint16_t* xb, int64_t T, int64_t K, fl
     // rows held in registers: the quantize kernel isolates the outliers too
     if (K <= (int64_t)kRowThreads * 4 * 8) {
         hipLaunchKernelGGL((k_rowquant_cached<HT, 4, kRowThreads>), dim3((unsigned)T), dim3(kRowThreads), 0,
-                           stream, xb, K, ws.flags, ws.idx, ws.count, ws.xq, ws.sx, ws.xo);
+                           stream, xb, T, K, ws.flags, ws.idx, ws.count, ws.xq, ws.sx, ws.xo);
     } else if (K <= (int64_t)kRowThreads * 12 * 8) {
         hipLaunchKernelGGL((k_rowquant_cached<HT, 12, kRowThreads>), dim3((unsigned)T), dim3(kRowThreads), 0,
-                           stream, xb, K, ws.flags, ws.idx, ws.count, ws.xq, ws.sx, ws.xo);
+                           stream, xb, T, K, ws.flags, ws.idx, ws.count, ws.xq, ws.sx, ws.xo);
     } else {
         hipLaunchKernelGGL(k_compact, dim3(1), dim3(kCompactThreads), 0, stream, ws.flags, kw,
                            ws.wprefix, ws.idx, ws.count);
         hipLaunchKernelGGL(k_rowquant<HT>, dim3((unsigned)T), dim3(kQuantThreads), 0, stream, xb,
-                           K, ws.flags, ws.wprefix, ws.count, ws.xq, ws.sx, ws.xo);
+                           T, K, ws.flags, ws.wprefix, ws.count, ws.xq, ws.sx, ws.xo);
     }
 }
 
@@ -666,6 +666,20 @@ hipError_t launch_activation_pass(const uint16_t* X, int ht, int64_t T, int64_t 
     return hipGetLastError();
 }
 
+namespace {
+// Debug copy of the quantized activations: the workspace's panel-blocked
+// Xq to a row-major [T,K] array, one 16-byte piece per thread.
+__global__ void k_unblock(const int8_t* __restrict__ src, int64_t T, int64_t K,
+                          int8_t* __restrict__ dst) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t per = K / 16;
+    if (i >= T * per) return;
+    const int64_t t = i / per, k = (i - t * per) * 16;
+    *reinterpret_cast<uint4*>(dst + t * K + k) =
+        *reinterpret_cast<const uint4*>(src + blk_offset(t, k, T, K));
+}
+}  // namespace
+
 hipError_t launch_debug_copies(const Workspace& ws, int64_t T, int64_t K, int32_t* count,
                                int32_t* idx, int8_t* xq, float* sx, hipStream_t stream) {
     hipError_t e = hipSuccess;
@@ -674,8 +688,12 @@ hipError_t launch_debug_copies(const Workspace& ws, int64_t T, int64_t K, int32_
     if (idx && e == hipSuccess)
         e = hipMemcpyAsync(idx, ws.idx, sizeof(int32_t) * (size_t)K, hipMemcpyDeviceToDevice,
                            stream);
-    if (xq && e == hipSuccess)
-        e = hipMemcpyAsync(xq, ws.xq, (size_t)(T * K), hipMemcpyDeviceToDevice, stream);
+    if (xq && e == hipSuccess) {
+        const int64_t pieces = T * (K / 16);
+        hipLaunchKernelGGL(k_unblock, dim3((unsigned)ceil_div(pieces, 256)), dim3(256), 0, stream,
+                           ws.xq, T, K, xq);
+        e = hipGetLastError();
+    }
     if (sx && e == hipSuccess)
         e = hipMemcpyAsync(sx, ws.sx, sizeof(float) * (size_t)T, hipMemcpyDeviceToDevice, stream);
     return e;

@@ -189,20 +189,29 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
     const int total = nbw * cpb;
 
     // Load i of a chunk: lane l holds weight row n0 + 16 (id / cpb) + l % 16
-    // and bytes 1024 (id % cpb) + 64 i + 16 (l / 16) .. +16.  Ids past the end
-    // read the first kilobyte of Wq on every lane instead (one line per
-    // load, never used): loads stay unconditional, so the wait counts stay
-    // exact.
+    // and bytes 1024 (id % cpb) + 64 i + 16 (l / 16) .. +16 of its k range.
+    // In the panel-blocked layout (K % 1024 == 0, so every k-tile is 64
+    // wide) a block's 16 rows lie in one panel and load i reads one
+    // contiguous kilobyte of k-tile 16 (id % cpb) + i; consecutive loads are
+    // one block (64 x the panel's rows) apart.  Ids past the end read the
+    // first 16 bytes of Wq on every lane instead (never used): loads stay
+    // unconditional, so the wait counts stay exact.
     const int kl = (lane >> 4) * 16;
     // loads lo .. hi-1 of chunk id into buf (lo and hi are constants)
     auto issue_part = [&](int id, v4i (&buf)[kLoads], int lo, int hi) {
         const int n = n0 + (id / cpb) * kRows + (lane & 15);
-        const int64_t off =
-            id < total ? (int64_t)(n < N ? n : N - 1) * K + kbase + (id % cpb) * kChunkK + kl : 0;
+        const int64_t nc = n < N ? n : N - 1;
+        const int64_t p0 = nc - nc % kPanel;
+        const int64_t prow = N - p0 < kPanel ? N - p0 : kPanel;
+        const bool live = id < total;
+        const int64_t off = live ? p0 * K + (int64_t)(kbase + (id % cpb) * kChunkK) * prow +
+                                       (nc - p0) * kKTile + kl
+                                 : 0;
+        const int64_t step = live ? kKTile * prow : 0;
         const int8_t* p = a.wq + off;
 #pragma unroll
         for (int i = 0; i < kLoads; ++i)
-            if (i >= lo && i < hi) buf[i] = *reinterpret_cast<const v4i*>(p + i * 64);
+            if (i >= lo && i < hi) buf[i] = *reinterpret_cast<const v4i*>(p + i * step);
     };
     auto issue = [&](int id, v4i (&buf)[kLoads]) { issue_part(id, buf, 0, kLoads); };
 
@@ -457,7 +466,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
         for (int u = 0; u < XV; ++u) {
             const int i = tid + kThreads * u;
             const int t = i / pr, c = i - t * pr;
-            xv[u] = i < nx ? *reinterpret_cast<const uint4*>(a.xq_pre + (int64_t)t * K + kbase + c * 16)
+            xv[u] = i < nx ? *reinterpret_cast<const uint4*>(a.xq_pre + blk_offset(t, kbase + c * 16, T, K))
                            : make_uint4(0u, 0u, 0u, 0u);
         }
         issue(id0, ring[0]);
@@ -615,7 +624,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
             const float xv = j < OXL ? sm.xo[t * OXL + j]
                              : PRE ? h16_to_f32<HT>(a.xo_pre[(int64_t)t * opad + j])
                                    : h16_to_f32<HT>(a.x[(int64_t)t * K + k]);
-            const uint16_t w = recover ? recover_weight<HT>(a.wq[(int64_t)n * K + k], sm.sw[r] / 127.0f)
+            const uint16_t w = recover ? recover_weight<HT>(a.wq[blk_offset(n, k, N, K)], sm.sw[r] / 127.0f)
                                        : a.w16[(int64_t)k * N + n];
             y += xv * h16_to_f32<HT>(w);
         }
@@ -651,7 +660,7 @@ __global__ __launch_bounds__(256) void k_decode_finish(DecodeArgs a) {
     const uint16_t* xo = a.xo_pre + (int64_t)t * opad;
     for (int j = 0; j < o; ++j) {
         const int k = a.idx_pre[j];
-        const uint16_t w = recover ? recover_weight<HT>(a.wq[(int64_t)n * K + k], dr)
+        const uint16_t w = recover ? recover_weight<HT>(a.wq[blk_offset(n, k, N, K)], dr)
                                    : a.w16[(int64_t)k * N + n];
         y += h16_to_f32<HT>(xo[j]) * h16_to_f32<HT>(w);
     }

@@ -10,8 +10,11 @@
 //   y  += sum_{j<o} X[t,idx_j] * W16[idx_j,n]        fp16 MFMA, fp32 accumulation
 //   Y   = fp16(y)                                    one rounding
 //
-// gfx950 design: both operands are K-contiguous (Xq [T,K], Wq [N,K]), so a
-// lane's 16 int8 of an MFMA operand are one 16-byte load.  Tiles are staged
+// gfx950 design: both operands are K-contiguous (Xq [T,K], Wq [N,K], each
+// in the panel-blocked layout of common.hpp: 256-row panels cut into
+// 64-column k-tiles, every (panel, k-tile) block row-major), so a lane's 16
+// int8 of an MFMA operand are one 16-byte load and a wave's copy of 16 rows
+// of a k-tile is one contiguous kilobyte.  Tiles are staged
 // through LDS, double-buffered, with an XOR swizzle of the 16-byte chunks so
 // the ds_read_b128 of the operand fragments avoid bank conflicts.  The
 // 16-bit outlier product reuses the dequantized fp32 accumulators as the C
@@ -184,11 +187,18 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a,
                         dcol[c] = n < N ? a.sw[n] / 127.0f : 0.0f;
                     }
                 }
+                // Wq byte (n, k) of this tile's panel (K % 64 == 0 here):
+                // wbase + the k part + 64 (n - wp0)
+                const int64_t wp0 = sc.n0 - sc.n0 % kPanel;
+                const int64_t wrows = N - wp0 < kPanel ? N - wp0 : kPanel;
                 int k_next = e < o ? (by_pos ? e : a.idx[e]) : -1;
                 uint4 wv[NV];
                 auto load_chunk = [&](int jc) {
                     const int k = k_next;
                     k_next = jc + kOC + e < o ? (by_pos ? jc + kOC + e : a.idx[jc + kOC + e]) : -1;
+                    const int kc = k < 0 ? 0 : k;   // (k < 0: nothing is read)
+                    const int8_t* wk = a.wq + wp0 * a.K + (int64_t)(kc & ~(int)(kKTile - 1)) * wrows +
+                                       (kc & (int)(kKTile - 1)) - wp0 * kKTile;
 #pragma unroll
                     for (int h = 0; h < NV; ++h) {
                         const int64_t n = sc.n0 + cb * CPB + h * 8;
@@ -202,10 +212,10 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a,
                             for (int c = 0; c < 8; c += 2) {
                                 const int64_t nc = n + c;
                                 const uint16_t lo = (k >= 0 && nc < N)
-                                                        ? recover_weight<HT>(a.wq[nc * a.K + k], dcol[h * 8 + c])
+                                                        ? recover_weight<HT>(wk[nc * kKTile], dcol[h * 8 + c])
                                                         : (uint16_t)0;
                                 const uint16_t hi = (k >= 0 && nc + 1 < N)
-                                                        ? recover_weight<HT>(a.wq[(nc + 1) * a.K + k],
+                                                        ? recover_weight<HT>(wk[(nc + 1) * kKTile],
                                                                              dcol[h * 8 + c + 1])
                                                         : (uint16_t)0;
                                 p[c >> 1] = (uint32_t)lo | ((uint32_t)hi << 16);
@@ -285,7 +295,7 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a,
     #pragma unroll
                     for (int e = 0; e < 8; ++e)
                         wb[j][e] = (kk[e] >= 0 && n < N)
-                                       ? recover_weight<HT>(a.wq[n * a.K + kk[e]], dn[j])
+                                       ? recover_weight<HT>(a.wq[blk_offset(n, kk[e], N, a.K)], dn[j])
                                        : (uint16_t)0;
                 }
             }
@@ -330,11 +340,17 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a,
         }
         // k: the W16 row of slot e (the outlier's dimension, or its position
         // for recovered rows), or the dimension whose Wq bytes are recovered
+        // (the tile's columns are one panel of the blocked Wq and K % 64 ==
+        // 0: byte (n, k) is at wk[64 (n - n0)] for the k part wk)
+        const int64_t wrows = N - sc.n0 < kPanel ? N - sc.n0 : kPanel;
         int k_next = e < o ? (by_pos ? e : a.idx[e]) : -1;
         uint4 wv[2], xv[2];
         auto load_chunk = [&](int jc) {
             const int k = k_next;
             k_next = jc + kOC + e < o ? (by_pos ? jc + kOC + e : a.idx[jc + kOC + e]) : -1;
+            const int kc = k < 0 ? 0 : k;   // (k < 0: nothing is read)
+            const int8_t* wk = a.wq + sc.n0 * a.K + (int64_t)(kc & ~(int)(kKTile - 1)) * wrows +
+                               (kc & (int)(kKTile - 1));
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int64_t n = sc.n0 + cb * 16 + h * 8;
@@ -346,12 +362,12 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a,
                     uint32_t p[4];
 #pragma unroll
                     for (int c = 0; c < 8; c += 2) {
-                        const int64_t n0c = n + c;
-                        const uint16_t lo = (k >= 0 && n0c < N)
-                                                ? recover_weight<HT>(a.wq[n0c * a.K + k], dcol[h * 8 + c])
+                        const int nl = cb * 16 + h * 8 + c;   // column inside the tile
+                        const uint16_t lo = (k >= 0 && n + c < N)
+                                                ? recover_weight<HT>(wk[nl * kKTile], dcol[h * 8 + c])
                                                 : (uint16_t)0;
-                        const uint16_t hi = (k >= 0 && n0c + 1 < N)
-                                                ? recover_weight<HT>(a.wq[(n0c + 1) * a.K + k],
+                        const uint16_t hi = (k >= 0 && n + c + 1 < N)
+                                                ? recover_weight<HT>(wk[(nl + 1) * kKTile],
                                                                      dcol[h * 8 + c + 1])
                                                 : (uint16_t)0;
                         p[c >> 1] = (uint32_t)lo | ((uint32_t)hi << 16);
@@ -502,7 +518,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_i8(GemmArgs a) {
             const int id = i * kThreads + tid;
             const int row = id / C::CPR, c = id % C::CPR;
             const int64_t gm = m0 + row, gk = k0 + c * 16;
-            ra[i] = (gm < T && gk < K) ? *reinterpret_cast<const v4i*>(a.xq + gm * K + gk)
+            ra[i] = (gm < T && gk < K) ? *reinterpret_cast<const v4i*>(a.xq + blk_offset(gm, gk, T, K))
                                        : v4i{0, 0, 0, 0};
         }
 #pragma unroll
@@ -510,7 +526,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_i8(GemmArgs a) {
             const int id = i * kThreads + tid;
             const int row = id / C::CPR, c = id % C::CPR;
             const int64_t gn = n0 + row, gk = k0 + c * 16;
-            rb[i] = (gn < N && gk < K) ? *reinterpret_cast<const v4i*>(a.wq + gn * K + gk)
+            rb[i] = (gn < N && gk < K) ? *reinterpret_cast<const v4i*>(a.wq + blk_offset(gn, gk, N, K))
                                        : v4i{0, 0, 0, 0};
         }
     };
@@ -662,9 +678,13 @@ __global__ __launch_bounds__(128 * WN) void k_gemm_i8_big(GemmArgs a) {
 
     // copy assignment: wave w fills the 1 KB groups GPW*w .. GPW*w+GPW-1 of A
     // and of B; in a group, lane l writes row 16g + l/4, physical chunk l%4.
-    // Copy u < GPW is an A group, u >= GPW a B group.  Addresses are a
-    // per-workgroup scalar base plus a 32-bit lane offset (a 256-row panel
-    // spans at most 256 * 133136 bytes).
+    // Copy u < GPW is an A group, u >= GPW a B group.  The tile's rows are
+    // one panel of the blocked layout (m0 and n0 are multiples of 256), whose
+    // k-tile kt is a block of rows x 64 bytes, row r at 64 r: an address is a
+    // per-workgroup scalar base plus a 32-bit lane offset inside the block,
+    // and a group's 16 rows are one contiguous kilobyte.
+    static_assert(BK == kKTile && BM == kPanel && BN == kPanel, "tile = panel x k-tile");
+    const int64_t arows = T - m0 < BM ? T - m0 : BM, brows = N - n0 < BN ? N - n0 : BN;
     const int8_t* abase = a.xq + m0 * K;
     const int8_t* bbase = a.wq + n0 * K;
     uint32_t goff[LOADS];
@@ -672,14 +692,14 @@ __global__ __launch_bounds__(128 * WN) void k_gemm_i8_big(GemmArgs a) {
     for (int u = 0; u < GPW; ++u) {
         const int row = (wave * GPW + u) * 16 + (lane >> 2);
         const int c = (lane & 3) ^ big_swz(row);
-        const int64_t ra = m0 + row < T ? row : T - 1 - m0;
-        const int64_t rb = n0 + row < N ? row : N - 1 - n0;
-        goff[u] = (uint32_t)(ra * K + c * 16);
-        goff[GPW + u] = (uint32_t)(rb * K + c * 16);
+        const int64_t ra = row < arows ? row : arows - 1;
+        const int64_t rb = row < brows ? row : brows - 1;
+        goff[u] = (uint32_t)(ra * BK + c * 16);
+        goff[GPW + u] = (uint32_t)(rb * BK + c * 16);
     }
     auto copy = [&](int u, int kt, int stage) {
         const bool isa = u < GPW;
-        const int8_t* base = (isa ? abase : bbase) + (int64_t)kt * BK;
+        const int8_t* base = isa ? abase + (int64_t)kt * BK * arows : bbase + (int64_t)kt * BK * brows;
         const int8_t* dst = lds + stage * STAGE_BYTES + (isa ? 0 : BM * BK) +
                             (wave * GPW + (isa ? u : u - GPW)) * 1024;
         copy_to_lds16(base, goff[u], dst);
@@ -861,10 +881,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_i8_stream(GemmA
     // copy u of this wave fills 1 KB group g = LOADS * wave + u of the tile
     // (g < GA: rows 8g .. 8g+7 of A, else rows 8(g - GA) .. of B); lane l
     // writes row 8g + l/8 at physical chunk l%8, so it fetches the logical
-    // chunk (l%8) ^ stream_swz(row).  32-bit lane offsets (a 128-row panel
-    // spans at most 128 * 133144 bytes).
-    const int8_t* abase = a.xq + m0 * K;
-    const int8_t* bbase = a.wq + n0 * K;
+    // chunk c = (l%8) ^ stream_swz(row).  In the blocked layout the tile's
+    // rows lie in one panel (BM and BN divide 256); k-tile kt of 128 is the
+    // panel's 64-column k-tiles 2 kt and 2 kt + 1, so chunk c of row r sits
+    // in block 2 kt + c/4 at 64 r + 16 (c%4): a scalar base per k-tile plus
+    // a 32-bit lane offset, and a group's copy touches 8 whole lines.
+    static_assert(BK == 2 * kKTile && kPanel % BM == 0 && kPanel % BN == 0, "tile inside a panel");
+    const int64_t pa = m0 - m0 % kPanel, pb = n0 - n0 % kPanel;      // panel starts
+    const int64_t arows = T - pa < kPanel ? T - pa : kPanel;
+    const int64_t brows = N - pb < kPanel ? N - pb : kPanel;
+    const int8_t* abase = a.xq + pa * K;
+    const int8_t* bbase = a.wq + pb * K;
     uint32_t goff[LOADS];
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
@@ -872,13 +899,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_i8_stream(GemmA
         const bool isa = g < GA;
         const int row = (isa ? g : g - GA) * 8 + (lane >> 3);
         const int c = (lane & 7) ^ stream_swz(row);
-        const int64_t r = isa ? (m0 + row < T ? row : T - 1 - m0) : (n0 + row < N ? row : N - 1 - n0);
-        goff[u] = (uint32_t)(r * K + c * 16);
+        // row inside the panel (rows past T or N read the last one)
+        const int64_t r = isa ? (m0 + row < T ? m0 - pa + row : T - 1 - pa)
+                              : (n0 + row < N ? n0 - pb + row : N - 1 - pb);
+        const int64_t rows = isa ? arows : brows;
+        goff[u] = (uint32_t)((c >> 2) * kKTile * rows + r * kKTile + (c & 3) * 16);
     }
     auto copy = [&](int u, int kt, int stage) {
         const int g = LOADS * wave + u;
         const bool isa = g < GA;
-        const int8_t* base = (isa ? abase : bbase) + (int64_t)kt * BK;
+        const int8_t* base = isa ? abase + (int64_t)kt * BK * arows : bbase + (int64_t)kt * BK * brows;
         const int8_t* dst = lds + stage * STAGE_BYTES + (isa ? g * 1024 : BM * BK + (g - GA) * 1024);
         copy_to_lds16(base, goff[u], dst);
     };

@@ -7,8 +7,10 @@
 //
 //   s_w[n] = max_k |W[k,n]|,  Wq[n,k] = clamp(rint(W[k,n] * fp32(127/s_w[n])), -127, 127)
 //
-// Wq is written transposed, [N,K] with K contiguous, so that the int8 GEMM
-// reads both of its operands along K with 16-byte loads.
+// Wq is written transposed, [N,K] with K contiguous inside the panel-blocked
+// layout (panels of 256 rows, k-tiles of 64 columns), so that the int8 GEMM
+// reads both of its operands along K with 16-byte loads, a kilobyte of 16
+// rows at a time.
 //
 // Two HBM-bound passes: a column-absmax reduction (16-byte loads along rows,
 // one atomicMax per column per workgroup) and a tiled quantize + transpose
@@ -102,9 +104,10 @@ __device__ inline int8_t quant(float x, float r) {
 
 // One tile of kTrK rows (k) by kTrN columns (n): read W[k0.., n0..] along n,
 // quantize with the column's scale, transpose through LDS, write Wq[n0.., k0..]
-// along k.  With w16 given, the fp16 copy of the values (round to nearest
-// even) is written to w16[k, n] on the way (the 16-bit weight of the outlier
-// path, for checkpoints that are not fp16).
+// along k (each 16-byte piece at its place in the blocked layout).  With
+// w16 given, the fp16 copy of the values (round to nearest even) is written
+// to w16[k, n] on the way (the 16-bit weight of the outlier path, for
+// checkpoints that are not fp16).
 template <int WT>
 __global__ __launch_bounds__(kTrThreads) void k_quant_transpose(const void* __restrict__ W,
                                                                 int64_t K, int64_t N,
@@ -149,7 +152,8 @@ __global__ __launch_bounds__(kTrThreads) void k_quant_transpose(const void* __re
         const int64_t nn = n0 + nr;
         const int64_t k = k0 + ck;
         if (nn < N && k < K)
-            *reinterpret_cast<uint4*>(Wq + nn * K + k) = *reinterpret_cast<const uint4*>(&tile[nr][ck]);
+            *reinterpret_cast<uint4*>(Wq + blk_offset(nn, k, N, K)) =
+                *reinterpret_cast<const uint4*>(&tile[nr][ck]);
     }
 }
 
@@ -169,7 +173,7 @@ hipError_t launch_typed(const void* W, int64_t K, int64_t N, int8_t* Wq, float* 
 // 127))) (HT: fp16 or bf16), so that the matmul reads them as contiguous rows
 // like a caller's W16.  Thread -> column n (stores coalesced along n); the
 // y dimension of the grid strides over the outliers.  Each thread reads one
-// byte per outlier from its Wq row.  Nothing is written when o > rows: the
+// byte per outlier from its row of Wq.  Nothing is written when o > rows: the
 // matmul then recovers the values itself.
 template <int HT>
 __global__ __launch_bounds__(256) void k_recover_rows(const int8_t* __restrict__ Wq,
@@ -182,9 +186,8 @@ __global__ __launch_bounds__(256) void k_recover_rows(const int8_t* __restrict__
     const int64_t o = count[0];
     if (n >= N || o > rows) return;
     const float d = sw[n] / 127.0f;
-    const int8_t* wrow = Wq + n * K;
     for (int64_t j = blockIdx.y; j < o; j += gridDim.y)
-        out[j * N + n] = recover_weight<HT>(wrow[idx[j]], d);
+        out[j * N + n] = recover_weight<HT>(Wq[blk_offset(n, idx[j], N, K)], d);
 }
 
 }  // namespace
