@@ -216,6 +216,24 @@ int int8mm_matmul_prepared(void* workspace, size_t workspace_bytes, int64_t T, i
                            const int8_t* Wq, const float* sw, const void* W16, int64_t N,
                            void* Y, void* stream);
 
+/* int8_mixed_matmul without a workspace argument and without allocating:
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * workspace is a scratch array of 128 MiB (134217728 bytes) inside the
+ * library, one per GPU, held from the first call on that GPU until the
+ * process ends; the first call on a GPU (with it current) looks its address
+ * up, so make that call outside graph capture.  Every call on one GPU uses
+ * the same array: calls that overlap on one GPU (different streams, or
+ * threads) race and give unspecified results; serialize them.  Shapes
+ * whose workspace without the optional regions exceeds the scratch are
+ * rejected (E_WORKSPACE): about 3*T*K bytes, e.g. T*K up to about 44
+ * million; the optional regions (recovered outlier rows, K split, K slabs)
+ * are used when they fit as well.  Arguments, results and the other errors
+ * as int8_mixed_matmul; E_UNSUPPORTED for a device index of 256 or more. */
+int int8_mixed_matmul_noalloc(const void* X, int64_t T, int64_t K, const int8_t* Wq,
+                              const float* sw, const void* W16, int64_t N, float tau, void* Y,
+                              void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -41,6 +41,7 @@ EXPORTS = [
     "int8_mixed_matmul_bf16_debug",
     "int8mm_quantize_activations",
     "int8mm_matmul_prepared",
+    "int8_mixed_matmul_noalloc",
 ]
 
 
@@ -70,6 +71,7 @@ def _load() -> ctypes.CDLL:
     lib.int8_mixed_matmul_bf16_debug.argtypes = lib.int8_mixed_matmul_debug.argtypes
     lib.int8mm_quantize_activations.argtypes = [vp, i64, i64, i64, f32, vp, sz, vp]
     lib.int8mm_matmul_prepared.argtypes = [vp, sz, i64, i64, vp, vp, vp, i64, vp, vp]
+    lib.int8_mixed_matmul_noalloc.argtypes = [vp, i64, i64, vp, vp, vp, i64, f32, vp, vp]
     for name in EXPORTS[1:]:
         getattr(lib, name).restype = c_int
     return lib
@@ -268,3 +270,17 @@ def matmul_prepared(workspace, T: int, K: int, Wq, sw, W16, out=None) -> torch.T
                                        _ptr(sw), _ptr(W16), N, _ptr(Y), _stream()),
            "int8mm_matmul_prepared")
     return Y
+
+
+def mixed_matmul_noalloc(X, Wq, sw, W16, tau: float, out) -> torch.Tensor:
+    """int8_mixed_matmul_noalloc: Y into `out` (float16 [T,N]) with the
+    library's per-GPU scratch as the workspace (no allocation in the call;
+    calls that overlap on one GPU race, see include/int8mm.h)."""
+    if not isinstance(X, torch.Tensor) or X.dtype != torch.float16:
+        raise ValueError("X must be a float16 tensor")
+    T, K, N = _mm_args(X, Wq, sw, W16)
+    _need_out(out, torch.float16, T, N)
+    _check(_lib.int8_mixed_matmul_noalloc(_ptr(X), T, K, _ptr(Wq), _ptr(sw), _ptr(W16), N,
+                                          float(tau), _ptr(out), _stream()),
+           "int8_mixed_matmul_noalloc")
+    return out

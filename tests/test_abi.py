@@ -27,7 +27,7 @@ def header_functions():
 def test_header_lists_entry_points():
     names = header_functions()
     assert "int8_mixed_matmul" in names and "int8_quantize_weight" in names
-    assert len(names) == 11, names
+    assert len(names) == 12, names
 
 
 def test_exports_every_declared_symbol(mm):
@@ -184,3 +184,24 @@ def test_binding_rejects_cpu_tensors(mm):
             call()
     with pytest.raises(TypeError):
         mm.matmul_prepared(None, 16, 64, Wq, sw, None)
+
+
+def test_noalloc_validation(mm):
+    """The allocation-free entry point checks its arguments and the scratch
+    size before it touches a device."""
+    lib, vp = mm.lib(), ctypes.c_void_p
+    f = lib.int8_mixed_matmul_noalloc
+    ok = dict(X=vp(FAKE), T=16, K=64, Wq=vp(FAKE), sw=vp(FAKE), W16=None, N=48, tau=6.0, Y=vp(FAKE))
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return f(a["X"], a["T"], a["K"], a["Wq"], a["sw"], a["W16"], a["N"], a["tau"], a["Y"], None)
+
+    assert call(X=None) == mm.E_NULL and call(Y=None) == mm.E_NULL
+    assert call(K=72) == mm.E_SHAPE and call(T=0) == mm.E_SHAPE
+    assert call(tau=float("nan")) == mm.E_TAU
+    assert call(Wq=vp(FAKE + 1)) == mm.E_ALIGN and call(W16=vp(FAKE + 8)) == mm.E_ALIGN
+    # about 3*T*K bytes of fixed workspace against the 128 MiB scratch:
+    # T=2048, K=12288 (75.5 MB) fits, T=4096, K=12288 (151 MB) does not
+    assert call(T=4096, K=12288, N=49152) == mm.E_WORKSPACE
+    assert call(T=2048, K=49152, N=12288) == mm.E_WORKSPACE
