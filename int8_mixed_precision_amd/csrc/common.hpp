@@ -79,6 +79,15 @@ struct Workspace {
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// The quantizer q = rint(x * fp32(127/s)) reads fp32(127/s) with an
+// unbounded exponent: for s below about 3.7e-37 (bf16 or fp32 values only;
+// an fp16 scale is at least 2^-24) the fp32 quotient would overflow.  Below
+// 2^-64 both s and x are multiplied by 2^64 first: the scalings are exact,
+// the quotient 127/(s * 2^64) is a normal fp32 equal to fp32(127/s) * 2^-64,
+// and (x * 2^64) * that quotient is the same product x * fp32(127/s).
+// Kernels take r = 127 / (s * qfactor(s)) and quantize x * qfactor(s).
+__device__ __forceinline__ float qfactor(float s) { return s < 0x1p-64f ? 0x1p64f : 1.0f; }
+
 // A weight value recovered from its Int8 code q and column scale s_w
 // (memory-halved variant): fp16(fp32(q * fp32(s_w / 127))) (bf16 for the bf16
 // variant).  The product is rounded to fp32 first: the empty asm keeps the

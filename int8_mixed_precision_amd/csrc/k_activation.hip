@@ -11,7 +11,8 @@
 //
 // Readings of the pages: k is an outlier when |X[t,k]| >= tau in some row;
 // the row scale is the absmax over non-outlier columns;
-// q = clamp(rint(x * fp32(127 / s)), -127, 127) with an IEEE fp32 divide.
+// q = clamp(rint(x * fp32(127 / s)), -127, 127) with an IEEE fp32 divide
+// (with an unbounded exponent: see qfactor in common.hpp).
 //
 // All three kernels stream X with 16-byte loads (8 halves per lane) and are
 // bound by HBM bandwidth; the X re-read of the quantize pass is served from
@@ -225,7 +226,8 @@ __global__ __launch_bounds__(kQuantThreads) void k_rowquant(
     mx = red[0];
 #pragma unroll
     for (int i = 1; i < kQuantThreads / kWave; ++i) mx = __builtin_fmaxf(mx, red[i]);
-    const float r = mx > 0.0f ? 127.0f / mx : 0.0f;
+    const float qk = HT == kHalfF16 ? 1.0f : qfactor(mx);   // fp16 scales are >= 2^-24
+    const float r = mx > 0.0f ? 127.0f / (mx * qk) : 0.0f;
     const int64_t opad = count[1];
     const int64_t o = count[0];
     uint16_t* xo_row = xo + t * opad;
@@ -239,7 +241,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_rowquant(
         for (int e = 0; e < 8; ++e) {
             uint16_t hb = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
             float x = h16_to_f32<HT>(hb);
-            uint32_t q = ((fm >> e) & 1u) ? 0u : (uint32_t)(uint8_t)quant(x, r);
+            uint32_t q = ((fm >> e) & 1u) ? 0u : (uint32_t)(uint8_t)quant(x * qk, r);
             packed[e >> 2] |= q << ((e & 3) * 8);
         }
         *reinterpret_cast<uint2*>(xq + blk_offset(t, c * 8, T, K)) = make_uint2(packed[0], packed[1]);
@@ -372,7 +374,8 @@ __global__ __launch_bounds__(NT) void k_rowquant_cached(
     mx = red[0];
 #pragma unroll
     for (int i = 1; i < NT / kWave; ++i) mx = __builtin_fmaxf(mx, red[i]);
-    const float r = mx > 0.0f ? 127.0f / mx : 0.0f;
+    const float qk = HT == kHalfF16 ? 1.0f : qfactor(mx);   // fp16 scales are >= 2^-24
+    const float r = mx > 0.0f ? 127.0f / (mx * qk) : 0.0f;
     uint16_t* xo_row = xo + t * opad;
 #pragma unroll
     for (int i = 0; i < kRowCache; ++i) {
@@ -385,7 +388,7 @@ __global__ __launch_bounds__(NT) void k_rowquant_cached(
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float x = h16_to_f32<HT>((uint16_t)(w[e >> 1] >> ((e & 1) * 16)));
-            const uint32_t q = ((fm >> e) & 1u) ? 0u : (uint32_t)(uint8_t)quant(x, r);
+            const uint32_t q = ((fm >> e) & 1u) ? 0u : (uint32_t)(uint8_t)quant(x * qk, r);
             packed[e >> 2] |= q << ((e & 3) * 8);
         }
         *reinterpret_cast<uint2*>(xq + blk_offset(t, (int64_t)c * 8, T, K)) = make_uint2(packed[0], packed[1]);
@@ -503,7 +506,7 @@ __global__ __launch_bounds__(kSegThreads) void k_seg_quant(
     constexpr int RB = kQuantRows, PARTS = kSegThreads / RB;
     __shared__ float red[PARTS][RB];
     __shared__ int cnt[2][PARTS];
-    __shared__ float sxs[RB], rxs[RB];
+    __shared__ float sxs[RB], rxs[RB], qks[RB];
     __shared__ int wtot[kSegThreads / kWave];
     const int tid = threadIdx.x;
     const int seg = blockIdx.x, nseg = gridDim.x;
@@ -543,8 +546,10 @@ __global__ __launch_bounds__(kSegThreads) void k_seg_quant(
             for (int p = l; p < PARTS; p += kWave) mx = __builtin_fmaxf(mx, red[p][r]);
             mx = wave_max(mx);
             if (l == 0) {
+                const float qk = HT == kHalfF16 ? 1.0f : qfactor(mx);   // fp16: >= 2^-24
                 sxs[r] = mx;
-                rxs[r] = mx > 0.0f ? 127.0f / mx : 0.0f;   // IEEE fp32 divide
+                qks[r] = qk;
+                rxs[r] = mx > 0.0f ? 127.0f / (mx * qk) : 0.0f;   // IEEE fp32 divide
             }
         }
     }
@@ -586,13 +591,13 @@ __global__ __launch_bounds__(kSegThreads) void k_seg_quant(
     for (int r = 0; r < RB; ++r) {
         const int64_t t = t0 + r;
         if (t < T) {
-            const float rr = rxs[r];
+            const float rr = rxs[r], qk = qks[r];
             const uint32_t w[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
             uint32_t packed[2] = {0u, 0u};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float x = h16_to_f32<HT>((uint16_t)(w[e >> 1] >> ((e & 1) * 16)));
-                const uint32_t q = ((fm >> e) & 1u) ? 0u : (uint32_t)(uint8_t)quant(x, rr);
+                const uint32_t q = ((fm >> e) & 1u) ? 0u : (uint32_t)(uint8_t)quant(x * qk, rr);
                 packed[e >> 2] |= q << ((e & 3) * 8);
             }
             *reinterpret_cast<uint2*>(xq + blk_offset(t, c0, T, K)) = make_uint2(packed[0], packed[1]);

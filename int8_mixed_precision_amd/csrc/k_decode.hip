@@ -109,7 +109,8 @@ struct SmemT {
     float sw[MAXB * kRows];                    // s_w of the rows
     float wmax[kWaves][kMaxT];
     float sx[kMaxT];
-    float rx[kMaxT];                           // 127 / s_x (0 when s_x = 0)
+    float rx[kMaxT];                           // 127 / (s_x * qk) (0 when s_x = 0)
+    float qk[kMaxT];                           // tiny-scale factor of the row (qfactor)
     int32_t wtot[kWaves * 2];
     int32_t next;                              // next chunk to hand out
 };
@@ -359,8 +360,10 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
             float v = sm.wmax[0][tid];
     #pragma unroll
             for (int w = 1; w < kWaves; ++w) v = __builtin_fmaxf(v, sm.wmax[w][tid]);
+            const float qk = HT == kHalfF16 ? 1.0f : qfactor(v);   // fp16 scales are >= 2^-24
             sm.sx[tid] = v;
-            sm.rx[tid] = v > 0.0f ? 127.0f / v : 0.0f;   // IEEE fp32 divide
+            sm.qk[tid] = qk;
+            sm.rx[tid] = v > 0.0f ? 127.0f / (v * qk) : 0.0f;   // IEEE fp32 divide
         }
     #pragma unroll
         for (int j = 0; j < CPT; ++j) {
@@ -399,10 +402,11 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
     #pragma unroll
             for (int t = 0; t < TMAX; ++t) {
                 const float rr = t < T ? sm.rx[t] : 0.0f;
+                const float qk = HT == kHalfF16 ? 1.0f : (t < T ? sm.qk[t] : 1.0f);
                 uint32_t f[8];
     #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float p = __builtin_fmaf(chunk_val<HT>(xr[j][t], e), rr, 0.0f);
+                    const float p = __builtin_fmaf(chunk_val<HT>(xr[j][t], e) * qk, rr, 0.0f);
                     f[e] = __builtin_bit_cast(uint32_t, __fadd_rn(p, 12582912.0f));
                 }
                 uint32_t packed[2];

@@ -6,6 +6,7 @@
 // on the checkpoint's own values.
 //
 //   s_w[n] = max_k |W[k,n]|,  Wq[n,k] = clamp(rint(W[k,n] * fp32(127/s_w[n])), -127, 127)
+// (fp32(127/s) with an unbounded exponent: see qfactor in common.hpp)
 //
 // Wq is written transposed, [N,K] with K contiguous inside the panel-blocked
 // layout (panels of 256 rows, k-tiles of 64 columns), so that the int8 GEMM
@@ -122,11 +123,13 @@ __global__ __launch_bounds__(kTrThreads) void k_quant_transpose(const void* __re
     // read phase: 8 lanes cover one 64-column row segment (8 values each)
     const int cn = (tid & 7) * 8;           // column inside the tile
     const int64_t n = n0 + cn;
-    float r[8];
+    // (fp16 scales are at least 2^-24: the tiny-scale factor is 1 for them)
+    float r[8], qk[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         float s = (n + e < N) ? sw[n + e] : 0.0f;
-        r[e] = s > 0.0f ? 127.0f / s : 0.0f;
+        qk[e] = WT == kWeightF16 ? 1.0f : qfactor(s);
+        r[e] = s > 0.0f ? 127.0f / (s * qk[e]) : 0.0f;
     }
     for (int kr = tid >> 3; kr < kTrK; kr += kTrThreads / 8) {
         const int64_t k = k0 + kr;
@@ -143,7 +146,7 @@ __global__ __launch_bounds__(kTrThreads) void k_quant_transpose(const void* __re
             }
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) tile[cn + e][kr] = quant(v[e], r[e]);
+        for (int e = 0; e < 8; ++e) tile[cn + e][kr] = quant(v[e] * qk[e], r[e]);
     }
     __syncthreads();
     // write phase: 8 lanes cover one 128-byte row of Wq

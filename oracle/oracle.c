@@ -24,7 +24,8 @@
  *   - symmetric absmax quantization to [-127, 127]:
  *       q = clamp(rint(x * fp32(127 / s)), -127, 127),
  *     the divide an IEEE fp32 divide, the product one fp32 multiply, rint
- *     rounding half to even; s = 0 gives q = 0;
+ *     rounding half to even; s = 0 gives q = 0; fp32(127/s) has no upper
+ *     exponent limit (it would overflow for s < ~3.7e-37);
  *   - the row scale s_x[t] is the absmax of row t over non-outlier columns
  *     only; outlier columns of Xq are 0;
  *   - the column scale s_w[n] is the absmax of column n of W over all K rows;
@@ -141,11 +142,19 @@ static uint16_t h_encode(int ht, double x) { return ht ? oracle_bf16_encode(x) :
 
 /* ---------------------------------------------------- the quantizer itself */
 
-/* Symmetric absmax quantization of one value with scale s (see header). */
+/* Symmetric absmax quantization of one value with scale s (see header).
+ * fp32(127/s) is the quotient rounded to nearest even at 24 significant
+ * bits, as an IEEE fp32 divide gives it; for s below about 3.7e-37 (bf16 or
+ * fp32 values only, never fp16) that quotient lies above the largest fp32,
+ * and it is read with an unbounded exponent instead of overflowing.  The
+ * quotient is formed in double first: rounding 53 bits and then 24 is the
+ * same as rounding 24 once for a quotient of 24-bit numbers. */
 static int8_t quant_one(float x, float s) {
     if (s == 0.0f) return 0;
-    float r = 127.0f / s;           /* IEEE fp32 divide */
-    float p = x * r;                /* one fp32 multiply */
+    int e;
+    double m = frexp(127.0 / (double)s, &e);      /* 127/s = m * 2^e, 0.5 <= m < 1 */
+    double r = ldexp((double)(float)m, e);        /* 24 significant bits, exponent unbounded */
+    float p = (float)((double)x * r);             /* exact 48-bit product, rounded to fp32 once */
     float q = rintf(p);             /* round half to even */
     if (q > 127.0f) q = 127.0f;
     if (q < -127.0f) q = -127.0f;

@@ -306,6 +306,43 @@ def pin_quant_ties(orc):
 
 # --------------------------------------------------------------- outlier set
 
+def tiny_scale_cases():
+    """The hand-derived tiny-scale cases (tests/golden/tiny_scale.json) as
+    arrays: a bf16 activation row (uint16 bit patterns) and an fp32
+    checkpoint column, each with its scale and codes."""
+    g = _load("tiny_scale.json")
+    b = g["bf16_row"]
+    # bf16 subnormal k * 2^-133 has bit pattern k (sign in bit 15)
+    assert b["unit_log2"] == -133
+    row_bits = np.array([abs(u) | (0x8000 if u < 0 else 0) for u in b["x_units"]], np.uint16)
+    c = g["f32_column"]
+    col = np.array([u * 2.0 ** c["unit_log2"] for u in c["x_units"]], np.float32)
+    assert all(float(v) == u * 2.0 ** c["unit_log2"] for v, u in zip(col, c["x_units"]))
+    return (row_bits, b["s_units"] * 2.0 ** b["unit_log2"], b["q"],
+            col, c["s_units"] * 2.0 ** c["unit_log2"], c["q"])
+
+
+def pin_tiny_scale(orc):
+    """Scales whose fp32 reciprocal 127/s would overflow: the reciprocal is
+    read with an unbounded exponent (tests/golden/tiny_scale.json)."""
+    row_bits, s_row, q_row, col, s_col, q_col = tiny_scale_cases()
+    K = 16
+    X = np.zeros((1, K), np.uint16)
+    X[0, :len(row_bits)] = row_bits
+    Xq, sx = orc.quantize_rows(X, np.zeros(K, np.uint8), htype="bf16")
+    assert float(sx[0]) == s_row, "tiny bf16 row scale"
+    assert Xq[0, :len(q_row)].tolist() == q_row and not Xq[0, len(q_row):].any(), \
+        f"tiny bf16 row codes {Xq[0].tolist()}"
+    W = np.zeros((K, 8), np.float32)
+    W[:len(col), 0] = col
+    W[:, 1:] = 1.0                      # other columns: plain values
+    Wq, sw = orc.quantize_weight_typed(W, "f32")
+    assert float(sw[0]) == s_col, "tiny fp32 column scale"
+    assert Wq[0, :len(q_col)].tolist() == q_col and not Wq[0, len(q_col):].any(), \
+        f"tiny fp32 column codes {Wq[0].tolist()}"
+    assert (Wq[1:] == 127).all() and (sw[1:] == 1.0).all()
+
+
 def pin_detect(orc):
     for seed, (T, K) in enumerate([(16, 64), (37, 80), (5, 304), (64, 128)]):
         X, _ = _case(100 + seed, T, K, 8, n_dims=3, factor=9.0)
@@ -506,7 +543,7 @@ def pin_row_sample(orc):
         assert np.array_equal(r[key], full[key][rows]), key
 
 
-ALL_PINS = [pin_f16_codec, pin_hand_example, pin_quant_ties, pin_detect, pin_compact,
+ALL_PINS = [pin_f16_codec, pin_hand_example, pin_quant_ties, pin_tiny_scale, pin_detect, pin_compact,
             pin_tiny_config, pin_quant_invariants, pin_gemm, pin_tau_inf, pin_tau_zero,
             pin_error_bound, pin_metamorphic_scale, pin_permutation, pin_row_sample,
             pin_hand_memory_halved, pin_dequant_weight, pin_memory_halved_tau_zero,

@@ -16,7 +16,11 @@ MUTANTS = [
     ("threshold_signed", "fabsf(h_f32(ht, X[t * K + k])) >= tau", "h_f32(ht, X[t * K + k]) >= tau"),
     ("round_half_away", "float q = rintf(p);", "float q = roundf(p);"),
     ("round_truncate", "float q = rintf(p);", "float q = truncf(p);"),
-    ("range_128", "float r = 127.0f / s;", "float r = 128.0f / s;"),
+    ("range_128", "frexp(127.0 / (double)s, &e)", "frexp(128.0 / (double)s, &e)"),
+    ("reciprocal_overflows", "double r = ldexp((double)(float)m, e);", "double r = (double)(127.0f / s);"),
+    ("reciprocal_unrounded", "double r = ldexp((double)(float)m, e);", "double r = ldexp(m, e);"),
+    ("product_unrounded", "float p = (float)((double)x * r);             /* exact 48-bit product, rounded to fp32 once */\n    float q = rintf(p);",
+     "double p = (double)x * r;\n    float q = (float)rint(p);"),
     ("row_scale_includes_outliers", "if (flag[k]) continue;", ";"),
     ("outlier_column_kept", "flag[k] ? 0 : quant_one", "0 ? 0 : quant_one"),
     ("drop_16bit_part", "double y = y8 + y16;", "double y = y8;"),
