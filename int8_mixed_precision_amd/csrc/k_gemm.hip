@@ -786,13 +786,14 @@ __global__ __launch_bounds__(128 * WN) void k_gemm_i8_big(GemmArgs a) {
         // K split: each half publishes its int32 sums, and the half that
         // finishes second adds the other's (exact, order independent) and
         // runs the epilogue.  The tile counters were zeroed at launch.
-        // The sums travel through device-coherent accesses (agent-scope
-        // atomic loads and stores: the other half may run on another XCD,
-        // whose L2 is not this one's), so no cache flush or invalidate is
-        // needed: a half's stores are complete (vmcnt 0) before its counter
-        // increment, and the second half reads only after its increment has
-        // returned the first's.  A half that finds the other one already
-        // done skips publishing its own sums.
+        // The sums travel through agent-scope atomic stores and loads (the
+        // other half may run on another XCD, whose L2 is not this one's);
+        // the ordering is the memory model's: every wave's stores, then a
+        // workgroup barrier, then thread 0's counter increment with
+        // release semantics at agent scope; in the other half the same
+        // increment acquires, and a barrier orders it before every wave's
+        // loads.  A half that finds the other one already done skips
+        // publishing its own sums.
         uint64_t* mine = reinterpret_cast<uint64_t*>(a.ks_part) +
                          ((tix * 2 + half) * WAVES + wave) * (TM * TN * 8 * 64);
         const uint64_t* other = reinterpret_cast<const uint64_t*>(a.ks_part) +
@@ -817,7 +818,7 @@ __global__ __launch_bounds__(128 * WN) void k_gemm_i8_big(GemmArgs a) {
         }
         __syncthreads();   // every wave's sums are out (and ks_first is read)
         if (tid == 0)
-            ks_first = __hip_atomic_fetch_add(&a.ks_count[tix], 1, __ATOMIC_RELAXED,
+            ks_first = __hip_atomic_fetch_add(&a.ks_count[tix], 1, __ATOMIC_ACQ_REL,
                                               __HIP_MEMORY_SCOPE_AGENT) == 0;
         __syncthreads();
         if (ks_first) return;   // the other half finishes the tile
