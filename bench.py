@@ -58,6 +58,11 @@ def parse():
                    help="instead of the headline run: the four projections of a 175B-class "
                         "block at T=4096 with 0, 8, 64 and 256 planted outlier dimensions "
                         "(time against the outlier count); prints one JSON line")
+    p.add_argument("--no-sweep", action="store_true",
+                   help="skip the outlier-count sweep of the 175B-class block projections that "
+                        "the default run reports under other_configs")
+    p.add_argument("--no-ceilings", action="store_true",
+                   help="skip the measured-ceiling kernels (bare int8 MFMA loop, HBM stream read)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device-to-device copy (a kernel of known "
                         "traffic, for scaling the HBM byte counters)")
@@ -513,7 +518,7 @@ def bench_decode(torch, mm, synth, steps, warmup, variants=True):
     }
 
 
-def bench_sweep(torch, mm, synth, steps, warmup):
+def bench_sweep(torch, mm, synth, steps, warmup, prewarm_s):
     """Every sweep workload: the full call (activation pass + matmul, both
     timed by events on the library's stream), with and without the 16-bit
     weight.  Inputs are generated per workload and freed after it."""
@@ -539,7 +544,7 @@ def bench_sweep(torch, mm, synth, steps, warmup):
                 mm.matmul_prepared(ws, T, K, Wq, sw, w16, out=Y)
                 if e is not None:
                     e[2].record()
-            prewarm(torch, step, 0.15)
+            prewarm(torch, step, prewarm_s)
             wall, evs = timed_loop(torch, steps, warmup, step)
             act = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
             gemm = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
@@ -557,34 +562,136 @@ def bench_sweep(torch, mm, synth, steps, warmup):
     return rows
 
 
-def cpu_baseline(synth, T, K, N):
-    """The oracle, timed on the host cores, on a row sample of the prefill
-    workload (outlier detection over all rows, the rest on the sample)."""
+def measured_ceilings(torch):
+    """What this chip delivers, measured in the same run: a bare int8 MFMA
+    loop (independent accumulators, no memory traffic) and a coalesced
+    stream read of 2 GiB, each with the shader clock it ran at (libceiling,
+    built beside the library)."""
+    import ctypes
+    path = os.path.join(ROOT, "int8_mixed_precision_amd", "libceiling.so")
+    lib = ctypes.CDLL(path)
+    vp, ci, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    lib.ceiling_mfma_i8.argtypes = [ci, ci, vp, vp, vp]
+    lib.ceiling_stream.argtypes = [vp, i64, ci, vp, vp, vp]
+    acc = lib.ceiling_mfma_acc()
+    stream = lambda: vp(torch.cuda.current_stream().cuda_stream)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    out = {}
+
+    def timed(launch, clk, reps=5):
+        for _ in range(2):
+            launch()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            launch()
+        b.record()
+        torch.cuda.synchronize()
+        c = clk.view(-1, 2).cpu().numpy().astype(np.float64)
+        ghz = float(np.mean(c[:, 0] / (c[:, 1] / 100e6)) / 1e9)
+        return a.elapsed_time(b) / reps, ghz
+
+    grid, iters = 1024, 400          # 4 workgroups of 4 waves per CU
+    clk = torch.zeros(2 * grid, dtype=torch.int64, device="cuda")
+    ms, ghz = timed(lambda: lib.ceiling_mfma_i8(grid, iters, vp(sink.data_ptr()),
+                                                 vp(clk.data_ptr()), stream()), clk)
+    ops = grid * 4 * iters * acc * 65536.0
+    out["mfma_i8"] = {"TOPS": round(ops / (ms * 1e-3) / 1e12, 1), "clock_GHz": round(ghz, 3),
+                      "kernel": "back-to-back v_mfma_i32_32x32x32_i8, no memory traffic"}
+    nbytes = 2 << 30
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    grid = 2048                      # 8 workgroups of 4 waves per CU, 16 loads each in flight
+    clk = torch.zeros(2 * grid, dtype=torch.int64, device="cuda")
+    ms, ghz = timed(lambda: lib.ceiling_stream(vp(buf.data_ptr()), nbytes, grid, vp(sink.data_ptr()),
+                                                vp(clk.data_ptr()), stream()), clk)
+    out["hbm_read"] = {"GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1), "clock_GHz": round(ghz, 3),
+                       "kernel": "coalesced 16-byte loads over 2 GiB, 16 per lane in flight"}
+    del buf
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_stages(oracle, X, Wq, sw, W16, tau, rows, threads):
+    """Seconds per oracle step (the steps as the pages order them) on the
+    listed rows; detection and isolation always see every row."""
+    t = {}
+    t0 = time.perf_counter()
+    flag = oracle.detect(X, tau)
+    t["detect"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    idx = oracle.compact(flag)
+    t["isolate"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    xq, sx = oracle.quantize_rows(X, flag, rows=rows)
+    t["quantize_x"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    acc = oracle.int8_gemm(xq, Wq, threads=threads)
+    t["int8_gemm"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.output(acc, sx, sw, X, W16, idx, rows=rows, threads=threads)
+    t["dequant_and_outliers"] = time.perf_counter() - t0
+    return t
+
+
+def cpu_baseline(synth):
+    """The oracle, as it is, on the host's cores: per-step times at one
+    thread and at CPU_THREADS threads (the host-core share of one GPU) for
+    the tiny and decode workloads in full and for a row sample of the
+    prefill up-projection; value = the up-projection's TOPS with the
+    per-row steps extrapolated from the sample to all rows."""
     import oracle
+    res = {"kind": "oracle", "unit": "TOPS", "cores": CPU_THREADS,
+           "nproc": os.cpu_count(), "cpu_model": cpu_model()}
+    stages = {}
+    for name in ("tiny", "dec"):
+        w = synth.WORKLOADS[name]
+        X, W = synth.make_x(w, threads=CPU_THREADS), synth.make_w(w, threads=CPU_THREADS)
+        Wq, sw = oracle.quantize_weight(W, threads=CPU_THREADS)
+        for th in (1, CPU_THREADS):
+            st = oracle_stages(oracle, X, Wq, sw, W, w.tau, None, th)
+            stages[f"{name}_{th}t"] = {k: round(v, 6) for k, v in st.items()}
+        del X, W, Wq
     w = synth.WORKLOADS["up"]
+    T, K, N = w.T, w.K, w.N
     X = synth.make_x(w, threads=CPU_THREADS)
     W = synth.make_w(w, threads=CPU_THREADS)
     Wq, sw = oracle.quantize_weight(W, threads=CPU_THREADS)
-    # size the sample so the timed run takes ~CPU_TARGET_S: a two-point fit
-    # separates the fixed cost (detection over all rows) from the cost per row
-    def run(nrows):
-        t0 = time.perf_counter()
-        oracle.mixed_matmul(X, Wq, sw, W, w.tau, rows=np.arange(nrows), threads=CPU_THREADS)
-        return time.perf_counter() - t0
-    t_a, t_b = run(CPU_THREADS), run(2 * CPU_THREADS)
-    per_row = max((t_b - t_a) / CPU_THREADS, 1e-6)
-    rows = int(min(T, max(CPU_THREADS, (CPU_TARGET_S - t_a + CPU_THREADS * per_row) / per_row)))
+    one = np.linspace(0, T - 1, 4).astype(np.int64)
+    st1 = oracle_stages(oracle, X, Wq, sw, W, w.tau, one, 1)
+    # size the all-core sample to about CPU_TARGET_S from the one-thread rate
+    per_row_1t = (st1["quantize_x"] + st1["int8_gemm"] + st1["dequant_and_outliers"]) / len(one)
+    rows = int(min(T, max(CPU_THREADS, CPU_TARGET_S * CPU_THREADS * 0.8 / max(per_row_1t, 1e-6))))
     rows -= rows % CPU_THREADS
     sample = np.linspace(0, T - 1, rows).astype(np.int64)
-    t0 = time.perf_counter()
-    oracle.mixed_matmul(X, Wq, sw, W, w.tau, rows=sample, threads=CPU_THREADS)
-    dt = time.perf_counter() - t0
-    return {
-        "value": 2.0 * rows * K * N / dt / 1e12, "unit": "TOPS", "cores": CPU_THREADS,
-        "kind": "oracle",
-        "sample": f"{rows} of {T} rows of the prefill up-projection (outlier detection over "
-                  f"all {T} rows), {dt:.1f} s; weight conversion untimed",
-    }
+    stn = oracle_stages(oracle, X, Wq, sw, W, w.tau, sample, CPU_THREADS)
+    stages[f"up_1t_{len(one)}rows"] = {k: round(v, 6) for k, v in st1.items()}
+    stages[f"up_{CPU_THREADS}t_{rows}rows"] = {k: round(v, 6) for k, v in stn.items()}
+    per_row = (stn["quantize_x"] + stn["int8_gemm"] + stn["dequant_and_outliers"]) / rows
+    whole = stn["detect"] + stn["isolate"] + per_row * T
+    res.update({
+        "value": round(2.0 * T * K * N / whole / 1e12, 4),
+        "sample": f"prefill up-projection: detection and isolation over all {T} rows, the "
+                  f"per-row steps on {rows} of {T} rows at {CPU_THREADS} threads, extrapolated "
+                  f"to {T} rows ({whole:.1f} s for the whole call); weight conversion untimed",
+        "stages_s": stages,
+        "note": "stages_s: seconds per oracle step (detect, isolate, quantize_x, int8_gemm, "
+                "dequant_and_outliers); <config>_<threads>t, tiny and dec in full; the "
+                "oracle runs detect, isolate and quantize_x on one thread whatever the "
+                "thread count, int8_gemm and dequant_and_outliers on the threads given",
+    })
+    return res
 
 
 def main():
@@ -614,7 +721,7 @@ def main():
         log("copy calibration: 3 copies of 1 GiB")
 
     if args.sweep:
-        rows = bench_sweep(torch, mm, synth, args.steps, args.warmup)
+        rows = bench_sweep(torch, mm, synth, args.steps, args.warmup, PREWARM_S / 2)
         print(json.dumps({"metric": "int8-mixed matmul time vs outlier count, 175B-class "
                                     "block projections at T=4096", "unit": "ms",
                           "steps": args.steps, "warmup": args.warmup, "data": "synthetic",
@@ -639,6 +746,15 @@ def main():
             + (f"; memory-halved {dec['halved_weight_gbs']:.1f} GB/s "
                f"({dec['halved_call_ms'] * 1e3:.1f} us/call), bf16 {dec['bf16_weight_gbs']:.1f} GB/s "
                f"({dec['bf16_call_ms'] * 1e3:.1f} us/call)" if "halved_weight_gbs" in dec else ""))
+
+    sweep = None
+    if args.only is None and not args.no_variants and not args.no_sweep:
+        log("sweep: 175B-class block projections at T=4096, 0/8/64/256 planted outlier dims")
+        sweep = bench_sweep(torch, mm, synth, 5, 2, 0.05)
+    ceil = None
+    if not args.no_ceilings:
+        log("measured ceilings: bare int8 MFMA loop, 2 GiB stream read")
+        ceil = measured_ceilings(torch)
 
     gemm_digest = src_digest(["k_gemm.hip", "common.hpp"])
     decode_digest = src_digest(["k_decode.hip", "common.hpp"])
@@ -688,6 +804,10 @@ def main():
             out["memory_halved"]["weight_memory_ratio"] = round((K * N + 4.0 * N) / (2.0 * K * N), 4)
         if "vendor_int8_gemm" in pre:
             out["roofline"]["vendor_int8_gemm"] = pre["vendor_int8_gemm"]
+        if ceil is not None:
+            m = ceil["mfma_i8"]["TOPS"]
+            out["roofline"]["measured_peak"] = {"value": m, "unit": "TFLOP/s", **ceil["mfma_i8"]}
+            out["roofline"]["frac_of_measured"] = round(ach / m, 4)
     if dec is not None:
         d = {"metric": "weight GB/s @ T=8", "value": round(dec["weight_gbs"], 1), "unit": "GB/s",
              "ms_per_step": round(dec["ms_per_step"], 5), "steps": dec["steps"],
@@ -715,6 +835,10 @@ def main():
                                  "rotates 8 copies",
                          "weight GB/s": round(dec["warm_weight_gbs"], 1),
                          "call_ms": round(dec["warm_call_ms"], 5)}
+        if ceil is not None:
+            m = ceil["hbm_read"]["GB/s"]
+            d["roofline"]["measured_peak"] = {"value": m, "unit": "GB/s", **ceil["hbm_read"]}
+            d["roofline"]["frac_of_measured"] = round(dec["alg_gbs"] / m, 4)
         if pre is None:
             out.update({"value": d["value"], "unit": "GB/s", "ms_per_step": d["ms_per_step"],
                         "config": d["config"], "roofline": d["roofline"]})
@@ -729,9 +853,18 @@ def main():
             "workload": "decode FFN up-projection weights (K=8192, N=28672, 8 rotating copies) "
                         "with 32 and 128 activation rows, whole calls from a HIP graph",
             "results": dec["batched"]}
+    if sweep is not None:
+        out.setdefault("other_configs", {})["sweep_175b_block"] = {
+            "workload": "175B-class block projections (QKV 12288->36864, out 12288->12288, up "
+                        "12288->49152, down 49152->12288) at T=4096 with 0, 8, 64 and 256 planted "
+                        "outlier dims; whole calls with and without W16 (memory-halved), "
+                        "5 timed steps each",
+            "results": sweep}
+    if ceil is not None:
+        out["measured_ceilings"] = ceil
     if not args.no_cpu_baseline and pre is not None:
-        log("cpu baseline: oracle on a row sample")
-        out["cpu_baseline"] = cpu_baseline(synth, pre["T"], pre["K"], pre["N"])
+        log("cpu baseline: oracle steps at 1 and all threads")
+        out["cpu_baseline"] = cpu_baseline(synth)
     print(json.dumps(out), flush=True)
 
 

@@ -14,9 +14,9 @@
 // q = clamp(rint(x * fp32(127 / s)), -127, 127) with an IEEE fp32 divide
 // (with an unbounded exponent: see qfactor in common.hpp).
 //
-// All three kernels stream X with 16-byte loads (8 halves per lane) and are
-// bound by HBM bandwidth; the X re-read of the quantize pass is served from
-// cache for the row a workgroup is working on.
+// The kernels stream X with 16-byte loads (8 halves per lane) and are bound
+// by HBM bandwidth; the X re-read of the quantize pass is served from cache
+// for the row a workgroup is working on.
 #include "common.hpp"
 
 // Quantization must round x * r and any following add separately, exactly
@@ -27,65 +27,9 @@ namespace i8mm {
 
 namespace {
 
-constexpr int kDetectThreads = 256;
-constexpr int kDetectCols = kDetectThreads * 8;   // columns per workgroup
-constexpr int kDetectRows = 16;                    // rows per workgroup
 constexpr int kCompactThreads = 1024;
 constexpr int kQuantThreads = 256;
 constexpr int kRowThreads = 512;            // k_rowquant_cached
-
-// Zeroes the outlier bitmap and the count before a detection pass.
-__global__ void k_clear(uint32_t* __restrict__ flags, int64_t kw, int32_t* __restrict__ count) {
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < kw) flags[i] = 0u;
-    if (i < 4) count[i] = 0;
-}
-
-// flags[k/32] bit k%32 |= (|X[t,k]| >= tau) over the workgroup's rows.
-// Each lane owns 8 consecutive columns; 4 lanes form one 32-bit word, which
-// is merged with one atomicOr only when some bit is set.
-template <int HT>
-__global__ __launch_bounds__(kDetectThreads) void k_detect(const uint16_t* __restrict__ X,
-                                                           int64_t T, int64_t K, float tau,
-                                                           uint32_t* __restrict__ flags) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t c0 = ((int64_t)blockIdx.x * kDetectThreads + threadIdx.x) * 8;
-    uint32_t m = 0;
-    // grid-stride over chunks of kDetectRows rows (grid.y is capped at 65535)
-    for (int64_t r0 = (int64_t)blockIdx.y * kDetectRows; c0 < K && r0 < T;
-         r0 += (int64_t)gridDim.y * kDetectRows) {
-        const int64_t r1 = r0 + kDetectRows < T ? r0 + kDetectRows : T;
-        const uint16_t* p = X + r0 * K + c0;
-        int64_t r = r0;
-        for (; r + 4 <= r1; r += 4, p += 4 * K) {
-            uint4 v[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const uint4*>(p + u * K);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float x = h16_to_f32<HT>((uint16_t)(w[e >> 1] >> ((e & 1) * 16)));
-                    m |= (__builtin_fabsf(x) >= tau ? 1u : 0u) << e;
-                }
-            }
-        }
-        for (; r < r1; ++r, p += K) {
-            uint4 v = *reinterpret_cast<const uint4*>(p);
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float x = h16_to_f32<HT>((uint16_t)(w[e >> 1] >> ((e & 1) * 16)));
-                m |= (__builtin_fabsf(x) >= tau ? 1u : 0u) << e;
-            }
-        }
-    }
-    uint32_t word = m << ((lane & 3) * 8);
-    word |= __shfl_xor(word, 1);
-    word |= __shfl_xor(word, 2);
-    if ((lane & 3) == 0 && word != 0u && c0 < K) atomicOr(&flags[c0 >> 5], word);
-}
 
 // Outlier flags for up to kOwnedMaxT rows without atomics: a workgroup owns
 // kOwnedCols columns (8 per lane, whole 32-bit words per 4 lanes) and reads
@@ -132,6 +76,65 @@ __global__ __launch_bounds__(kOwnedWaves * kWave) void k_detect_owned(const uint
         uint32_t f = 0;
 #pragma unroll
         for (int w = 0; w < kOwnedWaves; ++w) f |= wfm[w][lane];
+        uint32_t word = f << ((lane & 3) * 8);
+        word |= __shfl_xor(word, 1);
+        word |= __shfl_xor(word, 2);
+        if ((lane & 3) == 0 && in) flags[c0 >> 5] = word;
+    }
+}
+
+// Outlier flags for any number of rows without atomics or a clearing
+// kernel: a workgroup owns kColBlock = 64 columns (two bitmap words) and
+// reads every row of them.  A row's 64 columns are one 128-byte line, and a
+// wave's load instruction covers 8 rows (8 lanes per row, 16 bytes each), so
+// every request is a whole line; each lane keeps kColLoads rows' loads in
+// flight.  The lanes holding one column group merge their flags by
+// shuffles, the waves through LDS, and the two words are stored whole.
+// (Past 128 rows; the clearing kernel + atomic detection it replaces took
+// 3.8 + 12.2 us on T=2048, K=12288.)
+constexpr int kColBlock = 64;
+constexpr int kColWaves = 8;
+constexpr int kColLoads = 16;
+template <int HT>
+__global__ __launch_bounds__(kColWaves * kWave) void k_detect_cols(const uint16_t* __restrict__ X,
+                                                                   int64_t T, int64_t K, float tau,
+                                                                   uint32_t* __restrict__ flags) {
+    __shared__ uint32_t wfm[kColWaves][8];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid >> 6;
+    const int cg = lane & 7;                           // 8-column group of the lane
+    const int64_t c0 = (int64_t)blockIdx.x * kColBlock + cg * 8;
+    const bool in = c0 < K;
+    const uint16_t* xc = X + (in ? c0 : 0);
+    constexpr int kRowsPerPass = 8 * kColWaves * kColLoads;
+    uint32_t m = 0;
+    for (int64_t t0 = (lane >> 3) + 8 * wv; t0 < T; t0 += kRowsPerPass) {
+        uint4 v[kColLoads];
+#pragma unroll
+        for (int u = 0; u < kColLoads; ++u) {
+            const int64_t t = t0 + (int64_t)u * 8 * kColWaves;
+            v[u] = *reinterpret_cast<const uint4*>(xc + (t < T ? t : T - 1) * K);
+        }
+#pragma unroll
+        for (int u = 0; u < kColLoads; ++u) {
+            const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = h16_to_f32<HT>((uint16_t)(w[e >> 1] >> ((e & 1) * 16)));
+                m |= (__builtin_fabsf(x) >= tau ? 1u : 0u) << e;
+            }
+        }
+    }
+    // rows past T re-read row T-1 (no flag changes); lanes past K flag nothing
+    if (!in) m = 0;
+    m |= __shfl_xor(m, 8);
+    m |= __shfl_xor(m, 16);
+    m |= __shfl_xor(m, 32);
+    if (lane < 8) wfm[wv][lane] = m;
+    __syncthreads();
+    if (wv == 0 && lane < 8) {
+        uint32_t f = 0;
+#pragma unroll
+        for (int w = 0; w < kColWaves; ++w) f |= wfm[w][lane];
         uint32_t word = f << ((lane & 3) * 8);
         word |= __shfl_xor(word, 1);
         word |= __shfl_xor(word, 2);
@@ -643,11 +646,8 @@ static void launch_activation_typed(const uint16_t* xb, int64_t T, int64_t K, fl
         hipLaunchKernelGGL(k_detect_owned<HT>, dim3((unsigned)ceil_div(K, kOwnedCols)),
                            dim3(kOwnedWaves * kWave), 0, stream, xb, T, K, tau, ws.flags);
     } else {
-        int clear_blocks = (int)ceil_div(kw > 4 ? kw : 4, 256);
-        hipLaunchKernelGGL(k_clear, dim3(clear_blocks), dim3(256), 0, stream, ws.flags, kw, ws.count);
-        const int64_t row_chunks = ceil_div(T, kDetectRows);
-        dim3 dgrid((unsigned)ceil_div(K, kDetectCols), (unsigned)(row_chunks < 65535 ? row_chunks : 65535));
-        hipLaunchKernelGGL(k_detect<HT>, dgrid, dim3(kDetectThreads), 0, stream, xb, T, K, tau, ws.flags);
+        hipLaunchKernelGGL(k_detect_cols<HT>, dim3((unsigned)ceil_div(K, kColBlock)),
+                           dim3(kColWaves * kWave), 0, stream, xb, T, K, tau, ws.flags);
     }
     // rows held in registers: the quantize kernel isolates the outliers too
     if (K <= (int64_t)kRowThreads * 4 * 8) {
