@@ -66,13 +66,21 @@ struct StageCtx {
     float sx_pre;        // s_x of tile row tid (tid < 256; the last row past T)
     const float* sw_pre; // s_w of the lane's TN columns (0 past N)
     int o, opad;         // outlier count and its padded value
+    int k_first;         // outlier slot tid % 32's dimension (or -1), read before the main loop
+    // the first chunk's 16-bit W values and X columns of this thread, loaded
+    // by the kernel before the dequantization (valid when pre_loaded)
+    bool pre_loaded;
+    uint4 pre_w[2], pre_x[2];
 };
 constexpr int kOC = 32;                       // outliers per staged chunk
 constexpr int kOS = kOC * 2 + 16;             // bytes per staged row / column (padded)
 constexpr int kStageHalf = 256 * kOS;         // X part (rows) or W part (columns)
 constexpr int kStageBytes = 4 * kStageHalf;   // two buffers of X and W
-constexpr int kYS = 256 * 2 + 16;             // bytes per row of the staged Y tile (padded)
-constexpr int kYBytes = 256 * kYS;            // the 256 x 256 tile of 16-bit Y values
+// The staged Y tile: 64 groups of 4 rows; in a group, column c's 4 values
+// are 8 contiguous bytes at 8 c (so a lane stores the 4 rows of one column
+// that it holds as one 8-byte write), groups kYG bytes apart (padded).
+constexpr int kYG = 256 * 8 + 32;
+constexpr int kYBytes = 64 * kYG;             // the 256 x 256 tile of 16-bit Y values
 
 // SBN > 0 (streaming kernel, STH threads, n-tile of SBN columns): with more
 // than 16 outliers the outlier W rows go through LDS like the large-tile
@@ -343,7 +351,7 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a,
         // (the tile's columns are one panel of the blocked Wq and K % 64 ==
         // 0: byte (n, k) is at wk[64 (n - n0)] for the k part wk)
         const int64_t wrows = N - sc.n0 < kPanel ? N - sc.n0 : kPanel;
-        int k_next = e < o ? (by_pos ? e : a.idx[e]) : -1;
+        int k_next = e < o ? (by_pos ? e : sc.k_first) : -1;
         uint4 wv[2], xv[2];
         auto load_chunk = [&](int jc) {
             const int k = k_next;
@@ -393,7 +401,14 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a,
                         (uint16_t)(w4[c >> 1] >> ((c & 1) * 16));
             }
         };
-        load_chunk(0);
+        if (sc.pre_loaded && !recover) {
+            // chunk 0 was loaded before the dequantization
+            k_next = kOC + e < o ? (by_pos ? kOC + e : a.idx[kOC + e]) : -1;
+            wv[0] = sc.pre_w[0]; wv[1] = sc.pre_w[1];
+            xv[0] = sc.pre_x[0]; xv[1] = sc.pre_x[1];
+        } else {
+            load_chunk(0);
+        }
         for (int jc = 0; jc < opad; jc += kOC) {
             const int buf = (jc / kOC) & 1;
             store_chunk(buf);
@@ -430,11 +445,15 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a,
         }
     }
     if constexpr (STAGED) {
-        // Y through LDS: every wave writes its 16-bit values into a row-major
-        // 256 x 256 tile, then the workgroup stores whole 16-byte pieces of
-        // rows (1 KB per wave instruction) instead of 2-byte scattered
-        // stores.  Rows are padded by 16 bytes, so the two row groups of a
-        // lane write (rows 4 apart) fall on different banks.
+        // Y through LDS, then out as whole 16-byte pieces of rows (1 KB per
+        // wave store instruction) instead of 2-byte scattered stores.  A lane
+        // holds 4 consecutive rows of one column in registers 4g .. 4g+3
+        // (rows 8 g + row_l .. +3 of its 32 x 32 tile), so the tile is kept
+        // in LDS as groups of 4 rows with each column's 4 values contiguous:
+        // one 8-byte write per 4 values (a wave writes two groups of 256
+        // contiguous bytes).  The store phase reads, per thread, 8 columns of
+        // a group (64 contiguous bytes) and regroups the 16-bit values into
+        // the group's 4 row pieces with byte permutes.
         __syncthreads();   // every LDS read of the main loop and the outlier stage is done
         const int wm0 = (int)(mb - sc.m0), wn0 = (int)(nb - sc.n0);
 #pragma unroll
@@ -442,21 +461,42 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a,
 #pragma unroll
             for (int j = 0; j < TN; ++j)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int ml = wm0 + i * 32 + (r >> 2) * 8 + row_l + (r & 3);
+                for (int g = 0; g < 4; ++g) {
+                    const int grp = (wm0 + i * 32 + g * 8 + row_l) >> 2;   // row group
                     const int nl = wn0 + j * 32 + col_l;
-                    *reinterpret_cast<uint16_t*>(sc.lds + ml * kYS + nl * 2) =
-                        f32_to_h16<HT>(y[i][j][r]);
+                    const uint32_t lo = (uint32_t)f32_to_h16<HT>(y[i][j][4 * g]) |
+                                        ((uint32_t)f32_to_h16<HT>(y[i][j][4 * g + 1]) << 16);
+                    const uint32_t hi = (uint32_t)f32_to_h16<HT>(y[i][j][4 * g + 2]) |
+                                        ((uint32_t)f32_to_h16<HT>(y[i][j][4 * g + 3]) << 16);
+                    *reinterpret_cast<uint2*>(sc.lds + grp * kYG + nl * 8) = make_uint2(lo, hi);
                 }
         __syncthreads();
-        const int c = sc.tid & 31;
-        const int64_t n = sc.n0 + c * 8;   // N % 8 == 0: a piece is all in or all out
+        const int c = sc.tid & 31;           // columns 8 c .. 8 c + 7 of the tile
+        const int64_t n = sc.n0 + c * 8;     // N % 8 == 0: a piece is all in or all out
 #pragma unroll
-        for (int p = 0; p < 16; ++p) {
-            const int row = (sc.tid >> 5) + 16 * p;
-            const int64_t m = sc.m0 + row;
-            const uint4 v = *reinterpret_cast<const uint4*>(sc.lds + row * kYS + c * 16);
-            if (m < T && n < N) *reinterpret_cast<uint4*>(a.y + m * N + n) = v;
+        for (int q = 0; q < 4; ++q) {
+            const int grp = (sc.tid >> 5) + 16 * q;
+            const uint4* src = reinterpret_cast<const uint4*>(sc.lds + grp * kYG + c * 64);
+            // d[2 j] = rows 0, 1 of column j; d[2 j + 1] = rows 2, 3
+            uint32_t d[16];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const uint4 v = src[h];
+                d[4 * h] = v.x; d[4 * h + 1] = v.y; d[4 * h + 2] = v.z; d[4 * h + 3] = v.w;
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int64_t m = sc.m0 + grp * 4 + k;
+                uint32_t w[4];
+#pragma unroll
+                for (int j2 = 0; j2 < 4; ++j2) {
+                    // columns 2 j2 and 2 j2 + 1 of row k
+                    const uint32_t a0 = d[4 * j2 + (k >> 1)], a1 = d[4 * j2 + 2 + (k >> 1)];
+                    w[j2] = (k & 1) ? ((a0 >> 16) | (a1 & 0xFFFF0000u)) : ((a0 & 0xFFFFu) | (a1 << 16));
+                }
+                if (m < T && n < N)
+                    *reinterpret_cast<uint4*>(a.y + m * N + n) = make_uint4(w[0], w[1], w[2], w[3]);
+            }
         }
         return;
     }
@@ -675,6 +715,8 @@ __global__ __launch_bounds__(128 * WN) void k_gemm_i8_big(GemmArgs a) {
         sw_pre[j] = n < N ? a.sw[n] : 0.0f;
     }
     const int o_pre = a.count[0], opad_pre = a.count[1];
+    // the first outlier chunk's dimensions (slot tid % 32), for the epilogue
+    const int k_first = (tid & 31) < o_pre ? a.idx[tid & 31] : -1;
 
     // copy assignment: wave w fills the 1 KB groups GPW*w .. GPW*w+GPW-1 of A
     // and of B; in a group, lane l writes row 16g + l/4, physical chunk l%4.
@@ -836,9 +878,27 @@ __global__ __launch_bounds__(128 * WN) void k_gemm_i8_big(GemmArgs a) {
     }
     static_assert(THREADS == 512 && BM == 256 && BN == 256 && LDS_BYTES >= kStageBytes,
                   "staged epilogue: 512 threads, 256 x 256 tile");
-    epilogue<TM, TN, WRITE_ACC, HT, true>(
-        acc, a, m0 + wm0, n0 + wn0, lane,
-        StageCtx{lds, tid, m0, n0, sxs, sx_pre, sw_pre, o_pre, opad_pre});
+    // The first outlier chunk's operands (as the epilogue's staging assigns
+    // them: W row of slot tid % 32 over columns 16 (tid / 32) .. +16, X
+    // columns of tile row tid / 2), loaded now so that they arrive during
+    // the dequantization; rows recovered from Wq inside the epilogue are not.
+    StageCtx sc{lds, tid, m0, n0, sxs, sx_pre, sw_pre, o_pre, opad_pre, k_first, false, {}, {}};
+    if (opad_pre > 0 && a.w16 && !(a.w16_rows > 0 && o_pre > a.w16_rows)) {
+        const int e = tid & 31, cb = tid >> 5, xr = tid >> 1, xh = tid & 1;
+        const int k = e < o_pre ? (a.w16_rows > 0 ? e : k_first) : -1;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t n = n0 + cb * 16 + h * 8;
+            sc.pre_w[h] = (k >= 0 && n < N) ? *reinterpret_cast<const uint4*>(a.w16 + (int64_t)k * N + n)
+                                            : make_uint4(0u, 0u, 0u, 0u);
+            const int jx = xh * 16 + h * 8;
+            sc.pre_x[h] = (m0 + xr < T && jx < opad_pre)
+                              ? *reinterpret_cast<const uint4*>(a.xo + (m0 + xr) * opad_pre + jx)
+                              : make_uint4(0u, 0u, 0u, 0u);
+        }
+        sc.pre_loaded = true;
+    }
+    epilogue<TM, TN, WRITE_ACC, HT, true>(acc, a, m0 + wm0, n0 + wn0, lane, sc);
 }
 
 // XOR swizzle of the eight 16-byte chunks of a 128-byte LDS row (streaming
@@ -965,7 +1025,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_i8_stream(GemmA
     // land before the workgroup ends
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     epilogue<TM, TN, WRITE_ACC, HT, false, BN, 64 * NW>(acc, a, m0 + wm0, n0 + wn0, lane,
-                                                        StageCtx{lds, tid, m0, n0, nullptr, 0.0f, nullptr, 0, 0});
+                                                        StageCtx{lds, tid, m0, n0, nullptr, 0.0f, nullptr, 0, 0, -1,
+                                                                 false, {}, {}});
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int HT>
