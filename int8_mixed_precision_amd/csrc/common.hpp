@@ -29,6 +29,13 @@ __device__ __forceinline__ float h16_to_f32(uint16_t b) {
     else return (float)__builtin_bit_cast(_Float16, b);
 }
 
+// Packed unsigned max of two pairs of 16-bit lanes (v_pk_max_u16).
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                  __builtin_bit_cast(u16x2, b)));
+}
+
 // fp32 -> 16-bit, round to nearest even
 template <int HT>
 __device__ __forceinline__ uint16_t f32_to_h16(float f) {
@@ -37,7 +44,9 @@ __device__ __forceinline__ uint16_t f32_to_h16(float f) {
 }
 
 // Device workspace of one activation pass.  All regions are 256-byte aligned.
-//   flags   u32 [kw]     bit k%32 of word k/32 set when dimension k is an outlier
+//   flags   u32 [kDetectParts][kwp]  bit k%32 of word k/32 set when dimension k
+//           is an outlier: one bitmap, or (detection in row groups) one per
+//           group, to be ORed (kwp = kw rounded up to 64 words)
 //   wprefix i32 [kw]     number of outlier dimensions before word w
 //   count   i32 [4]      count[0] = o, count[1] = o rounded up to 16
 //   segmax  f32 [nseg][16], segcnt i32 [nseg]   per 2048-column segment, the
@@ -138,6 +147,12 @@ int device_cus();
 // 2 when the large-tile matmul of (T, K, N) runs each 256 x 256 output tile
 // as two halves of K on the current device, else 1.
 int gemm_ksplit(int64_t T, int64_t K, int64_t N);
+
+// Partial outlier bitmaps the workspace holds (row groups of the detection).
+constexpr int kDetectParts = 4;
+
+// Words between two partial outlier bitmaps of the workspace.
+inline int64_t bitmap_stride(int64_t K) { return (ceil_div(K, 32) + 63) & ~int64_t(63); }
 
 // Outlier rows the memory-halved variant recovers into the workspace before
 // the matmul (more outliers than this: the matmul recovers them itself).

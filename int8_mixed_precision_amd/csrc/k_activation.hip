@@ -19,6 +19,8 @@
 // for the row a workgroup is working on.
 #include "common.hpp"
 
+#include <algorithm>
+
 // Quantization must round x * r and any following add separately, exactly
 // like the definition; no multiply-add contraction in this file.
 #pragma clang fp contract(off)
@@ -84,35 +86,42 @@ __global__ __launch_bounds__(kOwnedWaves * kWave) void k_detect_owned(const uint
 }
 
 // Outlier flags for any number of rows without atomics or a clearing
-// kernel: a workgroup owns kColBlock = 64 columns (two bitmap words) and
-// reads every row of them.  A row's 64 columns are one 128-byte line, and a
-// wave's load instruction covers 8 rows (8 lanes per row, 16 bytes each), so
-// every request is a whole line; each lane keeps kColLoads rows' loads in
-// flight.  The lanes holding one column group merge their flags by
-// shuffles, the waves through LDS, and the two words are stored whole.
-// (Past 128 rows; the clearing kernel + atomic detection it replaces took
-// 3.8 + 12.2 us on T=2048, K=12288.)
+// kernel: a workgroup owns kColBlock = 64 columns (two bitmap words) of one
+// group of rows (blockIdx.y; gridDim.y groups of consecutive rows) and
+// stores the flags of its rows whole into that group's partial bitmap
+// (flags + group * kwp words); the consumers OR the partial bitmaps.  The
+// row groups give the launch enough workgroups to fill the chip (one group:
+// K / 64 = 192 workgroups at K = 12288).  A row's 64 columns are one
+// 128-byte line, and a wave's load instruction covers 8 rows (8 lanes per
+// row, 16 bytes each), so every request is a whole line; each lane keeps
+// kColLoads rows' loads in flight.  The lanes holding one column group
+// merge their flags by shuffles, the waves through LDS.
 constexpr int kColBlock = 64;
 constexpr int kColWaves = 8;
-constexpr int kColLoads = 16;
+constexpr int kColLoads = 8;
+constexpr int kColRowsPerPass = 8 * kColWaves * kColLoads;   // 512
 template <int HT>
 __global__ __launch_bounds__(kColWaves * kWave) void k_detect_cols(const uint16_t* __restrict__ X,
                                                                    int64_t T, int64_t K, float tau,
-                                                                   uint32_t* __restrict__ flags) {
+                                                                   uint32_t* __restrict__ flags,
+                                                                   int64_t kwp) {
     __shared__ uint32_t wfm[kColWaves][8];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid >> 6;
     const int cg = lane & 7;                           // 8-column group of the lane
     const int64_t c0 = (int64_t)blockIdx.x * kColBlock + cg * 8;
     const bool in = c0 < K;
     const uint16_t* xc = X + (in ? c0 : 0);
-    constexpr int kRowsPerPass = 8 * kColWaves * kColLoads;
+    // rows r0 .. r1-1 of this group
+    const int64_t per = ceil_div(T, (int64_t)gridDim.y);
+    const int64_t r0 = (int64_t)blockIdx.y * per;
+    const int64_t r1 = r0 + per < T ? r0 + per : T;
     uint32_t m = 0;
-    for (int64_t t0 = (lane >> 3) + 8 * wv; t0 < T; t0 += kRowsPerPass) {
+    for (int64_t t0 = r0 + (lane >> 3) + 8 * wv; t0 < r1; t0 += kColRowsPerPass) {
         uint4 v[kColLoads];
 #pragma unroll
         for (int u = 0; u < kColLoads; ++u) {
             const int64_t t = t0 + (int64_t)u * 8 * kColWaves;
-            v[u] = *reinterpret_cast<const uint4*>(xc + (t < T ? t : T - 1) * K);
+            v[u] = *reinterpret_cast<const uint4*>(xc + (t < r1 ? t : r1 - 1) * K);
         }
 #pragma unroll
         for (int u = 0; u < kColLoads; ++u) {
@@ -124,7 +133,8 @@ __global__ __launch_bounds__(kColWaves * kWave) void k_detect_cols(const uint16_
             }
         }
     }
-    // rows past T re-read row T-1 (no flag changes); lanes past K flag nothing
+    // rows past the group re-read its last row (no flag changes); lanes past
+    // K flag nothing
     if (!in) m = 0;
     m |= __shfl_xor(m, 8);
     m |= __shfl_xor(m, 16);
@@ -138,7 +148,7 @@ __global__ __launch_bounds__(kColWaves * kWave) void k_detect_cols(const uint16_
         uint32_t word = f << ((lane & 3) * 8);
         word |= __shfl_xor(word, 1);
         word |= __shfl_xor(word, 2);
-        if ((lane & 3) == 0 && in) flags[c0 >> 5] = word;
+        if ((lane & 3) == 0 && in) flags[(int64_t)blockIdx.y * kwp + (c0 >> 5)] = word;
     }
 }
 
@@ -411,6 +421,203 @@ __global__ __launch_bounds__(NT) void k_rowquant_cached(
     if (tid == 0) sx[t] = mx;
 }
 
+// Row-wise quantization with each row held in registers, for many rows
+// (T > kOwnedMaxT) of up to kRegMaxK values.  A workgroup of kRQWaves waves
+// takes kRQWaves / WR rows, WR waves per row, each lane CH 16-byte chunks of
+// it (chunk c = 64 (i WR + w) + lane for wave w of the row, so each load
+// instruction reads one contiguous kilobyte).  With one wave per row the row
+// maximum needs no barrier at all, and a compute unit holds a dozen rows in
+// flight.
+//   - The detection's partial bitmaps are loaded first (small and cached),
+//     then the row, so waiting for the bitmap leaves the row in flight; the
+//     workgroup ORs the partials into LDS and scans the words' popcounts for
+//     the outliers' positions (workgroup 0 also writes the ascending index
+//     list and the count).
+//   - Row maximum over the non-outlier columns on the 16-bit patterns of |x|
+//     (for non-negative halves the unsigned order is the numeric order) by
+//     packed unsigned max, outlier halves masked to zero in the few chunks
+//     that hold one; one conversion to float per lane.
+//   - q = rint(x * r) as fp32(x * r) (one rounding) + 1.5 * 2^23 (rounds to
+//     the nearest integer, ties to even): the low byte of the sum's bit
+//     pattern is q as int8.  |x| <= s_x in a non-outlier column keeps
+//     |x * r| <= 127 (1 + 2^-23), so q lies in [-127, 127] without a clamp;
+//     outlier columns are zeroed afterwards by a byte mask.
+constexpr int kDetectGroups = kDetectParts;  // partial bitmaps of the detection
+constexpr int64_t kRegMaxK = 49152;          // longest row held in registers
+
+template <int HT, int NW, int WR, int CH>
+__global__ __launch_bounds__(NW * kWave) void k_rowquant_regs(
+    const uint16_t* __restrict__ X, int64_t T, int64_t K, const uint32_t* __restrict__ parts,
+    int nparts, int64_t kwp, int32_t* __restrict__ idx, int32_t* __restrict__ count,
+    int8_t* __restrict__ xq, float* __restrict__ sx, uint16_t* __restrict__ xo) {
+    constexpr int kRQThreads = NW * kWave;
+    constexpr int RPW = NW / WR;                        // rows per workgroup
+    constexpr int KW = WR * CH * 64 * 8 / 32;          // bitmap words of the longest row
+    constexpr int WPT = (KW + kRQThreads - 1) / kRQThreads;
+    static_assert(NW % WR == 0, "whole rows per workgroup");
+    __shared__ uint32_t fl[KW];
+    __shared__ int pf[KW];
+    __shared__ int wtot[NW];
+    __shared__ float wmx[NW];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wr = wave % WR;
+    const int64_t t = (int64_t)blockIdx.x * RPW + wave / WR;
+    const bool live = t < T;                            // uniform over the wave
+    const int nch = (int)(K / 8);
+    const int kw = (int)((K + 31) / 32);
+
+    // partial bitmaps, then the row (rows past T read row 0; nothing uses it)
+    uint32_t fr[WPT][kDetectGroups];
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) {
+        const int w = tid + kRQThreads * j;
+#pragma unroll
+        for (int r = 0; r < kDetectGroups; ++r)
+            fr[j][r] = (w < kw && r < nparts) ? parts[(int64_t)r * kwp + w] : 0u;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const uint16_t* row = X + (live ? t : 0) * K;
+    uint4 v[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int c = (i * WR + wr) * kWave + lane;
+        v[i] = *reinterpret_cast<const uint4*>(row + (int64_t)(c < nch ? c : 0) * 8);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) {
+        const int w = tid + kRQThreads * j;
+        uint32_t f = 0;
+#pragma unroll
+        for (int r = 0; r < kDetectGroups; ++r) f |= fr[j][r];
+        if (w < kw) fl[w] = f;
+    }
+    __syncthreads();   // fl
+    // outliers before each word: thread l scans words WPT l .. WPT l + WPT - 1
+    int o = 0;
+    {
+        int cnt = 0;
+#pragma unroll
+        for (int i = 0; i < WPT; ++i) {
+            const int w = WPT * tid + i;
+            if (w < kw) cnt += __builtin_popcount(fl[w]);
+        }
+        int run = block_excl_scan<kRQThreads>(cnt, wtot, o);
+#pragma unroll
+        for (int i = 0; i < WPT; ++i) {
+            const int w = WPT * tid + i;
+            if (w < kw) {
+                pf[w] = run;
+                uint32_t f = fl[w];
+                if (blockIdx.x == 0) {
+                    int p = run;
+                    while (f) {
+                        idx[p++] = w * 32 + __builtin_ctz(f);
+                        f &= f - 1u;
+                    }
+                }
+                run += __builtin_popcount(fl[w]);
+            }
+        }
+    }
+    const int opad = (o + 15) & ~15;
+    if (blockIdx.x == 0 && tid == 0) {
+        count[0] = o;
+        count[1] = opad;
+    }
+    // row maximum over the non-outlier columns
+    uint32_t m0 = 0u, m1 = 0u;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int c = (i * WR + wr) * kWave + lane;
+        if (c < nch) {
+            const uint32_t fm = (fl[c >> 2] >> ((c & 3) * 8)) & 0xFFu;
+            const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+            uint32_t keep[4] = {0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu};
+            if (fm) {
+#pragma unroll
+                for (int d = 0; d < 4; ++d)
+                    keep[d] = (((fm >> (2 * d)) & 1u) ? 0u : 0x00007FFFu) |
+                              (((fm >> (2 * d + 1)) & 1u) ? 0u : 0x7FFF0000u);
+            }
+            m0 = pk_max_u16(m0, pk_max_u16(w[0] & keep[0], w[1] & keep[1]));
+            m1 = pk_max_u16(m1, pk_max_u16(w[2] & keep[2], w[3] & keep[3]));
+        }
+    }
+    const uint32_t m = pk_max_u16(m0, m1);
+    const uint32_t mh = (m & 0xFFFFu) > (m >> 16) ? (m & 0xFFFFu) : (m >> 16);
+    float mx = wave_max(h16_to_f32<HT>((uint16_t)mh));
+    if constexpr (WR > 1) {
+        if (lane == 0) wmx[wave] = mx;
+    }
+    __syncthreads();   // pf (and, several waves per row, the waves' maxima)
+    if constexpr (WR > 1) {
+        const int w0 = wave - wr;
+        mx = wmx[w0];
+#pragma unroll
+        for (int q = 1; q < WR; ++q) mx = __builtin_fmaxf(mx, wmx[w0 + q]);
+    }
+    if (!live) return;
+    const float qk = HT == kHalfF16 ? 1.0f : qfactor(mx);   // fp16 scales are >= 2^-24
+    const float rr = mx > 0.0f ? 127.0f / (mx * qk) : 0.0f;   // IEEE fp32 divide
+    uint16_t* xo_row = xo + t * opad;
+    // Xq addresses: with every k-tile 64 wide (K % 64 == 0) chunk i of the
+    // lane is q0 + i * qstep in the panel-blocked layout (lane l holds bytes
+    // 8 (l % 8) of k-tile 8 (i WR + w) + l / 8), else blk_offset
+    const bool whole_tiles = K % kKTile == 0;
+    const int64_t p0 = t - t % kPanel;
+    const int64_t prow = T - p0 < kPanel ? T - p0 : kPanel;
+    const int64_t qstep = 8 * WR * kKTile * prow;
+    const int64_t q0 = p0 * K + (t - p0) * kKTile + 8 * (lane & 7) +
+                       (int64_t)(8 * wr + (lane >> 3)) * kKTile * prow;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int c = (i * WR + wr) * kWave + lane;
+        if (c >= nch) continue;
+        const uint32_t word = fl[c >> 2];
+        const uint32_t fm = (word >> ((c & 3) * 8)) & 0xFFu;
+        const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+        uint32_t f[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float x = h16_to_f32<HT>((uint16_t)(w[e >> 1] >> ((e & 1) * 16)));
+            const float p = __builtin_fmaf(x * qk, rr, 0.0f);
+            f[e] = __builtin_bit_cast(uint32_t, __fadd_rn(p, 12582912.0f));
+        }
+        uint32_t packed[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t lo = __builtin_amdgcn_perm(f[4 * h + 1], f[4 * h], 0x0c0c0400u);
+            const uint32_t hi = __builtin_amdgcn_perm(f[4 * h + 3], f[4 * h + 2], 0x0c0c0400u);
+            packed[h] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+        }
+        if (fm) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                uint32_t keep = 0u;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    keep |= ((fm >> (4 * h + e)) & 1u) ? 0u : (0xFFu << (8 * e));
+                packed[h] &= keep;
+            }
+            const int base_bit = (c & 3) * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if ((fm >> e) & 1u) {
+                    const int bit = base_bit + e;
+                    const int pos = pf[c >> 2] + __builtin_popcount(word & ((1u << bit) - 1u));
+                    xo_row[pos] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
+                }
+            }
+        }
+        const int64_t qo = whole_tiles ? q0 + i * qstep : blk_offset(t, (int64_t)c * 8, T, K);
+        *reinterpret_cast<uint2*>(xq + qo) = make_uint2(packed[0], packed[1]);
+    }
+    for (int j = o + wr * kWave + lane; j < opad; j += WR * kWave) xo_row[j] = 0;   // +0 in both types
+    if (wr == 0 && lane == 0) sx[t] = mx;
+}
+
 // ---- activation pass for T <= kSmallT rows, two kernels over column
 // segments.  A workgroup of 256 lanes owns kSegCols = 2048 columns, a lane 8
 // of them in every row, so a column's outlier flag is the OR over the lane's
@@ -625,6 +832,31 @@ void launch_seg(const uint16_t* xb, int64_t T, int64_t K, float tau, const Works
                        ws.flags, ws.segmax, ws.segcnt, ws.idx, ws.count, ws.xq, ws.sx, ws.xo);
 }
 
+// Shape of the register-resident row quantization for rows of K values:
+// waves per workgroup, waves per row and 16-byte chunks per lane.  Many
+// waves with few chunks each measured fastest (rows in flight at different
+// stages overlap their loads, arithmetic and stores): about 6 chunks per
+// lane, 4 to 16 waves per row; at K = 32768 4 waves of 16 chunks.
+// Activation pass alone, against one workgroup of 512 lanes per row:
+// T=2048, K=12288 32.5 -> 25.2 us; T=2048, K=49152 110.1 -> 94.0 us;
+// T=4096, K=12288 57.3 -> 44.1 us; T=3000, K=24576 86.2 -> 62.5 us.
+template <int HT>
+void launch_rowquant_regs(const uint16_t* xb, int64_t T, int64_t K, int nparts, int64_t kwp,
+                          const Workspace& ws, hipStream_t stream) {
+    auto go = [&](auto kern, int nw, int wr) {
+        const unsigned grid = (unsigned)ceil_div(T, nw / wr);
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(nw * kWave), 0, stream, xb, T, K, ws.flags, nparts,
+                           kwp, ws.idx, ws.count, ws.xq, ws.sx, ws.xo);
+    };
+    if (K <= 4096) go(k_rowquant_regs<HT, 4, 2, 4>, 4, 2);
+    else if (K <= 8192) go(k_rowquant_regs<HT, 4, 4, 4>, 4, 4);
+    else if (K <= 12288) go(k_rowquant_regs<HT, 4, 4, 6>, 4, 4);
+    else if (K <= 16384) go(k_rowquant_regs<HT, 8, 8, 4>, 8, 8);
+    else if (K <= 24576) go(k_rowquant_regs<HT, 8, 8, 6>, 8, 8);
+    else if (K <= 32768) go(k_rowquant_regs<HT, 4, 4, 16>, 4, 4);
+    else go(k_rowquant_regs<HT, 16, 16, 6>, 16, 16);
+}
+
 }  // namespace
 
 template <int HT>
@@ -645,9 +877,17 @@ static void launch_activation_typed(const uint16_t* xb, int64_t T, int64_t K, fl
         // whole, no clearing kernel
         hipLaunchKernelGGL(k_detect_owned<HT>, dim3((unsigned)ceil_div(K, kOwnedCols)),
                            dim3(kOwnedWaves * kWave), 0, stream, xb, T, K, tau, ws.flags);
+    } else if (K <= kRegMaxK) {
+        // row groups: partial bitmaps, ORed by the quantize kernel
+        const int64_t kwp = bitmap_stride(K);
+        const int groups = (int)std::min<int64_t>(kDetectGroups, ceil_div(T, kColRowsPerPass));
+        hipLaunchKernelGGL(k_detect_cols<HT>, dim3((unsigned)ceil_div(K, kColBlock), (unsigned)groups),
+                           dim3(kColWaves * kWave), 0, stream, xb, T, K, tau, ws.flags, kwp);
+        launch_rowquant_regs<HT>(xb, T, K, groups, kwp, ws, stream);
+        return;
     } else {
-        hipLaunchKernelGGL(k_detect_cols<HT>, dim3((unsigned)ceil_div(K, kColBlock)),
-                           dim3(kColWaves * kWave), 0, stream, xb, T, K, tau, ws.flags);
+        hipLaunchKernelGGL(k_detect_cols<HT>, dim3((unsigned)ceil_div(K, kColBlock), 1u),
+                           dim3(kColWaves * kWave), 0, stream, xb, T, K, tau, ws.flags, (int64_t)0);
     }
     // rows held in registers: the quantize kernel isolates the outliers too
     if (K <= (int64_t)kRowThreads * 4 * 8) {
@@ -715,7 +955,7 @@ Workspace carve_workspace(void* base, int64_t T, int64_t K, int64_t N, bool wrec
         off += align256(n);
         return p;
     };
-    w.flags = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)kw));
+    w.flags = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)(kDetectParts * bitmap_stride(K))));
     w.wprefix = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)kw));
     w.count = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * 4));
     const int64_t nseg = ceil_div(K, kSegCols);

@@ -125,13 +125,6 @@ template <int MAXB>
 using SmemPre = SmemT<kMaxXKPre, kW16Cache, kOutliersLdsPre, kMaxCpbPre + 1, MAXB>;
 static_assert(sizeof(SmemPre<kMaxBpw>) <= 160 * 1024, "LDS of one workgroup");
 
-// Packed unsigned max of two pairs of 16-bit lanes.
-__device__ inline uint32_t pk_max_u16(uint32_t a, uint32_t b) {
-    const uint32_t lo = (a & 0xFFFFu) > (b & 0xFFFFu) ? (a & 0xFFFFu) : (b & 0xFFFFu);
-    const uint32_t hi = (a >> 16) > (b >> 16) ? (a >> 16) : (b >> 16);
-    return lo | (hi << 16);
-}
-
 template <int HT>
 __device__ inline float chunk_val(const uint4& v, int e) {
     const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;

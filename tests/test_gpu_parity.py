@@ -180,10 +180,20 @@ def test_ragged_shapes(mm, T, K, N, nd, dist):
 
 
 @pytest.mark.parametrize("T,K,nd,dist", [
-    (130, 16384, 5, "normal"),    # register-cached row quantizer, 4 chunks per lane: every word held
-    (130, 16400, 5, "normal"),    # 12 chunks per lane, most of them past the row
-    (129, 49152, 40, "laplace"),  # 12 chunks per lane, every word held, many outliers
-    (129, 49168, 7, "normal"),    # past the register cache: separate compaction, two-pass rows
+    # register-resident row quantizer (rows in registers, partial bitmaps of
+    # the detection in row groups), one case per row shape, at its longest
+    # row or with K % 64 != 0 (byte addressing of the last k-tile), T odd
+    # against the rows per workgroup
+    (131, 4096, 3, "normal"),     # 2 waves per row, 4 chunks per lane, 2 rows per workgroup
+    (200, 8192, 4, "laplace"),    # 4 waves x 4 chunks
+    (151, 10000, 5, "normal"),    # 4 waves x 6 chunks, the last k-tile 16 wide
+    (130, 16384, 5, "normal"),    # 8 waves x 4 chunks: every word held
+    (130, 16400, 5, "normal"),    # 8 waves x 6 chunks, most of the last ones past the row
+    (133, 30000, 6, "normal"),    # 4 waves x 16 chunks, ragged
+    (140, 32768, 9, "laplace"),   # 4 waves x 16 chunks, every word held
+    (129, 49152, 40, "laplace"),  # 16 waves x 6 chunks, every word held, many outliers
+    (129, 49168, 7, "normal"),    # past the registers: one bitmap, separate compaction, two-pass rows
+    (1100, 12288, 6, "normal"),   # three row groups in the detection
 ])
 def test_row_quantizer_limits(mm, T, K, nd, dist):
     """The activation pass for more than 128 rows at the row lengths where
