@@ -6,9 +6,9 @@
 //   k_mfma_i8:   back-to-back v_mfma_i32_32x32x32_i8 on independent
 //                accumulators, no memory traffic: the int8 MFMA rate the
 //                part sustains when nothing else draws power;
-//   k_stream:    a coalesced 16-byte-per-lane read of a large buffer with
-//                16 loads in flight per lane, the HBM read rate a plain
-//                stream reaches.
+//   k_stream:    coalesced 16-byte-per-lane reads of a large buffer with
+//                16 or 32 loads in flight per lane, in a few orders and
+//                launch shapes: the HBM read rate a plain stream reaches.
 // Both record each workgroup's shader-clock cycles (s_memtime) and elapsed
 // constant-clock ticks (s_memrealtime, 100 MHz) so the clock they ran at
 // can be reported.
@@ -48,27 +48,31 @@ __global__ __launch_bounds__(256) void k_mfma_i8(int iters, int* sink, unsigned 
     }
 }
 
-// Grid-stride 16-byte loads, kStreamLoads of them in flight per lane; XOR
-// of everything read keeps the loads.
-constexpr int kStreamLoads = 16;
-__global__ __launch_bounds__(256) void k_stream(const uint4* __restrict__ p, int64_t n16, int* sink,
-                                                unsigned long long* clk) {
+// Streams of 16-byte loads, L of them in flight per lane, B lanes per
+// workgroup, in one of two orders: grid-stride (every workgroup walks the
+// whole buffer, one 16-byte piece per lane per step) or partitioned (each
+// workgroup reads one contiguous range).  The rate depends on the order,
+// the launch shape and the run (6.0 to 6.5 TB/s for the good shapes on
+// 2 GiB), so the host times a few and reports the best.  XOR of everything
+// read keeps the loads.  The host makes the element count a multiple of
+// grid * B * L, so no lane reads past the buffer.
+template <int L, int B, bool PART>
+__global__ __launch_bounds__(B) void k_stream(const uint4* __restrict__ p, int64_t n16, int* sink,
+                                              unsigned long long* clk) {
     const unsigned long long t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     uint4 x = make_uint4(0u, 0u, 0u, 0u);
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    for (; i + (kStreamLoads - 1) * stride < n16; i += kStreamLoads * stride) {
-        uint4 v[kStreamLoads];
+    const int64_t per = PART ? n16 / gridDim.x : n16;             // elements this workgroup walks
+    const int64_t step = PART ? B : (int64_t)gridDim.x * B;       // between a lane's loads
+    const uint4* q = p + (PART ? (int64_t)blockIdx.x * per : (int64_t)blockIdx.x * B) + threadIdx.x;
+    const int64_t span = PART ? per : n16 - (int64_t)blockIdx.x * B;
+    for (int64_t i = 0; i + (L - 1) * step < span; i += L * step) {
+        uint4 v[L];
 #pragma unroll
-        for (int u = 0; u < kStreamLoads; ++u) v[u] = p[i + u * stride];
+        for (int u = 0; u < L; ++u) v[u] = q[i + u * step];
 #pragma unroll
-        for (int u = 0; u < kStreamLoads; ++u) {
+        for (int u = 0; u < L; ++u) {
             x.x ^= v[u].x; x.y ^= v[u].y; x.z ^= v[u].z; x.w ^= v[u].w;
         }
-    }
-    for (; i < n16; i += stride) {
-        const uint4 a = p[i];
-        x.x ^= a.x; x.y ^= a.y; x.z ^= a.z; x.w ^= a.w;
     }
     if ((x.x ^ x.y ^ x.z ^ x.w) == 0x7fffffffu) sink[0] = 1;
     if (threadIdx.x == 0) {
@@ -88,9 +92,25 @@ extern "C" int ceiling_mfma_i8(int grid, int iters, void* sink, void* clk, void*
 
 extern "C" int ceiling_mfma_acc(void) { return kAcc; }
 
-extern "C" int ceiling_stream(const void* buf, int64_t bytes, int grid, void* sink, void* clk,
-                              void* stream) {
-    hipLaunchKernelGGL(k_stream, dim3(grid), dim3(256), 0, (hipStream_t)stream,
-                       (const uint4*)buf, bytes / 16, (int*)sink, (unsigned long long*)clk);
+// Stream variants: 0 = grid-stride, 16 loads, 256 lanes; 1 = grid-stride,
+// 32 loads, 256 lanes; 2 = partitioned, 16 loads, 512 lanes; 3 =
+// partitioned, 16 loads, 256 lanes.  Returns 2 for an unknown variant or a
+// size that is not a multiple of grid * lanes * loads * 16 bytes.
+extern "C" int ceiling_stream(const void* buf, int64_t bytes, int grid, int variant, void* sink,
+                              void* clk, void* stream) {
+    static const int lanes[4] = {256, 256, 512, 256}, loads[4] = {16, 32, 16, 16};
+    if (variant < 0 || variant > 3 || grid <= 0 || bytes <= 0) return 2;
+    const int64_t n16 = bytes / 16;
+    if (bytes % 16 != 0 || n16 % ((int64_t)grid * lanes[variant] * loads[variant]) != 0) return 2;
+    const hipStream_t s = (hipStream_t)stream;
+    const uint4* p = (const uint4*)buf;
+    int* k = (int*)sink;
+    unsigned long long* c = (unsigned long long*)clk;
+    switch (variant) {
+        case 0: hipLaunchKernelGGL((k_stream<16, 256, false>), dim3(grid), dim3(256), 0, s, p, n16, k, c); break;
+        case 1: hipLaunchKernelGGL((k_stream<32, 256, false>), dim3(grid), dim3(256), 0, s, p, n16, k, c); break;
+        case 2: hipLaunchKernelGGL((k_stream<16, 512, true>), dim3(grid), dim3(512), 0, s, p, n16, k, c); break;
+        default: hipLaunchKernelGGL((k_stream<16, 256, true>), dim3(grid), dim3(256), 0, s, p, n16, k, c); break;
+    }
     return hipGetLastError() == hipSuccess ? 0 : 1;
 }
