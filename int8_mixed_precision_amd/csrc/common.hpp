@@ -54,6 +54,12 @@ __device__ __forceinline__ uint16_t f32_to_h16(float f) {
 //           (activation pass for T <= 16 only; nseg = ceil(K / 2048))
 //   idx     i32 [K]      outlier dimensions, ascending
 //   sx      f32 [T]      row scales
+//   cand    f32 [T]      per row, the maximum of |x| over the columns below tau
+//                        in that row (single-read activation pass)
+//   rcnt    i32 [T]      per row, its nonzero outlier-flag words listed in rent
+//                        (-1: all its words are in rbits)
+//   rent    {u32,u32} [T][32]  (word index, word) of those words
+//   rbits   u32 [T][kw]  a row's flag words when more than 32 are nonzero
 //   xq      i8  [T,K]    quantized activations, outlier columns 0
 //   xo      16-bit [T,opad] outlier columns of X, row stride count[1], zero padded
 //   wrec    16-bit [min(K, kRecoverRows), N]  the outlier rows of W recovered from
@@ -74,6 +80,10 @@ struct Workspace {
     int32_t* segcnt;
     int32_t* idx;
     float* sx;
+    float* cand;
+    int32_t* rcnt;
+    uint2* rent;
+    uint32_t* rbits;
     int8_t* xq;
     uint16_t* xo;
     uint16_t* wrec;      // NULL when the workspace has no room for it
@@ -143,6 +153,12 @@ inline int64_t wq_bytes(int64_t K, int64_t N) { return K * N; }
 
 // Compute units of the current device (256 if it cannot be queried).
 int device_cus();
+
+// Bits of the smallest 16-bit value (binary16, or bfloat16 for ht = bf16)
+// >= tau (tau >= 0, not NaN), or the +inf pattern when no finite value
+// reaches tau: for a non-negative 16-bit value x (not NaN),
+// x >= tau <=> bits(x) >= this.
+uint32_t tau_to_h16_ceil(float tau, int ht);
 
 // 2 when the large-tile matmul of (T, K, N) runs each 256 x 256 output tile
 // as two halves of K on the current device, else 1.

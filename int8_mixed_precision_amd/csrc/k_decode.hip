@@ -671,7 +671,7 @@ __global__ __launch_bounds__(256) void k_decode_finish(DecodeArgs a) {
 // reaches tau.  Found by a binary search over the non-negative bit patterns,
 // whose unsigned order is the numeric order; both widenings to fp32 are
 // exact.
-static uint32_t tau_to_h16_ceil(float tau, int ht) {
+uint32_t tau_to_h16_ceil(float tau, int ht) {
     const uint32_t inf = ht == kHalfBF16 ? 0x7F80u : 0x7C00u;
     uint32_t lo = 0, hi = inf;   // answer in [lo, hi]
     while (lo < hi) {

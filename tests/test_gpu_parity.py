@@ -194,12 +194,53 @@ def test_ragged_shapes(mm, T, K, N, nd, dist):
     (129, 49152, 40, "laplace"),  # 16 waves x 6 chunks, every word held, many outliers
     (129, 49168, 7, "normal"),    # past the registers: one bitmap, separate compaction, two-pass rows
     (1100, 12288, 6, "normal"),   # three row groups in the detection
+    (1100, 24576, 6, "normal"),   # single-read pass, many rows
 ])
 def test_row_quantizer_limits(mm, T, K, nd, dist):
     """The activation pass for more than 128 rows at the row lengths where
     the row quantizer changes form."""
     X, W = synth.random_case(60_000 + K, T, K, 136, n_dims=nd, x_dist=dist)
     run_case(mm, f"row quantizer {T}x{K}x136", X, W, 6.0)
+
+
+def _row_max_in_outlier_column(T, K, seed):
+    """Rows whose largest magnitude below tau sits in a column that another
+    row makes an outlier: column 777 holds 7.0 in row 0 (an outlier) and
+    5.5 in every other row (above the rest of those rows, |x| < 3), so the
+    row scale must skip it; column 40 is >= tau in every row; column 41
+    holds exactly the row maximum in a non-outlier column for even rows
+    (5.5 again), where the scale is 5.5."""
+    rng = np.random.default_rng(seed)
+    X = np.clip(rng.standard_normal((T, K)), -2.9, 2.9)
+    X[:, 777] = 5.5
+    X[0, 777] = 7.0
+    X[:, 40] = -6.5
+    X[::2, 41] = -5.5
+    return X.astype(np.float16)
+
+
+# (T, K) of the single-read activation pass (rows longer than 16384, at
+# least 2^25 values) and of the two-kernel pass
+SINGLE_READ = [(700, 49152), (1400, 24576)]
+
+
+@pytest.mark.parametrize("T,K", SINGLE_READ + [(300, 20480), (200, 8192)])
+def test_row_max_in_outlier_column(mm, T, K):
+    """Row scales over the non-outlier columns when a row's largest value
+    below tau is in an outlier column (the single-read activation pass has to
+    redo such rows; the two-kernel pass never sees them)."""
+    X = _row_max_in_outlier_column(T, K, 70_000 + K)
+    W = synth.random_case(71_000 + K, 1, K, 8)[1]
+    r, _ = run_case(mm, f"row max in an outlier column {T}x{K}", X, W, 6.0)
+    assert int(r["count"][0]) == 2
+
+
+@pytest.mark.parametrize("T,K", [(1100, 32768), (150, 20480)])
+def test_many_flag_words_per_row(mm, T, K):
+    """More than 32 flag words of one row hold an outlier (the single-read
+    pass's per-row list overflows into whole flag rows)."""
+    X, W = synth.random_case(72_000 + K, T, K, 8, n_dims=120)
+    run_case(mm, f"120 outlier dimensions {T}x{K}", X, W, 6.0)
 
 
 def _random_shapes(n=24, seed=2024, max_macs=6e8):
