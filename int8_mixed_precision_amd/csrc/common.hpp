@@ -44,9 +44,10 @@ __device__ __forceinline__ uint16_t f32_to_h16(float f) {
 }
 
 // Device workspace of one activation pass.  All regions are 256-byte aligned.
-//   flags   u32 [kDetectParts][kwp]  bit k%32 of word k/32 set when dimension k
-//           is an outlier: one bitmap, or (detection in row groups) one per
-//           group, to be ORed (kwp = kw rounded up to 64 words)
+//   flags   u32 [kw]     bit k%32 of word k/32 set when dimension k is an outlier;
+//           past 128 rows with K <= 49152, [kDetectParts][kwp]: one partial
+//           bitmap per row group of the detection, to be ORed (kwp = kw
+//           rounded up to 64 words)
 //   wprefix i32 [kw]     number of outlier dimensions before word w
 //   count   i32 [4]      count[0] = o, count[1] = o rounded up to 16
 //   segmax  f32 [nseg][16], segcnt i32 [nseg]   per 2048-column segment, the
@@ -54,12 +55,6 @@ __device__ __forceinline__ uint16_t f32_to_h16(float f) {
 //           (activation pass for T <= 16 only; nseg = ceil(K / 2048))
 //   idx     i32 [K]      outlier dimensions, ascending
 //   sx      f32 [T]      row scales
-//   cand    f32 [T]      per row, the maximum of |x| over the columns below tau
-//                        in that row (single-read activation pass)
-//   rcnt    i32 [T]      per row, its nonzero outlier-flag words listed in rent
-//                        (-1: all its words are in rbits)
-//   rent    {u32,u32} [T][32]  (word index, word) of those words
-//   rbits   u32 [T][kw]  a row's flag words when more than 32 are nonzero
 //   xq      i8  [T,K]    quantized activations, outlier columns 0
 //   xo      16-bit [T,opad] outlier columns of X, row stride count[1], zero padded
 //   wrec    16-bit [min(K, kRecoverRows), N]  the outlier rows of W recovered from
@@ -80,10 +75,6 @@ struct Workspace {
     int32_t* segcnt;
     int32_t* idx;
     float* sx;
-    float* cand;
-    int32_t* rcnt;
-    uint2* rent;
-    uint32_t* rbits;
     int8_t* xq;
     uint16_t* xo;
     uint16_t* wrec;      // NULL when the workspace has no room for it

@@ -619,351 +619,6 @@ __global__ __launch_bounds__(NW * kWave) void k_rowquant_regs(
     if (wr == 0 && lane == 0) sx[t] = mx;
 }
 
-// ---- single-read activation pass (T > kOwnedMaxT rows of up to
-// kRegMaxK values): X is read from HBM once.
-//
-// The outlier set depends on every row, the row scale on the outlier set,
-// so the pass quantizes each row speculatively against what the row itself
-// shows and fixes the result up once the set is known:
-//   k_rowpass    holds the row in registers (the shapes of k_rowquant_regs),
-//                flags its columns with |x| >= tau, appends the row's
-//                nonzero flag words to a short list of its own (the whole
-//                row of words when they do not fit), takes s' = the maximum
-//                of |x| over its other columns, and writes Xq as quantized
-//                with s' (flagged columns 0) and s' itself; workgroup 0
-//                clears the bitmap;
-//   k_flagmerge  ORs the rows' lists in LDS, one slice of rows per
-//                workgroup, and the nonzero words into the bitmap (a few
-//                atomics per word: the same columns are flagged in many
-//                rows, and atomics on one address serialize);
-//   k_rowfix     scans the complete bitmap (workgroup 0 writes the index
-//                list and the count), gathers each row's outlier values into
-//                xo and zeroes the row's Xq bytes in the outlier columns.
-// The true scale s (maximum over the non-outlier columns, a subset of the
-// columns s' was taken over) equals s' whenever s' is reached in a column
-// that is not an outlier, and s' is then final, codes included.  If some
-// outlier column of the row holds |x| = s' (s' > 0), s' may have come from
-// it: k_rowfix then recomputes the row from X (maximum over the
-// non-outlier columns, every code rewritten).  Elements are compared as
-// fp32 (exact for 16-bit inputs); a NaN is never an outlier nor a maximum.
-// Rows longer than kSingleReadMinK, in inputs of at least kSingleReadMinTK
-// values, take the single-read pass; the rest the detection in row groups +
-// k_rowquant_regs, whose two kernels cost less than the single-read pass's
-// three for them (a launch costs a few microseconds here whatever its
-// work).  Activation pass alone, against the two-kernel pass: T=2048,
-// K=49152 98.0 -> 81.4 us; T=4096, K=49152 231 -> 147 us; T=3000, K=24576
-// 62.1 -> 48.1 us; but T=2048, K=12288 25.3 -> 24.8 us only, T=520,
-// K=32768 24.9 -> 27.9 us and T <= 1000 with shorter rows 2-8 us slower.
-constexpr int64_t kSingleReadMinK = 16384;
-constexpr int64_t kSingleReadMinTK = int64_t(1) << 25;
-bool single_read_pass(int64_t T, int64_t K) {
-    return T > kOwnedMaxT && K > kSingleReadMinK && K <= kRegMaxK && T * K >= kSingleReadMinTK;
-}
-constexpr int kFlagList = 32;                // flag words a row lists (k_rowpass)
-constexpr int kMergeGroups = 64;             // k_flagmerge workgroups
-constexpr int kMergeThreads = 1024;
-constexpr int kFixWaves = 4;                 // k_rowfix: one row per wave
-constexpr int kFixThreads = kFixWaves * kWave;
-constexpr int kFixMaxKW = (int)(kRegMaxK / 32);
-
-template <int HT, int NW, int WR, int CH>
-__global__ __launch_bounds__(NW * kWave) void k_rowpass(
-    const uint16_t* __restrict__ X, int64_t T, int64_t K, float tau, uint32_t tau16,
-    uint32_t* __restrict__ flags, int32_t* __restrict__ rcnt, uint2* __restrict__ rent,
-    uint32_t* __restrict__ rbits, float* __restrict__ cand, int8_t* __restrict__ xq) {
-    constexpr int RPW = NW / WR;                        // rows per workgroup
-    static_assert(NW % WR == 0 && WR > 1, "whole rows per workgroup, several waves per row");
-    __shared__ float wmx[NW];
-    __shared__ int rc[RPW];                             // flag words listed per row
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    const int wr = wave % WR;
-    const int64_t t = (int64_t)blockIdx.x * RPW + wave / WR;
-    const bool live = t < T;                            // uniform over the wave
-    const int nch = (int)(K / 8);
-    const uint16_t* row = X + (live ? t : 0) * K;       // rows past T read row 0, unused
-    uint4 v[CH];
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-        const int c = (i * WR + wr) * kWave + lane;
-        v[i] = *reinterpret_cast<const uint4*>(row + (int64_t)(c < nch ? c : 0) * 8);
-    }
-    const int kw = (int)((K + 31) / 32);
-    if (blockIdx.x == 0)
-        for (int w = threadIdx.x; w < kw; w += NW * kWave) flags[w] = 0u;
-    if (threadIdx.x < RPW) rc[threadIdx.x] = 0;
-    __syncthreads();   // rc
-    // local flags and the maximum over the other columns, on packed 16-bit
-    // magnitudes; a chunk whose largest magnitude pattern reaches tau16
-    // (an element >= tau, an infinity or a NaN) is redone in fp32
-    uint32_t fmw[(CH + 3) / 4] = {};
-    uint32_t m0 = 0u, m1 = 0u;
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-        const int c = (i * WR + wr) * kWave + lane;
-        uint32_t a[4] = {v[i].x & 0x7FFF7FFFu, v[i].y & 0x7FFF7FFFu, v[i].z & 0x7FFF7FFFu,
-                         v[i].w & 0x7FFF7FFFu};
-        if (c < nch) {
-            const uint32_t cm = pk_max_u16(pk_max_u16(a[0], a[1]), pk_max_u16(a[2], a[3]));
-            const uint32_t cmax = (cm & 0xFFFFu) > (cm >> 16) ? (cm & 0xFFFFu) : (cm >> 16);
-            if (cmax >= tau16) {
-                uint32_t fm = 0u, drop = 0u;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float ax = __builtin_fabsf(
-                        h16_to_f32<HT>((uint16_t)((e & 1) ? a[e >> 1] >> 16 : a[e >> 1] & 0xFFFFu)));
-                    const bool out = ax >= tau;
-                    fm |= (out ? 1u : 0u) << e;
-                    drop |= (out || ax != ax ? 1u : 0u) << e;
-                }
-#pragma unroll
-                for (int d = 0; d < 4; ++d)
-                    a[d] &= (((drop >> (2 * d)) & 1u) ? 0u : 0x0000FFFFu) |
-                            (((drop >> (2 * d + 1)) & 1u) ? 0u : 0xFFFF0000u);
-                fmw[i >> 2] |= fm << (8 * (i & 3));
-            }
-            m0 = pk_max_u16(m0, pk_max_u16(a[0], a[1]));
-            m1 = pk_max_u16(m1, pk_max_u16(a[2], a[3]));
-        }
-    }
-    // the row's nonzero flag words into its list: 4 lanes make one word
-    // (chunks c..c+3), the lane of chunk c appends it (LDS slot counter)
-    const int rr_ = wave / WR;                          // the row's slot in the workgroup
-    if (live) {
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const uint32_t fm = (fmw[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-            if (__ballot(fm != 0u)) {
-                const int c = (i * WR + wr) * kWave + lane;
-                uint32_t word = fm << ((c & 3) * 8);
-                word |= __shfl_xor(word, 1);
-                word |= __shfl_xor(word, 2);
-                if ((c & 3) == 0 && word != 0u && c < nch) {
-                    const int slot = atomicAdd(&rc[rr_], 1);
-                    if (slot < kFlagList) rent[t * kFlagList + slot] = make_uint2((uint32_t)(c >> 2), word);
-                }
-            }
-        }
-    }
-    const uint32_t m = pk_max_u16(m0, m1);
-    const uint32_t mh = (m & 0xFFFFu) > (m >> 16) ? (m & 0xFFFFu) : (m >> 16);
-    float mx = wave_max(h16_to_f32<HT>((uint16_t)mh));
-    if (lane == 0) wmx[wave] = mx;
-    __syncthreads();   // the waves' maxima, and every append to the row's list
-    {
-        const int w0 = wave - wr;
-        mx = wmx[w0];
-#pragma unroll
-        for (int q = 1; q < WR; ++q) mx = __builtin_fmaxf(mx, wmx[w0 + q]);
-    }
-    if (!live) return;
-    const int listed = rc[rr_];
-    if (wr == 0 && lane == 0) rcnt[t] = listed <= kFlagList ? listed : -1;
-    if (listed > kFlagList) {
-        // too many for the list: every flag word of the row (zeros included)
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const uint32_t fm = (fmw[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-            const int c = (i * WR + wr) * kWave + lane;
-            uint32_t word = fm << ((c & 3) * 8);
-            word |= __shfl_xor(word, 1);
-            word |= __shfl_xor(word, 2);
-            if ((c & 3) == 0 && c < nch) rbits[t * kw + (c >> 2)] = word;
-        }
-    }
-    const float qk = HT == kHalfF16 ? 1.0f : qfactor(mx);   // fp16 scales are >= 2^-24
-    const float rr = mx > 0.0f ? 127.0f / (mx * qk) : 0.0f;   // IEEE fp32 divide
-    // Xq addresses as in k_rowquant_regs
-    const bool whole_tiles = K % kKTile == 0;
-    const int64_t p0 = t - t % kPanel;
-    const int64_t prow = T - p0 < kPanel ? T - p0 : kPanel;
-    const int64_t qstep = 8 * WR * kKTile * prow;
-    const int64_t q0 = p0 * K + (t - p0) * kKTile + 8 * (lane & 7) +
-                       (int64_t)(8 * wr + (lane >> 3)) * kKTile * prow;
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-        const int c = (i * WR + wr) * kWave + lane;
-        if (c >= nch) continue;
-        const uint32_t fm = (fmw[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-        const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-        uint32_t f[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float x = h16_to_f32<HT>((uint16_t)(w[e >> 1] >> ((e & 1) * 16)));
-            const float p = __builtin_fmaf(x * qk, rr, 0.0f);
-            f[e] = __builtin_bit_cast(uint32_t, __fadd_rn(p, 12582912.0f));
-        }
-        uint32_t packed[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const uint32_t lo = __builtin_amdgcn_perm(f[4 * h + 1], f[4 * h], 0x0c0c0400u);
-            const uint32_t hi = __builtin_amdgcn_perm(f[4 * h + 3], f[4 * h + 2], 0x0c0c0400u);
-            packed[h] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-        }
-        if (fm) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                uint32_t keep = 0u;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    keep |= ((fm >> (4 * h + e)) & 1u) ? 0u : (0xFFu << (8 * e));
-                packed[h] &= keep;
-            }
-        }
-        const int64_t qo = whole_tiles ? q0 + i * qstep : blk_offset(t, (int64_t)c * 8, T, K);
-        *reinterpret_cast<uint2*>(xq + qo) = make_uint2(packed[0], packed[1]);
-    }
-    if (wr == 0 && lane == 0) cand[t] = mx;
-}
-
-// Merge of the rows' flag lists (see above): thread (row, j) ORs entry j
-// of the row's list into an LDS bitmap (every load of a workgroup in flight
-// at once), then the workgroup ORs its nonzero words into the bitmap that
-// k_rowpass cleared.  Rows whose words did not fit their list bring all of
-// them (thread j takes words j, j + 32, ...).
-__global__ __launch_bounds__(kMergeThreads) void k_flagmerge(
-    int64_t T, int64_t K, const int32_t* __restrict__ rcnt, const uint2* __restrict__ rent,
-    const uint32_t* __restrict__ rbits, uint32_t* __restrict__ flags) {
-    static_assert(kMergeThreads % kFlagList == 0, "whole lists per workgroup");
-    constexpr int kRowsPer = kMergeThreads / kFlagList;
-    __shared__ uint32_t lb[kFixMaxKW];
-    const int kw = (int)((K + 31) / 32);
-    const int j = threadIdx.x % kFlagList;
-    for (int w = threadIdx.x; w < kw; w += kMergeThreads) lb[w] = 0u;
-    __syncthreads();
-    for (int64_t t = (int64_t)blockIdx.x * kRowsPer + threadIdx.x / kFlagList; t < T;
-         t += (int64_t)gridDim.x * kRowsPer) {
-        const int n = rcnt[t];
-        const uint2 e = rent[t * kFlagList + j];   // read whatever n is; used only below n
-        if (j < n) {
-            atomicOr(&lb[e.x], e.y);
-        } else if (n < 0) {
-            for (int w = j; w < kw; w += kFlagList) {
-                const uint32_t f = rbits[t * kw + w];
-                if (f) atomicOr(&lb[w], f);
-            }
-        }
-    }
-    __syncthreads();
-    for (int w = threadIdx.x; w < kw; w += kMergeThreads)
-        if (lb[w]) atomicOr(&flags[w], lb[w]);
-}
-
-// Last kernel of the single-read pass: the bitmap into LDS with its
-// popcount prefix per word (workgroup 0 writes the index list and the
-// count), then one row per wave (see above).  (Each wave holding the bitmap
-// in registers and taking four rows measured slower: 5.2 -> 11.3 us at
-// T=2048, K=12288.)
-template <int HT>
-__global__ __launch_bounds__(kFixThreads) void k_rowfix(
-    const uint16_t* __restrict__ X, int64_t T, int64_t K, const uint32_t* __restrict__ flags,
-    const float* __restrict__ cand, int32_t* __restrict__ idx, int32_t* __restrict__ count,
-    int8_t* __restrict__ xq, float* __restrict__ sx, uint16_t* __restrict__ xo) {
-    constexpr int WPT = (kFixMaxKW + kFixThreads - 1) / kFixThreads;
-    __shared__ uint32_t fl[kFixMaxKW];
-    __shared__ int pf[kFixMaxKW];
-    __shared__ int wtot[kFixWaves];
-    const int tid = threadIdx.x, lane = tid & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int kw = (int)((K + 31) / 32);
-    const int nch = (int)(K / 8);
-    const int64_t t = (int64_t)blockIdx.x * kFixWaves + wave;
-    for (int w = tid; w < kw; w += kFixThreads) fl[w] = flags[w];
-    __syncthreads();   // fl
-    int o = 0;
-    {
-        int cnt = 0;
-#pragma unroll
-        for (int i = 0; i < WPT; ++i) {
-            const int w = WPT * tid + i;
-            if (w < kw) cnt += __builtin_popcount(fl[w]);
-        }
-        int run = block_excl_scan<kFixThreads>(cnt, wtot, o);
-#pragma unroll
-        for (int i = 0; i < WPT; ++i) {
-            const int w = WPT * tid + i;
-            if (w < kw) {
-                pf[w] = run;
-                uint32_t f = fl[w];
-                if (blockIdx.x == 0) {
-                    int p = run;
-                    while (f) {
-                        idx[p++] = w * 32 + __builtin_ctz(f);
-                        f &= f - 1u;
-                    }
-                }
-                run += __builtin_popcount(fl[w]);
-            }
-        }
-    }
-    const int opad = (o + 15) & ~15;
-    if (blockIdx.x == 0 && tid == 0) {
-        count[0] = o;
-        count[1] = opad;
-    }
-    __syncthreads();   // pf
-    if (t >= T) return;
-    const float s1 = cand[t];
-    const uint16_t* xr = X + t * K;
-    uint16_t* xo_row = xo + t * opad;
-    // outlier values of the row into xo; is s' held by an outlier column?
-    bool redo = false;
-    for (int w = lane; w < kw; w += kWave) {
-        uint32_t f = fl[w];
-        int pos = pf[w];
-        while (f) {
-            const int b = __builtin_ctz(f);
-            f &= f - 1u;
-            const uint16_t hb = xr[32 * w + b];
-            xo_row[pos++] = hb;
-            redo |= s1 > 0.0f && __builtin_fabsf(h16_to_f32<HT>(hb)) == s1;
-        }
-    }
-    for (int j = o + lane; j < opad; j += kWave) xo_row[j] = 0;   // +0 in both types
-    if (!__ballot(redo)) {
-        // s' is the row scale: zero the codes of the outlier columns
-        for (int w = lane; w < kw; w += kWave) {
-            uint32_t f = fl[w];
-            while (f) {
-                const int b = __builtin_ctz(f);
-                f &= f - 1u;
-                xq[blk_offset(t, 32 * w + b, T, K)] = 0;
-            }
-        }
-        if (lane == 0) sx[t] = s1;
-        return;
-    }
-    // the row again: maximum over the non-outlier columns, every code rewritten
-    float mx = 0.0f;
-    for (int c = lane; c < nch; c += kWave) {
-        const uint4 q = *reinterpret_cast<const uint4*>(xr + (int64_t)c * 8);
-        const uint32_t fm = (fl[c >> 2] >> ((c & 3) * 8)) & 0xFFu;
-        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float a = __builtin_fabsf(h16_to_f32<HT>((uint16_t)(w[e >> 1] >> ((e & 1) * 16))));
-            mx = ((fm >> e) & 1u) ? mx : __builtin_fmaxf(mx, a);
-        }
-    }
-    mx = wave_max(mx);
-    const float qk = HT == kHalfF16 ? 1.0f : qfactor(mx);
-    const float rr = mx > 0.0f ? 127.0f / (mx * qk) : 0.0f;
-    for (int c = lane; c < nch; c += kWave) {
-        const uint4 q = *reinterpret_cast<const uint4*>(xr + (int64_t)c * 8);
-        const uint32_t fm = (fl[c >> 2] >> ((c & 3) * 8)) & 0xFFu;
-        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-        uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float x = h16_to_f32<HT>((uint16_t)(w[e >> 1] >> ((e & 1) * 16)));
-            const uint32_t qv = ((fm >> e) & 1u) ? 0u : (uint32_t)(uint8_t)quant(x * qk, rr);
-            packed[e >> 2] |= qv << ((e & 3) * 8);
-        }
-        *reinterpret_cast<uint2*>(xq + blk_offset(t, (int64_t)c * 8, T, K)) = make_uint2(packed[0], packed[1]);
-    }
-    if (lane == 0) sx[t] = mx;
-}
-
 // ---- activation pass for T <= kSmallT rows, two kernels over column
 // segments.  A workgroup of 256 lanes owns kSegCols = 2048 columns, a lane 8
 // of them in every row, so a column's outlier flag is the OR over the lane's
@@ -1203,29 +858,6 @@ void launch_rowquant_regs(const uint16_t* xb, int64_t T, int64_t K, int nparts, 
     else go(k_rowquant_regs<HT, 16, 16, 6>, 16, 16);
 }
 
-// The single-read activation pass (shapes as for k_rowquant_regs).
-template <int HT>
-void launch_single_read(const uint16_t* xb, int64_t T, int64_t K, float tau, const Workspace& ws,
-                        hipStream_t stream) {
-    const uint32_t tau16 = tau_to_h16_ceil(tau, HT);
-    auto go = [&](auto kern, int nw, int wr) {
-        const unsigned grid = (unsigned)ceil_div(T, nw / wr);
-        hipLaunchKernelGGL(kern, dim3(grid), dim3(nw * kWave), 0, stream, xb, T, K, tau, tau16,
-                           ws.flags, ws.rcnt, ws.rent, ws.rbits, ws.cand, ws.xq);
-    };
-    if (K <= 4096) go(k_rowpass<HT, 4, 2, 4>, 4, 2);
-    else if (K <= 8192) go(k_rowpass<HT, 4, 4, 4>, 4, 4);
-    else if (K <= 12288) go(k_rowpass<HT, 4, 4, 6>, 4, 4);
-    else if (K <= 16384) go(k_rowpass<HT, 8, 8, 4>, 8, 8);
-    else if (K <= 24576) go(k_rowpass<HT, 8, 8, 6>, 8, 8);
-    else if (K <= 32768) go(k_rowpass<HT, 4, 4, 16>, 4, 4);
-    else go(k_rowpass<HT, 16, 16, 6>, 16, 16);
-    hipLaunchKernelGGL(k_flagmerge, dim3(kMergeGroups), dim3(kMergeThreads), 0, stream, T, K, ws.rcnt,
-                       ws.rent, ws.rbits, ws.flags);
-    hipLaunchKernelGGL(k_rowfix<HT>, dim3((unsigned)ceil_div(T, kFixWaves)), dim3(kFixThreads), 0,
-                       stream, xb, T, K, ws.flags, ws.cand, ws.idx, ws.count, ws.xq, ws.sx, ws.xo);
-}
-
 }  // namespace
 
 template <int HT>
@@ -1246,9 +878,6 @@ static void launch_activation_typed(const uint16_t* xb, int64_t T, int64_t K, fl
         // whole, no clearing kernel
         hipLaunchKernelGGL(k_detect_owned<HT>, dim3((unsigned)ceil_div(K, kOwnedCols)),
                            dim3(kOwnedWaves * kWave), 0, stream, xb, T, K, tau, ws.flags);
-    } else if (single_read_pass(T, K)) {
-        launch_single_read<HT>(xb, T, K, tau, ws, stream);
-        return;
     } else if (K <= kRegMaxK) {
         // row groups: partial bitmaps, ORed by the quantize kernel
         const int64_t kwp = bitmap_stride(K);
@@ -1328,7 +957,7 @@ Workspace carve_workspace(void* base, int64_t T, int64_t K, int64_t N, bool wrec
         return p;
     };
     // partial bitmaps only for the detection in row groups
-    const bool groups = T > kOwnedMaxT && K <= kRegMaxK && !single_read_pass(T, K);
+    const bool groups = T > kOwnedMaxT && K <= kRegMaxK;
     w.flags = reinterpret_cast<uint32_t*>(
         take(sizeof(uint32_t) * (size_t)(groups ? kDetectParts * bitmap_stride(K) : kw)));
     w.wprefix = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)kw));
@@ -1338,12 +967,6 @@ Workspace carve_workspace(void* base, int64_t T, int64_t K, int64_t N, bool wrec
     w.segcnt = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)nseg));
     w.idx = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)K));
     w.sx = reinterpret_cast<float*>(take(sizeof(float) * (size_t)T));
-    if (single_read_pass(T, K)) {
-        w.cand = reinterpret_cast<float*>(take(sizeof(float) * (size_t)T));
-        w.rcnt = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)T));
-        w.rent = reinterpret_cast<uint2*>(take(sizeof(uint2) * (size_t)T * kFlagList));
-        w.rbits = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)T * (size_t)kw));
-    }
     w.xq = reinterpret_cast<int8_t*>(take((size_t)T * (size_t)K));
     // worst case: every dimension an outlier, o = K (K % 16 == 0, so opad <= K)
     w.xo = reinterpret_cast<uint16_t*>(take(sizeof(uint16_t) * (size_t)T * (size_t)K));

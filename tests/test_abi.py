@@ -64,11 +64,7 @@ def test_workspace_size(mm):
     assert t512 >= 3 * 512 * 12288 + 2 * 512 * 36864 + 288 * (2 * 65536 * 4 + 4)
     assert mm.workspace_size(256, 12288, 36864) < 3 * 256 * 12288 + 2 * 512 * 36864 + (1 << 20)
     t4096 = mm.workspace_size(4096, 49152, 12288)                         # 3 full rounds
-    # rows longer than 16384 values past 128 rows: the single-read activation
-    # pass's per-row outlier-flag lists (32 entries of 8 bytes), full flag
-    # rows (K/8 bytes) and candidate scales
-    lists = 4096 * (32 * 8 + 49152 // 8 + 8)
-    assert t4096 < 3 * 4096 * 49152 + 2 * 512 * 12288 + lists + (1 << 20)
+    assert t4096 < 3 * 4096 * 49152 + 2 * 512 * 12288 + (1 << 20)
     # decode shapes run as one kernel and need only the fixed regions
     assert mm.workspace_size(8, 8192, 28672) < 3 * 8 * 8192 + (1 << 16)
     # few rows with a long K: S = ceil(48 / 16) + 3 = 6 slabs of int32

@@ -194,7 +194,7 @@ def test_ragged_shapes(mm, T, K, N, nd, dist):
     (129, 49152, 40, "laplace"),  # 16 waves x 6 chunks, every word held, many outliers
     (129, 49168, 7, "normal"),    # past the registers: one bitmap, separate compaction, two-pass rows
     (1100, 12288, 6, "normal"),   # three row groups in the detection
-    (1100, 24576, 6, "normal"),   # single-read pass, many rows
+    (1100, 24576, 6, "normal"),   # 8 waves x 6 chunks, three row groups
 ])
 def test_row_quantizer_limits(mm, T, K, nd, dist):
     """The activation pass for more than 128 rows at the row lengths where
@@ -219,16 +219,12 @@ def _row_max_in_outlier_column(T, K, seed):
     return X.astype(np.float16)
 
 
-# (T, K) of the single-read activation pass (rows longer than 16384, at
-# least 2^25 values) and of the two-kernel pass
-SINGLE_READ = [(700, 49152), (1400, 24576)]
-
-
-@pytest.mark.parametrize("T,K", SINGLE_READ + [(300, 20480), (200, 8192)])
+@pytest.mark.parametrize("T,K", [(700, 49152), (1400, 24576), (300, 20480), (200, 8192)])
 def test_row_max_in_outlier_column(mm, T, K):
     """Row scales over the non-outlier columns when a row's largest value
-    below tau is in an outlier column (the single-read activation pass has to
-    redo such rows; the two-kernel pass never sees them)."""
+    below tau is in a column that other rows make an outlier (a pass that
+    took the row maximum before knowing the outlier set would get it
+    wrong)."""
     X = _row_max_in_outlier_column(T, K, 70_000 + K)
     W = synth.random_case(71_000 + K, 1, K, 8)[1]
     r, _ = run_case(mm, f"row max in an outlier column {T}x{K}", X, W, 6.0)
@@ -236,9 +232,9 @@ def test_row_max_in_outlier_column(mm, T, K):
 
 
 @pytest.mark.parametrize("T,K", [(1100, 32768), (150, 20480)])
-def test_many_flag_words_per_row(mm, T, K):
-    """More than 32 flag words of one row hold an outlier (the single-read
-    pass's per-row list overflows into whole flag rows)."""
+def test_many_outlier_dims(mm, T, K):
+    """120 outlier dimensions spread over the row (more than 32 flagged
+    bitmap words per row)."""
     X, W = synth.random_case(72_000 + K, T, K, 8, n_dims=120)
     run_case(mm, f"120 outlier dimensions {T}x{K}", X, W, 6.0)
 
