@@ -39,6 +39,11 @@ sys.path.insert(0, ROOT)
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, published
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
 DECODE_ROTATE = 8
+# decode graphs hold this many passes over the rotating weight copies (32
+# calls per replay), as one decode step of a model holds many matmuls in one
+# graph; with one pass (8 calls) the replay launch added ~4 us per call
+DECODE_PASSES = 4
+CALLS_PER_REPLAY = DECODE_ROTATE * DECODE_PASSES
 CPU_THREADS = 16             # host-core share of one GPU on an 8-GPU host
 CPU_TARGET_S = 15.0
 
@@ -48,7 +53,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--only", choices=["prefill", "decode"], default=None)
+    p.add_argument("--only", choices=["prefill", "decode", "down"], default=None,
+                   help="one workload only (down: the down-projection context timing, for "
+                        "profiling runs)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-variants", action="store_true",
                    help="skip the memory-halved and bf16 variants and the down-projection "
@@ -343,7 +350,8 @@ def decode_batched(torch, mm, synth, w, sets, rounds, warmup, rows=(32, 128)):
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            one_round()
+            for _ in range(DECODE_PASSES):
+                one_round()
         torch.cuda.synchronize()
 
         def step(i, e):
@@ -354,8 +362,8 @@ def decode_batched(torch, mm, synth, w, sets, rounds, warmup, rows=(32, 128)):
                 e[1].record()
 
         prewarm(torch, step)
-        wall, _ = timed_loop(torch, rounds, max(1, warmup // DECODE_ROTATE + 1), step)
-        calls = rounds * DECODE_ROTATE
+        wall, _ = timed_loop(torch, rounds, max(1, warmup // CALLS_PER_REPLAY + 1), step)
+        calls = rounds * CALLS_PER_REPLAY
         out.append({"T": T, "us_per_call": round(wall * 1e6 / calls, 2),
                     "weight_GB/s": round(K * N * calls / wall / 1e9, 1),
                     "TOPS": round(2.0 * T * K * N * calls / wall / 1e12, 1)})
@@ -368,7 +376,7 @@ def decode_variants(torch, mm, w, X, sets, ws, Y, rounds, warmup):
     """The memory-halved and bf16 variants of the decode call (graph replays
     over the same rotating weight copies)."""
     T, K, N = w.T, w.K, w.N
-    steps = rounds * DECODE_ROTATE
+    steps = rounds * CALLS_PER_REPLAY
     wbytes = K * N + 4.0 * N
     # the memory-halved variant: no 16-bit weight passed at all
     def one_round_halved():
@@ -379,7 +387,8 @@ def decode_variants(torch, mm, w, X, sets, ws, Y, rounds, warmup):
     torch.cuda.synchronize()
     graph_h = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph_h):
-        one_round_halved()
+        for _ in range(DECODE_PASSES):
+            one_round_halved()
     torch.cuda.synchronize()
 
     def step_halved(i, e):
@@ -391,8 +400,8 @@ def decode_variants(torch, mm, w, X, sets, ws, Y, rounds, warmup):
             e[2].record()
 
     log(f"decode, memory-halved: {rounds} timed graph replays")
-    wall_h, evs_h = timed_loop(torch, rounds, max(1, warmup // DECODE_ROTATE + 1), step_halved)
-    call_h_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs_h])) / DECODE_ROTATE
+    wall_h, evs_h = timed_loop(torch, rounds, max(1, warmup // CALLS_PER_REPLAY + 1), step_halved)
+    call_h_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs_h])) / CALLS_PER_REPLAY
 
     # the bf16 variant: bf16 X and W16 (the same values rounded), weight
     # copies converted from the bf16 checkpoint
@@ -412,7 +421,8 @@ def decode_variants(torch, mm, w, X, sets, ws, Y, rounds, warmup):
     torch.cuda.synchronize()
     graph_b = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph_b):
-        one_round_bf16()
+        for _ in range(DECODE_PASSES):
+            one_round_bf16()
     torch.cuda.synchronize()
 
     def step_bf16(i, e):
@@ -424,8 +434,8 @@ def decode_variants(torch, mm, w, X, sets, ws, Y, rounds, warmup):
             e[2].record()
 
     log(f"decode, bf16 variant: {rounds} timed graph replays")
-    wall_b, evs_b = timed_loop(torch, rounds, max(1, warmup // DECODE_ROTATE + 1), step_bf16)
-    call_b_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs_b])) / DECODE_ROTATE
+    wall_b, evs_b = timed_loop(torch, rounds, max(1, warmup // CALLS_PER_REPLAY + 1), step_bf16)
+    call_b_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs_b])) / CALLS_PER_REPLAY
     del sets_b, graph_b
     # warm: the same weight copy in every call (235 MB, which the 256 MB
     # last-level cache can hold) - context next to the cold metric
@@ -439,7 +449,8 @@ def decode_variants(torch, mm, w, X, sets, ws, Y, rounds, warmup):
     torch.cuda.synchronize()
     graph_w = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph_w):
-        one_round_warm()
+        for _ in range(DECODE_PASSES):
+            one_round_warm()
     torch.cuda.synchronize()
 
     def step_warm(i, e):
@@ -451,7 +462,7 @@ def decode_variants(torch, mm, w, X, sets, ws, Y, rounds, warmup):
 
     log(f"decode, warm weight: {rounds} timed graph replays")
     prewarm(torch, step_warm)
-    wall_w, _ = timed_loop(torch, rounds, max(1, warmup // DECODE_ROTATE + 1), step_warm)
+    wall_w, _ = timed_loop(torch, rounds, max(1, warmup // CALLS_PER_REPLAY + 1), step_warm)
     del graph_w
     return {"halved_weight_gbs": wbytes * steps / wall_h / 1e9, "halved_call_ms": call_h_ms,
             "bf16_weight_gbs": wbytes * steps / wall_b / 1e9, "bf16_call_ms": call_b_ms,
@@ -473,8 +484,9 @@ def bench_decode(torch, mm, synth, steps, warmup, variants=True):
 
     # A decode call is tens of microseconds of GPU work, less than the Python
     # binding takes to issue it, so the steps are launched from a HIP graph
-    # (one replay = DECODE_ROTATE calls, one per weight copy), as a serving
-    # loop would.  The graph holds only the library's own kernel launches.
+    # (one replay = DECODE_PASSES passes over the DECODE_ROTATE weight
+    # copies), as a serving loop would.  The graph holds only the library's
+    # own kernel launches.
     def one_round():
         for Wq, sw, W16 in sets:
             mm.mixed_matmul(X, Wq, sw, W16, w.tau, workspace=ws, out=Y)
@@ -483,10 +495,11 @@ def bench_decode(torch, mm, synth, steps, warmup, variants=True):
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        one_round()
+        for _ in range(DECODE_PASSES):
+            one_round()
     torch.cuda.synchronize()
-    rounds = max(1, (steps + DECODE_ROTATE - 1) // DECODE_ROTATE)
-    steps = rounds * DECODE_ROTATE
+    rounds = max(2, (steps + CALLS_PER_REPLAY - 1) // CALLS_PER_REPLAY)
+    steps = rounds * CALLS_PER_REPLAY
 
     def step(i, e):
         if e is not None:
@@ -497,10 +510,10 @@ def bench_decode(torch, mm, synth, steps, warmup, variants=True):
             e[2].record()
 
     log(f"decode: {PREWARM_S} s prewarm, {warmup} warmup + {rounds} timed graph replays of "
-        f"{DECODE_ROTATE} calls")
+        f"{CALLS_PER_REPLAY} calls")
     prewarm(torch, step)
-    wall, evs = timed_loop(torch, rounds, max(1, warmup // DECODE_ROTATE + 1), step)
-    call_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) / DECODE_ROTATE
+    wall, evs = timed_loop(torch, rounds, max(1, warmup // CALLS_PER_REPLAY + 1), step)
+    call_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) / CALLS_PER_REPLAY
 
     extra = decode_variants(torch, mm, w, X, sets, ws, Y, rounds, warmup) if variants else {}
     if variants:
@@ -752,7 +765,7 @@ def main():
                if "halved_tops" in pre else ""))
         torch.cuda.empty_cache()
     down = None
-    if args.only is None and not args.no_variants:
+    if (args.only is None and not args.no_variants) or args.only == "down":
         down = bench_down(torch, mm, synth, args.steps, args.warmup)
         log(f"down: {down['TOPS']:.1f} TOPS ({down['ms_per_call']:.3f} ms/call, o = {down['outlier_dims']})")
     if args.only in (None, "decode"):
@@ -826,7 +839,8 @@ def main():
     if dec is not None:
         d = {"metric": "weight GB/s @ T=8", "value": round(dec["weight_gbs"], 1), "unit": "GB/s",
              "ms_per_step": round(dec["ms_per_step"], 5), "steps": dec["steps"],
-             "launch": "HIP graph replay of 8 calls (one per rotating weight copy)",
+             "launch": f"HIP graph replays of {CALLS_PER_REPLAY} calls ({DECODE_PASSES} passes over "
+                       f"the {DECODE_ROTATE} rotating weight copies)",
              "config": {"workload": "decode FFN up-projection, W pre-converted to Int8, "
                                     f"{DECODE_ROTATE} rotating weight copies",
                         "T": dec["T"], "K": dec["K"], "N": dec["N"], "tau": dec["tau"],

@@ -211,6 +211,7 @@ struct GemmArgs {
     int ksplit;            // 1, or 2: K split in two halves (large-tile kernel only)
     int32_t* ks_count;     // [tiles] (ksplit = 2; zeroed by launch_gemm)
     int32_t* ks_part;      // [tiles][2][65536] (ksplit = 2)
+    int64_t ks_full;       // ksplit = 2: tiles that run all of K (set by launch_gemm)
 };
 hipError_t launch_gemm(const GemmArgs& a, int ht, hipStream_t stream);
 

@@ -695,12 +695,19 @@ __global__ __launch_bounds__(128 * WN) void k_gemm_i8_big(GemmArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t T = a.T, K = a.K, N = a.N;
     const int64_t MT = ceil_div(T, BM);
-    // With the K split (S = 2) the grid holds every tile's first half, then
-    // every tile's second half: a unit never waits for another.
-    const int S = a.ksplit;
-    const int64_t tiles = (int64_t)gridDim.x / S;
-    const int half = (int)(blockIdx.x / tiles);
-    const int64_t tix = (int64_t)blockIdx.x - half * tiles;
+    // With the K split (ksplit = 2) the first ks_full tiles run all of K
+    // (one round of the CUs) and the rest as two halves: the grid holds the
+    // whole tiles, then the split tiles' first halves, then their second
+    // halves, so a unit never waits for another (half = -1: a whole tile).
+    const int64_t tiles = ceil_div(T, (int64_t)BM) * ceil_div(N, (int64_t)BN);
+    const int64_t full = a.ksplit == 2 ? a.ks_full : tiles;
+    int half = -1;
+    int64_t tix = blockIdx.x;
+    if (tix >= full) {
+        const int64_t v = tix - full, nsplit = tiles - full;
+        half = (int)(v / nsplit);
+        tix = full + v - half * nsplit;
+    }
     const int64_t bid = xcd_tile(tix, tiles);
     const int64_t m0 = (bid % MT) * BM;
     const int64_t n0 = (bid / MT) * BN;
@@ -781,9 +788,10 @@ __global__ __launch_bounds__(128 * WN) void k_gemm_i8_big(GemmArgs a) {
     // Prologue: tiles 0..3 in flight, wait for tile 0, first F0.  Past the
     // last tile, copies re-fetch tile KT-1 into a buffer that is never read
     // again, which keeps the loop free of branches and the wait count fixed.
-    // this unit's k-tiles KT0 .. KT-1 (K / BK is even when S = 2)
-    const int KT0 = half * (int)(K / BK / S);
-    const int KT = KT0 + (int)(K / BK / S);
+    // this unit's k-tiles KT0 .. KT-1 (K / BK is even when K is split)
+    const int nkt = (int)(K / BK);
+    const int KT0 = half < 0 ? 0 : half * (nkt / 2);
+    const int KT = half < 0 ? nkt : KT0 + nkt / 2;
 #pragma unroll
     for (int st = 0; st < STAGES; ++st)
 #pragma unroll
@@ -824,7 +832,7 @@ __global__ __launch_bounds__(128 * WN) void k_gemm_i8_big(GemmArgs a) {
     // no LDS copy may still be in flight when the LDS is reused or the
     // workgroup retires
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    if (S > 1) {
+    if (half >= 0) {
         // K split: each half publishes its int32 sums, and the half that
         // finishes second adds the other's (exact, order independent) and
         // runs the epilogue.  The tile counters were zeroed at launch.
@@ -1061,21 +1069,30 @@ __global__ void k_zero_i32(int32_t* __restrict__ p, int64_t n) {
 
 template <int WN, int HT>
 hipError_t launch_big(const GemmArgs& a, hipStream_t stream) {
+    const int64_t tiles = ceil_div(a.T, 256) * ceil_div(a.N, 256);
+    GemmArgs b = a;
+    b.ks_full = tiles;
     if (a.ksplit == 2) {
         // the tile counters start at zero (a kernel rather than a memset, so
         // the call can be captured in a graph); a split matmul is long enough
         // that one more launch does not show
-        const int64_t n = ceil_div(a.T, 256) * ceil_div(a.N, 256);
-        hipLaunchKernelGGL(k_zero_i32, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, stream,
-                           a.ks_count, n);
+        hipLaunchKernelGGL(k_zero_i32, dim3((unsigned)ceil_div(tiles, 256)), dim3(256), 0, stream,
+                           a.ks_count, tiles);
+        // whole tiles fill whole rounds of the CUs; only the rest is split
+        // (T=2048, N=12288: 384 tiles on 256 CUs run as 256 whole tiles and
+        // 128 split ones, 1.5 tile times either way, a third of the partial
+        // sums of splitting all 384)
+        const int64_t cus = device_cus();
+        b.ks_full = tiles > cus ? cus * (tiles / cus) : 0;
+        if (b.ks_full == tiles) b.ks_full = 0;
     }
-    const int64_t tiles = ceil_div(a.T, 256) * ceil_div(a.N, 256) * a.ksplit;
+    const int64_t units = b.ks_full + 2 * (tiles - b.ks_full);
     if (a.acc_out)
-        hipLaunchKernelGGL((k_gemm_i8_big<WN, true, HT>), dim3((unsigned)tiles), dim3(128 * WN), 0,
-                           stream, a);
+        hipLaunchKernelGGL((k_gemm_i8_big<WN, true, HT>), dim3((unsigned)units), dim3(128 * WN), 0,
+                           stream, b);
     else
-        hipLaunchKernelGGL((k_gemm_i8_big<WN, false, HT>), dim3((unsigned)tiles), dim3(128 * WN), 0,
-                           stream, a);
+        hipLaunchKernelGGL((k_gemm_i8_big<WN, false, HT>), dim3((unsigned)units), dim3(128 * WN), 0,
+                           stream, b);
     return hipGetLastError();
 }
 

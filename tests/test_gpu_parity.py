@@ -410,6 +410,16 @@ def test_staged_entry_points_match(mm, T, K, N1, N2):
 
 # ----------------------------------------------------------- full-size workloads
 
+def test_split_whole_and_half_tiles(mm):
+    """More 256x256 tiles than compute units with K split in two: one round
+    of tiles runs all of K and only the rest are split in halves (9 x 29 =
+    261 tiles; on 256 CUs the split ones are tiles 256..260, in the last
+    column of tiles, rows 1024 on).  Rows checked in whole and split tiles."""
+    X, W = synth.random_case(73_000, 2304, 8192, 7424, n_dims=5)
+    run_case(mm, "whole and split tiles 2304x8192x7424", X, W, 6.0,
+             rows=[0, 255, 256, 1000, 1024, 2047, 2048, 2300, 2303])
+
+
 def _sample_rows(T, rowsel, n=12, seed=0):
     """Rows to check against the oracle: first, last, random, and rows that
     carry planted outliers."""
