@@ -143,36 +143,42 @@ def prefill_variants(torch, mm, w, X, W16, Wq, sw, ws, Y, steps, warmup):
     fp32/bf16 checkpoint conversion, on the same inputs."""
     T, K, N = w.T, w.K, w.N
     ops = 2.0 * T * K * N
-    # the memory-halved variant (no 16-bit weight: outlier rows recovered
-    # from the Int8 weight), same steps
-    def step_halved(i, e):
-        if e is not None:
-            e[0].record()
-        mm.quantize_activations(X, N, w.tau, ws)
-        if e is not None:
-            e[1].record()
-        mm.matmul_prepared(ws, T, K, Wq, sw, None, out=Y)
-        if e is not None:
-            e[2].record()
-
-    log(f"prefill, memory-halved: {warmup} warmup + {steps} timed steps")
-    wall_h, evs_h = timed_loop(torch, steps, warmup, step_halved)
-    gemm_h_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs_h]))
-    # the bf16 variant on the same values rounded to bf16 (whole calls)
+    # The memory-halved variant (no 16-bit weight: outlier rows recovered
+    # from the Int8 weight) and the bf16 variant (the same values rounded to
+    # bf16, weight converted from the bf16 checkpoint) are timed alternated
+    # call by call with the fp16 call, so all three see the same clocks
+    # (timed one after another, later loops ran at lower clocks).
     Xb, Wb = X.to(torch.bfloat16), W16.to(torch.bfloat16)
     Wqb, swb, _ = mm.quantize_checkpoint(Wb)
     Yb = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
 
-    def step_bf16(i, e):
-        if e is not None:
-            e[0].record()
-        mm.mixed_matmul(Xb, Wqb, swb, Wb, w.tau, workspace=ws, out=Yb)
-        if e is not None:
-            e[1].record()
-            e[2].record()
+    def call_f16():
+        mm.mixed_matmul(X, Wq, sw, W16, w.tau, workspace=ws, out=Y)
 
-    log(f"prefill, bf16 variant: {warmup} warmup + {steps} timed steps")
-    wall_b, _ = timed_loop(torch, steps, warmup, step_bf16)
+    def call_halved():
+        mm.quantize_activations(X, N, w.tau, ws)
+        mm.matmul_prepared(ws, T, K, Wq, sw, None, out=Y)
+
+    def call_bf16():
+        mm.mixed_matmul(Xb, Wqb, swb, Wb, w.tau, workspace=ws, out=Yb)
+
+    calls = (("f16", call_f16), ("halved", call_halved), ("bf16", call_bf16))
+    log(f"prefill variants (fp16, memory-halved, bf16 alternated): {warmup} warmup + {steps} "
+        "timed rounds")
+    for _ in range(max(1, warmup)):
+        for _, c in calls:
+            c()
+    prewarm(torch, lambda i, e: [c() for _, c in calls])
+    evs = {name: [] for name, _ in calls}
+    for _ in range(steps):
+        for name, c in calls:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            c()
+            b.record()
+            evs[name].append((a, b))
+    torch.cuda.synchronize()
+    call_ms = {name: float(np.mean([a.elapsed_time(b) for a, b in v])) for name, v in evs.items()}
     # weight conversion from fp32 and bf16 checkpoints
     conv = {}
     W32 = W16.float()
@@ -190,10 +196,10 @@ def prefill_variants(torch, mm, w, X, W16, Wq, sw, ws, Y, steps, warmup):
                      "GB/s": round((Wc.element_size() * K * N + K * N + 4.0 * N) /
                                    (ms * 1e-3) / 1e9, 1)}
     del W32, Xb, Wb, Wqb, swb, Yb
-    return {"halved_tops": ops * steps / wall_h / 1e12, "halved_ms_per_step": wall_h * 1e3 / steps,
-            "halved_gemm_ms": gemm_h_ms,
-            "bf16_tops": ops * steps / wall_b / 1e12, "bf16_ms_per_step": wall_b * 1e3 / steps,
-            "convert": conv}
+    return {"halved_tops": ops / (call_ms["halved"] * 1e-3) / 1e12,
+            "halved_ms_per_step": call_ms["halved"],
+            "bf16_tops": ops / (call_ms["bf16"] * 1e-3) / 1e12, "bf16_ms_per_step": call_ms["bf16"],
+            "alternated_f16_ms": call_ms["f16"], "convert": conv}
 
 
 def bench_prefill(torch, mm, synth, steps, warmup, variants=True):
@@ -815,13 +821,14 @@ def main():
                                          "written"},
         })
         if "halved_tops" in pre:
+            alt = ("timed call by call alternated with the fp16 call (fp16 "
+                   f"{pre['alternated_f16_ms']:.4f} ms per call in the same loop)")
             out["memory_halved"] = {"note": "W16 not passed: outlier rows recovered from the "
-                                            "Int8 weight (same X, W, tau)",
+                                            "Int8 weight (same X, W, tau); " + alt,
                                     "TOPS": round(pre["halved_tops"], 2),
-                                    "ms_per_step": round(pre["halved_ms_per_step"], 4),
-                                    "gemm_ms": round(pre["halved_gemm_ms"], 4)}
+                                    "ms_per_step": round(pre["halved_ms_per_step"], 4)}
             out["bf16_variant"] = {"note": "X, W16, Y bfloat16 (the same values rounded to "
-                                           "bf16); whole int8_mixed_matmul_bf16 calls",
+                                           "bf16); whole int8_mixed_matmul_bf16 calls; " + alt,
                                    "TOPS": round(pre["bf16_tops"], 2),
                                    "ms_per_step": round(pre["bf16_ms_per_step"], 4)}
             out["quantize_weight"]["from_bf16"] = pre["convert"]["bf16"]
