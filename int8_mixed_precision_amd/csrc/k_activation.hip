@@ -22,6 +22,7 @@
 #include <algorithm>
 
 
+
 // Quantization must round x * r and any following add separately, exactly
 // like the definition; no multiply-add contraction in this file.
 #pragma clang fp contract(off)
@@ -97,19 +98,28 @@ __global__ __launch_bounds__(kOwnedWaves * kWave) void k_detect_owned(const uint
 // row, 16 bytes each), so every request is a whole line; each lane keeps
 // kColLoads rows' loads in flight.  The lanes holding one column group
 // merge their flags by shuffles, the waves through LDS.
-constexpr int kColBlock = 64;
+// Columns per workgroup: 64 (a 128-byte line per row) up to K = 16384,
+// 256 (512 bytes per row) above: a longer piece of each row per DRAM page
+// opened (rows are 2K bytes apart); whole calls, down projection T=2048,
+// K=49152 -0.5%, up projection (K=12288) +0.2% with 256.
+constexpr int kColBlockShort = 64;
+constexpr int kColBlockLong = 256;
 constexpr int kColWaves = 8;
 constexpr int kColLoads = 8;
-constexpr int kColRowsPerPass = 8 * kColWaves * kColLoads;   // 512
-template <int HT>
+constexpr int kColRowsPerPass = 8 * kColWaves * kColLoads;   // 512 (row groups)
+template <int HT, int CB>
 __global__ __launch_bounds__(kColWaves * kWave) void k_detect_cols(const uint16_t* __restrict__ X,
                                                                    int64_t T, int64_t K, float tau,
                                                                    uint32_t* __restrict__ flags,
                                                                    int64_t kwp) {
-    __shared__ uint32_t wfm[kColWaves][8];
+    constexpr int LPR = CB / 8;                        // lanes per row
+    constexpr int RPL = kWave / LPR;                   // rows per wave load
+    constexpr int RPP = RPL * kColWaves * kColLoads;   // rows per pass
+    static_assert(CB % 32 == 0 && kWave % LPR == 0, "whole bitmap words, whole rows per wave");
+    __shared__ uint32_t wfm[kColWaves][LPR];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid >> 6;
-    const int cg = lane & 7;                           // 8-column group of the lane
-    const int64_t c0 = (int64_t)blockIdx.x * kColBlock + cg * 8;
+    const int cg = lane % LPR;                         // 8-column group of the lane
+    const int64_t c0 = (int64_t)blockIdx.x * CB + cg * 8;
     const bool in = c0 < K;
     const uint16_t* xc = X + (in ? c0 : 0);
     // rows r0 .. r1-1 of this group
@@ -117,11 +127,11 @@ __global__ __launch_bounds__(kColWaves * kWave) void k_detect_cols(const uint16_
     const int64_t r0 = (int64_t)blockIdx.y * per;
     const int64_t r1 = r0 + per < T ? r0 + per : T;
     uint32_t m = 0;
-    for (int64_t t0 = r0 + (lane >> 3) + 8 * wv; t0 < r1; t0 += kColRowsPerPass) {
+    for (int64_t t0 = r0 + lane / LPR + RPL * wv; t0 < r1; t0 += RPP) {
         uint4 v[kColLoads];
 #pragma unroll
         for (int u = 0; u < kColLoads; ++u) {
-            const int64_t t = t0 + (int64_t)u * 8 * kColWaves;
+            const int64_t t = t0 + (int64_t)u * RPL * kColWaves;
             v[u] = *reinterpret_cast<const uint4*>(xc + (t < r1 ? t : r1 - 1) * K);
         }
 #pragma unroll
@@ -137,12 +147,11 @@ __global__ __launch_bounds__(kColWaves * kWave) void k_detect_cols(const uint16_
     // rows past the group re-read its last row (no flag changes); lanes past
     // K flag nothing
     if (!in) m = 0;
-    m |= __shfl_xor(m, 8);
-    m |= __shfl_xor(m, 16);
-    m |= __shfl_xor(m, 32);
-    if (lane < 8) wfm[wv][lane] = m;
+#pragma unroll
+    for (int d = LPR; d < kWave; d <<= 1) m |= __shfl_xor(m, d);
+    if (lane < LPR) wfm[wv][lane] = m;
     __syncthreads();
-    if (wv == 0 && lane < 8) {
+    if (wv == 0 && lane < LPR) {
         uint32_t f = 0;
 #pragma unroll
         for (int w = 0; w < kColWaves; ++w) f |= wfm[w][lane];
@@ -837,7 +846,9 @@ void launch_seg(const uint16_t* xb, int64_t T, int64_t K, float tau, const Works
 // waves per workgroup, waves per row and 16-byte chunks per lane.  Many
 // waves with few chunks each measured fastest (rows in flight at different
 // stages overlap their loads, arithmetic and stores): about 6 chunks per
-// lane, 4 to 16 waves per row; at K = 32768 4 waves of 16 chunks.
+// lane, 4 to 8 waves per row; at K = 32768 4 waves of 16 chunks; past it 8
+// waves of 12 chunks, two rows per workgroup (whole calls, down projection:
+// -0.4% against 16 waves of 6, +1% with 4 waves of 24).
 // Activation pass alone, against one workgroup of 512 lanes per row:
 // T=2048, K=12288 32.5 -> 25.2 us; T=2048, K=49152 110.1 -> 94.0 us;
 // T=4096, K=12288 57.3 -> 44.1 us; T=3000, K=24576 86.2 -> 62.5 us.
@@ -855,7 +866,7 @@ void launch_rowquant_regs(const uint16_t* xb, int64_t T, int64_t K, int nparts, 
     else if (K <= 16384) go(k_rowquant_regs<HT, 8, 8, 4>, 8, 8);
     else if (K <= 24576) go(k_rowquant_regs<HT, 8, 8, 6>, 8, 8);
     else if (K <= 32768) go(k_rowquant_regs<HT, 4, 4, 16>, 4, 4);
-    else go(k_rowquant_regs<HT, 16, 16, 6>, 16, 16);
+    else go(k_rowquant_regs<HT, 16, 8, 12>, 16, 8);
 }
 
 }  // namespace
@@ -882,12 +893,16 @@ static void launch_activation_typed(const uint16_t* xb, int64_t T, int64_t K, fl
         // row groups: partial bitmaps, ORed by the quantize kernel
         const int64_t kwp = bitmap_stride(K);
         const int groups = (int)std::min<int64_t>(kDetectGroups, ceil_div(T, kColRowsPerPass));
-        hipLaunchKernelGGL(k_detect_cols<HT>, dim3((unsigned)ceil_div(K, kColBlock), (unsigned)groups),
-                           dim3(kColWaves * kWave), 0, stream, xb, T, K, tau, ws.flags, kwp);
+        if (K > 16384)
+            hipLaunchKernelGGL((k_detect_cols<HT, kColBlockLong>), dim3((unsigned)ceil_div(K, kColBlockLong), (unsigned)groups),
+                               dim3(kColWaves * kWave), 0, stream, xb, T, K, tau, ws.flags, kwp);
+        else
+            hipLaunchKernelGGL((k_detect_cols<HT, kColBlockShort>), dim3((unsigned)ceil_div(K, kColBlockShort), (unsigned)groups),
+                               dim3(kColWaves * kWave), 0, stream, xb, T, K, tau, ws.flags, kwp);
         launch_rowquant_regs<HT>(xb, T, K, groups, kwp, ws, stream);
         return;
     } else {
-        hipLaunchKernelGGL(k_detect_cols<HT>, dim3((unsigned)ceil_div(K, kColBlock), 1u),
+        hipLaunchKernelGGL((k_detect_cols<HT, kColBlockLong>), dim3((unsigned)ceil_div(K, kColBlockLong), 1u),
                            dim3(kColWaves * kWave), 0, stream, xb, T, K, tau, ws.flags, (int64_t)0);
     }
     // rows held in registers: the quantize kernel isolates the outliers too

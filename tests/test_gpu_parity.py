@@ -188,10 +188,14 @@ def test_ragged_shapes(mm, T, K, N, nd, dist):
     (200, 8192, 4, "laplace"),    # 4 waves x 4 chunks
     (151, 10000, 5, "normal"),    # 4 waves x 6 chunks, the last k-tile 16 wide
     (130, 16384, 5, "normal"),    # 8 waves x 4 chunks: every word held
-    (130, 16400, 5, "normal"),    # 8 waves x 6 chunks, most of the last ones past the row
+    (130, 16400, 5, "normal"),    # 8 waves x 6 chunks, most of the last ones past the row;
+                                  # detection blocks of 256 columns, the last one 16 wide
     (133, 30000, 6, "normal"),    # 4 waves x 16 chunks, ragged
     (140, 32768, 9, "laplace"),   # 4 waves x 16 chunks, every word held
-    (129, 49152, 40, "laplace"),  # 16 waves x 6 chunks, every word held, many outliers
+    (129, 49152, 40, "laplace"),  # 8 waves x 12 chunks, 2 rows per workgroup (the last one's
+                                  # second row past T), every word held, many outliers
+    (131, 40016, 5, "normal"),    # the same, ragged; detection blocks of 256 columns, the last
+                                  # one 80 wide
     (129, 49168, 7, "normal"),    # past the registers: one bitmap, separate compaction, two-pass rows
     (1100, 12288, 6, "normal"),   # three row groups in the detection
     (1100, 24576, 6, "normal"),   # 8 waves x 6 chunks, three row groups
