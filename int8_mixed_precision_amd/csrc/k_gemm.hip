@@ -18,8 +18,10 @@
 // through LDS, double-buffered, with an XOR swizzle of the 16-byte chunks so
 // the ds_read_b128 of the operand fragments avoid bank conflicts.  The
 // 16-bit outlier product reuses the dequantized fp32 accumulators as the C
-// operand of v_mfma_f32_32x32x16_f16, so it needs no extra registers and the
-// sum is rounded to fp16 once.  Workgroups are renumbered so that the tiles
+// operand of the fp16 (bf16) MFMA of the same tile shape as the int8 one
+// (v_mfma_f32_16x16x32_f16 in the large-tile kernel, 32x32x16 in the
+// others), so it needs no extra registers and the sum is rounded to fp16
+// once.  Workgroups are renumbered so that the tiles
 // sharing a weight panel run on the same XCD (one L2).
 #include "common.hpp"
 
@@ -52,12 +54,8 @@ __device__ inline int swz(int row, int c) {
     return c ^ ((row / RPW) & (CPR - 1));
 }
 
-// Epilogue shared by the matmul kernels, for one wave's TM x TN grid of
-// 32x32 accumulator tiles whose top-left output element is (mb, nb).
-// 32x32 accumulator layout: lane holds column (lane & 31) and, in register
-// r, row 8*(r/4) + 4*(lane/32) + (r%4) of the tile.
 // What the large-tile kernel hands its epilogue for staging the outlier
-// operands through LDS (the other kernels pass an empty one).
+// operands through LDS (the streaming kernel passes lds, tid and n0 only).
 struct StageCtx {
     int8_t* lds;         // at least kStageBytes and kYBytes, free once the main loop is done
     int tid;             // 0 .. 511
@@ -76,16 +74,22 @@ constexpr int kOC = 32;                       // outliers per staged chunk
 constexpr int kOS = kOC * 2 + 16;             // bytes per staged row / column (padded)
 constexpr int kStageHalf = 256 * kOS;         // X part (rows) or W part (columns)
 constexpr int kStageBytes = 4 * kStageHalf;   // two buffers of X and W
-// The staged Y tile: 64 groups of 4 rows; in a group, column c's 4 values
-// are 8 contiguous bytes at 8 c (so a lane stores the 4 rows of one column
-// that it holds as one 8-byte write), groups kYG bytes apart (padded).
-constexpr int kYG = 256 * 8 + 32;
+// The staged Y tile of the large-tile kernel: 64 groups of 4 rows; in a
+// group, column c's 4 values are 8 contiguous bytes at 8 c (so a lane
+// stores the 4 rows of one column that it holds as one 8-byte write),
+// groups kYG bytes apart (padded so that groups g and g+1 lie half a bank
+// period apart).
+constexpr int kYG = 256 * 8 + 128;
 constexpr int kYBytes = 64 * kYG;             // the 256 x 256 tile of 16-bit Y values
 
+// Epilogue of the register-staged and streaming kernels, for one wave's
+// TM x TN grid of 32x32 accumulator tiles whose top-left output element is
+// (mb, nb).  32x32 accumulator layout: lane holds column (lane & 31) and, in
+// register r, row 8*(r/4) + 4*(lane/32) + (r%4) of the tile.
 // SBN > 0 (streaming kernel, STH threads, n-tile of SBN columns): with more
 // than 16 outliers the outlier W rows go through LDS like the large-tile
 // kernel's (sc.lds, sc.tid and sc.n0 used).
-template <int TM, int TN, bool WRITE_ACC, int HT, bool STAGED = false, int SBN = 0, int STH = 256>
+template <int TM, int TN, bool WRITE_ACC, int HT, int SBN = 0, int STH = 256>
 __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a, int64_t mb,
                                          int64_t nb, int lane, const StageCtx& sc = StageCtx{}) {
     const int64_t T = a.T, N = a.N;
@@ -106,17 +110,14 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a,
     }
     // dequantization by the outer product of the scales (1/127^2 folded
     // into the column scale)
-    // (the large-tile kernel read s_w, s_x and the counts before its main
-    // loop, so their latency is hidden; s_x reaches every lane through LDS)
     float swn[TN];
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
         const int64_t n = nb + j * 32 + col_l;
-        if constexpr (STAGED) swn[j] = sc.sw_pre[j] * (1.0f / 16129.0f);
-        else swn[j] = n < N ? a.sw[n] * (1.0f / 16129.0f) : 0.0f;
+        swn[j] = n < N ? a.sw[n] * (1.0f / 16129.0f) : 0.0f;
     }
-    const int o = STAGED ? sc.o : a.count[0];
-    const int opad = STAGED ? sc.opad : a.count[1];
+    const int o = a.count[0];
+    const int opad = a.count[1];
     // 16-bit outlier rows: the caller's W16 (row idx_j), the rows recovered
     // before the matmul (row j, when o fits), or - memory-halved variant
     // without room for those - recovered here from the Int8 weight,
@@ -127,12 +128,7 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a,
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
         const int64_t n = nb + j * 32 + col_l;
-        if constexpr (STAGED) dn[j] = recover ? sc.sw_pre[j] / 127.0f : 0.0f;
-        else dn[j] = recover && n < N ? a.sw[n] / 127.0f : 0.0f;
-    }
-    if constexpr (STAGED) {
-        if (sc.tid < 256) sc.sxs[sc.tid] = sc.sx_pre;
-        __syncthreads();
+        dn[j] = recover && n < N ? a.sw[n] / 127.0f : 0.0f;
     }
     // dequantize every tile (the integer accumulators die here, so the fp32
     // values take their registers; keeping the fp32 values in the integer
@@ -152,17 +148,12 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a,
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int m = mrow0 + i * 32 + g * 8;
-            if constexpr (STAGED) {
-                const float4 v = *reinterpret_cast<const float4*>(sc.sxs + (m - (int)sc.m0));
+            if (m + 3 < Ti) {
+                const float4 v = *reinterpret_cast<const float4*>(a.sx + m);
                 sxm[4 * g] = v.x; sxm[4 * g + 1] = v.y; sxm[4 * g + 2] = v.z; sxm[4 * g + 3] = v.w;
             } else {
-                if (m + 3 < Ti) {
-                    const float4 v = *reinterpret_cast<const float4*>(a.sx + m);
-                    sxm[4 * g] = v.x; sxm[4 * g + 1] = v.y; sxm[4 * g + 2] = v.z; sxm[4 * g + 3] = v.w;
-                } else {
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) sxm[4 * g + q] = a.sx[m + q < Ti ? m + q : Ti - 1];
-                }
+                for (int q = 0; q < 4; ++q) sxm[4 * g + q] = a.sx[m + q < Ti ? m + q : Ti - 1];
             }
         }
 #pragma unroll
@@ -170,335 +161,159 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[TM][TN], const GemmArgs& a,
 #pragma unroll
             for (int r = 0; r < 16; ++r) y[i][j][r] = (float)acc[i][j][r] * sxm[r] * swn[j];
     }
-    if constexpr (!STAGED) {
-        int jstart = 0;   // outliers done through LDS
-        if constexpr (SBN > 0) {
-            if (opad > 16) {
-                // the W rows of 32 outliers at a time: thread (slot e, column
-                // block cb) loads its outlier's row segment (16-byte loads
-                // along n) and writes it transposed into LDS, so that a lane's
-                // 8 outliers of one column are one 16-byte read; double
-                // buffered, the next chunk's loads in flight during this
-                // chunk's MFMAs.  X values come straight from the gathered
-                // columns (16 contiguous bytes per lane).
-                constexpr int CPB = SBN / (STH / 32);     // columns per block (STH / 32 blocks)
-                constexpr int NV = CPB / 8;               // 16-byte loads per thread
-                constexpr int kWS = SBN * kOS;            // bytes of one buffer
-                static_assert(NV >= 1 && NV * 8 * (STH / 32) == SBN, "whole 8-column pieces per thread");
-                __syncthreads();   // the main loop's LDS reads are complete
-                const int e = sc.tid & 31, cb = sc.tid >> 5;
-                float dcol[CPB];
-                if (recover) {
+    int jstart = 0;   // outliers done through LDS
+    if constexpr (SBN > 0) {
+        if (opad > 16) {
+            // the W rows of 32 outliers at a time: thread (slot e, column
+            // block cb) loads its outlier's row segment (16-byte loads
+            // along n) and writes it transposed into LDS, so that a lane's
+            // 8 outliers of one column are one 16-byte read; double
+            // buffered, the next chunk's loads in flight during this
+            // chunk's MFMAs.  X values come straight from the gathered
+            // columns (16 contiguous bytes per lane).
+            constexpr int CPB = SBN / (STH / 32);     // columns per block (STH / 32 blocks)
+            constexpr int NV = CPB / 8;               // 16-byte loads per thread
+            constexpr int kWS = SBN * kOS;            // bytes of one buffer
+            static_assert(NV >= 1 && NV * 8 * (STH / 32) == SBN, "whole 8-column pieces per thread");
+            __syncthreads();   // the main loop's LDS reads are complete
+            const int e = sc.tid & 31, cb = sc.tid >> 5;
+            float dcol[CPB];
+            if (recover) {
 #pragma unroll
-                    for (int c = 0; c < CPB; ++c) {
-                        const int64_t n = sc.n0 + cb * CPB + c;
-                        dcol[c] = n < N ? a.sw[n] / 127.0f : 0.0f;
-                    }
+                for (int c = 0; c < CPB; ++c) {
+                    const int64_t n = sc.n0 + cb * CPB + c;
+                    dcol[c] = n < N ? a.sw[n] / 127.0f : 0.0f;
                 }
-                // Wq byte (n, k) of this tile's panel (K % 64 == 0 here):
-                // wbase + the k part + 64 (n - wp0)
-                const int64_t wp0 = sc.n0 - sc.n0 % kPanel;
-                const int64_t wrows = N - wp0 < kPanel ? N - wp0 : kPanel;
-                int k_next = e < o ? (by_pos ? e : a.idx[e]) : -1;
-                uint4 wv[NV];
-                auto load_chunk = [&](int jc) {
-                    const int k = k_next;
-                    k_next = jc + kOC + e < o ? (by_pos ? jc + kOC + e : a.idx[jc + kOC + e]) : -1;
-                    const int kc = k < 0 ? 0 : k;   // (k < 0: nothing is read)
-                    const int8_t* wk = a.wq + wp0 * a.K + (int64_t)(kc & ~(int)(kKTile - 1)) * wrows +
-                                       (kc & (int)(kKTile - 1)) - wp0 * kKTile;
+            }
+            // Wq byte (n, k) of this tile's panel (K % 64 == 0 here):
+            // wbase + the k part + 64 (n - wp0)
+            const int64_t wp0 = sc.n0 - sc.n0 % kPanel;
+            const int64_t wrows = N - wp0 < kPanel ? N - wp0 : kPanel;
+            int k_next = e < o ? (by_pos ? e : a.idx[e]) : -1;
+            uint4 wv[NV];
+            auto load_chunk = [&](int jc) {
+                const int k = k_next;
+                k_next = jc + kOC + e < o ? (by_pos ? jc + kOC + e : a.idx[jc + kOC + e]) : -1;
+                const int kc = k < 0 ? 0 : k;   // (k < 0: nothing is read)
+                const int8_t* wk = a.wq + wp0 * a.K + (int64_t)(kc & ~(int)(kKTile - 1)) * wrows +
+                                   (kc & (int)(kKTile - 1)) - wp0 * kKTile;
 #pragma unroll
-                    for (int h = 0; h < NV; ++h) {
-                        const int64_t n = sc.n0 + cb * CPB + h * 8;
-                        if (!recover) {
-                            wv[h] = (k >= 0 && n < N)
-                                        ? *reinterpret_cast<const uint4*>(a.w16 + (int64_t)k * N + n)
-                                        : make_uint4(0u, 0u, 0u, 0u);
-                        } else {
-                            uint32_t p[4];
+                for (int h = 0; h < NV; ++h) {
+                    const int64_t n = sc.n0 + cb * CPB + h * 8;
+                    if (!recover) {
+                        wv[h] = (k >= 0 && n < N)
+                                    ? *reinterpret_cast<const uint4*>(a.w16 + (int64_t)k * N + n)
+                                    : make_uint4(0u, 0u, 0u, 0u);
+                    } else {
+                        uint32_t p[4];
 #pragma unroll
-                            for (int c = 0; c < 8; c += 2) {
-                                const int64_t nc = n + c;
-                                const uint16_t lo = (k >= 0 && nc < N)
-                                                        ? recover_weight<HT>(wk[nc * kKTile], dcol[h * 8 + c])
-                                                        : (uint16_t)0;
-                                const uint16_t hi = (k >= 0 && nc + 1 < N)
-                                                        ? recover_weight<HT>(wk[(nc + 1) * kKTile],
-                                                                             dcol[h * 8 + c + 1])
-                                                        : (uint16_t)0;
-                                p[c >> 1] = (uint32_t)lo | ((uint32_t)hi << 16);
-                            }
-                            wv[h] = make_uint4(p[0], p[1], p[2], p[3]);
+                        for (int c = 0; c < 8; c += 2) {
+                            const int64_t nc = n + c;
+                            const uint16_t lo = (k >= 0 && nc < N)
+                                                    ? recover_weight<HT>(wk[nc * kKTile], dcol[h * 8 + c])
+                                                    : (uint16_t)0;
+                            const uint16_t hi = (k >= 0 && nc + 1 < N)
+                                                    ? recover_weight<HT>(wk[(nc + 1) * kKTile],
+                                                                         dcol[h * 8 + c + 1])
+                                                    : (uint16_t)0;
+                            p[c >> 1] = (uint32_t)lo | ((uint32_t)hi << 16);
                         }
-                    }
-                };
-                auto store_chunk = [&](int buf) {
-                    int8_t* ws = sc.lds + buf * kWS;
-#pragma unroll
-                    for (int h = 0; h < NV; ++h) {
-                        const uint32_t w4[4] = {wv[h].x, wv[h].y, wv[h].z, wv[h].w};
-#pragma unroll
-                        for (int c = 0; c < 8; ++c)
-                            *reinterpret_cast<uint16_t*>(ws + (cb * CPB + h * 8 + c) * kOS + e * 2) =
-                                (uint16_t)(w4[c >> 1] >> ((c & 1) * 16));
-                    }
-                };
-                load_chunk(0);
-                for (int jc = 0; jc < opad; jc += kOC) {
-                    const int buf = (jc / kOC) & 1;
-                    store_chunk(buf);
-                    __syncthreads();
-                    if (jc + kOC < opad) load_chunk(jc + kOC);
-                    const int8_t* ws = sc.lds + buf * kWS;
-                    const int wn0 = (int)(nb - sc.n0);
-#pragma unroll
-                    for (int ks = 0; ks < kOC / 16; ++ks) {
-                        if (jc + ks * 16 >= opad) break;
-                        const int ko = ks * 32 + (lane >> 5) * 16;
-                        const int jl = jc + ks * 16 + (lane >> 5) * 8;
-                        v8u16 wb[TN];
-#pragma unroll
-                        for (int j = 0; j < TN; ++j)
-                            wb[j] = *reinterpret_cast<const v8u16*>(ws + (wn0 + j * 32 + col_l) * kOS + ko);
-#pragma unroll
-                        for (int i = 0; i < TM; ++i) {
-                            const int64_t mrow = mb + i * 32 + (lane & 31);
-                            const v8u16 xa = mrow < T ? *reinterpret_cast<const v8u16*>(a.xo + mrow * opad + jl)
-                                                      : v8u16{0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-                            for (int j = 0; j < TN; ++j) {
-                                if constexpr (HT == kHalfBF16)
-                                    y[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                        __builtin_bit_cast(v8bf, xa), __builtin_bit_cast(v8bf, wb[j]),
-                                        y[i][j], 0, 0, 0);
-                                else
-                                    y[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                                        __builtin_bit_cast(v8h, xa), __builtin_bit_cast(v8h, wb[j]),
-                                        y[i][j], 0, 0, 0);
-                            }
-                        }
+                        wv[h] = make_uint4(p[0], p[1], p[2], p[3]);
                     }
                 }
-                jstart = opad;
-            }
-        }
-        // 16-bit matmul over the isolated outlier dimensions, 16 at a time, with
-        // the dequantized values as the fp32 C operand.  A group's weight
-        // fragments (8 gathered values of one column per lane) are loaded once
-        // and serve all TM row strips.
-        for (int jc = jstart; jc < opad; jc += 16) {
-            const int jl = jc + (lane >> 5) * 8;   // first of this lane's 8 outlier slots
-            int kk[8];
-    #pragma unroll
-            for (int e = 0; e < 8; ++e) kk[e] = (jl + e < o) ? (by_pos ? jl + e : a.idx[jl + e]) : -1;
-            v8u16 wb[TN];
-    #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int64_t n = nb + j * 32 + col_l;
-                if (!recover) {
-    #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        wb[j][e] = (kk[e] >= 0 && n < N) ? a.w16[(int64_t)kk[e] * N + n] : (uint16_t)0;
-                } else {
-    #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        wb[j][e] = (kk[e] >= 0 && n < N)
-                                       ? recover_weight<HT>(a.wq[blk_offset(n, kk[e], N, a.K)], dn[j])
-                                       : (uint16_t)0;
+            };
+            auto store_chunk = [&](int buf) {
+                int8_t* ws = sc.lds + buf * kWS;
+#pragma unroll
+                for (int h = 0; h < NV; ++h) {
+                    const uint32_t w4[4] = {wv[h].x, wv[h].y, wv[h].z, wv[h].w};
+#pragma unroll
+                    for (int c = 0; c < 8; ++c)
+                        *reinterpret_cast<uint16_t*>(ws + (cb * CPB + h * 8 + c) * kOS + e * 2) =
+                            (uint16_t)(w4[c >> 1] >> ((c & 1) * 16));
                 }
-            }
-    #pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int64_t mrow = mb + i * 32 + (lane & 31);
-                const v8u16 xa = mrow < T ? *reinterpret_cast<const v8u16*>(a.xo + mrow * opad + jl)
-                                          : v8u16{0, 0, 0, 0, 0, 0, 0, 0};
-    #pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    if constexpr (HT == kHalfBF16)
-                        y[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            __builtin_bit_cast(v8bf, xa), __builtin_bit_cast(v8bf, wb[j]), y[i][j],
-                            0, 0, 0);
-                    else
-                        y[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                            __builtin_bit_cast(v8h, xa), __builtin_bit_cast(v8h, wb[j]), y[i][j],
-                            0, 0, 0);
-                }
-            }
-        }
-    } else if (opad > 0) {
-        // Staged through LDS, kOC outliers per chunk, double buffered: the
-        // 512 threads load the chunk's X columns (256 rows x kOC, coalesced
-        // along the compacted outliers) and W rows (kOC x 256 columns,
-        // transposed on the way into LDS so that a lane's 8 outliers of one
-        // column are contiguous), then every wave reads its MFMA fragments
-        // from LDS.  The next chunk's loads fly during this chunk's MFMAs;
-        // the outlier indices are fetched one chunk ahead of their use.
-        __syncthreads();   // the main loop's LDS reads are complete
-        const int t = sc.tid;
-        const int e = t & 31, cb = t >> 5;        // W: outlier slot, 16-column block
-        const int xr = t >> 1, xh = t & 1;        // X: tile row, 16-outlier half
-        const int64_t xrow = sc.m0 + xr;
-        float dcol[16];
-        if (recover) {
-#pragma unroll
-            for (int c = 0; c < 16; ++c) {
-                const int64_t n = sc.n0 + cb * 16 + c;
-                dcol[c] = n < N ? a.sw[n] / 127.0f : 0.0f;
-            }
-        }
-        // k: the W16 row of slot e (the outlier's dimension, or its position
-        // for recovered rows), or the dimension whose Wq bytes are recovered
-        // (the tile's columns are one panel of the blocked Wq and K % 64 ==
-        // 0: byte (n, k) is at wk[64 (n - n0)] for the k part wk)
-        const int64_t wrows = N - sc.n0 < kPanel ? N - sc.n0 : kPanel;
-        int k_next = e < o ? (by_pos ? e : sc.k_first) : -1;
-        uint4 wv[2], xv[2];
-        auto load_chunk = [&](int jc) {
-            const int k = k_next;
-            k_next = jc + kOC + e < o ? (by_pos ? jc + kOC + e : a.idx[jc + kOC + e]) : -1;
-            const int kc = k < 0 ? 0 : k;   // (k < 0: nothing is read)
-            const int8_t* wk = a.wq + sc.n0 * a.K + (int64_t)(kc & ~(int)(kKTile - 1)) * wrows +
-                               (kc & (int)(kKTile - 1));
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int64_t n = sc.n0 + cb * 16 + h * 8;
-                if (!recover) {
-                    wv[h] = (k >= 0 && n < N)
-                                ? *reinterpret_cast<const uint4*>(a.w16 + (int64_t)k * N + n)
-                                : make_uint4(0u, 0u, 0u, 0u);
-                } else {
-                    uint32_t p[4];
-#pragma unroll
-                    for (int c = 0; c < 8; c += 2) {
-                        const int nl = cb * 16 + h * 8 + c;   // column inside the tile
-                        const uint16_t lo = (k >= 0 && n + c < N)
-                                                ? recover_weight<HT>(wk[nl * kKTile], dcol[h * 8 + c])
-                                                : (uint16_t)0;
-                        const uint16_t hi = (k >= 0 && n + c + 1 < N)
-                                                ? recover_weight<HT>(wk[(nl + 1) * kKTile],
-                                                                     dcol[h * 8 + c + 1])
-                                                : (uint16_t)0;
-                        p[c >> 1] = (uint32_t)lo | ((uint32_t)hi << 16);
-                    }
-                    wv[h] = make_uint4(p[0], p[1], p[2], p[3]);
-                }
-                const int jx = jc + xh * 16 + h * 8;
-                xv[h] = (xrow < T && jx < opad)
-                            ? *reinterpret_cast<const uint4*>(a.xo + xrow * opad + jx)
-                            : make_uint4(0u, 0u, 0u, 0u);
-            }
-        };
-        auto store_chunk = [&](int buf) {
-            int8_t* xs = sc.lds + buf * 2 * kStageHalf;
-            int8_t* ws = xs + kStageHalf;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                *reinterpret_cast<uint4*>(xs + xr * kOS + xh * 32 + h * 16) = xv[h];
-                const uint32_t w4[4] = {wv[h].x, wv[h].y, wv[h].z, wv[h].w};
-#pragma unroll
-                for (int c = 0; c < 8; ++c)
-                    *reinterpret_cast<uint16_t*>(ws + (cb * 16 + h * 8 + c) * kOS + e * 2) =
-                        (uint16_t)(w4[c >> 1] >> ((c & 1) * 16));
-            }
-        };
-        if (sc.pre_loaded && !recover) {
-            // chunk 0 was loaded before the dequantization
-            k_next = kOC + e < o ? (by_pos ? kOC + e : a.idx[kOC + e]) : -1;
-            wv[0] = sc.pre_w[0]; wv[1] = sc.pre_w[1];
-            xv[0] = sc.pre_x[0]; xv[1] = sc.pre_x[1];
-        } else {
+            };
             load_chunk(0);
-        }
-        for (int jc = 0; jc < opad; jc += kOC) {
-            const int buf = (jc / kOC) & 1;
-            store_chunk(buf);
-            __syncthreads();
-            if (jc + kOC < opad) load_chunk(jc + kOC);
-            const int8_t* xs = sc.lds + buf * 2 * kStageHalf;
-            const int8_t* ws = xs + kStageHalf;
-            const int wm0 = (int)(mb - sc.m0), wn0 = (int)(nb - sc.n0);
+            for (int jc = 0; jc < opad; jc += kOC) {
+                const int buf = (jc / kOC) & 1;
+                store_chunk(buf);
+                __syncthreads();
+                if (jc + kOC < opad) load_chunk(jc + kOC);
+                const int8_t* ws = sc.lds + buf * kWS;
+                const int wn0 = (int)(nb - sc.n0);
 #pragma unroll
-            for (int ks = 0; ks < kOC / 16; ++ks) {
-                if (jc + ks * 16 >= opad) break;
-                const int ko = ks * 32 + (lane >> 5) * 16;
-                v8u16 wb[TN];
+                for (int ks = 0; ks < kOC / 16; ++ks) {
+                    if (jc + ks * 16 >= opad) break;
+                    const int ko = ks * 32 + (lane >> 5) * 16;
+                    const int jl = jc + ks * 16 + (lane >> 5) * 8;
+                    v8u16 wb[TN];
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    wb[j] = *reinterpret_cast<const v8u16*>(ws + (wn0 + j * 32 + col_l) * kOS + ko);
+                    for (int j = 0; j < TN; ++j)
+                        wb[j] = *reinterpret_cast<const v8u16*>(ws + (wn0 + j * 32 + col_l) * kOS + ko);
 #pragma unroll
-                for (int i = 0; i < TM; ++i) {
-                    const v8u16 xa =
-                        *reinterpret_cast<const v8u16*>(xs + (wm0 + i * 32 + col_l) * kOS + ko);
+                    for (int i = 0; i < TM; ++i) {
+                        const int64_t mrow = mb + i * 32 + (lane & 31);
+                        const v8u16 xa = mrow < T ? *reinterpret_cast<const v8u16*>(a.xo + mrow * opad + jl)
+                                                  : v8u16{0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-                    for (int j = 0; j < TN; ++j) {
-                        if constexpr (HT == kHalfBF16)
-                            y[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                __builtin_bit_cast(v8bf, xa), __builtin_bit_cast(v8bf, wb[j]),
-                                y[i][j], 0, 0, 0);
-                        else
-                            y[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                                __builtin_bit_cast(v8h, xa), __builtin_bit_cast(v8h, wb[j]),
-                                y[i][j], 0, 0, 0);
+                        for (int j = 0; j < TN; ++j) {
+                            if constexpr (HT == kHalfBF16)
+                                y[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                    __builtin_bit_cast(v8bf, xa), __builtin_bit_cast(v8bf, wb[j]),
+                                    y[i][j], 0, 0, 0);
+                            else
+                                y[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                                    __builtin_bit_cast(v8h, xa), __builtin_bit_cast(v8h, wb[j]),
+                                    y[i][j], 0, 0, 0);
+                        }
                     }
                 }
             }
+            jstart = opad;
         }
     }
-    if constexpr (STAGED) {
-        // Y through LDS, then out as whole 16-byte pieces of rows (1 KB per
-        // wave store instruction) instead of 2-byte scattered stores.  A lane
-        // holds 4 consecutive rows of one column in registers 4g .. 4g+3
-        // (rows 8 g + row_l .. +3 of its 32 x 32 tile), so the tile is kept
-        // in LDS as groups of 4 rows with each column's 4 values contiguous:
-        // one 8-byte write per 4 values (a wave writes two groups of 256
-        // contiguous bytes).  The store phase reads, per thread, 8 columns of
-        // a group (64 contiguous bytes) and regroups the 16-bit values into
-        // the group's 4 row pieces with byte permutes.
-        __syncthreads();   // every LDS read of the main loop and the outlier stage is done
-        const int wm0 = (int)(mb - sc.m0), wn0 = (int)(nb - sc.n0);
+    // 16-bit matmul over the isolated outlier dimensions, 16 at a time, with
+    // the dequantized values as the fp32 C operand.  A group's weight
+    // fragments (8 gathered values of one column per lane) are loaded once
+    // and serve all TM row strips.
+    for (int jc = jstart; jc < opad; jc += 16) {
+        const int jl = jc + (lane >> 5) * 8;   // first of this lane's 8 outlier slots
+        int kk[8];
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int e = 0; e < 8; ++e) kk[e] = (jl + e < o) ? (by_pos ? jl + e : a.idx[jl + e]) : -1;
+        v8u16 wb[TN];
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
+        for (int j = 0; j < TN; ++j) {
+            const int64_t n = nb + j * 32 + col_l;
+            if (!recover) {
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int grp = (wm0 + i * 32 + g * 8 + row_l) >> 2;   // row group
-                    const int nl = wn0 + j * 32 + col_l;
-                    const uint32_t lo = (uint32_t)f32_to_h16<HT>(y[i][j][4 * g]) |
-                                        ((uint32_t)f32_to_h16<HT>(y[i][j][4 * g + 1]) << 16);
-                    const uint32_t hi = (uint32_t)f32_to_h16<HT>(y[i][j][4 * g + 2]) |
-                                        ((uint32_t)f32_to_h16<HT>(y[i][j][4 * g + 3]) << 16);
-                    *reinterpret_cast<uint2*>(sc.lds + grp * kYG + nl * 8) = make_uint2(lo, hi);
-                }
-        __syncthreads();
-        const int c = sc.tid & 31;           // columns 8 c .. 8 c + 7 of the tile
-        const int64_t n = sc.n0 + c * 8;     // N % 8 == 0: a piece is all in or all out
+                for (int e = 0; e < 8; ++e)
+                    wb[j][e] = (kk[e] >= 0 && n < N) ? a.w16[(int64_t)kk[e] * N + n] : (uint16_t)0;
+            } else {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int grp = (sc.tid >> 5) + 16 * q;
-            const uint4* src = reinterpret_cast<const uint4*>(sc.lds + grp * kYG + c * 64);
-            // d[2 j] = rows 0, 1 of column j; d[2 j + 1] = rows 2, 3
-            uint32_t d[16];
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                const uint4 v = src[h];
-                d[4 * h] = v.x; d[4 * h + 1] = v.y; d[4 * h + 2] = v.z; d[4 * h + 3] = v.w;
-            }
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int64_t m = sc.m0 + grp * 4 + k;
-                uint32_t w[4];
-#pragma unroll
-                for (int j2 = 0; j2 < 4; ++j2) {
-                    // columns 2 j2 and 2 j2 + 1 of row k
-                    const uint32_t a0 = d[4 * j2 + (k >> 1)], a1 = d[4 * j2 + 2 + (k >> 1)];
-                    w[j2] = (k & 1) ? ((a0 >> 16) | (a1 & 0xFFFF0000u)) : ((a0 & 0xFFFFu) | (a1 << 16));
-                }
-                if (m < T && n < N)
-                    *reinterpret_cast<uint4*>(a.y + m * N + n) = make_uint4(w[0], w[1], w[2], w[3]);
+                for (int e = 0; e < 8; ++e)
+                    wb[j][e] = (kk[e] >= 0 && n < N)
+                                   ? recover_weight<HT>(a.wq[blk_offset(n, kk[e], N, a.K)], dn[j])
+                                   : (uint16_t)0;
             }
         }
-        return;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int64_t mrow = mb + i * 32 + (lane & 31);
+            const v8u16 xa = mrow < T ? *reinterpret_cast<const v8u16*>(a.xo + mrow * opad + jl)
+                                      : v8u16{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                if constexpr (HT == kHalfBF16)
+                    y[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(v8bf, xa), __builtin_bit_cast(v8bf, wb[j]), y[i][j],
+                        0, 0, 0);
+                else
+                    y[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                        __builtin_bit_cast(v8h, xa), __builtin_bit_cast(v8h, wb[j]), y[i][j],
+                        0, 0, 0);
+            }
+        }
     }
     // the row indices are recomputed here rather than kept live through the
     // outlier loop (an empty asm hides the earlier values from the compiler)
@@ -639,53 +454,278 @@ __device__ __forceinline__ void copy_to_lds16(const void* gbase, uint32_t goff, 
 // s_waitcnt immediate that waits until at most `n` vector-memory operations
 // are outstanding (expcnt and lgkmcnt left at their no-wait maxima).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0xF70; }
-// s_waitcnt immediate for lgkmcnt(0) only (vmcnt 63, expcnt 7 = no wait)
-constexpr int kLgkm0 = 0xC07F;
 
 // XOR swizzle of the four 16-byte chunks of a 64-byte LDS row.  A fragment
-// read has lanes 0..31 on 32 consecutive rows at one logical chunk; with this
-// swizzle any 8 consecutive rows land on 8 distinct 16-byte slots of a
-// 128-byte window and any 16 consecutive rows on 16 distinct slots of a
-// 256-byte window, so the read is free of bank conflicts whether the LDS
-// serves 8 or 16 lanes of a ds_read_b128 per cycle.
+// read has lanes 16 c .. 16 c + 15 on 16 consecutive rows at logical chunk
+// c; with this swizzle any 8 consecutive rows land on 8 distinct 16-byte
+// slots of a 128-byte window and any 16 consecutive rows (rows 16 g ..) on
+// 16 distinct slots of a 256-byte window, so the read is free of bank
+// conflicts whether the LDS serves 8 or 16 lanes of a ds_read_b128 per
+// cycle.
 __device__ __forceinline__ int big_swz(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
 
-// Large-tile kernel for prefill shapes: a 256x256 workgroup tile split over
-// 2 x WN waves; each wave owns a 128 x (256/WN) grid of 32x32 MFMA tiles.
+// Epilogue of the large-tile kernel for one wave's 8 x 4 grid of 16x16
+// accumulator tiles (128 rows x 64 columns, top-left element (mb, nb)).
+// 16x16 accumulator layout: lane holds column lane % 16 and, in register v,
+// row 4 (lane / 16) + v of the tile - four consecutive rows of one column.
+// Dequantization by the outer product of the scales, the 16-bit outlier
+// product through LDS (v_mfma_f32_16x16x32_f16 / _bf16 with the dequantized
+// values as C, one 32-outlier chunk per instruction), then Y through LDS to
+// whole 16-byte row pieces.
+
+template <bool WRITE_ACC, int HT>
+__device__ __forceinline__ void epilogue_big(v4i (&acc)[8][4], const GemmArgs& a, int64_t mb,
+                                             int64_t nb, int lane, const StageCtx& sc) {
+    constexpr int TM = 8, TN = 4;
+    const int64_t T = a.T, N = a.N;
+    const int col_l = lane & 15;
+    const int row_l = (lane >> 4) * 4;
+    if (WRITE_ACC && a.acc_out) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int64_t n = nb + j * 16 + col_l;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int64_t m = mb + i * 16 + row_l + v;
+                    if (m < T && n < N) a.acc_out[m * N + n] = acc[i][j][v];
+                }
+            }
+    }
+    // dequantization by the outer product of the scales (1/127^2 folded
+    // into the column scale); s_w, s_x and the counts were read before the
+    // main loop, s_x reaches every lane through LDS
+    float swn[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) swn[j] = sc.sw_pre[j] * (1.0f / 16129.0f);
+    const int o = sc.o, opad = sc.opad;
+    // 16-bit outlier rows: the caller's W16 (row idx_j), the rows recovered
+    // before the matmul (row j, when o fits), or - memory-halved variant
+    // without room for those - recovered here from the Int8 weight,
+    // W^[k,n] = fp16(q[n,k] * fp32(s_w[n] / 127))
+    const bool recover = a.w16 == nullptr || (a.w16_rows > 0 && o > a.w16_rows);
+    const bool by_pos = !recover && a.w16_rows > 0;   // W16 row = outlier position
+    if (sc.tid < 256) sc.sxs[sc.tid] = sc.sx_pre;
+    __syncthreads();
+    const int wm0 = (int)(mb - sc.m0), wn0 = (int)(nb - sc.n0);
+    // the integer accumulators die here; the fp32 values take their registers
+    v4f y[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        // the lane's four rows of strip i: one 16-byte LDS read (rows past T
+        // hold the last row's scale; those outputs are never stored)
+        const float4 s = *reinterpret_cast<const float4*>(sc.sxs + wm0 + i * 16 + row_l);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            y[i][j][0] = (float)acc[i][j][0] * s.x * swn[j];
+            y[i][j][1] = (float)acc[i][j][1] * s.y * swn[j];
+            y[i][j][2] = (float)acc[i][j][2] * s.z * swn[j];
+            y[i][j][3] = (float)acc[i][j][3] * s.w * swn[j];
+        }
+    }
+    if (opad > 0) {
+        // Staged through LDS, kOC outliers per chunk, double buffered: the
+        // 512 threads load the chunk's X columns (256 rows x kOC, coalesced
+        // along the compacted outliers) and W rows (kOC x 256 columns,
+        // transposed on the way into LDS so that a lane's 8 outliers of one
+        // column are contiguous), then every wave reads its MFMA fragments
+        // from LDS.  The next chunk's loads fly during this chunk's MFMAs;
+        // the outlier indices are fetched one chunk ahead of their use.  A
+        // chunk's slots past o hold zeros on both sides.
+        __syncthreads();   // the main loop's LDS reads are complete
+        const int t = sc.tid;
+        const int e = t & 31, cb = t >> 5;        // W: outlier slot, 16-column block
+        const int xr = t >> 1, xh = t & 1;        // X: tile row, 16-outlier half
+        const int64_t xrow = sc.m0 + xr;
+        float dcol[16];
+        if (recover) {
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+                const int64_t n = sc.n0 + cb * 16 + c;
+                dcol[c] = n < N ? a.sw[n] / 127.0f : 0.0f;
+            }
+        }
+        // k: the W16 row of slot e (the outlier's dimension, or its position
+        // for recovered rows), or the dimension whose Wq bytes are recovered
+        // (the tile's columns are one panel of the blocked Wq and K % 64 ==
+        // 0: byte (n, k) is at wk[64 (n - n0)] for the k part wk)
+        const int64_t wrows = N - sc.n0 < kPanel ? N - sc.n0 : kPanel;
+        int k_next = e < o ? (by_pos ? e : sc.k_first) : -1;
+        uint4 wv[2], xv[2];
+        auto load_chunk = [&](int jc) {
+            const int k = k_next;
+            k_next = jc + kOC + e < o ? (by_pos ? jc + kOC + e : a.idx[jc + kOC + e]) : -1;
+            const int kc = k < 0 ? 0 : k;   // (k < 0: nothing is read)
+            const int8_t* wk = a.wq + sc.n0 * a.K + (int64_t)(kc & ~(int)(kKTile - 1)) * wrows +
+                               (kc & (int)(kKTile - 1));
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int64_t n = sc.n0 + cb * 16 + h * 8;
+                if (!recover) {
+                    wv[h] = (k >= 0 && n < N)
+                                ? *reinterpret_cast<const uint4*>(a.w16 + (int64_t)k * N + n)
+                                : make_uint4(0u, 0u, 0u, 0u);
+                } else {
+                    uint32_t p[4];
+#pragma unroll
+                    for (int c = 0; c < 8; c += 2) {
+                        const int nl = cb * 16 + h * 8 + c;   // column inside the tile
+                        const uint16_t lo = (k >= 0 && n + c < N)
+                                                ? recover_weight<HT>(wk[nl * kKTile], dcol[h * 8 + c])
+                                                : (uint16_t)0;
+                        const uint16_t hi = (k >= 0 && n + c + 1 < N)
+                                                ? recover_weight<HT>(wk[(nl + 1) * kKTile],
+                                                                     dcol[h * 8 + c + 1])
+                                                : (uint16_t)0;
+                        p[c >> 1] = (uint32_t)lo | ((uint32_t)hi << 16);
+                    }
+                    wv[h] = make_uint4(p[0], p[1], p[2], p[3]);
+                }
+                const int jx = jc + xh * 16 + h * 8;
+                xv[h] = (xrow < T && jx < opad)
+                            ? *reinterpret_cast<const uint4*>(a.xo + xrow * opad + jx)
+                            : make_uint4(0u, 0u, 0u, 0u);
+            }
+        };
+        auto store_chunk = [&](int buf) {
+            int8_t* xs = sc.lds + buf * 2 * kStageHalf;
+            int8_t* ws = xs + kStageHalf;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                *reinterpret_cast<uint4*>(xs + xr * kOS + xh * 32 + h * 16) = xv[h];
+                const uint32_t w4[4] = {wv[h].x, wv[h].y, wv[h].z, wv[h].w};
+#pragma unroll
+                for (int c = 0; c < 8; ++c)
+                    *reinterpret_cast<uint16_t*>(ws + (cb * 16 + h * 8 + c) * kOS + e * 2) =
+                        (uint16_t)(w4[c >> 1] >> ((c & 1) * 16));
+            }
+        };
+        if (sc.pre_loaded && !recover) {
+            // chunk 0 was loaded before the dequantization
+            k_next = kOC + e < o ? (by_pos ? kOC + e : a.idx[kOC + e]) : -1;
+            wv[0] = sc.pre_w[0]; wv[1] = sc.pre_w[1];
+            xv[0] = sc.pre_x[0]; xv[1] = sc.pre_x[1];
+        } else {
+            load_chunk(0);
+        }
+        // fragments: lane reads row (column) lane % 16 of its strip, outlier
+        // slots 8 (lane / 16) .. +7 of the chunk
+        const int ko = (lane >> 4) * 16;
+        for (int jc = 0; jc < opad; jc += kOC) {
+            const int buf = (jc / kOC) & 1;
+            store_chunk(buf);
+            __syncthreads();
+            if (jc + kOC < opad) load_chunk(jc + kOC);
+            const int8_t* xs = sc.lds + buf * 2 * kStageHalf;
+            const int8_t* ws = xs + kStageHalf;
+            v8u16 wb[TN];
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                wb[j] = *reinterpret_cast<const v8u16*>(ws + (wn0 + j * 16 + col_l) * kOS + ko);
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const v8u16 xa = *reinterpret_cast<const v8u16*>(xs + (wm0 + i * 16 + col_l) * kOS + ko);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    if constexpr (HT == kHalfBF16)
+                        y[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(v8bf, xa), __builtin_bit_cast(v8bf, wb[j]), y[i][j], 0, 0, 0);
+                    else
+                        y[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            __builtin_bit_cast(v8h, xa), __builtin_bit_cast(v8h, wb[j]), y[i][j], 0, 0, 0);
+                }
+            }
+        }
+    }
+    // Y through LDS, then out as whole 16-byte pieces of rows (1 KB per wave
+    // store instruction).  The tile is kept in LDS as groups of 4 rows with
+    // each column's 4 values contiguous, so a lane writes the 4 rows of one
+    // column it holds as one 8-byte write (16 lanes: 128 contiguous bytes of
+    // one group, the next 16 lanes the next group half a bank period away).
+    // The store phase reads, per thread, 8 columns of a group (64 contiguous
+    // bytes) and regroups the 16-bit values into the group's 4 row pieces
+    // with byte permutes.
+    __syncthreads();   // every LDS read of the main loop and the outlier stage is done
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int grp = (wm0 + i * 16 + row_l) >> 2;
+            const int nl = wn0 + j * 16 + col_l;
+            const uint32_t lo = (uint32_t)f32_to_h16<HT>(y[i][j][0]) | ((uint32_t)f32_to_h16<HT>(y[i][j][1]) << 16);
+            const uint32_t hi = (uint32_t)f32_to_h16<HT>(y[i][j][2]) | ((uint32_t)f32_to_h16<HT>(y[i][j][3]) << 16);
+            *reinterpret_cast<uint2*>(sc.lds + grp * kYG + nl * 8) = make_uint2(lo, hi);
+        }
+    __syncthreads();
+    const int c = sc.tid & 31;           // columns 8 c .. 8 c + 7 of the tile
+    const int64_t n = sc.n0 + c * 8;     // N % 8 == 0: a piece is all in or all out
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int grp = (sc.tid >> 5) + 16 * q;
+        const uint4* src = reinterpret_cast<const uint4*>(sc.lds + grp * kYG + c * 64);
+        // d[4 j2 + r/2 ...]: column pairs; d[2 j] = rows 0, 1 of column j;
+        // d[2 j + 1] = rows 2, 3
+        uint32_t d[16];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const uint4 v = src[h];
+            d[4 * h] = v.x; d[4 * h + 1] = v.y; d[4 * h + 2] = v.z; d[4 * h + 3] = v.w;
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int64_t m = sc.m0 + grp * 4 + k;
+            uint32_t w[4];
+#pragma unroll
+            for (int j2 = 0; j2 < 4; ++j2) {
+                // columns 2 j2 and 2 j2 + 1 of row k
+                const uint32_t a0 = d[4 * j2 + (k >> 1)], a1 = d[4 * j2 + 2 + (k >> 1)];
+                w[j2] = (k & 1) ? ((a0 >> 16) | (a1 & 0xFFFF0000u)) : ((a0 & 0xFFFFu) | (a1 << 16));
+            }
+            if (m < T && n < N)
+                *reinterpret_cast<uint4*>(a.y + m * N + n) = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    }
+}
+
+// Large-tile kernel for prefill shapes: a 256x256 workgroup tile over 8
+// waves of 128 x 64 (two waves share each SIMD: while one waits to issue,
+// the other keeps the MFMA pipe busy), each a grid of 8 x 4 16x16 tiles of
+// v_mfma_i32_16x16x64_i8 (128 int32 accumulators per lane; a 64-deep
+// k-tile is one instruction deep).  The int8 products run on the 16x16x64
+// instruction rather than 32x32x32 because the part's clock is power
+// limited: back-to-back on random operands the 32x32x32 form held 1.62 GHz
+// and the 16x16x64 form 1.92 GHz for the same work per cycle.
 // Operands go from global memory straight into LDS (global_load_lds_dwordx4:
 // no VGPR staging, no LDS store instructions) through a ring of 4 buffers of
 // 32 KB (BK = 64).  A wave instruction fills 1 KB of LDS, lane l landing at
 // byte 16*l, so the swizzle is applied by choosing which global chunk each
 // lane fetches.
 //
-// With WN = 4 (8 waves, 128 int32 accumulators per lane) two waves share
-// each SIMD: while one waits to issue its copies the other keeps the MFMA
-// pipe busy.  WN = 2 (4 waves, 256 accumulators) maximizes fragment reuse
-// instead.
-//
-// Per k-tile kt (two 32-deep sub-steps with fragments F0/F1):
-//   first half:  ds_read F1 of tile kt          under the MFMAs on F0
-//   wait until tile kt+1 has landed, barrier    (tile kt is now fully read)
-//   second half: copy tile kt+4 into kt's buffer, ds_read F0 of tile kt+1,
-//                under the MFMAs on F1
-// Each half is hand-ordered so that reads come early and every MFMA is
-// preceded by at most one read and one copy.  Requires K % 64 == 0; rows past
-// T or N are clamped to the last valid row (they only feed outputs that are
-// never stored).
-template <int WN, bool WRITE_ACC, int HT>
-__global__ __launch_bounds__(128 * WN) void k_gemm_i8_big(GemmArgs a) {
+// Per k-tile a wave issues 32 MFMAs on fragment set P (the 12 fragments of
+// tile kt, read during the previous k-tile) while it reads tile kt+1 into
+// set Q and copies tile kt+4 into tile kt's buffer; the sets alternate
+// between k-tiles.  The reads and copies are spread evenly over the 32
+// MFMAs (all 8 waves reach this phase together after the barrier, and
+// issuing the 12 reads back to back queued them behind each other in the
+// LDS: 4% slower).  One barrier per k-tile, before any of that: after it
+// every wave's reads of tile kt are complete (each waited for them) and
+// every wave's copies of tile kt+1 have landed.  Requires K % 64 == 0; rows
+// past T or N are clamped to the last valid row (they only feed outputs
+// that are never stored).
+template <bool WRITE_ACC, int HT>
+__global__ __launch_bounds__(512) void k_gemm_i8_big(GemmArgs a) {
     constexpr int BM = 256, BN = 256, BK = 64, STAGES = 4;
-    constexpr int WAVES = 2 * WN, THREADS = 64 * WAVES;
-    constexpr int TM = 4, TN = BN / WN / 32;
-    constexpr int NF = TM + TN;                      // fragments per sub-step
-    constexpr int NM = TM * TN;                      // MFMAs per sub-step
+    constexpr int WAVES = 8;
+    constexpr int TM = 8, TN = 4;                    // 16x16 tiles per wave
+    constexpr int NF = TM + TN;                      // fragments per k-tile
+    constexpr int NM = TM * TN;                      // MFMAs per k-tile
     constexpr int STAGE_BYTES = (BM + BN) * BK;
     constexpr int GPW = 16 / WAVES;                  // 1 KB groups of A (and of B) per wave
     constexpr int LOADS = 2 * GPW;                   // copies per lane per tile
     static_assert(NF <= NM && LOADS <= NM, "interleave needs one MFMA per read and copy");
-    // the operand ring, reused after the main loop by the epilogue (outlier
-    // stage, then the Y tile)
     constexpr int LDS_BYTES = STAGES * STAGE_BYTES > kYBytes ? STAGES * STAGE_BYTES : kYBytes;
+    static_assert(LDS_BYTES >= kStageBytes, "outlier stage fits");
     __shared__ __attribute__((aligned(1024))) int8_t lds[LDS_BYTES];
     __shared__ __attribute__((aligned(16))) float sxs[BM];
     __shared__ int ks_first;
@@ -695,10 +735,7 @@ __global__ __launch_bounds__(128 * WN) void k_gemm_i8_big(GemmArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t T = a.T, K = a.K, N = a.N;
     const int64_t MT = ceil_div(T, BM);
-    // With the K split (ksplit = 2) the first ks_full tiles run all of K
-    // (one round of the CUs) and the rest as two halves: the grid holds the
-    // whole tiles, then the split tiles' first halves, then their second
-    // halves, so a unit never waits for another (half = -1: a whole tile).
+    // K split: whole tiles first, then the split tiles' first and second halves
     const int64_t tiles = ceil_div(T, (int64_t)BM) * ceil_div(N, (int64_t)BN);
     const int64_t full = a.ksplit == 2 ? a.ks_full : tiles;
     int half = -1;
@@ -712,17 +749,16 @@ __global__ __launch_bounds__(128 * WN) void k_gemm_i8_big(GemmArgs a) {
     const int64_t m0 = (bid % MT) * BM;
     const int64_t n0 = (bid / MT) * BN;
     const int wm0 = (wave & 1) * 128;
-    const int wn0 = (wave >> 1) * (BN / WN);
+    const int wn0 = (wave >> 1) * 64;
     // what the epilogue needs, read now (the main loop hides the latency)
     const float sx_pre = a.sx[m0 + (tid & (BM - 1)) < T ? m0 + (tid & (BM - 1)) : T - 1];
     float sw_pre[TN];
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-        const int64_t n = n0 + wn0 + j * 32 + (lane & 31);
+        const int64_t n = n0 + wn0 + j * 16 + (lane & 15);
         sw_pre[j] = n < N ? a.sw[n] : 0.0f;
     }
     const int o_pre = a.count[0], opad_pre = a.count[1];
-    // the first outlier chunk's dimensions (slot tid % 32), for the epilogue
     const int k_first = (tid & 31) < o_pre ? a.idx[tid & 31] : -1;
 
     // copy assignment: wave w fills the 1 KB groups GPW*w .. GPW*w+GPW-1 of A
@@ -754,41 +790,23 @@ __global__ __launch_bounds__(128 * WN) void k_gemm_i8_big(GemmArgs a) {
         copy_to_lds16(base, goff[u], dst);
     };
 
-    v16i acc[TM][TN];
+    v4i acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+        for (int j = 0; j < TN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
-    // fragment offsets inside a stage (identical for every stage): fragment
-    // q < TM is A tile q, q >= TM is B tile q-TM, for sub-step ss
-    int foff[2][NF];
-#pragma unroll
-    for (int ss = 0; ss < 2; ++ss) {
-        const int c = ss * 2 + (lane >> 5);
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int row = wm0 + i * 32 + (lane & 31);
-            foff[ss][i] = row * BK + ((c ^ big_swz(row)) * 16);
-        }
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int col = wn0 + j * 32 + (lane & 31);
-            foff[ss][TM + j] = BM * BK + col * BK + ((c ^ big_swz(col)) * 16);
-        }
-    }
+    // fragment q < TM: A rows wm0 + 16 q + lane % 16, q >= TM: B rows
+    // wn0 + 16 (q - TM) + lane % 16; k bytes 16 (lane / 16) .. +16 (logical
+    // chunk lane / 16).  The swizzle depends on row bits 1..3 only, i.e. on
+    // lane % 16, so fragment q is a fixed 1 KB step from the first.
+    const int l15 = lane & 15;
+    const int csw = ((lane >> 4) ^ big_swz(l15)) * 16;
+    const int fa = (wm0 + l15) * BK + csw;
+    const int fb = BM * BK + (wn0 + l15) * BK + csw;
+    auto foff = [&](int q) { return q < TM ? fa + q * 1024 : fb + (q - TM) * 1024; };
     v4i f0[NF], f1[NF];
-    auto mfma = [&](const v4i (&f)[NF], int m) {
-        const int i = m / TN, j = m % TN;
-        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f[i], f[TM + j], acc[i][j], 0, 0, 0);
-    };
 
-    // Prologue: tiles 0..3 in flight, wait for tile 0, first F0.  Past the
-    // last tile, copies re-fetch tile KT-1 into a buffer that is never read
-    // again, which keeps the loop free of branches and the wait count fixed.
-    // this unit's k-tiles KT0 .. KT-1 (K / BK is even when K is split)
     const int nkt = (int)(K / BK);
     const int KT0 = half < 0 ? 0 : half * (nkt / 2);
     const int KT = half < 0 ? nkt : KT0 + nkt / 2;
@@ -799,39 +817,45 @@ __global__ __launch_bounds__(128 * WN) void k_gemm_i8_big(GemmArgs a) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS * (STAGES - 1)));
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < NF; ++q) f0[q] = *reinterpret_cast<const v4i*>(lds + foff[0][q]);
+    for (int q = 0; q < NF; ++q) f0[q] = *reinterpret_cast<const v4i*>(lds + foff(q));
 
     int s_cur = 0;
-    for (int kt = KT0; kt < KT; ++kt) {
+    // one k-tile: MFMAs on P (tile kt), reads of tile kt+1 into Q, copies of
+    // tile kt+4 (past the last tile: tile KT-1 again, into a buffer that is
+    // never read again) into tile kt's buffer.  At the last k-tile the reads
+    // of Q fetch a buffer nobody uses.
+    auto ktile = [&](int kt, const v4i (&P)[NF], v4i (&Q)[NF]) {
         const int s_next = (s_cur + 1) & (STAGES - 1);
-        const int8_t* cur = lds + s_cur * STAGE_BYTES;
         const int8_t* nxt = lds + s_next * STAGE_BYTES;
         const int kcopy = kt + STAGES < KT ? kt + STAGES : KT - 1;
-        __builtin_amdgcn_s_waitcnt(kLgkm0);   // F0 has arrived
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            if (m < NF) f1[m] = *reinterpret_cast<const v4i*>(cur + foff[1][m]);
-            mfma(f0, m);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // tile kt+1 has landed (tiles kt+2, kt+3 may still fly) and this
-        // wave's F1 reads are complete; after the barrier nobody reads tile kt
+        // P has arrived (this wave's reads of tile kt are done) and this
+        // wave's copies of tile kt+1 have landed
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS * (STAGES - 2)) & ~0xF00);
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
-            if (m < NF) f0[m] = *reinterpret_cast<const v4i*>(nxt + foff[0][m]);
-            if (m < LOADS) copy(m, kcopy, s_cur);
-            mfma(f1, m);
+#pragma unroll
+            for (int r = 0; r < NF; ++r) {
+                const int q = r < TN ? TM + r : r - TN;   // B fragments first
+                if ((r * NM) / NF == m) Q[q] = *reinterpret_cast<const v4i*>(nxt + foff(q));
+            }
+#pragma unroll
+            for (int u = 0; u < LOADS; ++u)
+                if (u * (NM / LOADS) + 1 == m) copy(u, kcopy, s_cur);
+            const int i = m / TN, j = m % TN;
+            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(P[i], P[TM + j], acc[i][j], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
         s_cur = s_next;
+    };
+    for (int kt = KT0; kt < KT; kt += 2) {
+        ktile(kt, f0, f1);
+        if (kt + 1 < KT) ktile(kt + 1, f1, f0);
     }
-    // no LDS copy may still be in flight when the LDS is reused or the
-    // workgroup retires
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    // no LDS copy or read may still be in flight when the LDS is reused or
+    // the workgroup retires
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0) & ~0xF00);
     if (half >= 0) {
         // K split: each half publishes its int32 sums, and the half that
         // finishes second adds the other's (exact, order independent) and
@@ -845,9 +869,9 @@ __global__ __launch_bounds__(128 * WN) void k_gemm_i8_big(GemmArgs a) {
         // loads.  A half that finds the other one already done skips
         // publishing its own sums.
         uint64_t* mine = reinterpret_cast<uint64_t*>(a.ks_part) +
-                         ((tix * 2 + half) * WAVES + wave) * (TM * TN * 8 * 64);
+                         ((tix * 2 + half) * WAVES + wave) * (TM * TN * 2 * 64);
         const uint64_t* other = reinterpret_cast<const uint64_t*>(a.ks_part) +
-                                ((tix * 2 + (1 - half)) * WAVES + wave) * (TM * TN * 8 * 64);
+                                ((tix * 2 + (1 - half)) * WAVES + wave) * (TM * TN * 2 * 64);
         if (tid == 0)
             ks_first = __hip_atomic_load(&a.ks_count[tix], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
@@ -858,10 +882,10 @@ __global__ __launch_bounds__(128 * WN) void k_gemm_i8_big(GemmArgs a) {
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
 #pragma unroll
-                    for (int q = 0; q < 8; ++q) {
+                    for (int q = 0; q < 2; ++q) {
                         const uint64_t v = (uint64_t)(uint32_t)acc[i][j][2 * q] |
                                            ((uint64_t)(uint32_t)acc[i][j][2 * q + 1] << 32);
-                        __hip_atomic_store(mine + ((i * TN + j) * 8 + q) * 64 + lane, v,
+                        __hip_atomic_store(mine + ((i * TN + j) * 2 + q) * 64 + lane, v,
                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     }
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -877,19 +901,15 @@ __global__ __launch_bounds__(128 * WN) void k_gemm_i8_big(GemmArgs a) {
 #pragma unroll
             for (int j = 0; j < TN; ++j)
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const uint64_t v = __hip_atomic_load(other + ((i * TN + j) * 8 + q) * 64 + lane,
+                for (int q = 0; q < 2; ++q) {
+                    const uint64_t v = __hip_atomic_load(other + ((i * TN + j) * 2 + q) * 64 + lane,
                                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     acc[i][j][2 * q] += (int32_t)(uint32_t)v;
                     acc[i][j][2 * q + 1] += (int32_t)(uint32_t)(v >> 32);
                 }
     }
-    static_assert(THREADS == 512 && BM == 256 && BN == 256 && LDS_BYTES >= kStageBytes,
-                  "staged epilogue: 512 threads, 256 x 256 tile");
-    // The first outlier chunk's operands (as the epilogue's staging assigns
-    // them: W row of slot tid % 32 over columns 16 (tid / 32) .. +16, X
-    // columns of tile row tid / 2), loaded now so that they arrive during
-    // the dequantization; rows recovered from Wq inside the epilogue are not.
+    // the first outlier chunk's operands (as the epilogue's staging assigns
+    // them), loaded now so that they arrive during the dequantization
     StageCtx sc{lds, tid, m0, n0, sxs, sx_pre, sw_pre, o_pre, opad_pre, k_first, false, {}, {}};
     if (opad_pre > 0 && a.w16 && !(a.w16_rows > 0 && o_pre > a.w16_rows)) {
         const int e = tid & 31, cb = tid >> 5, xr = tid >> 1, xh = tid & 1;
@@ -906,7 +926,7 @@ __global__ __launch_bounds__(128 * WN) void k_gemm_i8_big(GemmArgs a) {
         }
         sc.pre_loaded = true;
     }
-    epilogue<TM, TN, WRITE_ACC, HT, true>(acc, a, m0 + wm0, n0 + wn0, lane, sc);
+    epilogue_big<WRITE_ACC, HT>(acc, a, m0 + wm0, n0 + wn0, lane, sc);
 }
 
 // XOR swizzle of the eight 16-byte chunks of a 128-byte LDS row (streaming
@@ -1032,9 +1052,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_i8_stream(GemmA
     // the copies past the last tile went to buffers no one reads; let them
     // land before the workgroup ends
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    epilogue<TM, TN, WRITE_ACC, HT, false, BN, 64 * NW>(acc, a, m0 + wm0, n0 + wn0, lane,
-                                                        StageCtx{lds, tid, m0, n0, nullptr, 0.0f, nullptr, 0, 0, -1,
-                                                                 false, {}, {}});
+    epilogue<TM, TN, WRITE_ACC, HT, BN, 64 * NW>(acc, a, m0 + wm0, n0 + wn0, lane,
+                                                 StageCtx{lds, tid, m0, n0, nullptr, 0.0f, nullptr, 0, 0, -1,
+                                                          false, {}, {}});
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int HT>
@@ -1067,7 +1087,7 @@ __global__ void k_zero_i32(int32_t* __restrict__ p, int64_t n) {
     if (i < n) p[i] = 0;
 }
 
-template <int WN, int HT>
+template <int HT>
 hipError_t launch_big(const GemmArgs& a, hipStream_t stream) {
     const int64_t tiles = ceil_div(a.T, 256) * ceil_div(a.N, 256);
     GemmArgs b = a;
@@ -1087,12 +1107,10 @@ hipError_t launch_big(const GemmArgs& a, hipStream_t stream) {
         if (b.ks_full == tiles) b.ks_full = 0;
     }
     const int64_t units = b.ks_full + 2 * (tiles - b.ks_full);
-    if (a.acc_out)
-        hipLaunchKernelGGL((k_gemm_i8_big<WN, true, HT>), dim3((unsigned)units), dim3(128 * WN), 0,
-                           stream, b);
+if (a.acc_out)
+        hipLaunchKernelGGL((k_gemm_i8_big<true, HT>), dim3((unsigned)units), dim3(512), 0, stream, b);
     else
-        hipLaunchKernelGGL((k_gemm_i8_big<WN, false, HT>), dim3((unsigned)units), dim3(128 * WN), 0,
-                           stream, b);
+        hipLaunchKernelGGL((k_gemm_i8_big<false, HT>), dim3((unsigned)units), dim3(512), 0, stream, b);
     return hipGetLastError();
 }
 
@@ -1117,7 +1135,7 @@ hipError_t launch_gemm_typed(const GemmArgs& a, hipStream_t stream) {
     if (a.T > 128 && a.T <= 256 && a.K % 128 == 0 && ceil_div(a.N, 128) <= device_cus() &&
         gemm_ksplit(a.T, a.K, a.N) == 1)
         return launch_stream<256, 128, 4, 1, 3, HT>(a, stream);
-    if (a.T > 128 && a.K % 64 == 0) return launch_big<4, HT>(a, stream);
+    if (a.T > 128 && a.K % 64 == 0) return launch_big<HT>(a, stream);
     if (a.K % 128 == 0) {
         if (a.T <= 64) return launch_stream<64, 64, 2, 2, 4, HT>(a, stream);
         return launch_stream<128, 128, 2, 2, 4, HT>(a, stream);
