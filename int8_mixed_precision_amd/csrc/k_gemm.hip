@@ -455,14 +455,15 @@ __device__ __forceinline__ void copy_to_lds16(const void* gbase, uint32_t goff, 
 // are outstanding (expcnt and lgkmcnt left at their no-wait maxima).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0xF70; }
 
-// XOR swizzle of the four 16-byte chunks of a 64-byte LDS row.  A fragment
-// read has lanes 16 c .. 16 c + 15 on 16 consecutive rows at logical chunk
-// c; with this swizzle any 8 consecutive rows land on 8 distinct 16-byte
-// slots of a 128-byte window and any 16 consecutive rows (rows 16 g ..) on
-// 16 distinct slots of a 256-byte window, so the read is free of bank
-// conflicts whether the LDS serves 8 or 16 lanes of a ds_read_b128 per
-// cycle.
-__device__ __forceinline__ int big_swz(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
+// XOR swizzle of the four 16-byte chunks of a 64-byte LDS row (physical
+// chunk = logical chunk ^ big_swz(row)).  A fragment read has lane l on row
+// 16 g + l % 16 at logical chunk l / 16.  Chosen by measurement (a probe
+// timing ds_read_b128 of this fragment pattern, 16 waves per CU): with
+// (row / 2) % 4 the read runs at the rate of a contiguous 1 KB read; with
+// (row / 4) % 4, row % 4, no swizzle, or ((row / 2) % 4) ^ ((row / 8) % 2)
+// (conflict-free for 32 consecutive rows at one chunk) it takes 1.6-1.8
+// times as long.
+__device__ __forceinline__ int big_swz(int row) { return (row >> 1) & 3; }
 
 // Epilogue of the large-tile kernel for one wave's 8 x 4 grid of 16x16
 // accumulator tiles (128 rows x 64 columns, top-left element (mb, nb)).
@@ -798,7 +799,7 @@ __global__ __launch_bounds__(512) void k_gemm_i8_big(GemmArgs a) {
 
     // fragment q < TM: A rows wm0 + 16 q + lane % 16, q >= TM: B rows
     // wn0 + 16 (q - TM) + lane % 16; k bytes 16 (lane / 16) .. +16 (logical
-    // chunk lane / 16).  The swizzle depends on row bits 1..3 only, i.e. on
+    // chunk lane / 16).  The swizzle depends on row bits 1..2 only, i.e. on
     // lane % 16, so fragment q is a fixed 1 KB step from the first.
     const int l15 = lane & 15;
     const int csw = ((lane >> 4) ^ big_swz(l15)) * 16;
