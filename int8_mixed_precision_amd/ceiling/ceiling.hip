@@ -3,9 +3,13 @@
 // of the LLM.int8() library: bench.py loads this separately built library
 // (libceiling.so) only to time these two kernels.
 //
-//   k_mfma_i8:   back-to-back v_mfma_i32_32x32x32_i8 on independent
-//                accumulators, no memory traffic: the int8 MFMA rate the
-//                part sustains when nothing else draws power;
+//   k_mfma_i8:   back-to-back int8 MFMAs (v_mfma_i32_32x32x32_i8 or
+//                v_mfma_i32_16x16x64_i8) on independent accumulators, with
+//                pseudo-random operands that change from one instruction to
+//                the next and no memory traffic: the int8 MFMA rate the
+//                part sustains on matmul-like data when nothing else draws
+//                power (the part is power limited, so the rate depends on
+//                the instruction and on how many operand bits toggle);
 //   k_stream:    coalesced 16-byte-per-lane reads of a large buffer with
 //                16 or 32 loads in flight per lane, in a few orders and
 //                launch shapes: the HBM read rate a plain stream reaches.
@@ -20,27 +24,61 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 
 namespace {
 
-constexpr int kAcc = 8;   // independent 32x32 accumulators per wave
+constexpr int kOpsPerIter = 16 * 65536;   // int8 ops per wave per loop iteration
 
-__global__ __launch_bounds__(256) void k_mfma_i8(int iters, int* sink, unsigned long long* clk) {
+__device__ __forceinline__ int mix(uint32_t x) {   // integer hash (operand bits only)
+    x ^= x >> 16; x *= 0x7feb352du; x ^= x >> 15; x *= 0x846ca68bu; x ^= x >> 16;
+    return (int)x;
+}
+
+// FORM 0: 8 accumulators of 32x32x32, 16 instructions per iteration; FORM 1:
+// 32 accumulators of 16x16x64, 32 instructions per iteration (the same ops).
+// Four A and four B operand registers per lane, combined differently by
+// consecutive instructions.
+template <int FORM>
+__global__ __launch_bounds__(512) void k_mfma_i8(int iters, int* sink, unsigned long long* clk) {
     const unsigned long long t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
-    const int lane = threadIdx.x & 63;
-    v4i a = {lane, lane + 1, lane + 2, lane + 3};
-    v4i b = {lane * 3, lane ^ 5, lane + 7, 11};
-    v16i acc[kAcc];
+    const uint32_t l = threadIdx.x + 977u * blockIdx.x;
+    v4i a[4], b[4];
 #pragma unroll
-    for (int i = 0; i < kAcc; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][r] = 0;
-    for (int it = 0; it < iters; ++it) {
-#pragma unroll
-        for (int i = 0; i < kAcc; ++i) acc[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc[i], 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+        a[i] = v4i{mix(l * 16 + i * 4), mix(l * 16 + i * 4 + 1), mix(l * 16 + i * 4 + 2), mix(l * 16 + i * 4 + 3)};
+        b[i] = v4i{mix(~l * 16 + i * 4), mix(~l * 16 + i * 4 + 1), mix(~l * 16 + i * 4 + 2),
+                   mix(~l * 16 + i * 4 + 3)};
     }
     int s = 0;
+    if constexpr (FORM == 0) {
+        v16i acc[8];
 #pragma unroll
-    for (int i = 0; i < kAcc; ++i)
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s += acc[i][r];
+            for (int r = 0; r < 16; ++r) acc[i][r] = 0;
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                acc[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i & 3], b[(i >> 1) & 3], acc[i], 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                acc[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[(i + 1) & 3], b[((i >> 1) ^ 1) & 3], acc[i], 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s += acc[i][r];
+    } else {
+        v4i acc[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) acc[i] = v4i{0, 0, 0, 0};
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int i = 0; i < 32; ++i)
+                acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i & 3], b[i >> 3], acc[i], 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s += acc[i][r];
+    }
     if (s == 0x7fffffff) sink[0] = s;   // keeps the work
     if (threadIdx.x == 0) {
         clk[2 * blockIdx.x] = __builtin_amdgcn_s_memtime() - t0;
@@ -83,14 +121,22 @@ __global__ __launch_bounds__(B) void k_stream(const uint4* __restrict__ p, int64
 
 }  // namespace
 
-// int8 ops of one k_mfma_i8 launch: grid * 4 waves * iters * kAcc * 65536.
-extern "C" int ceiling_mfma_i8(int grid, int iters, void* sink, void* clk, void* stream) {
-    hipLaunchKernelGGL(k_mfma_i8, dim3(grid), dim3(256), 0, (hipStream_t)stream, iters,
-                       (int*)sink, (unsigned long long*)clk);
+// int8 ops of one k_mfma_i8 launch: grid * 8 waves * iters * ceiling_mfma_ops_per_iter().
+// form 0: v_mfma_i32_32x32x32_i8, form 1: v_mfma_i32_16x16x64_i8; returns 2
+// for an unknown form.
+extern "C" int ceiling_mfma_i8(int form, int grid, int iters, void* sink, void* clk, void* stream) {
+    if (form == 0)
+        hipLaunchKernelGGL(k_mfma_i8<0>, dim3(grid), dim3(512), 0, (hipStream_t)stream, iters,
+                           (int*)sink, (unsigned long long*)clk);
+    else if (form == 1)
+        hipLaunchKernelGGL(k_mfma_i8<1>, dim3(grid), dim3(512), 0, (hipStream_t)stream, iters,
+                           (int*)sink, (unsigned long long*)clk);
+    else
+        return 2;
     return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
-extern "C" int ceiling_mfma_acc(void) { return kAcc; }
+extern "C" int ceiling_mfma_ops_per_iter(void) { return kOpsPerIter; }
 
 // Stream variants: 0 = grid-stride, 16 loads, 256 lanes; 1 = grid-stride,
 // 32 loads, 256 lanes; 2 = partitioned, 16 loads, 512 lanes; 3 =
