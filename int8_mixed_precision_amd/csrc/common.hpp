@@ -184,8 +184,13 @@ hipError_t launch_recover_rows(const int8_t* Wq, const float* sw, const int32_t*
                                uint16_t* out, int64_t rows, hipStream_t stream);
 
 // ---- activation side (k_activation.hip)
+// zero, nzero: int32 words the pass also sets to zero (the matmul's K-split
+// tile counters, so the matmul of the same call needs no launch for them);
+// only with more than 128 rows, where the column detection runs
+// (hipErrorInvalidValue otherwise).
 hipError_t launch_activation_pass(const uint16_t* X, int ht, int64_t T, int64_t K, float tau,
-                                  const Workspace& ws, hipStream_t stream);
+                                  const Workspace& ws, hipStream_t stream,
+                                  int32_t* zero = nullptr, int64_t nzero = 0);
 
 // ---- weight side (k_weight.hip)
 // weight checkpoint types (the values of INT8MM_WEIGHT_* in include/int8mm.h)
@@ -209,9 +214,10 @@ struct GemmArgs {
     int32_t* acc_out;      // [T,N] or NULL
     int64_t T, K, N;
     int ksplit;            // 1, or 2: K split in two halves (large-tile kernel only)
-    int32_t* ks_count;     // [tiles] (ksplit = 2; zeroed by launch_gemm)
+    int32_t* ks_count;     // [tiles] (ksplit = 2; zero at launch_gemm or zeroed by it)
     int32_t* ks_part;      // [tiles][2][65536] (ksplit = 2)
     int64_t ks_full;       // ksplit = 2: tiles that run all of K (set by launch_gemm)
+    int ks_zeroed;         // ksplit = 2: ks_count already zero (else launch_gemm zeroes it)
 };
 hipError_t launch_gemm(const GemmArgs& a, int ht, hipStream_t stream);
 

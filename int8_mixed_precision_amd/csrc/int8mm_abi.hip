@@ -53,10 +53,11 @@ Workspace layout_for(void* base, int64_t T, int64_t K, int64_t N, size_t workspa
 // through the decode kernel's precomputed mode (with K slabs when Xq is long
 // and the workspace has their region); otherwise the GEMM runs, and without
 // W16 (memory-halved variant) the outlier rows are first recovered into the
-// workspace when it has room.
+// workspace when it has room.  ks_zeroed: the K-split tile counters were set
+// to zero by this call's activation pass.
 int run_prepared(const Workspace& ws, int ht, int64_t T, int64_t K, const int8_t* Wq,
                  const float* sw, const uint16_t* w16, int64_t N, uint16_t* y16, int32_t* acc,
-                 hipStream_t stream) {
+                 hipStream_t stream, bool ks_zeroed = false) {
     if (decode_pre_supported(T, K, N))
         return hip_status(launch_decode_pre(ht, T, K, Wq, sw, w16, N, y16, ws, acc, stream));
     if (ws.dpart)
@@ -71,7 +72,7 @@ int run_prepared(const Workspace& ws, int ht, int64_t T, int64_t K, const int8_t
         nrows = ws.wrec_rows;
     }
     GemmArgs g{ws.xq, ws.sx, Wq, sw, ws.xo, ws.idx, ws.count, rows, nrows, y16, acc, T, K, N,
-               ws.ks_count ? 2 : 1, ws.ks_count, ws.ks_part};
+               ws.ks_count ? 2 : 1, ws.ks_count, ws.ks_part, 0, ks_zeroed ? 1 : 0};
     return hip_status(launch_gemm(g, ht, stream));
 }
 
@@ -104,9 +105,12 @@ int run_matmul(const void* X, int ht, int64_t T, int64_t K, const int8_t* Wq, co
         return hip_status(launch_decode(x16, ht, T, K, Wq, sw, w16, N, tau, y16, count, idx, xq,
                                         sx, acc, stream));
     Workspace ws = layout_for(workspace, T, K, N, workspace_bytes);
-    hipError_t e = launch_activation_pass(x16, ht, T, K, tau, ws, stream);
+    // with the K split (more than 128 rows) the activation pass zeroes the
+    // matmul's tile counters, one launch fewer
+    const int64_t ntiles = ws.ks_count ? ceil_div(T, 256) * ceil_div(N, 256) : 0;
+    hipError_t e = launch_activation_pass(x16, ht, T, K, tau, ws, stream, ws.ks_count, ntiles);
     if (e != hipSuccess) return INT8MM_E_HIP;
-    const int st = run_prepared(ws, ht, T, K, Wq, sw, w16, N, y16, acc, stream);
+    const int st = run_prepared(ws, ht, T, K, Wq, sw, w16, N, y16, acc, stream, ntiles > 0);
     if (st) return st;
     return hip_status(launch_debug_copies(ws, T, K, count, idx, xq, sx, stream));
 }

@@ -111,13 +111,16 @@ template <int HT, int CB>
 __global__ __launch_bounds__(kColWaves * kWave) void k_detect_cols(const uint16_t* __restrict__ X,
                                                                    int64_t T, int64_t K, float tau,
                                                                    uint32_t* __restrict__ flags,
-                                                                   int64_t kwp) {
+                                                                   int64_t kwp, int32_t* __restrict__ zero,
+                                                                   int64_t nzero) {
     constexpr int LPR = CB / 8;                        // lanes per row
     constexpr int RPL = kWave / LPR;                   // rows per wave load
     constexpr int RPP = RPL * kColWaves * kColLoads;   // rows per pass
     static_assert(CB % 32 == 0 && kWave % LPR == 0, "whole bitmap words, whole rows per wave");
     __shared__ uint32_t wfm[kColWaves][LPR];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid >> 6;
+    if (blockIdx.x == 0 && blockIdx.y == 0)
+        for (int64_t i = tid; i < nzero; i += kColWaves * kWave) zero[i] = 0;
     const int cg = lane % LPR;                         // 8-column group of the lane
     const int64_t c0 = (int64_t)blockIdx.x * CB + cg * 8;
     const bool in = c0 < K;
@@ -873,7 +876,7 @@ void launch_rowquant_regs(const uint16_t* xb, int64_t T, int64_t K, int nparts, 
 
 template <int HT>
 static void launch_activation_typed(const uint16_t* xb, int64_t T, int64_t K, float tau,
-                             const Workspace& ws, hipStream_t stream) {
+                             const Workspace& ws, hipStream_t stream, int32_t* zero, int64_t nzero) {
     if (T <= kSmallT) {
         const dim3 grid((unsigned)ceil_div(K, kSegCols));
         if (T <= 1) launch_seg<HT, 1>(xb, T, K, tau, ws, stream);
@@ -895,15 +898,16 @@ static void launch_activation_typed(const uint16_t* xb, int64_t T, int64_t K, fl
         const int groups = (int)std::min<int64_t>(kDetectGroups, ceil_div(T, kColRowsPerPass));
         if (K > 16384)
             hipLaunchKernelGGL((k_detect_cols<HT, kColBlockLong>), dim3((unsigned)ceil_div(K, kColBlockLong), (unsigned)groups),
-                               dim3(kColWaves * kWave), 0, stream, xb, T, K, tau, ws.flags, kwp);
+                               dim3(kColWaves * kWave), 0, stream, xb, T, K, tau, ws.flags, kwp, zero, nzero);
         else
             hipLaunchKernelGGL((k_detect_cols<HT, kColBlockShort>), dim3((unsigned)ceil_div(K, kColBlockShort), (unsigned)groups),
-                               dim3(kColWaves * kWave), 0, stream, xb, T, K, tau, ws.flags, kwp);
+                               dim3(kColWaves * kWave), 0, stream, xb, T, K, tau, ws.flags, kwp, zero, nzero);
         launch_rowquant_regs<HT>(xb, T, K, groups, kwp, ws, stream);
         return;
     } else {
         hipLaunchKernelGGL((k_detect_cols<HT, kColBlockLong>), dim3((unsigned)ceil_div(K, kColBlockLong), 1u),
-                           dim3(kColWaves * kWave), 0, stream, xb, T, K, tau, ws.flags, (int64_t)0);
+                           dim3(kColWaves * kWave), 0, stream, xb, T, K, tau, ws.flags, (int64_t)0, zero,
+                           nzero);
     }
     // rows held in registers: the quantize kernel isolates the outliers too
     if (K <= (int64_t)kRowThreads * 4 * 8) {
@@ -921,9 +925,12 @@ static void launch_activation_typed(const uint16_t* xb, int64_t T, int64_t K, fl
 }
 
 hipError_t launch_activation_pass(const uint16_t* X, int ht, int64_t T, int64_t K, float tau,
-                                  const Workspace& ws, hipStream_t stream) {
-    if (ht == kHalfBF16) launch_activation_typed<kHalfBF16>(X, T, K, tau, ws, stream);
-    else launch_activation_typed<kHalfF16>(X, T, K, tau, ws, stream);
+                                  const Workspace& ws, hipStream_t stream, int32_t* zero,
+                                  int64_t nzero) {
+    // only the column detection (more than kOwnedMaxT rows) zeroes words
+    if (nzero > 0 && (!zero || T <= kOwnedMaxT)) return hipErrorInvalidValue;
+    if (ht == kHalfBF16) launch_activation_typed<kHalfBF16>(X, T, K, tau, ws, stream, zero, nzero);
+    else launch_activation_typed<kHalfF16>(X, T, K, tau, ws, stream, zero, nzero);
     return hipGetLastError();
 }
 

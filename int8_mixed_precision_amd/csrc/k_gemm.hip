@@ -1094,11 +1094,12 @@ hipError_t launch_big(const GemmArgs& a, hipStream_t stream) {
     GemmArgs b = a;
     b.ks_full = tiles;
     if (a.ksplit == 2) {
-        // the tile counters start at zero (a kernel rather than a memset, so
-        // the call can be captured in a graph); a split matmul is long enough
-        // that one more launch does not show
-        hipLaunchKernelGGL(k_zero_i32, dim3((unsigned)ceil_div(tiles, 256)), dim3(256), 0, stream,
-                           a.ks_count, tiles);
+        // the tile counters start at zero: set by the activation pass of the
+        // same call, or here (a kernel rather than a memset, so the call can
+        // be captured in a graph)
+        if (!a.ks_zeroed)
+            hipLaunchKernelGGL(k_zero_i32, dim3((unsigned)ceil_div(tiles, 256)), dim3(256), 0, stream,
+                               a.ks_count, tiles);
         // whole tiles fill whole rounds of the CUs; only the rest is split
         // (T=2048, N=12288: 384 tiles on 256 CUs run as 256 whole tiles and
         // 128 split ones, 1.5 tile times either way, a third of the partial
