@@ -631,6 +631,227 @@ __global__ __launch_bounds__(NW * kWave) void k_rowquant_regs(
     if (wr == 0 && lane == 0) sx[t] = mx;
 }
 
+// Rows of more than 32768 values and at most kStreamMaxT rows go to
+// k_rowquant_stream below.  Activation pass (detection + quantization),
+// against k_rowquant_regs<16, 8, 12>, one run: K=49152 with T=2048 and 625
+// outlier dims (Laplace rows) 123.1 -> 98.0 us, 9 dims 96.2 -> 84.5 us;
+// T=1024, K=40016 48.5 -> 41.0 us; T=700 46.2 -> 36.0 us; T=129 15.5 ->
+// 14.0 us; T=300, K=36864 19.4 -> 20.3 us; T=4096: 625 dims 264.2 ->
+// 235.7 us, 256 dims 253.8 -> 229.7 us but 8 dims 215.2 -> 228.6 us, so
+// the larger T keep the two-row kernel.
+constexpr int64_t kStreamMaxT = 2048;
+
+// Row quantization for long rows (K > 32768) by persistent workgroups of WR
+// waves that hold one row at a time in registers (CH 16-byte chunks per
+// lane, chunk c = 64 (i WR + w) + lane for wave w) and take rows
+// blockIdx.x, blockIdx.x + G, ... (G = gridDim.x): as soon as a chunk is
+// quantized and stored, its registers are loaded with the same chunk of the
+// workgroup's next row, so that row's loads fly while the current one is
+// quantized and stored.  (k_rowquant_regs, two rows per workgroup and every
+// load issued at once, ran its rounds of workgroups as loads, then
+// arithmetic, then stores.)  Per row as k_rowquant_regs: row maximum over
+// the non-outlier columns on the 16-bit patterns by packed unsigned max,
+// quantization by the magic add, outlier halves zeroed by a byte mask and
+// gathered into xo.
+template <int HT, int WR, int CH>
+__global__ __launch_bounds__(WR * kWave, 4) void k_rowquant_stream(
+    const uint16_t* __restrict__ X, int64_t T, int64_t K, const uint32_t* __restrict__ parts,
+    int nparts, int64_t kwp, int32_t* __restrict__ idx, int32_t* __restrict__ count,
+    int8_t* __restrict__ xq, float* __restrict__ sx, uint16_t* __restrict__ xo) {
+    constexpr int NT = WR * kWave;
+    constexpr int KW = WR * CH * 64 * 8 / 32;          // bitmap words of the longest row
+    constexpr int WPT = (KW + NT - 1) / NT;
+    __shared__ uint32_t fl[KW];
+    __shared__ int pf[KW];
+    __shared__ int wtot[WR];
+    __shared__ float wmx[2][WR];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int wr = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nch = (int)(K / 8);
+    const int kw = (int)((K + 31) / 32);
+    const int64_t G = gridDim.x;
+    // row of this workgroup in round j (rows G j .. G j + G - 1): with G a
+    // multiple of 16, rows 2k and 2k+1 - the two 64-byte halves of each
+    // 128-byte line of Xq - go to workgroups b and b + 8, which the
+    // round-robin dispatch puts on the same XCD (one L2)
+    const int64_t b = blockIdx.x;
+    auto row_of = [&](int64_t j) -> int64_t {
+        if (G % 16 == 0) return G * j + 2 * ((b >> 4) * 8 + (b & 7)) + ((b >> 3) & 1);
+        return G * j + b;
+    };
+
+    // (a row pointer in scalar registers plus a 32-bit byte offset per load)
+    auto load_row = [&](uint4 (&v)[CH], int64_t t) {
+        const char* row = reinterpret_cast<const char*>(X + t * K);
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int c = (i * WR + wr) * kWave + lane;
+            v[i] = *reinterpret_cast<const uint4*>(row + (uint32_t)(c < nch ? c : 0) * 16u);
+        }
+    };
+
+    // partial bitmaps, then the first row
+    uint32_t fr[WPT][kDetectGroups];
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) {
+        const int w = tid + NT * j;
+#pragma unroll
+        for (int r = 0; r < kDetectGroups; ++r)
+            fr[j][r] = (w < kw && r < nparts) ? parts[(int64_t)r * kwp + w] : 0u;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    int64_t t = row_of(0);   // the grid has at most T workgroups, so t < T
+    uint4 v[CH];
+    load_row(v, t);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) {
+        const int w = tid + NT * j;
+        uint32_t f = 0;
+#pragma unroll
+        for (int r = 0; r < kDetectGroups; ++r) f |= fr[j][r];
+        if (w < kw) fl[w] = f;
+    }
+    __syncthreads();   // fl
+    int o = 0;
+    {
+        int cnt = 0;
+#pragma unroll
+        for (int i = 0; i < WPT; ++i) {
+            const int w = WPT * tid + i;
+            if (w < kw) cnt += __builtin_popcount(fl[w]);
+        }
+        int run = block_excl_scan<NT>(cnt, wtot, o);
+#pragma unroll
+        for (int i = 0; i < WPT; ++i) {
+            const int w = WPT * tid + i;
+            if (w < kw) {
+                pf[w] = run;
+                uint32_t f = fl[w];
+                if (blockIdx.x == 0) {
+                    int p = run;
+                    while (f) {
+                        idx[p++] = w * 32 + __builtin_ctz(f);
+                        f &= f - 1u;
+                    }
+                }
+                run += __builtin_popcount(fl[w]);
+            }
+        }
+    }
+    const int opad = (o + 15) & ~15;
+    if (blockIdx.x == 0 && tid == 0) {
+        count[0] = o;
+        count[1] = opad;
+    }
+    __syncthreads();   // pf
+    const bool whole_tiles = K % kKTile == 0;
+
+    // one row: maximum, scale, quantize, store (slot: which wmx half); each
+    // chunk's registers then take the next row's chunk (tn < 0: none)
+    auto process = [&](int64_t tr, int slot, int64_t tn) {
+        // the lane index through an empty asm: every per-chunk value is
+        // recomputed for each row instead of twelve of each being hoisted
+        // out of the row loop into registers
+        int lane = threadIdx.x & (kWave - 1);
+        asm volatile("" : "+v"(lane));
+        const char* nrow = reinterpret_cast<const char*>(X + (tn >= 0 ? tn : 0) * K);
+        // the row has arrived (one wait outside the per-chunk branches, so
+        // the compiler knows no load into v is pending in the quantize loop
+        // but the next row's, and adds no wait before each chunk there)
+        __builtin_amdgcn_s_waitcnt(0xF70);   // vmcnt(0), expcnt and lgkmcnt not waited
+        uint32_t m0 = 0u, m1 = 0u;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int c = (i * WR + wr) * kWave + lane;
+            if (c < nch) {
+                const uint32_t fm = (fl[c >> 2] >> ((c & 3) * 8)) & 0xFFu;
+                const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+                uint32_t keep[4] = {0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu, 0x7FFF7FFFu};
+                if (fm) {
+#pragma unroll
+                    for (int d = 0; d < 4; ++d)
+                        keep[d] = (((fm >> (2 * d)) & 1u) ? 0u : 0x00007FFFu) |
+                                  (((fm >> (2 * d + 1)) & 1u) ? 0u : 0x7FFF0000u);
+                }
+                m0 = pk_max_u16(m0, pk_max_u16(w[0] & keep[0], w[1] & keep[1]));
+                m1 = pk_max_u16(m1, pk_max_u16(w[2] & keep[2], w[3] & keep[3]));
+            }
+        }
+        const uint32_t m = pk_max_u16(m0, m1);
+        const uint32_t mh = (m & 0xFFFFu) > (m >> 16) ? (m & 0xFFFFu) : (m >> 16);
+        float mx = wave_max(h16_to_f32<HT>((uint16_t)mh));
+        if (lane == 0) wmx[slot][wr] = mx;
+        __syncthreads();   // the waves' maxima of this row (the other slot is the next row's)
+        mx = wmx[slot][0];
+#pragma unroll
+        for (int q = 1; q < WR; ++q) mx = __builtin_fmaxf(mx, wmx[slot][q]);
+        const float qk = HT == kHalfF16 ? 1.0f : qfactor(mx);   // fp16 scales are >= 2^-24
+        const float rr = mx > 0.0f ? 127.0f / (mx * qk) : 0.0f;   // IEEE fp32 divide
+        uint16_t* xo_row = xo + tr * opad;
+        const int64_t p0 = tr - tr % kPanel;
+        const int64_t prow = T - p0 < kPanel ? T - p0 : kPanel;
+        const int64_t qstep = 8 * WR * kKTile * prow;
+        const int64_t q0 = p0 * K + (tr - p0) * kKTile + 8 * (lane & 7) +
+                           (int64_t)(8 * wr + (lane >> 3)) * kKTile * prow;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int c = (i * WR + wr) * kWave + lane;
+            if (c >= nch) continue;
+            const uint32_t word = fl[c >> 2];
+            const uint32_t fm = (word >> ((c & 3) * 8)) & 0xFFu;
+            const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+            uint32_t f[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = h16_to_f32<HT>((uint16_t)(w[e >> 1] >> ((e & 1) * 16)));
+                const float p = __builtin_fmaf(x * qk, rr, 0.0f);
+                f[e] = __builtin_bit_cast(uint32_t, __fadd_rn(p, 12582912.0f));
+            }
+            uint32_t packed[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t lo = __builtin_amdgcn_perm(f[4 * h + 1], f[4 * h], 0x0c0c0400u);
+                const uint32_t hi = __builtin_amdgcn_perm(f[4 * h + 3], f[4 * h + 2], 0x0c0c0400u);
+                packed[h] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+            }
+            if (fm) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    uint32_t keep = 0u;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        keep |= ((fm >> (4 * h + e)) & 1u) ? 0u : (0xFFu << (8 * e));
+                    packed[h] &= keep;
+                }
+                const int base_bit = (c & 3) * 8;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    if ((fm >> e) & 1u) {
+                        const int bit = base_bit + e;
+                        const int pos = pf[c >> 2] + __builtin_popcount(word & ((1u << bit) - 1u));
+                        xo_row[pos] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
+                    }
+                }
+            }
+            const int64_t qo = whole_tiles ? q0 + i * qstep : blk_offset(tr, (int64_t)c * 8, T, K);
+            *reinterpret_cast<uint2*>(xq + qo) = make_uint2(packed[0], packed[1]);
+            if (tn >= 0) v[i] = *reinterpret_cast<const uint4*>(nrow + (uint32_t)c * 16u);
+            // keep each reload after its chunk's use (no second register set)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        for (int j = o + tid; j < opad; j += NT) xo_row[j] = 0;   // +0 in both types
+        if (tid == 0) sx[tr] = mx;
+    };
+
+    for (int64_t j = 1;; ++j) {
+        const int64_t tn = row_of(j) < T ? row_of(j) : -1;   // uniform
+        process(t, (int)(j & 1), tn);
+        if (tn < 0) break;
+        t = tn;
+    }
+}
+
 // ---- activation pass for T <= kSmallT rows, two kernels over column
 // segments.  A workgroup of 256 lanes owns kSegCols = 2048 columns, a lane 8
 // of them in every row, so a column's outlier flag is the OR over the lane's
@@ -869,7 +1090,14 @@ void launch_rowquant_regs(const uint16_t* xb, int64_t T, int64_t K, int nparts, 
     else if (K <= 16384) go(k_rowquant_regs<HT, 8, 8, 4>, 8, 8);
     else if (K <= 24576) go(k_rowquant_regs<HT, 8, 8, 6>, 8, 8);
     else if (K <= 32768) go(k_rowquant_regs<HT, 4, 4, 16>, 4, 4);
-    else go(k_rowquant_regs<HT, 16, 8, 12>, 16, 8);
+    else if (T <= kStreamMaxT) {
+        // persistent, two workgroups of 8 waves per CU
+        const int64_t g = std::min<int64_t>(T, 2 * (int64_t)device_cus());
+        hipLaunchKernelGGL((k_rowquant_stream<HT, 8, 12>), dim3((unsigned)g), dim3(8 * kWave), 0, stream, xb, T, K,
+                           ws.flags, nparts, kwp, ws.idx, ws.count, ws.xq, ws.sx, ws.xo);
+    } else {
+        go(k_rowquant_regs<HT, 16, 8, 12>, 16, 8);
+    }
 }
 
 }  // namespace

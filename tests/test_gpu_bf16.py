@@ -95,6 +95,7 @@ def run_bf16(mm, name, X16, W16, tau, halved=False, big=None, rows=None):
 @pytest.mark.parametrize("T,K,N,nd,tau,halved", [
     (37, 80, 200, 2, 6.0, False), (300, 1040, 520, 3, 6.0, False),       # staged kernels
     (1400, 24576, 8, 5, 6.0, False),                                      # long rows past 128 rows
+    (600, 40960, 8, 9, 6.0, False),                                       # persistent long rows
     (257, 2048, 1000, 70, 6.0, False), (513, 128, 264, 2, 6.0, True),    # large-tile kernel
     (1, 4096, 1000, 3, 6.0, False), (8, 8192, 264, 300, 6.0, False),     # decode kernel
     (16, 4096, 520, 5, 6.0, True), (8, 8192, 2056, 6, 6.0, True),

@@ -192,10 +192,14 @@ def test_ragged_shapes(mm, T, K, N, nd, dist):
                                   # detection blocks of 256 columns, the last one 16 wide
     (133, 30000, 6, "normal"),    # 4 waves x 16 chunks, ragged
     (140, 32768, 9, "laplace"),   # 4 waves x 16 chunks, every word held
-    (129, 49152, 40, "laplace"),  # 8 waves x 12 chunks, 2 rows per workgroup (the last one's
-                                  # second row past T), every word held, many outliers
+    (129, 49152, 40, "laplace"),  # persistent rows of 8 waves x 12 chunks, one row per
+                                  # workgroup (grid = T), every word held, many outliers
     (131, 40016, 5, "normal"),    # the same, ragged; detection blocks of 256 columns, the last
                                   # one 80 wide
+    (1000, 40016, 9, "laplace"),  # persistent rows, 512 workgroups (rows 2k and 2k+1 paired),
+                                  # two rows per workgroup for most, ragged rows and last panel
+    (2048, 36864, 30, "normal"),  # persistent rows, four per workgroup, whole k-tiles
+    (2049, 49152, 8, "normal"),   # past the persistent kernel's row limit: 2 rows per workgroup
     (129, 49168, 7, "normal"),    # past the registers: one bitmap, separate compaction, two-pass rows
     (1100, 12288, 6, "normal"),   # three row groups in the detection
     (1100, 24576, 6, "normal"),   # 8 waves x 6 chunks, three row groups
