@@ -199,6 +199,8 @@ def test_ragged_shapes(mm, T, K, N, nd, dist):
     (1000, 40016, 9, "laplace"),  # persistent rows, 512 workgroups (rows 2k and 2k+1 paired),
                                   # two rows per workgroup for most, ragged rows and last panel
     (2048, 36864, 30, "normal"),  # persistent rows, four per workgroup, whole k-tiles
+    (256, 49152, 12, "laplace"),  # persistent rows, grid = T = 256 with the row pairing
+    (2000, 36880, 6, "normal"),   # persistent rows, a partial last round, ragged k-tiles
     (2049, 49152, 8, "normal"),   # past the persistent kernel's row limit: 2 rows per workgroup
     (129, 49168, 7, "normal"),    # past the registers: one bitmap, separate compaction, two-pass rows
     (1100, 12288, 6, "normal"),   # three row groups in the detection
