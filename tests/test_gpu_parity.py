@@ -274,6 +274,29 @@ def test_random_shapes(mm, T, K, N, nd, halved):
     run_case(mm, f"random {T}x{K}x{N}{' halved' if halved else ''}", X, W, 6.0, halved=halved)
 
 
+def _random_long_rows(n=10, seed=77, max_macs=6e8):
+    """Seeded shapes for the long-row activation kernels and the large-tile
+    matmul: 300-2600 rows, K past 16384 (multiples of 16, of 64 or of 1024),
+    narrow ragged N."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        T = int(rng.integers(300, 2600))
+        K = int(rng.choice([16 * rng.integers(1025, 3073), 64 * rng.integers(257, 769),
+                            1024 * rng.integers(17, 49)]))
+        N = int(8 * rng.integers(1, 40))
+        if T * K * N > max_macs:
+            continue
+        out.append((T, K, N, int(rng.integers(0, 40)), len(out) % 3 == 2))
+    return out
+
+
+@pytest.mark.parametrize("T,K,N,nd,halved", _random_long_rows())
+def test_random_long_rows(mm, T, K, N, nd, halved):
+    X, W = synth.random_case(51_000 + T + K + N + nd, T, K, N, n_dims=nd, x_dist="laplace")
+    run_case(mm, f"long rows {T}x{K}x{N}{' halved' if halved else ''}", X, W, 6.0, halved=halved)
+
+
 @pytest.mark.parametrize("T,K,N,nd,tau", [
     (1, 4096, 1000, 3, 6.0), (3, 4096, 8, 0, 6.0), (8, 8192, 2056, 6, 6.0),
     (16, 4096, 520, 5, 6.0), (8, 8192, 264, 300, 6.0),   # o > 256: values read from X
