@@ -61,9 +61,9 @@ __device__ __forceinline__ uint16_t f32_to_h16(float f) {
 //           Wq for the memory-halved variant, row j = outlier j (present when the
 //           workspace is large enough for it)
 // and, only when the matmul splits K in two (gemm_ksplit), after all of the above:
-//   ks_count i32 [tiles]            per output tile, halves finished (zeroed by the
-//                                   matmul's launch)
-//   ks_part  i32 [tiles][2][65536]  each half's int32 sums of its 256 x 256 tile
+//   ks_count i32 [nsplit]            per split tile, halves finished (zeroed by
+//                                    the call's activation pass or the matmul's launch)
+//   ks_part  i32 [nsplit][2][65536]  each half's int32 sums of its 256 x 256 tile
 // or, for few rows with a long K (decode_split_reserve), instead of wrec and
 // the split:
 //   dpart    i32 [dslabs][T][N]     each K slab's int32 sums
@@ -154,6 +154,12 @@ uint32_t tau_to_h16_ceil(float tau, int ht);
 // 2 when the large-tile matmul of (T, K, N) runs each 256 x 256 output tile
 // as two halves of K on the current device, else 1.
 int gemm_ksplit(int64_t T, int64_t K, int64_t N);
+// The large-tile matmul's K split on this device: the first `full` tiles run
+// all of K, the last `nsplit` as two halves (nsplit = 0: no split).
+struct KSplitPlan {
+    int64_t full, nsplit;
+};
+KSplitPlan gemm_ksplit_plan(int64_t T, int64_t K, int64_t N);
 
 // Partial outlier bitmaps the workspace holds (row groups of the detection).
 constexpr int kDetectParts = 4;
@@ -214,8 +220,8 @@ struct GemmArgs {
     int32_t* acc_out;      // [T,N] or NULL
     int64_t T, K, N;
     int ksplit;            // 1, or 2: K split in two halves (large-tile kernel only)
-    int32_t* ks_count;     // [tiles] (ksplit = 2; zero at launch_gemm or zeroed by it)
-    int32_t* ks_part;      // [tiles][2][65536] (ksplit = 2)
+    int32_t* ks_count;     // [nsplit] (ksplit = 2; zero at launch_gemm or zeroed by it)
+    int32_t* ks_part;      // [nsplit][2][65536] (ksplit = 2)
     int64_t ks_full;       // ksplit = 2: tiles that run all of K (set by launch_gemm)
     int ks_zeroed;         // ksplit = 2: ks_count already zero (else launch_gemm zeroes it)
 };

@@ -107,7 +107,7 @@ int run_matmul(const void* X, int ht, int64_t T, int64_t K, const int8_t* Wq, co
     Workspace ws = layout_for(workspace, T, K, N, workspace_bytes);
     // with the K split (more than 128 rows) the activation pass zeroes the
     // matmul's tile counters, one launch fewer
-    const int64_t ntiles = ws.ks_count ? ceil_div(T, 256) * ceil_div(N, 256) : 0;
+    const int64_t ntiles = ws.ks_count ? gemm_ksplit_plan(T, K, N).nsplit : 0;
     hipError_t e = launch_activation_pass(x16, ht, T, K, tau, ws, stream, ws.ks_count, ntiles);
     if (e != hipSuccess) return INT8MM_E_HIP;
     const int st = run_prepared(ws, ht, T, K, Wq, sw, w16, N, y16, acc, stream, ntiles > 0);

@@ -1228,10 +1228,11 @@ Workspace carve_workspace(void* base, int64_t T, int64_t K, int64_t N, bool wrec
         w.wrec = reinterpret_cast<uint16_t*>(take(sizeof(uint16_t) * (size_t)w.wrec_rows * (size_t)N));
     }
     if (wrec && ksplit == 2) {
-        // after everything else, so the layout without the split is a prefix
-        const int64_t tiles = ceil_div(T, 256) * ceil_div(N, 256);
-        w.ks_count = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)tiles));
-        w.ks_part = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)tiles * 2 * 65536));
+        // after everything else, so the layout without the split is a prefix;
+        // one counter and two halves of partial sums per split tile
+        const int64_t nsplit = gemm_ksplit_plan(T, K, N).nsplit;
+        w.ks_count = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)nsplit));
+        w.ks_part = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)nsplit * 2 * 65536));
     }
     if (dslabs > 0) {
         w.dslabs = dslabs;

@@ -737,6 +737,11 @@ __global__ __launch_bounds__(512) void k_gemm_i8_big(GemmArgs a) {
     const int64_t T = a.T, K = a.K, N = a.N;
     const int64_t MT = ceil_div(T, BM);
     // K split: whole tiles first, then the split tiles' first and second halves
+    // With the K split (ksplit = 2) the first ks_full tiles run all of K
+    // (whole rounds of the CUs) and the rest as two halves: the grid holds
+    // the whole tiles, then the split tiles' first halves, then their second
+    // halves, so a unit never waits for another (half = -1: a whole tile).
+    // Split tile si = tix - full keeps its partial sums and counter at si.
     const int64_t tiles = ceil_div(T, (int64_t)BM) * ceil_div(N, (int64_t)BN);
     const int64_t full = a.ksplit == 2 ? a.ks_full : tiles;
     int half = -1;
@@ -746,6 +751,7 @@ __global__ __launch_bounds__(512) void k_gemm_i8_big(GemmArgs a) {
         half = (int)(v / nsplit);
         tix = full + v - half * nsplit;
     }
+    const int64_t si = tix - full;   // split tile index (half >= 0)
     const int64_t bid = xcd_tile(tix, tiles);
     const int64_t m0 = (bid % MT) * BM;
     const int64_t n0 = (bid / MT) * BN;
@@ -870,11 +876,11 @@ __global__ __launch_bounds__(512) void k_gemm_i8_big(GemmArgs a) {
         // loads.  A half that finds the other one already done skips
         // publishing its own sums.
         uint64_t* mine = reinterpret_cast<uint64_t*>(a.ks_part) +
-                         ((tix * 2 + half) * WAVES + wave) * (TM * TN * 2 * 64);
+                         ((si * 2 + half) * WAVES + wave) * (TM * TN * 2 * 64);
         const uint64_t* other = reinterpret_cast<const uint64_t*>(a.ks_part) +
-                                ((tix * 2 + (1 - half)) * WAVES + wave) * (TM * TN * 2 * 64);
+                                ((si * 2 + (1 - half)) * WAVES + wave) * (TM * TN * 2 * 64);
         if (tid == 0)
-            ks_first = __hip_atomic_load(&a.ks_count[tix], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ks_first = __hip_atomic_load(&a.ks_count[si], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
         const bool other_done = ks_first != 0;
         if (!other_done) {
@@ -893,7 +899,7 @@ __global__ __launch_bounds__(512) void k_gemm_i8_big(GemmArgs a) {
         }
         __syncthreads();   // every wave's sums are out (and ks_first is read)
         if (tid == 0)
-            ks_first = __hip_atomic_fetch_add(&a.ks_count[tix], 1, __ATOMIC_ACQ_REL,
+            ks_first = __hip_atomic_fetch_add(&a.ks_count[si], 1, __ATOMIC_ACQ_REL,
                                               __HIP_MEMORY_SCOPE_AGENT) == 0;
         __syncthreads();
         if (ks_first) return;   // the other half finishes the tile
@@ -1094,22 +1100,18 @@ hipError_t launch_big(const GemmArgs& a, hipStream_t stream) {
     GemmArgs b = a;
     b.ks_full = tiles;
     if (a.ksplit == 2) {
-        // the tile counters start at zero: set by the activation pass of the
-        // same call, or here (a kernel rather than a memset, so the call can
-        // be captured in a graph)
+        const KSplitPlan p = gemm_ksplit_plan(a.T, a.K, a.N);
+        if (p.nsplit <= 0) return hipErrorInvalidValue;
+        // the split tiles' counters start at zero: set by the activation pass
+        // of the same call, or here (a kernel rather than a memset, so the
+        // call can be captured in a graph)
         if (!a.ks_zeroed)
-            hipLaunchKernelGGL(k_zero_i32, dim3((unsigned)ceil_div(tiles, 256)), dim3(256), 0, stream,
-                               a.ks_count, tiles);
-        // whole tiles fill whole rounds of the CUs; only the rest is split
-        // (T=2048, N=12288: 384 tiles on 256 CUs run as 256 whole tiles and
-        // 128 split ones, 1.5 tile times either way, a third of the partial
-        // sums of splitting all 384)
-        const int64_t cus = device_cus();
-        b.ks_full = tiles > cus ? cus * (tiles / cus) : 0;
-        if (b.ks_full == tiles) b.ks_full = 0;
+            hipLaunchKernelGGL(k_zero_i32, dim3((unsigned)ceil_div(p.nsplit, 256)), dim3(256), 0, stream,
+                               a.ks_count, p.nsplit);
+        b.ks_full = p.full;
     }
     const int64_t units = b.ks_full + 2 * (tiles - b.ks_full);
-if (a.acc_out)
+    if (a.acc_out)
         hipLaunchKernelGGL((k_gemm_i8_big<true, HT>), dim3((unsigned)units), dim3(512), 0, stream, b);
     else
         hipLaunchKernelGGL((k_gemm_i8_big<false, HT>), dim3((unsigned)units), dim3(512), 0, stream, b);
@@ -1159,14 +1161,34 @@ hipError_t launch_gemm_typed(const GemmArgs& a, hipStream_t stream) {
 // projection T=2048, K=49152, N=12288 13% faster; T=512, K=12288: N=36864
 // 344 -> 304 us, N=49152 347 -> 342 us (T=384, N=49152 1% slower).  Up to
 // 256 rows the 256x128 streaming tile takes the shapes with K below 24576.
-int gemm_ksplit(int64_t T, int64_t K, int64_t N) {
-    const int64_t kmin = T > 256 ? 8192 : 24576;
-    if (!(T > 128 && K % 128 == 0 && K >= kmin)) return 1;
+// Only the split tiles hold partial sums (workspace: 128 split tiles of the
+// down projection's 384, 32 of 288 at T=512, N=36864).  Staggering whole
+// rounds with a split half-round dispatched first (so that half the CUs
+// store their Y tiles half a tile apart from the other half) measured
+// level on the up, QKV, out and down projections.
+KSplitPlan gemm_ksplit_plan(int64_t T, int64_t K, int64_t N) {
     const int64_t tiles = ceil_div(T, 256) * ceil_div(N, 256);
     const int64_t cus = device_cus();
-    const int64_t r1 = ceil_div(tiles, cus);          // rounds of whole tiles
-    const int64_t r2 = ceil_div(2 * tiles, cus);      // rounds of half tiles
-    return 2 * r2 <= 3 * r1 ? 2 : 1;                  // half-rounds r2/2 <= 3/4 of r1
+    const KSplitPlan none{tiles, 0};
+    if (!(T > 128 && K % 128 == 0)) return none;
+    const int64_t kmin = T > 256 ? 8192 : 24576;
+    if (K >= kmin) {
+        const int64_t r1 = ceil_div(tiles, cus);          // rounds of whole tiles
+        const int64_t r2 = ceil_div(2 * tiles, cus);      // rounds of half tiles
+        if (2 * r2 <= 3 * r1) {                           // half-rounds r2/2 <= 3/4 of r1
+            // whole tiles fill whole rounds of the CUs; only the rest is split
+            // (T=2048, N=12288: 384 tiles on 256 CUs run as 256 whole tiles and
+            // 128 split ones, 1.5 tile times either way, a third of the partial
+            // sums of splitting all 384)
+            const int64_t full = tiles > cus && tiles % cus != 0 ? cus * (tiles / cus) : 0;
+            return {full, tiles - full};
+        }
+    }
+    return none;
+}
+
+int gemm_ksplit(int64_t T, int64_t K, int64_t N) {
+    return gemm_ksplit_plan(T, K, N).nsplit > 0 ? 2 : 1;
 }
 
 hipError_t launch_gemm(const GemmArgs& a, int ht, hipStream_t stream) {

@@ -51,20 +51,25 @@ def test_workspace_size(mm):
     # min(K, 512) recovered 16-bit outlier rows of N values (memory-halved
     # variant), plus alignment padding
     rec = 2 * 512 * 49152
+    # the matmul's K split adds 2 x 256 KB of partial sums and a counter per
+    # split 256 x 256 tile (without a device the size query assumes 256 CUs)
+    split = 2 * 65536 * 4 + 4
     assert 3 * 2048 * 12288 + rec <= big < 3 * 2048 * 12288 + rec + (1 << 20)
     assert 0 < small < big
     assert mm.workspace_size(16, 64, 8) < small    # fewer recovered-row columns
-    # the matmul's K split adds 2 x 256 KB of partial sums and a counter per
-    # 256 x 256 tile (384 tiles: 2 rounds on 256 CUs become 1.5; without a
-    # device the size query assumes 256 CUs)
+    # 384 tiles: 256 whole tiles and 128 split ones (2 rounds become 1.5)
     down = mm.workspace_size(2048, 49152, 12288)
-    assert down >= 3 * 2048 * 49152 + 2 * 512 * 12288 + 384 * (2 * 65536 * 4 + 4)
-    # past 256 rows from K = 8192: T=512, N=36864 gives 288 tiles (2 rounds -> 1.5)
+    base = 3 * 2048 * 49152 + 2 * 512 * 12288
+    assert base + 128 * split <= down < base + 128 * split + (1 << 20)
+    # past 256 rows from K = 8192: T=512, N=36864 gives 288 tiles, 32 split
     t512 = mm.workspace_size(512, 12288, 36864)
-    assert t512 >= 3 * 512 * 12288 + 2 * 512 * 36864 + 288 * (2 * 65536 * 4 + 4)
+    base = 3 * 512 * 12288 + 2 * 512 * 36864
+    assert base + 32 * split <= t512 < base + 32 * split + (1 << 20)
     assert mm.workspace_size(256, 12288, 36864) < 3 * 256 * 12288 + 2 * 512 * 36864 + (1 << 20)
     t4096 = mm.workspace_size(4096, 49152, 12288)                         # 3 full rounds
     assert t4096 < 3 * 4096 * 49152 + 2 * 512 * 12288 + (1 << 20)
+    # fewer than two whole rounds: no split (T=512, N=32768: 256 tiles)
+    assert mm.workspace_size(512, 12288, 32768) < 3 * 512 * 12288 + 2 * 512 * 32768 + (1 << 20)
     # decode shapes run as one kernel and need only the fixed regions
     assert mm.workspace_size(8, 8192, 28672) < 3 * 8 * 8192 + (1 << 16)
     # few rows with a long K: S = ceil(48 / 16) + 3 = 6 slabs of int32
