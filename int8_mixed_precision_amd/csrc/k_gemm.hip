@@ -706,10 +706,11 @@ __device__ __forceinline__ void epilogue_big(v4i (&acc)[8][4], const GemmArgs& a
 // Per k-tile a wave issues 32 MFMAs on fragment set P (the 12 fragments of
 // tile kt, read during the previous k-tile) while it reads tile kt+1 into
 // set Q and copies tile kt+4 into tile kt's buffer; the sets alternate
-// between k-tiles.  The reads and copies are spread evenly over the 32
-// MFMAs (all 8 waves reach this phase together after the barrier, and
-// issuing the 12 reads back to back queued them behind each other in the
-// LDS: 4% slower).  One barrier per k-tile, before any of that: after it
+// between k-tiles.  The reads are spread over the first 16 MFMAs and the
+// copies over all 32 (all 8 waves reach this phase together after the
+// barrier, and issuing the 12 reads back to back queued them behind each
+// other in the LDS: 4% slower).  One barrier per k-tile, before any of
+// that: after it
 // every wave's reads of tile kt are complete (each waited for them) and
 // every wave's copies of tile kt+1 have landed.  Requires K % 64 == 0; rows
 // past T or N are clamped to the last valid row (they only feed outputs
