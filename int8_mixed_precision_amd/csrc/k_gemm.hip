@@ -706,13 +706,12 @@ __device__ __forceinline__ void epilogue_big(v4i (&acc)[8][4], const GemmArgs& a
 // Per k-tile a wave issues 32 MFMAs on fragment set P (the 12 fragments of
 // tile kt, read during the previous k-tile) while it reads tile kt+1 into
 // set Q and copies tile kt+4 into tile kt's buffer; the sets alternate
-// between k-tiles.  The reads are spread over the first 16 MFMAs and the
-// copies over all 32 (all 8 waves reach this phase together after the
-// barrier, and issuing the 12 reads back to back queued them behind each
-// other in the LDS: 4% slower).  One barrier per k-tile, before any of
-// that: after it
-// every wave's reads of tile kt are complete (each waited for them) and
-// every wave's copies of tile kt+1 have landed.  Requires K % 64 == 0; rows
+// between k-tiles.  One barrier per k-tile, after the first 4 MFMAs: after
+// it every wave's reads of tile kt are complete (each waited for them) and
+// every wave's copies of tile kt+1 have landed.  The reads then go out over
+// 16 MFMAs and the copies over the rest (all 8 waves leave the barrier
+// together, and issuing the 12 reads back to back queued them behind each
+// other in the LDS: 4% slower).  Requires K % 64 == 0; rows
 // past T or N are clamped to the last valid row (they only feed outputs
 // that are never stored).
 template <bool WRITE_ACC, int HT>
@@ -836,29 +835,37 @@ __global__ __launch_bounds__(512) void k_gemm_i8_big(GemmArgs a) {
         const int s_next = (s_cur + 1) & (STAGES - 1);
         const int8_t* nxt = lds + s_next * STAGE_BYTES;
         const int kcopy = kt + STAGES < KT ? kt + STAGES : KT - 1;
-        // P has arrived (this wave's reads of tile kt are done) and this
-        // wave's copies of tile kt+1 have landed
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS * (STAGES - 2)) & ~0xF00);
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-        // The next tile's 12 fragment reads go out over the first half of
-        // the 32 MFMAs, so they have landed when the wave reaches the next
-        // barrier (whose wait includes them); spread over all 32 the last
-        // read left with 3 MFMAs to go.  Measured on whole calls, alternated:
-        // up-projection -0.8 to -1.2%, down -0.6%, QKV -0.7 to -1.2%; over
-        // the first 24, 20 or 12 MFMAs, or with the copies moved, level or
-        // slower.
+        // The first BPOS MFMAs need only P, which is in registers: they go
+        // out before the barrier, so the pipe has work while the waves meet
+        // (whole calls, alternated: up-projection -1.2 to -1.5%, down -0.4
+        // to -0.9%, QKV -0.4%; after 2 or 8 MFMAs within noise of 4).  At
+        // the barrier P has arrived (this wave's reads of tile kt are done:
+        // no wave reads tile kt's buffer again, which the copies below
+        // overwrite) and this wave's copies of tile kt+1 have landed.
+        // The next tile's 12 fragment reads follow over 16 MFMAs, so they
+        // have landed when the wave reaches the next barrier (whose wait
+        // includes them); spread over all 32 the last read left with 3
+        // MFMAs to go (whole calls -0.6 to -1.2%; over 24, 20 or 12 MFMAs,
+        // or with the copies moved, level or slower).  The 4 copies are
+        // spread over the rest.
+        constexpr int BPOS = 4;
         constexpr int RSPAN = NM / 2;
+        static_assert(BPOS + RSPAN <= NM && BPOS + LOADS * ((NM - BPOS) / LOADS) <= NM, "schedule");
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
+            if (m == BPOS) {
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS * (STAGES - 2)) & ~0xF00);
+                __syncthreads();
+                __builtin_amdgcn_sched_barrier(0);
+            }
 #pragma unroll
             for (int r = 0; r < NF; ++r) {
                 const int q = r < TN ? TM + r : r - TN;   // B fragments first
-                if ((r * RSPAN) / NF == m) Q[q] = *reinterpret_cast<const v4i*>(nxt + foff(q));
+                if (BPOS + (r * RSPAN) / NF == m) Q[q] = *reinterpret_cast<const v4i*>(nxt + foff(q));
             }
 #pragma unroll
             for (int u = 0; u < LOADS; ++u)
-                if (u * (NM / LOADS) + 1 == m) copy(u, kcopy, s_cur);
+                if (BPOS + u * ((NM - BPOS) / LOADS) + 1 == m) copy(u, kcopy, s_cur);
             const int i = m / TN, j = m % TN;
             acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(P[i], P[TM + j], acc[i][j], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
