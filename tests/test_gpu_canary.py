@@ -103,6 +103,7 @@ ROUTES = [
     # (label, T, K, N, outlier dims): one line per kernel route
     ("decode fused K=8192", 8, 8192, 1040, 3),
     ("decode fused T=1", 1, 4096, 520, 2),
+    ("decode fused, half last block", 8, 8192, 28680, 3),
     ("decode precomputed", 4, 12288, 520, 3),
     ("decode K slabs", 8, 49152, 264, 3),
     ("few rows, seg pass", 16, 12288, 520, 3),

@@ -304,6 +304,10 @@ def test_random_long_rows(mm, T, K, N, nd, halved):
     # 9 and 12 (the most) 16-row blocks per workgroup; 49160 columns: 3073
     # blocks, one more workgroup holding a half block
     (2, 4096, 36864, 3, 6.0), (1, 4096, 49160, 2, 6.0),
+    # the decode workload's width with a half last block, more outliers than
+    # the W16 values kept in LDS at that width, and 9 blocks per workgroup
+    # with K = 4096 (4 chunks per block)
+    (4, 8192, 28680, 5, 6.0), (8, 8192, 28672, 40, 6.0), (16, 4096, 36864, 3, 6.0),
 ])
 def test_decode_path(mm, T, K, N, nd, tau):
     """Shapes on the single-kernel decode path (T <= 16, K in {4096, 8192})."""
@@ -341,6 +345,7 @@ def test_decode_precomputed(mm, T, K, N, nd, tau, halved):
     (30, 2048, 136, 0, 0.0),        # 30 rows, every dimension an outlier
     (160, 2048, 264, 300, 6.0),     # 256x128 streaming tile, recovered rows
     (300, 8192, 264, 40, 6.0),      # K split in two past 256 rows
+    (8, 8192, 28680, 40, 6.0),      # decode kernel, half last block, o > 16
 ])
 def test_memory_halved(mm, T, K, N, nd, tau):
     """W16 = NULL: outlier rows recovered from the Int8 weight."""

@@ -46,6 +46,7 @@ def call_noalloc(mm, Xd, Wq, sw, W16, out):
 
 @pytest.mark.parametrize("big,small,halved", [
     ((8, 8192, 1040), (4, 4096, 264), False),        # single decode kernel
+    ((8, 8192, 28672), (2, 4096, 36864), True),      # decode kernel at full width, memory-halved
     ((8, 49152, 264), (2, 24576, 136), False),       # decode K slabs
     ((64, 2048, 520), (40, 1024, 264), True),        # streaming tile, memory-halved
     ((600, 12288, 776), (300, 2048, 520), False),    # large tile (K split), then streaming
