@@ -145,10 +145,13 @@ static_assert(kChunkK == kChunkKConst, "chunk size");
 // (the host sends it T <= 8 only, and longer K in slabs).
 // MAXB: the most 16-row blocks a workgroup owns (a.bpw <= MAXB); the LDS
 // arrays per row are sized for it (kSmallBpw keeps the common case's
-// footprint and code as small as they were).
-template <int CPB, int HT, bool PRE, int MAXB>
+// footprint and code as small as they were).  EARLY (activation side
+// computed in the kernel only): the second ring slot's chunk is issued
+// before the prologue's last barrier.
+template <int CPB, int HT, bool PRE, int MAXB, bool EARLY>
 __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
     static_assert(PRE == (CPB == 0), "the precomputed mode takes its chunk count at run time");
+    static_assert(!(PRE && EARLY), "the early second chunk belongs to the in-kernel prologue");
     // W16 values of the first outliers fetched per thread during the stream
     constexpr int kW16Pairs = MAXB * kRows / 2;
     constexpr int kW16PerThread = kW16Cache * kW16Pairs / kThreads;
@@ -435,6 +438,18 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
             const int c8 = tid + kThreads * j;
             if ((c8 & (kChunkK / 8 - 1)) == 0) sm.cfirst[c8 / (kChunkK / 8)] = pc[j];
         }
+        // EARLY: the second chunk goes out here rather than after the last
+        // barrier; the first has landed by now, so the HBM would otherwise
+        // idle through the barrier and the W16 fetch (decode workload 45.8 ->
+        // 45.3 us per call; when the 16 chunks the waves start with are all
+        // of a workgroup's, as at K = 4096, N = 14336, 2.4-3.3% slower).  A
+        // run-time choice made the compiler's wait counts at the loop entry
+        // cover both orders (up to 10% slower), hence a template parameter.
+        if constexpr (EARLY) {
+            __builtin_amdgcn_sched_barrier(0);
+            issue(id1, ring[1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         if (tid == 0) sm.cfirst[K / kChunkK] = o;
         if (blockIdx.x == 0 && tid == 0 && a.dbg_count) a.dbg_count[0] = o;
         if (blockIdx.x == 0 && a.dbg_sx && tid < T) a.dbg_sx[tid] = sm.sx[tid];
@@ -515,7 +530,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
             w16v[h] = *reinterpret_cast<const uint32_t*>(a.w16 + off);
         }
     }
-    issue(id1, ring[1]);
+    if constexpr (!EARLY) issue(id1, ring[1]);
 
     // ---- stream the workgroup's chunks.  The loop body is unrolled over the
     // two ring slots (compile-time register indices) and every slot is
@@ -709,20 +724,35 @@ int device_cus() {
 
 // One instantiation per 16-bit type and LDS size (the smaller one whenever
 // the workgroup owns at most kSmallBpw blocks).
-template <int CPB, bool PRE>
-static void launch_k(int ht, const DecodeArgs& a, unsigned grid, hipStream_t stream) {
+template <int CPB, bool PRE, bool EARLY>
+static void launch_k2(int ht, const DecodeArgs& a, unsigned grid, hipStream_t stream) {
     const bool small = a.bpw <= kSmallBpw;
     if (ht == kHalfBF16) {
         if (small)
-            hipLaunchKernelGGL((k_decode<CPB, kHalfBF16, PRE, kSmallBpw>), dim3(grid), dim3(kThreads), 0, stream, a);
+            hipLaunchKernelGGL((k_decode<CPB, kHalfBF16, PRE, kSmallBpw, EARLY>), dim3(grid), dim3(kThreads), 0, stream, a);
         else
-            hipLaunchKernelGGL((k_decode<CPB, kHalfBF16, PRE, kMaxBpw>), dim3(grid), dim3(kThreads), 0, stream, a);
+            hipLaunchKernelGGL((k_decode<CPB, kHalfBF16, PRE, kMaxBpw, EARLY>), dim3(grid), dim3(kThreads), 0, stream, a);
     } else {
         if (small)
-            hipLaunchKernelGGL((k_decode<CPB, kHalfF16, PRE, kSmallBpw>), dim3(grid), dim3(kThreads), 0, stream, a);
+            hipLaunchKernelGGL((k_decode<CPB, kHalfF16, PRE, kSmallBpw, EARLY>), dim3(grid), dim3(kThreads), 0, stream, a);
         else
-            hipLaunchKernelGGL((k_decode<CPB, kHalfF16, PRE, kMaxBpw>), dim3(grid), dim3(kThreads), 0, stream, a);
+            hipLaunchKernelGGL((k_decode<CPB, kHalfF16, PRE, kMaxBpw, EARLY>), dim3(grid), dim3(kThreads), 0, stream, a);
     }
+}
+// The early second chunk for K = 8192 when a workgroup has more chunks than
+// the 16 its waves start with (in-kernel prologue only).  Measured per call
+// against the late issue: K = 8192, N = 28672 with T = 8 and 1 and N = 36864
+// with T = 8 -0.8 to -1.2%; at K = 4096 T = 2, N = 36864 -1.4% but T = 4,
+// N = 49152 +2.7%, so K = 4096 keeps the late issue.
+template <int CPB, bool PRE>
+static void launch_k(int ht, const DecodeArgs& a, unsigned grid, hipStream_t stream) {
+    if constexpr (!PRE && CPB == 8) {
+        if ((int64_t)a.bpw * CPB > 2 * kWaves) {
+            launch_k2<CPB, PRE, true>(ht, a, grid, stream);
+            return;
+        }
+    }
+    launch_k2<CPB, PRE, false>(ht, a, grid, stream);
 }
 
 hipError_t launch_decode(const uint16_t* X, int ht, int64_t T, int64_t K, const int8_t* Wq,
