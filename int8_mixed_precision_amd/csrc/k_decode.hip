@@ -17,12 +17,13 @@
 //     arbitration favours simply take more chunks and all of them finish
 //     together; each chunk's int32 partial sums are added into LDS (exact and
 //     order independent);
-//   - every wave first issues the loads of its first chunk, then the
-//     workgroup recomputes the activation side from X (T*K fp16, cache
+//   - the workgroup recomputes the activation side from X (T*K fp16, cache
 //     resident): a thread owns whole 8-column pieces across all T rows, so
 //     the outlier flags of its columns need no exchange; row absmax by a
 //     transposed butterfly and LDS; ascending outlier indices by a popcount
-//     prefix scan; Xq to LDS;
+//     prefix scan; Xq to LDS.  Every wave's first chunk goes out in four
+//     parts over that work once X has arrived, and (K = 8192 with more than
+//     16 chunks per workgroup) its second chunk before the last barrier;
 //   - Wq goes from global memory straight into registers as the A operand of
 //     v_mfma_i32_16x16x64_i8 (16 weight rows x 64 k), through a ring of two
 //     chunks of 16 loads per wave; the B operand (the T activation rows as
