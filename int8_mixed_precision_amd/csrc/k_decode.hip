@@ -70,6 +70,7 @@ struct DecodeArgs {
     uint32_t tau16;         // bits of the smallest 16-bit value >= tau (+inf if none finite)
     int T, K, N;
     int bpw;                // 16-row blocks per workgroup (1..kMaxBpw)
+    int ileave;             // 1: workgroup g owns blocks g, g + groups, ...; 0: bpw consecutive blocks
     int cpb;                // K / 1024 (used when the chunk count is not a template constant)
     // activation side computed beforehand by the activation-pass kernels
     // (precomputed mode only): Xq [T,K], s_x [T], count {o, opad}, idx [o],
@@ -178,15 +179,21 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
     const int T = a.T, K = a.K, N = a.N;
     const int ldx = cpb * kChunkK + 16;        // LDS row stride of Xq (the slab's k)
     const int nblocks = (N + kRows - 1) / kRows;
-    // this workgroup's weight rows n0 .. n0 + rows - 1 (rows past N are read
-    // as row N-1 and never stored); chunk id -> block id / cpb, k-chunk id % cpb
-    const int b0 = grp * a.bpw;
-    const int nbw = a.bpw < nblocks - b0 ? a.bpw : nblocks - b0;
+    // this workgroup's blocks: slot s holds block b0 + s * bstep (rows past N
+    // are read as row N-1 and never stored); chunk id -> slot id / cpb,
+    // k-chunk id % cpb.  Consecutive blocks (bstep = 1), or with ileave the
+    // blocks grp, grp + groups, ... (see launch_decode)
+    const bool ilv = a.ileave != 0;
+    const int b0 = ilv ? grp : grp * a.bpw;
+    const int bstep = ilv ? groups : 1;
+    const int nbw = ilv ? (nblocks - grp + groups - 1) / groups
+                        : (a.bpw < nblocks - b0 ? a.bpw : nblocks - b0);
     const int rows = nbw * kRows;
-    const int n0 = b0 * kRows;
+    // weight row of the workgroup's row r (slot r / 16)
+    auto nrow = [&](int r) { return (b0 + (r >> 4) * bstep) * kRows + (r & 15); };
     const int total = nbw * cpb;
 
-    // Load i of a chunk: lane l holds weight row n0 + 16 (id / cpb) + l % 16
+    // Load i of a chunk: lane l holds weight row nrow(16 (id / cpb) + l % 16)
     // and bytes 1024 (id % cpb) + 64 i + 16 (l / 16) .. +16 of its k range.
     // In the panel-blocked layout (K % 1024 == 0, so every k-tile is 64
     // wide) a block's 16 rows lie in one panel and load i reads one
@@ -197,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
     const int kl = (lane >> 4) * 16;
     // loads lo .. hi-1 of chunk id into buf (lo and hi are constants)
     auto issue_part = [&](int id, v4i (&buf)[kLoads], int lo, int hi) {
-        const int n = n0 + (id / cpb) * kRows + (lane & 15);
+        const int n = (b0 + (id / cpb) * bstep) * kRows + (lane & 15);
         const int64_t nc = n < N ? n : N - 1;
         const int64_t p0 = nc - nc % kPanel;
         const int64_t prow = N - p0 < kPanel ? N - p0 : kPanel;
@@ -213,11 +220,11 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
     };
     auto issue = [&](int id, v4i (&buf)[kLoads]) { issue_part(id, buf, 0, kLoads); };
 
-    // s_w of the rows, one float4 per thread (n0 and N are multiples of 8,
-    // so a group of 4 rows is all in range or read as the last 4)
+    // s_w of the rows, one float4 per thread (a block's first row and N are
+    // multiples of 8, so a group of 4 rows is all in range or read as the last 4)
     float4 sw4;
     {
-        const int n = tid * 4 < rows && n0 + tid * 4 < N ? n0 + tid * 4 : N - 4;
+        const int n = tid * 4 < rows && nrow(tid * 4) < N ? nrow(tid * 4) : N - 4;
         sw4 = *reinterpret_cast<const float4*>(a.sw + n);
     }
     {
@@ -526,7 +533,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
             const int q = tid + kThreads * h;
             const int j = q / kW16Pairs;
             const int r = 2 * (q % kW16Pairs);
-            const int n = r < rows && n0 + r < N ? n0 + r : 0;
+            const int n = r < rows && nrow(r) < N ? nrow(r) : 0;
             const int64_t off = j < o ? (int64_t)sm.idx[j] * N + n : 0;
             w16v[h] = *reinterpret_cast<const uint32_t*>(a.w16 + off);
         }
@@ -603,7 +610,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
             // this slab's int32 sums of the workgroup's rows
             for (int e = tid; e < rows * T; e += kThreads) {
                 const int r = e % rows, t = e / rows;
-                const int n = n0 + r;
+                const int n = nrow(r);
                 if (n < N) a.part[((int64_t)slab * T + t) * N + n] = sm.acc[r >> 4][r & 15][t];
             }
             return;
@@ -615,7 +622,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
     const int oc = o < kW16Cache ? o : kW16Cache;
     for (int e = tid; e < rows * T; e += kThreads) {
         const int r = e % rows, t = e / rows;
-        const int n = n0 + r;
+        const int n = nrow(r);
         if (n >= N) continue;
         const int32_t acc = sm.acc[r >> 4][r & 15][t];
         if (a.dbg_acc) a.dbg_acc[(int64_t)t * N + n] = acc;
@@ -756,6 +763,17 @@ static void launch_k(int ht, const DecodeArgs& a, unsigned grid, hipStream_t str
     launch_k2<CPB, PRE, false>(ht, a, grid, stream);
 }
 
+// Which blocks a workgroup owns.  Measured per call (alternated, one box,
+// Y bit-identical): with 12 blocks per workgroup (N = 49152, and the K-slab
+// plans that give 12 per group), owning blocks g, g + groups, ... instead of
+// 12 consecutive ones was faster on 12 of 13 shapes (K = 4096 T = 1..16
+// -15 to -16.5%, K = 5120 -8.5%, K = 12288 -11 to -12%, K = 16384 -5.7%,
+// T = 8 and 16 with K = 49152, N = 12288 in slabs -11% and -5%; T = 12,
+// K = 32768, N = 12288 in slabs +2.9%); with 7, 9 or 11 blocks it was
+// slower on the decode workload (+10.6%) and mixed elsewhere (-9% to +8%),
+// so only the 12-block split interleaves.
+static int interleave_blocks(int bpw) { return bpw == kMaxBpw ? 1 : 0; }
+
 hipError_t launch_decode(const uint16_t* X, int ht, int64_t T, int64_t K, const int8_t* Wq,
                          const float* sw, const uint16_t* W16, int64_t N, float tau,
                          uint16_t* Y, int32_t* dbg_count, int32_t* dbg_idx, int8_t* dbg_xq,
@@ -767,7 +785,7 @@ hipError_t launch_decode(const uint16_t* X, int ht, int64_t T, int64_t K, const 
     const int64_t nblocks = ceil_div(N, kRows);
     const int bpw = (int)std::min<int64_t>(kMaxBpw, std::max<int64_t>(1, ceil_div(nblocks, device_cus())));
     DecodeArgs a{X, Wq, sw, W16, Y, tau, tau_to_h16_ceil(tau, ht), (int)T, (int)K, (int)N, bpw,
-                 (int)(K / kChunkK), nullptr, nullptr, nullptr, nullptr, nullptr,
+                 interleave_blocks(bpw), (int)(K / kChunkK), nullptr, nullptr, nullptr, nullptr, nullptr,
                  1, (int)(K / kChunkK), nullptr,
                  dbg_count, dbg_idx, dbg_xq, dbg_sx, dbg_acc};
     const unsigned grid = (unsigned)ceil_div(nblocks, bpw);
@@ -798,7 +816,7 @@ hipError_t launch_decode_pre(int ht, int64_t T, int64_t K, const int8_t* Wq, con
     const int64_t nblocks = ceil_div(N, kRows);
     const int bpw = (int)std::min<int64_t>(kMaxBpw, std::max<int64_t>(1, ceil_div(nblocks, device_cus())));
     DecodeArgs a{nullptr, Wq, sw, W16, Y, 0.0f, 0u, (int)T, (int)K, (int)N, bpw,
-                 (int)(K / kChunkK), ws.xq, ws.sx, ws.count, ws.idx, ws.xo,
+                 interleave_blocks(bpw), (int)(K / kChunkK), ws.xq, ws.sx, ws.count, ws.idx, ws.xo,
                  1, (int)(K / kChunkK), nullptr,
                  nullptr, nullptr, nullptr, nullptr, dbg_acc};
     const unsigned grid = (unsigned)ceil_div(nblocks, bpw);
@@ -856,7 +874,7 @@ hipError_t launch_decode_split(int ht, int64_t T, int64_t K, const int8_t* Wq, c
     const SlabPlan p = plan_slabs(T, K, N, reserve);
     const int64_t nblocks = ceil_div(N, kRows);
     DecodeArgs a{nullptr, Wq, sw, W16, Y, 0.0f, 0u, (int)T, (int)K, (int)N, p.bpw,
-                 (int)(K / kChunkK), ws.xq, ws.sx, ws.count, ws.idx, ws.xo,
+                 interleave_blocks(p.bpw), (int)(K / kChunkK), ws.xq, ws.sx, ws.count, ws.idx, ws.xo,
                  p.slabs, p.cps, ws.dpart,
                  nullptr, nullptr, nullptr, nullptr, dbg_acc};
     const unsigned grid = (unsigned)(ceil_div(nblocks, p.bpw) * p.slabs);
