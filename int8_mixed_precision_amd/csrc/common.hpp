@@ -60,10 +60,13 @@ __device__ __forceinline__ uint16_t f32_to_h16(float f) {
 //   wrec    16-bit [min(K, kRecoverRows), N]  the outlier rows of W recovered from
 //           Wq for the memory-halved variant, row j = outlier j (present when the
 //           workspace is large enough for it)
-// and, only when the matmul splits K in two (gemm_ksplit), after all of the above:
-//   ks_count i32 [nsplit]            per split tile, halves finished (zeroed by
+// and, only when the matmul splits K (gemm_ksplit), after all of the above:
+//   ks_count i32 [nsplit]            per split tile, parts finished (zeroed by
 //                                    the call's activation pass or the matmul's launch)
 //   ks_part  i32 [nsplit][2][65536]  each half's int32 sums of its 256 x 256 tile
+//                                    (large-tile kernel, T > 128), or
+//            i32 [tiles][S][BM*BN]   each K slab's sums of its tile (streaming
+//                                    kernel, 65..128 rows, stream_split)
 // or, for few rows with a long K (decode_split_reserve), instead of wrec and
 // the split:
 //   dpart    i32 [dslabs][T][N]     each K slab's int32 sums
@@ -154,6 +157,15 @@ uint32_t tau_to_h16_ceil(float tau, int ht);
 // 2 when the large-tile matmul of (T, K, N) runs each 256 x 256 output tile
 // as two halves of K on the current device, else 1.
 int gemm_ksplit(int64_t T, int64_t K, int64_t N);
+// K split of the streaming kernel (65..128 rows): s slabs (1: none) of
+// tiles tiles with tile_bytes of int32 partial sums per slab (k_gemm.hip).
+constexpr int64_t kStreamMinSlab = 16;   // k-tiles of 128 per slab, at least
+constexpr int kStreamMaxSplit = 8;
+struct StreamSplit {
+    int s;
+    int64_t tiles, tile_bytes;
+};
+StreamSplit stream_split(int64_t T, int64_t K, int64_t N);
 // The large-tile matmul's K split on this device: the first `full` tiles run
 // all of K, the last `nsplit` as two halves (nsplit = 0: no split).
 struct KSplitPlan {
@@ -219,7 +231,7 @@ struct GemmArgs {
     uint16_t* y;           // [T,N] 16-bit
     int32_t* acc_out;      // [T,N] or NULL
     int64_t T, K, N;
-    int ksplit;            // 1, or 2: K split in two halves (large-tile kernel only)
+    int ksplit;            // 1; 2: K split in two halves (large-tile kernel); S: slabs (streaming kernel)
     int32_t* ks_count;     // [nsplit] (ksplit = 2; zero at launch_gemm or zeroed by it)
     int32_t* ks_part;      // [nsplit][2][65536] (ksplit = 2)
     int64_t ks_full;       // ksplit = 2: tiles that run all of K (set by launch_gemm)

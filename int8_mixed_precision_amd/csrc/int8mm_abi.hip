@@ -41,9 +41,10 @@ Workspace layout_for(void* base, int64_t T, int64_t K, int64_t N, size_t workspa
     if (ds > 0 && workspace_bytes >= carve_workspace(nullptr, T, K, N, false, 1, ds).bytes)
         return carve_workspace(base, T, K, N, false, 1, ds);
     const bool wrec = workspace_bytes >= carve_workspace(nullptr, T, K, N, true, 1).bytes;
-    const int ks = wrec && gemm_ksplit(T, K, N) == 2 &&
-                           workspace_bytes >= carve_workspace(nullptr, T, K, N, true, 2).bytes
-                       ? 2
+    const int want = gemm_ksplit(T, K, N);
+    const int ks = wrec && want >= 2 &&
+                           workspace_bytes >= carve_workspace(nullptr, T, K, N, true, want).bytes
+                       ? want
                        : 1;
     return carve_workspace(base, T, K, N, wrec, ks);
 }
@@ -72,7 +73,7 @@ int run_prepared(const Workspace& ws, int ht, int64_t T, int64_t K, const int8_t
         nrows = ws.wrec_rows;
     }
     GemmArgs g{ws.xq, ws.sx, Wq, sw, ws.xo, ws.idx, ws.count, rows, nrows, y16, acc, T, K, N,
-               ws.ks_count ? 2 : 1, ws.ks_count, ws.ks_part, 0, ks_zeroed ? 1 : 0};
+               ws.ks_count ? gemm_ksplit(T, K, N) : 1, ws.ks_count, ws.ks_part, 0, ks_zeroed ? 1 : 0};
     return hip_status(launch_gemm(g, ht, stream));
 }
 

@@ -1227,12 +1227,20 @@ Workspace carve_workspace(void* base, int64_t T, int64_t K, int64_t N, bool wrec
         w.wrec_rows = K < kRecoverRows ? K : kRecoverRows;
         w.wrec = reinterpret_cast<uint16_t*>(take(sizeof(uint16_t) * (size_t)w.wrec_rows * (size_t)N));
     }
-    if (wrec && ksplit == 2) {
+    if (wrec && ksplit >= 2) {
         // after everything else, so the layout without the split is a prefix;
-        // one counter and two halves of partial sums per split tile
-        const int64_t nsplit = gemm_ksplit_plan(T, K, N).nsplit;
-        w.ks_count = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)nsplit));
-        w.ks_part = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)nsplit * 2 * 65536));
+        // one counter per split tile and the partial sums of each part:
+        // large-tile kernel (more than 128 rows) two halves of 256 x 256,
+        // streaming kernel S slabs of its tile
+        if (T > 128) {
+            const int64_t nsplit = gemm_ksplit_plan(T, K, N).nsplit;
+            w.ks_count = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)nsplit));
+            w.ks_part = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)nsplit * 2 * 65536));
+        } else {
+            const StreamSplit sp = stream_split(T, K, N);
+            w.ks_count = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)sp.tiles));
+            w.ks_part = reinterpret_cast<int32_t*>(take((size_t)sp.tiles * (size_t)sp.s * (size_t)sp.tile_bytes));
+        }
     }
     if (dslabs > 0) {
         w.dslabs = dslabs;

@@ -984,7 +984,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_i8_stream(GemmA
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t T = a.T, K = a.K, N = a.N;
     const int64_t MT = ceil_div(T, BM);
-    const int64_t bid = xcd_tile(blockIdx.x, gridDim.x);
+    // K split (ksplit = S > 1): unit u is slab u / tiles of tile u % tiles
+    // (every tile's first slab is dispatched before any second one)
+    const int64_t tiles = MT * ceil_div(N, (int64_t)BN);
+    const int S = a.ksplit > 1 ? a.ksplit : 1;
+    const int64_t tix = S > 1 ? (int64_t)blockIdx.x % tiles : (int64_t)blockIdx.x;
+    const int slab = S > 1 ? (int)((int64_t)blockIdx.x / tiles) : 0;
+    const int64_t bid = xcd_tile(tix, tiles);
     const int64_t m0 = (bid % MT) * BM;
     const int64_t n0 = (bid / MT) * BN;
     const int wm0 = (wave % WAVES_M) * WM;
@@ -1035,14 +1041,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_i8_stream(GemmA
 
     // fragment offsets inside a tile for k-step 0; k-step s adds 32 s bytes
     // of logical k, i.e. logical chunk 2 s + lane / 32
-    const int KT = (int)(K / BK);
+    // k-tiles KT0 .. KT-1 of 128 (all of K without the split)
+    const int KTA = (int)(K / BK);
+    const int kps = (KTA + S - 1) / S;
+    const int KT0 = slab * kps;
+    const int KT = KT0 + kps < KTA ? KT0 + kps : KTA;
 #pragma unroll
     for (int st = 0; st < STAGES - 1; ++st)
 #pragma unroll
-        for (int u = 0; u < LOADS; ++u) copy(u, st < KT ? st : KT - 1, st);
+        for (int u = 0; u < LOADS; ++u) copy(u, KT0 + st < KT ? KT0 + st : KT - 1, st);
 
     int s_cur = 0;
-    for (int kt = 0; kt < KT; ++kt) {
+    for (int kt = KT0; kt < KT; ++kt) {
         __builtin_amdgcn_s_waitcnt(vmcnt_imm((STAGES - 2) * LOADS));   // this wave's part of tile kt
         __syncthreads();                                                 // everyone's part; tile kt-1 read
         const int s_fill = s_cur == 0 ? STAGES - 1 : s_cur - 1;
@@ -1075,21 +1085,84 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_i8_stream(GemmA
     // the copies past the last tile went to buffers no one reads; let them
     // land before the workgroup ends
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    if (S > 1) {
+        // Every slab publishes its int32 sums, then counts itself done on the
+        // tile's counter (zeroed before the launch); the slab that counts
+        // last adds the others' sums (exact, in any order) and runs the
+        // epilogue.  Ordering as in the large-tile kernel's K split: agent-
+        // scope atomic stores (the slabs may run on different XCDs, whose L2
+        // caches are not shared), a workgroup barrier, thread 0's acq_rel
+        // increment at agent scope, a barrier, agent-scope atomic loads.  No
+        // unit waits for another.
+        __shared__ int last;
+        constexpr int PER = TM * TN * 8 * 64;                 // 64-bit words per wave
+        uint64_t* part = reinterpret_cast<uint64_t*>(a.ks_part) + (tix * S) * NW * PER;
+        uint64_t* mine = part + (slab * NW + wave) * PER;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const uint64_t v = (uint64_t)(uint32_t)acc[i][j][2 * q] |
+                                       ((uint64_t)(uint32_t)acc[i][j][2 * q + 1] << 32);
+                    __hip_atomic_store(mine + ((i * TN + j) * 8 + q) * 64 + lane, v, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                }
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __syncthreads();   // every wave's sums are out
+        if (tid == 0)
+            last = __hip_atomic_fetch_add(&a.ks_count[tix], 1, __ATOMIC_ACQ_REL,
+                                          __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+        __syncthreads();
+        if (!last) return;   // the last slab finishes the tile
+        for (int o = 0; o < S; ++o) {
+            if (o == slab) continue;
+            const uint64_t* other = part + (o * NW + wave) * PER;
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const uint64_t v = __hip_atomic_load(other + ((i * TN + j) * 8 + q) * 64 + lane,
+                                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        acc[i][j][2 * q] += (int32_t)(uint32_t)v;
+                        acc[i][j][2 * q + 1] += (int32_t)(uint32_t)(v >> 32);
+                    }
+        }
+    }
     epilogue<TM, TN, WRITE_ACC, HT, BN, 64 * NW>(acc, a, m0 + wm0, n0 + wn0, lane,
                                                  StageCtx{lds, tid, m0, n0, nullptr, 0.0f, nullptr, 0, 0, -1,
                                                           false, {}, {}});
+}
+
+__global__ void k_zero_i32(int32_t* __restrict__ p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0;
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int HT>
 hipError_t launch_stream(const GemmArgs& a, hipStream_t stream) {
     const int64_t tiles = ceil_div(a.T, BM) * ceil_div(a.N, BN);
     constexpr int threads = 64 * WAVES_M * WAVES_N;
+    GemmArgs b = a;
+    if (b.ksplit > 1) {
+        // the K split's tile counters start at zero (a kernel, not a memset,
+        // so the call can be captured in a graph)
+        if (!b.ks_count || !b.ks_part) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(k_zero_i32, dim3((unsigned)ceil_div(tiles, 256)), dim3(256), 0, stream,
+                           b.ks_count, tiles);
+    } else {
+        b.ksplit = 1;
+    }
+    const int64_t units = tiles * b.ksplit;
     if (a.acc_out)
         hipLaunchKernelGGL((k_gemm_i8_stream<BM, BN, WAVES_M, WAVES_N, STAGES, true, HT>),
-                           dim3((unsigned)tiles), dim3(threads), 0, stream, a);
+                           dim3((unsigned)units), dim3(threads), 0, stream, b);
     else
         hipLaunchKernelGGL((k_gemm_i8_stream<BM, BN, WAVES_M, WAVES_N, STAGES, false, HT>),
-                           dim3((unsigned)tiles), dim3(threads), 0, stream, a);
+                           dim3((unsigned)units), dim3(threads), 0, stream, b);
     return hipGetLastError();
 }
 
@@ -1103,11 +1176,6 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL((k_gemm_i8<BM, BN, BK, WAVES_M, false, HT>), dim3((unsigned)tiles),
                            dim3(kThreads), 0, stream, a);
     return hipGetLastError();
-}
-
-__global__ void k_zero_i32(int32_t* __restrict__ p, int64_t n) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = 0;
 }
 
 template <int HT>
@@ -1203,12 +1271,38 @@ KSplitPlan gemm_ksplit_plan(int64_t T, int64_t K, int64_t N) {
     return none;
 }
 
+// The streaming kernel's 128x128 tiles (65..128 rows, K % 128 == 0) run
+// one per CU, all at once; when they occupy at most half of the CUs, K is
+// cut into S slabs so that tiles x S fill them once, each slab at least 16
+// k-tiles of 128 (e.g. T = 128, N = 12288: 96 tiles on 256 CUs, S = 2).
+// Partial sums: S x 64 KB per tile.  Measured, whole calls: T = 128, N =
+// 12288: K = 12288 -9%, K = 49152 -26%.  The 64x64 tiles (up to 64 rows,
+// two per CU) are not split: there the split ran 15-49% slower (each of
+// the many small units pays the release/acquire pair, an L2 write-back and
+// invalidate, against a short slab).
+StreamSplit stream_split(int64_t T, int64_t K, int64_t N) {
+    StreamSplit p{1, 0, 0};
+    if (T <= 64 || T > 128 || K % 128 != 0) return p;
+    const int64_t bm = 128;
+    const int64_t per_cu = 1;
+    p.tiles = ceil_div(T, bm) * ceil_div(N, bm);
+    p.tile_bytes = bm * bm * 4;
+    const int64_t slots = device_cus() * per_cu;
+    const int64_t s = std::min<int64_t>(slots / p.tiles, (K / 128) / kStreamMinSlab);
+    if (2 * p.tiles <= slots && s >= 2) p.s = (int)std::min<int64_t>(s, kStreamMaxSplit);
+    return p;
+}
+
 int gemm_ksplit(int64_t T, int64_t K, int64_t N) {
+    if (T <= 128) return stream_split(T, K, N).s;
     return gemm_ksplit_plan(T, K, N).nsplit > 0 ? 2 : 1;
 }
 
 hipError_t launch_gemm(const GemmArgs& a, int ht, hipStream_t stream) {
-    if (a.ksplit != 1 && !(a.ksplit == 2 && a.ks_count && a.ks_part && a.T > 128 && a.K % 128 == 0))
+    const bool big_split = a.ksplit == 2 && a.T > 128;
+    const bool stream_split_ok = a.ksplit >= 2 && a.T <= 128 && a.ksplit == stream_split(a.T, a.K, a.N).s;
+    if (a.ksplit != 1 &&
+        !((big_split || stream_split_ok) && a.ks_count && a.ks_part && a.K % 128 == 0))
         return hipErrorInvalidValue;
     return ht == kHalfBF16 ? launch_gemm_typed<kHalfBF16>(a, stream)
                            : launch_gemm_typed<kHalfF16>(a, stream);

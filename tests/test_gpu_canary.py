@@ -114,6 +114,8 @@ ROUTES = [
     ("owned detection, cached quantizer 12", 40, 20000, 264, 3),
     ("owned detection, compacted quantizer", 24, 65536, 264, 3),
     ("256x128 stream tile", 200, 1024, 520, 4),
+    ("stream 128x128, K split in 8", 72, 49152, 264, 3),
+    ("stream 128x128, K split in 2", 128, 12288, 1040, 4),
     ("big tile, register quantizer K<=4096", 300, 1024, 520, 5),
     ("big tile, all tiles split in K", 300, 8192, 520, 5),
     ("register quantizer K<=12288", 140, 12288, 264, 3),

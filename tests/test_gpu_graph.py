@@ -21,7 +21,7 @@ def mm():
 @pytest.mark.parametrize("T,K,N", [(8, 8192, 1040), (300, 1024, 520), (300, 24576, 520),
                                    (16, 8192, 1040), (8, 49152, 264), (4, 12288, 520),
                                    (200, 1024, 520), (64, 2048, 264),
-                                   (8, 8192, 28672)])
+                                   (8, 8192, 28672), (96, 12288, 520)])   # last: K split
 def test_graph_replays_match_eager(mm, T, K, N):
     print(f"[case] graph replay {T}x{K}x{N}", flush=True)
     X, W = synth.random_case(40_000 + T, T, K, N, n_dims=3)
@@ -55,7 +55,7 @@ def test_concurrent_streams_match_eager(mm):
     print("[case] concurrent streams", flush=True)
     cases = []
     for i, (T, K, N) in enumerate([(8, 8192, 1040), (8, 49152, 264), (64, 2048, 264),
-                                   (300, 24576, 520), (4, 8192, 28680)]):
+                                   (300, 24576, 520), (4, 8192, 28680), (128, 12288, 1040)]):
         X, W = synth.random_case(41_000 + i, T, K, N, n_dims=3)
         Xd, Wd = torch.from_numpy(X).cuda(), torch.from_numpy(W).cuda()
         Wq, sw = mm.quantize_weight(Wd)

@@ -297,6 +297,26 @@ def test_random_long_rows(mm, T, K, N, nd, halved):
     run_case(mm, f"long rows {T}x{K}x{N}{' halved' if halved else ''}", X, W, 6.0, halved=halved)
 
 
+@pytest.mark.parametrize("T,K,N,nd,halved", [
+    # streaming matmul's 128x128 tiles with K cut into slabs (tiles on at
+    # most half of the CUs): 8 slabs, 6, 4 and 2 (ragged rows and columns),
+    # many outliers, memory-halved
+    (72, 49152, 264, 3, False), (128, 12288, 1032, 6, False), (100, 8192, 776, 4, False),
+    (65, 4096, 136, 40, False), (96, 12288, 520, 20, True),
+])
+def test_stream_k_split(mm, T, K, N, nd, halved):
+    X, W = synth.random_case(34_000 + T + K + N + nd, T, K, N, n_dims=nd)
+    run_case(mm, f"stream K split {T}x{K}x{N}", X, W, 6.0, halved=halved)
+
+
+def test_stream_k_split_out_projection(mm):
+    """The 175B-class out-projection at 128 rows (96 tiles of 128x128 on 256
+    CUs, K split in two), checked on sampled rows."""
+    X, W = synth.random_case(35_128, 128, 12288, 12288, n_dims=6)
+    run_case(mm, "stream K split 128x12288x12288 (sampled rows)", X, W, 6.0,
+             rows=[0, 1, 37, 64, 101, 127])
+
+
 @pytest.mark.parametrize("T,K,N,nd,tau", [
     (1, 4096, 1000, 3, 6.0), (3, 4096, 8, 0, 6.0), (8, 8192, 2056, 6, 6.0),
     (16, 4096, 520, 5, 6.0), (8, 8192, 264, 300, 6.0),   # o > 256: values read from X
