@@ -49,6 +49,7 @@ def call_noalloc(mm, Xd, Wq, sw, W16, out):
     ((8, 8192, 28672), (2, 4096, 36864), True),      # decode kernel at full width, memory-halved
     ((8, 49152, 264), (2, 24576, 136), False),       # decode K slabs
     ((64, 2048, 520), (40, 1024, 264), True),        # streaming tile, memory-halved
+    ((128, 12288, 1040), (72, 49152, 264), False),   # streaming tile with K split in 2, then 8
     ((600, 12288, 776), (300, 2048, 520), False),    # large tile (K split), then streaming
     ((2048, 12288, 2048), (520, 4096, 1032), False), # headline T and K, then a ragged tile
 ])
