@@ -166,6 +166,15 @@ struct StreamSplit {
     int64_t tiles, tile_bytes;
 };
 StreamSplit stream_split(int64_t T, int64_t K, int64_t N);
+// Completes Y from int32 partial sums part [slabs][T][N] (sum of the slabs,
+// dequantization, the outlier terms from W16 [K,N] or, W16 = NULL, from the
+// Int8 weight; one fp16/bf16 rounding) - the decode kernel's finishing
+// kernel, also used by the streaming matmul's 64x64 K split (k_decode.hip).
+hipError_t launch_finish_partials(int ht, int64_t T, int64_t K, int64_t N, int slabs,
+                                  const int32_t* part, const int8_t* Wq, const float* sw,
+                                  const uint16_t* W16, const float* sx, const int32_t* count,
+                                  const int32_t* idx, const uint16_t* xo, uint16_t* Y,
+                                  int32_t* dbg_acc, hipStream_t stream);
 // The large-tile matmul's K split on this device: the first `full` tiles run
 // all of K, the last `nsplit` as two halves (nsplit = 0: no split).
 struct KSplitPlan {

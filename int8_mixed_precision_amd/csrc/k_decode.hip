@@ -707,6 +707,34 @@ uint32_t tau_to_h16_ceil(float tau, int ht) {
     return lo;
 }
 
+hipError_t launch_finish_partials(int ht, int64_t T, int64_t K, int64_t N, int slabs,
+                                  const int32_t* part, const int8_t* Wq, const float* sw,
+                                  const uint16_t* W16, const float* sx, const int32_t* count,
+                                  const int32_t* idx, const uint16_t* xo, uint16_t* Y,
+                                  int32_t* dbg_acc, hipStream_t stream) {
+    DecodeArgs a{};
+    a.wq = Wq;
+    a.sw = sw;
+    a.w16 = W16;
+    a.y = Y;
+    a.T = (int)T;
+    a.K = (int)K;
+    a.N = (int)N;
+    a.sx_pre = sx;
+    a.count_pre = count;
+    a.idx_pre = idx;
+    a.xo_pre = xo;
+    a.slabs = slabs;
+    a.part = const_cast<int32_t*>(part);
+    a.dbg_acc = dbg_acc;
+    const dim3 fgrid((unsigned)ceil_div(N, 256), (unsigned)T);
+    if (ht == kHalfBF16)
+        hipLaunchKernelGGL(k_decode_finish<kHalfBF16>, fgrid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(k_decode_finish<kHalfF16>, fgrid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
 bool decode_path_supported(int64_t T, int64_t K, int64_t N) {
     (void)N;
     return T >= 1 && T <= kMaxT && (K == 4096 || K == 8192) && T * K <= kMaxXK;

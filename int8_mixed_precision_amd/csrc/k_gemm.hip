@@ -1085,6 +1085,26 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_i8_stream(GemmA
     // the copies past the last tile went to buffers no one reads; let them
     // land before the workgroup ends
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    if (BM == 64 && S > 1) {
+        // 64x64 tiles: the slab's int32 sums go to part [S][T][N] with plain
+        // stores and a second kernel (launch_finish_partials) adds the slabs
+        // and completes Y; the kernel boundary orders the two.  32x32
+        // accumulator layout: lane holds column lane % 32 and, in register
+        // r, row 8 (r / 4) + 4 (lane / 32) + r % 4 of the 32x32 tile.
+        int32_t* part = a.ks_part + (int64_t)slab * T * N;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int64_t n = n0 + wn0 + j * 32 + (lane & 31);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t m = m0 + wm0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                    if (m < T && n < N) part[m * N + n] = acc[i][j][r];
+                }
+            }
+        return;
+    }
     if (S > 1) {
         // Every slab publishes its int32 sums, then counts itself done on the
         // tile's counter (zeroed before the launch); the slab that counts
@@ -1147,7 +1167,9 @@ hipError_t launch_stream(const GemmArgs& a, hipStream_t stream) {
     const int64_t tiles = ceil_div(a.T, BM) * ceil_div(a.N, BN);
     constexpr int threads = 64 * WAVES_M * WAVES_N;
     GemmArgs b = a;
-    if (b.ksplit > 1) {
+    if (b.ksplit > 1 && BM == 64) {
+        if (!b.ks_part) return hipErrorInvalidValue;   // partial sums, finished by a second kernel
+    } else if (b.ksplit > 1) {
         // the K split's tile counters start at zero (a kernel, not a memset,
         // so the call can be captured in a graph)
         if (!b.ks_count || !b.ks_part) return hipErrorInvalidValue;
@@ -1163,6 +1185,14 @@ hipError_t launch_stream(const GemmArgs& a, hipStream_t stream) {
     else
         hipLaunchKernelGGL((k_gemm_i8_stream<BM, BN, WAVES_M, WAVES_N, STAGES, false, HT>),
                            dim3((unsigned)units), dim3(threads), 0, stream, b);
+    if (b.ksplit > 1 && BM == 64) {
+        // the recovered rows of the memory-halved variant are indexed by
+        // outlier position; the finishing kernel takes W16 [K,N] or recovers
+        // from Wq itself
+        const uint16_t* w16 = b.w16_rows > 0 ? nullptr : b.w16;
+        return launch_finish_partials(HT, b.T, b.K, b.N, b.ksplit, b.ks_part, b.wq, b.sw, w16, b.sx,
+                                      b.count, b.idx, b.xo, b.y, b.acc_out, stream);
+    }
     return hipGetLastError();
 }
 
@@ -1271,25 +1301,32 @@ KSplitPlan gemm_ksplit_plan(int64_t T, int64_t K, int64_t N) {
     return none;
 }
 
-// The streaming kernel's 128x128 tiles (65..128 rows, K % 128 == 0) run
-// one per CU, all at once; when they occupy at most half of the CUs, K is
-// cut into S slabs so that tiles x S fill them once, each slab at least 16
-// k-tiles of 128 (e.g. T = 128, N = 12288: 96 tiles on 256 CUs, S = 2).
-// Partial sums: S x 64 KB per tile.  Measured, whole calls: T = 128, N =
-// 12288: K = 12288 -9%, K = 49152 -26%.  The 64x64 tiles (up to 64 rows,
-// two per CU) are not split: there the split ran 15-49% slower (each of
-// the many small units pays the release/acquire pair, an L2 write-back and
-// invalidate, against a short slab).
+// K split of the streaming kernel (K % 128 == 0), when its tiles leave
+// workgroup slots idle: S slabs so that tiles x S fill the slots once, each
+// slab at least 16 k-tiles of 128, at most 8 slabs.
+//  - 128x128 tiles (65..128 rows, one per CU), at most half of the CUs
+//    busy: the last slab to finish adds the others' sums (published with
+//    agent-scope atomics) and runs the epilogue.  Whole calls: T = 128,
+//    N = 12288: K = 12288 -9%, K = 49152 -26%; T = 80, K = 49152 -28%.
+//  - 64x64 tiles (up to 64 rows, two per CU), at most a quarter of the
+//    slots busy (128 tiles on 256 CUs): every slab writes plain partial
+//    sums [S][T][N] and a finishing kernel completes Y (the same scheme
+//    with the release/acquire handoff ran 15-49% slower: each of the many
+//    small units pays an L2 write-back and invalidate).  Whole calls:
+//    T = 64, K = 12288: N = 2048 -39%, 4096 -23%, 8192 -10%; T = 64,
+//    K = 49152, N = 4096 -45%; T = 32, K = 4096, N = 4096 -4%; with 192
+//    tiles (N = 12288) it was 8-19% slower, hence the quarter.
 StreamSplit stream_split(int64_t T, int64_t K, int64_t N) {
     StreamSplit p{1, 0, 0};
-    if (T <= 64 || T > 128 || K % 128 != 0) return p;
-    const int64_t bm = 128;
-    const int64_t per_cu = 1;
+    if (T > 128 || K % 128 != 0) return p;
+    const int64_t bm = T <= 64 ? 64 : 128;
+    const int64_t per_cu = T <= 64 ? 2 : 1;
     p.tiles = ceil_div(T, bm) * ceil_div(N, bm);
     p.tile_bytes = bm * bm * 4;
     const int64_t slots = device_cus() * per_cu;
     const int64_t s = std::min<int64_t>(slots / p.tiles, (K / 128) / kStreamMinSlab);
-    if (2 * p.tiles <= slots && s >= 2) p.s = (int)std::min<int64_t>(s, kStreamMaxSplit);
+    const int64_t fill = T <= 64 ? 4 : 2;   // tiles may occupy at most 1/fill of the slots
+    if (fill * p.tiles <= slots && s >= 2) p.s = (int)std::min<int64_t>(s, kStreamMaxSplit);
     return p;
 }
 

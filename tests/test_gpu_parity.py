@@ -303,6 +303,10 @@ def test_random_long_rows(mm, T, K, N, nd, halved):
     # many outliers, memory-halved
     (72, 49152, 264, 3, False), (128, 12288, 1032, 6, False), (100, 8192, 776, 4, False),
     (65, 4096, 136, 40, False), (96, 12288, 520, 20, True),
+    # 64x64 tiles on at most a quarter of the slots: partial sums [S][T][N]
+    # and the finishing kernel (8, 6 and 2 slabs; o > 16; memory-halved)
+    (40, 12288, 1032, 3, False), (64, 49152, 4096, 5, False), (17, 4096, 264, 40, False),
+    (33, 49152, 520, 20, True),
 ])
 def test_stream_k_split(mm, T, K, N, nd, halved):
     X, W = synth.random_case(34_000 + T + K + N + nd, T, K, N, n_dims=nd)
