@@ -66,7 +66,7 @@ __device__ __forceinline__ uint16_t f32_to_h16(float f) {
 //   ks_part  i32 [nsplit][2][65536]  each half's int32 sums of its 256 x 256 tile
 //                                    (large-tile kernel, T > 128), or
 //            i32 [tiles][S][BM*BN]   each K slab's sums of its tile (streaming
-//                                    kernel, 65..128 rows, stream_split)
+//                                    kernel up to 256 rows, stream_split)
 // or, for few rows with a long K (decode_split_reserve), instead of wrec and
 // the split:
 //   dpart    i32 [dslabs][T][N]     each K slab's int32 sums
@@ -166,6 +166,8 @@ struct StreamSplit {
     int64_t tiles, tile_bytes;
 };
 StreamSplit stream_split(int64_t T, int64_t K, int64_t N);
+// 129..256 rows that run on the streaming kernel's 256x128 tile (k_gemm.hip)
+bool stream_256x128(int64_t T, int64_t K, int64_t N);
 // Completes Y from int32 partial sums part [slabs][T][N] (sum of the slabs,
 // dequantization, the outlier terms from W16 [K,N] or, W16 = NULL, from the
 // Int8 weight; one fp16/bf16 rounding) - the decode kernel's finishing

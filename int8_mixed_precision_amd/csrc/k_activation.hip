@@ -1232,7 +1232,7 @@ Workspace carve_workspace(void* base, int64_t T, int64_t K, int64_t N, bool wrec
         // one counter per split tile and the partial sums of each part:
         // large-tile kernel (more than 128 rows) two halves of 256 x 256,
         // streaming kernel S slabs of its tile
-        if (T > 128) {
+        if (T > 128 && !stream_256x128(T, K, N)) {
             const int64_t nsplit = gemm_ksplit_plan(T, K, N).nsplit;
             w.ks_count = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)nsplit));
             w.ks_part = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)nsplit * 2 * 65536));

@@ -1250,9 +1250,7 @@ hipError_t launch_big(const GemmArgs& a, hipStream_t stream) {
 // more tiles (N >= 36864) or a split K the large-tile kernel stays ahead.
 template <int HT>
 hipError_t launch_gemm_typed(const GemmArgs& a, hipStream_t stream) {
-    if (a.T > 128 && a.T <= 256 && a.K % 128 == 0 && ceil_div(a.N, 128) <= device_cus() &&
-        gemm_ksplit(a.T, a.K, a.N) == 1)
-        return launch_stream<256, 128, 4, 1, 3, HT>(a, stream);
+    if (stream_256x128(a.T, a.K, a.N)) return launch_stream<256, 128, 4, 1, 3, HT>(a, stream);
     if (a.T > 128 && a.K % 64 == 0) return launch_big<HT>(a, stream);
     if (a.K % 128 == 0) {
         if (a.T <= 64) return launch_stream<64, 64, 2, 2, 4, HT>(a, stream);
@@ -1304,8 +1302,9 @@ KSplitPlan gemm_ksplit_plan(int64_t T, int64_t K, int64_t N) {
 // K split of the streaming kernel (K % 128 == 0), when its tiles leave
 // workgroup slots idle: S slabs so that tiles x S fill the slots once, each
 // slab at least 16 k-tiles of 128, at most 8 slabs.
-//  - 128x128 tiles (65..128 rows, one per CU), at most half of the CUs
-//    busy: the last slab to finish adds the others' sums (published with
+//  - 128x128 tiles (65..128 rows, one per CU) and 256x128 tiles (129..256
+//    rows, one per CU), at most half of the CUs busy: the last slab to
+//    finish adds the others' sums (published with
 //    agent-scope atomics) and runs the epilogue.  Whole calls: T = 128,
 //    N = 12288: K = 12288 -9%, K = 49152 -26%; T = 80, K = 49152 -28%.
 //  - 64x64 tiles (up to 64 rows, two per CU), at most a quarter of the
@@ -1318,11 +1317,13 @@ KSplitPlan gemm_ksplit_plan(int64_t T, int64_t K, int64_t N) {
 //    tiles (N = 12288) it was 8-19% slower, hence the quarter.
 StreamSplit stream_split(int64_t T, int64_t K, int64_t N) {
     StreamSplit p{1, 0, 0};
-    if (T > 128 || K % 128 != 0) return p;
-    const int64_t bm = T <= 64 ? 64 : 128;
+    const bool wide = stream_256x128(T, K, N);   // 129..256 rows: 256x128 tiles, one per CU
+    if ((T > 128 && !wide) || K % 128 != 0) return p;
+    const int64_t bm = T <= 64 ? 64 : T <= 128 ? 128 : 256;
+    const int64_t bn = wide ? 128 : bm;
     const int64_t per_cu = T <= 64 ? 2 : 1;
-    p.tiles = ceil_div(T, bm) * ceil_div(N, bm);
-    p.tile_bytes = bm * bm * 4;
+    p.tiles = ceil_div(T, bm) * ceil_div(N, bn);
+    p.tile_bytes = bm * bn * 4;
     const int64_t slots = device_cus() * per_cu;
     const int64_t s = std::min<int64_t>(slots / p.tiles, (K / 128) / kStreamMinSlab);
     const int64_t fill = T <= 64 ? 4 : 2;   // tiles may occupy at most 1/fill of the slots
@@ -1331,13 +1332,22 @@ StreamSplit stream_split(int64_t T, int64_t K, int64_t N) {
 }
 
 int gemm_ksplit(int64_t T, int64_t K, int64_t N) {
-    if (T <= 128) return stream_split(T, K, N).s;
+    if (T <= 128 || stream_256x128(T, K, N)) return stream_split(T, K, N).s;
     return gemm_ksplit_plan(T, K, N).nsplit > 0 ? 2 : 1;
 }
 
+// 129..256 rows on the 256x128 streaming tile while its tiles fit the CUs
+// in one round and the large-tile kernel would not split K
+bool stream_256x128(int64_t T, int64_t K, int64_t N) {
+    return T > 128 && T <= 256 && K % 128 == 0 && ceil_div(N, 128) <= device_cus() &&
+           gemm_ksplit_plan(T, K, N).nsplit == 0;
+}
+
 hipError_t launch_gemm(const GemmArgs& a, int ht, hipStream_t stream) {
-    const bool big_split = a.ksplit == 2 && a.T > 128;
-    const bool stream_split_ok = a.ksplit >= 2 && a.T <= 128 && a.ksplit == stream_split(a.T, a.K, a.N).s;
+    const bool wide = stream_256x128(a.T, a.K, a.N);
+    const bool big_split = a.ksplit == 2 && a.T > 128 && !wide;
+    const bool stream_split_ok = a.ksplit >= 2 && (a.T <= 128 || wide) &&
+                                 a.ksplit == stream_split(a.T, a.K, a.N).s;
     if (a.ksplit != 1 &&
         !((big_split || stream_split_ok) && a.ks_count && a.ks_part && a.K % 128 == 0))
         return hipErrorInvalidValue;

@@ -107,6 +107,7 @@ def run_bf16(mm, name, X16, W16, tau, halved=False, big=None, rows=None):
     (16, 8192, 520, 5, 6.0, False), (50, 1152, 520, 3, 6.0, True),       # streaming matmul
     (80, 12288, 520, 5, 6.0, False), (128, 8192, 1032, 4, 6.0, True),    # streaming, K split
     (48, 8192, 1032, 5, 6.0, False), (24, 12288, 264, 3, 6.0, True),     # 64x64 split, finishing kernel
+    (192, 8192, 1032, 4, 6.0, False),                                     # 256x128 split
     (100, 2048, 264, 70, 6.0, False), (200, 2048, 264, 40, 6.0, True),   # outlier W rows through LDS
 ])
 def test_bf16_path(mm, T, K, N, nd, tau, halved):

@@ -116,6 +116,7 @@ ROUTES = [
     ("256x128 stream tile", 200, 1024, 520, 4),
     ("stream 128x128, K split in 8", 72, 49152, 264, 3),
     ("stream 64x64, K split, finishing kernel", 40, 12288, 1032, 3),
+    ("stream 256x128, K split", 200, 8192, 1032, 3),
     ("stream 128x128, K split in 2", 128, 12288, 1040, 4),
     ("big tile, register quantizer K<=4096", 300, 1024, 520, 5),
     ("big tile, all tiles split in K", 300, 8192, 520, 5),

@@ -22,7 +22,7 @@ def mm():
                                    (16, 8192, 1040), (8, 49152, 264), (4, 12288, 520),
                                    (200, 1024, 520), (64, 2048, 264),
                                    (8, 8192, 28672), (96, 12288, 520),
-                                   (48, 12288, 2048)])   # last two: K split
+                                   (48, 12288, 2048), (160, 8192, 520)])   # last three: K split
 def test_graph_replays_match_eager(mm, T, K, N):
     print(f"[case] graph replay {T}x{K}x{N}", flush=True)
     X, W = synth.random_case(40_000 + T, T, K, N, n_dims=3)

@@ -307,6 +307,8 @@ def test_random_long_rows(mm, T, K, N, nd, halved):
     # and the finishing kernel (8, 6 and 2 slabs; o > 16; memory-halved)
     (40, 12288, 1032, 3, False), (64, 49152, 4096, 5, False), (17, 4096, 264, 40, False),
     (33, 49152, 520, 20, True),
+    # 256x128 tiles (129..256 rows) on at most half of the CUs: 6, 8 and 4 slabs
+    (200, 12288, 1032, 4, False), (160, 16384, 520, 20, True), (256, 8192, 2056, 3, False),
 ])
 def test_stream_k_split(mm, T, K, N, nd, halved):
     X, W = synth.random_case(34_000 + T + K + N + nd, T, K, N, n_dims=nd)
