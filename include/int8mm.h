@@ -84,10 +84,12 @@ const char* int8mm_status_string(int status);
  * also covers, per
  * output tile, two 256 KB blocks of int32 partial sums and a counter; this
  * part depends on N and on the device's compute-unit count (256 when no
- * device can be queried).  For up to 128 rows with K a multiple of 128 and
- * at least 4096, whose output tiles (128 x 128 one per compute unit past 64
- * rows, 64 x 64 two per compute unit below) occupy at most half (128 x 128)
- * or a quarter (64 x 64) of the slots, the matmul splits K into
+ * device can be queried).  For up to 256 rows with K a multiple of 128 and
+ * at least 4096, whose output tiles (256 x 128 one per compute unit past
+ * 128 rows when K is not split in two as above and the N / 128 column
+ * tiles fit the device, 128 x 128 one per compute unit past 64 rows,
+ * 64 x 64 two per compute unit below) occupy at most half (256 x 128 and
+ * 128 x 128) or a quarter (64 x 64) of the slots, the matmul splits K into
  * S = min(slots / tiles, K / 2048, 8) slabs and the size covers, per tile,
  * S blocks of int32 partial sums of the tile's size and a counter.  A
  * workspace at least as large as the size without the split part is
