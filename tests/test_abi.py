@@ -70,6 +70,19 @@ def test_workspace_size(mm):
     assert t4096 < 3 * 4096 * 49152 + 2 * 512 * 12288 + (1 << 20)
     # fewer than two whole rounds: no split (T=512, N=32768: 256 tiles)
     assert mm.workspace_size(512, 12288, 32768) < 3 * 512 * 12288 + 2 * 512 * 32768 + (1 << 20)
+    # up to 256 rows, streaming tiles that fill at most half of the 256 CUs
+    # (a quarter of the 512 slots for 64 x 64) split K into
+    # S = min(slots / tiles, K / 2048, 8) slabs, each tile holding S blocks
+    # of int32 partial sums of its size
+    for T, K, N, tiles, bm, bn, s in ((256, 12288, 12288, 96, 256, 128, 2),
+                                      (160, 12288, 4096, 32, 256, 128, 6),
+                                      (128, 12288, 12288, 96, 128, 128, 2),
+                                      (64, 49152, 4096, 64, 64, 64, 8)):
+        base = 3 * T * K + 2 * 512 * N
+        part = tiles * s * bm * bn * 4
+        assert base + part <= mm.workspace_size(T, K, N) < base + part + (1 << 20), (T, K, N)
+    # more than half of the CUs (T=256, N=36864 above; T=128, N=36864 here): no split
+    assert mm.workspace_size(128, 12288, 36864) < 3 * 128 * 12288 + 2 * 512 * 36864 + (1 << 20)
     # decode shapes run as one kernel and need only the fixed regions
     assert mm.workspace_size(8, 8192, 28672) < 3 * 8 * 8192 + (1 << 16)
     # few rows with a long K: S = ceil(48 / 16) + 3 = 6 slabs of int32
